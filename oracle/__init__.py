@@ -1,0 +1,292 @@
+"""ctypes binding of the plain sequential C oracle (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  The product path (``libbrq``) never
+touches it.  All arrays are host numpy arrays; bfloat16 tensors are carried
+as ``numpy.uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("BRQ_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
+
+F32, BF16, I8, I32, U8 = 0, 1, 2, 3, 4
+PER_TENSOR, PER_ROW = 0, 1
+FLAG_NONFINITE = 1
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = C.CDLL(LIB_PATH)
+        vp, i64, f32, i32 = C.c_void_p, C.c_int64, C.c_float, C.c_int
+        L.orc_flush.restype = f32
+        L.orc_flush.argtypes = [f32]
+        L.orc_bf16_to_f32.restype = f32
+        L.orc_bf16_to_f32.argtypes = [C.c_uint16]
+        L.orc_f32_to_bf16.restype = C.c_uint16
+        L.orc_f32_to_bf16.argtypes = [f32]
+        L.orc_lsq_k2.restype = f32
+        L.orc_lsq_k2.argtypes = []
+        L.orc_tree_sum.restype = f32
+        L.orc_tree_sum.argtypes = [vp, i64]
+        L.orc_tree_sum_recursive.restype = f32
+        L.orc_tree_sum_recursive.argtypes = [vp, i64]
+        L.orc_lsq_scale.restype = None
+        L.orc_lsq_scale.argtypes = [f32, i64, vp, vp]
+        L.orc_quant1.restype = C.c_int8
+        L.orc_quant1.argtypes = [f32, f32]
+        L.orc_quantize_lsq.restype = i32
+        L.orc_quantize_lsq.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
+        L.orc_qgemm_fwd.restype = None
+        L.orc_qgemm_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp]
+        L.orc_qgemm_bwd_dx.restype = None
+        L.orc_qgemm_bwd_dx.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.orc_wht_int.restype = None
+        L.orc_wht_int.argtypes = [vp, i64, i64, i32, vp]
+        L.orc_wht_int_quant.restype = None
+        L.orc_wht_int_quant.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+        L.orc_wht_fp_quant.restype = i32
+        L.orc_wht_fp_quant.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+        L.orc_dw_gemm.restype = None
+        L.orc_dw_gemm.argtypes = [vp, vp, i64, i64, i64, f32, f32, f32, i32, i64, i64, vp]
+        L.orc_qgemm_bwd_dw_wht.restype = i32
+        L.orc_qgemm_bwd_dw_wht.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp, vp]
+        L.orc_rmsnorm_fwd.restype = i32
+        L.orc_rmsnorm_fwd.argtypes = [vp, vp, i32, i64, i64, f32, vp, vp]
+        L.orc_rmsnorm_bwd.restype = None
+        L.orc_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, vp, vp]
+        L.orc_grad_norm.restype = i32
+        L.orc_grad_norm.argtypes = [vp, i64, vp, vp]
+        L.orc_sha256.restype = None
+        L.orc_sha256.argtypes = [vp, C.c_uint64, vp]
+        L.orc_merkle_root.restype = None
+        L.orc_merkle_root.argtypes = [vp, C.c_uint64, vp]
+        L.orc_tensor_digest.restype = None
+        L.orc_tensor_digest.argtypes = [vp, C.c_uint64, i32, i32, vp, C.c_char_p, vp]
+        L.orc_hash_state.restype = None
+        L.orc_hash_state.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def _c(a, dt=None):
+    a = np.ascontiguousarray(a if dt is None else a.astype(dt, copy=False))
+    return a
+
+
+def flush(v: float) -> float:
+    return lib().orc_flush(v)
+
+
+def bf16_to_f32(h: int) -> float:
+    return lib().orc_bf16_to_f32(h)
+
+
+def f32_to_bf16(f: float) -> int:
+    return lib().orc_f32_to_bf16(f)
+
+
+def lsq_k2() -> float:
+    return lib().orc_lsq_k2()
+
+
+def tree_sum(leaves, recursive: bool = False) -> np.float32:
+    a = _c(leaves, np.float32)
+    f = lib().orc_tree_sum_recursive if recursive else lib().orc_tree_sum
+    return np.float32(f(_p(a), a.size))
+
+
+def lsq_scale(S: float, n: int):
+    s = np.zeros(1, np.float32)
+    r = np.zeros(1, np.float32)
+    lib().orc_lsq_scale(S, n, _p(s), _p(r))
+    return s[0], r[0]
+
+
+def quant1(x: float, r: float) -> int:
+    return int(lib().orc_quant1(x, r))
+
+
+def quantize_lsq(x: np.ndarray, per_row: bool = False, col_mul=None, want_t: bool = False):
+    """Returns (q, q_t or None, scale, amax, flags)."""
+    x = _c(x)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.int8)
+    q_t = np.empty((cols, rows), np.int8) if want_t else None
+    ns = rows if per_row else 1
+    scale = np.empty(ns, np.float32)
+    amax = np.empty(ns, np.float32)
+    cm = None if col_mul is None else _c(col_mul, np.float32)
+    flags = lib().orc_quantize_lsq(_p(x), _dtype_code(x), rows, cols,
+                                   PER_ROW if per_row else PER_TENSOR,
+                                   _p(cm), _p(q), _p(q_t), _p(scale), _p(amax))
+    return q, q_t, scale, amax, flags
+
+
+def qgemm_fwd(q_x, s_x, q_w, s_w):
+    q_x, q_w = _c(q_x, np.int8), _c(q_w, np.int8)
+    M, K = q_x.shape
+    N = q_w.shape[0]
+    s_x = _c(np.atleast_1d(s_x), np.float32)
+    s_w = _c(np.atleast_1d(s_w), np.float32)
+    y = np.empty((M, N), np.float32)
+    lib().orc_qgemm_fwd(_p(q_x), _p(s_x), _p(q_w), _p(s_w), int(s_w.size > 1),
+                        M, N, K, _p(y))
+    return y
+
+
+def qgemm_bwd_dx(q_g, s_g, q_w):
+    q_g, q_w = _c(q_g, np.int8), _c(q_w, np.int8)
+    M, N = q_g.shape
+    K = q_w.shape[1]
+    s_g = _c(np.atleast_1d(s_g), np.float32)
+    dx = np.empty((M, K), np.float32)
+    lib().orc_qgemm_bwd_dx(_p(q_g), _p(s_g), _p(q_w), M, N, K, _p(dx))
+    return dx
+
+
+def wht_int(q_x, b: int):
+    q_x = _c(q_x, np.int8)
+    M, K = q_x.shape
+    u = np.empty((M, K), np.int32)
+    lib().orc_wht_int(_p(q_x), M, K, b, _p(u))
+    return u
+
+
+def wht_int_quant(q_x, b: int):
+    q_x = _c(q_x, np.int8)
+    M, K = q_x.shape
+    q_u = np.empty((M, K), np.int8)
+    s_u = np.zeros(1, np.float32)
+    S = np.zeros(1, np.int64)
+    lib().orc_wht_int_quant(_p(q_x), M, K, b, _p(q_u), _p(s_u), _p(S))
+    return q_u, s_u[0], int(S[0])
+
+
+def wht_fp_quant(dy, b: int, want_v: bool = False):
+    dy = _c(dy)
+    M, N = dy.shape
+    q_v = np.empty((M, N), np.int8)
+    s_v = np.zeros(1, np.float32)
+    v = np.empty((M, N), np.float32) if want_v else None
+    flags = lib().orc_wht_fp_quant(_p(dy), _dtype_code(dy), M, N, b, _p(q_v), _p(s_v), _p(v))
+    return q_v, s_v[0], v, flags
+
+
+def dw_gemm(q_v, q_u, s_x, s_u, s_v, b: int, n_lo: int = 0, n_hi=None):
+    q_v, q_u = _c(q_v, np.int8), _c(q_u, np.int8)
+    M, N = q_v.shape
+    K = q_u.shape[1]
+    n_hi = N if n_hi is None else n_hi
+    dw = np.zeros((N, K), np.float32)
+    lib().orc_dw_gemm(_p(q_v), _p(q_u), M, N, K, float(s_x), float(s_u), float(s_v), b,
+                      n_lo, n_hi, _p(dw))
+    return dw
+
+
+def qgemm_bwd_dw_wht(q_x, s_x, dy, b: int):
+    q_x = _c(q_x, np.int8)
+    dy = _c(dy)
+    M, K = q_x.shape
+    N = dy.shape[1]
+    s_x = _c(np.atleast_1d(s_x), np.float32)
+    dw = np.empty((N, K), np.float32)
+    su = np.zeros(1, np.float32)
+    sv = np.zeros(1, np.float32)
+    flags = lib().orc_qgemm_bwd_dw_wht(_p(q_x), _p(s_x), _p(dy), _dtype_code(dy), M, N, K, b,
+                                       _p(dw), _p(su), _p(sv))
+    return dw, su[0], sv[0], flags
+
+
+def rmsnorm_fwd(x, g, eps: float = 1e-6):
+    x, g = _c(x), _c(g)
+    T, D = x.shape
+    y = np.empty_like(x)
+    rstd = np.empty(T, np.float32)
+    flags = lib().orc_rmsnorm_fwd(_p(x), _p(g), _dtype_code(x), T, D, eps, _p(y), _p(rstd))
+    return y, rstd, flags
+
+
+def rmsnorm_bwd(x, g, rstd, dy):
+    x, g, dy = _c(x), _c(g), _c(dy)
+    rstd = _c(rstd, np.float32)
+    T, D = x.shape
+    dx = np.empty_like(x)
+    dg = np.empty(D, np.float32)
+    lib().orc_rmsnorm_bwd(_p(x), _p(g), _p(rstd), _p(dy), _dtype_code(x), T, D, _p(dx), _p(dg))
+    return dx, dg
+
+
+def grad_norm(v):
+    v = _c(v, np.float32).reshape(-1)
+    ss = np.zeros(1, np.float32)
+    nrm = np.zeros(1, np.float32)
+    flags = lib().orc_grad_norm(_p(v), v.size, _p(ss), _p(nrm))
+    return ss[0], nrm[0], flags
+
+
+def sha256(data: bytes) -> bytes:
+    buf = np.frombuffer(data, np.uint8) if len(data) else np.zeros(1, np.uint8)
+    out = np.zeros(32, np.uint8)
+    lib().orc_sha256(_p(buf), len(data), _p(out))
+    return out.tobytes()
+
+
+def merkle_root(a: np.ndarray) -> bytes:
+    b = np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+    buf = b if b.size else np.zeros(1, np.uint8)
+    out = np.zeros(32, np.uint8)
+    lib().orc_merkle_root(_p(buf), b.size, _p(out))
+    return out.tobytes()
+
+
+_DT = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.int8): I8,
+       np.dtype(np.int32): I32, np.dtype(np.uint8): U8}
+
+
+def hash_state(tensors):
+    """tensors: list of (name, numpy array[, dtype code]).  bf16 arrays are
+    uint16 and hash with the bf16 dtype code unless one is given."""
+    n = len(tensors)
+    arrs, names, dtypes, ndims, dims, nbytes = [], [], [], [], [], []
+    for t in tensors:
+        name, a = t[0], np.ascontiguousarray(t[1])
+        code = t[2] if len(t) > 2 else _DT[a.dtype]
+        arrs.append(a if a.size else np.zeros(1, a.dtype))
+        names.append(name.encode())
+        dtypes.append(code)
+        ndims.append(a.ndim)
+        dims.extend(a.shape)
+        nbytes.append(a.nbytes)
+    ptrs = (C.c_void_p * max(n, 1))(*[x.ctypes.data for x in arrs])
+    nb = np.array(nbytes, np.uint64)
+    dt = np.array(dtypes, np.int32)
+    nd = np.array(ndims, np.int32)
+    dm = np.array(dims if dims else [0], np.int64)
+    nm = (C.c_char_p * max(n, 1))(*names)
+    out = np.zeros(32, np.uint8)
+    lib().orc_hash_state(n, ptrs, _p(nb), _p(dt), _p(nd), _p(dm), nm, _p(out))
+    return out.tobytes()

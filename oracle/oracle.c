@@ -1,0 +1,559 @@
+/*
+ * oracle.c -- plain, sequential CPU oracle (TEST INFRASTRUCTURE ONLY).
+ *
+ * Compiled with gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math on
+ * x86-64 (SSE2 scalar arithmetic, default MXCSR: round to nearest even,
+ * gradual underflow).  The flush of subnormals is written out below, so
+ * the hardware flush modes are never relied upon.
+ *
+ * OpenMP (when enabled) only splits loops over independent outputs: every
+ * output value is produced by the same sequential code whatever the thread
+ * count, so results do not depend on it.  Reductions never run in parallel.
+ *
+ * Page references are to "Open-1B: A Fully Auditable Training Run"
+ * (arXiv 2609.17380): section, table or appendix named at each routine.
+ */
+#include "oracle.h"
+
+#include <assert.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------
+ * Arithmetic model -- §2.1 "Subnormals", "Fused multiply-add", Table 1.
+ * Each helper performs exactly one IEEE binary32 operation and then flushes
+ * a subnormal result to a zero of the same sign.
+ * ---------------------------------------------------------------------- */
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+float orc_flush(float v) {
+  uint32_t u = f2u(v);
+  if ((u & 0x7f800000u) == 0) u &= 0x80000000u;
+  return u2f(u);
+}
+static float fadd(float a, float b) { return orc_flush(a + b); }
+static float fsub(float a, float b) { return orc_flush(a - b); }
+static float fmul(float a, float b) { return orc_flush(a * b); }
+static float fdiv(float a, float b) { return orc_flush(a / b); }
+static float fsqrt(float a) { return orc_flush(sqrtf(a)); }
+static float fabs_(float a) { return u2f(f2u(a) & 0x7fffffffu); }
+
+float orc_bf16_to_f32(uint16_t h) { return orc_flush(u2f((uint32_t)h << 16)); }
+
+uint16_t orc_f32_to_bf16(float f) {
+  uint32_t u = f2u(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* Element i of a tensor of dtype F32 or BF16, after DAZ. */
+static float load(const void* p, int dtype, int64_t i) {
+  if (dtype == ORC_BF16) return orc_bf16_to_f32(((const uint16_t*)p)[i]);
+  return orc_flush(((const float*)p)[i]);
+}
+static void store(void* p, int dtype, int64_t i, float v) {
+  if (dtype == ORC_BF16) ((uint16_t*)p)[i] = orc_f32_to_bf16(v);
+  else ((float*)p)[i] = v;
+}
+
+/* ------------------------------------------------------------------------
+ * Canonical reduction tree -- §2.1 "Reduction order", Table 1 row 2.
+ * Level 0 holds the leaves in logical row-major order; each level pairs
+ * neighbours (2i, 2i+1) with the lower index on the left, and an unpaired
+ * last node moves up unchanged.  The root is the sum.
+ * ---------------------------------------------------------------------- */
+static float tree_inplace(float* buf, int64_t n) {
+  if (n <= 0) return 0.0f;
+  int64_t len = n;
+  while (len > 1) {
+    int64_t half = len / 2;
+    for (int64_t i = 0; i < half; i++) buf[i] = fadd(buf[2 * i], buf[2 * i + 1]);
+    if (len & 1) {
+      buf[half] = buf[len - 1];
+      len = half + 1;
+    } else {
+      len = half;
+    }
+  }
+  return buf[0];
+}
+
+float orc_tree_sum(const float* leaves, int64_t n) {
+  if (n <= 0) return 0.0f;
+  float* buf = (float*)malloc((size_t)n * sizeof(float));
+  assert(buf);
+  memcpy(buf, leaves, (size_t)n * sizeof(float));
+  float s = tree_inplace(buf, n);
+  free(buf);
+  return s;
+}
+
+/* The same tree, coded top-down: the root's left child covers the largest
+ * power of two strictly below n, the right child covers the rest. */
+static float tree_rec(const float* l, int64_t n) {
+  if (n == 1) return l[0];
+  int64_t p = 1;
+  while (p * 2 < n) p *= 2;
+  return fadd(tree_rec(l, p), tree_rec(l + p, n - p));
+}
+float orc_tree_sum_recursive(const float* leaves, int64_t n) {
+  if (n <= 0) return 0.0f;
+  return tree_rec(leaves, n);
+}
+
+/* ------------------------------------------------------------------------
+ * LSQ quantiser -- §3.1 "int8 quantization-aware training", §4.2: the
+ * step size is 2*mean(|w|)/sqrt(q_max) with q_max = 127, re-evaluated from
+ * the tensor it quantises.  App. A.3: the mean multiplies by fl(1/n) and
+ * the division by sqrt(q_max) is a multiply by its fp32 reciprocal, so the
+ * factor is K2 = 2 * fl(1/fl(sqrt(127))).  The quantiser divides by the
+ * step as a multiply by r = fl(1/s), rounds half to even, clamps to +-127.
+ * ---------------------------------------------------------------------- */
+float orc_lsq_k2(void) {
+  volatile float q = 127.0f;
+  float rs = fdiv(1.0f, fsqrt(q));
+  return fmul(2.0f, rs);
+}
+
+static float inv_count(int64_t n) { return fdiv(1.0f, (float)n); }
+
+void orc_lsq_scale(float S, int64_t n, float* s_out, float* r_out) {
+  float m = fmul(S, inv_count(n));
+  float s = fmul(m, orc_lsq_k2());
+  *s_out = s;
+  *r_out = (s == 0.0f) ? 0.0f : fdiv(1.0f, s);
+}
+
+int8_t orc_quant1(float x, float r) {
+  float t = rintf(fmul(x, r));
+  if (t > 127.0f) t = 127.0f;
+  if (t < -127.0f) t = -127.0f;
+  return (int8_t)t;
+}
+
+/* One quantisation group of n values: tree of |v|, scale, codes. */
+static int lsq_group(const float* v, int64_t n, int8_t* q, float* s_out,
+                     float* amax_out) {
+  float* leaves = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+  assert(leaves);
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; i++) {
+    leaves[i] = fabs_(v[i]);
+    if (leaves[i] > amax) amax = leaves[i];
+  }
+  float S = tree_inplace(leaves, n);
+  free(leaves);
+  float s, r;
+  orc_lsq_scale(S, n, &s, &r);
+  for (int64_t i = 0; i < n; i++) q[i] = orc_quant1(v[i], r);
+  *s_out = s;
+  if (amax_out) *amax_out = amax;
+  return isfinite(S) ? 0 : ORC_FLAG_NONFINITE;
+}
+
+int orc_quantize_lsq(const void* x, int dtype, int64_t rows, int64_t cols,
+                     int gran, const float* col_mul, int8_t* q, int8_t* q_t,
+                     float* scale, float* amax) {
+  int64_t n = rows * cols;
+  float* v = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+  assert(v);
+  for (int64_t i = 0; i < n; i++) {
+    float e = load(x, dtype, i);
+    if (col_mul) e = fmul(e, orc_flush(col_mul[i % cols]));
+    v[i] = e;
+  }
+  int flags = 0;
+  if (gran == ORC_PER_TENSOR) {
+    flags |= lsq_group(v, n, q, &scale[0], amax ? &amax[0] : NULL);
+  } else {
+    for (int64_t r = 0; r < rows; r++)
+      flags |= lsq_group(v + r * cols, cols, q + r * cols, &scale[r],
+                         amax ? &amax[r] : NULL);
+  }
+  if (q_t)
+    for (int64_t r = 0; r < rows; r++)
+      for (int64_t c = 0; c < cols; c++) q_t[c * rows + r] = q[r * cols + c];
+  free(v);
+  return flags;
+}
+
+/* ------------------------------------------------------------------------
+ * int8 GEMMs -- §3.2 "int8 computation": int32 accumulation, then
+ * dequantisation.  The integer sum is exact, so its order is immaterial;
+ * int64 is used here and the int32 range is asserted.
+ * ---------------------------------------------------------------------- */
+static float acc_to_f32(int64_t acc) {
+  assert(acc <= INT32_MAX && acc >= INT32_MIN);
+  return (float)(int32_t)acc; /* int32 -> binary32, round to nearest even */
+}
+
+void orc_qgemm_fwd(const int8_t* qx, const float* s_x, const int8_t* qw,
+                   const float* s_w, int w_per_row, int64_t M, int64_t N,
+                   int64_t K, float* y) {
+  float sx = orc_flush(s_x[0]);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t m = 0; m < M; m++) {
+    for (int64_t n = 0; n < N; n++) {
+      int64_t acc = 0;
+      for (int64_t k = 0; k < K; k++)
+        acc += (int64_t)qx[m * K + k] * (int64_t)qw[n * K + k];
+      float c = fmul(sx, orc_flush(w_per_row ? s_w[n] : s_w[0]));
+      y[m * N + n] = fmul(acc_to_f32(acc), c);
+    }
+  }
+}
+
+void orc_qgemm_bwd_dx(const int8_t* qg, const float* s_g, const int8_t* qw,
+                      int64_t M, int64_t N, int64_t K, float* dx) {
+  float sg = orc_flush(s_g[0]);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t m = 0; m < M; m++) {
+    int64_t* acc = (int64_t*)calloc((size_t)K, sizeof(int64_t));
+    assert(acc);
+    for (int64_t n = 0; n < N; n++) {
+      int64_t g = qg[m * N + n];
+      for (int64_t k = 0; k < K; k++) acc[k] += g * (int64_t)qw[n * K + k];
+    }
+    for (int64_t k = 0; k < K; k++) dx[m * K + k] = fmul(acc_to_f32(acc[k]), sg);
+    free(acc);
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Walsh-Hadamard rotation along tokens -- §3.2 "int8 computation": a
+ * Walsh-Hadamard rotation along the contraction dimension (tokens, for the
+ * weight gradient) flattens gradient outliers before int8 quantisation.
+ * H_b[i][j] = (-1)^popcount(i & j): Sylvester order, unnormalised; the 1/b
+ * of H^T H = b I is folded into the dW dequantisation factor.
+ * ---------------------------------------------------------------------- */
+static int hadamard(int i, int j) { return (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1; }
+
+void orc_wht_int(const int8_t* qx, int64_t M, int64_t K, int b, int32_t* u) {
+  /* u[t][k] = sum_j H_b[t mod b][j] * qx[b*floor(t/b) + j][k], exact. */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t t = 0; t < M; t++) {
+    int64_t base = (t / b) * b;
+    int i = (int)(t % b);
+    for (int64_t k = 0; k < K; k++) u[t * K + k] = 0;
+    for (int j = 0; j < b; j++) {
+      int h = hadamard(i, j);
+      const int8_t* row = qx + (base + j) * K;
+      for (int64_t k = 0; k < K; k++) u[t * K + k] += h * (int32_t)row[k];
+    }
+  }
+}
+
+void orc_wht_int_quant(const int8_t* qx, int64_t M, int64_t K, int b,
+                       int8_t* q_u, float* s_u_out, int64_t* S_u_out) {
+  int64_t n = M * K;
+  int32_t* u = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+  assert(u);
+  orc_wht_int(qx, M, K, b, u);
+  int64_t S = 0;
+  for (int64_t i = 0; i < n; i++) S += (u[i] < 0) ? -(int64_t)u[i] : (int64_t)u[i];
+  /* The exact integer sum (below 2^53) goes through double unchanged, then
+   * rounds once to binary32. */
+  float Sf = (float)(double)S;
+  float s, r;
+  orc_lsq_scale(Sf, n, &s, &r);
+  for (int64_t i = 0; i < n; i++) q_u[i] = orc_quant1((float)u[i], r);
+  *s_u_out = s;
+  if (S_u_out) *S_u_out = S;
+  free(u);
+}
+
+int orc_wht_fp_quant(const void* dy, int dtype, int64_t M, int64_t N, int b,
+                     int8_t* q_v, float* s_v, float* v_out) {
+  int64_t n = M * N;
+  float* v = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+  assert(v);
+  for (int64_t i = 0; i < n; i++) v[i] = load(dy, dtype, i);
+  /* Per column and aligned block of b tokens, butterflies in stage order
+   * h = 1, 2, 4, ..., b/2: (v_j, v_j+h) <- (v_j + v_j+h, v_j - v_j+h). */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t c = 0; c < N; c++) {
+    for (int64_t base = 0; base < M; base += b) {
+      for (int h = 1; h < b; h *= 2) {
+        for (int j = 0; j < b; j++) {
+          if ((j % (2 * h)) >= h) continue;
+          float* a = &v[(base + j) * N + c];
+          float* d = &v[(base + j + h) * N + c];
+          float x0 = *a, x1 = *d;
+          *a = fadd(x0, x1);
+          *d = fsub(x0, x1);
+        }
+      }
+    }
+  }
+  float amax;
+  int flags = lsq_group(v, n, q_v, s_v, &amax);
+  if (v_out) memcpy(v_out, v, (size_t)n * sizeof(float));
+  free(v);
+  return flags;
+}
+
+void orc_dw_gemm(const int8_t* q_v, const int8_t* q_u, int64_t M, int64_t N,
+                 int64_t K, float s_x, float s_u, float s_v, int b,
+                 int64_t n_lo, int64_t n_hi, float* dw) {
+  float inv_b = ldexpf(1.0f, -__builtin_ctz((unsigned)b)); /* exact 1/b */
+  float c = fmul(fmul(fmul(orc_flush(s_x), orc_flush(s_u)), orc_flush(s_v)), inv_b);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t n = n_lo; n < n_hi; n++) {
+    int64_t* acc = (int64_t*)calloc((size_t)K, sizeof(int64_t));
+    assert(acc);
+    for (int64_t m = 0; m < M; m++) {
+      int64_t g = q_v[m * N + n];
+      if (g == 0) continue;
+      const int8_t* row = q_u + m * K;
+      for (int64_t k = 0; k < K; k++) acc[k] += g * (int64_t)row[k];
+    }
+    for (int64_t k = 0; k < K; k++) dw[n * K + k] = fmul(acc_to_f32(acc[k]), c);
+    free(acc);
+  }
+}
+
+int orc_qgemm_bwd_dw_wht(const int8_t* qx, const float* s_x, const void* dy,
+                         int dtype, int64_t M, int64_t N, int64_t K, int b,
+                         float* dw, float* s_u_out, float* s_v_out) {
+  int8_t* q_u = (int8_t*)malloc((size_t)(M * K > 0 ? M * K : 1));
+  int8_t* q_v = (int8_t*)malloc((size_t)(M * N > 0 ? M * N : 1));
+  assert(q_u && q_v);
+  float s_u, s_v;
+  orc_wht_int_quant(qx, M, K, b, q_u, &s_u, NULL);
+  int flags = orc_wht_fp_quant(dy, dtype, M, N, b, q_v, &s_v, NULL);
+  orc_dw_gemm(q_v, q_u, M, N, K, s_x[0], s_u, s_v, b, 0, N, dw);
+  if (s_u_out) *s_u_out = s_u;
+  if (s_v_out) *s_v_out = s_v;
+  free(q_u);
+  free(q_v);
+  return flags;
+}
+
+/* ------------------------------------------------------------------------
+ * RMSNorm -- §3.1 "RMSNorm" (pre-norm, no bias) and the precision note
+ * (normalisation in FP32, parameters BF16): y = x * rsqrt(mean(x^2)+eps)*g
+ * with a correctly rounded sqrt followed by a reciprocal.
+ * ---------------------------------------------------------------------- */
+int orc_rmsnorm_fwd(const void* x, const void* g, int dtype, int64_t T,
+                    int64_t D, float eps, void* y, float* rstd) {
+  float* xs = (float*)malloc((size_t)D * sizeof(float));
+  float* sq = (float*)malloc((size_t)D * sizeof(float));
+  assert(xs && sq);
+  float invD = inv_count(D);
+  float e = orc_flush(eps);
+  int flags = 0;
+  for (int64_t t = 0; t < T; t++) {
+    for (int64_t j = 0; j < D; j++) {
+      xs[j] = load(x, dtype, t * D + j);
+      sq[j] = fmul(xs[j], xs[j]);
+    }
+    float ss = tree_inplace(sq, D);
+    if (!isfinite(ss)) flags |= ORC_FLAG_NONFINITE;
+    float ms = fmul(ss, invD);
+    float r = fdiv(1.0f, fsqrt(fadd(ms, e)));
+    rstd[t] = r;
+    for (int64_t j = 0; j < D; j++)
+      store(y, dtype, t * D + j, fmul(fmul(xs[j], r), load(g, dtype, j)));
+  }
+  free(xs);
+  free(sq);
+  return flags;
+}
+
+/* Backward per row: xh = x*rstd, d = dy*g, dot = tree(d*xh), mu = dot/D,
+ * dx = rstd*(d - xh*mu).  dg[j] = tree over tokens of dy*xh. */
+void orc_rmsnorm_bwd(const void* x, const void* g, const float* rstd,
+                     const void* dy, int dtype, int64_t T, int64_t D,
+                     void* dx, float* dg) {
+  float invD = inv_count(D);
+  float* xh = (float*)malloc((size_t)D * sizeof(float));
+  float* d = (float*)malloc((size_t)D * sizeof(float));
+  float* p = (float*)malloc((size_t)D * sizeof(float));
+  float* col = (float*)malloc((size_t)(T > 0 ? T : 1) * sizeof(float));
+  assert(xh && d && p && col);
+  for (int64_t t = 0; t < T; t++) {
+    float r = orc_flush(rstd[t]);
+    for (int64_t j = 0; j < D; j++) {
+      xh[j] = fmul(load(x, dtype, t * D + j), r);
+      d[j] = fmul(load(dy, dtype, t * D + j), load(g, dtype, j));
+      p[j] = fmul(d[j], xh[j]);
+    }
+    float dot = tree_inplace(p, D);
+    float mu = fmul(dot, invD);
+    for (int64_t j = 0; j < D; j++)
+      store(dx, dtype, t * D + j, fmul(r, fsub(d[j], fmul(xh[j], mu))));
+  }
+  for (int64_t j = 0; j < D; j++) {
+    for (int64_t t = 0; t < T; t++) {
+      float xhat = fmul(load(x, dtype, t * D + j), orc_flush(rstd[t]));
+      col[t] = fmul(load(dy, dtype, t * D + j), xhat);
+    }
+    dg[j] = tree_inplace(col, T);
+  }
+  free(xh);
+  free(d);
+  free(p);
+  free(col);
+}
+
+/* ------------------------------------------------------------------------
+ * Global gradient norm -- §3.2 "Optimizer" (global l2 clipping) with FP32
+ * gradient reduction: ss = tree(v*v), norm = sqrt(ss).
+ * ---------------------------------------------------------------------- */
+int orc_grad_norm(const float* v, int64_t n, float* sumsq, float* norm) {
+  float* sq = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+  assert(sq);
+  for (int64_t i = 0; i < n; i++) {
+    float e = orc_flush(v[i]);
+    sq[i] = fmul(e, e);
+  }
+  float ss = tree_inplace(sq, n);
+  free(sq);
+  *sumsq = ss;
+  *norm = fsqrt(ss);
+  return isfinite(ss) ? 0 : ORC_FLAG_NONFINITE;
+}
+
+/* ------------------------------------------------------------------------
+ * SHA-256, FIPS 180-4 §6.2, and the canonical state hash (§5 "Runtime
+ * overhead" and App. B: a canonical per-step hash of the training state;
+ * computed here over raw little-endian tensor bytes in a Merkle tree).
+ * ---------------------------------------------------------------------- */
+static const uint32_t SHA_K[64] = {
+    0x428a2f98, 0x71374491, 0xb5c0fbcf, 0xe9b5dba5, 0x3956c25b, 0x59f111f1,
+    0x923f82a4, 0xab1c5ed5, 0xd807aa98, 0x12835b01, 0x243185be, 0x550c7dc3,
+    0x72be5d74, 0x80deb1fe, 0x9bdc06a7, 0xc19bf174, 0xe49b69c1, 0xefbe4786,
+    0x0fc19dc6, 0x240ca1cc, 0x2de92c6f, 0x4a7484aa, 0x5cb0a9dc, 0x76f988da,
+    0x983e5152, 0xa831c66d, 0xb00327c8, 0xbf597fc7, 0xc6e00bf3, 0xd5a79147,
+    0x06ca6351, 0x14292967, 0x27b70a85, 0x2e1b2138, 0x4d2c6dfc, 0x53380d13,
+    0x650a7354, 0x766a0abb, 0x81c2c92e, 0x92722c85, 0xa2bfe8a1, 0xa81a664b,
+    0xc24b8b70, 0xc76c51a3, 0xd192e819, 0xd6990624, 0xf40e3585, 0x106aa070,
+    0x19a4c116, 0x1e376c08, 0x2748774c, 0x34b0bcb5, 0x391c0cb3, 0x4ed8aa4a,
+    0x5b9cca4f, 0x682e6ff3, 0x748f82ee, 0x78a5636f, 0x84c87814, 0x8cc70208,
+    0x90befffa, 0xa4506ceb, 0xbef9a3f7, 0xc67178f2};
+
+static uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
+
+static void sha_block(uint32_t H[8], const uint8_t blk[64]) {
+  uint32_t W[64];
+  for (int t = 0; t < 16; t++)
+    W[t] = ((uint32_t)blk[4 * t] << 24) | ((uint32_t)blk[4 * t + 1] << 16) |
+           ((uint32_t)blk[4 * t + 2] << 8) | (uint32_t)blk[4 * t + 3];
+  for (int t = 16; t < 64; t++) {
+    uint32_t s0 = rotr(W[t - 15], 7) ^ rotr(W[t - 15], 18) ^ (W[t - 15] >> 3);
+    uint32_t s1 = rotr(W[t - 2], 17) ^ rotr(W[t - 2], 19) ^ (W[t - 2] >> 10);
+    W[t] = W[t - 16] + s0 + W[t - 7] + s1;
+  }
+  uint32_t a = H[0], b = H[1], c = H[2], d = H[3], e = H[4], f = H[5], g = H[6], h = H[7];
+  for (int t = 0; t < 64; t++) {
+    uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
+    uint32_t ch = (e & f) ^ (~e & g);
+    uint32_t T1 = h + S1 + ch + SHA_K[t] + W[t];
+    uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
+    uint32_t maj = (a & b) ^ (a & c) ^ (b & c);
+    uint32_t T2 = S0 + maj;
+    h = g; g = f; f = e; e = d + T1; d = c; c = b; b = a; a = T1 + T2;
+  }
+  H[0] += a; H[1] += b; H[2] += c; H[3] += d;
+  H[4] += e; H[5] += f; H[6] += g; H[7] += h;
+}
+
+void orc_sha256(const uint8_t* msg, uint64_t len, uint8_t out[32]) {
+  uint32_t H[8] = {0x6a09e667, 0xbb67ae85, 0x3c6ef372, 0xa54ff53a,
+                   0x510e527f, 0x9b05688c, 0x1f83d9ab, 0x5be0cd19};
+  uint64_t full = len / 64;
+  for (uint64_t i = 0; i < full; i++) sha_block(H, msg + 64 * i);
+  uint8_t tail[128];
+  uint64_t rem = len - 64 * full;
+  memset(tail, 0, sizeof tail);
+  if (rem) memcpy(tail, msg + 64 * full, (size_t)rem);
+  tail[rem] = 0x80;
+  uint64_t tl = (rem + 1 + 8 <= 64) ? 64 : 128;
+  uint64_t bits = len * 8;
+  for (int i = 0; i < 8; i++) tail[tl - 1 - i] = (uint8_t)(bits >> (8 * i));
+  sha_block(H, tail);
+  if (tl == 128) sha_block(H, tail + 64);
+  for (int i = 0; i < 8; i++) {
+    out[4 * i] = (uint8_t)(H[i] >> 24);
+    out[4 * i + 1] = (uint8_t)(H[i] >> 16);
+    out[4 * i + 2] = (uint8_t)(H[i] >> 8);
+    out[4 * i + 3] = (uint8_t)H[i];
+  }
+}
+
+void orc_merkle_root(const uint8_t* bytes, uint64_t nbytes, uint8_t out[32]) {
+  const uint64_t LEAF = 4096, FAN = 128;
+  uint64_t cnt = nbytes == 0 ? 1 : (nbytes + LEAF - 1) / LEAF;
+  uint8_t* d = (uint8_t*)malloc((size_t)cnt * 32);
+  assert(d);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t i = 0; i < (int64_t)cnt; i++) {
+    uint64_t off = (uint64_t)i * LEAF;
+    uint64_t len = nbytes - off < LEAF ? nbytes - off : LEAF;
+    orc_sha256(bytes + off, nbytes == 0 ? 0 : len, d + 32 * i);
+  }
+  while (cnt > 1) {
+    uint64_t nc = (cnt + FAN - 1) / FAN;
+    for (uint64_t j = 0; j < nc; j++) {
+      uint64_t k = cnt - FAN * j < FAN ? cnt - FAN * j : FAN;
+      uint8_t tmp[32];
+      orc_sha256(d + 32 * FAN * j, 32 * k, tmp);
+      memcpy(d + 32 * j, tmp, 32); /* j <= FAN*j, so the source is read first */
+    }
+    cnt = nc;
+  }
+  memcpy(out, d, 32);
+  free(d);
+}
+
+void orc_tensor_digest(const uint8_t* bytes, uint64_t nbytes, int dtype,
+                       int ndim, const int64_t* dims, const char* name,
+                       uint8_t out[32]) {
+  uint8_t root[32];
+  orc_merkle_root(bytes, nbytes, root);
+  size_t nl = strlen(name);
+  size_t hl = 4 + 1 + 1 + 8 * (size_t)ndim + 2 + nl + 32;
+  uint8_t* h = (uint8_t*)malloc(hl);
+  assert(h);
+  size_t o = 0;
+  memcpy(h, "BRQ1", 4); o = 4;
+  h[o++] = (uint8_t)dtype;
+  h[o++] = (uint8_t)ndim;
+  for (int i = 0; i < ndim; i++)
+    for (int b = 0; b < 8; b++) h[o++] = (uint8_t)((uint64_t)dims[i] >> (8 * b));
+  h[o++] = (uint8_t)(nl & 0xff);
+  h[o++] = (uint8_t)(nl >> 8);
+  memcpy(h + o, name, nl); o += nl;
+  memcpy(h + o, root, 32); o += 32;
+  orc_sha256(h, o, out);
+  free(h);
+}
+
+void orc_hash_state(int n, const uint8_t* const* ptrs, const uint64_t* nbytes,
+                    const int* dtypes, const int* ndims, const int64_t* dims,
+                    const char* const* names, uint8_t out[32]) {
+  uint8_t* cat = (uint8_t*)malloc((size_t)(n > 0 ? n : 1) * 32);
+  assert(cat);
+  const int64_t* dp = dims;
+  for (int i = 0; i < n; i++) {
+    orc_tensor_digest(ptrs[i], nbytes[i], dtypes[i], ndims[i], dp, names[i], cat + 32 * i);
+    dp += ndims[i];
+  }
+  orc_sha256(cat, 32 * (uint64_t)n, out);
+  free(cat);
+}

@@ -1,0 +1,159 @@
+/*
+ * oracle.h -- plain, sequential CPU oracle for the bitwise-reproducible W8A8
+ * QAT linear layer (TEST INFRASTRUCTURE ONLY).
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  The product path (libbrq, HIP) shares no code,
+ * header, table or constant with it.
+ *
+ * Every routine is the definition written out, in the order the pages give
+ * it (Open-1B: A Fully Auditable Training Run, arXiv 2609.17380):
+ *   - §2.1 "Reproducible Operations" and Table 1: one fixed reduction order,
+ *     no fused multiply-add, subnormals flushed to zero on input and output.
+ *   - §3.1 "int8 quantization-aware training" and §4.2 "Implementation
+ *     notes": per-channel weight step size 2*mean(|w|)/sqrt(q_max),
+ *     recomputed every step.
+ *   - §3.2 "int8 computation": W8A8 with per-channel weight and per-tensor
+ *     activation scales, int32 accumulation then dequantisation, both STE
+ *     gradient GEMMs in int8, Walsh-Hadamard rotation along the contraction
+ *     dimension before the weight-gradient quantisation.
+ *   - §3.1 "RMSNorm", "Weights are initialized..." paragraph: normalisation
+ *     in FP32, parameters BF16, FP32 gradient reduction.
+ *   - §3.2 "Optimizer": global l2 gradient norm.
+ *   - App. A.3: every average is a multiply by a precomputed reciprocal.
+ *   - §5 "Runtime overhead" / App. B: a canonical state hash per step.
+ *
+ * Arithmetic model: each floating-point operation is one IEEE-754 binary32
+ * operation in round-to-nearest-even (gcc, -ffp-contract=off, SSE2, default
+ * MXCSR).  A value loaded from memory whose exponent field is zero becomes
+ * a zero of the same sign (DAZ); a result that is subnormal becomes a zero
+ * of the same sign (FTZ).  Both flushes are explicit in the code.
+ *
+ * Parity pins (all in tests/, none re-types a formula of this file):
+ *   tree sum ........ hand-computed order-sensitive vectors, closed forms on
+ *                     powers of two, a second independent (recursive) coding
+ *   quantiser ....... quantise(dequant(q)) == q, RNE ties, clamps, fp64
+ *                     single-rounding evaluation
+ *   int8 GEMMs ...... brute-force int64 dot products (numpy), fp64 dots
+ *   int WHT ......... H*H^T = b*I, H(Hv) = b*v, butterfly vs definition
+ *   fp WHT .......... integer-valued inputs equal the integer transform
+ *   dW .............. (H qx)^T (H qv) = b * qx^T qv exactly
+ *   RMSNorm ......... +-1 rows give closed-form rstd; fp64 bounds
+ *   grad-norm ....... 2^k leaves of 2^-j give exact closed forms
+ *   SHA-256 ......... Python hashlib (FIPS 180-4), independent Python Merkle
+ * The butterfly stage order of the fp WHT and the RMSNorm backward operation
+ * order are definitions that no external value fixes: parity unpinned beyond
+ * the bounds and special cases above.
+ */
+#ifndef BRQ_ORACLE_H
+#define BRQ_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_I32 = 3, ORC_U8 = 4 };
+enum { ORC_PER_TENSOR = 0, ORC_PER_ROW = 1 };
+enum { ORC_FLAG_NONFINITE = 1 };
+
+/* ---- arithmetic model helpers, exported so the pins can probe them ---- */
+float orc_flush(float v);                 /* subnormal -> signed zero */
+float orc_bf16_to_f32(uint16_t h);        /* exact widen, then DAZ */
+uint16_t orc_f32_to_bf16(float f);        /* RNE on the bit pattern */
+float orc_lsq_k2(void);                   /* 2 * fl(1/fl(sqrt(127))) */
+
+/* Canonical pairwise tree over leaves[0..n): node(j+1,i) = node(j,2i) +
+ * node(j,2i+1) when the right child exists, else node(j,2i).  Two codings. */
+float orc_tree_sum(const float* leaves, int64_t n);
+float orc_tree_sum_recursive(const float* leaves, int64_t n);
+
+/* LSQ scale from the tree sum S of |x| over n leaves: s = (S*(1/n))*K2,
+ * r = 1/s (0 when s == 0). */
+void orc_lsq_scale(float S, int64_t n, float* s, float* r);
+/* q = clamp(rint(x*r), -127, 127) */
+int8_t orc_quant1(float x, float r);
+
+/* quantize_lsq: x [rows][cols] (F32 or BF16), optional col_mul[cols]
+ * multiplied into every element first.  PER_TENSOR writes scale[0],
+ * amax[0]; PER_ROW writes scale[rows], amax[rows].  q [rows][cols];
+ * q_t [cols][rows] when non-NULL.  Returns flags. */
+int orc_quantize_lsq(const void* x, int dtype, int64_t rows, int64_t cols,
+                     int gran, const float* col_mul, int8_t* q, int8_t* q_t,
+                     float* scale, float* amax);
+
+/* qgemm_fwd: y[m][n] = fl(fl(sum_k qx[m][k]*qw[n][k]) * fl(s_x*s_w[n]))
+ * (s_w[0] for every n when w_per_row == 0). */
+void orc_qgemm_fwd(const int8_t* qx, const float* s_x, const int8_t* qw,
+                   const float* s_w, int w_per_row, int64_t M, int64_t N,
+                   int64_t K, float* y);
+
+/* qgemm_bwd_dx: dx[m][k] = fl(fl(sum_n qg[m][n]*qw[n][k]) * s_g);
+ * qw is the [N][K] weight code (the definition), not a transposed copy. */
+void orc_qgemm_bwd_dx(const int8_t* qg, const float* s_g, const int8_t* qw,
+                      int64_t M, int64_t N, int64_t K, float* dx);
+
+/* Integer Walsh-Hadamard transform of qx [M][K] along tokens: u [M][K]. */
+void orc_wht_int(const int8_t* qx, int64_t M, int64_t K, int b, int32_t* u);
+
+/* Integer Walsh-Hadamard of qx [M][K] along tokens in aligned blocks of b
+ * (Sylvester, natural order, unnormalised), exact; S_u = sum |u| (int64);
+ * s_u, r_u from S_u; q_u [M][K]. */
+void orc_wht_int_quant(const int8_t* qx, int64_t M, int64_t K, int b,
+                       int8_t* q_u, float* s_u, int64_t* S_u_out);
+
+/* fp32 Walsh-Hadamard of dy [M][N] (F32 or BF16) along tokens in aligned
+ * blocks of b: butterflies in stage order h = 1, 2, ..., b/2, then
+ * per-tensor LSQ over the rotated values in row-major order.  v_out
+ * (optional, [M][N]) receives the rotated values.  Returns flags. */
+int orc_wht_fp_quant(const void* dy, int dtype, int64_t M, int64_t N, int b,
+                     int8_t* q_v, float* s_v, float* v_out);
+
+/* dW rows [n_lo, n_hi): dw[n][k] = fl(fl(sum_m qv[m][n]*qu[m][k]) * c_w),
+ * c_w = fl(fl(fl(s_x*s_u)*s_v) * 2^-log2(b)).  dw is the full [N][K]. */
+void orc_dw_gemm(const int8_t* q_v, const int8_t* q_u, int64_t M, int64_t N,
+                 int64_t K, float s_x, float s_u, float s_v, int b,
+                 int64_t n_lo, int64_t n_hi, float* dw);
+
+/* The whole qgemm_bwd_dw_wht step: rotate+quantise qx and dy, dW GEMM. */
+int orc_qgemm_bwd_dw_wht(const int8_t* qx, const float* s_x, const void* dy,
+                         int dtype, int64_t M, int64_t N, int64_t K, int b,
+                         float* dw, float* s_u_out, float* s_v_out);
+
+/* RMSNorm forward per row: ss = tree(x*x), ms = ss*(1/D),
+ * rstd = 1/sqrt(ms+eps), y = (x*rstd)*g.  x, g, y in `dtype`. */
+int orc_rmsnorm_fwd(const void* x, const void* g, int dtype, int64_t T,
+                    int64_t D, float eps, void* y, float* rstd);
+
+/* RMSNorm backward: dx (dtype), dg [D] fp32 (tree over tokens). */
+void orc_rmsnorm_bwd(const void* x, const void* g, const float* rstd,
+                     const void* dy, int dtype, int64_t T, int64_t D,
+                     void* dx, float* dg);
+
+/* Global grad-norm: ss = tree(v*v), norm = sqrt(ss). */
+int orc_grad_norm(const float* v, int64_t n, float* sumsq, float* norm);
+
+/* SHA-256 (FIPS 180-4). */
+void orc_sha256(const uint8_t* msg, uint64_t len, uint8_t out[32]);
+
+/* Merkle root of a byte buffer: 4096-byte leaves, fan-in 128. */
+void orc_merkle_root(const uint8_t* bytes, uint64_t nbytes, uint8_t out[32]);
+
+/* Tensor digest: SHA-256("BRQ1" | dtype u8 | ndim u8 | dims u64le... |
+ * name_len u16le | name | merkle root). */
+void orc_tensor_digest(const uint8_t* bytes, uint64_t nbytes, int dtype,
+                       int ndim, const int64_t* dims, const char* name,
+                       uint8_t out[32]);
+
+/* State digest: SHA-256 of the concatenated tensor digests, in call order.
+ * ptrs[i] points at tensor i's bytes; dims is concatenated. */
+void orc_hash_state(int n, const uint8_t* const* ptrs, const uint64_t* nbytes,
+                    const int* dtypes, const int* ndims, const int64_t* dims,
+                    const char* const* names, uint8_t out[32]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,60 @@
+"""Planted mistakes in a copy of the oracle must fail the pins.
+
+Each mutant edits one line of oracle.c (a dropped term, a wrong sign, a
+transposed operand, a wrong rounding or constant), builds it into a
+temporary library, and runs tests/test_oracle_pins.py against it in a child
+process.  The pins pass on the real oracle and must fail on every mutant.
+All of this runs on the CPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "tree_tail_pairs_from_right": (
+        "buf[half] = buf[len - 1];", "buf[half] = fadd(buf[len - 1], -0.0f);\n      for (int64_t i = half; i > 0; i--) buf[i] = buf[i - 1]; buf[0] = buf[0];"),
+    "tree_sequential": (
+        "for (int64_t i = 0; i < half; i++) buf[i] = fadd(buf[2 * i], buf[2 * i + 1]);",
+        "for (int64_t i = 1; i < len; i++) buf[0] = fadd(buf[0], buf[i]); len = 1; half = 0; continue;"),
+    "quant_truncates": ("float t = rintf(fmul(x, r));", "float t = truncf(fmul(x, r));"),
+    "quant_clamp_128": ("if (t < -127.0f) t = -127.0f;", "if (t < -128.0f) t = -128.0f;"),
+    "k2_drops_factor_two": ("return fmul(2.0f, rs);", "return rs;"),
+    "mean_divides": ("float m = fmul(S, inv_count(n));", "float m = fdiv(S, (float)n);"),
+    "no_daz_on_load": ("return orc_flush(((const float*)p)[i]);", "return ((const float*)p)[i];"),
+    "dx_transposed_weight": ("acc[k] += g * (int64_t)qw[n * K + k];", "acc[k] += g * (int64_t)qw[(k * N + n) % (N * K)];"),
+    "fwd_scale_ignores_sx": ("float c = fmul(sx, orc_flush(w_per_row ? s_w[n] : s_w[0]));",
+                             "float c = orc_flush(w_per_row ? s_w[n] : s_w[0]);"),
+    "hadamard_or_not_and": ("__builtin_popcount((unsigned)(i & j))", "__builtin_popcount((unsigned)(i | j))"),
+    "fp_wht_sign": ("*d = fsub(x0, x1);", "*d = fsub(x1, x0);"),
+    "dw_missing_inv_b": ("orc_flush(s_v)), inv_b);", "orc_flush(s_v)), 1.0f);"),
+    "rmsnorm_no_eps": ("float r = fdiv(1.0f, fsqrt(fadd(ms, e)));", "float r = fdiv(1.0f, fsqrt(ms));"),
+    "rmsnorm_bwd_sign": ("fmul(r, fsub(d[j], fmul(xh[j], mu)))", "fmul(r, fadd(d[j], fmul(xh[j], mu)))"),
+    "gradnorm_abs_not_square": ("sq[i] = fmul(e, e);", "sq[i] = fabs_(e);"),
+    "sha_wrong_rotate": ("uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);",
+                         "uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 24);"),
+    "merkle_fanin_64": ("const uint64_t LEAF = 4096, FAN = 128;", "const uint64_t LEAF = 4096, FAN = 64;"),
+    "bf16_round_truncates": ("u += 0x7fffu + ((u >> 16) & 1u);", "u += 0;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_pins(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, name
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                    "-shared", "-I", os.path.join(ROOT, "oracle"), str(mut), "-o", str(lib), "-lm"],
+                   check=True)
+    env = dict(os.environ, BRQ_ORACLE_LIB=str(lib), OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
