@@ -1,0 +1,354 @@
+"""Python binding of libbrq (argument marshalling only).
+
+Every step of the path runs in libbrq's HIP kernels; this module checks
+tensors, allocates outputs and workspaces with torch (device memory and
+streams are all torch is used for), and calls the C ABI declared in
+include/brq.h on torch's current stream.  There is no fallback: if the
+shared library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbrq.so")
+
+F32, BF16, I8, I32, U8 = 0, 1, 2, 3, 4
+PER_TENSOR, PER_ROW = 0, 1
+FLAG_NONFINITE = 1
+OP_QUANTIZE, OP_QGEMM, OP_DW_WHT, OP_RMSNORM_BWD, OP_GRAD_NORM = 1, 2, 3, 4, 5
+MAX_CONTRACTION = 133144
+
+SYMBOLS = [
+    "brq_workspace_size", "brq_quantize_lsq", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
+    "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
+    "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm",
+    "brq_hash_workspace_size", "brq_hash_state", "brq_status_string",
+    "brq_last_hip_error", "brq_spec_version",
+]
+
+
+class BrqError(RuntimeError):
+    pass
+
+
+class Tune(C.Structure):
+    _fields_ = [("gemm_kernel", C.c_int), ("split_k", C.c_int), ("chunk_log2", C.c_int),
+                ("rows_per_block", C.c_int)]
+
+
+class TensorRef(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("dtype", C.c_int), ("ndim", C.c_int),
+                ("dims", C.c_int64 * 8), ("name", C.c_char_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise BrqError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        vp, i64, i32, sz, f32 = C.c_void_p, C.c_int64, C.c_int, C.c_size_t, C.c_float
+        L.brq_workspace_size.restype = sz
+        L.brq_workspace_size.argtypes = [i32, i64, i64, i64, i32, vp]
+        L.brq_quantize_lsq.restype = i32
+        L.brq_quantize_lsq.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.brq_qgemm_fwd.restype = i32
+        L.brq_qgemm_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, sz, vp, vp]
+        L.brq_qgemm_bwd_dx.restype = i32
+        L.brq_qgemm_bwd_dx.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, sz, vp, vp]
+        L.brq_qgemm_bwd_dw_wht.restype = i32
+        L.brq_qgemm_bwd_dw_wht.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp, vp, vp,
+                                           sz, vp, vp, vp]
+        L.brq_wht_quant_x.restype = i32
+        L.brq_wht_quant_x.argtypes = [vp, i64, i64, i32, vp, vp, vp, sz, vp, vp]
+        L.brq_wht_quant_dy.restype = i32
+        L.brq_wht_quant_dy.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, sz, vp, vp, vp]
+        L.brq_qgemm_dw.restype = i32
+        L.brq_qgemm_dw.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, sz, vp, vp]
+        L.brq_rmsnorm_fixed_fwd.restype = i32
+        L.brq_rmsnorm_fixed_fwd.argtypes = [vp, vp, i32, i64, i64, f32, vp, vp, vp, vp, vp]
+        L.brq_rmsnorm_fixed_bwd.restype = i32
+        L.brq_rmsnorm_fixed_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, vp, vp, vp, sz, vp, vp]
+        L.brq_grad_norm.restype = i32
+        L.brq_grad_norm.argtypes = [vp, i64, vp, vp, vp, sz, vp, vp, vp]
+        L.brq_hash_workspace_size.restype = sz
+        L.brq_hash_workspace_size.argtypes = [vp, i32]
+        L.brq_hash_state.restype = i32
+        L.brq_hash_state.argtypes = [vp, i32, vp, vp, sz, vp]
+        L.brq_status_string.restype = C.c_char_p
+        L.brq_status_string.argtypes = [i32]
+        L.brq_last_hip_error.restype = i32
+        L.brq_last_hip_error.argtypes = []
+        L.brq_spec_version.restype = i32
+        L.brq_spec_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().brq_status_string(status).decode()
+        extra = f" (hipError {lib().brq_last_hip_error()})" if status == -8 else ""
+        raise BrqError(f"{what}: {msg}{extra}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _tune(t):
+    if t is None:
+        return None
+    if isinstance(t, Tune):
+        return C.byref(t)
+    return C.byref(Tune(**t))
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise BrqError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise BrqError(f"{name} must be contiguous")
+
+
+def _fp_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise BrqError(f"unsupported dtype {t.dtype}")
+
+
+_HASH_CODES = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.int32: I32,
+               torch.uint8: U8}
+
+
+class Workspace:
+    """A growable device byte buffer (one per device), reused across calls
+    issued on the same stream."""
+
+    def __init__(self):
+        self.buf = {}
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        key = torch.device(device)
+        b = self.buf.get(key)
+        if b is None or b.numel() < nbytes:
+            b = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=key)
+            self.buf[key] = b
+        return b
+
+
+_WS = Workspace()
+
+
+def workspace_size(op: int, a: int, b: int = 0, c: int = 0, block: int = 0, tune=None) -> int:
+    return int(lib().brq_workspace_size(op, a, b, c, block, _tune(tune)))
+
+
+def _ws(nbytes, device, ws):
+    if ws is not None:
+        if ws.numel() < nbytes:
+            raise BrqError(f"workspace too small: {ws.numel()} < {nbytes}")
+        return ws
+    return _WS.get(nbytes, device)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def quantize_lsq(x, per_row=False, col_mul=None, want_t=False, tune=None, ws=None, flags=None):
+    """LSQ int8 quantisation.  Returns (q, q_t or None, scale, amax)."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    q_t = torch.empty((cols, rows), dtype=torch.int8, device=x.device) if want_t else None
+    ns = rows if per_row else 1
+    scale = torch.empty(ns, dtype=torch.float32, device=x.device)
+    amax = torch.empty(ns, dtype=torch.float32, device=x.device)
+    if col_mul is not None:
+        _dev(col_mul, "col_mul")
+    need = workspace_size(OP_QUANTIZE, rows, cols, tune=tune)
+    w = _ws(need, x.device, ws)
+    _check(lib().brq_quantize_lsq(_ptr(x), _fp_code(x), rows, cols, PER_ROW if per_row else PER_TENSOR,
+                                  _ptr(col_mul), _ptr(q), _ptr(q_t), _ptr(scale), _ptr(amax),
+                                  _ptr(w), w.numel(), _ptr(flags), _tune(tune), _stream()),
+           "quantize_lsq")
+    return q, q_t, scale, amax
+
+
+def qgemm_fwd(q_x, s_x, q_w, s_w, tune=None, out=None, ws=None):
+    _dev(q_x, "q_x"); _dev(q_w, "q_w")
+    M, K = q_x.shape
+    N = q_w.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=q_x.device)
+    need = workspace_size(OP_QGEMM, M, N, K, tune=tune)
+    w = _ws(need, q_x.device, ws) if need else None
+    _check(lib().brq_qgemm_fwd(_ptr(q_x), _ptr(s_x), _ptr(q_w), _ptr(s_w), int(s_w.numel() > 1),
+                               M, N, K, _ptr(y), _ptr(w), 0 if w is None else w.numel(),
+                               _tune(tune), _stream()), "qgemm_fwd")
+    return y
+
+
+def qgemm_bwd_dx(q_g, s_g, q_wt, tune=None, out=None, ws=None):
+    _dev(q_g, "q_g"); _dev(q_wt, "q_wt")
+    M, N = q_g.shape
+    K = q_wt.shape[0]
+    dx = out if out is not None else torch.empty((M, K), dtype=torch.float32, device=q_g.device)
+    need = workspace_size(OP_QGEMM, M, K, N, tune=tune)
+    w = _ws(need, q_g.device, ws) if need else None
+    _check(lib().brq_qgemm_bwd_dx(_ptr(q_g), _ptr(s_g), _ptr(q_wt), M, N, K, _ptr(dx), _ptr(w),
+                                  0 if w is None else w.numel(), _tune(tune), _stream()),
+           "qgemm_bwd_dx")
+    return dx
+
+
+def qgemm_bwd_dw_wht(q_x, s_x, dy, block, tune=None, out=None, ws=None, flags=None,
+                     return_codes=False):
+    """Returns (dw, s_u, s_v) and, with return_codes, also (q_ut, q_vt): the
+    rotated codes the call left at the start of its workspace."""
+    _dev(q_x, "q_x"); _dev(dy, "dy")
+    M, K = q_x.shape
+    N = dy.shape[1]
+    dw = out if out is not None else torch.empty((N, K), dtype=torch.float32, device=q_x.device)
+    s_u = torch.empty(1, dtype=torch.float32, device=q_x.device)
+    s_v = torch.empty(1, dtype=torch.float32, device=q_x.device)
+    need = workspace_size(OP_DW_WHT, M, N, K, block, tune=tune)
+    w = _ws(need, q_x.device, ws)
+    _check(lib().brq_qgemm_bwd_dw_wht(_ptr(q_x), _ptr(s_x), _ptr(dy), _fp_code(dy), M, N, K, block,
+                                      _ptr(dw), _ptr(s_u), _ptr(s_v), _ptr(w), w.numel(),
+                                      _ptr(flags), _tune(tune), _stream()), "qgemm_bwd_dw_wht")
+    if not return_codes:
+        return dw, s_u, s_v
+    off = (K * M + 255) // 256 * 256
+    q_ut = w[:K * M].view(torch.int8).view(K, M).clone()
+    q_vt = w[off:off + N * M].view(torch.int8).view(N, M).clone()
+    return dw, s_u, s_v, q_ut, q_vt
+
+
+def wht_quant_x(q_x, block, tune=None, ws=None):
+    _dev(q_x, "q_x")
+    M, K = q_x.shape
+    q_ut = torch.empty((K, M), dtype=torch.int8, device=q_x.device)
+    s_u = torch.empty(1, dtype=torch.float32, device=q_x.device)
+    need = workspace_size(OP_DW_WHT, M, 64, K, block, tune=tune)
+    w = _ws(need, q_x.device, ws)
+    _check(lib().brq_wht_quant_x(_ptr(q_x), M, K, block, _ptr(q_ut), _ptr(s_u), _ptr(w), w.numel(),
+                                 _tune(tune), _stream()), "wht_quant_x")
+    return q_ut, s_u
+
+
+def wht_quant_dy(dy, block, tune=None, ws=None, flags=None):
+    _dev(dy, "dy")
+    M, N = dy.shape
+    q_vt = torch.empty((N, M), dtype=torch.int8, device=dy.device)
+    s_v = torch.empty(1, dtype=torch.float32, device=dy.device)
+    need = workspace_size(OP_DW_WHT, M, N, 64, block, tune=tune)
+    w = _ws(need, dy.device, ws)
+    _check(lib().brq_wht_quant_dy(_ptr(dy), _fp_code(dy), M, N, block, _ptr(q_vt), _ptr(s_v),
+                                  _ptr(w), w.numel(), _ptr(flags), _tune(tune), _stream()),
+           "wht_quant_dy")
+    return q_vt, s_v
+
+
+def qgemm_dw(q_vt, q_ut, s_x, s_u, s_v, block, tune=None, out=None, ws=None):
+    _dev(q_vt, "q_vt"); _dev(q_ut, "q_ut")
+    N, M = q_vt.shape
+    K = q_ut.shape[0]
+    dw = out if out is not None else torch.empty((N, K), dtype=torch.float32, device=q_vt.device)
+    need = workspace_size(OP_QGEMM, N, K, M, tune=tune)
+    w = _ws(need, q_vt.device, ws) if need else None
+    _check(lib().brq_qgemm_dw(_ptr(q_vt), _ptr(q_ut), _ptr(s_x), _ptr(s_u), _ptr(s_v), M, N, K,
+                              block, _ptr(dw), _ptr(w), 0 if w is None else w.numel(),
+                              _tune(tune), _stream()), "qgemm_dw")
+    return dw
+
+
+def rmsnorm_fixed_fwd(x, g, eps=1e-6, flags=None, tune=None):
+    _dev(x, "x"); _dev(g, "g")
+    T, D = x.shape
+    y = torch.empty_like(x)
+    rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check(lib().brq_rmsnorm_fixed_fwd(_ptr(x), _ptr(g), _fp_code(x), T, D, eps, _ptr(y),
+                                       _ptr(rstd), _ptr(flags), _tune(tune), _stream()),
+           "rmsnorm_fixed_fwd")
+    return y, rstd
+
+
+def rmsnorm_fixed_bwd(x, g, rstd, dy, tune=None, ws=None):
+    _dev(x, "x"); _dev(g, "g"); _dev(rstd, "rstd"); _dev(dy, "dy")
+    T, D = x.shape
+    dx = torch.empty_like(x)
+    dg = torch.empty(D, dtype=torch.float32, device=x.device)
+    need = workspace_size(OP_RMSNORM_BWD, T, D, tune=tune)
+    w = _ws(need, x.device, ws)
+    _check(lib().brq_rmsnorm_fixed_bwd(_ptr(x), _ptr(g), _ptr(rstd), _ptr(dy), _fp_code(x), T, D,
+                                       _ptr(dx), _ptr(dg), _ptr(w), w.numel(), _tune(tune),
+                                       _stream()), "rmsnorm_fixed_bwd")
+    return dx, dg
+
+
+def grad_norm(v, flags=None, tune=None, ws=None, out=None):
+    _dev(v, "v")
+    if v.dtype != torch.float32:
+        raise BrqError("grad_norm takes fp32 gradients")
+    n = v.numel()
+    res = out if out is not None else torch.empty(2, dtype=torch.float32, device=v.device)
+    need = workspace_size(OP_GRAD_NORM, n, tune=tune)
+    w = _ws(need, v.device, ws)
+    _check(lib().brq_grad_norm(_ptr(v), n, res.data_ptr(), res.data_ptr() + 4, _ptr(w), w.numel(),
+                               _ptr(flags), _tune(tune), _stream()), "grad_norm")
+    return res[0], res[1]
+
+
+def _refs(tensors):
+    refs = (TensorRef * max(len(tensors), 1))()
+    names = []
+    for i, t in enumerate(tensors):
+        name, a = t[0], t[1]
+        _dev(a, name)
+        code = t[2] if len(t) > 2 else _HASH_CODES[a.dtype]
+        if a.dim() > 8:
+            raise BrqError("at most 8 dims")
+        nb = name.encode()
+        names.append(nb)
+        refs[i].data = a.data_ptr() if a.numel() else None
+        refs[i].dtype = code
+        refs[i].ndim = a.dim()
+        for d in range(a.dim()):
+            refs[i].dims[d] = a.shape[d]
+        refs[i].name = nb
+    return refs, names
+
+
+def hash_state_workspace_size(tensors) -> int:
+    refs, _ = _refs(tensors)
+    return int(lib().brq_hash_workspace_size(refs, len(tensors)))
+
+
+def hash_state(tensors, ws=None, out=None):
+    """tensors: list of (name, device tensor[, dtype code]).  Returns the
+    32-byte state digest as a device uint8 tensor."""
+    refs, _keep = _refs(tensors)
+    dev = tensors[0][1].device if tensors else torch.device("cuda")
+    need = int(lib().brq_hash_workspace_size(refs, len(tensors)))
+    w = _ws(need, dev, ws)
+    digest = out if out is not None else torch.empty(32, dtype=torch.uint8, device=dev)
+    _check(lib().brq_hash_state(refs, len(tensors), _ptr(digest), _ptr(w), w.numel(), _stream()),
+           "hash_state")
+    return digest

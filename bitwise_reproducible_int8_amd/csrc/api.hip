@@ -1,0 +1,288 @@
+// api.hip -- the extern "C" entry points of libbrq (declared in
+// include/brq.h): argument checks on the host, workspace carving, and the
+// kernel launches on the caller's stream.  No device memory is allocated
+// here; nothing synchronises.
+#include <string.h>
+
+#include "internal.hpp"
+
+using namespace brq;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return BRQ_OK;
+  g_last_hip = (int)e;
+  return BRQ_E_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool fp_dtype(int d) { return d == BRQ_F32 || d == BRQ_BF16; }
+int vec_elems(int d) { return d == BRQ_BF16 ? 8 : 4; }
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+// Fixed scratch block at the end of several workspaces: sum, max, s, r.
+constexpr size_t kScalars = 256;
+
+size_t quant_ws(int64_t rows, int64_t cols, const brq_tune* t) {
+  return flat_reduce_ws(rows * cols, flat_chunk_log2(t)) + kScalars;
+}
+
+size_t dw_stage_ws(int64_t M, int64_t N, int64_t K, int block, const brq_tune* t) {
+  size_t a = wht_x_ws(M, K, block), b = wht_dy_ws(M, N, block, flat_chunk_log2(t));
+  return a > b ? a : b;
+}
+
+size_t dw_ws(int64_t M, int64_t N, int64_t K, int block, const brq_tune* t) {
+  return align256((size_t)(K * M)) + align256((size_t)(N * M)) + kScalars +
+         dw_stage_ws(M, N, K, block, t) + gemm_ws(N, K, M, t);
+}
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int check_dw_shape(int64_t M, int64_t N, int64_t K, int block) {
+  if (M < 0 || N < 0 || K < 0) return BRQ_E_SHAPE;
+  if (!pow2(block) || block > 128) return BRQ_E_UNSUPPORTED;
+  if (M % block || M % 64 || K % 64 || N % 64) return BRQ_E_UNSUPPORTED;
+  if (M > BRQ_MAX_CONTRACTION) return BRQ_E_RANGE;
+  return BRQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int brq_spec_version(void) { return BRQ_SPEC_VERSION; }
+int brq_last_hip_error(void) { return g_last_hip; }
+
+const char* brq_status_string(int s) {
+  switch (s) {
+    case BRQ_OK: return "ok";
+    case BRQ_E_NULL: return "required pointer is NULL";
+    case BRQ_E_DTYPE: return "unsupported dtype";
+    case BRQ_E_SHAPE: return "invalid shape";
+    case BRQ_E_ALIGN: return "pointer not 16-byte aligned";
+    case BRQ_E_UNSUPPORTED: return "shape outside the supported set";
+    case BRQ_E_RANGE: return "contraction too long for exact int32 accumulation";
+    case BRQ_E_WORKSPACE: return "workspace missing or too small";
+    case BRQ_E_HIP: return "HIP launch error";
+    case BRQ_E_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block, const brq_tune* t) {
+  if (a < 0 || b < 0 || c < 0) return 0;
+  switch (op) {
+    case BRQ_OP_QUANTIZE: return quant_ws(a, b, t);
+    case BRQ_OP_QGEMM: return gemm_ws(a, b, c, t);
+    case BRQ_OP_DW_WHT: return dw_ws(a, b, c, block > 0 ? block : 1, t);
+    case BRQ_OP_RMSNORM_BWD: {
+      size_t x = rmsnorm_bwd_ws(a, b, BRQ_BF16, t), y = rmsnorm_bwd_ws(a, b, BRQ_F32, t);
+      return x > y ? x : y;
+    }
+    case BRQ_OP_GRAD_NORM: return kScalars + flat_reduce_ws(a, flat_chunk_log2(t));
+    default: return 0;
+  }
+}
+
+int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                     const float* col_mul, int8_t* q, int8_t* q_t, float* scale, float* amax,
+                     void* ws, size_t ws_bytes, int32_t* dflags, const brq_tune* tune,
+                     void* stream) {
+  if (!fp_dtype(x_dtype)) return BRQ_E_DTYPE;
+  if (rows < 0 || cols < 0) return BRQ_E_SHAPE;
+  if (gran != BRQ_PER_TENSOR && gran != BRQ_PER_ROW) return BRQ_E_ARG;
+  const int64_t n = rows * cols;
+  if (!scale || (n > 0 && (!x || !q))) return BRQ_E_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(q_t) || !aligned16(col_mul)) return BRQ_E_ALIGN;
+  if (cols % vec_elems(x_dtype)) return BRQ_E_UNSUPPORTED;
+  if (q_t && (rows % 16 || cols % 16)) return BRQ_E_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  hipError_t e;
+  if (gran == BRQ_PER_ROW) {
+    if (col_mul) return BRQ_E_UNSUPPORTED;
+    if (cols > 16384 || cols == 0) return BRQ_E_UNSUPPORTED;
+    if (rows == 0) return BRQ_OK;
+    if ((e = quant_rows(x, x_dtype, rows, cols, q, scale, amax, dflags, s)) != hipSuccess)
+      return hip_status(e);
+  } else {
+    const size_t need = quant_ws(rows, cols, tune);
+    if (!ws || ws_bytes < need) return BRQ_E_WORKSPACE;
+    float* sc = (float*)((char*)ws + need - kScalars);  // [0]sum [1]max [2]s [3]r
+    const int leaf = col_mul ? LEAF_ABS_COLMUL : LEAF_ABS;
+    if ((e = flat_reduce(x, x_dtype, leaf, col_mul, n, cols > 0 ? cols : 1, sc, ws,
+                         flat_chunk_log2(tune), dflags, s)) != hipSuccess)
+      return hip_status(e);
+    // an empty group has step size 0 (no mean is taken)
+    const float inv_n = n > 0 ? 1.0f / (float)n : 0.0f;
+    if ((e = lsq_finalize(sc, inv_n, sc + 2, scale, amax, s)) != hipSuccess) return hip_status(e);
+    if (n > 0 && (e = quant_flat(x, x_dtype, col_mul, n, cols, sc + 2, q, s)) != hipSuccess)
+      return hip_status(e);
+  }
+  if (q_t && n > 0 && (e = transpose_i8(q, rows, cols, q_t, s)) != hipSuccess) return hip_status(e);
+  return BRQ_OK;
+}
+
+static int gemm_common(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64_t Kc,
+                       float* C, const EpiArgs& epi, void* ws, size_t ws_bytes,
+                       const brq_tune* tune, void* stream) {
+  if (I < 0 || J < 0 || Kc < 0) return BRQ_E_SHAPE;
+  if (Kc % 16) return BRQ_E_UNSUPPORTED;
+  if (Kc > BRQ_MAX_CONTRACTION) return BRQ_E_RANGE;
+  if (I > 0 && J > 0 && (!C || (Kc > 0 && (!A || !B)))) return BRQ_E_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return BRQ_E_ALIGN;
+  if (ws_bytes < gemm_ws(I, J, Kc, tune) || (gemm_ws(I, J, Kc, tune) && !ws))
+    return BRQ_E_WORKSPACE;
+  return hip_status(gemm_i8(A, B, I, J, Kc, C, epi, ws, ws_bytes, tune, as_stream(stream)));
+}
+
+int brq_qgemm_fwd(const int8_t* q_x, const float* s_x, const int8_t* q_w, const float* s_w,
+                  int w_per_row, int64_t M, int64_t N, int64_t K, float* y, void* ws,
+                  size_t ws_bytes, const brq_tune* tune, void* stream) {
+  if (!s_x || !s_w) return BRQ_E_NULL;
+  EpiArgs epi{EPI_FWD, s_x, s_w, nullptr, w_per_row ? 1 : 0, 1.0f};
+  return gemm_common(q_x, q_w, M, N, K, y, epi, ws, ws_bytes, tune, stream);
+}
+
+int brq_qgemm_bwd_dx(const int8_t* q_g, const float* s_g, const int8_t* q_wt, int64_t M,
+                     int64_t N, int64_t K, float* dx, void* ws, size_t ws_bytes,
+                     const brq_tune* tune, void* stream) {
+  if (!s_g) return BRQ_E_NULL;
+  EpiArgs epi{EPI_SCALAR, s_g, nullptr, nullptr, 0, 1.0f};
+  return gemm_common(q_g, q_wt, M, K, N, dx, epi, ws, ws_bytes, tune, stream);
+}
+
+int brq_qgemm_dw(const int8_t* q_vt, const int8_t* q_ut, const float* s_x, const float* s_u,
+                 const float* s_v, int64_t M, int64_t N, int64_t K, int block, float* dw,
+                 void* ws, size_t ws_bytes, const brq_tune* tune, void* stream) {
+  if (!s_x || !s_u || !s_v) return BRQ_E_NULL;
+  if (!pow2(block) || block > 128) return BRQ_E_UNSUPPORTED;
+  int lb = 0;
+  while ((1 << lb) < block) ++lb;
+  EpiArgs epi{EPI_DW, s_x, s_u, s_v, 0, ldexpf(1.0f, -lb)};
+  return gemm_common(q_vt, q_ut, N, K, M, dw, epi, ws, ws_bytes, tune, stream);
+}
+
+int brq_wht_quant_x(const int8_t* q_x, int64_t M, int64_t K, int block, int8_t* q_ut, float* s_u,
+                    void* ws, size_t ws_bytes, const brq_tune* tune, void* stream) {
+  (void)tune;
+  int st = check_dw_shape(M, 64, K, block);
+  if (st != BRQ_OK) return st;
+  if (!s_u || (M * K > 0 && (!q_x || !q_ut))) return BRQ_E_NULL;
+  if (!aligned16(q_x) || !aligned16(q_ut)) return BRQ_E_ALIGN;
+  if (!ws || ws_bytes < wht_x_ws(M, K, block)) return BRQ_E_WORKSPACE;
+  return hip_status(wht_quant_x(q_x, M, K, block, q_ut, s_u, ws, as_stream(stream)));
+}
+
+int brq_wht_quant_dy(const void* dy, int dy_dtype, int64_t M, int64_t N, int block, int8_t* q_vt,
+                     float* s_v, void* ws, size_t ws_bytes, int32_t* dflags,
+                     const brq_tune* tune, void* stream) {
+  if (!fp_dtype(dy_dtype)) return BRQ_E_DTYPE;
+  int st = check_dw_shape(M, N, 64, block);
+  if (st != BRQ_OK) return st;
+  if (!s_v || (M * N > 0 && (!dy || !q_vt))) return BRQ_E_NULL;
+  if (!aligned16(dy) || !aligned16(q_vt)) return BRQ_E_ALIGN;
+  const int c = flat_chunk_log2(tune);
+  if (!ws || ws_bytes < wht_dy_ws(M, N, block, c)) return BRQ_E_WORKSPACE;
+  return hip_status(wht_quant_dy(dy, dy_dtype, M, N, block, q_vt, s_v, ws, c, dflags,
+                                 as_stream(stream)));
+}
+
+int brq_qgemm_bwd_dw_wht(const int8_t* q_x, const float* s_x, const void* dy, int dy_dtype,
+                         int64_t M, int64_t N, int64_t K, int block, float* dw, float* s_u_out,
+                         float* s_v_out, void* ws, size_t ws_bytes, int32_t* dflags,
+                         const brq_tune* tune, void* stream) {
+  if (!fp_dtype(dy_dtype)) return BRQ_E_DTYPE;
+  int st = check_dw_shape(M, N, K, block);
+  if (st != BRQ_OK) return st;
+  if (!s_x) return BRQ_E_NULL;
+  const size_t need = dw_ws(M, N, K, block, tune);
+  if (!ws || ws_bytes < need) return BRQ_E_WORKSPACE;
+  char* w = (char*)ws;
+  int8_t* q_ut = (int8_t*)w;
+  w += align256((size_t)(K * M));
+  int8_t* q_vt = (int8_t*)w;
+  w += align256((size_t)(N * M));
+  float* scal = (float*)w;
+  w += kScalars;
+  void* stage = w;
+  w += dw_stage_ws(M, N, K, block, tune);
+  void* gws = w;
+  float* s_u = s_u_out ? s_u_out : scal;
+  float* s_v = s_v_out ? s_v_out : scal + 1;
+  const size_t stage_bytes = dw_stage_ws(M, N, K, block, tune);
+  int r = brq_wht_quant_x(q_x, M, K, block, q_ut, s_u, stage, stage_bytes, tune, stream);
+  if (r != BRQ_OK) return r;
+  r = brq_wht_quant_dy(dy, dy_dtype, M, N, block, q_vt, s_v, stage, stage_bytes, dflags, tune,
+                       stream);
+  if (r != BRQ_OK) return r;
+  return brq_qgemm_dw(q_vt, q_ut, s_x, s_u, s_v, M, N, K, block, dw, gws, gemm_ws(N, K, M, tune),
+                      tune, stream);
+}
+
+int brq_rmsnorm_fixed_fwd(const void* x, const void* g, int dtype, int64_t T, int64_t D, float eps,
+                          void* y, float* rstd, int32_t* dflags, const brq_tune* tune,
+                          void* stream) {
+  (void)tune;
+  if (!fp_dtype(dtype)) return BRQ_E_DTYPE;
+  if (T < 0 || D <= 0) return BRQ_E_SHAPE;
+  if (D % 8 || D > 64 * vec_elems(dtype) * 32) return BRQ_E_UNSUPPORTED;
+  if (T > 0 && (!x || !g || !y || !rstd)) return BRQ_E_NULL;
+  if (!aligned16(x) || !aligned16(g) || !aligned16(y)) return BRQ_E_ALIGN;
+  if (T == 0) return BRQ_OK;
+  return hip_status(rmsnorm_fwd(x, g, dtype, T, D, eps, y, rstd, dflags, as_stream(stream)));
+}
+
+int brq_rmsnorm_fixed_bwd(const void* x, const void* g, const float* rstd, const void* dy,
+                          int dtype, int64_t T, int64_t D, void* dx, float* dg, void* ws,
+                          size_t ws_bytes, const brq_tune* tune, void* stream) {
+  if (!fp_dtype(dtype)) return BRQ_E_DTYPE;
+  if (T < 0 || D <= 0) return BRQ_E_SHAPE;
+  if (D % 8 || D > 256 * vec_elems(dtype) * 2) return BRQ_E_UNSUPPORTED;
+  if (!dg || (T > 0 && (!x || !g || !rstd || !dy || !dx))) return BRQ_E_NULL;
+  if (!aligned16(x) || !aligned16(g) || !aligned16(dy) || !aligned16(dx) || !aligned16(dg))
+    return BRQ_E_ALIGN;
+  if (!ws || ws_bytes < rmsnorm_bwd_ws(T, D, dtype, tune)) return BRQ_E_WORKSPACE;
+  return hip_status(rmsnorm_bwd(x, g, rstd, dy, dtype, T, D, dx, dg, ws, tune, as_stream(stream)));
+}
+
+int brq_grad_norm(const float* v, int64_t n, float* sumsq, float* norm, void* ws, size_t ws_bytes,
+                  int32_t* dflags, const brq_tune* tune, void* stream) {
+  if (n < 0) return BRQ_E_SHAPE;
+  if (!sumsq || !norm || (n > 0 && !v)) return BRQ_E_NULL;
+  if (!aligned16(v)) return BRQ_E_ALIGN;
+  const int c = flat_chunk_log2(tune);
+  if (!ws || ws_bytes < kScalars + flat_reduce_ws(n, c)) return BRQ_E_WORKSPACE;
+  return hip_status(grad_norm(v, n, sumsq, norm, ws, c, dflags, as_stream(stream)));
+}
+
+size_t brq_hash_workspace_size(const brq_tensor_ref* t, int n) {
+  if (n < 0 || (n > 0 && !t)) return 0;
+  return hash_ws(t, n);
+}
+
+int brq_hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* ws, size_t ws_bytes,
+                   void* stream) {
+  if (n < 0) return BRQ_E_SHAPE;
+  if (!digest32 || (n > 0 && !t)) return BRQ_E_NULL;
+  for (int i = 0; i < n; ++i) {
+    if (t[i].dtype < BRQ_F32 || t[i].dtype > BRQ_U8) return BRQ_E_DTYPE;
+    if (t[i].ndim < 0 || t[i].ndim > 8) return BRQ_E_SHAPE;
+    int64_t cnt = 1;
+    for (int d = 0; d < t[i].ndim; ++d) {
+      if (t[i].dims[d] < 0) return BRQ_E_SHAPE;
+      cnt *= t[i].dims[d];
+    }
+    if (cnt > 0 && !t[i].data) return BRQ_E_NULL;
+    if (!aligned16(t[i].data)) return BRQ_E_ALIGN;
+    if (t[i].name && strlen(t[i].name) > 255) return BRQ_E_ARG;
+  }
+  if (!aligned16(digest32)) return BRQ_E_ALIGN;
+  if (!ws || ws_bytes < hash_ws(t, n)) return BRQ_E_WORKSPACE;
+  return hip_status(hash_state(t, n, digest32, ws, as_stream(stream)));
+}
+
+}  // extern "C"

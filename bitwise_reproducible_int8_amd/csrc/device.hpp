@@ -1,0 +1,178 @@
+// device.hpp -- gfx950 device helpers for libbrq: the binary32 arithmetic
+// model, bf16 conversion, and the canonical pairwise tree on 64-lane waves.
+//
+// Arithmetic model (Open-1B report, §2.1 "Fused multiply-add",
+// "Subnormals" and Table 1): one IEEE binary32 operation per step, round to
+// nearest even, never contracted (the library is built with
+// -ffp-contract=off and this header repeats it as a pragma); fp32 denormals
+// are kept by the hardware (IEEE mode) and every result that lands in the
+// subnormal range is replaced by a zero of the same sign here, explicitly,
+// as is every subnormal value read from memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace brq {
+
+constexpr int kWave = 64;
+
+// ---- binary32 model ------------------------------------------------------
+__device__ __forceinline__ float flush(float v) {
+  uint32_t u = __float_as_uint(v);
+  return ((u & 0x7f800000u) == 0u) ? __uint_as_float(u & 0x80000000u) : v;
+}
+// A non-negative value: 0 or >= 2^-126 after the flush.
+__device__ __forceinline__ float flush_nonneg(float v) {
+  return (v < 1.17549435e-38f) ? 0.0f : v;
+}
+__device__ __forceinline__ float fadd(float a, float b) { return flush(a + b); }
+__device__ __forceinline__ float fsub(float a, float b) { return flush(a - b); }
+__device__ __forceinline__ float fmul(float a, float b) { return flush(a * b); }
+__device__ __forceinline__ float fabs_bits(float a) {
+  return __uint_as_float(__float_as_uint(a) & 0x7fffffffu);
+}
+
+// bf16 <-> fp32: widening is exact (then DAZ); narrowing rounds to nearest
+// even on the bit pattern (a NaN stays a quiet NaN).
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
+  return flush(__uint_as_float(h16 << 16));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// LSQ factor 2 * fl(1/fl(sqrt(127))) as binary32 bits 0x3e35bb0a:
+// fl(sqrt(127)) = 0x41344f93, its binary32 reciprocal 0x3db5bb0a, times 2.
+__device__ __forceinline__ float lsq_k2() { return __uint_as_float(0x3e35bb0au); }
+
+// q = clamp(rint(fl(v * r)), -127, 127); v_rndne_f32 rounds half to even.
+__device__ __forceinline__ int quant_code(float v, float r) {
+  float t = __builtin_rintf(fmul(v, r));
+  t = t > 127.0f ? 127.0f : t;
+  t = t < -127.0f ? -127.0f : t;
+  return (int)t;
+}
+
+// ---- wave-level canonical tree ---------------------------------------------
+// Lane l holds node(j, l) of some level j for 64 consecutive nodes.  After
+// the butterfly every lane holds node(j + 6, 0): at step s the partner lane
+// is l ^ s, and because binary32 addition is commutative bit for bit the
+// two partners compute the same value node(2i) + node(2i+1).
+// The first four steps use DPP (quad permutes, half-row and row mirrors,
+// valid because each group is uniform by then); the last two go through
+// ds_swizzle / bpermute.
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_half_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+}
+
+template <bool kSigned>
+__device__ __forceinline__ float tree_add(float a, float b) {
+  // Sums of values that are each +0 or >= 2^-126 never land in the
+  // subnormal range, so the flush is only needed when signs can differ.
+  return kSigned ? fadd(a, b) : (a + b);
+}
+
+template <bool kSigned>
+__device__ __forceinline__ float wave_tree(float v) {
+  v = tree_add<kSigned>(v, dpp_xor1(v));
+  v = tree_add<kSigned>(v, dpp_xor2(v));
+  v = tree_add<kSigned>(v, dpp_half_mirror(v));
+  v = tree_add<kSigned>(v, dpp_mirror(v));
+  v = tree_add<kSigned>(v, __shfl_xor(v, 16, kWave));
+  v = tree_add<kSigned>(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+
+// Tree over the first `w` lanes only (w a power of two <= 64): lanes in each
+// aligned group of w end up holding that group's node.
+template <bool kSigned>
+__device__ __forceinline__ float wave_tree_partial(float v, int w) {
+  if (w >= 2) v = tree_add<kSigned>(v, dpp_xor1(v));
+  if (w >= 4) v = tree_add<kSigned>(v, dpp_xor2(v));
+  if (w >= 8) v = tree_add<kSigned>(v, dpp_half_mirror(v));
+  if (w >= 16) v = tree_add<kSigned>(v, dpp_mirror(v));
+  if (w >= 32) v = tree_add<kSigned>(v, __shfl_xor(v, 16, kWave));
+  if (w >= 64) v = tree_add<kSigned>(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+
+// In-register tree over a[0..N), N a power of two; a is destroyed.
+template <bool kSigned, int N>
+__device__ __forceinline__ float reg_tree(float* a) {
+#pragma unroll
+  for (int w = N; w > 1; w >>= 1) {
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) a[i] = tree_add<kSigned>(a[2 * i], a[2 * i + 1]);
+  }
+  return a[0];
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_xor1(v));
+  v = fmaxf(v, dpp_xor2(v));
+  v = fmaxf(v, dpp_half_mirror(v));
+  v = fmaxf(v, dpp_mirror(v));
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+
+// ---- 16-byte vectors -------------------------------------------------------
+struct alignas(16) u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Unpack 16 bytes of bf16 (8 values) or fp32 (4 values) into floats (DAZ).
+__device__ __forceinline__ void unpack_bf16x8(u32x4 v, float* f) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+    f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+__device__ __forceinline__ void unpack_f32x4(u32x4 v, float* f) {
+  f[0] = flush(__uint_as_float(v.x));
+  f[1] = flush(__uint_as_float(v.y));
+  f[2] = flush(__uint_as_float(v.z));
+  f[3] = flush(__uint_as_float(v.w));
+}
+
+// Element type traits: values per 16-byte vector.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPerVec = 4;
+  __device__ static void unpack(u32x4 v, float* f) { unpack_f32x4(v, f); }
+  __device__ static float load1(const float* p, int64_t i) { return flush(p[i]); }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kPerVec = 8;
+  __device__ static void unpack(u32x4 v, float* f) { unpack_bf16x8(v, f); }
+  __device__ static float load1(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+};
+
+__device__ __forceinline__ void set_flag(int32_t* flags, int32_t bit) {
+  if (flags) atomicOr(flags, bit);
+}
+
+}  // namespace brq

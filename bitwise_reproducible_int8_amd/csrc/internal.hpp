@@ -1,0 +1,95 @@
+// internal.hpp -- launcher declarations shared by the libbrq translation
+// units (host side).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/brq.h"
+
+namespace brq {
+
+// Sizes of scratch regions, in bytes, rounded up to 256.
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Leaves per work-group of the flat tree reductions.
+int flat_chunk_log2(const brq_tune* t);
+
+// ---- canonical-tree reductions over a flat array -------------------------
+// Leaf kinds of the first pass.
+enum LeafKind { LEAF_ABS = 0, LEAF_ABS_COLMUL = 1, LEAF_SQUARE = 2, LEAF_RAW = 3 };
+
+// Workspace needed to reduce n leaves to one value (partials of every level
+// plus the small scalar block).
+size_t flat_reduce_ws(int64_t n, int chunk_log2);
+
+// Reduce n leaves of kind `leaf` (dtype of x) to the tree sum; writes the
+// sum and the max of |leaf| into out[0], out[1] (device), raising
+// BRQ_FLAG_NONFINITE when the sum is not finite.  Uses ws.
+hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul,
+                       int64_t n, int64_t cols, float* out2, void* ws,
+                       int chunk_log2, int32_t* dflags, hipStream_t s);
+
+// From a tree sum on device, compute the LSQ step size and reciprocal:
+// sr[0] = s, sr[1] = r.  Optionally copies s and the max into scale/amax.
+hipError_t lsq_finalize(const float* sum_max, float inv_n, float* sr,
+                        float* scale, float* amax, hipStream_t s);
+
+// Elementwise quantisation with the device reciprocal sr[1].
+hipError_t quant_flat(const void* x, int dtype, const float* col_mul, int64_t n,
+                      int64_t cols, const float* sr, int8_t* q, hipStream_t s);
+
+// Per-row quantisation (one wave per row).
+hipError_t quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
+                      int8_t* q, float* scale, float* amax, int32_t* dflags,
+                      hipStream_t s);
+
+// int8 transpose: q [rows][cols] -> qt [cols][rows].
+hipError_t transpose_i8(const int8_t* q, int64_t rows, int64_t cols, int8_t* qt,
+                        hipStream_t s);
+
+// ---- GEMMs ------------------------------------------------------------------
+enum EpiKind { EPI_FWD = 0, EPI_SCALAR = 1, EPI_DW = 2 };
+struct EpiArgs {
+  int kind;
+  const float* s0;   // fwd: s_x   scalar: s     dw: s_x
+  const float* s1;   // fwd: s_w   dw: s_u
+  const float* s2;   // dw: s_v
+  int per_row;       // fwd: s_w is per output column
+  float inv_b;       // dw: exact 2^-log2(block)
+};
+size_t gemm_ws(int64_t I, int64_t J, int64_t Kc, const brq_tune* t);
+// C[i][j] = epi(sum_k A[i][k] * B[j][k]); A [I][Kc], B [J][Kc], C [I][J].
+hipError_t gemm_i8(const int8_t* A, const int8_t* B, int64_t I, int64_t J,
+                   int64_t Kc, float* C, const EpiArgs& epi, void* ws,
+                   size_t ws_bytes, const brq_tune* t, hipStream_t s);
+
+// ---- Walsh-Hadamard rotations ----------------------------------------------
+size_t wht_x_ws(int64_t M, int64_t K, int block);
+size_t wht_dy_ws(int64_t M, int64_t N, int block, int chunk_log2);
+hipError_t wht_quant_x(const int8_t* q_x, int64_t M, int64_t K, int block,
+                       int8_t* q_ut, float* s_u, void* ws, hipStream_t s);
+hipError_t wht_quant_dy(const void* dy, int dtype, int64_t M, int64_t N,
+                        int block, int8_t* q_vt, float* s_v, void* ws,
+                        int chunk_log2, int32_t* dflags, hipStream_t s);
+
+// ---- RMSNorm / grad-norm ------------------------------------------------------
+hipError_t rmsnorm_fwd(const void* x, const void* g, int dtype, int64_t T,
+                       int64_t D, float eps, void* y, float* rstd,
+                       int32_t* dflags, hipStream_t s);
+int rmsnorm_bwd_rows(int64_t D, int dtype, const brq_tune* t);
+size_t rmsnorm_bwd_ws(int64_t T, int64_t D, int dtype, const brq_tune* t);
+hipError_t rmsnorm_bwd(const void* x, const void* g, const float* rstd,
+                       const void* dy, int dtype, int64_t T, int64_t D,
+                       void* dx, float* dg, void* ws, const brq_tune* t,
+                       hipStream_t s);
+hipError_t grad_norm(const float* v, int64_t n, float* sumsq, float* norm,
+                     void* ws, int chunk_log2, int32_t* dflags, hipStream_t s);
+
+// ---- hash ------------------------------------------------------------------------
+size_t hash_ws(const brq_tensor_ref* t, int n);
+hipError_t hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32,
+                      void* ws, hipStream_t s);
+
+}  // namespace brq

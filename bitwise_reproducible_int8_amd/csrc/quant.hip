@@ -1,0 +1,430 @@
+// quant.hip -- LSQ int8 quantisation on gfx950 (Open-1B report §3.1 "int8
+// quantization-aware training", §4.2 "Implementation notes", §3.2 "int8
+// computation"): step size s = 2*mean(|v|)/sqrt(127) recomputed from the
+// tensor, q = clamp(rint(v / s), -127, 127) with the divide done as a
+// multiply by fl(1/s) (App. A.3).
+//
+// Per-tensor groups take two passes over the input: the statistic (a
+// canonical-tree sum of |v| plus max|v|) and then the codes.  The tree is
+// cut into aligned power-of-two chunks, one per work-group: every chunk is a
+// complete subtree of the whole-tensor tree, so summing the chunk sums with
+// the same pairwise rule gives exactly the whole-tensor tree, whatever the
+// chunk size, wave size or grid size.  Lanes beyond the end contribute +0,
+// an exact identity for these non-negative leaves (it equals the "unpaired
+// node moves up" rule).
+//
+// Per-row groups (weights, one step size per output channel) fit in one
+// wave: one read, one write.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace brq {
+
+// --------------------------------------------------------------------------
+// flat tree, pass 1: one aligned chunk of C = 4 waves * 64 lanes * V vectors
+// * E elements per work-group.  Vector v of lane l covers elements
+// [wave_base + (64 v + l) E, + E): each wave-wide vector load is one
+// contiguous 64*16-byte run, and the 64 lanes' subtrees pair up through the
+// butterfly into node(log2(64E), .) of that run.
+// --------------------------------------------------------------------------
+template <typename T, int LEAF>
+__device__ __forceinline__ void leaves_of(const T* x, const float* cm, int64_t n,
+                                          int64_t cols, int64_t idx0, float* f) {
+  constexpr int E = Elem<T>::kPerVec;
+  if (idx0 + E <= n) {
+    Elem<T>::unpack(ld16(x + idx0), f);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = (idx0 + e < n) ? Elem<T>::load1(x, idx0 + e) : 0.0f;
+  }
+  if (LEAF == LEAF_ABS_COLMUL) {
+    int64_t col = idx0 % cols;  // cols % E == 0: the vector sits in one row
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = fmul(f[e], flush(cm[col + e]));
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (LEAF == LEAF_SQUARE) f[e] = flush_nonneg(f[e] * f[e]);
+    else if (LEAF != LEAF_RAW) f[e] = fabs_bits(f[e]);
+  }
+}
+
+template <typename T, int LEAF, int V>
+__global__ __launch_bounds__(256) void k_flat_leaves(const T* __restrict__ x,
+                                                     const float* __restrict__ cm,
+                                                     int64_t n, int64_t cols,
+                                                     float* __restrict__ psum,
+                                                     float* __restrict__ pmax) {
+  constexpr int E = Elem<T>::kPerVec;
+  constexpr int64_t WAVE_SPAN = int64_t(64) * E * V;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = (int64_t)blockIdx.x * 4 * WAVE_SPAN + wave * WAVE_SPAN;
+  float node[V];
+  float mx = 0.0f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float f[E];
+    leaves_of<T, LEAF>(x, cm, n, cols, base + (int64_t)(v * 64 + lane) * E, f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) mx = fmaxf(mx, f[e]);
+    node[v] = wave_tree<false>(reg_tree<false, E>(f));
+  }
+  float w = reg_tree<false, V>(node);
+  mx = wave_max(mx);
+  __shared__ float sw[4], sm[4];
+  if (lane == 0) { sw[wave] = w; sm[wave] = mx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    psum[blockIdx.x] = (sw[0] + sw[1]) + (sw[2] + sw[3]);
+    pmax[blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  }
+}
+
+// Final level: up to 32768 partials in one work-group of 1024 lanes, each
+// lane an aligned run of 32.  Writes out[0] = sum, out[1] = max.
+__global__ __launch_bounds__(1024) void k_flat_final(const float* __restrict__ psum,
+                                                     const float* __restrict__ pmax,
+                                                     int64_t P, float* out,
+                                                     int32_t* flags) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  float a[32];
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    int64_t j = (int64_t)t * 32 + i;
+    a[i] = j < P ? psum[j] : 0.0f;
+    mx = fmaxf(mx, j < P ? pmax[j] : 0.0f);
+  }
+  float w = wave_tree<false>(reg_tree<false, 32>(a));
+  mx = wave_max(mx);
+  __shared__ float sw[16], sm[16];
+  if (lane == 0) { sw[wave] = w; sm[wave] = mx; }
+  __syncthreads();
+  if (t == 0) {
+    float b[16], m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { b[i] = sw[i]; m = fmaxf(m, sm[i]); }
+    float s = reg_tree<false, 16>(b);
+    out[0] = s;
+    out[1] = m;
+    if (!__builtin_isfinite(s)) set_flag(flags, BRQ_FLAG_NONFINITE);
+  }
+}
+
+int flat_chunk_log2(const brq_tune* t) {
+  int c = (t && t->chunk_log2) ? t->chunk_log2 : 13;
+  return c < 10 ? 10 : (c > 16 ? 16 : c);
+}
+
+static int vectors_for(int chunk_log2, int E) {
+  int v = (int)((1ll << chunk_log2) / (256 * E));
+  return v < 1 ? 1 : (v > 16 ? 16 : v);
+}
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of partials after each pass; the last level holds <= 32768.
+static int levels_of(int64_t n, int64_t C0, int64_t C, int64_t* P, int maxlev) {
+  int L = 0;
+  P[L++] = cdiv(n > 0 ? n : 1, C0);
+  while (P[L - 1] > 32768 && L < maxlev) { P[L] = cdiv(P[L - 1], C); ++L; }
+  return L;
+}
+
+size_t flat_reduce_ws(int64_t n, int chunk_log2) {
+  int64_t P[16];
+  int64_t C0 = int64_t(256) * 8 * vectors_for(chunk_log2, 8);  // conservative (bf16 chunk)
+  int64_t C0f = int64_t(256) * 4 * vectors_for(chunk_log2, 4);
+  if (C0f < C0) C0 = C0f;
+  int L = levels_of(n, C0, int64_t(256) * 4 * 16, P, 16);
+  size_t b = 0;
+  for (int i = 0; i < L; ++i) b += align256(2 * sizeof(float) * (size_t)P[i]);
+  return b + 256;
+}
+
+template <typename T, int LEAF>
+static hipError_t launch_leaves(const T* x, const float* cm, int64_t n, int64_t cols, int V,
+                                int64_t P, float* ps, float* pm, hipStream_t s) {
+  dim3 g((unsigned)P), b(256);
+  switch (V) {
+    case 1: hipLaunchKernelGGL((k_flat_leaves<T, LEAF, 1>), g, b, 0, s, x, cm, n, cols, ps, pm); break;
+    case 2: hipLaunchKernelGGL((k_flat_leaves<T, LEAF, 2>), g, b, 0, s, x, cm, n, cols, ps, pm); break;
+    case 4: hipLaunchKernelGGL((k_flat_leaves<T, LEAF, 4>), g, b, 0, s, x, cm, n, cols, ps, pm); break;
+    case 8: hipLaunchKernelGGL((k_flat_leaves<T, LEAF, 8>), g, b, 0, s, x, cm, n, cols, ps, pm); break;
+    default: hipLaunchKernelGGL((k_flat_leaves<T, LEAF, 16>), g, b, 0, s, x, cm, n, cols, ps, pm); break;
+  }
+  return hipGetLastError();
+}
+
+// Max partials of a level: one work-group per 16384 entries of the level
+// below, matching the raw-sum pass, so both arrays have the same length.
+// (max is order-free: any grouping is exact.)
+__global__ __launch_bounds__(256) void k_max_partials(const float* __restrict__ pm, int64_t P,
+                                                      float* __restrict__ out) {
+  const int64_t i0 = (int64_t)blockIdx.x * 16384;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < 16384; i += 256) {
+    int64_t j = i0 + i;
+    if (j < P) m = fmaxf(m, pm[j]);
+  }
+  m = wave_max(m);
+  __shared__ float sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+}
+
+hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul, int64_t n,
+                       int64_t cols, float* out2, void* ws, int chunk_log2, int32_t* dflags,
+                       hipStream_t s) {
+  const int E = dtype == BRQ_BF16 ? 8 : 4;
+  const int V = vectors_for(chunk_log2, E);
+  const int64_t C0 = int64_t(256) * E * V;
+  const int Vr = 16;  // raw partial levels: 16384 leaves per work-group
+  int64_t P[16];
+  int L = levels_of(n, C0, int64_t(256) * 4 * Vr, P, 16);
+  char* w = (char*)ws;
+  float* ps[16];
+  float* pm[16];
+  for (int i = 0; i < L; ++i) {
+    ps[i] = (float*)w;
+    pm[i] = ps[i] + P[i];
+    w += align256(2 * sizeof(float) * (size_t)P[i]);
+  }
+  hipError_t e;
+  if (dtype == BRQ_BF16) {
+    const uint16_t* xb = (const uint16_t*)x;
+    if (leaf == LEAF_ABS) e = launch_leaves<uint16_t, LEAF_ABS>(xb, col_mul, n, cols, V, P[0], ps[0], pm[0], s);
+    else if (leaf == LEAF_ABS_COLMUL) e = launch_leaves<uint16_t, LEAF_ABS_COLMUL>(xb, col_mul, n, cols, V, P[0], ps[0], pm[0], s);
+    else e = launch_leaves<uint16_t, LEAF_SQUARE>(xb, col_mul, n, cols, V, P[0], ps[0], pm[0], s);
+  } else {
+    const float* xf = (const float*)x;
+    if (leaf == LEAF_ABS) e = launch_leaves<float, LEAF_ABS>(xf, col_mul, n, cols, V, P[0], ps[0], pm[0], s);
+    else if (leaf == LEAF_ABS_COLMUL) e = launch_leaves<float, LEAF_ABS_COLMUL>(xf, col_mul, n, cols, V, P[0], ps[0], pm[0], s);
+    else if (leaf == LEAF_SQUARE) e = launch_leaves<float, LEAF_SQUARE>(xf, col_mul, n, cols, V, P[0], ps[0], pm[0], s);
+    else e = launch_leaves<float, LEAF_RAW>(xf, col_mul, n, cols, V, P[0], ps[0], pm[0], s);
+  }
+  if (e != hipSuccess) return e;
+  for (int i = 1; i < L; ++i) {
+    e = launch_leaves<float, LEAF_RAW>(ps[i - 1], nullptr, P[i - 1], 1, Vr, P[i], ps[i], pm[i], s);
+    if (e != hipSuccess) return e;
+    // the max partials of this level are recomputed from the previous level
+    hipLaunchKernelGGL(k_max_partials, dim3((unsigned)P[i]), dim3(256), 0, s, pm[i - 1],
+                       P[i - 1], pm[i]);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_flat_final, dim3(1), dim3(1024), 0, s, ps[L - 1], pm[L - 1], P[L - 1],
+                     out2, dflags);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// LSQ scale from a tree sum: m = fl(S * inv_n), s = fl(m * K2), r = fl(1/s).
+// --------------------------------------------------------------------------
+__global__ void k_lsq_finalize(const float* sum_max, float inv_n, float* sr, float* scale,
+                               float* amax) {
+  float m = fmul(sum_max[0], inv_n);
+  float sc = fmul(m, lsq_k2());
+  float r = (sc == 0.0f) ? 0.0f : flush(1.0f / sc);
+  sr[0] = sc;
+  sr[1] = r;
+  if (scale) scale[0] = sc;
+  if (amax) amax[0] = sum_max[1];
+}
+
+hipError_t lsq_finalize(const float* sum_max, float inv_n, float* sr, float* scale, float* amax,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(k_lsq_finalize, dim3(1), dim3(1), 0, s, sum_max, inv_n, sr, scale, amax);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Elementwise codes: 16 outputs (one 16-byte store) per lane and step.
+// --------------------------------------------------------------------------
+template <typename T, bool COLMUL>
+__global__ __launch_bounds__(256) void k_quant_flat(const T* __restrict__ x,
+                                                    const float* __restrict__ cm, int64_t n,
+                                                    int64_t cols, const float* __restrict__ sr,
+                                                    int8_t* __restrict__ q) {
+  constexpr int E = Elem<T>::kPerVec;
+  constexpr int NV = 16 / E;
+  const float r = sr[1];
+  const int64_t groups = n / 16;
+  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups;
+       gi += (int64_t)gridDim.x * 256) {
+    const int64_t i0 = gi * 16;
+    uint32_t packed[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      float f[E];
+      Elem<T>::unpack(ld16(x + i0 + v * E), f);
+      if (COLMUL) {
+        int64_t col = (i0 + v * E) % cols;
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] = fmul(f[e], flush(cm[col + e]));
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        int k = v * E + e;
+        packed[k >> 2] |= (uint32_t)(quant_code(f[e], r) & 0xff) << (8 * (k & 3));
+      }
+    }
+    st16(q + i0, u32x4{packed[0], packed[1], packed[2], packed[3]});
+  }
+  // tail (n % 16 elements), handled by the first lanes of block 0
+  if (blockIdx.x == 0 && threadIdx.x < (n & 15)) {
+    int64_t i = groups * 16 + threadIdx.x;
+    float f = Elem<T>::load1(x, i);
+    if (COLMUL) f = fmul(f, flush(cm[i % cols]));
+    q[i] = (int8_t)quant_code(f, r);
+  }
+}
+
+hipError_t quant_flat(const void* x, int dtype, const float* col_mul, int64_t n, int64_t cols,
+                      const float* sr, int8_t* q, hipStream_t s) {
+  int64_t groups = n / 16;
+  int64_t blocks = cdiv(groups > 0 ? groups : 1, 256);
+  if (blocks > 65536) blocks = 65536;
+  dim3 g((unsigned)blocks), b(256);
+  if (dtype == BRQ_BF16) {
+    if (col_mul) hipLaunchKernelGGL((k_quant_flat<uint16_t, true>), g, b, 0, s, (const uint16_t*)x, col_mul, n, cols, sr, q);
+    else hipLaunchKernelGGL((k_quant_flat<uint16_t, false>), g, b, 0, s, (const uint16_t*)x, col_mul, n, cols, sr, q);
+  } else {
+    if (col_mul) hipLaunchKernelGGL((k_quant_flat<float, true>), g, b, 0, s, (const float*)x, col_mul, n, cols, sr, q);
+    else hipLaunchKernelGGL((k_quant_flat<float, false>), g, b, 0, s, (const float*)x, col_mul, n, cols, sr, q);
+  }
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Per-row LSQ: one wave per row, 4 rows per work-group.  Vector v of lane l
+// covers columns [(64 v + l) E, + E); columns past the end are +0 leaves.
+// --------------------------------------------------------------------------
+template <typename T, int V>
+__global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int64_t rows,
+                                                    int64_t cols, float inv_cols,
+                                                    int8_t* __restrict__ q,
+                                                    float* __restrict__ scale,
+                                                    float* __restrict__ amax, int32_t* flags) {
+  constexpr int E = Elem<T>::kPerVec;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const T* xr = x + row * cols;
+  u32x4 raw[V];
+  float node[V];
+  float mx = 0.0f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int64_t c0 = (int64_t)(v * 64 + lane) * E;
+    float f[E];
+    if (c0 < cols) {
+      raw[v] = ld16(xr + c0);
+      Elem<T>::unpack(raw[v], f);
+    } else {
+      raw[v] = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      f[e] = fabs_bits(f[e]);
+      mx = fmaxf(mx, f[e]);
+    }
+    node[v] = wave_tree<false>(reg_tree<false, E>(f));
+  }
+  const float S = reg_tree<false, V>(node);
+  mx = wave_max(mx);
+  const float sc = fmul(fmul(S, inv_cols), lsq_k2());
+  const float r = (sc == 0.0f) ? 0.0f : flush(1.0f / sc);
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int64_t c0 = (int64_t)(v * 64 + lane) * E;
+    if (c0 >= cols) continue;
+    float f[E];
+    Elem<T>::unpack(raw[v], f);
+    uint32_t p[2] = {0, 0};
+#pragma unroll
+    for (int e = 0; e < E; ++e) p[e >> 2] |= (uint32_t)(quant_code(f[e], r) & 0xff) << (8 * (e & 3));
+    if (E == 8) *reinterpret_cast<uint2*>(q + row * cols + c0) = make_uint2(p[0], p[1]);
+    else *reinterpret_cast<uint32_t*>(q + row * cols + c0) = p[0];
+  }
+  if (lane == 0) {
+    scale[row] = sc;
+    if (amax) amax[row] = mx;
+    if (!__builtin_isfinite(S)) set_flag(flags, BRQ_FLAG_NONFINITE);
+  }
+}
+
+hipError_t quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int8_t* q,
+                      float* scale, float* amax, int32_t* dflags, hipStream_t s) {
+  const int E = dtype == BRQ_BF16 ? 8 : 4;
+  int64_t per = (cols + 64 * E - 1) / (64 * E);
+  int V = 1;
+  while (V < per) V *= 2;
+  const float inv_cols = 1.0f / (float)cols;  // host binary32 division, correctly rounded
+  dim3 g((unsigned)cdiv(rows, 4)), b(256);
+#define BRQ_ROWS(TT, VV)                                                                    \
+  hipLaunchKernelGGL((k_quant_rows<TT, VV>), g, b, 0, s, (const TT*)x, rows, cols, inv_cols, q, \
+                     scale, amax, dflags)
+  if (dtype == BRQ_BF16) {
+    switch (V) {
+      case 1: BRQ_ROWS(uint16_t, 1); break;
+      case 2: BRQ_ROWS(uint16_t, 2); break;
+      case 4: BRQ_ROWS(uint16_t, 4); break;
+      case 8: BRQ_ROWS(uint16_t, 8); break;
+      case 16: BRQ_ROWS(uint16_t, 16); break;
+      default: BRQ_ROWS(uint16_t, 32); break;
+    }
+  } else {
+    switch (V) {
+      case 1: BRQ_ROWS(float, 1); break;
+      case 2: BRQ_ROWS(float, 2); break;
+      case 4: BRQ_ROWS(float, 4); break;
+      case 8: BRQ_ROWS(float, 8); break;
+      case 16: BRQ_ROWS(float, 16); break;
+      case 32: BRQ_ROWS(float, 32); break;
+      default: BRQ_ROWS(float, 64); break;
+    }
+  }
+#undef BRQ_ROWS
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// int8 transpose through LDS, 64x64 tiles.  rows % 16 == 0, cols % 16 == 0.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_transpose_i8(const int8_t* __restrict__ q, int64_t rows,
+                                                      int64_t cols, int8_t* __restrict__ qt) {
+  __shared__ uint32_t tile[64][17];  // 64 rows x 64 bytes, one padding word per row
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  {
+    const int r = t >> 2, ch = t & 3;
+    u32x4 v = {0, 0, 0, 0};
+    if (r0 + r < rows && c0 + ch * 16 < cols) v = ld16(q + (r0 + r) * cols + c0 + ch * 16);
+    tile[r][ch * 4 + 0] = v.x;
+    tile[r][ch * 4 + 1] = v.y;
+    tile[r][ch * 4 + 2] = v.z;
+    tile[r][ch * 4 + 3] = v.w;
+  }
+  __syncthreads();
+  const int c = t >> 2, rg = (t & 3) * 16;  // output row c (input column), 16 input rows
+  if (c0 + c >= cols || r0 + rg >= rows) return;
+  uint32_t p[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t word = tile[rg + i][c >> 2];
+    uint32_t byte = (word >> (8 * (c & 3))) & 0xffu;
+    p[i >> 2] |= byte << (8 * (i & 3));
+  }
+  st16(qt + (c0 + c) * rows + r0 + rg, u32x4{p[0], p[1], p[2], p[3]});
+}
+
+hipError_t transpose_i8(const int8_t* q, int64_t rows, int64_t cols, int8_t* qt, hipStream_t s) {
+  dim3 g((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows, 64)), b(256);
+  hipLaunchKernelGGL(k_transpose_i8, g, b, 0, s, q, rows, cols, qt);
+  return hipGetLastError();
+}
+
+}  // namespace brq

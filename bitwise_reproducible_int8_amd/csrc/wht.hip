@@ -1,0 +1,293 @@
+// wht.hip -- Walsh-Hadamard rotation along tokens before the int8 weight-
+// gradient GEMM (Open-1B report §3.2 "int8 computation": a Walsh-Hadamard
+// rotation along the contraction dimension flattens gradient outliers
+// before int8 quantisation).  H_b is the unnormalised Sylvester matrix,
+// H[i][j] = (-1)^popcount(i & j), applied to each aligned block of b
+// tokens; the 1/b of H^T H = b I is folded into the dW epilogue.
+//
+// Both rotated tensors are written transposed (token-contiguous) so the dW
+// GEMM reads its contraction dimension contiguously.
+//
+// Integer side: u = H q_x is exact (|u| <= 127 b fits int16), so two
+// columns ride in one register as packed int16 lanes, and the statistic
+// sum |u| is an exact integer (any order).
+//
+// Float side: v is computed by butterflies in stage order h = 1, 2, ...,
+// b/2, each (v_j, v_j+h) <- (fl(v_j + v_j+h), fl(v_j - v_j+h)) -- the
+// rounding sequence the definition fixes -- one column per lane, all b
+// tokens in registers.  Its per-tensor statistic is the canonical tree over
+// |v| in row-major [M][N] order: each wave owns 64 aligned columns, so for
+// every token row it produces node(6, .) of the row-major tree (an LDS
+// transpose gives each lane 16 consecutive columns of one row; the lane
+// quad then pairs up), and the flat tree reduction finishes the job.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace brq {
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- integer rotation ---------------------------------------------------------
+template <int TB>
+__device__ __forceinline__ void load_int_cols(const int8_t* __restrict__ q_x, int64_t M, int64_t K,
+                                              int64_t m0, int64_t k, s16x2* u) {
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    uint32_t w = *reinterpret_cast<const uint16_t*>(q_x + (m0 + i) * K + k);
+    s16x2 p;
+    p.x = (short)(int8_t)(w & 0xffu);
+    p.y = (short)(int8_t)(w >> 8);
+    u[i] = p;
+  }
+}
+
+template <int TB, typename V>
+__device__ __forceinline__ void butterflies_int(V* u, int b) {
+#pragma unroll
+  for (int h = 1; h < TB; h *= 2) {
+    if (h < b) {
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        if (j & h) continue;
+        V a = u[j], c = u[j + h];
+        u[j] = a + c;
+        u[j + h] = a - c;
+      }
+    }
+  }
+}
+
+// Pass 1: sum |u| per work-group (int64 partials).
+template <int TB>
+__global__ __launch_bounds__(256) void k_wht_int_stats(const int8_t* __restrict__ q_x, int64_t M,
+                                                       int64_t K, int b,
+                                                       long long* __restrict__ part) {
+  const int64_t k = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+  const int64_t m0 = (int64_t)blockIdx.y * TB;
+  int s = 0;
+  if (k < K) {
+    s16x2 u[TB];
+    load_int_cols<TB>(q_x, M, K, m0, k, u);
+    butterflies_int<TB>(u, b);
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      int a = u[i].x, c = u[i].y;
+      s += (a < 0 ? -a : a) + (c < 0 ? -c : c);
+    }
+  }
+  // integer sums: exact in any order
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  __shared__ int ws[4];
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    part[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] =
+        (long long)ws[0] + ws[1] + ws[2] + ws[3];
+}
+
+// Exact total, then the LSQ step: fl(double(S)) -> fl(* inv_n) -> fl(* K2).
+__global__ __launch_bounds__(256) void k_wht_int_finalize(const long long* __restrict__ part,
+                                                          int64_t P, float inv_n, float* sr,
+                                                          float* s_out) {
+  long long s = 0;
+  for (int64_t i = threadIdx.x; i < P; i += 256) s += part[i];
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  __shared__ long long ws[4];
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long S = ws[0] + ws[1] + ws[2] + ws[3];
+    float Sf = (float)(double)S;  // exact in double (S < 2^53), one rounding
+    float sc = fmul(fmul(Sf, inv_n), lsq_k2());
+    float r = (sc == 0.0f) ? 0.0f : flush(1.0f / sc);
+    sr[0] = sc;
+    sr[1] = r;
+    if (s_out) s_out[0] = sc;
+  }
+}
+
+// Pass 2: recompute u, quantise, write q_u^T [K][M] (16 tokens per store).
+template <int TB>
+__global__ __launch_bounds__(256) void k_wht_int_quant(const int8_t* __restrict__ q_x, int64_t M,
+                                                       int64_t K, int b, const float* __restrict__ sr,
+                                                       int8_t* __restrict__ q_ut) {
+  const int64_t k = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+  const int64_t m0 = (int64_t)blockIdx.y * TB;
+  if (k >= K) return;
+  const float r = sr[1];
+  s16x2 u[TB];
+  load_int_cols<TB>(q_x, M, K, m0, k, u);
+  butterflies_int<TB>(u, b);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int p = 0; p < TB / 16; ++p) {
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        int val = c ? u[16 * p + i].y : u[16 * p + i].x;
+        w[i >> 2] |= (uint32_t)(quant_code((float)val, r) & 0xff) << (8 * (i & 3));
+      }
+      st16(q_ut + (k + c) * M + m0 + 16 * p, u32x4{w[0], w[1], w[2], w[3]});
+    }
+  }
+}
+
+size_t wht_x_ws(int64_t M, int64_t K, int block) {
+  const int TB = block > 64 ? 128 : 64;
+  int64_t P = cdiv(K, 512) * (M / TB);
+  return align256((size_t)(P > 0 ? P : 1) * sizeof(long long)) + 256;
+}
+
+hipError_t wht_quant_x(const int8_t* q_x, int64_t M, int64_t K, int block, int8_t* q_ut,
+                       float* s_u, void* ws, hipStream_t s) {
+  const int TB = block > 64 ? 128 : 64;
+  dim3 g((unsigned)cdiv(K, 512), (unsigned)(M / TB)), bl(256);
+  const int64_t P = (int64_t)g.x * g.y;
+  long long* part = (long long*)ws;
+  float* sr = (float*)((char*)ws + align256((size_t)(P > 0 ? P : 1) * sizeof(long long)));
+  const float inv_n = 1.0f / (float)(M * K);
+  if (TB == 128) hipLaunchKernelGGL(k_wht_int_stats<128>, g, bl, 0, s, q_x, M, K, block, part);
+  else hipLaunchKernelGGL(k_wht_int_stats<64>, g, bl, 0, s, q_x, M, K, block, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_wht_int_finalize, dim3(1), dim3(256), 0, s, part, P, inv_n, sr, s_u);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (TB == 128) hipLaunchKernelGGL(k_wht_int_quant<128>, g, bl, 0, s, q_x, M, K, block, sr, q_ut);
+  else hipLaunchKernelGGL(k_wht_int_quant<64>, g, bl, 0, s, q_x, M, K, block, sr, q_ut);
+  return hipGetLastError();
+}
+
+// ---- fp32 rotation ------------------------------------------------------------------
+template <typename T, int TB>
+__device__ __forceinline__ void load_fp_col(const T* __restrict__ dy, int64_t N, int64_t m0,
+                                            int64_t col, float* v) {
+#pragma unroll
+  for (int i = 0; i < TB; ++i) v[i] = Elem<T>::load1(dy, (m0 + i) * N + col);
+}
+
+template <int TB>
+__device__ __forceinline__ void butterflies_fp(float* v, int b) {
+#pragma unroll
+  for (int h = 1; h < TB; h *= 2) {
+    if (h < b) {
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        if (j & h) continue;
+        float a = v[j], c = v[j + h];
+        v[j] = fadd(a, c);
+        v[j + h] = fsub(a, c);
+      }
+    }
+  }
+}
+
+// Pass 1: node(6, .) of the row-major |v| tree for each token row of the
+// tile and each wave's 64 columns: part[m * (N/64) + col/64].
+template <typename T, int TB>
+__global__ __launch_bounds__(256) void k_wht_fp_stats(const T* __restrict__ dy, int64_t M,
+                                                      int64_t N, int b, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float tr[4][16][68];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.y * TB;
+  const bool live = col < N;  // N % 64 == 0: whole waves are live or not
+  float v[TB];
+  if (live) {
+    load_fp_col<T, TB>(dy, N, m0, col, v);
+    butterflies_fp<TB>(v, b);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TB; ++i) v[i] = 0.0f;
+  }
+  const int64_t nb = N / 64;
+  const int64_t cb = ((int64_t)blockIdx.x * 256 + wave * 64) / 64;
+#pragma unroll
+  for (int p = 0; p < TB / 16; ++p) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tr[wave][i][lane] = fabs_bits(v[16 * p + i]);
+    __syncthreads();
+    const int r = lane >> 2, c16 = (lane & 3) * 16;
+    float a[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float4 x4 = *reinterpret_cast<const float4*>(&tr[wave][r][c16 + 4 * q]);
+      a[4 * q] = x4.x; a[4 * q + 1] = x4.y; a[4 * q + 2] = x4.z; a[4 * q + 3] = x4.w;
+    }
+    float node = reg_tree<false, 16>(a);
+    node = node + dpp_xor1(node);  // non-negative: no flush needed
+    node = node + dpp_xor2(node);
+    if (live && (lane & 3) == 0) part[(m0 + 16 * p + r) * nb + cb] = node;
+    __syncthreads();
+  }
+}
+
+// Pass 2: recompute v, quantise with r_v, write q_v^T [N][M].
+template <typename T, int TB>
+__global__ __launch_bounds__(256) void k_wht_fp_quant(const T* __restrict__ dy, int64_t M,
+                                                      int64_t N, int b, const float* __restrict__ sr,
+                                                      int8_t* __restrict__ q_vt) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.y * TB;
+  if (col >= N) return;
+  const float r = sr[1];
+  float v[TB];
+  load_fp_col<T, TB>(dy, N, m0, col, v);
+  butterflies_fp<TB>(v, b);
+#pragma unroll
+  for (int p = 0; p < TB / 16; ++p) {
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      w[i >> 2] |= (uint32_t)(quant_code(v[16 * p + i], r) & 0xff) << (8 * (i & 3));
+    st16(q_vt + col * M + m0 + 16 * p, u32x4{w[0], w[1], w[2], w[3]});
+  }
+}
+
+size_t wht_dy_ws(int64_t M, int64_t N, int block, int chunk_log2) {
+  (void)block;
+  const int64_t P = M * (N / 64);
+  return align256((size_t)(P > 0 ? P : 1) * sizeof(float)) + flat_reduce_ws(P, chunk_log2) + 256;
+}
+
+hipError_t wht_quant_dy(const void* dy, int dtype, int64_t M, int64_t N, int block, int8_t* q_vt,
+                        float* s_v, void* ws, int chunk_log2, int32_t* dflags, hipStream_t s) {
+  const int TB = block > 64 ? 128 : 64;
+  const int64_t P = M * (N / 64);
+  char* w = (char*)ws;
+  float* part = (float*)w;
+  w += align256((size_t)(P > 0 ? P : 1) * sizeof(float));
+  void* fws = w;
+  w += flat_reduce_ws(P, chunk_log2);
+  float* sum2 = (float*)w;  // [0] sum, [1] max, [2] s, [3] r
+  float* sr = sum2 + 2;
+  dim3 g((unsigned)cdiv(N, 256), (unsigned)(M / TB)), bl(256);
+#define BRQ_FP(KERN, ...)                                                                         \
+  do {                                                                                           \
+    if (dtype == BRQ_BF16) {                                                                     \
+      if (TB == 128) hipLaunchKernelGGL((KERN<uint16_t, 128>), g, bl, 0, s, (const uint16_t*)dy, \
+                                        M, N, block, __VA_ARGS__);                               \
+      else hipLaunchKernelGGL((KERN<uint16_t, 64>), g, bl, 0, s, (const uint16_t*)dy, M, N,      \
+                              block, __VA_ARGS__);                                               \
+    } else {                                                                                     \
+      if (TB == 128) hipLaunchKernelGGL((KERN<float, 128>), g, bl, 0, s, (const float*)dy, M, N, \
+                                        block, __VA_ARGS__);                                     \
+      else hipLaunchKernelGGL((KERN<float, 64>), g, bl, 0, s, (const float*)dy, M, N, block,     \
+                              __VA_ARGS__);                                                      \
+    }                                                                                            \
+  } while (0)
+  BRQ_FP(k_wht_fp_stats, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = flat_reduce(part, BRQ_F32, LEAF_RAW, nullptr, P, 1, sum2, fws, chunk_log2, dflags, s)) !=
+      hipSuccess)
+    return e;
+  if ((e = lsq_finalize(sum2, 1.0f / (float)(M * N), sr, s_v, nullptr, s)) != hipSuccess) return e;
+  BRQ_FP(k_wht_fp_quant, sr, q_vt);
+#undef BRQ_FP
+  return hipGetLastError();
+}
+
+}  // namespace brq

@@ -1,0 +1,248 @@
+/*
+ * brq.h -- C ABI of libbrq: the bitwise-reproducible W8A8 quantisation-aware
+ * linear layer of the Open-1B report (arXiv 2609.17380), for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Conventions (all entry points):
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates or frees device memory; scratch space comes from the
+ *    caller's workspace `ws` of at least brq_workspace_size(...) bytes.
+ *  - Row-major, contiguous.  int8 / bf16 / fp32 tensors must be 16-byte
+ *    aligned; shapes satisfy the per-call rules stated below.
+ *  - Every call enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ *    null stream) and returns once they are launched.  Nothing synchronises.
+ *  - Return value: BRQ_OK (0) or a negative brq_status, detected on the host
+ *    before anything is launched (argument errors) or from the launch itself
+ *    (BRQ_E_HIP; brq_last_hip_error() has the code).
+ *  - Data errors found on the device (a non-finite statistic) are OR-ed into
+ *    `dflags` (device int32*, may be NULL) as BRQ_FLAG_*; outputs are
+ *    unspecified when a flag is raised.  The caller zeroes `dflags`.
+ *  - Results are bit-identical for every `tune` setting and every launch
+ *    geometry; `tune` may be NULL (defaults).
+ *  - Calls that share a workspace must be ordered (same stream or explicit
+ *    synchronisation); calls with distinct workspaces may run concurrently.
+ *
+ * Numerics (the pages' bitwise-reproducibility contract, §2.1 and Table 1):
+ *  every floating-point operation is one IEEE binary32 operation, round to
+ *  nearest even, never contracted into a fused multiply-add; inputs whose
+ *  exponent field is zero read as signed zero and subnormal results are
+ *  replaced by signed zero; every reduction follows one canonical pairwise
+ *  tree over the leaves in logical row-major order (pairs (2i, 2i+1), lower
+ *  index on the left, an unpaired last node moves up unchanged); every mean
+ *  is a multiply by fl(1/n) (App. A.3).
+ */
+#ifndef BRQ_H
+#define BRQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BRQ_SPEC_VERSION 1
+
+enum brq_status {
+  BRQ_OK = 0,
+  BRQ_E_NULL = -1,        /* a required pointer is NULL */
+  BRQ_E_DTYPE = -2,       /* unsupported dtype code */
+  BRQ_E_SHAPE = -3,       /* negative size or inconsistent shape */
+  BRQ_E_ALIGN = -4,       /* pointer not 16-byte aligned */
+  BRQ_E_UNSUPPORTED = -5, /* shape outside the supported set (see call) */
+  BRQ_E_RANGE = -6,       /* contraction too long for exact int32 sums */
+  BRQ_E_WORKSPACE = -7,   /* workspace missing or too small */
+  BRQ_E_HIP = -8,         /* kernel launch failed */
+  BRQ_E_ARG = -9          /* other invalid argument */
+};
+
+enum brq_dtype { BRQ_F32 = 0, BRQ_BF16 = 1, BRQ_I8 = 2, BRQ_I32 = 3, BRQ_U8 = 4 };
+enum brq_gran { BRQ_PER_TENSOR = 0, BRQ_PER_ROW = 1 };
+enum brq_flag { BRQ_FLAG_NONFINITE = 1 };
+
+/* Longest contraction whose int8 x int8 sums stay inside int32:
+ * 127 * 127 * 133144 < 2^31. */
+#define BRQ_MAX_CONTRACTION 133144
+
+/* Launch geometry.  None of these fields changes any result bit. */
+typedef struct brq_tune {
+  int gemm_kernel;   /* 0 default, 1 reference (one output per thread),
+                        2 MFMA 128x128 tile, 3 MFMA 256x128 tile,
+                        4 MFMA 128x256 tile */
+  int split_k;       /* 0 default, else 1, 2 or 4 contraction slices */
+  int chunk_log2;    /* 0 default (13), else log2 of the leaves each
+                        reduction work-group owns, in [10, 16] */
+  int rows_per_block;/* 0 default, else RMSNorm backward rows per block:
+                        1..64 power of two */
+} brq_tune;
+
+/* Workspace sizing.  `op` is one of brq_op; unused sizes are ignored. */
+enum brq_op {
+  BRQ_OP_QUANTIZE = 1,     /* a = rows, b = cols */
+  BRQ_OP_QGEMM = 2,        /* a = M, b = N, c = K (fwd, dx, dw GEMMs) */
+  BRQ_OP_DW_WHT = 3,       /* a = M, b = N, c = K, block = Hadamard block */
+  BRQ_OP_RMSNORM_BWD = 4,  /* a = T, b = D */
+  BRQ_OP_GRAD_NORM = 5     /* a = n */
+};
+size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block,
+                          const struct brq_tune* tune);
+
+/* ---------------------------------------------------------------------
+ * quantize_lsq -- LSQ fake-quantisation to int8 (§3.1 "int8
+ * quantization-aware training", §4.2 "Implementation notes", §3.2 "int8
+ * computation").
+ *
+ * x [rows][cols], dtype BRQ_F32 or BRQ_BF16.  When col_mul ([cols] fp32)
+ * is given every element is first multiplied by col_mul[col].
+ * For each group (the whole tensor for BRQ_PER_TENSOR, each row for
+ * BRQ_PER_ROW) of n values v:
+ *     S = tree(|v|);  s = fl(fl(S * fl(1/n)) * K2),  K2 = 2*fl(1/fl(sqrt 127))
+ *     r = fl(1/s) (0 when s == 0);  q = clamp(rint(fl(v * r)), -127, 127)
+ * Outputs: q [rows][cols] int8; q_t [cols][rows] int8 (optional);
+ * scale [1] or [rows]; amax [1] or [rows] = max |v| (optional).
+ * Raises BRQ_FLAG_NONFINITE when S is not finite.
+ * Shapes: cols % 8 == 0 (bf16) / cols % 4 == 0 (fp32); BRQ_PER_ROW needs
+ * cols <= 16384.  Workspace: BRQ_OP_QUANTIZE.
+ * --------------------------------------------------------------------- */
+int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                     int gran, const float* col_mul, int8_t* q, int8_t* q_t,
+                     float* scale, float* amax, void* ws, size_t ws_bytes,
+                     int32_t* dflags, const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * qgemm_fwd -- forward W8A8 GEMM with int32 accumulation, then dequant
+ * (§3.2 "int8 computation").
+ *     acc[m][n] = sum_k q_x[m][k] * q_w[n][k]        (exact int32)
+ *     y[m][n]   = fl(fl(acc) * fl(s_x[0] * s_w[n]))  (s_w[0] when
+ *                                                     w_per_row == 0)
+ * q_x [M][K], q_w [N][K] (nn.Linear layout), y [M][N] fp32.
+ * Shapes: K % 16 == 0, K <= BRQ_MAX_CONTRACTION.  Workspace: BRQ_OP_QGEMM
+ * (only used when split_k > 1).
+ * --------------------------------------------------------------------- */
+int brq_qgemm_fwd(const int8_t* q_x, const float* s_x, const int8_t* q_w,
+                  const float* s_w, int w_per_row, int64_t M, int64_t N,
+                  int64_t K, float* y, void* ws, size_t ws_bytes,
+                  const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * qgemm_bwd_dx -- input-gradient GEMM of the straight-through estimator
+ * (§3.2 "int8 computation").  q_g is the int8 code of g = dY * s_w[n]
+ * (quantize_lsq with col_mul = s_w), s_g its scale:
+ *     dx[m][k] = fl(fl(sum_n q_g[m][n] * q_w[n][k]) * s_g[0])
+ * q_g [M][N]; q_wt [K][N] is the transposed weight code (quantize_lsq's
+ * q_t); dx [M][K] fp32.  Shapes: N % 16 == 0, N <= BRQ_MAX_CONTRACTION.
+ * --------------------------------------------------------------------- */
+int brq_qgemm_bwd_dx(const int8_t* q_g, const float* s_g, const int8_t* q_wt,
+                     int64_t M, int64_t N, int64_t K, float* dx, void* ws,
+                     size_t ws_bytes, const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * qgemm_bwd_dw_wht -- weight-gradient GEMM in int8 after a Walsh-Hadamard
+ * rotation along tokens (§3.2 "int8 computation").  With H_b the
+ * unnormalised Sylvester matrix, H[i][j] = (-1)^popcount(i & j), applied
+ * per aligned block of `block` tokens:
+ *     u = H q_x (exact integers); S_u = sum |u| (exact); s_u from S_u as
+ *         quantize_lsq (fl(double(S_u)) first); q_u = quantised u
+ *     v = fp32 butterflies of dY in stage order h = 1, 2, ..., block/2,
+ *         (v_j, v_j+h) <- (fl(v_j + v_j+h), fl(v_j - v_j+h));
+ *         per-tensor LSQ over v in row-major [M][N] order -> q_v, s_v
+ *     dw[n][k] = fl(fl(sum_m q_v[m][n] * q_u[m][k]) * c_w),
+ *     c_w = fl(fl(fl(s_x * s_u) * s_v) * 2^-log2(block))
+ * q_x [M][K] (the forward activation code), dy [M][N] (BRQ_F32 or BRQ_BF16),
+ * dw [N][K] fp32; s_u_out, s_v_out optional device floats.
+ * Shapes: block a power of two in [1, 128], M % block == 0, M % 64 == 0,
+ * K % 64 == 0, N % 64 == 0, M <= BRQ_MAX_CONTRACTION.
+ * Workspace: BRQ_OP_DW_WHT (it holds the rotated codes q_u^T [K][M] and
+ * q_v^T [N][M] at the start, in that order).
+ * --------------------------------------------------------------------- */
+int brq_qgemm_bwd_dw_wht(const int8_t* q_x, const float* s_x, const void* dy,
+                         int dy_dtype, int64_t M, int64_t N, int64_t K,
+                         int block, float* dw, float* s_u_out, float* s_v_out,
+                         void* ws, size_t ws_bytes, int32_t* dflags,
+                         const struct brq_tune* tune, void* stream);
+
+/* The three stages of qgemm_bwd_dw_wht, callable on their own.
+ * brq_wht_quant_x: q_x [M][K] -> q_ut [K][M] (token-contiguous), s_u [1].
+ * brq_wht_quant_dy: dy [M][N] -> q_vt [N][M], s_v [1].
+ * brq_qgemm_dw: dw [N][K] from q_vt, q_ut and the scales (device floats).
+ * Workspace for the first two: BRQ_OP_DW_WHT. */
+int brq_wht_quant_x(const int8_t* q_x, int64_t M, int64_t K, int block,
+                    int8_t* q_ut, float* s_u, void* ws, size_t ws_bytes,
+                    const struct brq_tune* tune, void* stream);
+int brq_wht_quant_dy(const void* dy, int dy_dtype, int64_t M, int64_t N,
+                     int block, int8_t* q_vt, float* s_v, void* ws,
+                     size_t ws_bytes, int32_t* dflags,
+                     const struct brq_tune* tune, void* stream);
+int brq_qgemm_dw(const int8_t* q_vt, const int8_t* q_ut, const float* s_x,
+                 const float* s_u, const float* s_v, int64_t M, int64_t N,
+                 int64_t K, int block, float* dw, void* ws, size_t ws_bytes,
+                 const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * rmsnorm_fixed -- RMSNorm in FP32 with a fixed reduction order (§3.1
+ * "RMSNorm": pre-norm, no bias; normalisation computed in FP32).
+ * Forward per row t of x [T][D]:
+ *     ss = tree(fl(x*x));  ms = fl(ss * fl(1/D));
+ *     rstd[t] = fl(1 / fl(sqrt(fl(ms + eps))));  y = fl(fl(x * rstd) * g)
+ * Backward:  xh = fl(x * rstd); d = fl(dy * g); dot = tree(fl(d * xh));
+ *     mu = fl(dot * fl(1/D)); dx = fl(rstd * fl(d - fl(xh * mu)));
+ *     dg[j] = tree over tokens t of fl(dy[t][j] * xh[t][j])   (fp32)
+ * x, g, y, dy, dx share `dtype` (BRQ_F32 or BRQ_BF16; bf16 results round to
+ * nearest even); rstd [T] fp32.  Shapes: D % 8 == 0; forward D <= 16384
+ * (bf16) or 8192 (fp32); backward D <= 4096 (bf16) or 2048 (fp32).
+ * Backward workspace: BRQ_OP_RMSNORM_BWD.
+ * --------------------------------------------------------------------- */
+int brq_rmsnorm_fixed_fwd(const void* x, const void* g, int dtype, int64_t T,
+                          int64_t D, float eps, void* y, float* rstd,
+                          int32_t* dflags, const struct brq_tune* tune,
+                          void* stream);
+int brq_rmsnorm_fixed_bwd(const void* x, const void* g, const float* rstd,
+                          const void* dy, int dtype, int64_t T, int64_t D,
+                          void* dx, float* dg, void* ws, size_t ws_bytes,
+                          const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * grad_norm -- global l2 norm of the FP32 gradients (§3.2 "Optimizer":
+ * clipping at global norm 1.0):  ss = tree(fl(v*v)) over v[0..n),
+ * norm = fl(sqrt(ss)).  sumsq, norm: device floats.  Raises
+ * BRQ_FLAG_NONFINITE when ss is not finite.  Workspace: BRQ_OP_GRAD_NORM.
+ * --------------------------------------------------------------------- */
+int brq_grad_norm(const float* v, int64_t n, float* sumsq, float* norm,
+                  void* ws, size_t ws_bytes, int32_t* dflags,
+                  const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * hash_state -- on-device canonical state hash (§5 "Runtime overhead" and
+ * App. B: a per-step state hash, computed here on the device).
+ *   leaf digests: SHA-256 (FIPS 180-4) of each 4096-byte slice of a
+ *     tensor's raw bytes (the last slice may be shorter; an empty tensor
+ *     has one empty leaf);
+ *   levels: SHA-256 of the concatenation of up to 128 consecutive digests,
+ *     repeated until one root remains;
+ *   tensor digest: SHA-256("BRQ1" | dtype u8 | ndim u8 | dims u64 LE ... |
+ *     name length u16 LE | name bytes | root);
+ *   state digest: SHA-256 of the tensor digests in call order.
+ * t[i].data are device pointers (16-byte aligned); digest32 is a device
+ * buffer of 32 bytes.  Workspace: brq_hash_workspace_size(t, n).
+ * --------------------------------------------------------------------- */
+typedef struct brq_tensor_ref {
+  const void* data;
+  int dtype;          /* brq_dtype code, hashed into the tensor digest */
+  int ndim;           /* 0..8 */
+  int64_t dims[8];
+  const char* name;   /* at most 255 bytes */
+} brq_tensor_ref;
+
+size_t brq_hash_workspace_size(const brq_tensor_ref* t, int n);
+int brq_hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* Status text, HIP error of the last BRQ_E_HIP in this thread, version. */
+const char* brq_status_string(int status);
+int brq_last_hip_error(void);
+int brq_spec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BRQ_H */

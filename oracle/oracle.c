@@ -121,6 +121,11 @@ float orc_lsq_k2(void) {
 static float inv_count(int64_t n) { return fdiv(1.0f, (float)n); }
 
 void orc_lsq_scale(float S, int64_t n, float* s_out, float* r_out) {
+  if (n == 0) { /* an empty group has step size 0: no mean is taken */
+    *s_out = 0.0f;
+    *r_out = 0.0f;
+    return;
+  }
   float m = fmul(S, inv_count(n));
   float s = fmul(m, orc_lsq_k2());
   *s_out = s;

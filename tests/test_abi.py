@@ -1,0 +1,86 @@
+"""The C-ABI library loads and exports every entry point include/brq.h
+declares; host-side argument checks return their status codes without
+touching a GPU (no compute calls here)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "brq.h")
+LIB = os.path.join(ROOT, "bitwise_reproducible_int8_amd", "libbrq.so")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(brq_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libbrq.so is not built: run __graft_entry__.build()")
+    return C.CDLL(LIB)
+
+
+def test_header_declares_the_path():
+    names = declared()
+    for n in ["brq_quantize_lsq", "brq_qgemm_fwd", "brq_qgemm_bwd_dx", "brq_qgemm_bwd_dw_wht",
+              "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm", "brq_hash_state"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (brq_\w+)", out))
+    missing = [n for n in declared() if n not in exported]
+    assert not missing, missing
+    for n in declared():
+        getattr(lib, n)
+
+
+def test_binding_symbol_list_matches_header():
+    import bitwise_reproducible_int8_amd as brq
+    assert sorted(brq.SYMBOLS) == declared()
+
+
+def test_host_side_status_codes(lib):
+    vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
+    lib.brq_status_string.restype = C.c_char_p
+    lib.brq_spec_version.restype = i32
+    assert lib.brq_spec_version() == 1
+    assert lib.brq_status_string(0) == b"ok"
+    q = lib.brq_quantize_lsq
+    q.restype = i32
+    q.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, C.c_size_t, vp, vp, vp]
+    fake = 0x1000
+    # bad dtype, negative shape, NULL output, misalignment, missing workspace
+    assert q(fake, 7, 4, 8, 0, None, fake, None, fake, None, None, 0, None, None, None) == -2
+    assert q(fake, 1, -1, 8, 0, None, fake, None, fake, None, None, 0, None, None, None) == -3
+    assert q(fake, 1, 4, 8, 0, None, fake, None, None, None, None, 0, None, None, None) == -1
+    assert q(fake + 2, 1, 4, 8, 0, None, fake, None, fake, None, None, 0, None, None, None) == -4
+    assert q(fake, 1, 4, 12, 0, None, fake, None, fake, None, None, 0, None, None, None) == -5
+    assert q(fake, 1, 4, 8, 0, None, fake, None, fake, None, None, 0, None, None, None) == -7
+    g = lib.brq_qgemm_fwd
+    g.restype = i32
+    g.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, C.c_size_t, vp, vp]
+    assert g(fake, fake, fake, fake, 1, 64, 64, 24, fake, None, 0, None, None) == -5   # K % 16
+    assert g(fake, fake, fake, fake, 1, 64, 64, 133152, fake, None, 0, None, None) == -6  # int32 range
+    d = lib.brq_qgemm_bwd_dw_wht
+    d.restype = i32
+    d.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp, vp, vp, C.c_size_t, vp, vp, vp]
+    assert d(fake, fake, fake, 1, 128, 64, 64, 96, fake, None, None, fake, 1 << 30, None, None, None) == -5
+    assert d(fake, fake, fake, 1, 96, 64, 64, 64, fake, None, None, fake, 1 << 30, None, None, None) == -5
+
+
+def test_workspace_sizes_are_monotone(lib):
+    lib.brq_workspace_size.restype = C.c_size_t
+    lib.brq_workspace_size.argtypes = [C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_void_p]
+    a = lib.brq_workspace_size(1, 4096, 2048, 0, 0, None)
+    b = lib.brq_workspace_size(1, 16384, 8192, 0, 0, None)
+    assert 0 < a < b
+    assert lib.brq_workspace_size(3, 16384, 8192, 2048, 128, None) > 16384 * (8192 + 2048)

@@ -1,0 +1,369 @@
+"""GPU parity, small and ragged shapes: every libbrq entry point through the
+C ABI against the CPU oracle, bit for bit, across launch geometries.
+
+Shapes span several tiles and leave ragged tails; tune settings sweep the
+GEMM kernel (reference / three MFMA tilings), split-K, the reduction chunk
+size and the RMSNorm backward block height.  Outputs must be identical for
+every setting.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import brq_synth as syn
+import oracle as orc
+from tests.gpu_util import DEV, assert_bitwise, codes, sha, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+brq = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global brq
+    import bitwise_reproducible_int8_amd as m
+    m.lib()
+    brq = m
+    yield
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# quantize_lsq
+# --------------------------------------------------------------------------
+QUANT_CASES = [
+    ((64, 256), False, None),      # tiny activation, fp32
+    ((100, 264), True, None),      # ragged rows, bf16
+    ((257, 520), False, None),     # ragged everything, fp32
+    ((300, 512), True, "cm"),      # bf16 with a per-column multiplier
+    ((64, 256), False, "cm"),
+]
+
+
+@pytest.mark.parametrize("shape,bf16,cm", QUANT_CASES)
+@pytest.mark.parametrize("chunk", [0, 10, 12, 15])
+def test_quantize_per_tensor(shape, bf16, cm, chunk):
+    say("quantize_per_tensor", shape, bf16, cm, chunk)
+    x = syn.normal(shape, 1.0, tag=201, bf16=bf16)
+    col = syn.normal((shape[1],), 0.01, mean=0.02, tag=202) if cm else None
+    q, qt, s, amax, fl = orc.quantize_lsq(x, col_mul=col, want_t=(shape[0] % 16 == 0 and shape[1] % 16 == 0))
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gq, gqt, gs, gamax = brq.quantize_lsq(to_dev(x), col_mul=None if col is None else to_dev(col),
+                                          want_t=qt is not None, tune={"chunk_log2": chunk},
+                                          flags=flags)
+    assert_bitwise(gq, q, "q")
+    assert_bitwise(gs, s, "scale")
+    assert_bitwise(gamax, amax, "amax")
+    if qt is not None:
+        assert_bitwise(gqt, qt, "q_t")
+    assert int(flags.item()) == fl == 0
+
+
+@pytest.mark.parametrize("shape,bf16", [((256, 256), False), ((3072, 2048), True),
+                                        ((48, 8192), True), ((16, 264), True), ((5, 16384), True),
+                                        ((33, 100), False)])
+def test_quantize_per_row(shape, bf16):
+    say("quantize_per_row", shape, bf16)
+    w = syn.normal(shape, 0.02, tag=203, bf16=bf16)
+    want_t = shape[0] % 16 == 0 and shape[1] % 16 == 0
+    q, qt, s, amax, fl = orc.quantize_lsq(w, per_row=True, want_t=want_t)
+    gq, gqt, gs, gamax = brq.quantize_lsq(to_dev(w), per_row=True, want_t=want_t)
+    assert_bitwise(gq, q, "q")
+    assert_bitwise(gs, s, "scale")
+    assert_bitwise(gamax, amax, "amax")
+    if want_t:
+        assert_bitwise(gqt, qt, "q_t")
+
+
+def test_quantize_edge_cases():
+    say("quantize_edge_cases")
+    z = np.zeros((32, 64), np.float32)
+    gq, _, gs, _ = brq.quantize_lsq(to_dev(z))
+    assert not to_np(gq).any() and float(gs.item()) == 0.0
+    gq, _, gs, _ = brq.quantize_lsq(to_dev(z), per_row=True)
+    assert not to_np(gq).any() and not to_np(gs).any()
+    # empty tensor: step size 0
+    e = torch.empty((0, 64), dtype=torch.float32, device=DEV)
+    _, _, gs, _ = brq.quantize_lsq(e)
+    q, _, s, _, _ = orc.quantize_lsq(np.zeros((0, 64), np.float32))
+    assert_bitwise(gs, s, "empty scale")
+    # non-finite statistic raises the device flag, per-tensor and per-row
+    bad = np.ones((16, 64), np.float32)
+    bad[3, 5] = np.inf
+    for per_row in (False, True):
+        flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+        brq.quantize_lsq(to_dev(bad), per_row=per_row, flags=flags)
+        assert int(flags.item()) == brq.FLAG_NONFINITE
+    # subnormal inputs read as zero; +-0 keep sign semantics in codes
+    sub = np.full((16, 64), 1.0, np.float32)
+    sub[0, :16] = np.float32(1e-40)
+    sub[1, :16] = -np.float32(1e-40)
+    q, _, s, _, _ = orc.quantize_lsq(sub)
+    gq, _, gs, _ = brq.quantize_lsq(to_dev(sub))
+    assert_bitwise(gq, q, "q subnormal")
+    assert_bitwise(gs, s, "s subnormal")
+
+
+def test_quantize_ties_and_clamps():
+    """Values landing exactly on x*r = k + 1/2 and beyond +-127.5."""
+    say("quantize_ties")
+    rng = np.random.default_rng(5)
+    base = rng.standard_normal((64, 128)).astype(np.float32)
+    q0, _, s0, _, _ = orc.quantize_lsq(base)
+    st = np.float32(s0[0])
+    half = (np.arange(-130, 130, dtype=np.float32) + np.float32(0.5)) * st
+    base.reshape(-1)[:half.size] = half
+    base[10, :8] = np.float32(1000) * st
+    q, _, s, _, _ = orc.quantize_lsq(base)
+    gq, _, gs, _ = brq.quantize_lsq(to_dev(base))
+    assert_bitwise(gq, q, "q ties")
+    assert_bitwise(gs, s, "s ties")
+
+
+# --------------------------------------------------------------------------
+# GEMMs
+# --------------------------------------------------------------------------
+GEMM_TUNES = [dict(gemm_kernel=k, split_k=s) for k, s in
+              [(1, 1), (2, 1), (3, 1), (4, 1), (2, 2), (2, 4), (3, 2), (4, 4)]]
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 2048), (128, 512, 16),
+                                   (333, 515, 1152), (1, 1, 64), (256, 512, 256),
+                                   (1024, 2048, 128)])
+def test_qgemm_fwd(M, N, K):
+    say("qgemm_fwd", M, N, K)
+    rng = np.random.default_rng(M * 7 + N)
+    qx, qw = codes(rng, (M, K)), codes(rng, (N, K))
+    sx = np.array([0.0173], np.float32)
+    sw = (np.abs(rng.standard_normal(N)) * 1e-3 + 1e-4).astype(np.float32)
+    want = orc.qgemm_fwd(qx, sx, qw, sw)
+    want_pt = orc.qgemm_fwd(qx, sx, qw, sw[:1])
+    dqx, dqw, dsx, dsw = to_dev(qx), to_dev(qw), to_dev(sx), to_dev(sw)
+    for t in GEMM_TUNES:
+        assert_bitwise(brq.qgemm_fwd(dqx, dsx, dqw, dsw, tune=t), want, f"y {t}")
+    assert_bitwise(brq.qgemm_fwd(dqx, dsx, dqw, dsw[:1]), want_pt, "y per-tensor w")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (160, 336, 528), (256, 2048, 64)])
+def test_qgemm_bwd_dx(M, N, K):
+    say("qgemm_bwd_dx", M, N, K)
+    rng = np.random.default_rng(N)
+    qg, qw = codes(rng, (M, N)), codes(rng, (N, K))
+    sg = np.array([3.1e-5], np.float32)
+    want = orc.qgemm_bwd_dx(qg, sg, qw)
+    dqg, dqwt, dsg = to_dev(qg), to_dev(np.ascontiguousarray(qw.T)), to_dev(sg)
+    for t in GEMM_TUNES:
+        assert_bitwise(brq.qgemm_bwd_dx(dqg, dsg, dqwt, tune=t), want, f"dx {t}")
+
+
+def test_gemm_extreme_accumulator():
+    """All-127 codes at the int32 bound of the contraction."""
+    say("gemm_extreme")
+    K = 133136  # multiple of 16, <= 133144
+    qx = np.full((2, K), 127, np.int8)
+    qx[1] = -127
+    qw = np.full((3, K), 127, np.int8)
+    one = np.ones(1, np.float32)
+    want = orc.qgemm_fwd(qx, one, qw, np.ones(3, np.float32))
+    for t in GEMM_TUNES:
+        assert_bitwise(brq.qgemm_fwd(to_dev(qx), to_dev(one), to_dev(qw), to_dev(np.ones(3, np.float32)), tune=t),
+                       want, f"extreme {t}")
+
+
+# --------------------------------------------------------------------------
+# Walsh-Hadamard stages and the dW GEMM
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("b", [1, 2, 16, 64, 128])
+def test_wht_quant_x(b):
+    say("wht_quant_x", b)
+    rng = np.random.default_rng(b)
+    M, K = 256, 192
+    qx = codes(rng, (M, K))
+    qu, su, _ = orc.wht_int_quant(qx, b)
+    gqut, gsu = brq.wht_quant_x(to_dev(qx), b)
+    assert_bitwise(gqut, np.ascontiguousarray(qu.T), "q_u^T")
+    assert_bitwise(gsu, np.array([su], np.float32), "s_u")
+
+
+@pytest.mark.parametrize("b", [1, 16, 64, 128])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_wht_quant_dy(b, bf16):
+    say("wht_quant_dy", b, bf16)
+    M, N = 384, 320
+    dy = syn.student_t3((M, N), 1e-3, tag=204, bf16=bf16)
+    qv, sv, _, fl = orc.wht_fp_quant(dy, b)
+    for chunk in (0, 10):
+        flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+        gqvt, gsv = brq.wht_quant_dy(to_dev(dy), b, tune={"chunk_log2": chunk}, flags=flags)
+        assert_bitwise(gqvt, np.ascontiguousarray(qv.T), f"q_v^T chunk {chunk}")
+        assert_bitwise(gsv, np.array([sv], np.float32), "s_v")
+        assert int(flags.item()) == fl == 0
+
+
+@pytest.mark.parametrize("M,N,K,b", [(64, 256, 256, 64), (512, 192, 320, 128), (384, 64, 64, 16)])
+def test_qgemm_bwd_dw_wht(M, N, K, b):
+    say("qgemm_bwd_dw_wht", M, N, K, b)
+    x = syn.normal((M, K), 1.0, tag=205)
+    dy = syn.student_t3((M, N), 1e-3, tag=206, bf16=True)
+    qx, _, sx, _, _ = orc.quantize_lsq(x)
+    want, su, sv, _ = orc.qgemm_bwd_dw_wht(qx, sx, dy, b)
+    dqx, dsx, ddy = to_dev(qx), to_dev(sx), to_dev(dy)
+    for t in GEMM_TUNES[:6]:
+        dw, gsu, gsv = brq.qgemm_bwd_dw_wht(dqx, dsx, ddy, b, tune=t)
+        assert_bitwise(dw, want, f"dw {t}")
+        assert_bitwise(gsu, np.array([su], np.float32), "s_u")
+        assert_bitwise(gsv, np.array([sv], np.float32), "s_v")
+
+
+def test_qgemm_dw_stage_alone():
+    say("qgemm_dw")
+    rng = np.random.default_rng(17)
+    M, N, K, b = 256, 128, 192, 64
+    qv, qu = codes(rng, (M, N)), codes(rng, (M, K))
+    want = orc.dw_gemm(qv, qu, 0.0123, 0.5, 3e-4, b)
+    f = lambda v: to_dev(np.array([v], np.float32))
+    got = brq.qgemm_dw(to_dev(np.ascontiguousarray(qv.T)), to_dev(np.ascontiguousarray(qu.T)),
+                       f(0.0123), f(0.5), f(3e-4), b)
+    assert_bitwise(got, want, "dw stage")
+
+
+# --------------------------------------------------------------------------
+# the whole tiny layer (64 tokens x 256 -> 256), fp32 inputs
+# --------------------------------------------------------------------------
+def test_tiny_layer_chain():
+    say("tiny_layer_chain")
+    d = syn.tiny()
+    x, w, dy, b = d["x"], d["w"], d["dy"], d["block"]
+    X, W, DY = to_dev(x), to_dev(w), to_dev(dy)
+    oqx, _, osx, oax, _ = orc.quantize_lsq(x)
+    oqw, oqwt, osw, oaw, _ = orc.quantize_lsq(w, per_row=True, want_t=True)
+    oy = orc.qgemm_fwd(oqx, osx, oqw, osw)
+    oqg, _, osg, _, _ = orc.quantize_lsq(dy, col_mul=osw)
+    odx = orc.qgemm_bwd_dx(oqg, osg, oqw)
+    odw, osu, osv, _ = orc.qgemm_bwd_dw_wht(oqx, osx, dy, b)
+    qx, _, sx, ax = brq.quantize_lsq(X)
+    qw, qwt, sw, aw = brq.quantize_lsq(W, per_row=True, want_t=True)
+    y = brq.qgemm_fwd(qx, sx, qw, sw)
+    qg, _, sg, _ = brq.quantize_lsq(DY, col_mul=sw)
+    dx = brq.qgemm_bwd_dx(qg, sg, qwt)
+    dw, su, sv, qut, qvt = brq.qgemm_bwd_dw_wht(qx, sx, DY, b, return_codes=True)
+    for name, g, o in [("q_x", qx, oqx), ("s_x", sx, osx), ("amax_x", ax, oax), ("q_w", qw, oqw),
+                       ("q_wt", qwt, oqwt), ("s_w", sw, osw), ("y", y, oy), ("q_g", qg, oqg),
+                       ("s_g", sg, osg), ("dx", dx, odx), ("dw", dw, odw)]:
+        assert_bitwise(g, o, name)
+    qu, _, _ = orc.wht_int_quant(oqx, b)
+    qv, _, _, _ = orc.wht_fp_quant(dy, b)
+    assert_bitwise(qut, np.ascontiguousarray(qu.T), "q_u^T")
+    assert_bitwise(qvt, np.ascontiguousarray(qv.T), "q_v^T")
+    # on-device state hash of the outputs equals the oracle's
+    ts = [("y", y), ("dx", dx), ("dw", dw)]
+    want = orc.hash_state([(n, to_np(t)) for n, t in ts])
+    assert bytes(to_np(brq.hash_state(ts))) == want
+
+
+# --------------------------------------------------------------------------
+# RMSNorm and grad-norm
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,D,bf16", [(100, 2048, True), (64, 264, True), (33, 512, False),
+                                      (17, 4096, True), (8, 8192, True)])
+def test_rmsnorm_fwd(T, D, bf16):
+    say("rmsnorm_fwd", T, D, bf16)
+    x = syn.normal((T, D), 1.0, tag=207, bf16=bf16)
+    if bf16:
+        syn.bf16_subnormals(x, 100, tag=208)
+    g = syn.normal((D,), 0.1, mean=1.0, tag=209, bf16=bf16)
+    y, rstd, fl = orc.rmsnorm_fwd(x, g, 1e-6)
+    gy, grstd = brq.rmsnorm_fixed_fwd(to_dev(x), to_dev(g), 1e-6)
+    assert_bitwise(gy, y, "y")
+    assert_bitwise(grstd, rstd, "rstd")
+
+
+@pytest.mark.parametrize("T,D,bf16", [(100, 2048, True), (64, 264, True), (33, 512, False),
+                                      (70, 4096, True)])
+@pytest.mark.parametrize("rows", [0, 1, 4])
+def test_rmsnorm_bwd(T, D, bf16, rows):
+    say("rmsnorm_bwd", T, D, bf16, rows)
+    x = syn.normal((T, D), 1.0, tag=210, bf16=bf16)
+    if bf16:
+        syn.bf16_subnormals(x, 100, tag=211)
+    g = syn.normal((D,), 0.1, mean=1.0, tag=212, bf16=bf16)
+    dy = syn.normal((T, D), 1e-3, tag=213, bf16=bf16)
+    _, rstd, _ = orc.rmsnorm_fwd(x, g, 1e-6)
+    dx, dg = orc.rmsnorm_bwd(x, g, rstd, dy)
+    gdx, gdg = brq.rmsnorm_fixed_bwd(to_dev(x), to_dev(g), to_dev(rstd), to_dev(dy),
+                                     tune={"rows_per_block": rows})
+    assert_bitwise(gdx, dx, "dx")
+    assert_bitwise(gdg, dg, "dg")
+
+
+@pytest.mark.parametrize("n", [1, 1000, 4096 * 5 + 1664, (1 << 20) + 3])
+@pytest.mark.parametrize("chunk", [0, 10, 14])
+def test_grad_norm(n, chunk):
+    say("grad_norm", n, chunk)
+    v = syn.normal((n,), 1e-4, tag=214)
+    ss, nrm, fl = orc.grad_norm(v)
+    gs, gn = brq.grad_norm(to_dev(v), tune={"chunk_log2": chunk})
+    assert_bitwise(gs, np.array(ss, np.float32), "sumsq")
+    assert_bitwise(gn, np.array(nrm, np.float32), "norm")
+
+
+def test_grad_norm_order_sensitive_vector():
+    """The hand-derived tree vectors, as squares: leaves 4096^2 = 2^24 and
+    ones.  Different reduction orders give different sums here."""
+    say("grad_norm_order")
+    for leaves in ([4096.0, 1, 1, 1], [4096.0, 1, 1], [4096.0, 1, 1, 1, 1, 1, 1]):
+        v = np.array(leaves, np.float32)
+        ss, _, _ = orc.grad_norm(v)
+        gs, _ = brq.grad_norm(to_dev(v))
+        assert_bitwise(gs, np.array(ss, np.float32), f"sumsq {leaves}")
+
+
+# --------------------------------------------------------------------------
+# hash
+# --------------------------------------------------------------------------
+def test_hash_state_vs_oracle():
+    say("hash_state")
+    rng = np.random.default_rng(19)
+    ts = [("y", rng.standard_normal((33, 70)).astype(np.float32)),
+          ("dw", rng.standard_normal((5, 4096 * 3 + 1)).astype(np.float32)),
+          ("x", rng.integers(0, 65535, size=(7, 9), dtype=np.uint16)),
+          ("big", rng.integers(0, 255, size=(4096 * 130 + 77,), dtype=np.uint8)),
+          ("q", np.zeros((0, 4), np.int8))]
+    want = orc.hash_state(ts)
+    dts = []
+    for n, a in ts:
+        t = to_dev(a) if a.dtype != np.uint16 else to_dev(a)
+        dts.append((n, t))
+    got = bytes(to_np(brq.hash_state(dts)))
+    assert got == want
+    ts[1][1].view(np.uint8).reshape(-1)[4097] ^= 1
+    assert bytes(to_np(brq.hash_state([(n, to_dev(a)) for n, a in ts]))) != want
+
+
+# --------------------------------------------------------------------------
+# determinism: repeated calls and concurrent streams
+# --------------------------------------------------------------------------
+def test_repeat_and_streams():
+    say("repeat_and_streams")
+    x = to_dev(syn.normal((1024, 2048), 1.0, tag=215, bf16=True))
+    w = to_dev(syn.normal((768, 2048), 0.02, tag=216, bf16=True))
+    def run():
+        qx, _, sx, _ = brq.quantize_lsq(x, ws=torch.zeros(1 << 22, dtype=torch.uint8, device=DEV))
+        qw, _, sw, _ = brq.quantize_lsq(w, per_row=True)
+        return brq.qgemm_fwd(qx, sx, qw, sw)
+    ref = sha(run())
+    for _ in range(3):
+        assert sha(run()) == ref
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for s in (s1, s2):
+        with torch.cuda.stream(s):
+            outs.append(run())
+    torch.cuda.synchronize()
+    assert all(sha(o) == ref for o in outs)
