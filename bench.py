@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Throughput of one Open-1B decoder layer's bitwise-reproducible W8A8 QAT
+hot path on one MI355X, through libbrq's C ABI.
+
+Workload (one step, 32768 tokens = 8 windows of 4096): the seven W8A8 LSQ
+linears of the layer (Q, K, V, O at 2048/512/512/2048 outputs, gate/up
+2048->8192, down 8192->2048), forward and both backward GEMMs, the weight
+gradient after a Walsh-Hadamard rotation (block 128) along tokens; the
+layer's two fixed-order RMSNorms forward and backward; the global grad-norm
+over the layer's gradients; and the SHA-256 state hash over every output and
+gradient.  Inputs are seeded synthetic tensors (Philox4x32-10), resident in
+HBM before timing starts.
+
+Printed: one JSON line.  value = int8 TOPS of the whole step (2*M*N*K ops
+for each of the 21 GEMMs, divided by the step's wall time);
+tokens_per_s = 32768 / step time.  The roofline object covers the int8 MFMA
+GEMM kernel, timed with HIP events around each GEMM launch on the stream the
+library launches on; cpu_baseline is the plain CPU oracle on a slice of the
+same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "bitwise-exact W8A8 QAT linear fwd+bwd int8 TOPS (% MFMA peak), tokens/s"
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+BLOCK = 128
+EPS = 1e-6
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_ops(linears, M):
+    return sum(3 * 2 * M * N * K for _, K, N, _ in linears)
+
+
+def algorithmic_bytes(linears, inputs, norms, M, arena_elems, hash_bytes):
+    """Algorithmic HBM bytes of each call family over one step.  Per-tensor
+    quantisers need the statistic before any code: 2 reads + 1 int8 write per
+    element; single-pass kernels count 1 read + 1 write."""
+    b = {}
+    b["quant_x"] = sum(M * K * (2 + 2 + 1) for _, K in inputs)
+    b["quant_w"] = sum(N * K * (2 + 1 + 1) for _, K, N, _ in linears)
+    b["quant_g"] = sum(M * N * (2 + 2 + 1) for _, _, N, _ in linears)
+    b["wht_x"] = sum(M * K * (1 + 1 + 1) for _, K in inputs)
+    b["wht_dy"] = sum(M * N * (2 + 2 + 1) for _, _, N, _ in linears)
+    b["rmsnorm_fwd"] = sum(M * D * (2 + 2) + 4 * M for _, D in norms)
+    b["rmsnorm_bwd"] = sum(M * D * (2 + 2 + 2) + 4 * M + 4 * D for _, D in norms)
+    b["grad_norm"] = 4 * arena_elems
+    b["hash_state"] = hash_bytes
+    return b
+
+
+class EventTimer:
+    """HIP events (torch.cuda.Event on the current stream, the stream libbrq
+    launches on) around each call family."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.open = {}
+        self.pairs = {}
+
+    def begin(self, kind):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.open[kind] = e
+
+    def end(self, kind):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(kind, []).append((self.open.pop(kind), e))
+
+    def totals_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) for k, v in self.pairs.items()}
+
+    def counts(self):
+        return {k: len(v) for k, v in self.pairs.items()}
+
+
+def stored_digest(cfg, name):
+    p = os.path.join(ROOT, "tests", "golden", "config_digests.txt")
+    if not os.path.exists(p):
+        return None
+    for line in open(p):
+        f = line.split()
+        if len(f) >= 3 and f[0] == cfg and f[1] == name:
+            return f[2]
+    return None
+
+
+def stored_traffic():
+    """HBM bytes per launch of the GEMM kernel from the rocprofv3 counter
+    summary, valid only while gemm.hip is the source the counters were taken
+    on (its SHA-256 is recorded in the summary)."""
+    p = os.path.join(ROOT, "profiles", "gemm_mfma_layer_counters.md")
+    src = os.path.join(ROOT, "bitwise_reproducible_int8_amd", "csrc", "gemm.hip")
+    if not (os.path.exists(p) and os.path.exists(src)):
+        return None
+    rec = {}
+    for line in open(p):
+        if line.startswith("traffic:"):
+            for kv in line[len("traffic:"):].split():
+                k, _, v = kv.partition("=")
+                rec[k] = v
+    want = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("gemm_hip_sha256") != want or "bytes_per_launch" not in rec:
+        return None
+    return float(rec["bytes_per_launch"])
+
+
+def cpu_baseline(tokens):
+    """The plain CPU oracle on the first `tokens` tokens of the same layer
+    workload: both norms, the seven linears forward and backward, grad-norm
+    over the gradients, state hash (the oracle as written, untuned)."""
+    import numpy as np
+
+    import brq_synth as syn
+    import oracle as orc
+
+    M = tokens
+    xs = {name: syn.layer_input(name, M) for name, _ in syn.LAYER_INPUTS}
+    ws = [syn.layer_weight(i) for i in range(len(syn.LAYER_LINEARS))]
+    dys = [syn.layer_dy(i, M) for i in range(len(syn.LAYER_LINEARS))]
+    nin = [syn.layer_norm_inputs(j, M) for j in range(len(syn.LAYER_NORMS))]
+    t0 = time.perf_counter()
+    outs, arena = [], []
+    nrm = []
+    for (h, g, ndy) in nin:
+        y, rstd, _ = orc.rmsnorm_fwd(h, g, EPS)
+        nrm.append((h, g, ndy, y, rstd))
+    codes = {}
+    for name, x in xs.items():
+        qx, _, sx, _, _ = orc.quantize_lsq(x)
+        codes[name] = [qx, sx, None, None]
+    ys, qws = [], []
+    for i, (lname, K, N, xin) in enumerate(syn.LAYER_LINEARS):
+        qx, sx = codes[xin][:2]
+        qw, _, sw, _, _ = orc.quantize_lsq(ws[i], per_row=True)
+        qws.append((qw, sw))
+        ys.append(orc.qgemm_fwd(qx, sx, qw, sw))
+    dxs = []
+    for i in range(len(syn.LAYER_LINEARS)):
+        qw, sw = qws[i]
+        qg, _, sg, _, _ = orc.quantize_lsq(dys[i], col_mul=sw)
+        dxs.append(orc.qgemm_bwd_dx(qg, sg, qw))
+    for name in xs:
+        qu, su, _ = orc.wht_int_quant(codes[name][0], BLOCK)
+        codes[name][2:] = [qu, su]
+    dws = []
+    for i, (lname, K, N, xin) in enumerate(syn.LAYER_LINEARS):
+        qx, sx, qu, su = codes[xin]
+        qv, sv, _, _ = orc.wht_fp_quant(dys[i], BLOCK)
+        dws.append(orc.dw_gemm(qv, qu, sx[0], su, sv, BLOCK))
+        arena.append(dws[-1].reshape(-1))
+    for i, (lname, _, _, _) in enumerate(syn.LAYER_LINEARS):
+        outs += [(f"{lname}.y", ys[i]), (f"{lname}.dx", dxs[i]), (f"{lname}.dw", dws[i])]
+    for j, (nname, _) in enumerate(syn.LAYER_NORMS):
+        h, g, ndy, y, rstd = nrm[j]
+        dx, dg = orc.rmsnorm_bwd(h, g, rstd, ndy)
+        arena.append(dg)
+        outs += [(f"{nname}.y", y), (f"{nname}.dx", dx), (f"{nname}.dg", dg)]
+    ss, n2, _ = orc.grad_norm(np.concatenate(arena))
+    outs.append(("grad_norm", np.array([ss, n2], np.float32)))
+    orc.hash_state(outs)
+    dt = time.perf_counter() - t0
+    ops = gemm_ops(syn.LAYER_LINEARS, M)
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": (f"the whole layer step (2 RMSNorms, 7 W8A8 linears fwd+bwd with WHT, "
+                       f"grad-norm, state hash) on the first {M} of 32768 tokens; "
+                       f"{dt:.2f} s wall, {M / dt:.1f} tokens/s"),
+            "tokens_per_s": round(M / dt, 3), "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=32768,
+                    help="tokens per step (a multiple of 128; 32768 is the measured workload)")
+    ap.add_argument("--cpu-tokens", type=int, default=512,
+                    help="tokens of the CPU-oracle sample (0 skips it)")
+    ap.add_argument("--no-instrument", action="store_true",
+                    help="skip the per-call event pass (for profiler runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the multi-GPU exchange is not part of this library)", file=sys.stderr)
+        sys.exit(2)
+    if args.tokens % BLOCK or args.tokens <= 0:
+        sys.exit("--tokens must be a positive multiple of 128")
+
+    import numpy as np
+    import torch
+
+    import brq_synth as syn
+    import bitwise_reproducible_int8_amd as brq
+    from bitwise_reproducible_int8_amd.layer import LayerStep
+
+    dev = torch.device("cuda:0")
+    brq.lib()  # fails loudly when the HIP library is missing
+    M = args.tokens
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t_gen = time.perf_counter()
+    x = {name: up(syn.layer_input(name, M)) for name, _ in syn.LAYER_INPUTS}
+    w = [up(syn.layer_weight(i)) for i in range(len(syn.LAYER_LINEARS))]
+    dy = [up(syn.layer_dy(i, M)) for i in range(len(syn.LAYER_LINEARS))]
+    norms = []
+    for j, (nname, _) in enumerate(syn.LAYER_NORMS):
+        h, g, ndy = syn.layer_norm_inputs(j, M)
+        norms.append((nname, up(h), up(g), up(ndy)))
+    step = LayerStep(syn.LAYER_LINEARS, x, w, dy, norms, block=BLOCK, eps=EPS)
+    torch.cuda.synchronize()
+    log(f"inputs generated and resident in {time.perf_counter() - t_gen:.1f} s")
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, nothing else enqueued
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step.run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (host wall {1e3 * wall / args.steps:.3f})")
+
+    digest = bytes(step.digest.cpu().numpy()).hex()
+    flags = int(step.flags.item())
+    want = stored_digest("layer", "state") if M == 32768 else None
+    exact = None if want is None else (digest == want and flags == 0)
+
+    ops = gemm_ops(syn.LAYER_LINEARS, M)
+    tops = ops / (ms * 1e-3) / 1e12
+
+    # per-call HIP-event pass over K more steps: kernel-family durations
+    kernels, roofline, hash_off_ms = {}, None, None
+    if not args.no_instrument:
+        timer = EventTimer(torch)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            step.run(timer=timer)
+        torch.cuda.synchronize()
+        tot, cnt = timer.totals_ms(), timer.counts()
+        hash_bytes = sum(t.numel() * t.element_size() for _, t in step.hash_list())
+        ab = algorithmic_bytes(syn.LAYER_LINEARS, syn.LAYER_INPUTS, syn.LAYER_NORMS, M,
+                               step.arena.numel(), hash_bytes)
+        per_step = {k: v / args.steps for k, v in tot.items()}
+        gemm_ms = sum(per_step[k] for k in ("gemm_fwd", "gemm_dx", "gemm_dw"))
+        for k, v in sorted(per_step.items()):
+            d = {"ms_per_step": round(v, 4), "launches_per_step": cnt[k] // args.steps}
+            if k.startswith("gemm"):
+                fam = {"gemm_fwd": 1, "gemm_dx": 1, "gemm_dw": 1}
+                share = sum(2 * M * N * K for _, K, N, _ in syn.LAYER_LINEARS) * fam[k]
+                d["tops"] = round(share / (v * 1e-3) / 1e12, 2)
+                d["frac_peak"] = round(d["tops"] / PEAK_INT8_TOPS, 4)
+            elif k in ab:
+                gbs = ab[k] / (v * 1e-3) / 1e9
+                d["gb_per_s"] = round(gbs, 1)
+                if k == "hash_state":
+                    d["bound"] = "alu"
+                else:
+                    d["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
+                d["algorithmic_bytes"] = ab[k]
+            kernels[k] = d
+        n_gemm = sum(cnt[k] for k in ("gemm_fwd", "gemm_dx", "gemm_dw")) // args.steps
+        achieved = ops / (gemm_ms * 1e-3) / 1e12
+        traffic = stored_traffic()
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                    "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                    "traffic": traffic,
+                    "kernel": "k_gemm_mfma<128,128,2,2> (int8 MFMA 16x16x64, fp32 dequant)",
+                    "launches_per_step": n_gemm,
+                    "avg_launch_us": round(1e3 * gemm_ms / n_gemm, 2),
+                    "algorithmic_ops_per_launch": ops / n_gemm}
+        hash_off_ms = ms - per_step.get("hash_state", 0.0)
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(args.cpu_tokens)
+
+    line = {
+        "metric": METRIC, "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (seeded Philox4x32-10, the workload's shapes and distributions)",
+        "config": {"workload": "open1b_layer_w8a8_qat_fwd_bwd", "tokens": M,
+                   "windows": M // 4096 if M % 4096 == 0 else None, "d_model": 2048,
+                   "linears": "q,k,v,o 2048->2048/512/512/2048; gate,up 2048->8192; down 8192->2048",
+                   "hadamard_block": BLOCK, "rmsnorms": 2, "state_hash": True,
+                   "int8_ops_per_step": ops},
+        "tokens_per_s": round(M / (ms * 1e-3), 1),
+        "frac_mfma_peak_step": round(tops / PEAK_INT8_TOPS, 4),
+        "tokens_per_s_hash_off": None if hash_off_ms is None else round(M / (hash_off_ms * 1e-3), 1),
+        "bitwise_exact": exact, "state_digest": digest,
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -126,6 +126,15 @@ def _dev(t: torch.Tensor, name: str):
         raise BrqError(f"{name} must be contiguous")
 
 
+def _out(t, shape, dtype, name):
+    """Check a caller-provided output tensor: device, contiguous, exact shape
+    and dtype (a wrong shape would let a kernel write past its end)."""
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise BrqError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    return t
+
+
 def _fp_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return F32
@@ -172,15 +181,32 @@ def _ws(nbytes, device, ws):
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
-def quantize_lsq(x, per_row=False, col_mul=None, want_t=False, tune=None, ws=None, flags=None):
-    """LSQ int8 quantisation.  Returns (q, q_t or None, scale, amax)."""
+def quantize_lsq(x, per_row=False, col_mul=None, want_t=False, tune=None, ws=None, flags=None,
+                 out=None):
+    """LSQ int8 quantisation.  Returns (q, q_t or None, scale, amax).
+    ``out`` may hold preallocated (q, q_t, scale, amax); a None entry is
+    allocated here (q_t only when want_t)."""
     _dev(x, "x")
     rows, cols = x.shape
-    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
-    q_t = torch.empty((cols, rows), dtype=torch.int8, device=x.device) if want_t else None
     ns = rows if per_row else 1
-    scale = torch.empty(ns, dtype=torch.float32, device=x.device)
-    amax = torch.empty(ns, dtype=torch.float32, device=x.device)
+    q, q_t, scale, amax = out if out is not None else (None, None, None, None)
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if q_t is None and want_t:
+        q_t = torch.empty((cols, rows), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty(ns, dtype=torch.float32, device=x.device)
+    if amax is None:
+        amax = torch.empty(ns, dtype=torch.float32, device=x.device)
+    for t, shape, dt, name in ((q, (rows, cols), torch.int8, "q"), (scale, (ns,), torch.float32, "scale"),
+                               (amax, (ns,), torch.float32, "amax")):
+        _dev(t, name)
+        if tuple(t.shape) != shape or t.dtype != dt:
+            raise BrqError(f"{name}: expected {dt} {shape}, got {t.dtype} {tuple(t.shape)}")
+    if q_t is not None:
+        _dev(q_t, "q_t")
+        if tuple(q_t.shape) != (cols, rows) or q_t.dtype != torch.int8:
+            raise BrqError("q_t: expected int8 (cols, rows)")
     if col_mul is not None:
         _dev(col_mul, "col_mul")
     need = workspace_size(OP_QUANTIZE, rows, cols, tune=tune)
@@ -196,7 +222,10 @@ def qgemm_fwd(q_x, s_x, q_w, s_w, tune=None, out=None, ws=None):
     _dev(q_x, "q_x"); _dev(q_w, "q_w")
     M, K = q_x.shape
     N = q_w.shape[0]
-    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=q_x.device)
+    if q_w.shape[1] != K:
+        raise BrqError("q_w: contraction length differs from q_x")
+    y = _out(out, (M, N), torch.float32, "y") if out is not None else \
+        torch.empty((M, N), dtype=torch.float32, device=q_x.device)
     need = workspace_size(OP_QGEMM, M, N, K, tune=tune)
     w = _ws(need, q_x.device, ws) if need else None
     _check(lib().brq_qgemm_fwd(_ptr(q_x), _ptr(s_x), _ptr(q_w), _ptr(s_w), int(s_w.numel() > 1),
@@ -209,7 +238,10 @@ def qgemm_bwd_dx(q_g, s_g, q_wt, tune=None, out=None, ws=None):
     _dev(q_g, "q_g"); _dev(q_wt, "q_wt")
     M, N = q_g.shape
     K = q_wt.shape[0]
-    dx = out if out is not None else torch.empty((M, K), dtype=torch.float32, device=q_g.device)
+    if q_wt.shape[1] != N:
+        raise BrqError("q_wt: contraction length differs from q_g")
+    dx = _out(out, (M, K), torch.float32, "dx") if out is not None else \
+        torch.empty((M, K), dtype=torch.float32, device=q_g.device)
     need = workspace_size(OP_QGEMM, M, K, N, tune=tune)
     w = _ws(need, q_g.device, ws) if need else None
     _check(lib().brq_qgemm_bwd_dx(_ptr(q_g), _ptr(s_g), _ptr(q_wt), M, N, K, _ptr(dx), _ptr(w),
@@ -225,7 +257,10 @@ def qgemm_bwd_dw_wht(q_x, s_x, dy, block, tune=None, out=None, ws=None, flags=No
     _dev(q_x, "q_x"); _dev(dy, "dy")
     M, K = q_x.shape
     N = dy.shape[1]
-    dw = out if out is not None else torch.empty((N, K), dtype=torch.float32, device=q_x.device)
+    if dy.shape[0] != M:
+        raise BrqError("dy: token count differs from q_x")
+    dw = _out(out, (N, K), torch.float32, "dw") if out is not None else \
+        torch.empty((N, K), dtype=torch.float32, device=q_x.device)
     s_u = torch.empty(1, dtype=torch.float32, device=q_x.device)
     s_v = torch.empty(1, dtype=torch.float32, device=q_x.device)
     need = workspace_size(OP_DW_WHT, M, N, K, block, tune=tune)
@@ -241,11 +276,16 @@ def qgemm_bwd_dw_wht(q_x, s_x, dy, block, tune=None, out=None, ws=None, flags=No
     return dw, s_u, s_v, q_ut, q_vt
 
 
-def wht_quant_x(q_x, block, tune=None, ws=None):
+def wht_quant_x(q_x, block, tune=None, ws=None, out=None):
+    """Returns (q_ut [K][M], s_u); ``out`` may hold preallocated (q_ut, s_u)."""
     _dev(q_x, "q_x")
     M, K = q_x.shape
-    q_ut = torch.empty((K, M), dtype=torch.int8, device=q_x.device)
-    s_u = torch.empty(1, dtype=torch.float32, device=q_x.device)
+    q_ut, s_u = out if out is not None else (None, None)
+    q_ut = torch.empty((K, M), dtype=torch.int8, device=q_x.device) if q_ut is None else q_ut
+    s_u = torch.empty(1, dtype=torch.float32, device=q_x.device) if s_u is None else s_u
+    _dev(q_ut, "q_ut")
+    if tuple(q_ut.shape) != (K, M) or q_ut.dtype != torch.int8:
+        raise BrqError("q_ut: expected int8 (K, M)")
     need = workspace_size(OP_DW_WHT, M, 64, K, block, tune=tune)
     w = _ws(need, q_x.device, ws)
     _check(lib().brq_wht_quant_x(_ptr(q_x), M, K, block, _ptr(q_ut), _ptr(s_u), _ptr(w), w.numel(),
@@ -253,11 +293,16 @@ def wht_quant_x(q_x, block, tune=None, ws=None):
     return q_ut, s_u
 
 
-def wht_quant_dy(dy, block, tune=None, ws=None, flags=None):
+def wht_quant_dy(dy, block, tune=None, ws=None, flags=None, out=None):
+    """Returns (q_vt [N][M], s_v); ``out`` may hold preallocated (q_vt, s_v)."""
     _dev(dy, "dy")
     M, N = dy.shape
-    q_vt = torch.empty((N, M), dtype=torch.int8, device=dy.device)
-    s_v = torch.empty(1, dtype=torch.float32, device=dy.device)
+    q_vt, s_v = out if out is not None else (None, None)
+    q_vt = torch.empty((N, M), dtype=torch.int8, device=dy.device) if q_vt is None else q_vt
+    s_v = torch.empty(1, dtype=torch.float32, device=dy.device) if s_v is None else s_v
+    _dev(q_vt, "q_vt")
+    if tuple(q_vt.shape) != (N, M) or q_vt.dtype != torch.int8:
+        raise BrqError("q_vt: expected int8 (N, M)")
     need = workspace_size(OP_DW_WHT, M, N, 64, block, tune=tune)
     w = _ws(need, dy.device, ws)
     _check(lib().brq_wht_quant_dy(_ptr(dy), _fp_code(dy), M, N, block, _ptr(q_vt), _ptr(s_v),
@@ -270,7 +315,10 @@ def qgemm_dw(q_vt, q_ut, s_x, s_u, s_v, block, tune=None, out=None, ws=None):
     _dev(q_vt, "q_vt"); _dev(q_ut, "q_ut")
     N, M = q_vt.shape
     K = q_ut.shape[0]
-    dw = out if out is not None else torch.empty((N, K), dtype=torch.float32, device=q_vt.device)
+    if q_ut.shape[1] != M:
+        raise BrqError("q_ut: token count differs from q_vt")
+    dw = _out(out, (N, K), torch.float32, "dw") if out is not None else \
+        torch.empty((N, K), dtype=torch.float32, device=q_vt.device)
     need = workspace_size(OP_QGEMM, N, K, M, tune=tune)
     w = _ws(need, q_vt.device, ws) if need else None
     _check(lib().brq_qgemm_dw(_ptr(q_vt), _ptr(q_ut), _ptr(s_x), _ptr(s_u), _ptr(s_v), M, N, K,
@@ -279,22 +327,32 @@ def qgemm_dw(q_vt, q_ut, s_x, s_u, s_v, block, tune=None, out=None, ws=None):
     return dw
 
 
-def rmsnorm_fixed_fwd(x, g, eps=1e-6, flags=None, tune=None):
+def rmsnorm_fixed_fwd(x, g, eps=1e-6, flags=None, tune=None, out=None):
+    """Returns (y, rstd); ``out`` may hold preallocated (y, rstd)."""
     _dev(x, "x"); _dev(g, "g")
     T, D = x.shape
-    y = torch.empty_like(x)
-    rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    y, rstd = out if out is not None else (None, None)
+    y = torch.empty_like(x) if y is None else y
+    rstd = torch.empty(T, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _dev(y, "y"); _dev(rstd, "rstd")
+    if y.shape != x.shape or y.dtype != x.dtype or rstd.numel() != T:
+        raise BrqError("rmsnorm_fixed_fwd: output shapes")
     _check(lib().brq_rmsnorm_fixed_fwd(_ptr(x), _ptr(g), _fp_code(x), T, D, eps, _ptr(y),
                                        _ptr(rstd), _ptr(flags), _tune(tune), _stream()),
            "rmsnorm_fixed_fwd")
     return y, rstd
 
 
-def rmsnorm_fixed_bwd(x, g, rstd, dy, tune=None, ws=None):
+def rmsnorm_fixed_bwd(x, g, rstd, dy, tune=None, ws=None, out=None):
+    """Returns (dx, dg); ``out`` may hold preallocated (dx, dg)."""
     _dev(x, "x"); _dev(g, "g"); _dev(rstd, "rstd"); _dev(dy, "dy")
     T, D = x.shape
-    dx = torch.empty_like(x)
-    dg = torch.empty(D, dtype=torch.float32, device=x.device)
+    dx, dg = out if out is not None else (None, None)
+    dx = torch.empty_like(x) if dx is None else dx
+    dg = torch.empty(D, dtype=torch.float32, device=x.device) if dg is None else dg
+    _dev(dx, "dx"); _dev(dg, "dg")
+    if dx.shape != x.shape or dx.dtype != x.dtype or dg.numel() != D or dg.dtype != torch.float32:
+        raise BrqError("rmsnorm_fixed_bwd: output shapes")
     need = workspace_size(OP_RMSNORM_BWD, T, D, tune=tune)
     w = _ws(need, x.device, ws)
     _check(lib().brq_rmsnorm_fixed_bwd(_ptr(x), _ptr(g), _ptr(rstd), _ptr(dy), _fp_code(x), T, D,

@@ -1,0 +1,200 @@
+"""One decoder layer's data-parallel hot path as a fixed sequence of libbrq
+calls on preallocated device buffers (composition and marshalling only:
+every step runs in libbrq's HIP kernels).
+
+The layer is the Open-1B block shape (report §3.1 "Architecture", Table 3:
+d_model 2048, GQA 16 query / 4 KV heads of 128, SwiGLU): seven W8A8 linears
+(§3.2 "int8 computation") and the two pre-norm RMSNorms, over one rank's
+micro-batch of tokens.  One call of :meth:`LayerStep.run` enqueues, on
+torch's current stream:
+
+  1. RMSNorm forward of each norm input                       (rmsnorm_fixed)
+  2. per-tensor LSQ codes of each distinct linear input        (quantize_lsq)
+  3. per-output-channel LSQ codes of each weight, plus the
+     transposed copy for the input-gradient GEMM, then the
+     forward GEMM + dequantisation                             (qgemm_fwd)
+  4. dY scaled by the weight step sizes and quantised, then
+     the input-gradient GEMM                                   (qgemm_bwd_dx)
+  5. Walsh-Hadamard rotation + requantisation of each distinct
+     activation code and of each dY along tokens, then the
+     weight-gradient GEMM into the gradient arena              (qgemm_bwd_dw_wht,
+                                                                in its three stages)
+  6. RMSNorm backward of each norm into the arena              (rmsnorm_fixed)
+  7. global l2 norm over the gradient arena                     (grad_norm)
+  8. SHA-256 state hash of every output and gradient          (hash_state)
+
+The rotated code of an activation depends on that activation alone, so
+linears that share an input (Q/K/V, gate/up) share one rotation; the results
+are the same bits as the one-call qgemm_bwd_dw_wht per linear.
+
+Gradient arena: one fp32 buffer holding, in order, dW of every linear
+([N][K] row-major each) and then dg of every norm; grad_norm reduces it as
+one vector in that order.
+
+State hash tensors, in order: for each linear "<name>.y", "<name>.dx",
+"<name>.dw"; for each norm "<name>.y", "<name>.dx", "<name>.dg"; then
+"grad_norm" = [sum of squares, norm] (fp32).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (BrqError, OP_DW_WHT, OP_GRAD_NORM, OP_QGEMM, OP_QUANTIZE, OP_RMSNORM_BWD,
+               grad_norm, hash_state, hash_state_workspace_size, qgemm_bwd_dx, qgemm_dw,
+               qgemm_fwd, quantize_lsq, rmsnorm_fixed_bwd, rmsnorm_fixed_fwd, wht_quant_dy,
+               wht_quant_x, workspace_size)
+
+
+class _NoTimer:
+    def begin(self, kind):
+        pass
+
+    def end(self, kind):
+        pass
+
+
+class LayerStep:
+    """Buffers and call sequence of one layer step.
+
+    linears: list of (name, in_features K, out_features N, input name)
+    x:       dict input name -> bf16/fp32 device tensor [M][K]
+    w:       list of device tensors [N][K] (nn.Linear layout), one per linear
+    dy:      list of device tensors [M][N], one per linear
+    norms:   list of (name, h [M][D], g [D], dy [M][D]) device tensors
+    """
+
+    def __init__(self, linears, x, w, dy, norms=(), block=128, eps=1e-6, tune=None):
+        self.linears = list(linears)
+        self.x, self.w, self.dy = x, list(w), list(dy)
+        self.norms = list(norms)
+        self.block, self.eps, self.tune = block, eps, tune
+        first = next(iter(x.values()))
+        dev = first.device
+        self.device = dev
+        M = first.shape[0]
+        self.M = M
+        if len(self.w) != len(self.linears) or len(self.dy) != len(self.linears):
+            raise BrqError("one weight and one dY per linear")
+        for i, (name, K, N, xin) in enumerate(self.linears):
+            if tuple(x[xin].shape) != (M, K):
+                raise BrqError(f"{name}: input {xin} is not [{M}, {K}]")
+            if tuple(self.w[i].shape) != (N, K) or tuple(self.dy[i].shape) != (M, N):
+                raise BrqError(f"{name}: weight or dY shape")
+        i8, f32 = torch.int8, torch.float32
+        e = lambda *s, dt=f32: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+        self.flags = torch.zeros(1, dtype=torch.int32, device=dev)
+        # activation codes and rotated codes, one per distinct input
+        self.q_x, self.s_x, self.amax_x, self.q_ut, self.s_u = {}, {}, {}, {}, {}
+        for xin, t in x.items():
+            K = t.shape[1]
+            self.q_x[xin], self.s_x[xin], self.amax_x[xin] = e(M, K, dt=i8), e(1), e(1)
+            self.q_ut[xin], self.s_u[xin] = e(K, M, dt=i8), e(1)
+        # per linear
+        self.q_w, self.q_wt, self.s_w, self.amax_w = [], [], [], []
+        self.y, self.q_g, self.s_g, self.amax_g, self.dx = [], [], [], [], []
+        self.q_vt, self.s_v = [], []
+        sizes = [N * K for _, K, N, _ in self.linears] + [h.shape[1] for _, h, _, _ in self.norms]
+        self.arena = e(sum(sizes))
+        off = 0
+        self.dw = []
+        for (name, K, N, _xin) in self.linears:
+            self.q_w.append(e(N, K, dt=i8)); self.q_wt.append(e(K, N, dt=i8))
+            self.s_w.append(e(N)); self.amax_w.append(e(N))
+            self.y.append(e(M, N))
+            self.q_g.append(e(M, N, dt=i8)); self.s_g.append(e(1)); self.amax_g.append(e(1))
+            self.dx.append(e(M, K))
+            self.q_vt.append(e(N, M, dt=i8)); self.s_v.append(e(1))
+            self.dw.append(self.arena[off:off + N * K].view(N, K))
+            off += N * K
+        self.ny, self.nrstd, self.ndx, self.ndg = [], [], [], []
+        for (_name, h, g, ndy) in self.norms:
+            T, D = h.shape
+            if T != M or tuple(g.shape) != (D,) or tuple(ndy.shape) != (T, D):
+                raise BrqError("norm shapes")
+            self.ny.append(torch.empty_like(h)); self.nrstd.append(e(T))
+            self.ndx.append(torch.empty_like(h))
+            self.ndg.append(self.arena[off:off + D])
+            off += D
+        self.gn = e(2)
+        self.digest = torch.empty(32, dtype=torch.uint8, device=dev)
+        # one workspace, large enough for every call (calls are stream-ordered)
+        need = [workspace_size(OP_GRAD_NORM, self.arena.numel(), tune=tune)]
+        for xin, t in x.items():
+            need.append(workspace_size(OP_QUANTIZE, *t.shape, tune=tune))
+            need.append(workspace_size(OP_DW_WHT, M, 64, t.shape[1], block, tune=tune))
+        for (name, K, N, _xin) in self.linears:
+            need += [workspace_size(OP_QUANTIZE, M, N, tune=tune),
+                     workspace_size(OP_QGEMM, M, N, K, tune=tune),
+                     workspace_size(OP_QGEMM, M, K, N, tune=tune),
+                     workspace_size(OP_QGEMM, N, K, M, tune=tune),
+                     workspace_size(OP_DW_WHT, M, N, 64, block, tune=tune)]
+        for (_n, h, _g, _d) in self.norms:
+            need.append(workspace_size(OP_RMSNORM_BWD, *h.shape, tune=tune))
+        need.append(hash_state_workspace_size(self.hash_list()))
+        self.ws = torch.zeros(max(need), dtype=torch.uint8, device=dev)
+
+    # -- the state-hash contents, in order ------------------------------------
+    def hash_list(self):
+        out = []
+        for i, (name, _K, _N, _x) in enumerate(self.linears):
+            out += [(f"{name}.y", self.y[i]), (f"{name}.dx", self.dx[i]), (f"{name}.dw", self.dw[i])]
+        for j, (name, _h, _g, _d) in enumerate(self.norms):
+            out += [(f"{name}.y", self.ny[j]), (f"{name}.dx", self.ndx[j]),
+                    (f"{name}.dg", self.ndg[j])]
+        out.append(("grad_norm", self.gn))
+        return out
+
+    # -- one step --------------------------------------------------------------
+    def run(self, timer=None, hash_outputs=True):
+        T = timer or _NoTimer()
+        tune, ws, fl, b = self.tune, self.ws, self.flags, self.block
+        for j, (_name, h, g, _d) in enumerate(self.norms):
+            T.begin("rmsnorm_fwd")
+            rmsnorm_fixed_fwd(h, g, self.eps, flags=fl, tune=tune, out=(self.ny[j], self.nrstd[j]))
+            T.end("rmsnorm_fwd")
+        for xin, t in self.x.items():
+            T.begin("quant_x")
+            quantize_lsq(t, tune=tune, ws=ws, flags=fl,
+                         out=(self.q_x[xin], None, self.s_x[xin], self.amax_x[xin]))
+            T.end("quant_x")
+        for i, (_name, _K, _N, xin) in enumerate(self.linears):
+            T.begin("quant_w")
+            quantize_lsq(self.w[i], per_row=True, want_t=True, tune=tune, ws=ws, flags=fl,
+                         out=(self.q_w[i], self.q_wt[i], self.s_w[i], self.amax_w[i]))
+            T.end("quant_w")
+            T.begin("gemm_fwd")
+            qgemm_fwd(self.q_x[xin], self.s_x[xin], self.q_w[i], self.s_w[i], tune=tune,
+                      out=self.y[i], ws=ws)
+            T.end("gemm_fwd")
+        for i in range(len(self.linears)):
+            T.begin("quant_g")
+            quantize_lsq(self.dy[i], col_mul=self.s_w[i], tune=tune, ws=ws, flags=fl,
+                         out=(self.q_g[i], None, self.s_g[i], self.amax_g[i]))
+            T.end("quant_g")
+            T.begin("gemm_dx")
+            qgemm_bwd_dx(self.q_g[i], self.s_g[i], self.q_wt[i], tune=tune, out=self.dx[i], ws=ws)
+            T.end("gemm_dx")
+        for xin in self.x:
+            T.begin("wht_x")
+            wht_quant_x(self.q_x[xin], b, tune=tune, ws=ws, out=(self.q_ut[xin], self.s_u[xin]))
+            T.end("wht_x")
+        for i, (_name, _K, _N, xin) in enumerate(self.linears):
+            T.begin("wht_dy")
+            wht_quant_dy(self.dy[i], b, tune=tune, ws=ws, flags=fl, out=(self.q_vt[i], self.s_v[i]))
+            T.end("wht_dy")
+            T.begin("gemm_dw")
+            qgemm_dw(self.q_vt[i], self.q_ut[xin], self.s_x[xin], self.s_u[xin], self.s_v[i], b,
+                     tune=tune, out=self.dw[i], ws=ws)
+            T.end("gemm_dw")
+        for j, (_name, h, g, ndy) in enumerate(self.norms):
+            T.begin("rmsnorm_bwd")
+            rmsnorm_fixed_bwd(h, g, self.nrstd[j], ndy, tune=tune, ws=ws,
+                              out=(self.ndx[j], self.ndg[j]))
+            T.end("rmsnorm_bwd")
+        T.begin("grad_norm")
+        grad_norm(self.arena, flags=fl, tune=tune, ws=ws, out=self.gn)
+        T.end("grad_norm")
+        if hash_outputs:
+            T.begin("hash_state")
+            hash_state(self.hash_list(), ws=ws, out=self.digest)
+            T.end("hash_state")

@@ -20,7 +20,10 @@ micro-batches; §3.1 Table 3, §3.2 "Batch size"):
   norm   x bf16 [32768,2048] N(0,1) with 1% bf16 subnormals; g bf16 [2048]
          1+N(0,0.1); dy bf16 [32768,2048] N(0,1e-3); grad vector fp32
          [1.61e9] N(0,1e-4)
-  layer  seven linears of one decoder layer over 32768 tokens
+  layer  seven linears of one decoder layer over 32768 tokens (8 windows of
+         4096): inputs bf16 N(0,1), weights bf16 N(0,0.02), dY per linear bf16
+         N(0,1e-3); plus the layer's two RMSNorms at the norm recipe's
+         distributions (h with 1% bf16 subnormals, g 1+N(0,0.1), dy N(0,1e-3))
 """
 from __future__ import annotations
 
@@ -188,3 +191,19 @@ def layer_weight(i, seed=SEED):
 def layer_dy(i, M=32768, seed=SEED):
     _, _, N, _ = LAYER_LINEARS[i]
     return normal((M, N), 1e-3, tag=tag_for(i, TAG_DY), bf16=True, seed=seed)
+
+
+# the layer's two pre-norm RMSNorms: (name, width)
+LAYER_NORMS = [("attn_norm", 2048), ("mlp_norm", 2048)]
+
+
+def layer_norm_inputs(j, M=32768, seed=SEED):
+    """(h, g, dy) of norm j: h bf16 N(0,1) with 1% bf16 subnormals, g bf16
+    1+N(0,0.1), dy bf16 N(0,1e-3)."""
+    D = LAYER_NORMS[j][1]
+    base = 20 + j
+    h = normal((M, D), 1.0, tag=tag_for(base, TAG_X), bf16=True, seed=seed)
+    bf16_subnormals(h, 100, tag=tag_for(base, TAG_SUBN), seed=seed)
+    g = normal((D,), 0.1, mean=1.0, tag=tag_for(base, TAG_G), bf16=True, seed=seed)
+    dy = normal((M, D), 1e-3, tag=tag_for(base, TAG_DY), bf16=True, seed=seed)
+    return h, g, dy

@@ -30,6 +30,8 @@ def lib():
             _b.build()
         L = C.CDLL(LIB_PATH)
         vp, i64, f32, i32 = C.c_void_p, C.c_int64, C.c_float, C.c_int
+        L.orc_num_threads.restype = i32
+        L.orc_num_threads.argtypes = []
         L.orc_flush.restype = f32
         L.orc_flush.argtypes = [f32]
         L.orc_bf16_to_f32.restype = f32
@@ -95,6 +97,10 @@ def _dtype_code(a: np.ndarray) -> int:
 def _c(a, dt=None):
     a = np.ascontiguousarray(a if dt is None else a.astype(dt, copy=False))
     return a
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
 
 
 def flush(v: float) -> float:
@@ -265,6 +271,18 @@ def merkle_root(a: np.ndarray) -> bytes:
 
 _DT = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.int8): I8,
        np.dtype(np.int32): I32, np.dtype(np.uint8): U8}
+
+
+def tensor_digest(name: str, a: np.ndarray, code=None) -> bytes:
+    """Digest of one tensor: SHA-256 over the typed header and the Merkle
+    root of its raw bytes (the per-tensor part of hash_state)."""
+    a = np.ascontiguousarray(a)
+    code = _DT[a.dtype] if code is None else code
+    buf = a.view(np.uint8).reshape(-1) if a.size else np.zeros(1, np.uint8)
+    dims = np.array(a.shape if a.ndim else [0], np.int64)
+    out = np.zeros(32, np.uint8)
+    lib().orc_tensor_digest(_p(buf), a.nbytes, code, a.ndim, _p(dims), name.encode(), _p(out))
+    return out.tobytes()
 
 
 def hash_state(tensors):

@@ -20,6 +20,17 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* Threads the OpenMP loops over independent outputs may use (1 without
+ * OpenMP); reported next to the oracle's timings. */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------------
  * Arithmetic model -- §2.1 "Subnormals", "Fused multiply-add", Table 1.
  * Each helper performs exactly one IEEE binary32 operation and then flushes

@@ -59,6 +59,9 @@ enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_I32 = 3, ORC_U8 = 4 };
 enum { ORC_PER_TENSOR = 0, ORC_PER_ROW = 1 };
 enum { ORC_FLAG_NONFINITE = 1 };
 
+/* OpenMP threads available to the loops over independent outputs. */
+int orc_num_threads(void);
+
 /* ---- arithmetic model helpers, exported so the pins can probe them ---- */
 float orc_flush(float v);                 /* subnormal -> signed zero */
 float orc_bf16_to_f32(uint16_t h);        /* exact widen, then DAZ */

@@ -1,0 +1,192 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (default tune): every output's SHA-256 against the digests
+the CPU oracle wrote (tests/golden/config_digests.txt, produced by
+tests/golden/make_digests.py from oracle/ alone), plus outputs the oracle
+recomputes here row by row, so a mismatch names where it is.
+
+Workloads (seeded synthetic inputs, brq_synth):
+  qkv    4096 tokens x 2048 -> 3072 forward, per-channel and per-tensor W
+  mlp    16384 tokens x 2048 -> 8192 forward + backward, Hadamard block 128
+  norm   RMSNorm 32768 x 2048 forward + backward; grad-norm over 1.61e9
+  layer  one decoder layer's step over 32768 tokens (the benchmark step)
+"""
+import hashlib
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import brq_synth as syn
+import oracle as orc
+from tests.gpu_util import DEV, assert_bitwise, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+DIGESTS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "config_digests.txt")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stored(cfg):
+    out = {}
+    if os.path.exists(DIGESTS):
+        for line in open(DIGESTS):
+            f = line.split()
+            if len(f) >= 3 and f[0] == cfg:
+                out[f[1]] = f[2]
+    if not out:
+        pytest.skip(f"no oracle digests for {cfg}: run tests/golden/make_digests.py {cfg}")
+    return out
+
+
+def sha_dev(t: torch.Tensor) -> str:
+    return hashlib.sha256(to_np(t).tobytes()).hexdigest()
+
+
+def check_digests(cfg, got):
+    want = stored(cfg)
+    bad = [n for n, t in got.items() if n in want and sha_dev(t) != want[n]]
+    missing = [n for n in got if n not in want]
+    assert not missing, f"{cfg}: no stored digest for {missing}"
+    assert not bad, f"{cfg}: outputs differ from the oracle: {bad}"
+
+
+def sample_rows(M, k=6):
+    return sorted(set([0, 1, M // 2 - 1, M // 2, M - 2, M - 1][:k]))
+
+
+@pytest.fixture(scope="module")
+def brq():
+    import bitwise_reproducible_int8_amd as m
+    m.lib()
+    return m
+
+
+@pytest.mark.timeout(600)
+def test_qkv_full(brq):
+    say("full qkv 4096x2048->3072")
+    d = syn.qkv()
+    X, W = to_dev(d["x"]), to_dev(d["w"])
+    qx, _, sx, ax = brq.quantize_lsq(X)
+    qw, _, sw, aw = brq.quantize_lsq(W, per_row=True)
+    y = brq.qgemm_fwd(qx, sx, qw, sw)
+    qp, _, sp, ap = brq.quantize_lsq(W)
+    ypt = brq.qgemm_fwd(qx, sx, qp, sp)
+    # the oracle, row by row on sampled tokens
+    oqx, _, osx, _, _ = orc.quantize_lsq(d["x"])
+    oqw, _, osw, _, _ = orc.quantize_lsq(d["w"], per_row=True)
+    rows = sample_rows(4096)
+    assert_bitwise(to_np(y)[rows], orc.qgemm_fwd(oqx[rows], osx, oqw, osw), "y sampled rows")
+    check_digests("qkv", {"q_x": qx, "s_x": sx, "amax_x": ax, "q_w": qw, "s_w": sw, "amax_w": aw,
+                          "y": y, "q_w_pt": qp, "s_w_pt": sp, "amax_w_pt": ap, "y_pt": ypt})
+
+
+@pytest.mark.timeout(900)
+def test_mlp_full(brq):
+    say("full mlp 16384x2048->8192 fwd+bwd")
+    d = syn.mlp()
+    b = d["block"]
+    X, W, DY = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    qx, _, sx, ax = brq.quantize_lsq(X, flags=flags)
+    qw, qwt, sw, aw = brq.quantize_lsq(W, per_row=True, want_t=True, flags=flags)
+    y = brq.qgemm_fwd(qx, sx, qw, sw)
+    qg, _, sg, ag = brq.quantize_lsq(DY, col_mul=sw, flags=flags)
+    dx = brq.qgemm_bwd_dx(qg, sg, qwt)
+    dw, su, sv, qut, qvt = brq.qgemm_bwd_dw_wht(qx, sx, DY, b, flags=flags, return_codes=True)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    got = {"q_x": qx, "s_x": sx, "amax_x": ax, "q_w": qw, "q_wt": qwt, "s_w": sw, "amax_w": aw,
+           "y": y, "q_g": qg, "s_g": sg, "amax_g": ag, "dx": dx, "q_ut": qut, "s_u": su,
+           "q_vt": qvt, "s_v": sv, "dw": dw}
+    # oracle recomputation of sampled rows of every GEMM output
+    oqx, _, osx, _, _ = orc.quantize_lsq(d["x"])
+    oqw, _, osw, _, _ = orc.quantize_lsq(d["w"], per_row=True)
+    rows = sample_rows(16384)
+    assert_bitwise(to_np(y)[rows], orc.qgemm_fwd(oqx[rows], osx, oqw, osw), "y sampled rows")
+    oqg, _, osg, _, _ = orc.quantize_lsq(d["dy"], col_mul=osw)
+    assert_bitwise(to_np(dx)[rows], orc.qgemm_bwd_dx(oqg[rows], osg, oqw), "dx sampled rows")
+    oqu, osu, _ = orc.wht_int_quant(oqx, b)
+    oqv, osv, _, _ = orc.wht_fp_quant(d["dy"], b)
+    n_lo, n_hi = 8192 - 4, 8192
+    odw = orc.dw_gemm(oqv, oqu, osx[0], osu, osv, b, n_lo, n_hi)
+    assert_bitwise(to_np(dw)[n_lo:n_hi], odw[n_lo:n_hi], "dw sampled rows")
+    check_digests("mlp", got)
+    ts = [("y", y), ("dx", dx), ("dw", dw)]
+    assert bytes(to_np(brq.hash_state(ts))).hex() == stored("mlp")["state"]
+
+
+@pytest.mark.timeout(900)
+def test_norm_full(brq):
+    say("full norm 32768x2048 + grad-norm 1.61e9")
+    d = syn.norm(n_grad=0)
+    X, G, DY = to_dev(d["x"]), to_dev(d["g"]), to_dev(d["dy"])
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y, rstd = brq.rmsnorm_fixed_fwd(X, G, 1e-6, flags=flags)
+    dx, dg = brq.rmsnorm_fixed_bwd(X, G, rstd, DY)
+    rows = sample_rows(32768)
+    oy, orstd, _ = orc.rmsnorm_fwd(d["x"][rows], d["g"], 1e-6)
+    assert_bitwise(to_np(y)[rows], oy, "y sampled rows")
+    assert_bitwise(to_np(rstd)[rows], orstd, "rstd sampled rows")
+    odx, _ = orc.rmsnorm_bwd(d["x"][rows], d["g"], orstd, d["dy"][rows])
+    assert_bitwise(to_np(dx)[rows], odx, "dx sampled rows")
+    got = {"y": y, "rstd": rstd, "dx": dx, "dg": dg}
+    del X, DY, d
+    v = syn.normal((syn.GRAD_NORM_N,), 1e-4, tag=syn.TAG_V)
+    V = torch.from_numpy(v).to(DEV)
+    del v
+    ss, nrm = brq.grad_norm(V, flags=flags)
+    got["grad_norm"] = torch.stack([ss, nrm])
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    check_digests("norm", got)
+
+
+@pytest.mark.timeout(900)
+def test_layer_full(brq):
+    """The benchmark's step: digests of every output, gradient and scale,
+    and the on-device state hash."""
+    say("full layer 32768 tokens (the benchmark step)")
+    from bitwise_reproducible_int8_amd.layer import LayerStep
+    M = 32768
+    x = {name: to_dev(syn.layer_input(name, M)) for name, _ in syn.LAYER_INPUTS}
+    w = [to_dev(syn.layer_weight(i)) for i in range(len(syn.LAYER_LINEARS))]
+    dy = [to_dev(syn.layer_dy(i, M)) for i in range(len(syn.LAYER_LINEARS))]
+    norms = [(n,) + tuple(to_dev(a) for a in syn.layer_norm_inputs(j, M))
+             for j, (n, _) in enumerate(syn.LAYER_NORMS)]
+    step = LayerStep(syn.LAYER_LINEARS, x, w, dy, norms, block=128)
+    step.run()
+    torch.cuda.synchronize()
+    assert int(step.flags.item()) == 0
+    got = {}
+    for name in x:
+        got.update({f"{name}.q_x": step.q_x[name], f"{name}.s_x": step.s_x[name],
+                    f"{name}.amax_x": step.amax_x[name], f"{name}.q_ut": step.q_ut[name],
+                    f"{name}.s_u": step.s_u[name]})
+    for i, (ln, _, _, _) in enumerate(syn.LAYER_LINEARS):
+        got.update({f"{ln}.q_w": step.q_w[i], f"{ln}.q_wt": step.q_wt[i], f"{ln}.s_w": step.s_w[i],
+                    f"{ln}.y": step.y[i], f"{ln}.q_g": step.q_g[i], f"{ln}.s_g": step.s_g[i],
+                    f"{ln}.dx": step.dx[i], f"{ln}.q_vt": step.q_vt[i], f"{ln}.s_v": step.s_v[i],
+                    f"{ln}.dw": step.dw[i]})
+    for j, (nn, _) in enumerate(syn.LAYER_NORMS):
+        got.update({f"{nn}.y": step.ny[j], f"{nn}.rstd": step.nrstd[j], f"{nn}.dx": step.ndx[j],
+                    f"{nn}.dg": step.ndg[j]})
+    got["grad_norm"] = step.gn
+    # oracle on sampled tokens of the widest-contraction linear (down, K=8192)
+    i = [n for n, _, _, _ in syn.LAYER_LINEARS].index("down")
+    xin = syn.LAYER_LINEARS[i][3]
+    xd = syn.layer_input(xin, M)
+    oqx, _, osx, _, _ = orc.quantize_lsq(xd)
+    oqw, _, osw, _, _ = orc.quantize_lsq(syn.layer_weight(i), per_row=True)
+    rows = sample_rows(M, 4)
+    assert_bitwise(to_np(step.y[i])[rows], orc.qgemm_fwd(oqx[rows], osx, oqw, osw),
+                   "down.y sampled rows")
+    check_digests("layer", got)
+    assert bytes(to_np(step.digest)).hex() == stored("layer")["state"]
+    # a second step on the same inputs reproduces the digest
+    step.run()
+    assert bytes(to_np(step.digest)).hex() == stored("layer")["state"]
