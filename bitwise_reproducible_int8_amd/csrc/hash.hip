@@ -5,12 +5,29 @@
 // tensor bytes, 4096-byte leaves, 128 digests per interior node, a typed
 // header per tensor, and one digest over all tensor digests in call order.
 //
-// The leaf pass is integer ALU work: one lane per 4096-byte leaf runs 64 or
-// 65 compressions with the message schedule in registers.
+// The work is integer ALU (about 24 VALU operations per hashed byte), so
+// the kernels are built to keep every SIMD busy:
+//   - one launch hashes every 4096-byte slice of up to kBatch buffers (all
+//     tensors' leaves together, then each Merkle level of all tensors
+//     together), one lane per slice;
+//   - a full slice streams its 64 blocks with the next block's loads in
+//     flight while the current one is compressed, and its 65th (padding)
+//     block is a constant;
+//   - the round function is written in the shapes gfx950 has single
+//     instructions for: rotate (v_alignbit_b32), three-way xor
+//     (v_xor3_b32), bit select (v_bfi_b32), three-way add (v_add3_u32).
 #include "device.hpp"
 #include "internal.hpp"
 
 namespace brq {
+
+namespace {
+
+constexpr int kLeaf = 4096;     // bytes per leaf (and per interior node's input)
+constexpr int kFan = 128;       // digests per interior node
+constexpr int kBatch = 32;      // buffers per slice launch
+constexpr int kHdrBatch = 8;    // tensor headers per header launch
+constexpr int kHdrMax = 336;    // header bytes: 4+1+1+8*8+2+255 = 327
 
 __constant__ uint32_t kSha256K[64] = {
     0x428a2f98u, 0x71374491u, 0xb5c0fbcfu, 0xe9b5dba5u, 0x3956c25bu, 0x59f111f1u, 0x923f82a4u,
@@ -24,20 +41,26 @@ __constant__ uint32_t kSha256K[64] = {
     0x748f82eeu, 0x78a5636fu, 0x84c87814u, 0x8cc70208u, 0x90befffau, 0xa4506cebu, 0xbef9a3f7u,
     0xc67178f2u};
 
-__device__ __forceinline__ uint32_t rotr32(uint32_t x, int n) {
+__device__ __forceinline__ uint32_t rotr(uint32_t x, int n) {
   return __builtin_amdgcn_alignbit(x, x, n);
 }
-__device__ __forceinline__ uint32_t bswap32(uint32_t x) {
-  return __builtin_bswap32(x);
+__device__ __forceinline__ uint32_t bswap(uint32_t x) { return __builtin_bswap32(x); }
+// x ^ y ^ z in one v_bitop3_b32 (truth table 0x96, symmetric in its inputs)
+__device__ __forceinline__ uint32_t xor3(uint32_t x, uint32_t y, uint32_t z) {
+  return __builtin_amdgcn_bitop3_b32(x, y, z, 0x96);
+}
+// (m & x) | (~m & y)
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t x, uint32_t y) {
+  return (m & x) | (~m & y);
 }
 
 struct Sha {
   uint32_t h[8];
-  __device__ void init() {
+  __device__ __forceinline__ void init() {
     h[0] = 0x6a09e667u; h[1] = 0xbb67ae85u; h[2] = 0x3c6ef372u; h[3] = 0xa54ff53au;
     h[4] = 0x510e527fu; h[5] = 0x9b05688cu; h[6] = 0x1f83d9abu; h[7] = 0x5be0cd19u;
   }
-  // One compression of 16 big-endian words.
+  // One compression of 16 big-endian message words (FIPS 180-4 §6.2.2).
   __device__ __forceinline__ void block(const uint32_t* win) {
     uint32_t w[16];
 #pragma unroll
@@ -49,33 +72,40 @@ struct Sha {
       if (t < 16) {
         wt = w[t];
       } else {
-        uint32_t w15 = w[(t - 15) & 15], w2 = w[(t - 2) & 15];
-        uint32_t s0 = rotr32(w15, 7) ^ rotr32(w15, 18) ^ (w15 >> 3);
-        uint32_t s1 = rotr32(w2, 17) ^ rotr32(w2, 19) ^ (w2 >> 10);
+        const uint32_t w15 = w[(t - 15) & 15], w2 = w[(t - 2) & 15];
+        const uint32_t s0 = xor3(rotr(w15, 7), rotr(w15, 18), w15 >> 3);
+        const uint32_t s1 = xor3(rotr(w2, 17), rotr(w2, 19), w2 >> 10);
         wt = w[t & 15] + s0 + w[(t - 7) & 15] + s1;
         w[t & 15] = wt;
       }
-      uint32_t S1 = rotr32(e, 6) ^ rotr32(e, 11) ^ rotr32(e, 25);
-      uint32_t ch = (e & f) ^ (~e & g);
-      uint32_t t1 = hh + S1 + ch + kSha256K[t] + wt;
-      uint32_t S0 = rotr32(a, 2) ^ rotr32(a, 13) ^ rotr32(a, 22);
-      uint32_t mj = (a & b) ^ (a & c) ^ (b & c);
-      uint32_t t2 = S0 + mj;
-      hh = g; g = f; f = e; e = d + t1; d = c; c = b; b = a; a = t1 + t2;
+      const uint32_t S1 = xor3(rotr(e, 6), rotr(e, 11), rotr(e, 25));
+      const uint32_t t1 = hh + S1 + bitsel(e, f, g) + kSha256K[t] + wt;
+      const uint32_t S0 = xor3(rotr(a, 2), rotr(a, 13), rotr(a, 22));
+      // majority(a, b, c): one v_bitop3_b32, truth table 0xE8 (symmetric)
+      const uint32_t mj = __builtin_amdgcn_bitop3_b32(a, b, c, 0xE8);
+      hh = g; g = f; f = e; e = d + t1; d = c; c = b; b = a; a = t1 + S0 + mj;
     }
     h[0] += a; h[1] += b; h[2] += c; h[3] += d; h[4] += e; h[5] += f; h[6] += g; h[7] += hh;
   }
-  __device__ void store(uint8_t* out) const {
-    u32x4 lo{bswap32(h[0]), bswap32(h[1]), bswap32(h[2]), bswap32(h[3])};
-    u32x4 hi{bswap32(h[4]), bswap32(h[5]), bswap32(h[6]), bswap32(h[7])};
-    st16(out, lo);
-    st16(out + 16, hi);
+  __device__ __forceinline__ void store(uint8_t* out) const {
+    st16(out, u32x4{bswap(h[0]), bswap(h[1]), bswap(h[2]), bswap(h[3])});
+    st16(out + 16, u32x4{bswap(h[4]), bswap(h[5]), bswap(h[6]), bswap(h[7])});
   }
 };
 
+__device__ __forceinline__ void be_words(const u32x4* v, uint32_t* w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[4 * i] = bswap(v[i].x);
+    w[4 * i + 1] = bswap(v[i].y);
+    w[4 * i + 2] = bswap(v[i].z);
+    w[4 * i + 3] = bswap(v[i].w);
+  }
+}
+
 // Tail of a message: `rem` (< 64) bytes at p, then 0x80, zero fill and the
-// 64-bit big-endian bit length; one or two blocks.  Byte loads only, each
-// under its own predicate, so the block words keep static register indices.
+// 64-bit big-endian bit length; one or two blocks.  Byte loads under their
+// own predicates keep the block words at static register indices.
 __device__ void sha_tail(Sha& st, const uint8_t* p, int rem, uint64_t total_len) {
   uint32_t w[32];
 #pragma unroll
@@ -98,129 +128,237 @@ __device__ void sha_tail(Sha& st, const uint8_t* p, int rem, uint64_t total_len)
   }
 }
 
-// Digest of `len` bytes at p (p 16-byte aligned); full blocks use 16-byte
-// loads, the tail byte loads.
-__device__ void sha256_region(const uint8_t* p, uint64_t len, uint8_t* out) {
+// Digest of len bytes at p (16-byte aligned): full blocks by 16-byte loads.
+__device__ void sha256_bytes(const uint8_t* p, uint64_t len, uint8_t* out) {
   Sha st;
   st.init();
   const uint64_t full = len / 64;
   for (uint64_t i = 0; i < full; ++i) {
-    const uint8_t* q = p + 64 * i;
-    u32x4 v0 = ld16(q), v1 = ld16(q + 16), v2 = ld16(q + 32), v3 = ld16(q + 48);
-    uint32_t w[16] = {bswap32(v0.x), bswap32(v0.y), bswap32(v0.z), bswap32(v0.w),
-                      bswap32(v1.x), bswap32(v1.y), bswap32(v1.z), bswap32(v1.w),
-                      bswap32(v2.x), bswap32(v2.y), bswap32(v2.z), bswap32(v2.w),
-                      bswap32(v3.x), bswap32(v3.y), bswap32(v3.z), bswap32(v3.w)};
+    const u32x4* q = reinterpret_cast<const u32x4*>(p + 64 * i);
+    u32x4 v[4] = {q[0], q[1], q[2], q[3]};
+    uint32_t w[16];
+    be_words(v, w);
     st.block(w);
   }
   sha_tail(st, p + 64 * full, (int)(len - 64 * full), len);
   st.store(out);
 }
 
-// One lane per leaf of `leaf` bytes (4096): digest i covers
-// [i*leaf, min((i+1)*leaf, nbytes)).  An empty buffer has one empty leaf.
-__global__ __launch_bounds__(64) void k_sha_leaves(const uint8_t* __restrict__ data, uint64_t nbytes,
-                                                   uint64_t nleaves, uint8_t* __restrict__ out) {
-  const uint64_t i = (uint64_t)blockIdx.x * 64 + threadIdx.x;
-  if (i >= nleaves) return;
-  const uint64_t off = i * 4096;
-  const uint64_t len = nbytes > off ? (nbytes - off < 4096 ? nbytes - off : 4096) : 0;
-  sha256_region(data + off, len, out + 32 * i);
+// A full 4096-byte slice: 64 data blocks, the next block's loads issued
+// before the current compression, then the constant padding block (0x80,
+// zeros, bit length 32768).
+__device__ __forceinline__ void sha256_slice4096(const uint8_t* p, uint8_t* out) {
+  Sha st;
+  st.init();
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  u32x4 cur[4] = {q[0], q[1], q[2], q[3]};
+#pragma unroll 1
+  for (int i = 0; i < kLeaf / 64; ++i) {
+    u32x4 nxt[4];
+    if (i + 1 < kLeaf / 64) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nxt[j] = q[4 * (i + 1) + j];
+    }
+    uint32_t w[16];
+    be_words(cur, w);
+    st.block(w);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+  }
+  uint32_t pad[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pad[i] = 0;
+  pad[0] = 0x80000000u;
+  pad[15] = (uint32_t)(kLeaf * 8);
+  st.block(pad);
+  st.store(out);
 }
 
-// Tensor digest: header prefix (passed by value) followed by the root.
-struct HeaderArg {
-  uint8_t bytes[352];
-  int len;
+// Slices of up to kBatch buffers: buffer i has n_slices[i] = max(1,
+// ceil(nbytes[i] / 4096)) slices, and slice j's digest goes to dst[i] +
+// 32 j.  first[] holds the prefix sums of the slice counts.
+struct SliceBatch {
+  const uint8_t* src[kBatch];
+  uint8_t* dst[kBatch];
+  uint64_t nbytes[kBatch];
+  uint64_t first[kBatch + 1];
+  int n;
 };
 
-__global__ void k_sha_header(HeaderArg h, const uint8_t* __restrict__ root, uint8_t* __restrict__ out) {
-  uint8_t msg[352 + 32];
-  const int n = h.len;
-  for (int i = 0; i < n; ++i) msg[i] = h.bytes[i];
-  for (int i = 0; i < 32; ++i) msg[n + i] = root[i];
+__global__ __launch_bounds__(256) void k_sha_slices(SliceBatch b) {
+  const uint64_t g = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= b.first[b.n]) return;
+  int i = 0;
+  while (i + 1 < b.n && g >= b.first[i + 1]) ++i;
+  const uint64_t j = g - b.first[i];
+  const uint64_t off = j * kLeaf;
+  const uint64_t nb = b.nbytes[i];
+  const uint64_t len = nb > off ? (nb - off < (uint64_t)kLeaf ? nb - off : (uint64_t)kLeaf) : 0;
+  if (len == (uint64_t)kLeaf) sha256_slice4096(b.src[i] + off, b.dst[i] + 32 * j);
+  else sha256_bytes(b.src[i] + off, len, b.dst[i] + 32 * j);
+}
+
+// Tensor digests: SHA-256(header | root), one lane per tensor.
+struct HeaderBatch {
+  uint8_t bytes[kHdrBatch][kHdrMax];
+  int len[kHdrBatch];
+  const uint8_t* root[kHdrBatch];
+  uint8_t* out[kHdrBatch];
+  int n;
+};
+
+__global__ __launch_bounds__(64) void k_sha_headers(HeaderBatch hb) {
+  const int i = threadIdx.x;
+  if (i >= hb.n) return;
+  const int n = hb.len[i];
   const int len = n + 32;
   Sha st;
   st.init();
   int off = 0;
+  // message = header bytes then the 32 root bytes, fed block by block
+  auto byte_at = [&](int k) -> uint32_t {
+    return k < n ? (uint32_t)hb.bytes[i][k] : (uint32_t)hb.root[i][k - n];
+  };
   for (; off + 64 <= len; off += 64) {
     uint32_t w[16];
-    for (int j = 0; j < 16; ++j)
-      w[j] = ((uint32_t)msg[off + 4 * j] << 24) | ((uint32_t)msg[off + 4 * j + 1] << 16) |
-             ((uint32_t)msg[off + 4 * j + 2] << 8) | (uint32_t)msg[off + 4 * j + 3];
+    for (int q = 0; q < 16; ++q)
+      w[q] = (byte_at(off + 4 * q) << 24) | (byte_at(off + 4 * q + 1) << 16) |
+             (byte_at(off + 4 * q + 2) << 8) | byte_at(off + 4 * q + 3);
     st.block(w);
   }
-  sha_tail(st, msg + off, len - off, (uint64_t)len);
-  st.store(out);
+  uint8_t tail[64];
+  const int rem = len - off;
+  for (int q = 0; q < rem; ++q) tail[q] = (uint8_t)byte_at(off + q);
+  sha_tail(st, tail, rem, (uint64_t)len);
+  st.store(hb.out[i]);
 }
 
 // State digest over n tensor digests (32 n bytes, 16-byte aligned).
 __global__ void k_sha_state(const uint8_t* __restrict__ digests, int n, uint8_t* __restrict__ out) {
-  sha256_region(digests, (uint64_t)n * 32, out);
+  sha256_bytes(digests, (uint64_t)n * 32, out);
 }
 
-static uint64_t cdivu(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+uint64_t cdivu(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
-static uint64_t tensor_bytes(const brq_tensor_ref& t) {
+uint64_t tensor_bytes(const brq_tensor_ref& t) {
   static const int esz[5] = {4, 2, 1, 4, 1};
   uint64_t n = 1;
   for (int i = 0; i < t.ndim; ++i) n *= (uint64_t)t.dims[i];
   return n * (uint64_t)esz[t.dtype];
 }
 
-size_t hash_ws(const brq_tensor_ref* t, int n) {
-  uint64_t maxleaf = 1;
-  for (int i = 0; i < n; ++i) {
-    uint64_t l = cdivu(tensor_bytes(t[i]), 4096);
-    if (l > maxleaf) maxleaf = l;
+// Digest counts of tensor i's levels: level 0 = leaves, then ceil(/128)
+// until one remains.  Returns the number of levels.
+int level_counts(uint64_t nbytes, uint64_t* cnt) {
+  int L = 0;
+  cnt[L++] = nbytes == 0 ? 1 : cdivu(nbytes, kLeaf);
+  while (cnt[L - 1] > 1) {
+    cnt[L] = cdivu(cnt[L - 1], kFan);
+    ++L;
   }
-  return align256(32 * maxleaf) + align256(32 * cdivu(maxleaf, 128)) +
-         align256(32 * (uint64_t)(n > 0 ? n : 1));
+  return L;
+}
+
+// Bytes of one tensor's digest region (every level, 256-byte aligned).
+size_t tensor_region(uint64_t nbytes) {
+  uint64_t cnt[40];
+  int L = level_counts(nbytes, cnt);
+  size_t s = 0;
+  for (int l = 0; l < L; ++l) s += align256(32 * cnt[l]);
+  return s;
+}
+
+hipError_t launch_slices(SliceBatch& b, hipStream_t s) {
+  if (b.n == 0) return hipSuccess;
+  const uint64_t total = b.first[b.n];
+  hipLaunchKernelGGL(k_sha_slices, dim3((unsigned)cdivu(total, 256)), dim3(256), 0, s, b);
+  b.n = 0;
+  b.first[0] = 0;
+  return hipGetLastError();
+}
+
+void add_slices(SliceBatch& b, const uint8_t* src, uint64_t nbytes, uint8_t* dst) {
+  const uint64_t cnt = nbytes == 0 ? 1 : cdivu(nbytes, kLeaf);
+  b.src[b.n] = src;
+  b.dst[b.n] = dst;
+  b.nbytes[b.n] = nbytes;
+  b.first[b.n + 1] = b.first[b.n] + cnt;
+  ++b.n;
+}
+
+}  // namespace
+
+size_t hash_ws(const brq_tensor_ref* t, int n) {
+  size_t s = align256(32 * (uint64_t)(n > 0 ? n : 1));
+  for (int i = 0; i < n; ++i) s += tensor_region(tensor_bytes(t[i]));
+  return s;
 }
 
 hipError_t hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* ws, hipStream_t s) {
-  uint64_t maxleaf = 1;
-  for (int i = 0; i < n; ++i) {
-    uint64_t l = cdivu(tensor_bytes(t[i]), 4096);
-    if (l > maxleaf) maxleaf = l;
-  }
-  uint8_t* bufA = (uint8_t*)ws;
-  uint8_t* bufB = bufA + align256(32 * maxleaf);
-  uint8_t* tdig = bufB + align256(32 * cdivu(maxleaf, 128));
+  uint8_t* tdig = (uint8_t*)ws;
+  uint8_t* base = tdig + align256(32 * (uint64_t)(n > 0 ? n : 1));
   hipError_t e;
+  SliceBatch b{};
+  // pass over levels: level 0 hashes tensor bytes, level l > 0 hashes the
+  // digests of level l - 1; tensors whose tree has ended drop out
+  for (int l = 0;; ++l) {
+    bool any = false;
+    uint8_t* region = base;
+    for (int i = 0; i < n; ++i) {
+      const uint64_t nb = tensor_bytes(t[i]);
+      uint64_t cnt[40];
+      const int L = level_counts(nb, cnt);
+      uint8_t* lv[40];
+      uint8_t* r = region;
+      for (int k = 0; k < L; ++k) {
+        lv[k] = r;
+        r += align256(32 * cnt[k]);
+      }
+      region = r;
+      if (l >= L) continue;
+      any = true;
+      if (l == 0) add_slices(b, (const uint8_t*)t[i].data, nb, lv[0]);
+      else add_slices(b, lv[l - 1], 32 * cnt[l - 1], lv[l]);
+      if (b.n == kBatch && (e = launch_slices(b, s)) != hipSuccess) return e;
+    }
+    if ((e = launch_slices(b, s)) != hipSuccess) return e;
+    if (!any) break;
+  }
+  // tensor digests
+  HeaderBatch hb{};
+  uint8_t* region = base;
   for (int i = 0; i < n; ++i) {
     const uint64_t nb = tensor_bytes(t[i]);
-    uint64_t cnt = nb == 0 ? 1 : cdivu(nb, 4096);
-    hipLaunchKernelGGL(k_sha_leaves, dim3((unsigned)cdivu(cnt, 64)), dim3(64), 0, s,
-                       (const uint8_t*)t[i].data, nb, cnt, bufA);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    uint8_t* cur = bufA;
-    uint8_t* nxt = bufB;
-    while (cnt > 1) {
-      uint64_t nc = cdivu(cnt, 128);
-      hipLaunchKernelGGL(k_sha_leaves, dim3((unsigned)cdivu(nc, 64)), dim3(64), 0, s, cur,
-                         32 * cnt, nc, nxt);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      uint8_t* tmp = cur;
-      cur = nxt;
-      nxt = tmp;
-      cnt = nc;
+    uint64_t cnt[40];
+    const int L = level_counts(nb, cnt);
+    uint8_t* r = region;
+    uint8_t* root = r;
+    for (int k = 0; k < L; ++k) {
+      root = r;
+      r += align256(32 * cnt[k]);
     }
-    HeaderArg h{};
+    region = r;
+    const int k = hb.n;
     int o = 0;
-    h.bytes[o++] = 'B'; h.bytes[o++] = 'R'; h.bytes[o++] = 'Q'; h.bytes[o++] = '1';
-    h.bytes[o++] = (uint8_t)t[i].dtype;
-    h.bytes[o++] = (uint8_t)t[i].ndim;
+    uint8_t* h = hb.bytes[k];
+    h[o++] = 'B'; h[o++] = 'R'; h[o++] = 'Q'; h[o++] = '1';
+    h[o++] = (uint8_t)t[i].dtype;
+    h[o++] = (uint8_t)t[i].ndim;
     for (int d = 0; d < t[i].ndim; ++d)
-      for (int b = 0; b < 8; ++b) h.bytes[o++] = (uint8_t)((uint64_t)t[i].dims[d] >> (8 * b));
+      for (int q = 0; q < 8; ++q) h[o++] = (uint8_t)((uint64_t)t[i].dims[d] >> (8 * q));
     size_t nl = 0;
     while (t[i].name && t[i].name[nl]) ++nl;
-    h.bytes[o++] = (uint8_t)(nl & 0xff);
-    h.bytes[o++] = (uint8_t)(nl >> 8);
-    for (size_t c = 0; c < nl; ++c) h.bytes[o++] = (uint8_t)t[i].name[c];
-    h.len = o;
-    hipLaunchKernelGGL(k_sha_header, dim3(1), dim3(1), 0, s, h, cur, tdig + 32 * i);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    h[o++] = (uint8_t)(nl & 0xff);
+    h[o++] = (uint8_t)(nl >> 8);
+    for (size_t c = 0; c < nl; ++c) h[o++] = (uint8_t)t[i].name[c];
+    hb.len[k] = o;
+    hb.root[k] = root;
+    hb.out[k] = tdig + 32 * i;
+    if (++hb.n == kHdrBatch || i == n - 1) {
+      hipLaunchKernelGGL(k_sha_headers, dim3(1), dim3(64), 0, s, hb);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hb.n = 0;
+    }
   }
   hipLaunchKernelGGL(k_sha_state, dim3(1), dim3(1), 0, s, tdig, n, digest32);
   return hipGetLastError();

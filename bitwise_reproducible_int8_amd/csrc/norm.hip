@@ -14,9 +14,9 @@
 // consecutive (aligned) tokens and folds its rows, in token order, with a
 // binary-carry stack per column: pushing row t merges ctz(t+1) pending
 // nodes, lower tokens always on the left, which is exactly node(log2 R, .)
-// of the token tree.  A second kernel folds those per-block nodes the same
-// way; the pending nodes left by a count that is not a power of two are
-// combined from the smallest block up, which is the tree's right spine.
+// of the token tree.  Fold kernels then combine those per-block nodes 32 at
+// a time with the same stack, padding past the last block with -0, until one
+// node per column remains.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -150,23 +150,36 @@ __global__ __launch_bounds__(256) void k_rms_bwd(const T* __restrict__ x, const 
   }
   float stk[LOGR + 1][NE];
 
+  // raw 16-byte vectors of the next row: its loads are in flight while the
+  // current row is reduced and written
+  u32x4 xn[V], dn[V];
+  auto fetch = [&](int rr) {
+    const int64_t row = r0 + rr;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int64_t c0 = (int64_t)(v * 256 + t) * E;
+      const bool ok = rr < R && row < Tn && colok[v];
+      xn[v] = ok ? ld16(x + row * D + c0) : u32x4{0, 0, 0, 0};
+      dn[v] = ok ? ld16(dy + row * D + c0) : u32x4{0, 0, 0, 0};
+    }
+  };
+  fetch(0);
+
 #pragma unroll 1
   for (int rr = 0; rr < R; ++rr) {
     const int64_t row = r0 + rr;
     const bool rowok = row < Tn;  // uniform across the work-group
+    u32x4 xc[V], dc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) { xc[v] = xn[v]; dc[v] = dn[v]; }
+    fetch(rr + 1);
     float xh[NE], d[NE], leaf[NE];
     const float rs = rowok ? flush(rstd[row]) : 0.0f;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const int64_t c0 = (int64_t)(v * 256 + t) * E;
       float xv[E], dv[E];
-      if (rowok && colok[v]) {
-        Elem<T>::unpack(ld16(x + row * D + c0), xv);
-        Elem<T>::unpack(ld16(dy + row * D + c0), dv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) { xv[e] = 0.0f; dv[e] = 0.0f; }
-      }
+      Elem<T>::unpack(xc[v], xv);
+      Elem<T>::unpack(dc[v], dv);
       float p[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -233,42 +246,48 @@ __global__ __launch_bounds__(256) void k_rms_bwd(const T* __restrict__ x, const 
   }
 }
 
-// Token-order fold of the per-block nodes: 4 columns per lane.
-__global__ __launch_bounds__(256) void k_dg_final(const float* __restrict__ part, int64_t P,
-                                                  int64_t D, float* __restrict__ dg) {
-  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+// Next tree levels over the per-block nodes: in [P][D] holds node(l, p) of
+// every column for p < P; a lane owns 4 columns of one aligned group of
+// 32 nodes and folds them with the same binary-carry stack (nodes past P are
+// -0, the exact identity), giving node(l + 5, q) in out [ceil(P/32)][D].
+constexpr int kFoldLog = 5;
+__global__ __launch_bounds__(256) void k_dg_fold(const float* __restrict__ in, int64_t P, int64_t D,
+                                                 int64_t col_blocks, float* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x / col_blocks;
+  const int64_t c = (((int64_t)blockIdx.x % col_blocks) * 256 + threadIdx.x) * 4;
   if (c >= D) return;
-  float stk[32][4];
-  for (int64_t p = 0; p < P; ++p) {
-    float4 v4 = *reinterpret_cast<const float4*>(part + p * D + c);
-    float val[4] = {v4.x, v4.y, v4.z, v4.w};
+  float stk[kFoldLog + 1][4];
+#pragma unroll 1
+  for (int i = 0; i < (1 << kFoldLog); ++i) {
+    const int64_t p = q * (1 << kFoldLog) + i;
+    float val[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
+    if (p < P) {
+      const float4 v4 = *reinterpret_cast<const float4*>(in + p * D + c);
+      val[0] = v4.x; val[1] = v4.y; val[2] = v4.z; val[3] = v4.w;
+    }
     bool carry = true;
 #pragma unroll
-    for (int l = 0; l < 32; ++l) {
+    for (int l = 0; l <= kFoldLog; ++l) {
       if (carry) {
-        if ((p >> l) & 1) {
+        if ((i >> l) & 1) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) val[q] = fadd(stk[l][q], val[q]);
+          for (int k = 0; k < 4; ++k) val[k] = fadd(stk[l][k], val[k]);
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) stk[l][q] = val[q];
+          for (int k = 0; k < 4; ++k) stk[l][k] = val[k];
           carry = false;
         }
       }
     }
   }
-  // pending nodes: set bits of P, combined from the lowest (rightmost) up
-  float acc[4] = {0, 0, 0, 0};
-  bool have = false;
-#pragma unroll
-  for (int l = 0; l < 32; ++l) {
-    if ((P >> l) & 1) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = have ? fadd(stk[l][q], acc[q]) : stk[l][q];
-      have = true;
-    }
-  }
-  *reinterpret_cast<float4*>(dg + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(out + q * D + c) =
+      make_float4(stk[kFoldLog][0], stk[kFoldLog][1], stk[kFoldLog][2], stk[kFoldLog][3]);
+}
+
+// dg of an empty token range: the tree over no leaves is +0.
+__global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
 }
 
 int rmsnorm_bwd_rows(int64_t D, int dtype, const brq_tune* t) {
@@ -286,7 +305,9 @@ int rmsnorm_bwd_rows(int64_t D, int dtype, const brq_tune* t) {
 
 size_t rmsnorm_bwd_ws(int64_t T, int64_t D, int dtype, const brq_tune* t) {
   int R = rmsnorm_bwd_rows(D, dtype, t);
-  return align256((size_t)cdiv(T > 0 ? T : 1, R) * (size_t)D * sizeof(float));
+  const int64_t P = cdiv(T > 0 ? T : 1, R);
+  return align256((size_t)P * (size_t)D * sizeof(float)) +
+         align256((size_t)cdiv(P, 1 << kFoldLog) * (size_t)D * sizeof(float));
 }
 
 template <typename TT, int VV>
@@ -331,8 +352,28 @@ hipError_t rmsnorm_bwd(const void* x, const void* g, const float* rstd, const vo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_dg_final, dim3((unsigned)cdiv(D, 1024)), dim3(256), 0, s, part, P, D, dg);
-  return hipGetLastError();
+  if (P == 0) {
+    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)cdiv(D, 256)), dim3(256), 0, s, dg, D);
+    return hipGetLastError();
+  }
+  // fold the per-block nodes 32 at a time until one row remains (at least
+  // once, so that the last fold writes dg itself)
+  float* bufs[2] = {part, part + align256((size_t)P * (size_t)D * sizeof(float)) / sizeof(float)};
+  const float* cur = part;
+  int64_t n = P;
+  int which = 1;
+  const int64_t cb = cdiv(D, 1024);
+  do {
+    const int64_t nn = cdiv(n, 1 << kFoldLog);
+    float* dst = nn == 1 ? dg : bufs[which];
+    hipLaunchKernelGGL(k_dg_fold, dim3((unsigned)(nn * cb)), dim3(256), 0, s, cur, n, D, cb, dst);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    cur = dst;
+    which ^= 1;
+    n = nn;
+  } while (n > 1);
+  return hipSuccess;
 }
 
 // ---- global gradient norm ------------------------------------------------------
