@@ -57,32 +57,36 @@ __global__ __launch_bounds__(256) void k_gemm_ref(const int8_t* __restrict__ A,
 }
 
 // --------------------------------------------------------------------------
-// MFMA kernel.  Block tile BM x BN, contraction step BK = 128 bytes (one
-// 128-byte line per operand row), WGM x WGN waves, each wave a
-// (BM/WGM) x (BN/WGN) tile of 16x16 v_mfma_i32_16x16x64_i8 blocks.
+// MFMA kernel.  Block tile BM x BN, contraction step BK bytes (64 or 128),
+// WGM x WGN waves, each wave a (BM/WGM) x (BN/WGN) tile of 16x16
+// v_mfma_i32_16x16x64_i8 blocks.
 //
-// LDS holds each operand tile row-major [rows][128 B] with the 16-byte chunk
-// index XOR-ed by (row >> 1) & 7, so the 16 rows one MFMA operand read
-// touches spread over all banks.  Two LDS stages: while the waves multiply
-// out of one stage, the next tile's global loads are in flight in registers
-// and land in the other stage; one barrier per step.
+// LDS holds each operand tile row-major [rows][BK bytes] in 16-byte chunks,
+// chunk index XOR-ed with a row hash chosen so that the rows one MFMA
+// operand read touches (16 consecutive rows, one chunk each) fall in
+// distinct bank groups whether the hardware serves 8 or 16 lanes of a
+// 128-bit read per cycle.  Two LDS stages: while the waves multiply out of
+// one stage, the next tile's global loads are in flight in registers and
+// land in the other stage; one barrier per step.
 //
 // MFMA operand layout (16x16x64, int8): lane l supplies 16 consecutive
 // contraction bytes, k-group l>>4, of row (A) or column (B) l&15; both
 // operands use the same (lane, byte) -> k map, so the product sums all 64
 // contraction terms.  Result: lane l holds rows 4*(l>>4)+r, column l&15.
 // --------------------------------------------------------------------------
-constexpr int BK = 128;
-
+template <int BK>
 __device__ __forceinline__ int lds_off(int row, int kc) {
-  return row * BK + ((kc ^ ((row >> 1) & 7)) << 4);
+  constexpr int CH = BK / 16;
+  const int f = CH == 8 ? ((row ^ (row >> 3)) & 7) : (((row >> 1) ^ (row >> 2)) & 3);
+  return row * BK + ((kc ^ f) << 4);
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int BK>
 __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t I, int64_t J,
     int64_t Kc, float* __restrict__ C, int* __restrict__ Cpart, int ktiles_per_split, Epi epi) {
   constexpr int NT = WGM * WGN * 64;
+  constexpr int CH = BK / 16;  // 16-byte chunks per operand row
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TI = WM / 16, TJ = WN / 16;
   constexpr int LA = BM * BK / 16 / NT, LB = BN * BK / 16 / NT;
@@ -117,13 +121,13 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
     const int64_t k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int c = t + NT * i, r = c >> 3, kc = c & 7;
+      const int c = t + NT * i, r = c / CH, kc = c % CH;
       const int64_t gr = row0 + r, gk = k0 + kc * 16;
       ra[i] = (gr < I && gk < Kc) ? ld16(A + gr * Kc + gk) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int c = t + NT * i, r = c >> 3, kc = c & 7;
+      const int c = t + NT * i, r = c / CH, kc = c % CH;
       const int64_t gr = col0 + r, gk = k0 + kc * 16;
       rb[i] = (gr < J && gk < Kc) ? ld16(B + gr * Kc + gk) : u32x4{0, 0, 0, 0};
     }
@@ -132,12 +136,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int c = t + NT * i;
-      st16(&As[st][lds_off(c >> 3, c & 7)], ra[i]);
+      st16(&As[st][lds_off<BK>(c / CH, c % CH)], ra[i]);
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       const int c = t + NT * i;
-      st16(&Bs[st][lds_off(c >> 3, c & 7)], rb[i]);
+      st16(&Bs[st][lds_off<BK>(c / CH, c % CH)], rb[i]);
     }
   };
 
@@ -161,12 +165,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
           const int r = wm * WM + i * 16 + (lane & 15);
-          af[i] = *reinterpret_cast<const v4i*>(&As[st][lds_off(r, kc)]);
+          af[i] = *reinterpret_cast<const v4i*>(&As[st][lds_off<BK>(r, kc)]);
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           const int r = wn * WN + j * 16 + (lane & 15);
-          bf[j] = *reinterpret_cast<const v4i*>(&Bs[st][lds_off(r, kc)]);
+          bf[j] = *reinterpret_cast<const v4i*>(&Bs[st][lds_off<BK>(r, kc)]);
         }
 #pragma unroll
         for (int i = 0; i < TI; ++i)
@@ -198,6 +202,225 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
   }
 }
 
+// --------------------------------------------------------------------------
+// Deep-pipelined MFMA kernel: operand tiles go from global memory straight
+// into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at the
+// instruction's LDS base + 16 * lane), through kStages LDS stages, with the
+// loads for contraction step t + kStages - 1 issued while step t is
+// multiplied -- so each load has kStages - 1 steps of MFMA work to arrive.
+// BK = 64 bytes (4 chunks of 16 per operand row).  The XOR-swizzled LDS
+// layout of the register-staged kernel is kept: since a lane's LDS slot is
+// fixed by its lane number, each lane picks the global chunk that belongs in
+// its slot.  Rows past the matrix edge read a clamped (valid) row; they only
+// feed output rows or columns that are never stored.  The contraction
+// length must be a multiple of 64 (no partial chunks).
+//
+// Synchronisation per step: wait until this wave's loads of step t have
+// landed (vmcnt counts only the direct-to-LDS loads issued in the loop),
+// one workgroup barrier (every wave's step-t data is in LDS and every wave
+// has finished reading step t - 1's stage), issue step t + kStages - 1 into
+// that freed stage, then multiply step t.  The barrier is the bare
+// s_barrier: the loads are tracked by the explicit wait, not by a fence.
+// --------------------------------------------------------------------------
+constexpr int kStages = 4;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt (7) and
+  // lgkmcnt (15) left at their no-wait values
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 4x4 transpose inside each quad of lanes.  On entry lane q of a quad holds
+// v[r] = M[r][q] (the MFMA result layout: one column, four rows); on exit it
+// holds v[e] = M[q][e] (one row, four consecutive columns), so each lane can
+// store 16 contiguous bytes.  Two exchange stages: off-diagonal elements of
+// the 2x2 sub-blocks between lanes q, q^1, then off-diagonal 2x2 blocks
+// between lanes q, q^2.  Integer moves only.
+__device__ __forceinline__ int dpp_xor1_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int dpp_xor2_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ v4i quad_transpose(v4i v, int q) {
+  const bool odd = q & 1, hi = q & 2;
+#pragma unroll
+  for (int r0 = 0; r0 < 4; r0 += 2) {
+    const int recv = dpp_xor1_i(odd ? v[r0] : v[r0 + 1]);
+    if (odd) v[r0] = recv;
+    else v[r0 + 1] = recv;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int recv = dpp_xor2_i(hi ? v[r] : v[r + 2]);
+    if (hi) v[r] = recv;
+    else v[r + 2] = recv;
+  }
+  return v;
+}
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t I, int64_t J,
+    int64_t Kc, float* __restrict__ C, int* __restrict__ Cpart, int ktiles_per_split, Epi epi) {
+  constexpr int BK = 64, CH = BK / 16;
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int DA = BM * CH / 64 / NW, DB = BN * CH / 64 / NW;  // loads per wave per step
+  constexpr int L = DA + DB;
+  static_assert(DA * 64 * NW == BM * CH && DB * 64 * NW == BN * CH, "tile/waves");
+  constexpr int STAGE = (BM + BN) * BK;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * STAGE];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // XCD-aware tile order (as the register-staged kernel)
+  const int64_t gm = (I + BM - 1) / BM, gn = (J + BN - 1) / BN;
+  const int64_t total = gm * gn;
+  int64_t pid = blockIdx.x;
+  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+  const int64_t group = 8 * gn;
+  const int64_t first_m = (pid / group) * 8;
+  const int64_t gsz = (gm - first_m) < 8 ? (gm - first_m) : 8;
+  const int64_t bm = first_m + (pid % group) % gsz;
+  const int64_t bn = (pid % group) / gsz;
+  const int64_t row0 = bm * BM, col0 = bn * BN;
+
+  const int64_t nk_total = Kc / BK;
+  const int64_t kt0 = (int64_t)blockIdx.z * ktiles_per_split;
+  int64_t kt1 = kt0 + ktiles_per_split;
+  if (kt1 > nk_total) kt1 = nk_total;
+  const int64_t nk = kt1 > kt0 ? kt1 - kt0 : 0;
+
+  // per-lane source of each direct-to-LDS load: slot sigma of the stage's
+  // A (then B) region holds row sigma / 4, chunk (sigma % 4) ^ f(row)
+  const int8_t* srcA[DA];
+  const int8_t* srcB[DB];
+#pragma unroll
+  for (int i = 0; i < DA; ++i) {
+    const int sg = (wave * DA + i) * 64 + lane, r = sg / CH;
+    const int f = ((r >> 1) ^ (r >> 2)) & 3;
+    int64_t gr = row0 + r;
+    gr = gr < I ? gr : I - 1;
+    srcA[i] = A + gr * Kc + (int64_t)(((sg % CH) ^ f) * 16) + kt0 * BK;
+  }
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    const int sg = (wave * DB + i) * 64 + lane, r = sg / CH;
+    const int f = ((r >> 1) ^ (r >> 2)) & 3;
+    int64_t gr = col0 + r;
+    gr = gr < J ? gr : J - 1;
+    srcB[i] = B + gr * Kc + (int64_t)(((sg % CH) ^ f) * 16) + kt0 * BK;
+  }
+  auto issue = [&](int64_t it) {
+    int8_t* st = smem + (it % kStages) * STAGE;
+#pragma unroll
+    for (int i = 0; i < DA; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(srcA[i] + it * BK),
+          (__attribute__((address_space(3))) void*)(st + (wave * DA + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(srcB[i] + it * BK),
+          (__attribute__((address_space(3))) void*)(st + BM * BK + (wave * DB + i) * 1024), 16,
+          0, 0);
+  };
+
+  v4i acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk) issue(s);
+
+  const int kc = lane >> 4;
+#pragma unroll 1
+  for (int64_t it = 0; it < nk; ++it) {
+    // loads still allowed in flight: those of the (up to kStages - 2) later
+    // steps already issued
+    const int64_t later = nk - 1 - it;
+    if (later >= 2) wait_vmcnt<2 * L>();
+    else if (later == 1) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    if (it + kStages - 1 < nk) issue(it + kStages - 1);
+    const int8_t* st = smem + (it % kStages) * STAGE;
+    v4i af[TI], bf[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int r = wm * WM + i * 16 + (lane & 15);
+      af[i] = *reinterpret_cast<const v4i*>(st + lds_off<BK>(r, kc));
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int r = wn * WN + j * 16 + (lane & 15);
+      bf[j] = *reinterpret_cast<const v4i*>(st + BM * BK + lds_off<BK>(r, kc));
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    asm volatile("" ::: "memory");
+  }
+
+  // Epilogue: quad-transpose each 16x16 result block so a lane holds four
+  // consecutive columns of one row, then 16-byte stores (element-wise at a
+  // ragged right edge).  Split-K writes exact int32 partials instead.
+  const int q = lane & 3;
+  const int rsub = 4 * (lane >> 4) + q;   // row within the 16x16 block
+  const int csub = (lane & 15) & ~3;      // first of the lane's 4 columns
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int64_t col = col0 + wn * WN + j * 16 + csub;
+    float c4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (!Cpart) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c4[e] = col + e < J ? epi.scale(col + e) : 0.0f;
+    }
+    const bool full = col + 4 <= J && (J & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const v4i v = quad_transpose(acc[i][j], q);
+      const int64_t row = row0 + wm * WM + i * 16 + rsub;
+      if (row >= I || col >= J) continue;
+      if (Cpart) {
+        int* dst = Cpart + ((int64_t)blockIdx.z * I + row) * J + col;
+        if (full) {
+          *reinterpret_cast<v4i*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < J) dst[e] = v[e];
+        }
+      } else {
+        float* dst = C + row * J + col;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = dequant(v[e], c4[e]);
+        if (full) {
+          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < J) dst[e] = o[e];
+        }
+      }
+    }
+  }
+}
+
 // Sum of the split-K partials in split order (exact in int32), then the
 // same epilogue.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const int* __restrict__ Cpart, int splits,
@@ -213,27 +436,63 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const int* __restrict__ C
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-static int pick_kernel(const brq_tune* t) { return (t && t->gemm_kernel) ? t->gemm_kernel : 2; }
-static int pick_splits(const brq_tune* t) {
-  int s = (t && t->split_k) ? t->split_k : 1;
-  return (s == 2 || s == 4) ? s : 1;
+// Launch plan: the tune's kernel and split-K when given, else by shape --
+// the deep-pipelined 256x256 kernel whenever the contraction is a multiple
+// of 64 bytes, with the contraction split so that tiles x splits reaches
+// about one work-group per CU when the output has few tiles.  None of this
+// changes a result bit: the int32 sums are exact in any grouping.
+struct Plan {
+  int kern;
+  int splits;
+};
+
+static Plan plan_of(int64_t I, int64_t J, int64_t Kc, const brq_tune* t) {
+  Plan p{2, 1};
+  const int tk = t ? t->gemm_kernel : 0;
+  const int ts = t ? t->split_k : 0;
+  if (tk) {
+    p.kern = tk;
+  } else if (Kc % 64 == 0) {
+    p.kern = 10;
+  }
+  if (ts) {
+    p.splits = (ts == 2 || ts == 4 || ts == 8 || ts == 16) ? ts : 1;
+  } else if (!tk && p.kern == 10) {
+    const int64_t tiles = cdiv(I, 256) * cdiv(J, 256);
+    int s = 1;
+    while (s < 16 && tiles * s < 256 && Kc / 64 / (2 * s) >= 32) s *= 2;
+    p.splits = s;
+  }
+  if (p.kern == 1) p.splits = 1;
+  return p;
 }
 
 size_t gemm_ws(int64_t I, int64_t J, int64_t Kc, const brq_tune* t) {
-  (void)Kc;
-  int s = pick_splits(t);
-  if (s == 1 || pick_kernel(t) == 1) return 0;
-  return align256((size_t)s * (size_t)I * (size_t)J * sizeof(int));
+  const Plan p = plan_of(I, J, Kc, t);
+  if (p.splits == 1) return 0;
+  return align256((size_t)p.splits * (size_t)I * (size_t)J * sizeof(int));
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int BK>
 static hipError_t launch_mfma(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64_t Kc,
                               float* C, int* Cpart, int splits, Epi epi, hipStream_t s) {
   const int64_t tiles = cdiv(I, BM) * cdiv(J, BN);
   const int64_t nk = cdiv(Kc, BK);
   const int kps = (int)cdiv(nk, splits);
   dim3 g((unsigned)tiles, 1, (unsigned)splits), b(WGM * WGN * 64);
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WGM, WGN>), g, b, 0, s, A, B, I, J, Kc, C, Cpart, kps,
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WGM, WGN, BK>), g, b, 0, s, A, B, I, J, Kc, C, Cpart, kps,
+                     epi);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+static hipError_t launch_dma(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64_t Kc,
+                             float* C, int* Cpart, int splits, Epi epi, hipStream_t s) {
+  const int64_t tiles = cdiv(I, BM) * cdiv(J, BN);
+  const int64_t nk = Kc / 64;
+  const int kps = (int)cdiv(nk, splits);
+  dim3 g((unsigned)tiles, 1, (unsigned)splits), b(WGM * WGN * 64);
+  hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN>), g, b, 0, s, A, B, I, J, Kc, C, Cpart, kps,
                      epi);
   return hipGetLastError();
 }
@@ -243,23 +502,34 @@ hipError_t gemm_i8(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64
                    hipStream_t s) {
   Epi epi{ea.kind, ea.s0, ea.s1, ea.s2, ea.per_row, ea.inv_b};
   if (I == 0 || J == 0) return hipSuccess;
-  const int kern = pick_kernel(t);
+  const Plan pl = plan_of(I, J, Kc, t);
+  int kern = pl.kern;
   if (kern == 1) {
     dim3 g((unsigned)cdiv(J, 64), (unsigned)cdiv(I, 4)), b(256);
     hipLaunchKernelGGL(k_gemm_ref, g, b, 0, s, A, B, I, J, Kc, C, epi);
     return hipGetLastError();
   }
-  const int splits = pick_splits(t);
+  const int splits = pl.splits;
   int* part = nullptr;
   if (splits > 1) {
     if (ws_bytes < gemm_ws(I, J, Kc, t)) return hipErrorInvalidValue;
     part = (int*)ws;
   }
   hipError_t e;
+  // the direct-to-LDS kernels need whole 64-byte contraction chunks
+  if (kern >= 9 && Kc % 64) kern = 2;
   switch (kern) {
-    case 3: e = launch_mfma<256, 128, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
-    case 4: e = launch_mfma<128, 256, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
-    default: e = launch_mfma<128, 128, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 9: e = launch_dma<256, 256, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 10: e = launch_dma<256, 256, 2, 4>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 11: e = launch_dma<128, 256, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 12: e = launch_dma<128, 128, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 3: e = launch_mfma<256, 128, 2, 2, 128>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 4: e = launch_mfma<128, 256, 2, 2, 128>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 5: e = launch_mfma<256, 256, 2, 2, 64>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 6: e = launch_mfma<256, 256, 2, 2, 128>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 7: e = launch_mfma<256, 256, 2, 4, 64>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 8: e = launch_mfma<256, 256, 4, 2, 128>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    default: e = launch_mfma<128, 128, 2, 2, 128>(A, B, I, J, Kc, C, part, splits, epi, s); break;
   }
   if (e != hipSuccess || splits == 1) return e;
   int64_t blocks = cdiv(I * J, 256);

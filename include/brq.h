@@ -66,10 +66,15 @@ enum brq_flag { BRQ_FLAG_NONFINITE = 1 };
 
 /* Launch geometry.  None of these fields changes any result bit. */
 typedef struct brq_tune {
-  int gemm_kernel;   /* 0 default, 1 reference (one output per thread),
-                        2 MFMA 128x128 tile, 3 MFMA 256x128 tile,
-                        4 MFMA 128x256 tile */
-  int split_k;       /* 0 default, else 1, 2 or 4 contraction slices */
+  int gemm_kernel;   /* 0 default (by shape), 1 reference (one output per
+                        thread); register-staged MFMA tiles: 2 128x128,
+                        3 256x128, 4 128x256, 5 256x256 (BK 64), 6 256x256,
+                        7 256x256 (8 waves, BK 64), 8 256x256 (8 waves);
+                        direct-to-LDS 4-stage MFMA tiles (contraction a
+                        multiple of 64, else 2 is used): 9 256x256 (4 waves),
+                        10 256x256 (8 waves), 11 128x256, 12 128x128 */
+  int split_k;       /* 0 default (by shape), else 1, 2, 4, 8 or 16
+                        contraction slices (exact int32 partials) */
   int chunk_log2;    /* 0 default (13), else log2 of the leaves each
                         reduction work-group owns, in [10, 16] */
   int rows_per_block;/* 0 default, else RMSNorm backward rows per block:
@@ -117,7 +122,7 @@ int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols,
  *                                                     w_per_row == 0)
  * q_x [M][K], q_w [N][K] (nn.Linear layout), y [M][N] fp32.
  * Shapes: K % 16 == 0, K <= BRQ_MAX_CONTRACTION.  Workspace: BRQ_OP_QGEMM
- * (only used when split_k > 1).
+ * (non-zero only when the plan splits the contraction).
  * --------------------------------------------------------------------- */
 int brq_qgemm_fwd(const int8_t* q_x, const float* s_x, const int8_t* q_w,
                   const float* s_w, int w_per_row, int64_t M, int64_t N,
