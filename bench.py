@@ -51,9 +51,10 @@ def algorithmic_bytes(linears, inputs, norms, M, arena_elems, hash_bytes):
     b = {}
     b["quant_x"] = sum(M * K * (2 + 2 + 1) for _, K in inputs)
     b["quant_w"] = sum(N * K * (2 + 1 + 1) for _, K, N, _ in linears)
-    b["quant_g"] = sum(M * N * (2 + 2 + 1) for _, _, N, _ in linears)
+    # both dY codes: 2 reads of dY (every statistic needs a full pass) +
+    # two int8 writes
+    b["quant_dy"] = sum(M * N * (2 + 2 + 1 + 1) for _, _, N, _ in linears)
     b["wht_x"] = sum(M * K * (1 + 1 + 1) for _, K in inputs)
-    b["wht_dy"] = sum(M * N * (2 + 2 + 1) for _, _, N, _ in linears)
     b["rmsnorm_fwd"] = sum(M * D * (2 + 2) + 4 * M for _, D in norms)
     b["rmsnorm_bwd"] = sum(M * D * (2 + 2 + 2) + 4 * M + 4 * D for _, D in norms)
     b["grad_norm"] = 4 * arena_elems

@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(HERE, "libbrq.so")
 F32, BF16, I8, I32, U8 = 0, 1, 2, 3, 4
 PER_TENSOR, PER_ROW = 0, 1
 FLAG_NONFINITE = 1
-OP_QUANTIZE, OP_QGEMM, OP_DW_WHT, OP_RMSNORM_BWD, OP_GRAD_NORM = 1, 2, 3, 4, 5
+OP_QUANTIZE, OP_QGEMM, OP_DW_WHT, OP_RMSNORM_BWD, OP_GRAD_NORM, OP_DY_BWD = 1, 2, 3, 4, 5, 6
 MAX_CONTRACTION = 133144
 
 SYMBOLS = [
     "brq_workspace_size", "brq_quantize_lsq", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
     "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
+    "brq_quantize_dy_bwd",
     "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm",
     "brq_hash_workspace_size", "brq_hash_state", "brq_status_string",
     "brq_last_hip_error", "brq_spec_version",
@@ -73,6 +74,9 @@ def lib():
         L.brq_wht_quant_dy.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, sz, vp, vp, vp]
         L.brq_qgemm_dw.restype = i32
         L.brq_qgemm_dw.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, sz, vp, vp]
+        L.brq_quantize_dy_bwd.restype = i32
+        L.brq_quantize_dy_bwd.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp,
+                                          vp, vp]
         L.brq_rmsnorm_fixed_fwd.restype = i32
         L.brq_rmsnorm_fixed_fwd.argtypes = [vp, vp, i32, i64, i64, f32, vp, vp, vp, vp, vp]
         L.brq_rmsnorm_fixed_bwd.restype = i32
@@ -309,6 +313,29 @@ def wht_quant_dy(dy, block, tune=None, ws=None, flags=None, out=None):
                                   _ptr(w), w.numel(), _ptr(flags), _tune(tune), _stream()),
            "wht_quant_dy")
     return q_vt, s_v
+
+
+def quantize_dy_bwd(dy, s_w, block, tune=None, ws=None, flags=None, out=None):
+    """Both backward codes of dY: returns (q_g [M][N], s_g, amax_g, q_vt [N][M],
+    s_v).  ``out`` may hold preallocated tensors in that order (None entries
+    are allocated here)."""
+    _dev(dy, "dy"); _dev(s_w, "s_w")
+    M, N = dy.shape
+    if s_w.numel() != N or s_w.dtype != torch.float32:
+        raise BrqError("s_w: expected fp32 [N]")
+    o = list(out) if out is not None else [None] * 5
+    shapes = [((M, N), torch.int8), ((1,), torch.float32), ((1,), torch.float32),
+              ((N, M), torch.int8), ((1,), torch.float32)]
+    names = ["q_g", "s_g", "amax_g", "q_vt", "s_v"]
+    for i, ((shp, dt), nm) in enumerate(zip(shapes, names)):
+        o[i] = torch.empty(shp, dtype=dt, device=dy.device) if o[i] is None else _out(o[i], shp, dt, nm)
+    need = workspace_size(OP_DY_BWD, M, N, 0, block, tune=tune)
+    w = _ws(need, dy.device, ws)
+    _check(lib().brq_quantize_dy_bwd(_ptr(dy), _fp_code(dy), M, N, _ptr(s_w), block, _ptr(o[0]),
+                                     _ptr(o[1]), _ptr(o[2]), _ptr(o[3]), _ptr(o[4]), _ptr(w),
+                                     w.numel(), _ptr(flags), _tune(tune), _stream()),
+           "quantize_dy_bwd")
+    return tuple(o)
 
 
 def qgemm_dw(q_vt, q_ut, s_x, s_u, s_v, block, tune=None, out=None, ws=None):

@@ -4,6 +4,8 @@
 // here; nothing synchronises.
 #include <string.h>
 
+#include <algorithm>
+
 #include "internal.hpp"
 
 using namespace brq;
@@ -41,6 +43,12 @@ size_t dw_ws(int64_t M, int64_t N, int64_t K, int block, const brq_tune* t) {
 }
 
 bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+size_t dy_bwd_ws(int64_t M, int64_t N, int block, const brq_tune* t) {
+  const int c = flat_chunk_log2(t);
+  size_t a = dy_fused_ws(M, N, c), b = quant_ws(M, N, t), d = wht_dy_ws(M, N, block, c);
+  return std::max(a, std::max(b, d));
+}
 
 int check_dw_shape(int64_t M, int64_t N, int64_t K, int block) {
   if (M < 0 || N < 0 || K < 0) return BRQ_E_SHAPE;
@@ -84,6 +92,7 @@ size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block, co
       return x > y ? x : y;
     }
     case BRQ_OP_GRAD_NORM: return kScalars + flat_reduce_ws(a, flat_chunk_log2(t));
+    case BRQ_OP_DY_BWD: return dy_bwd_ws(a, b, block > 0 ? block : 1, t);
     default: return 0;
   }
 }
@@ -221,6 +230,28 @@ int brq_qgemm_bwd_dw_wht(const int8_t* q_x, const float* s_x, const void* dy, in
   if (r != BRQ_OK) return r;
   return brq_qgemm_dw(q_vt, q_ut, s_x, s_u, s_v, M, N, K, block, dw, gws, gemm_ws(N, K, M, tune),
                       tune, stream);
+}
+
+int brq_quantize_dy_bwd(const void* dy, int dy_dtype, int64_t M, int64_t N, const float* s_w,
+                        int block, int8_t* q_g, float* s_g, float* amax_g, int8_t* q_vt,
+                        float* s_v, void* ws, size_t ws_bytes, int32_t* dflags,
+                        const brq_tune* tune, void* stream) {
+  if (!fp_dtype(dy_dtype)) return BRQ_E_DTYPE;
+  int st = check_dw_shape(M, N, 64, block);
+  if (st != BRQ_OK) return st;
+  if (!s_g || !s_v || (M * N > 0 && (!dy || !s_w || !q_g || !q_vt))) return BRQ_E_NULL;
+  if (!aligned16(dy) || !aligned16(q_g) || !aligned16(q_vt) || !aligned16(s_w)) return BRQ_E_ALIGN;
+  if (!ws || ws_bytes < dy_bwd_ws(M, N, block, tune)) return BRQ_E_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  if (M * N > 0 && dy_fused_ok(dy_dtype, M, N, block))
+    return hip_status(quantize_dy_fused(dy, M, N, s_w, block, q_g, s_g, amax_g, q_vt, s_v, ws,
+                                        flat_chunk_log2(tune), dflags, s));
+  // other shapes: the two definitions one after the other
+  int r = brq_quantize_lsq(dy, dy_dtype, M, N, BRQ_PER_TENSOR, s_w, q_g, nullptr, s_g, amax_g, ws,
+                           ws_bytes, dflags, tune, stream);
+  if (r != BRQ_OK) return r;
+  return brq_wht_quant_dy(dy, dy_dtype, M, N, block, q_vt, s_v, ws, ws_bytes, dflags, tune,
+                          stream);
 }
 
 int brq_rmsnorm_fixed_fwd(const void* x, const void* g, int dtype, int64_t T, int64_t D, float eps,

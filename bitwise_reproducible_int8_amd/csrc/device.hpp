@@ -52,8 +52,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 __device__ __forceinline__ float lsq_k2() { return __uint_as_float(0x3e35bb0au); }
 
 // q = clamp(rint(fl(v * r)), -127, 127); v_rndne_f32 rounds half to even.
+// The product is not flushed: a subnormal v * r and its flushed zero both
+// round to the code 0.
 __device__ __forceinline__ int quant_code(float v, float r) {
-  float t = __builtin_rintf(fmul(v, r));
+  float t = __builtin_rintf(v * r);
   t = t > 127.0f ? 127.0f : t;
   t = t < -127.0f ? -127.0f : t;
   return (int)t;

@@ -1,0 +1,316 @@
+// dy.hip -- both int8 codes of the upstream gradient dY in two passes over
+// it (Open-1B report §3.2 "int8 computation": both straight-through
+// gradient GEMMs run in int8, the weight-gradient one after a Walsh-Hadamard
+// rotation along the contraction dimension, i.e. tokens).
+//
+//   q_g  = LSQ per tensor of g = fl(dY * s_w[n])        (input-gradient GEMM)
+//   q_vt = LSQ per tensor of v = fp32 butterflies of dY
+//          along tokens in aligned blocks, written
+//          token-contiguous [N][M]                     (weight-gradient GEMM)
+//
+// The definitions are those of quantize_lsq with col_mul and of
+// wht_quant_dy; only the data movement is fused.  Both statistics are the
+// canonical pairwise tree over their leaves in row-major [M][N] order.
+// Every 64 aligned leaves of a row form one node(6, .) of that tree
+// (N % 64 == 0, so no run crosses a row), and the node(6) arrays, in
+// row-major order of (row, column / 64), are reduced by the flat tree --
+// levels 6 and up of the same tree.
+//
+// Tile: 128 tokens x 128 columns of bf16 per 256-thread work-group.
+//   row phase:    16-byte loads (8 columns of one row per lane); the g
+//                 leaves of 8 lanes (64 columns) pair up in registers and
+//                 through three DPP butterfly steps; the tile lands in LDS.
+//   column phase: wave w owns columns 32w .. 32w+31; lane l holds column
+//                 32w + (l & 31), tokens 64 (l >> 5) .. +63.  Butterfly
+//                 stages h = 1 .. 32 run in registers; stage 64 pairs lane l
+//                 with lane l ^ 32.  The |v| leaves go back through LDS to
+//                 row order, 16 rows at a time, to form node(6) per row and
+//                 64 columns.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace brq {
+
+namespace {
+
+constexpr int kRows = 128;                 // tokens per tile
+constexpr int kCols = 128;                 // columns per tile
+constexpr int kHalf = 64;                  // tokens per lane in the column phase
+constexpr int kRowBytes = kCols * 2 + 16;  // padded LDS row of the bf16 tile
+constexpr int kTrStride = kCols + 4;       // padded fp32 row of the |v| transpose
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Row phase shared by both passes: lane t covers columns 8 (t & 15) .. +7 of
+// rows (t >> 4) + 16 i, i = 0..7.
+__device__ __forceinline__ u32x4 load_vec(const uint16_t* __restrict__ dy, int64_t N, int64_t m0,
+                                          int64_t col, int r) {
+  return col < N ? ld16(dy + (m0 + r) * N + col) : u32x4{0, 0, 0, 0};
+}
+
+// Column phase: the lane's 64 tokens of its column (DAZ), then the
+// butterflies in stage order h = 1, 2, ..., b/2, each a rounded sum and
+// difference (v_j, v_j+h) <- (fl(v_j + v_j+h), fl(v_j - v_j+h)).
+//
+// Fast path, exact: if every nonzero input of the wave has magnitude
+// >= 2^-103, every input is a multiple of 2^-110 (a bf16 value of exponent e
+// is a multiple of 2^(e-7)), so every sum and difference -- exact, or
+// rounded to binary32, whose ulp is then at least 2^-109 -- is a multiple of
+// 2^-110 and never subnormal: the flushes are no-ops and DAZ has nothing to
+// clear.  A wave holding a smaller nonzero input takes the flushing path.
+template <bool kFlush>
+__device__ __forceinline__ void butterflies(float* v, int b, bool upper) {
+#pragma unroll
+  for (int h = 1; h < kHalf; h *= 2) {
+    if (h < b) {
+#pragma unroll
+      for (int j = 0; j < kHalf; ++j) {
+        if (j & h) continue;
+        const float a = v[j], c = v[j + h];
+        v[j] = kFlush ? fadd(a, c) : a + c;
+        v[j + h] = kFlush ? fsub(a, c) : a - c;
+      }
+    }
+  }
+  if (b > kHalf) {
+    // stage 64: the lower lane holds v_j, the upper lane v_j+64.
+    // v_permlane32_swap exchanges lanes 32..63 of its first operand with
+    // lanes 0..31 of its second: with both operands v_j, the first result
+    // carries the lower half's values in the upper lanes and the second the
+    // upper half's values in the lower lanes.
+#pragma unroll
+    for (int j = 0; j < kHalf; ++j) {
+      const uint32_t x = __float_as_uint(v[j]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      const float p = __uint_as_float(upper ? sw[0] : sw[1]);
+      const float a = upper ? p : v[j], c = upper ? v[j] : p;
+      v[j] = upper ? (kFlush ? fsub(a, c) : a - c) : (kFlush ? fadd(a, c) : a + c);
+    }
+  }
+}
+
+__device__ __forceinline__ void column_wht(const uint8_t* lds, int col, int half, int b,
+                                           float* v) {
+  uint32_t lo = 0xffffffffu;  // min over (|bits| - 1): zero wraps to the top
+#pragma unroll
+  for (int r = 0; r < kHalf; ++r) {
+    const uint32_t h =
+        *reinterpret_cast<const uint16_t*>(lds + (kHalf * half + r) * kRowBytes + 2 * col);
+    lo = min(lo, (h & 0x7fffu) - 1u);
+    v[r] = __uint_as_float(h << 16);
+  }
+  // 0x0C00 is the bf16 pattern of 2^-103
+  if (__any(lo < 0x0C00u - 1u)) {
+#pragma unroll
+    for (int r = 0; r < kHalf; ++r) v[r] = flush(v[r]);
+    butterflies<true>(v, b, half != 0);
+  } else {
+    butterflies<false>(v, b, half != 0);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ dy,
+                                                  const float* __restrict__ sw, int64_t M,
+                                                  int64_t N, int b, float* __restrict__ part_g,
+                                                  float* __restrict__ part_v,
+                                                  float* __restrict__ bmax) {
+  constexpr int kTileBytes = kRows * kRowBytes;
+  constexpr int kTrBytes = 16 * kTrStride * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kTileBytes > kTrBytes ? kTileBytes : kTrBytes];
+  __shared__ float wmax[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t m0 = (int64_t)blockIdx.y * kRows, c0 = (int64_t)blockIdx.x * kCols;
+  const int64_t nb = N / 64;
+
+  // row phase: g leaves and their node(6) per 64 columns
+  const int cg = t & 15, rb = t >> 4;
+  const int64_t colv = c0 + 8 * cg;
+  float s8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s8[e] = colv + e < N ? flush(sw[colv + e]) : 0.0f;
+  u32x4 raw[kRows / 16];
+#pragma unroll
+  for (int i = 0; i < kRows / 16; ++i) raw[i] = load_vec(dy, N, m0, colv, rb + 16 * i);
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRows / 16; ++i) {
+    const int r = rb + 16 * i;
+    st16(lds + r * kRowBytes + 16 * cg, raw[i]);
+    float f[8];
+    unpack_bf16x8(raw[i], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f[e] = fabs_bits(fmul(f[e], s8[e]));
+      mx = fmaxf(mx, f[e]);
+    }
+    const float node = wave_tree_partial<false>(reg_tree<false, 8>(f), 8);
+    if ((cg & 7) == 0 && colv < N) part_g[(m0 + r) * nb + colv / 64] = node;
+  }
+  mx = wave_max(mx);
+  if (lane == 0) wmax[wave] = mx;
+  __syncthreads();
+  if (t == 0)
+    bmax[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] =
+        fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+
+  // column phase
+  const int ccol = 32 * wave + (lane & 31), half = lane >> 5;
+  float v[kHalf];
+  column_wht(lds, ccol, half, b, v);
+  __syncthreads();  // every column read: the tile memory is reused below
+  // |v| to row order, 16 rows at a time: the lanes owning rows
+  // 16p .. 16p+15 (half p / 4) write them, then lane L reads row L >> 3,
+  // columns 16 (L & 7) .. +15 (128 lanes cover 16 rows x 128 columns)
+  float* tr = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int p = 0; p < kRows / 16; ++p) {
+    if (half == p / 4) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tr[i * kTrStride + ccol] = fabs_bits(v[16 * (p & 3) + i]);
+    }
+    __syncthreads();
+    if (t < 128) {
+      const int r = t >> 3, c16 = (t & 7) * 16;
+      float a[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 x4 = *reinterpret_cast<const float4*>(&tr[r * kTrStride + c16 + 4 * q]);
+        a[4 * q] = x4.x; a[4 * q + 1] = x4.y; a[4 * q + 2] = x4.z; a[4 * q + 3] = x4.w;
+      }
+      float node = reg_tree<false, 16>(a);
+      // lanes 4k .. 4k+3 hold the four 16-column nodes of one 64-column run
+      node = node + dpp_xor1(node);  // non-negative leaves: no flush needed
+      node = node + dpp_xor2(node);
+      const int64_t cc = c0 + c16;
+      if ((t & 3) == 0 && cc < N) part_v[(m0 + 16 * p + r) * nb + cc / 64] = node;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ dy,
+                                                  const float* __restrict__ sw, int64_t M,
+                                                  int64_t N, int b,
+                                                  const float* __restrict__ sr4,
+                                                  int8_t* __restrict__ q_g,
+                                                  int8_t* __restrict__ q_vt) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kRows * kRowBytes];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t m0 = (int64_t)blockIdx.y * kRows, c0 = (int64_t)blockIdx.x * kCols;
+  const float r_g = sr4[1], r_v = sr4[3];
+
+  const int cg = t & 15, rb = t >> 4;
+  const int64_t colv = c0 + 8 * cg;
+  float s8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s8[e] = colv + e < N ? flush(sw[colv + e]) : 0.0f;
+  u32x4 raw[kRows / 16];
+#pragma unroll
+  for (int i = 0; i < kRows / 16; ++i) raw[i] = load_vec(dy, N, m0, colv, rb + 16 * i);
+#pragma unroll
+  for (int i = 0; i < kRows / 16; ++i) {
+    const int r = rb + 16 * i;
+    st16(lds + r * kRowBytes + 16 * cg, raw[i]);
+    if (colv < N) {
+      float f[8];
+      unpack_bf16x8(raw[i], f);
+      uint32_t p[2] = {0, 0};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        p[e >> 2] |= (uint32_t)(quant_code(fmul(f[e], s8[e]), r_g) & 0xff) << (8 * (e & 3));
+      *reinterpret_cast<uint2*>(q_g + (m0 + r) * N + colv) = make_uint2(p[0], p[1]);
+    }
+  }
+  __syncthreads();
+  const int ccol = 32 * wave + (lane & 31), half = lane >> 5;
+  float v[kHalf];
+  column_wht(lds, ccol, half, b, v);
+  const int64_t col = c0 + ccol;
+  if (col >= N) return;
+#pragma unroll
+  for (int p = 0; p < kHalf / 16; ++p) {
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      w[i >> 2] |= (uint32_t)(quant_code(v[16 * p + i], r_v) & 0xff) << (8 * (i & 3));
+    st16(q_vt + col * M + m0 + kHalf * half + 16 * p, u32x4{w[0], w[1], w[2], w[3]});
+  }
+}
+
+// Order-free max of the per-work-group maxima, then both LSQ steps:
+// sr4 = {s_g, r_g, s_v, r_v}.
+__global__ __launch_bounds__(256) void k_dy_finalize(const float* __restrict__ sum_g,
+                                                     const float* __restrict__ sum_v,
+                                                     const float* __restrict__ bmax, int64_t nb,
+                                                     float inv_n, float* sr4, float* s_g,
+                                                     float* amax_g, float* s_v) {
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < nb; i += 256) m = fmaxf(m, bmax[i]);
+  m = wave_max(m);
+  __shared__ float w[4];
+  if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float sg = fmul(fmul(sum_g[0], inv_n), lsq_k2());
+    const float sv = fmul(fmul(sum_v[0], inv_n), lsq_k2());
+    sr4[0] = sg;
+    sr4[1] = sg == 0.0f ? 0.0f : flush(1.0f / sg);
+    sr4[2] = sv;
+    sr4[3] = sv == 0.0f ? 0.0f : flush(1.0f / sv);
+    s_g[0] = sg;
+    s_v[0] = sv;
+    if (amax_g) amax_g[0] = fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3]));
+  }
+}
+
+}  // namespace
+
+bool dy_fused_ok(int dtype, int64_t M, int64_t N, int block) {
+  return dtype == BRQ_BF16 && M % kRows == 0 && N % 64 == 0 && block >= 1 && block <= kRows &&
+         M > 0 && N > 0;
+}
+
+size_t dy_fused_ws(int64_t M, int64_t N, int chunk_log2) {
+  const int64_t P = M * (N / 64);
+  const int64_t nblk = cdiv(N, kCols) * (M / kRows);
+  return 2 * align256((size_t)(P > 0 ? P : 1) * sizeof(float)) +
+         align256((size_t)(nblk > 0 ? nblk : 1) * sizeof(float)) +
+         flat_reduce_ws(P, chunk_log2) + 256;
+}
+
+hipError_t quantize_dy_fused(const void* dy, int64_t M, int64_t N, const float* sw, int block,
+                             int8_t* q_g, float* s_g, float* amax_g, int8_t* q_vt, float* s_v,
+                             void* ws, int chunk_log2, int32_t* dflags, hipStream_t s) {
+  const int64_t P = M * (N / 64);
+  const int64_t gx = cdiv(N, kCols), gy = M / kRows;
+  char* w = (char*)ws;
+  float* part_g = (float*)w;
+  w += align256((size_t)P * sizeof(float));
+  float* part_v = (float*)w;
+  w += align256((size_t)P * sizeof(float));
+  float* bmax = (float*)w;
+  w += align256((size_t)(gx * gy) * sizeof(float));
+  void* fws = w;
+  w += flat_reduce_ws(P, chunk_log2);
+  float* sc = (float*)w;  // [0,1] g sum/max, [2,3] v sum/max, [4..7] s_g r_g s_v r_v
+  dim3 g((unsigned)gx, (unsigned)gy), b(256);
+  hipLaunchKernelGGL(k_dy_stats, g, b, 0, s, (const uint16_t*)dy, sw, M, N, block, part_g, part_v,
+                     bmax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = flat_reduce(part_g, BRQ_F32, LEAF_RAW, nullptr, P, 1, sc, fws, chunk_log2, dflags, s)) !=
+      hipSuccess)
+    return e;
+  if ((e = flat_reduce(part_v, BRQ_F32, LEAF_RAW, nullptr, P, 1, sc + 2, fws, chunk_log2, dflags,
+                       s)) != hipSuccess)
+    return e;
+  const float inv_n = 1.0f / (float)(M * N);  // host binary32 division, correctly rounded
+  hipLaunchKernelGGL(k_dy_finalize, dim3(1), dim3(256), 0, s, sc, sc + 2, bmax, gx * gy, inv_n,
+                     sc + 4, s_g, amax_g, s_v);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dy_codes, g, b, 0, s, (const uint16_t*)dy, sw, M, N, block, sc + 4, q_g,
+                     q_vt);
+  return hipGetLastError();
+}
+
+}  // namespace brq

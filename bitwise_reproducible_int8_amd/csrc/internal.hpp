@@ -74,6 +74,13 @@ hipError_t wht_quant_dy(const void* dy, int dtype, int64_t M, int64_t N,
                         int block, int8_t* q_vt, float* s_v, void* ws,
                         int chunk_log2, int32_t* dflags, hipStream_t s);
 
+// ---- both backward codes of dY in two passes (dy.hip) -------------------------
+bool dy_fused_ok(int dtype, int64_t M, int64_t N, int block);
+size_t dy_fused_ws(int64_t M, int64_t N, int chunk_log2);
+hipError_t quantize_dy_fused(const void* dy, int64_t M, int64_t N, const float* sw, int block,
+                             int8_t* q_g, float* s_g, float* amax_g, int8_t* q_vt, float* s_v,
+                             void* ws, int chunk_log2, int32_t* dflags, hipStream_t s);
+
 // ---- RMSNorm / grad-norm ------------------------------------------------------
 hipError_t rmsnorm_fwd(const void* x, const void* g, int dtype, int64_t T,
                        int64_t D, float eps, void* y, float* rstd,

@@ -13,12 +13,14 @@ torch's current stream:
   3. per-output-channel LSQ codes of each weight, plus the
      transposed copy for the input-gradient GEMM, then the
      forward GEMM + dequantisation                             (qgemm_fwd)
-  4. dY scaled by the weight step sizes and quantised, then
-     the input-gradient GEMM                                   (qgemm_bwd_dx)
+  4. both backward codes of each dY in two passes over it: dY
+     scaled by the weight step sizes and quantised, and dY
+     rotated along tokens and quantised                       (quantize_dy_bwd)
+     then the input-gradient GEMM                              (qgemm_bwd_dx)
   5. Walsh-Hadamard rotation + requantisation of each distinct
-     activation code and of each dY along tokens, then the
-     weight-gradient GEMM into the gradient arena              (qgemm_bwd_dw_wht,
-                                                                in its three stages)
+     activation code along tokens, then the weight-gradient
+     GEMM into the gradient arena                              (qgemm_bwd_dw_wht,
+                                                                in its stages)
   6. RMSNorm backward of each norm into the arena              (rmsnorm_fixed)
   7. global l2 norm over the gradient arena                     (grad_norm)
   8. SHA-256 state hash of every output and gradient          (hash_state)
@@ -39,10 +41,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (BrqError, OP_DW_WHT, OP_GRAD_NORM, OP_QGEMM, OP_QUANTIZE, OP_RMSNORM_BWD,
-               grad_norm, hash_state, hash_state_workspace_size, qgemm_bwd_dx, qgemm_dw,
-               qgemm_fwd, quantize_lsq, rmsnorm_fixed_bwd, rmsnorm_fixed_fwd, wht_quant_dy,
-               wht_quant_x, workspace_size)
+from . import (BrqError, OP_DW_WHT, OP_DY_BWD, OP_GRAD_NORM, OP_QGEMM, OP_QUANTIZE,
+               OP_RMSNORM_BWD, grad_norm, hash_state, hash_state_workspace_size, qgemm_bwd_dx,
+               qgemm_dw, qgemm_fwd, quantize_dy_bwd, quantize_lsq, rmsnorm_fixed_bwd,
+               rmsnorm_fixed_fwd, wht_quant_x, workspace_size)
 
 
 class _NoTimer:
@@ -127,7 +129,7 @@ class LayerStep:
                      workspace_size(OP_QGEMM, M, N, K, tune=tune),
                      workspace_size(OP_QGEMM, M, K, N, tune=tune),
                      workspace_size(OP_QGEMM, N, K, M, tune=tune),
-                     workspace_size(OP_DW_WHT, M, N, 64, block, tune=tune)]
+                     workspace_size(OP_DY_BWD, M, N, 0, block, tune=tune)]
         for (_n, h, _g, _d) in self.norms:
             need.append(workspace_size(OP_RMSNORM_BWD, *h.shape, tune=tune))
         need.append(hash_state_workspace_size(self.hash_list()))
@@ -167,10 +169,11 @@ class LayerStep:
                       out=self.y[i], ws=ws)
             T.end("gemm_fwd")
         for i in range(len(self.linears)):
-            T.begin("quant_g")
-            quantize_lsq(self.dy[i], col_mul=self.s_w[i], tune=tune, ws=ws, flags=fl,
-                         out=(self.q_g[i], None, self.s_g[i], self.amax_g[i]))
-            T.end("quant_g")
+            T.begin("quant_dy")
+            quantize_dy_bwd(self.dy[i], self.s_w[i], b, tune=tune, ws=ws, flags=fl,
+                            out=(self.q_g[i], self.s_g[i], self.amax_g[i], self.q_vt[i],
+                                 self.s_v[i]))
+            T.end("quant_dy")
             T.begin("gemm_dx")
             qgemm_bwd_dx(self.q_g[i], self.s_g[i], self.q_wt[i], tune=tune, out=self.dx[i], ws=ws)
             T.end("gemm_dx")
@@ -179,9 +182,6 @@ class LayerStep:
             wht_quant_x(self.q_x[xin], b, tune=tune, ws=ws, out=(self.q_ut[xin], self.s_u[xin]))
             T.end("wht_x")
         for i, (_name, _K, _N, xin) in enumerate(self.linears):
-            T.begin("wht_dy")
-            wht_quant_dy(self.dy[i], b, tune=tune, ws=ws, flags=fl, out=(self.q_vt[i], self.s_v[i]))
-            T.end("wht_dy")
             T.begin("gemm_dw")
             qgemm_dw(self.q_vt[i], self.q_ut[xin], self.s_x[xin], self.s_u[xin], self.s_v[i], b,
                      tune=tune, out=self.dw[i], ws=ws)

@@ -87,7 +87,8 @@ enum brq_op {
   BRQ_OP_QGEMM = 2,        /* a = M, b = N, c = K (fwd, dx, dw GEMMs) */
   BRQ_OP_DW_WHT = 3,       /* a = M, b = N, c = K, block = Hadamard block */
   BRQ_OP_RMSNORM_BWD = 4,  /* a = T, b = D */
-  BRQ_OP_GRAD_NORM = 5     /* a = n */
+  BRQ_OP_GRAD_NORM = 5,    /* a = n */
+  BRQ_OP_DY_BWD = 6        /* a = M, b = N, block = Hadamard block */
 };
 size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block,
                           const struct brq_tune* tune);
@@ -182,6 +183,25 @@ int brq_qgemm_dw(const int8_t* q_vt, const int8_t* q_ut, const float* s_x,
                  const float* s_u, const float* s_v, int64_t M, int64_t N,
                  int64_t K, int block, float* dw, void* ws, size_t ws_bytes,
                  const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * quantize_dy_bwd -- both int8 codes of the upstream gradient for the two
+ * straight-through gradient GEMMs (§3.2 "int8 computation"), in two passes
+ * over dY.  Bit-identical to the two calls it fuses:
+ *     q_g, s_g, amax_g  = brq_quantize_lsq(dy, PER_TENSOR, col_mul = s_w)
+ *     q_vt, s_v         = brq_wht_quant_dy(dy, block)
+ * dy [M][N] (BRQ_F32 or BRQ_BF16), s_w [N] fp32 (the per-channel weight
+ * step sizes), q_g [M][N] int8, q_vt [N][M] int8 (token-contiguous),
+ * s_g, s_v [1] fp32, amax_g [1] fp32 or NULL.  Shapes as brq_wht_quant_dy.
+ * The two-pass form runs for bf16 with M % 128 == 0; other shapes run the
+ * two definitions in sequence.  Raises BRQ_FLAG_NONFINITE when a statistic
+ * is not finite.  Workspace: BRQ_OP_DY_BWD.
+ * --------------------------------------------------------------------- */
+int brq_quantize_dy_bwd(const void* dy, int dy_dtype, int64_t M, int64_t N,
+                        const float* s_w, int block, int8_t* q_g, float* s_g,
+                        float* amax_g, int8_t* q_vt, float* s_v, void* ws,
+                        size_t ws_bytes, int32_t* dflags,
+                        const struct brq_tune* tune, void* stream);
 
 /* ---------------------------------------------------------------------
  * rmsnorm_fixed -- RMSNorm in FP32 with a fixed reduction order (§3.1

@@ -223,6 +223,45 @@ def test_qgemm_bwd_dw_wht(M, N, K, b):
         assert_bitwise(gsv, np.array([sv], np.float32), "s_v")
 
 
+@pytest.mark.parametrize("M,N,b,bf16", [(384, 320, 128, True), (256, 512, 64, True),
+                                        (128, 64, 16, True), (1024, 2048, 128, True),
+                                        (64, 256, 64, False), (192, 256, 64, True),
+                                        (512, 768, 1, True)])
+def test_quantize_dy_bwd(M, N, b, bf16):
+    """Both dY codes in one call equal quantize_lsq(col_mul) and the rotated
+    LSQ of the oracle (two-pass form and its fallbacks)."""
+    say("quantize_dy_bwd", M, N, b, bf16)
+    dy = syn.student_t3((M, N), 1e-3, tag=230, bf16=bf16)
+    sw = syn.normal((N,), 0.01, mean=0.02, tag=231)
+    qg, _, sg, ag, fl = orc.quantize_lsq(dy, col_mul=sw)
+    qv, sv, _, fl2 = orc.wht_fp_quant(dy, b)
+    for chunk in (0, 10):
+        flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+        gqg, gsg, gag, gqvt, gsv = brq.quantize_dy_bwd(to_dev(dy), to_dev(sw), b,
+                                                       tune={"chunk_log2": chunk}, flags=flags)
+        assert_bitwise(gqg, qg, f"q_g chunk {chunk}")
+        assert_bitwise(gsg, sg, "s_g")
+        assert_bitwise(gag, ag, "amax_g")
+        assert_bitwise(gqvt, np.ascontiguousarray(qv.T), "q_v^T")
+        assert_bitwise(gsv, np.array([sv], np.float32), "s_v")
+        assert int(flags.item()) == fl == fl2 == 0
+
+
+def test_quantize_dy_bwd_edges():
+    say("quantize_dy_bwd_edges")
+    M, N = 256, 128
+    z = np.zeros((M, N), np.uint16)
+    sw = np.full(N, 0.5, np.float32)
+    gqg, gsg, _, gqvt, gsv = brq.quantize_dy_bwd(to_dev(z), to_dev(sw), 128)
+    assert not to_np(gqg).any() and not to_np(gqvt).any()
+    assert float(gsg.item()) == 0.0 and float(gsv.item()) == 0.0
+    bad = syn.normal((M, N), 1e-3, tag=232, bf16=True)
+    bad[7, 9] = 0x7f80  # +inf in bf16
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    brq.quantize_dy_bwd(to_dev(bad), to_dev(sw), 128, flags=flags)
+    assert int(flags.item()) == brq.FLAG_NONFINITE
+
+
 def test_qgemm_dw_stage_alone():
     say("qgemm_dw")
     rng = np.random.default_rng(17)
