@@ -27,7 +27,8 @@ SYMBOLS = [
     "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
     "brq_quantize_dy_bwd",
     "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm",
-    "brq_hash_workspace_size", "brq_hash_state", "brq_status_string",
+    "brq_hash_workspace_size", "brq_hash_state", "brq_hash_digests_workspace_size",
+    "brq_hash_tensor_digests", "brq_hash_combine", "brq_status_string",
     "brq_last_hip_error", "brq_spec_version",
 ]
 
@@ -87,6 +88,12 @@ def lib():
         L.brq_hash_workspace_size.argtypes = [vp, i32]
         L.brq_hash_state.restype = i32
         L.brq_hash_state.argtypes = [vp, i32, vp, vp, sz, vp]
+        L.brq_hash_digests_workspace_size.restype = sz
+        L.brq_hash_digests_workspace_size.argtypes = [vp, i32]
+        L.brq_hash_tensor_digests.restype = i32
+        L.brq_hash_tensor_digests.argtypes = [vp, i32, vp, vp, sz, vp]
+        L.brq_hash_combine.restype = i32
+        L.brq_hash_combine.argtypes = [vp, i32, vp, vp]
         L.brq_status_string.restype = C.c_char_p
         L.brq_status_string.argtypes = [i32]
         L.brq_last_hip_error.restype = i32
@@ -437,3 +444,34 @@ def hash_state(tensors, ws=None, out=None):
     _check(lib().brq_hash_state(refs, len(tensors), _ptr(digest), _ptr(w), w.numel(), _stream()),
            "hash_state")
     return digest
+
+
+def hash_digests_workspace_size(tensors) -> int:
+    refs, _ = _refs(tensors)
+    return int(lib().brq_hash_digests_workspace_size(refs, len(tensors)))
+
+
+def hash_tensor_digests(tensors, out, ws=None):
+    """Tensor digests of ``tensors`` (list of (name, device tensor[, dtype
+    code])) into ``out``, a device uint8 tensor of 32 * len(tensors) bytes."""
+    refs, _keep = _refs(tensors)
+    _dev(out, "out")
+    if out.dtype != torch.uint8 or out.numel() != 32 * len(tensors):
+        raise BrqError("out: expected uint8 [32 * n]")
+    need = int(lib().brq_hash_digests_workspace_size(refs, len(tensors)))
+    w = _ws(need, out.device, ws)
+    _check(lib().brq_hash_tensor_digests(refs, len(tensors), _ptr(out), _ptr(w), w.numel(),
+                                         _stream()), "hash_tensor_digests")
+    return out
+
+
+def hash_combine(digests, out=None):
+    """State digest: SHA-256 of the concatenated 32-byte tensor digests."""
+    _dev(digests, "digests")
+    if digests.dtype != torch.uint8 or digests.numel() % 32:
+        raise BrqError("digests: expected uint8 [32 * n]")
+    d = out if out is not None else torch.empty(32, dtype=torch.uint8, device=digests.device)
+    _out(d, (32,), torch.uint8, "out")
+    _check(lib().brq_hash_combine(_ptr(digests), digests.numel() // 32, _ptr(d), _stream()),
+           "hash_combine")
+    return d

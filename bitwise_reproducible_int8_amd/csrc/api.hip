@@ -295,10 +295,9 @@ size_t brq_hash_workspace_size(const brq_tensor_ref* t, int n) {
   return hash_ws(t, n);
 }
 
-int brq_hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* ws, size_t ws_bytes,
-                   void* stream) {
+static int check_refs(const brq_tensor_ref* t, int n) {
   if (n < 0) return BRQ_E_SHAPE;
-  if (!digest32 || (n > 0 && !t)) return BRQ_E_NULL;
+  if (n > 0 && !t) return BRQ_E_NULL;
   for (int i = 0; i < n; ++i) {
     if (t[i].dtype < BRQ_F32 || t[i].dtype > BRQ_U8) return BRQ_E_DTYPE;
     if (t[i].ndim < 0 || t[i].ndim > 8) return BRQ_E_SHAPE;
@@ -311,9 +310,39 @@ int brq_hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* ws, 
     if (!aligned16(t[i].data)) return BRQ_E_ALIGN;
     if (t[i].name && strlen(t[i].name) > 255) return BRQ_E_ARG;
   }
+  return BRQ_OK;
+}
+
+int brq_hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int st = check_refs(t, n);
+  if (st != BRQ_OK) return st;
+  if (!digest32) return BRQ_E_NULL;
   if (!aligned16(digest32)) return BRQ_E_ALIGN;
   if (!ws || ws_bytes < hash_ws(t, n)) return BRQ_E_WORKSPACE;
   return hip_status(hash_state(t, n, digest32, ws, as_stream(stream)));
+}
+
+size_t brq_hash_digests_workspace_size(const brq_tensor_ref* t, int n) {
+  if (n < 0 || (n > 0 && !t)) return 0;
+  return hash_digests_ws(t, n);
+}
+
+int brq_hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* digests, void* ws,
+                            size_t ws_bytes, void* stream) {
+  int st = check_refs(t, n);
+  if (st != BRQ_OK) return st;
+  if (n > 0 && !digests) return BRQ_E_NULL;
+  if (!aligned16(digests)) return BRQ_E_ALIGN;
+  if (!ws || ws_bytes < hash_digests_ws(t, n)) return BRQ_E_WORKSPACE;
+  return hip_status(hash_tensor_digests(t, n, digests, ws, as_stream(stream)));
+}
+
+int brq_hash_combine(const uint8_t* digests, int n, uint8_t* digest32, void* stream) {
+  if (n < 0) return BRQ_E_SHAPE;
+  if (!digest32 || (n > 0 && !digests)) return BRQ_E_NULL;
+  if (!aligned16(digests) || !aligned16(digest32)) return BRQ_E_ALIGN;
+  return hip_status(hash_combine(digests, n, digest32, as_stream(stream)));
 }
 
 }  // extern "C"

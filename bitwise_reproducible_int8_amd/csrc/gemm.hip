@@ -15,6 +15,7 @@
 namespace brq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Epi {
   int kind;
@@ -377,7 +378,10 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
 
   // Epilogue: quad-transpose each 16x16 result block so a lane holds four
   // consecutive columns of one row, then 16-byte stores (element-wise at a
-  // ragged right edge).  Split-K writes exact int32 partials instead.
+  // ragged right edge).  The fp32 outputs go out as non-temporal (streaming)
+  // stores: nothing in the kernel reads them back, and on MI355X this runs
+  // the output write markedly faster than the default cached path.  Split-K
+  // writes exact int32 partials instead (cached: the reduction reads them).
   const int q = lane & 3;
   const int rsub = 4 * (lane >> 4) + q;   // row within the 16x16 block
   const int csub = (lane & 15) & ~3;      // first of the lane's 4 columns
@@ -410,7 +414,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = dequant(v[e], c4[e]);
         if (full) {
-          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+          __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(dst));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)

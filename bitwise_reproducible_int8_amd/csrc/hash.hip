@@ -7,12 +7,12 @@
 //
 // The work is integer ALU (about 24 VALU operations per hashed byte), so
 // the kernels are built to keep every SIMD busy:
-//   - one launch hashes every 4096-byte slice of up to kBatch buffers (all
-//     tensors' leaves together, then each Merkle level of all tensors
-//     together), one lane per slice;
-//   - a full slice streams its 64 blocks with the next block's loads in
-//     flight while the current one is compressed, and its 65th (padding)
-//     block is a constant;
+//   - one launch hashes every full 4096-byte slice of up to kBatch buffers
+//     (all tensors' leaves together, then each Merkle level of all tensors
+//     together), one lane per slice; a second, one-wave launch takes each
+//     buffer's shorter last slice;
+//   - a full slice streams its 64 blocks (other waves hide the load
+//     latency), and its 65th (padding) block is a constant;
 //   - the round function is written in the shapes gfx950 has single
 //     instructions for: rotate (v_alignbit_b32), three-way xor
 //     (v_xor3_b32), bit select (v_bfi_b32), three-way add (v_add3_u32).
@@ -144,26 +144,19 @@ __device__ void sha256_bytes(const uint8_t* p, uint64_t len, uint8_t* out) {
   st.store(out);
 }
 
-// A full 4096-byte slice: 64 data blocks, the next block's loads issued
-// before the current compression, then the constant padding block (0x80,
-// zeros, bit length 32768).
+// A full 4096-byte slice: 64 data blocks, then the constant padding block
+// (0x80, zeros, bit length 32768).  Load latency is hidden by the other
+// waves of the SIMD rather than by a prefetch that would cost 16 registers.
 __device__ __forceinline__ void sha256_slice4096(const uint8_t* p, uint8_t* out) {
   Sha st;
   st.init();
   const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  u32x4 cur[4] = {q[0], q[1], q[2], q[3]};
 #pragma unroll 1
   for (int i = 0; i < kLeaf / 64; ++i) {
-    u32x4 nxt[4];
-    if (i + 1 < kLeaf / 64) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) nxt[j] = q[4 * (i + 1) + j];
-    }
+    const u32x4 cur[4] = {q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]};
     uint32_t w[16];
     be_words(cur, w);
     st.block(w);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
   }
   uint32_t pad[16];
 #pragma unroll
@@ -185,17 +178,31 @@ struct SliceBatch {
   int n;
 };
 
-__global__ __launch_bounds__(256) void k_sha_slices(SliceBatch b) {
+// Full 4096-byte slices, one lane each; a buffer's partial last slice (or
+// the one empty slice of an empty buffer) is left to k_sha_partial.  Kept
+// apart from the generic path so the 4 KiB loop needs few registers: the
+// hash runs beside the GEMMs on a second stream, and its waves must fit next
+// to a GEMM work-group's.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_sha_full(
+    SliceBatch b) {
   const uint64_t g = (uint64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= b.first[b.n]) return;
   int i = 0;
   while (i + 1 < b.n && g >= b.first[i + 1]) ++i;
   const uint64_t j = g - b.first[i];
   const uint64_t off = j * kLeaf;
+  if (b.nbytes[i] >= off + kLeaf) sha256_slice4096(b.src[i] + off, b.dst[i] + 32 * j);
+}
+
+// The last slice of each buffer when it is shorter than 4096 bytes.
+__global__ __launch_bounds__(64) void k_sha_partial(SliceBatch b) {
+  const int i = threadIdx.x;
+  if (i >= b.n) return;
   const uint64_t nb = b.nbytes[i];
-  const uint64_t len = nb > off ? (nb - off < (uint64_t)kLeaf ? nb - off : (uint64_t)kLeaf) : 0;
-  if (len == (uint64_t)kLeaf) sha256_slice4096(b.src[i] + off, b.dst[i] + 32 * j);
-  else sha256_bytes(b.src[i] + off, len, b.dst[i] + 32 * j);
+  if (nb != 0 && nb % kLeaf == 0) return;
+  const uint64_t j = b.first[i + 1] - b.first[i] - 1;
+  const uint64_t off = j * kLeaf;
+  sha256_bytes(b.src[i] + off, nb - off, b.dst[i] + 32 * j);
 }
 
 // Tensor digests: SHA-256(header | root), one lane per tensor.
@@ -271,7 +278,10 @@ size_t tensor_region(uint64_t nbytes) {
 hipError_t launch_slices(SliceBatch& b, hipStream_t s) {
   if (b.n == 0) return hipSuccess;
   const uint64_t total = b.first[b.n];
-  hipLaunchKernelGGL(k_sha_slices, dim3((unsigned)cdivu(total, 256)), dim3(256), 0, s, b);
+  hipLaunchKernelGGL(k_sha_full, dim3((unsigned)cdivu(total, 256)), dim3(256), 0, s, b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sha_partial, dim3(1), dim3(64), 0, s, b);
   b.n = 0;
   b.first[0] = 0;
   return hipGetLastError();
@@ -288,15 +298,19 @@ void add_slices(SliceBatch& b, const uint8_t* src, uint64_t nbytes, uint8_t* dst
 
 }  // namespace
 
-size_t hash_ws(const brq_tensor_ref* t, int n) {
-  size_t s = align256(32 * (uint64_t)(n > 0 ? n : 1));
+size_t hash_digests_ws(const brq_tensor_ref* t, int n) {
+  size_t s = 256;
   for (int i = 0; i < n; ++i) s += tensor_region(tensor_bytes(t[i]));
   return s;
 }
 
-hipError_t hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* ws, hipStream_t s) {
-  uint8_t* tdig = (uint8_t*)ws;
-  uint8_t* base = tdig + align256(32 * (uint64_t)(n > 0 ? n : 1));
+size_t hash_ws(const brq_tensor_ref* t, int n) {
+  return align256(32 * (uint64_t)(n > 0 ? n : 1)) + hash_digests_ws(t, n);
+}
+
+hipError_t hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* tdig, void* ws,
+                               hipStream_t s) {
+  uint8_t* base = (uint8_t*)ws;
   hipError_t e;
   SliceBatch b{};
   // pass over levels: level 0 hashes tensor bytes, level l > 0 hashes the
@@ -324,7 +338,7 @@ hipError_t hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* w
     if ((e = launch_slices(b, s)) != hipSuccess) return e;
     if (!any) break;
   }
-  // tensor digests
+  // tensor digests: SHA-256(header | root)
   HeaderBatch hb{};
   uint8_t* region = base;
   for (int i = 0; i < n; ++i) {
@@ -360,8 +374,20 @@ hipError_t hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* w
       hb.n = 0;
     }
   }
+  return hipSuccess;
+}
+
+hipError_t hash_combine(const uint8_t* tdig, int n, uint8_t* digest32, hipStream_t s) {
   hipLaunchKernelGGL(k_sha_state, dim3(1), dim3(1), 0, s, tdig, n, digest32);
   return hipGetLastError();
+}
+
+hipError_t hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* ws, hipStream_t s) {
+  uint8_t* tdig = (uint8_t*)ws;
+  void* rest = tdig + align256(32 * (uint64_t)(n > 0 ? n : 1));
+  hipError_t e = hash_tensor_digests(t, n, tdig, rest, s);
+  if (e != hipSuccess) return e;
+  return hash_combine(tdig, n, digest32, s);
 }
 
 }  // namespace brq

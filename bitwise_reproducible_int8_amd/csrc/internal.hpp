@@ -96,6 +96,10 @@ hipError_t grad_norm(const float* v, int64_t n, float* sumsq, float* norm,
 
 // ---- hash ------------------------------------------------------------------------
 size_t hash_ws(const brq_tensor_ref* t, int n);
+size_t hash_digests_ws(const brq_tensor_ref* t, int n);
+hipError_t hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* digests, void* ws,
+                               hipStream_t s);
+hipError_t hash_combine(const uint8_t* digests, int n, uint8_t* digest32, hipStream_t s);
 hipError_t hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32,
                       void* ws, hipStream_t s);
 

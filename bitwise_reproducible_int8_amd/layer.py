@@ -25,6 +25,11 @@ torch's current stream:
   7. global l2 norm over the gradient arena                     (grad_norm)
   8. SHA-256 state hash of every output and gradient          (hash_state)
 
+The hash runs last, in one batched call on the same stream.  (Hashing each
+tensor on a second stream as soon as it is written measured slower on
+MI355X: the integer-ALU hash and the GEMMs then share CUs and both slow
+down.)
+
 The rotated code of an activation depends on that activation alone, so
 linears that share an input (Q/K/V, gate/up) share one rotation; the results
 are the same bits as the one-call qgemm_bwd_dw_wht per linear.

@@ -262,6 +262,21 @@ size_t brq_hash_workspace_size(const brq_tensor_ref* t, int n);
 int brq_hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32, void* ws,
                    size_t ws_bytes, void* stream);
 
+/* hash_state in its two halves, so each tensor can be digested as soon as it
+ * is final (for instance on a second stream, overlapping other work):
+ *   brq_hash_tensor_digests: digests[32 i .. 32 i + 31] = tensor digest of
+ *     t[i] (the Merkle root under its typed header, as above); `digests` is
+ *     a 16-byte aligned device buffer of 32 n bytes.  Workspace:
+ *     brq_hash_digests_workspace_size(t, n); calls that overlap need
+ *     distinct workspaces.
+ *   brq_hash_combine: digest32 = SHA-256 of the n digests in order.
+ * brq_hash_state(t, n) equals brq_hash_combine over the digests of t. */
+size_t brq_hash_digests_workspace_size(const brq_tensor_ref* t, int n);
+int brq_hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* digests,
+                            void* ws, size_t ws_bytes, void* stream);
+int brq_hash_combine(const uint8_t* digests, int n, uint8_t* digest32,
+                     void* stream);
+
 /* Status text, HIP error of the last BRQ_E_HIP in this thread, version. */
 const char* brq_status_string(int status);
 int brq_last_hip_error(void);

@@ -387,6 +387,30 @@ def test_hash_state_vs_oracle():
     assert bytes(to_np(brq.hash_state([(n, to_dev(a)) for n, a in ts]))) != want
 
 
+def test_hash_split_equals_state():
+    """Tensor digests in groups (and on another stream), then the combine,
+    equal hash_state over the same list and the oracle."""
+    say("hash_split")
+    rng = np.random.default_rng(23)
+    ts = [("a", rng.standard_normal((40, 4096 + 8)).astype(np.float32)),
+          ("b", rng.integers(0, 65535, size=(9, 17), dtype=np.uint16)),
+          ("c", rng.integers(-128, 127, size=(4096 * 129,), dtype=np.int8)),
+          ("d", np.zeros((0, 4), np.float32))]
+    want = orc.hash_state(ts)
+    dts = [(n, to_dev(a)) for n, a in ts]
+    assert bytes(to_np(brq.hash_state(dts))) == want
+    dig = torch.zeros(32 * len(dts), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        brq.hash_tensor_digests(dts[:2], dig[:64])
+        brq.hash_tensor_digests(dts[2:], dig[64:])
+    torch.cuda.current_stream().wait_stream(side)
+    assert bytes(to_np(brq.hash_combine(dig))) == want
+    for i, (n, a) in enumerate(ts):
+        assert bytes(to_np(dig[32 * i:32 * i + 32])) == orc.tensor_digest(n, a)
+
+
 # --------------------------------------------------------------------------
 # determinism: repeated calls and concurrent streams
 # --------------------------------------------------------------------------
