@@ -194,6 +194,9 @@ def main():
                     help="tokens of the CPU-oracle sample (0 skips it)")
     ap.add_argument("--no-instrument", action="store_true",
                     help="skip the per-call event pass (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy one 1 GiB device buffer once, so "
+                         "that a counter run sees a kernel of known HBM traffic")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -260,6 +263,15 @@ def main():
     torch.cuda.synchronize()
     ms_hash_off = e0.elapsed_time(e1) / args.steps
     log(f"hash off: {ms_hash_off:.3f} ms/step")
+    if args.copy_calibration:
+        # 1 GiB read + 1 GiB written; the counter readings of this copy scale
+        # the GEMM's FETCH_SIZE / WRITE_SIZE readings to bytes
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     flags = int(step.flags.item())
     want = stored_digest("layer", "state") if M == 32768 else None
     exact = None if want is None else (digest == want and flags == 0)

@@ -215,28 +215,34 @@ struct HeaderBatch {
 };
 
 __global__ __launch_bounds__(64) void k_sha_headers(HeaderBatch hb) {
+  // the batch's header bytes and each tensor's root, staged in LDS with
+  // coalesced word copies, then one lane per tensor hashes its message
+  __shared__ __attribute__((aligned(16))) uint8_t msg[kHdrBatch][kHdrMax + 32];
+  static_assert(kHdrMax % 4 == 0, "word copies");
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&hb.bytes[0][0]);
+    for (int w = threadIdx.x; w < kHdrBatch * kHdrMax / 4; w += 64) {
+      const int row = w / (kHdrMax / 4), col = w % (kHdrMax / 4);
+      *reinterpret_cast<uint32_t*>(&msg[row][4 * col]) = src[w];
+    }
+  }
+  __syncthreads();
   const int i = threadIdx.x;
   if (i >= hb.n) return;
   const int n = hb.len[i];
   const int len = n + 32;
+  for (int k = 0; k < 32; ++k) msg[i][n + k] = hb.root[i][k];
   Sha st;
   st.init();
   int off = 0;
-  // message = header bytes then the 32 root bytes, fed block by block
-  auto byte_at = [&](int k) -> uint32_t {
-    return k < n ? (uint32_t)hb.bytes[i][k] : (uint32_t)hb.root[i][k - n];
-  };
   for (; off + 64 <= len; off += 64) {
     uint32_t w[16];
     for (int q = 0; q < 16; ++q)
-      w[q] = (byte_at(off + 4 * q) << 24) | (byte_at(off + 4 * q + 1) << 16) |
-             (byte_at(off + 4 * q + 2) << 8) | byte_at(off + 4 * q + 3);
+      w[q] = ((uint32_t)msg[i][off + 4 * q] << 24) | ((uint32_t)msg[i][off + 4 * q + 1] << 16) |
+             ((uint32_t)msg[i][off + 4 * q + 2] << 8) | (uint32_t)msg[i][off + 4 * q + 3];
     st.block(w);
   }
-  uint8_t tail[64];
-  const int rem = len - off;
-  for (int q = 0; q < rem; ++q) tail[q] = (uint8_t)byte_at(off + q);
-  sha_tail(st, tail, rem, (uint64_t)len);
+  sha_tail(st, &msg[i][off], len - off, (uint64_t)len);
   st.store(hb.out[i]);
 }
 
