@@ -34,6 +34,26 @@ struct Epi {
 
 __device__ __forceinline__ float dequant(int acc, float c) { return fmul((float)acc, c); }
 
+// XCD-aware tile order.  Work-group p runs on XCD p % 8 (round-robin
+// dispatch), so when the tile count is a multiple of 8 the linear index is
+// permuted to give each XCD a contiguous range; inside a range, groups of 8
+// tile rows are swept column by column, so concurrently running tiles share
+// operand rows in that XCD's L2.
+__device__ __forceinline__ void tile_of(uint32_t p, uint32_t gm, uint32_t gn, int64_t& bm,
+                                        int64_t& bn) {
+  // tile counts fit 32 bits (the host rejects larger launches), so the
+  // index arithmetic is unsigned 32-bit
+  const uint32_t total = gm * gn;
+  if ((total & 7) == 0) p = (p & 7) * (total >> 3) + (p >> 3);
+  const uint32_t group = 8 * gn;
+  const uint32_t g = p / group, in = p - g * group;
+  const uint32_t first_m = g * 8;
+  const uint32_t gsz = (gm - first_m) < 8 ? (gm - first_m) : 8;
+  const uint32_t n = in / gsz;
+  bm = first_m + (in - n * gsz);
+  bn = n;
+}
+
 // --------------------------------------------------------------------------
 // Reference kernel: one output per thread, 16-byte loads, v_dot4 products.
 // --------------------------------------------------------------------------
@@ -98,18 +118,9 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // XCD-aware tile order: work-groups are dealt round-robin over the 8
-  // XCDs; give each XCD a contiguous run of tiles (shared operand rows in
-  // its own L2), then walk tiles in groups of 8 block-rows.
   const int64_t gm = (I + BM - 1) / BM, gn = (J + BN - 1) / BN;
-  const int64_t total = gm * gn;
-  int64_t pid = blockIdx.x;
-  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
-  const int64_t group = 8 * gn;
-  const int64_t first_m = (pid / group) * 8;
-  const int64_t gsz = (gm - first_m) < 8 ? (gm - first_m) : 8;
-  const int64_t bm = first_m + (pid % group) % gsz;
-  const int64_t bn = (pid % group) / gsz;
+  int64_t bm, bn;
+  tile_of(blockIdx.x, (uint32_t)gm, (uint32_t)gn, bm, bn);
   const int64_t row0 = bm * BM, col0 = bn * BN;
 
   const int64_t nk_total = (Kc + BK - 1) / BK;
@@ -219,11 +230,14 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
 // Synchronisation per step: wait until this wave's loads of step t have
 // landed (vmcnt counts only the direct-to-LDS loads issued in the loop),
 // one workgroup barrier (every wave's step-t data is in LDS and every wave
-// has finished reading step t - 1's stage), issue step t + kStages - 1 into
-// that freed stage, then multiply step t.  The barrier is the bare
+// has finished reading step t - 1's stage), read step t's fragments, issue
+// the first MFMA row groups, then the loads of step t + kStages - 1 into the
+// freed stage, then the remaining MFMAs.  The barrier is the bare
 // s_barrier: the loads are tracked by the explicit wait, not by a fence.
 // --------------------------------------------------------------------------
 constexpr int kStages = 4;
+// MFMA row groups of a step issued before that step's loads
+constexpr int kIssueAfter = 2;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -262,6 +276,61 @@ __device__ __forceinline__ v4i quad_transpose(v4i v, int q) {
   return v;
 }
 
+// Epilogue of one output tile: quad-transpose each 16x16 result block so a
+// lane holds four consecutive columns of one row, then 16-byte stores
+// (element-wise at a ragged right edge).  The fp32 outputs go out as
+// non-temporal (streaming) stores: nothing in the kernel reads them back,
+// and on MI355X this runs the output write markedly faster than the default
+// cached path.  Split-K writes exact int32 partials (slice z) instead,
+// cached: the reduction reads them.  scale(j) gives the column scale c_j.
+template <int TI, int TJ, int WM, int WN, class Scale>
+__device__ __forceinline__ void store_tile(const v4i (&acc)[TI][TJ], int64_t row0, int64_t col0,
+                                           int wm, int wn, int lane, int64_t I, int64_t J,
+                                           float* __restrict__ C, int* __restrict__ Cpart,
+                                           int64_t z, const Scale& scale) {
+  const int q = lane & 3;
+  const int rsub = 4 * (lane >> 4) + q;   // row within the 16x16 block
+  const int csub = (lane & 15) & ~3;      // first of the lane's 4 columns
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int64_t col = col0 + wn * WN + j * 16 + csub;
+    float c4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (!Cpart) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c4[e] = col + e < J ? scale(col + e) : 0.0f;
+    }
+    const bool full = col + 4 <= J && (J & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const v4i v = quad_transpose(acc[i][j], q);
+      const int64_t row = row0 + wm * WM + i * 16 + rsub;
+      if (row >= I || col >= J) continue;
+      if (Cpart) {
+        int* dst = Cpart + (z * I + row) * J + col;
+        if (full) {
+          *reinterpret_cast<v4i*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < J) dst[e] = v[e];
+        }
+      } else {
+        float* dst = C + row * J + col;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = dequant(v[e], c4[e]);
+        if (full) {
+          __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(dst));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < J) dst[e] = o[e];
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t I, int64_t J,
@@ -279,16 +348,9 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // XCD-aware tile order (as the register-staged kernel)
   const int64_t gm = (I + BM - 1) / BM, gn = (J + BN - 1) / BN;
-  const int64_t total = gm * gn;
-  int64_t pid = blockIdx.x;
-  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
-  const int64_t group = 8 * gn;
-  const int64_t first_m = (pid / group) * 8;
-  const int64_t gsz = (gm - first_m) < 8 ? (gm - first_m) : 8;
-  const int64_t bm = first_m + (pid % group) % gsz;
-  const int64_t bn = (pid % group) / gsz;
+  int64_t bm, bn;
+  tile_of(blockIdx.x, (uint32_t)gm, (uint32_t)gn, bm, bn);
   const int64_t row0 = bm * BM, col0 = bn * BN;
 
   const int64_t nk_total = Kc / BK;
@@ -355,7 +417,6 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    if (it + kStages - 1 < nk) issue(it + kStages - 1);
     const int8_t* st = smem + (it % kStages) * STAGE;
     v4i af[TI], bf[TJ];
 #pragma unroll
@@ -368,60 +429,248 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
       const int r = wn * WN + j * 16 + (lane & 15);
       bf[j] = *reinterpret_cast<const v4i*>(st + BM * BK + lds_off<BK>(r, kc));
     }
+    constexpr int IA = kIssueAfter < TI ? kIssueAfter : TI;
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < IA; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + kStages - 1 < nk) issue(it + kStages - 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = IA; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
     asm volatile("" ::: "memory");
   }
 
-  // Epilogue: quad-transpose each 16x16 result block so a lane holds four
-  // consecutive columns of one row, then 16-byte stores (element-wise at a
-  // ragged right edge).  The fp32 outputs go out as non-temporal (streaming)
-  // stores: nothing in the kernel reads them back, and on MI355X this runs
-  // the output write markedly faster than the default cached path.  Split-K
-  // writes exact int32 partials instead (cached: the reduction reads them).
-  const int q = lane & 3;
-  const int rsub = 4 * (lane >> 4) + q;   // row within the 16x16 block
-  const int csub = (lane & 15) & ~3;      // first of the lane's 4 columns
+  store_tile<TI, TJ, WM, WN>(acc, row0, col0, wm, wn, lane, I, J, C, Cpart, blockIdx.z,
+                             [&](int64_t j) { return epi.scale(j); });
+}
+
+// --------------------------------------------------------------------------
+// Persistent form of the direct-to-LDS kernel.  One work-group per CU walks
+// work units u = blockIdx.x, blockIdx.x + gridDim.x, ... (a unit is one
+// output tile of one contraction slice: u = slice * tiles + tile), and the
+// load pipeline runs across unit boundaries: the loads of the next unit's
+// first kStages - 1 steps are issued during the last steps of the current
+// unit and land while its epilogue runs, so no tile starts on a cold
+// pipeline.  Unit u runs on XCD u % 8 when the grid is a multiple of 8, as
+// tile u does in the one-tile-per-group launch, so the same tile order
+// applies.
+//
+// Every unit needs at least kStages contraction steps.  The issue cursor
+// runs kStages - 1 steps ahead, so it then enters unit u + 2 (and loads
+// that unit's column scales into the buffer of unit u's parity) only after
+// unit u's epilogue has read them.
+//
+// The wait before step t allows the loads of the steps already issued after
+// t to stay in flight.  Any other memory operation still outstanding (the
+// previous tile's stores) only makes that wait stricter: loads complete in
+// order among themselves, so step t's loads cannot be pending while fewer
+// ops than the later steps' loads are.
+// --------------------------------------------------------------------------
+template <int L, int MAXL>
+__device__ __forceinline__ void wait_later(int64_t later) {
+  if constexpr (MAXL == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= MAXL) wait_vmcnt<MAXL * L>();
+    else wait_later<L, MAXL - 1>(later);
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_stream(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t I, int64_t J,
+    int64_t Kc, float* __restrict__ C, int* __restrict__ Cpart, int ktiles_per_split,
+    int splits, Epi epi) {
+  constexpr int BK = 64, CH = BK / 16;
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int DA = BM * CH / 64 / NW, DB = BN * CH / 64 / NW;  // loads per wave per step
+  constexpr int L = DA + DB;
+  static_assert(DA * 64 * NW == BM * CH && DB * 64 * NW == BN * CH, "tile/waves");
+  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(BN % 64 == 0 && BN / 64 <= NW, "one scale load per wave");
+  static_assert(kIssueAfter <= TI, "issue point inside the MFMA rows");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * STAGE];
+  __shared__ __attribute__((aligned(16))) float cs[2][BN];  // per-unit column scales
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int64_t gm = (I + BM - 1) / BM, gn = (J + BN - 1) / BN;
+  const int64_t tiles = gm * gn, units = tiles * splits;
+  // Column scales: a per-output-channel forward scale s1[j] travels with
+  // the operand loads (one direct-to-LDS load per unit into cs[unit
+  // parity], issued just before the unit's first stage, so it has landed
+  // once that stage has); every other scale is uniform and read here, before
+  // any load is in flight.
+  const bool col_scales = !Cpart && epi.kind == EPI_FWD && epi.per_row;
+  const float c_uni = Cpart ? 0.0f : col_scales ? flush(epi.s0[0]) : epi.scale(0);
+  const int64_t nk_total = Kc / BK;
+  const int64_t G = gridDim.x;
+
+  struct Unit {
+    int64_t row0, col0, kt0, nk;
+  };
+  auto unit_at = [&](int64_t u) {
+    Unit w;
+    const uint32_t z = (uint32_t)u / (uint32_t)tiles;
+    int64_t bm, bn;
+    tile_of((uint32_t)u - z * (uint32_t)tiles, (uint32_t)gm, (uint32_t)gn, bm, bn);
+    w.row0 = bm * BM;
+    w.col0 = bn * BN;
+    w.kt0 = z * ktiles_per_split;
+    int64_t kt1 = w.kt0 + ktiles_per_split;
+    if (kt1 > nk_total) kt1 = nk_total;
+    w.nk = kt1 > w.kt0 ? kt1 - w.kt0 : 0;
+    return w;
+  };
+
+  // per-lane part of each direct-to-LDS load: slot sigma of the stage's A
+  // (then B) region holds row sigma / 4, chunk (sigma % 4) ^ f(row)
+  int rowA[DA], offA[DA], rowB[DB], offB[DB];
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int64_t col = col0 + wn * WN + j * 16 + csub;
-    float c4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (!Cpart) {
+  for (int i = 0; i < DA; ++i) {
+    const int sg = (wave * DA + i) * 64 + lane, r = sg / CH;
+    rowA[i] = r;
+    offA[i] = ((sg % CH) ^ (((r >> 1) ^ (r >> 2)) & 3)) * 16;
+  }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c4[e] = col + e < J ? epi.scale(col + e) : 0.0f;
-    }
-    const bool full = col + 4 <= J && (J & 3) == 0;
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const v4i v = quad_transpose(acc[i][j], q);
-      const int64_t row = row0 + wm * WM + i * 16 + rsub;
-      if (row >= I || col >= J) continue;
-      if (Cpart) {
-        int* dst = Cpart + ((int64_t)blockIdx.z * I + row) * J + col;
-        if (full) {
-          *reinterpret_cast<v4i*>(dst) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < J) dst[e] = v[e];
-        }
-      } else {
-        float* dst = C + row * J + col;
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = dequant(v[e], c4[e]);
-        if (full) {
-          __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(dst));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < J) dst[e] = o[e];
-        }
+  for (int i = 0; i < DB; ++i) {
+    const int sg = (wave * DB + i) * 64 + lane, r = sg / CH;
+    rowB[i] = r;
+    offB[i] = ((sg % CH) ^ (((r >> 1) ^ (r >> 2)) & 3)) * 16;
+  }
+
+  // issue cursor: unit ui, its step iit of inks, ring slot islot
+  const int8_t* srcA[DA];
+  const int8_t* srcB[DB];
+  int64_t ui = blockIdx.x, iit = 0, inks = 0, issued = 0;
+  int islot = 0;
+  uint32_t iord = 0;  // ordinal of unit ui in this work-group's sequence
+  auto seek = [&]() {  // first unit at or after ui with contraction steps
+    for (; ui < units; ui += G, ++iord) {
+      const Unit w = unit_at(ui);
+      if (w.nk == 0) continue;
+      inks = w.nk;
+      if (col_scales && wave < BN / 64) {
+        int64_t c = w.col0 + wave * 64 + lane;
+        c = c < J ? c : J - 1;
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(epi.s1 + c),
+            (__attribute__((address_space(3))) void*)(&cs[iord & 1][wave * 64]),
+            4, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < DA; ++i) {
+        int64_t gr = w.row0 + rowA[i];
+        gr = gr < I ? gr : I - 1;
+        srcA[i] = A + gr * Kc + offA[i] + w.kt0 * BK;
+      }
+#pragma unroll
+      for (int i = 0; i < DB; ++i) {
+        int64_t gr = w.col0 + rowB[i];
+        gr = gr < J ? gr : J - 1;
+        srcB[i] = B + gr * Kc + offB[i] + w.kt0 * BK;
+      }
+      return;
     }
+  };
+  auto issue_next = [&]() {
+    if (ui >= units) return;
+    int8_t* st = smem + islot * STAGE;
+#pragma unroll
+    for (int i = 0; i < DA; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(srcA[i] + iit * BK),
+          (__attribute__((address_space(3))) void*)(st + (wave * DA + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(srcB[i] + iit * BK),
+          (__attribute__((address_space(3))) void*)(st + BM * BK + (wave * DB + i) * 1024), 16,
+          0, 0);
+    islot = islot == kStages - 1 ? 0 : islot + 1;
+    ++issued;
+    if (++iit == inks) {
+      iit = 0;
+      ui += G;
+      ++iord;
+      seek();
+    }
+  };
+
+  v4i acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  seek();
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue_next();
+
+  const int kc = lane >> 4;
+  int cslot = 0;
+  int64_t computed = 0;
+  uint32_t cord = 0;  // ordinal of unit uc
+#pragma unroll 1
+  for (int64_t uc = blockIdx.x; uc < units; uc += G, ++cord) {
+    const Unit w = unit_at(uc);
+#pragma unroll 1
+    for (int64_t it = 0; it < w.nk; ++it) {
+      wait_later<L, kStages - 2>(issued - computed - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      const int8_t* st = smem + cslot * STAGE;
+      v4i af[TI], bf[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int r = wm * WM + i * 16 + (lane & 15);
+        af[i] = *reinterpret_cast<const v4i*>(st + lds_off<BK>(r, kc));
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int r = wn * WN + j * 16 + (lane & 15);
+        bf[j] = *reinterpret_cast<const v4i*>(st + BM * BK + lds_off<BK>(r, kc));
+      }
+      // the next loads go out after the fragment reads and the first MFMA
+      // row group: issued right after the barrier, all waves' loads queue
+      // at once and hold up the reads and MFMAs behind them
+#pragma unroll
+      for (int i = 0; i < kIssueAfter; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_next();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = kIssueAfter; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+      asm volatile("" ::: "memory");
+      cslot = cslot == kStages - 1 ? 0 : cslot + 1;
+      ++computed;
+    }
+    const float* cu = cs[cord & 1];
+    store_tile<TI, TJ, WM, WN>(acc, w.row0, w.col0, wm, wn, lane, I, J, C, Cpart,
+                               (uint32_t)uc / (uint32_t)tiles,
+                               [&](int64_t j) {
+                                 return col_scales ? fmul(c_uni, flush(cu[j - w.col0])) : c_uni;
+                               });
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
   }
 }
 
@@ -441,9 +690,11 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const int* __restrict__ C
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Launch plan: the tune's kernel and split-K when given, else by shape --
-// the deep-pipelined 256x256 kernel whenever the contraction is a multiple
-// of 64 bytes, with the contraction split so that tiles x splits reaches
-// about one work-group per CU when the output has few tiles.  None of this
+// the persistent deep-pipelined 256x256 kernel whenever the contraction is
+// a multiple of 64 bytes (the one-tile-per-group form when a unit would
+// hold fewer than kStages steps), with the contraction split so that tiles
+// x splits reaches about one work-group per CU when the output has few
+// tiles.  None of this
 // changes a result bit: the int32 sums are exact in any grouping.
 struct Plan {
   int kern;
@@ -457,11 +708,11 @@ static Plan plan_of(int64_t I, int64_t J, int64_t Kc, const brq_tune* t) {
   if (tk) {
     p.kern = tk;
   } else if (Kc % 64 == 0) {
-    p.kern = 10;
+    p.kern = 13;
   }
   if (ts) {
     p.splits = (ts == 2 || ts == 4 || ts == 8 || ts == 16) ? ts : 1;
-  } else if (!tk && p.kern == 10) {
+  } else if (!tk && p.kern == 13) {
     const int64_t tiles = cdiv(I, 256) * cdiv(J, 256);
     int s = 1;
     while (s < 16 && tiles * s < 256 && Kc / 64 / (2 * s) >= 32) s *= 2;
@@ -501,11 +752,43 @@ static hipError_t launch_dma(const int8_t* A, const int8_t* B, int64_t I, int64_
   return hipGetLastError();
 }
 
+// Work-groups the persistent kernel keeps resident: one per CU (its LDS
+// stages take most of a CU's LDS).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int BM, int BN, int WGM, int WGN>
+static hipError_t launch_stream(const int8_t* A, const int8_t* B, int64_t I, int64_t J,
+                                int64_t Kc, float* C, int* Cpart, int splits, Epi epi,
+                                hipStream_t s) {
+  const int64_t units = cdiv(I, BM) * cdiv(J, BN) * splits;
+  const int64_t nk = Kc / 64;
+  const int kps = (int)cdiv(nk, splits);
+  int64_t grid = cu_count();
+  if (grid > units) grid = units;
+  hipLaunchKernelGGL((k_gemm_stream<BM, BN, WGM, WGN>), dim3((unsigned)grid), dim3(WGM * WGN * 64),
+                     0, s, A, B, I, J, Kc, C, Cpart, kps, splits, epi);
+  return hipGetLastError();
+}
+
 hipError_t gemm_i8(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64_t Kc, float* C,
                    const EpiArgs& ea, void* ws, size_t ws_bytes, const brq_tune* t,
                    hipStream_t s) {
   Epi epi{ea.kind, ea.s0, ea.s1, ea.s2, ea.per_row, ea.inv_b};
   if (I == 0 || J == 0) return hipSuccess;
+  // tile indices are unsigned 32-bit: at most 2^31 work units of the
+  // smallest tile (128 x 128) times the largest split
+  if (cdiv(I, 128) * cdiv(J, 128) * 16 > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   const Plan pl = plan_of(I, J, Kc, t);
   int kern = pl.kern;
   if (kern == 1) {
@@ -521,12 +804,19 @@ hipError_t gemm_i8(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64
   }
   hipError_t e;
   // the direct-to-LDS kernels need whole 64-byte contraction chunks
-  if (kern >= 9 && Kc % 64) kern = 2;
+  if (kern >= 9 && kern <= 13 && Kc % 64) kern = 2;
   switch (kern) {
     case 9: e = launch_dma<256, 256, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
     case 10: e = launch_dma<256, 256, 2, 4>(A, B, I, J, Kc, C, part, splits, epi, s); break;
     case 11: e = launch_dma<128, 256, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
     case 12: e = launch_dma<128, 128, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 13:
+      // every unit must hold at least kStages contraction steps
+      if (Kc / 64 / splits >= kStages && (Kc / 64) % splits == 0)
+        e = launch_stream<256, 256, 2, 4>(A, B, I, J, Kc, C, part, splits, epi, s);
+      else
+        e = launch_dma<256, 256, 2, 4>(A, B, I, J, Kc, C, part, splits, epi, s);
+      break;
     case 3: e = launch_mfma<256, 128, 2, 2, 128>(A, B, I, J, Kc, C, part, splits, epi, s); break;
     case 4: e = launch_mfma<128, 256, 2, 2, 128>(A, B, I, J, Kc, C, part, splits, epi, s); break;
     case 5: e = launch_mfma<256, 256, 2, 2, 64>(A, B, I, J, Kc, C, part, splits, epi, s); break;

@@ -72,7 +72,12 @@ typedef struct brq_tune {
                         7 256x256 (8 waves, BK 64), 8 256x256 (8 waves);
                         direct-to-LDS 4-stage MFMA tiles (contraction a
                         multiple of 64, else 2 is used): 9 256x256 (4 waves),
-                        10 256x256 (8 waves), 11 128x256, 12 128x128 */
+                        10 256x256 (8 waves), 11 128x256, 12 128x128,
+                        13 256x256 (8 waves) persistent: one work-group
+                        per CU walks its tiles with the load pipeline
+                        running across tile boundaries (10 is used when a
+                        tile's contraction slice has fewer than 4 steps of
+                        64 or the slices are unequal) */
   int split_k;       /* 0 default (by shape), else 1, 2, 4, 8 or 16
                         contraction slices (exact int32 partials) */
   int chunk_log2;    /* 0 default (13), else log2 of the leaves each

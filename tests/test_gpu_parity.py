@@ -132,7 +132,8 @@ def test_quantize_ties_and_clamps():
 GEMM_TUNES = [dict(gemm_kernel=k, split_k=s) for k, s in
               [(1, 1), (2, 1), (3, 1), (4, 1), (2, 2), (2, 4), (3, 2), (4, 4),
                (5, 1), (6, 1), (7, 1), (8, 1), (7, 2), (5, 4), (0, 0),
-               (9, 1), (10, 1), (11, 1), (12, 1), (10, 2), (12, 4), (10, 16), (0, 8)]]
+               (9, 1), (10, 1), (11, 1), (12, 1), (10, 2), (12, 4), (10, 16), (0, 8),
+               (13, 1), (13, 2), (13, 4)]]
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 2048), (128, 512, 16),
@@ -162,6 +163,37 @@ def test_qgemm_bwd_dx(M, N, K):
     dqg, dqwt, dsg = to_dev(qg), to_dev(np.ascontiguousarray(qw.T)), to_dev(sg)
     for t in GEMM_TUNES:
         assert_bitwise(brq.qgemm_bwd_dx(dqg, dsg, dqwt, tune=t), want, f"dx {t}")
+
+
+@pytest.mark.parametrize("M,N,K,split", [(8200, 4000, 256, 1), (4100, 4001, 320, 1),
+                                         (8200, 4000, 512, 2), (2304, 2560, 1024, 4),
+                                         (8200, 4000, 192, 1)])
+def test_qgemm_persistent_many_tiles(M, N, K, split):
+    """The persistent kernel with more tiles than CUs: several tiles per
+    work-group, the load pipeline crossing tile boundaries, column scales
+    double-buffered per tile, ragged right and bottom edges; 4 contraction
+    steps per tile is the kernel's minimum, 3 takes the one-tile-per-group
+    kernel.  Sampled rows (every tile-row boundary and the ragged tail)
+    against the oracle."""
+    say("qgemm_persistent", M, N, K, split)
+    rng = np.random.default_rng(M + N + K)
+    qx, qw = codes(rng, (M, K)), codes(rng, (N, K))
+    sx = np.array([0.0173], np.float32)
+    sw = (np.abs(rng.standard_normal(N)) * 1e-3 + 1e-4).astype(np.float32)
+    rows = sorted(set([0, 1, M - 1] + [r for b in range(256, M, 256) for r in (b - 1, b)]
+                      + list(rng.integers(0, M, 24))))
+    t = dict(gemm_kernel=13, split_k=split)
+    dqx, dqw, dsx, dsw = to_dev(qx), to_dev(qw), to_dev(sx), to_dev(sw)
+    y = to_np(brq.qgemm_fwd(dqx, dsx, dqw, dsw, tune=t))
+    assert_bitwise(y[rows], orc.qgemm_fwd(qx[rows], sx, qw, sw), f"y rows {t}")
+    y1 = to_np(brq.qgemm_fwd(dqx, dsx, dqw, dsw[:1], tune=t))
+    assert_bitwise(y1[rows], orc.qgemm_fwd(qx[rows], sx, qw, sw[:1]), f"y per-tensor rows {t}")
+    # the same codes as an input-gradient GEMM (uniform scale): q_g [M][K'],
+    # q_w^T [N'][K'] with K' = K the contraction
+    sg = np.array([3.1e-5], np.float32)
+    dx = to_np(brq.qgemm_bwd_dx(dqx, to_dev(sg), dqw, tune=t))
+    assert_bitwise(dx[rows], orc.qgemm_bwd_dx(qx[rows], sg, np.ascontiguousarray(qw.T)),
+                   f"dx rows {t}")
 
 
 def test_gemm_extreme_accumulator():
