@@ -315,7 +315,7 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                     "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                     "traffic": traffic,
-                    "kernel": "brq::k_gemm_stream<256,256,2,4> (persistent, int8 MFMA 16x16x64, direct-to-LDS, fp32 dequant)",
+                    "kernel": "brq::k_gemm_dma / k_gemm_stream <256,256,2,4> (int8 MFMA 16x16x64, direct-to-LDS, fp32 dequant; all 21 GEMM launches)",
                     "launches_per_step": n_gemm,
                     "avg_launch_us": round(1e3 * gemm_ms / n_gemm, 2),
                     "algorithmic_ops_per_launch": ops / n_gemm}

@@ -276,35 +276,66 @@ __device__ __forceinline__ v4i quad_transpose(v4i v, int q) {
   return v;
 }
 
-// Epilogue of one output tile: quad-transpose each 16x16 result block so a
-// lane holds four consecutive columns of one row, then 16-byte stores
-// (element-wise at a ragged right edge).  The fp32 outputs go out as
-// non-temporal (streaming) stores: nothing in the kernel reads them back,
-// and on MI355X this runs the output write markedly faster than the default
-// cached path.  Split-K writes exact int32 partials (slice z) instead,
-// cached: the reduction reads them.  scale(j) gives the column scale c_j.
-template <int TI, int TJ, int WM, int WN, class Scale>
-__device__ __forceinline__ void store_tile(const v4i (&acc)[TI][TJ], int64_t row0, int64_t col0,
-                                           int wm, int wn, int lane, int64_t I, int64_t J,
-                                           float* __restrict__ C, int* __restrict__ Cpart,
-                                           int64_t z, const Scale& scale) {
-  const int q = lane & 3;
-  const int rsub = 4 * (lane >> 4) + q;   // row within the 16x16 block
-  const int csub = (lane & 15) & ~3;      // first of the lane's 4 columns
+// Epilogue of one output tile, staged through LDS so that every global
+// store instruction writes whole rows: one wave's 16-byte-per-lane store
+// covers BN * 4 / 1024 rows of 1 KiB contiguous (one row for BN = 256).
+// Straight from the MFMA layout (one column, four rows per lane) a store
+// instruction would touch 16 rows 64 bytes each, and the output write runs
+// about 2.5x slower per CU.  Per 16-row block of the tile: every wave
+// writes its 16 x WN values (dequantised, or raw int32 for split-K
+// partials) into the staging area -- WGM groups of 16 rows x BN words, 16-byte
+// chunks XOR-swizzled by row -- barrier, then the waves of each row group
+// read back whole rows and store them, barrier.  The fp32 outputs go out as
+// non-temporal (streaming) stores: nothing in the kernel reads them back.
+// Split-K partials (slice z) are cached: the reduction reads them.
+// scale(j) gives the column scale c_j.  The caller guarantees that no wave
+// still reads `stage` and that no load is in flight into it.
+template <int BM, int BN, int WGM, int WGN, class Scale>
+__device__ __forceinline__ void store_tile(const v4i (&acc)[BM / WGM / 16][BN / WGN / 16],
+                                           int64_t row0, int64_t col0, int wave, int lane,
+                                           int64_t I, int64_t J, float* __restrict__ C,
+                                           int* __restrict__ Cpart, int64_t z,
+                                           const Scale& scale, int8_t* stage) {
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int CPR = BN / 4;                 // 16-byte chunks per staged row
+  constexpr int GROUP = 16 * BN * 4;          // bytes per row group
+  constexpr int RCH = 16 * CPR / (WGN * 64);  // chunks each lane stores per block
+  static_assert(CPR >= 8 && RCH * WGN * 64 == 16 * CPR, "staging layout");
+  const int wm = wave / WGN, wn = wave % WGN;
+  int8_t* grp = stage + wm * GROUP;
+  const int rq = 4 * (lane >> 4);  // first of the lane's 4 rows in a block
+  const int cc = wn * WN + (lane & 15);  // the lane's column in j-block 0
+  float cj[TJ];
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
-    const int64_t col = col0 + wn * WN + j * 16 + csub;
-    float c4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (!Cpart) {
+    const int64_t col = col0 + cc + j * 16;
+    cj[j] = (!Cpart && col < J) ? scale(col) : 0.0f;
+  }
+  auto word = [&](int r, int c) {  // byte offset of staged word (r, c)
+    return (r * CPR + ((c >> 2) ^ (r & 7))) * 16 + (c & 3) * 4;
+  };
+#pragma unroll  // fully: acc must stay in registers
+  for (int i = 0; i < TI; ++i) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c4[e] = col + e < J ? scale(col + e) : 0.0f;
+    for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = acc[i][j][r];
+        const int bits = Cpart ? v : __float_as_int(dequant(v, cj[j]));
+        *reinterpret_cast<int*>(grp + word(rq + r, cc + j * 16)) = bits;
+      }
     }
-    const bool full = col + 4 <= J && (J & 3) == 0;
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const v4i v = quad_transpose(acc[i][j], q);
-      const int64_t row = row0 + wm * WM + i * 16 + rsub;
+    for (int k = 0; k < RCH; ++k) {
+      const int ch = (k * WGN + wn) * 64 + lane;  // chunk of the group
+      const int r = ch / CPR, c4 = ch % CPR;
+      const v4i v = *reinterpret_cast<const v4i*>(grp + (r * CPR + (c4 ^ (r & 7))) * 16);
+      const int64_t row = row0 + wm * WM + i * 16 + r;
+      const int64_t col = col0 + c4 * 4;
       if (row >= I || col >= J) continue;
+      const bool full = col + 4 <= J && (J & 3) == 0;
       if (Cpart) {
         int* dst = Cpart + (z * I + row) * J + col;
         if (full) {
@@ -316,18 +347,19 @@ __device__ __forceinline__ void store_tile(const v4i (&acc)[TI][TJ], int64_t row
         }
       } else {
         float* dst = C + row * J + col;
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = dequant(v[e], c4[e]);
         if (full) {
-          __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(dst));
+          __builtin_nontemporal_store(
+              f32x4{__int_as_float(v[0]), __int_as_float(v[1]), __int_as_float(v[2]),
+                    __int_as_float(v[3])},
+              reinterpret_cast<f32x4*>(dst));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (col + e < J) dst[e] = o[e];
+            if (col + e < J) dst[e] = __int_as_float(v[e]);
         }
       }
     }
+    __syncthreads();
   }
 }
 
@@ -343,6 +375,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
   constexpr int L = DA + DB;
   static_assert(DA * 64 * NW == BM * CH && DB * 64 * NW == BN * CH, "tile/waves");
   constexpr int STAGE = (BM + BN) * BK;
+  static_assert(WGM * 16 * BN * 4 <= kStages * STAGE, "epilogue staging fits the stages");
   __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * STAGE];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -446,8 +479,11 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
     asm volatile("" ::: "memory");
   }
 
-  store_tile<TI, TJ, WM, WN>(acc, row0, col0, wm, wn, lane, I, J, C, Cpart, blockIdx.z,
-                             [&](int64_t j) { return epi.scale(j); });
+  // every load has landed (the last step waited for all); the barrier
+  // frees the stages for the epilogue
+  __syncthreads();
+  store_tile<BM, BN, WGM, WGN>(acc, row0, col0, wave, lane, I, J, C, Cpart, blockIdx.z,
+                               [&](int64_t j) { return epi.scale(j); }, smem);
 }
 
 // --------------------------------------------------------------------------
@@ -497,6 +533,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_stream(
   constexpr int STAGE = (BM + BN) * BK;
   static_assert(BN % 64 == 0 && BN / 64 <= NW, "one scale load per wave");
   static_assert(kIssueAfter <= TI, "issue point inside the MFMA rows");
+  static_assert(WGM * 16 * BN * 4 <= STAGE, "epilogue staging fits one stage");
   __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * STAGE];
   __shared__ __attribute__((aligned(16))) float cs[2][BN];  // per-unit column scales
 
@@ -662,11 +699,17 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_stream(
       ++computed;
     }
     const float* cu = cs[cord & 1];
-    store_tile<TI, TJ, WM, WN>(acc, w.row0, w.col0, wm, wn, lane, I, J, C, Cpart,
-                               (uint32_t)uc / (uint32_t)tiles,
-                               [&](int64_t j) {
-                                 return col_scales ? fmul(c_uni, flush(cu[j - w.col0])) : c_uni;
-                               });
+    // stage through the slot the last step consumed: the loads in flight
+    // target the other kStages - 1 slots, and the next load into this one
+    // is issued after the next step's barrier
+    const int last = cslot == 0 ? kStages - 1 : cslot - 1;
+    __syncthreads();  // every wave has read its last fragments
+    store_tile<BM, BN, WGM, WGN>(acc, w.row0, w.col0, wave, lane, I, J, C, Cpart,
+                                 (uint32_t)uc / (uint32_t)tiles,
+                                 [&](int64_t j) {
+                                   return col_scales ? fmul(c_uni, flush(cu[j - w.col0])) : c_uni;
+                                 },
+                                 smem + last * STAGE);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -690,12 +733,27 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const int* __restrict__ C
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Launch plan: the tune's kernel and split-K when given, else by shape --
-// the persistent deep-pipelined 256x256 kernel whenever the contraction is
-// a multiple of 64 bytes (the one-tile-per-group form when a unit would
-// hold fewer than kStages steps), with the contraction split so that tiles
-// x splits reaches about one work-group per CU when the output has few
+// the deep-pipelined 256x256 kernel whenever the contraction is a multiple
+// of 64 bytes, persistent when there are more tiles than CUs and each
+// tile's contraction is short, with the contraction split so that tiles x
+// splits reaches about one work-group per CU when the output has few
 // tiles.  None of this
 // changes a result bit: the int32 sums are exact in any grouping.
+// Work-groups the persistent kernel keeps resident: one per CU (its LDS
+// stages take most of a CU's LDS).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 struct Plan {
   int kern;
   int splits;
@@ -708,15 +766,21 @@ static Plan plan_of(int64_t I, int64_t J, int64_t Kc, const brq_tune* t) {
   if (tk) {
     p.kern = tk;
   } else if (Kc % 64 == 0) {
-    p.kern = 13;
+    p.kern = 10;
   }
   if (ts) {
     p.splits = (ts == 2 || ts == 4 || ts == 8 || ts == 16) ? ts : 1;
-  } else if (!tk && p.kern == 13) {
+  } else if (!tk && p.kern == 10) {
     const int64_t tiles = cdiv(I, 256) * cdiv(J, 256);
     int s = 1;
     while (s < 16 && tiles * s < 256 && Kc / 64 / (2 * s) >= 32) s *= 2;
     p.splits = s;
+    // persistent when each CU gets several tiles of a short contraction
+    // (a tile start costs the most there); long ones run as well or
+    // better one tile per group
+    const int64_t steps = Kc / 64 / s;
+    if (tiles * s > cu_count() && steps >= kStages && steps < 64 && (Kc / 64) % s == 0)
+      p.kern = 13;
   }
   if (p.kern == 1) p.splits = 1;
   return p;
@@ -750,21 +814,6 @@ static hipError_t launch_dma(const int8_t* A, const int8_t* B, int64_t I, int64_
   hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN>), g, b, 0, s, A, B, I, J, Kc, C, Cpart, kps,
                      epi);
   return hipGetLastError();
-}
-
-// Work-groups the persistent kernel keeps resident: one per CU (its LDS
-// stages take most of a CU's LDS).
-static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
 }
 
 template <int BM, int BN, int WGM, int WGN>

@@ -167,7 +167,8 @@ def test_qgemm_bwd_dx(M, N, K):
 
 @pytest.mark.parametrize("M,N,K,split", [(8200, 4000, 256, 1), (4100, 4001, 320, 1),
                                          (8200, 4000, 512, 2), (2304, 2560, 1024, 4),
-                                         (8200, 4000, 192, 1)])
+                                         (8200, 4000, 192, 1), (8200, 4000, 1024, 1),
+                                         (8200, 4001, 1088, 1)])
 def test_qgemm_persistent_many_tiles(M, N, K, split):
     """The persistent kernel with more tiles than CUs: several tiles per
     work-group, the load pipeline crossing tile boundaries, column scales
