@@ -239,18 +239,30 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
 
 // Order-free max of the per-work-group maxima, then both LSQ steps:
 // sr4 = {s_g, r_g, s_v, r_v}.
-__global__ __launch_bounds__(256) void k_dy_finalize(const float* __restrict__ sum_g,
-                                                     const float* __restrict__ sum_v,
-                                                     const float* __restrict__ bmax, int64_t nb,
-                                                     float inv_n, float* sr4, float* s_g,
-                                                     float* amax_g, float* s_v) {
+__global__ __launch_bounds__(1024) void k_dy_finalize(const float* __restrict__ sum_g,
+                                                      const float* __restrict__ sum_v,
+                                                      const float* __restrict__ bmax, int64_t nb,
+                                                      float inv_n, float* sr4, float* s_g,
+                                                      float* amax_g, float* s_v) {
+  // 8 independent loads in flight per lane per round (max is order-free)
   float m = 0.0f;
-  for (int64_t i = threadIdx.x; i < nb; i += 256) m = fmaxf(m, bmax[i]);
+  for (int64_t i0 = 0; i0 < nb; i0 += 8 * 1024) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * 1024 + threadIdx.x;
+      x[u] = i < nb ? bmax[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, x[u]);
+  }
   m = wave_max(m);
-  __shared__ float w[4];
+  __shared__ float w[16];
   if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 4; i < 16; ++i) w[0] = fmaxf(w[0], w[i]);
     const float sg = fmul(fmul(sum_g[0], inv_n), lsq_k2());
     const float sv = fmul(fmul(sum_v[0], inv_n), lsq_k2());
     sr4[0] = sg;
@@ -275,7 +287,7 @@ size_t dy_fused_ws(int64_t M, int64_t N, int chunk_log2) {
   const int64_t nblk = cdiv(N, kCols) * (M / kRows);
   return 2 * align256((size_t)(P > 0 ? P : 1) * sizeof(float)) +
          align256((size_t)(nblk > 0 ? nblk : 1) * sizeof(float)) +
-         flat_reduce_ws(P, chunk_log2) + 256;
+         flat_reduce_pair_ws(P, chunk_log2) + 256;
 }
 
 hipError_t quantize_dy_fused(const void* dy, int64_t M, int64_t N, const float* sw, int block,
@@ -291,21 +303,18 @@ hipError_t quantize_dy_fused(const void* dy, int64_t M, int64_t N, const float* 
   float* bmax = (float*)w;
   w += align256((size_t)(gx * gy) * sizeof(float));
   void* fws = w;
-  w += flat_reduce_ws(P, chunk_log2);
+  w += flat_reduce_pair_ws(P, chunk_log2);
   float* sc = (float*)w;  // [0,1] g sum/max, [2,3] v sum/max, [4..7] s_g r_g s_v r_v
   dim3 g((unsigned)gx, (unsigned)gy), b(256);
   hipLaunchKernelGGL(k_dy_stats, g, b, 0, s, (const uint16_t*)dy, sw, M, N, block, part_g, part_v,
                      bmax);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = flat_reduce(part_g, BRQ_F32, LEAF_RAW, nullptr, P, 1, sc, fws, chunk_log2, dflags, s)) !=
+  if ((e = flat_reduce_pair(part_g, part_v, P, sc, sc + 2, fws, chunk_log2, dflags, s)) !=
       hipSuccess)
     return e;
-  if ((e = flat_reduce(part_v, BRQ_F32, LEAF_RAW, nullptr, P, 1, sc + 2, fws, chunk_log2, dflags,
-                       s)) != hipSuccess)
-    return e;
   const float inv_n = 1.0f / (float)(M * N);  // host binary32 division, correctly rounded
-  hipLaunchKernelGGL(k_dy_finalize, dim3(1), dim3(256), 0, s, sc, sc + 2, bmax, gx * gy, inv_n,
+  hipLaunchKernelGGL(k_dy_finalize, dim3(1), dim3(1024), 0, s, sc, sc + 2, bmax, gx * gy, inv_n,
                      sc + 4, s_g, amax_g, s_v);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_dy_codes, g, b, 0, s, (const uint16_t*)dy, sw, M, N, block, sc + 4, q_g,

@@ -31,6 +31,13 @@ hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul,
                        int64_t n, int64_t cols, float* out2, void* ws,
                        int chunk_log2, int32_t* dflags, hipStream_t s);
 
+// Two raw fp32 leaf arrays of equal length n reduced as two flat_reduce
+// calls would, in one launch per level; workspace flat_reduce_pair_ws.
+size_t flat_reduce_pair_ws(int64_t n, int chunk_log2);
+hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* out0,
+                            float* out1, void* ws, int chunk_log2, int32_t* dflags,
+                            hipStream_t s);
+
 // From a tree sum on device, compute the LSQ step size and reciprocal:
 // sr[0] = s, sr[1] = r.  Optionally copies s and the max into scale/amax.
 hipError_t lsq_finalize(const float* sum_max, float inv_n, float* sr,

@@ -50,11 +50,10 @@ __device__ __forceinline__ void leaves_of(const T* x, const float* cm, int64_t n
 }
 
 template <typename T, int LEAF, int V>
-__global__ __launch_bounds__(256) void k_flat_leaves(const T* __restrict__ x,
-                                                     const float* __restrict__ cm,
-                                                     int64_t n, int64_t cols,
-                                                     float* __restrict__ psum,
-                                                     float* __restrict__ pmax) {
+__device__ __forceinline__ void flat_leaves_body(const T* __restrict__ x,
+                                                 const float* __restrict__ cm, int64_t n,
+                                                 int64_t cols, float* __restrict__ psum,
+                                                 float* __restrict__ pmax) {
   constexpr int E = Elem<T>::kPerVec;
   constexpr int64_t WAVE_SPAN = int64_t(64) * E * V;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -80,12 +79,33 @@ __global__ __launch_bounds__(256) void k_flat_leaves(const T* __restrict__ x,
   }
 }
 
+template <typename T, int LEAF, int V>
+__global__ __launch_bounds__(256) void k_flat_leaves(const T* __restrict__ x,
+                                                     const float* __restrict__ cm,
+                                                     int64_t n, int64_t cols,
+                                                     float* __restrict__ psum,
+                                                     float* __restrict__ pmax) {
+  flat_leaves_body<T, LEAF, V>(x, cm, n, cols, psum, pmax);
+}
+
+// Two independent raw-leaf reductions of equal length in one launch:
+// blockIdx.y selects the array.
+struct FlatPair {
+  const float* x[2];
+  float* ps[2];
+  float* pm[2];
+};
+template <int V>
+__global__ __launch_bounds__(256) void k_flat_leaves_pair(FlatPair a, int64_t n) {
+  const int y = blockIdx.y;
+  flat_leaves_body<float, LEAF_RAW, V>(a.x[y], nullptr, n, 1, a.ps[y], a.pm[y]);
+}
+
 // Final level: up to 32768 partials in one work-group of 1024 lanes, each
 // lane an aligned run of 32.  Writes out[0] = sum, out[1] = max.
-__global__ __launch_bounds__(1024) void k_flat_final(const float* __restrict__ psum,
-                                                     const float* __restrict__ pmax,
-                                                     int64_t P, float* out,
-                                                     int32_t* flags) {
+__device__ __forceinline__ void flat_final_body(const float* __restrict__ psum,
+                                                const float* __restrict__ pmax, int64_t P,
+                                                float* out, int32_t* flags) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   float a[32];
   float mx = 0.0f;
@@ -109,6 +129,19 @@ __global__ __launch_bounds__(1024) void k_flat_final(const float* __restrict__ p
     out[1] = m;
     if (!__builtin_isfinite(s)) set_flag(flags, BRQ_FLAG_NONFINITE);
   }
+}
+
+__global__ __launch_bounds__(1024) void k_flat_final(const float* __restrict__ psum,
+                                                     const float* __restrict__ pmax,
+                                                     int64_t P, float* out, int32_t* flags) {
+  flat_final_body(psum, pmax, P, out, flags);
+}
+
+// blockIdx.x selects the array of the pair
+__global__ __launch_bounds__(1024) void k_flat_final_pair(FlatPair a, int64_t P, float* out0,
+                                                          float* out1, int32_t* flags) {
+  const int y = blockIdx.x;
+  flat_final_body(a.ps[y], a.pm[y], P, y ? out1 : out0, flags);
 }
 
 int flat_chunk_log2(const brq_tune* t) {
@@ -159,8 +192,8 @@ static hipError_t launch_leaves(const T* x, const float* cm, int64_t n, int64_t 
 // Max partials of a level: one work-group per 16384 entries of the level
 // below, matching the raw-sum pass, so both arrays have the same length.
 // (max is order-free: any grouping is exact.)
-__global__ __launch_bounds__(256) void k_max_partials(const float* __restrict__ pm, int64_t P,
-                                                      float* __restrict__ out) {
+__device__ __forceinline__ void max_partials_body(const float* __restrict__ pm, int64_t P,
+                                                  float* __restrict__ out) {
   const int64_t i0 = (int64_t)blockIdx.x * 16384;
   float m = 0.0f;
   for (int i = threadIdx.x; i < 16384; i += 256) {
@@ -172,6 +205,18 @@ __global__ __launch_bounds__(256) void k_max_partials(const float* __restrict__ 
   if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) out[blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+}
+
+__global__ __launch_bounds__(256) void k_max_partials(const float* __restrict__ pm, int64_t P,
+                                                      float* __restrict__ out) {
+  max_partials_body(pm, P, out);
+}
+
+// pm_in = the pair's level below, pm_out = this level (blockIdx.y selects)
+__global__ __launch_bounds__(256) void k_max_partials_pair(FlatPair below, FlatPair level,
+                                                           int64_t P) {
+  const int y = blockIdx.y;
+  max_partials_body(below.pm[y], P, level.pm[y]);
 }
 
 hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul, int64_t n,
@@ -215,6 +260,57 @@ hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul,
   }
   hipLaunchKernelGGL(k_flat_final, dim3(1), dim3(1024), 0, s, ps[L - 1], pm[L - 1], P[L - 1],
                      out2, dflags);
+  return hipGetLastError();
+}
+
+size_t flat_reduce_pair_ws(int64_t n, int chunk_log2) { return 2 * flat_reduce_ws(n, chunk_log2); }
+
+// Two raw fp32 leaf arrays of equal length n, reduced exactly as two
+// flat_reduce calls would (same chunks, same tree), in one launch per level.
+hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* out0,
+                            float* out1, void* ws, int chunk_log2, int32_t* dflags,
+                            hipStream_t s) {
+  const int V = vectors_for(chunk_log2, 4);
+  const int64_t C0 = int64_t(256) * 4 * V;
+  const int Vr = 16;
+  int64_t P[16];
+  int L = levels_of(n, C0, int64_t(256) * 4 * Vr, P, 16);
+  FlatPair lv[16];
+  char* w = (char*)ws;
+  for (int y = 0; y < 2; ++y) {
+    for (int i = 0; i < L; ++i) {
+      lv[i].ps[y] = (float*)w;
+      lv[i].pm[y] = lv[i].ps[y] + P[i];
+      w += align256(2 * sizeof(float) * (size_t)P[i]);
+    }
+  }
+  lv[0].x[0] = x0;
+  lv[0].x[1] = x1;
+  for (int i = 1; i < L; ++i) {
+    lv[i].x[0] = lv[i - 1].ps[0];
+    lv[i].x[1] = lv[i - 1].ps[1];
+  }
+  auto leaves = [&](int i, int v, int64_t len) {
+    dim3 g((unsigned)P[i], 2), b(256);
+    switch (v) {
+      case 1: hipLaunchKernelGGL((k_flat_leaves_pair<1>), g, b, 0, s, lv[i], len); break;
+      case 2: hipLaunchKernelGGL((k_flat_leaves_pair<2>), g, b, 0, s, lv[i], len); break;
+      case 4: hipLaunchKernelGGL((k_flat_leaves_pair<4>), g, b, 0, s, lv[i], len); break;
+      case 8: hipLaunchKernelGGL((k_flat_leaves_pair<8>), g, b, 0, s, lv[i], len); break;
+      default: hipLaunchKernelGGL((k_flat_leaves_pair<16>), g, b, 0, s, lv[i], len); break;
+    }
+    return hipGetLastError();
+  };
+  hipError_t e = leaves(0, V, n);
+  if (e != hipSuccess) return e;
+  for (int i = 1; i < L; ++i) {
+    if ((e = leaves(i, Vr, P[i - 1])) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_max_partials_pair, dim3((unsigned)P[i], 2), dim3(256), 0, s, lv[i - 1],
+                       lv[i], P[i - 1]);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_flat_final_pair, dim3(2), dim3(1024), 0, s, lv[L - 1], P[L - 1], out0,
+                     out1, dflags);
   return hipGetLastError();
 }
 
