@@ -70,6 +70,12 @@ def lib():
         L.orc_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, vp, vp]
         L.orc_grad_norm.restype = i32
         L.orc_grad_norm.argtypes = [vp, i64, vp, vp]
+        L.orc_adamw_bias_corrections.restype = None
+        L.orc_adamw_bias_corrections.argtypes = [i64, f32, f32, vp, vp]
+        L.orc_adamw_decide.restype = i32
+        L.orc_adamw_decide.argtypes = [f32, f32, f32, i32, vp, vp, vp]
+        L.orc_adamw_step.restype = None
+        L.orc_adamw_step.argtypes = [vp, i32, vp, i32, vp, vp, i64] + [f32] * 9
         L.orc_sha256.restype = None
         L.orc_sha256.argtypes = [vp, C.c_uint64, vp]
         L.orc_merkle_root.restype = None
@@ -252,6 +258,40 @@ def grad_norm(v):
     nrm = np.zeros(1, np.float32)
     flags = lib().orc_grad_norm(_p(v), v.size, _p(ss), _p(nrm))
     return ss[0], nrm[0], flags
+
+
+# AdamW defaults of the pages (report §3.2 "Optimizer").
+ADAMW_BETA1, ADAMW_BETA2, ADAMW_EPS, ADAMW_WD = 0.9, 0.95, 1e-8, 0.1
+CLIP_MAX_NORM, SPIKE_THRESHOLD, SPIKE_SKIP_STEPS = 1.0, 5.0, 5
+
+
+def adamw_bias_corrections(t: int, beta1: float = ADAMW_BETA1, beta2: float = ADAMW_BETA2):
+    b1, b2 = C.c_float(), C.c_float()
+    lib().orc_adamw_bias_corrections(t, beta1, beta2, C.byref(b1), C.byref(b2))
+    return np.float32(b1.value), np.float32(b2.value)
+
+
+def adamw_decide(norm: float, skip_state: int, max_norm: float = CLIP_MAX_NORM,
+                 spike_threshold: float = SPIKE_THRESHOLD, skip_steps: int = SPIKE_SKIP_STEPS):
+    """Returns (apply, clip, new_skip_state, flags)."""
+    st = C.c_int32(skip_state)
+    ap, cl = C.c_float(), C.c_float()
+    fl = lib().orc_adamw_decide(norm, max_norm, spike_threshold, skip_steps, C.byref(st),
+                                C.byref(ap), C.byref(cl))
+    return np.float32(ap.value), np.float32(cl.value), int(st.value), int(fl)
+
+
+def adamw_step(param, grad, m, v, lr: float, bc1: float, bc2: float, apply: float = 1.0,
+               clip: float = 1.0, beta1: float = ADAMW_BETA1, beta2: float = ADAMW_BETA2,
+               eps: float = ADAMW_EPS, wd: float = ADAMW_WD):
+    """Returns updated copies (param, m, v); param bf16 (uint16) or fp32."""
+    p = _c(param).copy()
+    g = _c(grad)
+    m2, v2 = _c(m, np.float32).copy(), _c(v, np.float32).copy()
+    assert p.size == g.size == m2.size == v2.size
+    lib().orc_adamw_step(_p(p), _dtype_code(p), _p(g), _dtype_code(g), _p(m2), _p(v2), p.size,
+                         lr, beta1, beta2, eps, wd, bc1, bc2, apply, clip)
+    return p, m2, v2
 
 
 def sha256(data: bytes) -> bytes:

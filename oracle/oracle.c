@@ -444,6 +444,78 @@ int orc_grad_norm(const float* v, int64_t n, float* sumsq, float* norm) {
 }
 
 /* ------------------------------------------------------------------------
+ * Optimizer step -- §3.2 "Optimizer" (AdamW with beta1 0.9, beta2 0.95,
+ * eps 1e-8 through a reproducible fused kernel; decoupled weight decay 0.1
+ * on the linear layers and the LM head, none on normalisation weights;
+ * gradients clipped to a global l2 norm of 1.0), §3.2 "Optimizer-state
+ * precision" (BF16 parameters, FP32 moments: widen parameter and gradient,
+ * update in FP32, round to BF16 once per step), §3.4.2 "Gradient behavior,
+ * Clipping, and Spike Protocol" (five optimizer steps skipped when the
+ * pre-clip norm exceeds 5).
+ *
+ * The pages name the algorithm, not its operation order; this is the
+ * decoupled form of AdamW written out one rounded operation at a time:
+ *   m = b1*m + (1-b1)*g              v = b2*v + (1-b2)*(g*g)
+ *   mh = m / bc1    vh = v / bc2     u = mh / (sqrt(vh) + eps)
+ *   p = p - lr*(u + wd*p)
+ * with bc = 1 - beta^t, beta^t the t-fold product of rounded multiplies.
+ * ---------------------------------------------------------------------- */
+void orc_adamw_bias_corrections(int64_t t, float beta1, float beta2, float* bc1,
+                                float* bc2) {
+  float p1 = 1.0f, p2 = 1.0f;
+  for (int64_t i = 0; i < t; i++) {
+    p1 = fmul(p1, beta1);
+    p2 = fmul(p2, beta2);
+  }
+  *bc1 = fsub(1.0f, p1);
+  *bc2 = fsub(1.0f, p2);
+}
+
+/* One step's control from the pre-clip global norm.  A norm above
+ * spike_threshold, or not finite, (re)starts a window of skip_steps skipped
+ * optimizer steps, this one first; inside a window nothing is applied.
+ * Otherwise a norm above max_norm scales the gradient by max_norm / norm,
+ * and a smaller one leaves it as it is. */
+int orc_adamw_decide(float norm, float max_norm, float spike_threshold,
+                     int skip_steps, int32_t* skip_state, float* apply,
+                     float* clip) {
+  norm = orc_flush(norm);
+  const int finite = isfinite(norm);
+  if (!finite || norm > spike_threshold) *skip_state = skip_steps;
+  if (*skip_state > 0) {
+    *skip_state -= 1;
+    *apply = 0.0f;
+    *clip = 0.0f;
+  } else {
+    *apply = 1.0f;
+    *clip = norm > max_norm ? fdiv(orc_flush(max_norm), norm) : 1.0f;
+  }
+  return finite ? 0 : ORC_FLAG_NONFINITE;
+}
+
+void orc_adamw_step(void* param, int pdtype, const void* grad, int gdtype,
+                    float* m, float* v, int64_t n, float lr, float beta1,
+                    float beta2, float eps, float wd, float bc1, float bc2,
+                    float apply, float clip) {
+  if (apply == 0.0f) return;
+  const float omb1 = fsub(1.0f, beta1), omb2 = fsub(1.0f, beta2);
+  for (int64_t i = 0; i < n; i++) {
+    float g = load(grad, gdtype, i);
+    if (clip != 1.0f) g = fmul(g, clip);
+    const float p = load(param, pdtype, i);
+    const float mi = fadd(fmul(beta1, orc_flush(m[i])), fmul(omb1, g));
+    const float vi = fadd(fmul(beta2, orc_flush(v[i])), fmul(omb2, fmul(g, g)));
+    const float mh = fdiv(mi, bc1);
+    const float vh = fdiv(vi, bc2);
+    const float u = fdiv(mh, fadd(fsqrt(vh), eps));
+    const float pn = fsub(p, fmul(lr, fadd(u, fmul(wd, p))));
+    m[i] = mi;
+    v[i] = vi;
+    store(param, pdtype, i, pn);
+  }
+}
+
+/* ------------------------------------------------------------------------
  * SHA-256, FIPS 180-4 §6.2, and the canonical state hash (§5 "Runtime
  * overhead" and App. B: a canonical per-step hash of the training state;
  * computed here over raw little-endian tensor bytes in a Merkle tree).

@@ -19,7 +19,9 @@
  *     dimension before the weight-gradient quantisation.
  *   - §3.1 "RMSNorm", "Weights are initialized..." paragraph: normalisation
  *     in FP32, parameters BF16, FP32 gradient reduction.
- *   - §3.2 "Optimizer": global l2 gradient norm.
+ *   - §3.2 "Optimizer": global l2 gradient norm; AdamW, clipping;
+ *     "Optimizer-state precision": BF16 parameters, FP32 moments.
+ *   - §3.4.2: the spike protocol (five skipped optimizer steps).
  *   - App. A.3: every average is a multiply by a precomputed reciprocal.
  *   - §5 "Runtime overhead" / App. B: a canonical state hash per step.
  *
@@ -41,6 +43,8 @@
  *   RMSNorm ......... +-1 rows give closed-form rstd; fp64 bounds
  *   grad-norm ....... 2^k leaves of 2^-j give exact closed forms
  *   SHA-256 ......... Python hashlib (FIPS 180-4), independent Python Merkle
+ *   AdamW ........... fp64 evaluation within rounding bounds, zero-gradient
+ *                     and first-step closed forms, the skip-window sequence
  * The butterfly stage order of the fp WHT and the RMSNorm backward operation
  * order are definitions that no external value fixes: parity unpinned beyond
  * the bounds and special cases above.
@@ -137,6 +141,22 @@ void orc_rmsnorm_bwd(const void* x, const void* g, const float* rstd,
 
 /* Global grad-norm: ss = tree(v*v), norm = sqrt(ss). */
 int orc_grad_norm(const float* v, int64_t n, float* sumsq, float* norm);
+
+/* AdamW step (decoupled weight decay), global-norm clip and spike skip.
+ * bias corrections: bc = 1 - beta^t, beta^t a t-fold rounded product. */
+void orc_adamw_bias_corrections(int64_t t, float beta1, float beta2, float* bc1,
+                                float* bc2);
+/* Step control from the pre-clip norm: apply (1 or 0) and clip scale;
+ * skip_state counts the skipped steps still due. */
+int orc_adamw_decide(float norm, float max_norm, float spike_threshold,
+                     int skip_steps, int32_t* skip_state, float* apply,
+                     float* clip);
+/* One update of n elements: param (dtype pdtype) and the fp32 moments m, v
+ * in place, from grad (dtype gdtype). */
+void orc_adamw_step(void* param, int pdtype, const void* grad, int gdtype,
+                    float* m, float* v, int64_t n, float lr, float beta1,
+                    float beta2, float eps, float wd, float bc1, float bc2,
+                    float apply, float clip);
 
 /* SHA-256 (FIPS 180-4). */
 void orc_sha256(const uint8_t* msg, uint64_t len, uint8_t out[32]);

@@ -39,6 +39,18 @@ MUTANTS = {
                          "uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 24);"),
     "merkle_fanin_64": ("const uint64_t LEAF = 4096, FAN = 128;", "const uint64_t LEAF = 4096, FAN = 64;"),
     "bf16_round_truncates": ("u += 0x7fffu + ((u >> 16) & 1u);", "u += 0;"),
+    "adamw_beta2_on_m": ("const float mi = fadd(fmul(beta1, orc_flush(m[i])), fmul(omb1, g));",
+                         "const float mi = fadd(fmul(beta2, orc_flush(m[i])), fmul(omb1, g));"),
+    "adamw_no_bias_correction": ("const float mh = fdiv(mi, bc1);", "const float mh = mi;"),
+    "adamw_eps_inside_sqrt": ("const float u = fdiv(mh, fadd(fsqrt(vh), eps));",
+                              "const float u = fdiv(mh, fsqrt(fadd(vh, eps)));"),
+    "adamw_decay_sign": ("const float pn = fsub(p, fmul(lr, fadd(u, fmul(wd, p))));",
+                         "const float pn = fsub(p, fmul(lr, fsub(u, fmul(wd, p))));"),
+    "adamw_bias_power_of_beta2": ("    p1 = fmul(p1, beta1);", "    p1 = fmul(p1, beta2);"),
+    "spike_skips_four": ("if (!finite || norm > spike_threshold) *skip_state = skip_steps;",
+                         "if (!finite || norm > spike_threshold) *skip_state = skip_steps - 1;"),
+    "clip_always_scales": ("*clip = norm > max_norm ? fdiv(orc_flush(max_norm), norm) : 1.0f;",
+                           "*clip = fdiv(orc_flush(max_norm), norm);"),
 }
 
 

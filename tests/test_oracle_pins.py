@@ -690,3 +690,149 @@ def test_generator_counter_based(syn):
     assert np.array_equal(a, b[:1000])       # value i depends on (seed, tag, i) only
     c = syn.normal((1000,), 1.0, tag=78)
     assert not np.array_equal(a, c)
+
+
+# --------------------------------------------------------------------------
+# optimizer: AdamW, global-norm clip, spike skip (report §3.2 "Optimizer",
+# "Optimizer-state precision"; §3.4.2 "Gradient behavior, Clipping, and
+# Spike Protocol")
+# --------------------------------------------------------------------------
+def test_adamw_bias_corrections_exact_and_bounded(orc):
+    b1, b2 = Fraction(float(f32(0.9))), Fraction(float(f32(0.95)))
+    # t = 1: 1 - beta is exact in binary32 (Sterbenz)
+    bc1, bc2 = orc.adamw_bias_corrections(1)
+    assert Fraction(float(bc1)) == 1 - b1 and Fraction(float(bc2)) == 1 - b2
+    # t > 1: within t half-ulp relative errors of the exact power, plus the
+    # final rounding
+    for t in (2, 3, 10, 100, 1000):
+        bc1, bc2 = orc.adamw_bias_corrections(t)
+        for bc, b in ((bc1, b1), (bc2, b2)):
+            exact = 1 - b ** t
+            bound = (b ** t) * Fraction(t, 2 ** 23) + Fraction(float(np.spacing(f32(bc))))
+            assert abs(Fraction(float(bc)) - exact) <= bound, (t, float(bc), float(exact))
+    # very long runs: beta^t flushes to zero, the correction is 1
+    assert orc.adamw_bias_corrections(100000) == (f32(1.0), f32(1.0))
+
+
+def test_adamw_decide_spike_protocol(orc):
+    """A pre-clip norm above 5 skips five optimizer steps (this one and the
+    next four); two spikes skip ten; a norm in (1, 5] is clipped to 1; a norm
+    of at most 1 is left alone.  A non-finite norm counts as a spike (the
+    reading for a case the pages leave open)."""
+    norms = [0.3, 1.0, 2.5, 5.0, 5.78, 0.4, 0.4, 0.4, 0.4, 0.4, 0.4, 6.88, 0.2, 7.0, 0.2,
+             0.2, 0.2, 0.2, 0.2, 0.2, float("inf"), 0.2, 0.2, 0.2, 0.2, 0.2]
+    # the protocol written out independently: remaining skips after a spike
+    expect, remaining = [], 0
+    for n in norms:
+        if not math.isfinite(n) or n > 5.0:
+            remaining = 5
+        if remaining:
+            remaining -= 1
+            expect.append("skip")
+        else:
+            expect.append("clip" if n > 1.0 else "keep")
+    st, skipped, got = 0, 0, []
+    for n in norms:
+        ap, cl, st, fl = orc.adamw_decide(n, st)
+        assert fl == (0 if math.isfinite(n) else 1)
+        if ap == 0.0:
+            got.append("skip")
+            skipped += 1
+            assert cl == 0.0
+        elif cl != 1.0:
+            got.append("clip")
+            # the clipped gradient has norm 1 up to the rounding of 1 / norm
+            assert abs(float(cl) * n - 1.0) <= 2.0 ** -23, (n, cl)
+        else:
+            got.append("keep")
+            assert cl == 1.0
+    assert got == expect
+    # the pages' run: two spikes, ten skipped steps; here a third spike lands
+    # inside the second window and restarts it, and the inf adds a fourth
+    assert expect.count("skip") == skipped == 5 + 2 + 5 + 5
+
+
+def _adamw_f64(p, g, m, v, lr, t, wd, beta1=0.9, beta2=0.95, eps=1e-8):
+    """The same update in binary64 from the same binary32 inputs."""
+    b1, b2, e = float(f32(beta1)), float(f32(beta2)), float(f32(eps))
+    p, g, m, v = (np.asarray(a, np.float64) for a in (p, g, m, v))
+    m2 = b1 * m + (1 - b1) * g
+    v2 = b2 * v + (1 - b2) * g * g
+    mh = m2 / (1 - b1 ** t)
+    vh = v2 / (1 - b2 ** t)
+    u = mh / (np.sqrt(vh) + e)
+    return p - float(f32(lr)) * (u + float(f32(wd)) * p), m2, v2, u
+
+
+def test_adamw_step_fp32_param_vs_fp64(orc):
+    rng = np.random.default_rng(11)
+    n = 4096
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (np.abs(rng.standard_normal(n)) * 1e-7 + 1e-9).astype(np.float32)
+    lr, t = 3e-4, 7
+    bc1, bc2 = orc.adamw_bias_corrections(t)
+    p1, m1, v1 = orc.adamw_step(p, g, m, v, lr, bc1, bc2)
+    pe, me, ve, ue = _adamw_f64(p, g, m, v, lr, t, 0.1)
+    # moments: two products and a sum, each rounded once -- half an ulp of
+    # each product and of the sum (the terms may cancel)
+    b1, b2 = float(f32(0.9)), float(f32(0.95))
+    tm = (np.abs(b1 * m.astype(np.float64)) + np.abs((1 - b1) * g.astype(np.float64))) * 2.0 ** -24
+    tv = (np.abs(b2 * v.astype(np.float64)) + (1 - b2) * g.astype(np.float64) ** 2 * 2) * 2.0 ** -24
+    assert np.all(np.abs(m1 - me) <= tm + np.spacing(np.abs(m1)) / 2)
+    assert np.all(np.abs(v1 - ve) <= tv + np.spacing(np.abs(v1)) / 2)
+    # parameter: one rounding of p plus lr times the few-ulp error of u
+    tol = np.spacing(np.abs(p1)) + float(lr) * np.abs(ue) * 16 * 2.0 ** -24
+    assert np.all(np.abs(p1 - pe) <= tol)
+    # and it moved against the gradient direction of u for every element
+    assert np.all(np.sign(p - p1) == np.sign(ue + 0.1 * p))
+
+
+def test_adamw_step_bf16_param_rounds_once(orc):
+    rng = np.random.default_rng(12)
+    n = 4096
+    pf = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    pb = np.array([orc.f32_to_bf16(float(x)) for x in pf], np.uint16)
+    pw = np.array([orc.bf16_to_f32(int(h)) for h in pb], np.float32)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    lr, t = 1e-3, 1
+    bc1, bc2 = orc.adamw_bias_corrections(t)
+    p1, _, _ = orc.adamw_step(pb, g, m, v, lr, bc1, bc2)
+    pe, _, _, ue = _adamw_f64(pw, g, m, v, lr, t, 0.1)
+    # first step from zero moments: u = g / (|g| + eps), +-1 up to eps/|g|
+    assert np.all(np.abs(np.abs(ue) - 1.0) <= 1e-8 / np.abs(g) + 1e-6)
+    # the bf16 result is one of the two bf16 neighbours of the exact value,
+    # and the nearest whenever the exact value is not within 2^-14 relative
+    # of a rounding boundary
+    got = np.array([orc.bf16_to_f32(int(h)) for h in p1], np.float64)
+    ulp = np.array([float(np.spacing(np.float32(abs(x)))) * 65536 for x in pe])
+    assert np.all(np.abs(got - pe) <= ulp)
+    nearest = np.array([orc.bf16_to_f32(orc.f32_to_bf16(float(x))) for x in pe], np.float64)
+    frac = np.abs(pe / ulp - np.round(pe / ulp))
+    safe = np.abs(frac - 0.5) > 1e-3
+    assert np.all(got[safe] == nearest[safe])
+
+
+def test_adamw_zero_gradient_and_skip_are_identities(orc):
+    rng = np.random.default_rng(13)
+    n = 257
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    z = np.zeros(n, np.float32)
+    bc1, bc2 = orc.adamw_bias_corrections(3)
+    # zero gradient, zero moments, no weight decay: u = 0 / (0 + eps) = 0
+    p1, m1, v1 = orc.adamw_step(p, z, z, z, 3e-4, bc1, bc2, wd=0.0)
+    assert np.array_equal(p1.view(np.uint32), p.view(np.uint32))
+    assert not m1.any() and not v1.any()
+    # a skipped step changes nothing at all
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (np.abs(rng.standard_normal(n)) * 1e-7).astype(np.float32)
+    p2, m2, v2 = orc.adamw_step(p, g, m, v, 3e-4, bc1, bc2, apply=0.0, clip=0.0)
+    for a, b in ((p2, p), (m2, m), (v2, v)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # decay alone (zero gradient and moments) shrinks every weight toward 0
+    p3, _, _ = orc.adamw_step(p, z, z, z, 0.1, bc1, bc2, wd=0.5)
+    assert np.all(np.abs(p3) <= np.abs(p)) and np.all(np.sign(p3) * np.sign(p) >= 0)
