@@ -28,13 +28,26 @@ SYMBOLS = [
     "brq_quantize_dy_bwd",
     "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm",
     "brq_hash_workspace_size", "brq_hash_state", "brq_hash_digests_workspace_size",
-    "brq_hash_tensor_digests", "brq_hash_combine", "brq_status_string",
+    "brq_hash_tensor_digests", "brq_hash_combine", "brq_adamw_bias_corrections",
+    "brq_adamw_decide", "brq_adamw_step", "brq_status_string",
     "brq_last_hip_error", "brq_spec_version",
 ]
 
 
 class BrqError(RuntimeError):
     pass
+
+
+class AdamWHparams(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("weight_decay", C.c_float), ("bias_correction1", C.c_float),
+                ("bias_correction2", C.c_float)]
+
+
+# AdamW, clipping and spike-protocol defaults of the report (§3.2 "Optimizer",
+# §3.4.2)
+ADAMW_BETA1, ADAMW_BETA2, ADAMW_EPS, ADAMW_WD = 0.9, 0.95, 1e-8, 0.1
+CLIP_MAX_NORM, SPIKE_THRESHOLD, SPIKE_SKIP_STEPS = 1.0, 5.0, 5
 
 
 class Tune(C.Structure):
@@ -94,6 +107,12 @@ def lib():
         L.brq_hash_tensor_digests.argtypes = [vp, i32, vp, vp, sz, vp]
         L.brq_hash_combine.restype = i32
         L.brq_hash_combine.argtypes = [vp, i32, vp, vp]
+        L.brq_adamw_bias_corrections.restype = i32
+        L.brq_adamw_bias_corrections.argtypes = [i64, C.c_float, C.c_float, vp, vp]
+        L.brq_adamw_decide.restype = i32
+        L.brq_adamw_decide.argtypes = [vp, C.c_float, C.c_float, i32, vp, vp, vp, vp]
+        L.brq_adamw_step.restype = i32
+        L.brq_adamw_step.argtypes = [vp, i32, vp, i32, vp, vp, i64, vp, vp, vp]
         L.brq_status_string.restype = C.c_char_p
         L.brq_status_string.argtypes = [i32]
         L.brq_last_hip_error.restype = i32
@@ -475,3 +494,52 @@ def hash_combine(digests, out=None):
     _check(lib().brq_hash_combine(_ptr(digests), digests.numel() // 32, _ptr(d), _stream()),
            "hash_combine")
     return d
+
+
+# --------------------------------------------------------------------------
+# optimizer step
+# --------------------------------------------------------------------------
+def adamw_bias_corrections(t: int, beta1: float = ADAMW_BETA1, beta2: float = ADAMW_BETA2):
+    """(1 - beta1^t, 1 - beta2^t) as binary32, computed by libbrq on the host."""
+    b1, b2 = C.c_float(), C.c_float()
+    _check(lib().brq_adamw_bias_corrections(int(t), beta1, beta2, C.byref(b1), C.byref(b2)),
+           "adamw_bias_corrections")
+    return b1.value, b2.value
+
+
+def adamw_decide(norm, skip_state, out=None, max_norm: float = CLIP_MAX_NORM,
+                 spike_threshold: float = SPIKE_THRESHOLD, skip_steps: int = SPIKE_SKIP_STEPS,
+                 flags=None):
+    """Step decision on the device: norm is a device fp32 tensor holding the
+    pre-clip global norm (first element); skip_state a device int32 [1].
+    Returns ctl, a device fp32 [2] = (apply, clip)."""
+    _dev(norm, "norm")
+    if norm.dtype != torch.float32 or norm.numel() < 1:
+        raise BrqError("norm: expected a device fp32 tensor")
+    _out(skip_state, (1,), torch.int32, "skip_state")
+    ctl = _out(out, (2,), torch.float32, "ctl") if out is not None else \
+        torch.empty(2, dtype=torch.float32, device=norm.device)
+    _check(lib().brq_adamw_decide(norm.data_ptr(), max_norm, spike_threshold, skip_steps,
+                                  skip_state.data_ptr(), ctl.data_ptr(), _ptr(flags), _stream()),
+           "adamw_decide")
+    return ctl
+
+
+def adamw_step(param, grad, m, v, ctl, lr: float, bias_corrections, beta1: float = ADAMW_BETA1,
+               beta2: float = ADAMW_BETA2, eps: float = ADAMW_EPS,
+               weight_decay: float = ADAMW_WD):
+    """In-place AdamW update of param (bf16 or fp32) and the fp32 moments m, v
+    from grad (fp32 or bf16), under the decision ctl of adamw_decide."""
+    for t, nm in ((param, "param"), (grad, "grad"), (m, "m"), (v, "v"), (ctl, "ctl")):
+        _dev(t, nm)
+    n = param.numel()
+    if grad.numel() != n or m.numel() != n or v.numel() != n:
+        raise BrqError("adamw_step: param, grad, m, v must have the same size")
+    if m.dtype != torch.float32 or v.dtype != torch.float32 or ctl.dtype != torch.float32 \
+            or ctl.numel() != 2:
+        raise BrqError("adamw_step: m, v fp32 and ctl fp32 [2]")
+    bc1, bc2 = bias_corrections
+    hp = AdamWHparams(lr, beta1, beta2, eps, weight_decay, bc1, bc2)
+    _check(lib().brq_adamw_step(param.data_ptr(), _fp_code(param), grad.data_ptr(), _fp_code(grad),
+                                m.data_ptr(), v.data_ptr(), n, C.byref(hp), ctl.data_ptr(),
+                                _stream()), "adamw_step")

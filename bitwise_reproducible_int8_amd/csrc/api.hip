@@ -290,6 +290,48 @@ int brq_grad_norm(const float* v, int64_t n, float* sumsq, float* norm, void* ws
   return hip_status(grad_norm(v, n, sumsq, norm, ws, c, dflags, as_stream(stream)));
 }
 
+int brq_adamw_bias_corrections(int64_t t, float beta1, float beta2, float* bc1, float* bc2) {
+  if (t < 1 || !bc1 || !bc2) return BRQ_E_ARG;
+  // host binary32 arithmetic (no contraction); a subnormal product is
+  // flushed to zero, after which the power stays zero
+  auto flush_h = [](float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0u) u &= 0x80000000u;
+    memcpy(&f, &u, 4);
+    return f;
+  };
+  float p1 = 1.0f, p2 = 1.0f;
+  for (int64_t i = 0; i < t; ++i) {
+    if (p1 == 0.0f && p2 == 0.0f) break;
+    p1 = flush_h(p1 * beta1);
+    p2 = flush_h(p2 * beta2);
+  }
+  *bc1 = flush_h(1.0f - p1);
+  *bc2 = flush_h(1.0f - p2);
+  return BRQ_OK;
+}
+
+int brq_adamw_decide(const float* norm, float max_norm, float spike_threshold, int skip_steps,
+                     int32_t* skip_state, float* ctl, int32_t* dflags, void* stream) {
+  if (!norm || !skip_state || !ctl) return BRQ_E_NULL;
+  if (skip_steps < 0) return BRQ_E_ARG;
+  return hip_status(adamw_decide(norm, max_norm, spike_threshold, skip_steps, skip_state, ctl,
+                                 dflags, as_stream(stream)));
+}
+
+int brq_adamw_step(void* param, int param_dtype, const void* grad, int grad_dtype, float* m,
+                   float* v, int64_t n, const brq_adamw_hparams* hp, const float* ctl,
+                   void* stream) {
+  if (n < 0) return BRQ_E_SHAPE;
+  if (!fp_dtype(param_dtype) || !fp_dtype(grad_dtype)) return BRQ_E_DTYPE;
+  if (!hp || !ctl || (n > 0 && (!param || !grad || !m || !v))) return BRQ_E_NULL;
+  if (!aligned16(param) || !aligned16(grad) || !aligned16(m) || !aligned16(v))
+    return BRQ_E_ALIGN;
+  return hip_status(
+      adamw_step(param, param_dtype, grad, grad_dtype, m, v, n, *hp, ctl, as_stream(stream)));
+}
+
 size_t brq_hash_workspace_size(const brq_tensor_ref* t, int n) {
   if (n < 0 || (n > 0 && !t)) return 0;
   return hash_ws(t, n);

@@ -38,6 +38,12 @@ hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* 
                             float* out1, void* ws, int chunk_log2, int32_t* dflags,
                             hipStream_t s);
 
+// Optimizer step (optim.hip).
+hipError_t adamw_decide(const float* norm, float max_norm, float spike, int skip_steps,
+                        int32_t* skip_state, float* ctl, int32_t* dflags, hipStream_t s);
+hipError_t adamw_step(void* param, int pdtype, const void* grad, int gdtype, float* m, float* v,
+                      int64_t n, const brq_adamw_hparams& h, const float* ctl, hipStream_t s);
+
 // From a tree sum on device, compute the LSQ step size and reciprocal:
 // sr[0] = s, sr[1] = r.  Optionally copies s and the max into scale/amax.
 hipError_t lsq_finalize(const float* sum_max, float inv_n, float* sr,

@@ -46,10 +46,11 @@ from __future__ import annotations
 
 import torch
 
-from . import (BrqError, OP_DW_WHT, OP_DY_BWD, OP_GRAD_NORM, OP_QGEMM, OP_QUANTIZE,
-               OP_RMSNORM_BWD, grad_norm, hash_state, hash_state_workspace_size, qgemm_bwd_dx,
-               qgemm_dw, qgemm_fwd, quantize_dy_bwd, quantize_lsq, rmsnorm_fixed_bwd,
-               rmsnorm_fixed_fwd, wht_quant_x, workspace_size)
+from . import (ADAMW_WD, SPIKE_THRESHOLD, BrqError, OP_DW_WHT, OP_DY_BWD, OP_GRAD_NORM, OP_QGEMM, OP_QUANTIZE,
+               OP_RMSNORM_BWD, adamw_bias_corrections, adamw_decide, adamw_step, grad_norm,
+               hash_state, hash_state_workspace_size, qgemm_bwd_dx, qgemm_dw, qgemm_fwd,
+               quantize_dy_bwd, quantize_lsq, rmsnorm_fixed_bwd, rmsnorm_fixed_fwd, wht_quant_x,
+               workspace_size)
 
 
 class _NoTimer:
@@ -203,3 +204,63 @@ class LayerStep:
             T.begin("hash_state")
             hash_state(self.hash_list(), ws=ws, out=self.digest)
             T.end("hash_state")
+
+
+class OptimizerStep:
+    """The optimizer step after a LayerStep (report §3.2 "Optimizer",
+    "Optimizer-state precision"; §3.4.2 spike protocol): AdamW on the
+    layer's parameters, clipped by the step's global grad-norm, skipped for
+    five steps after a spike.
+
+    Parameters live in one bf16 arena laid out like the gradient arena
+    (every weight [N][K] in linear order, then every norm gain); the layer's
+    weight and gain tensors are rebound to views of it, so the next layer
+    step sees the update.  Moments m, v are fp32 arenas of the same layout.
+    Per step: the decision on the device from the step's norm, then one
+    update of the linear weights (weight decay 0.1) and one of the norm
+    gains (no decay).  Nothing leaves the device.
+    """
+
+    def __init__(self, step, lr=3e-4, weight_decay=ADAMW_WD, spike_threshold=SPIKE_THRESHOLD):
+        self.step, self.lr, self.wd = step, lr, weight_decay
+        self.spike_threshold = spike_threshold
+        dev = step.device
+        n = step.arena.numel()
+        self.param = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        off = 0
+        for i, w in enumerate(step.w):
+            if w.dtype != torch.bfloat16:
+                raise BrqError("OptimizerStep keeps bf16 parameters")
+            k = w.numel()
+            self.param[off:off + k].copy_(w.reshape(-1))
+            step.w[i] = self.param[off:off + k].view(w.shape)
+            off += k
+        self.n_linear = off
+        for j, (name, h, g, ndy) in enumerate(step.norms):
+            k = g.numel()
+            self.param[off:off + k].copy_(g.reshape(-1))
+            step.norms[j] = (name, h, self.param[off:off + k].view(g.shape), ndy)
+            off += k
+        self.m = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.v = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.skip = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.ctl = torch.empty(2, dtype=torch.float32, device=dev)
+        self.t = 0
+
+    def hash_list(self):
+        return [("param", self.param), ("adam.m", self.m), ("adam.v", self.v)]
+
+    def run(self, timer=None):
+        T = timer or _NoTimer()
+        st, nl = self.step, self.n_linear
+        self.t += 1
+        bc = adamw_bias_corrections(self.t)
+        T.begin("optimizer")
+        adamw_decide(st.gn[1:2], self.skip, out=self.ctl, spike_threshold=self.spike_threshold,
+                     flags=st.flags)
+        adamw_step(self.param[:nl], st.arena[:nl], self.m[:nl], self.v[:nl], self.ctl, self.lr, bc,
+                   weight_decay=self.wd)
+        if self.param.numel() > nl:
+            adamw_step(self.param[nl:], st.arena[nl:], self.m[nl:], self.v[nl:], self.ctl, self.lr,
+                       bc, weight_decay=0.0)
+        T.end("optimizer")

@@ -38,6 +38,7 @@ SEED = 42
 
 # tensor tags (the Philox key's second word)
 TAG_X, TAG_W, TAG_DY, TAG_OUTLIER, TAG_G, TAG_V, TAG_SUBN = 1, 2, 3, 4, 5, 6, 7
+TAG_P, TAG_M, TAG_S = 8, 9, 10
 
 _lib = None
 
@@ -207,3 +208,18 @@ def layer_norm_inputs(j, M=32768, seed=SEED):
     g = normal((D,), 0.1, mean=1.0, tag=tag_for(base, TAG_G), bf16=True, seed=seed)
     dy = normal((M, D), 1e-3, tag=tag_for(base, TAG_DY), bf16=True, seed=seed)
     return h, g, dy
+
+
+def optimizer_group(n, grad_std=1e-4, param_bf16=True, grad_bf16=False, group=0, seed=SEED):
+    """One synthetic parameter group for the optimizer step: parameters
+    N(0, 0.02) (bf16 or fp32), gradients N(0, grad_std), first moments
+    N(0, grad_std / 10), second moments |N(0, grad_std^2)| (fp32).  A Philox
+    mask replaces 1% of the gradients with bf16 subnormals (read as zeros)."""
+    base = 40 + group
+    p = normal((n,), 0.02, tag=tag_for(base, TAG_P), bf16=param_bf16, seed=seed)
+    g = normal((n,), grad_std, tag=tag_for(base, TAG_DY), bf16=grad_bf16, seed=seed)
+    if grad_bf16:
+        bf16_subnormals(g, 100, tag=tag_for(base, TAG_SUBN), seed=seed)
+    m = normal((n,), grad_std / 10, tag=tag_for(base, TAG_M), seed=seed)
+    v = np.abs(normal((n,), grad_std * grad_std, tag=tag_for(base, TAG_S), seed=seed))
+    return p, g, m, v

@@ -282,6 +282,55 @@ int brq_hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* digests,
 int brq_hash_combine(const uint8_t* digests, int n, uint8_t* digest32,
                      void* stream);
 
+/* ---------------------------------------------------------------------
+ * Optimizer step after the layer: AdamW with global-norm clipping and the
+ * spike protocol (§3.2 "Optimizer": beta1 0.9, beta2 0.95, eps 1e-8,
+ * decoupled weight decay 0.1 on linear layers and none on normalisation
+ * weights, global l2 clip at 1.0; §3.2 "Optimizer-state precision": BF16
+ * parameters, FP32 moments, widen -> update in FP32 -> round to BF16 once;
+ * §3.4.2 "Gradient behavior, Clipping, and Spike Protocol": five optimizer
+ * steps skipped when the pre-clip norm exceeds 5).
+ *
+ * Per element, each operation one rounded binary32 operation, flushed:
+ *   g = g * clip (when clip != 1)
+ *   m = b1*m + (1-b1)*g          v = b2*v + (1-b2)*(g*g)
+ *   u = (m / bc1) / (sqrt(v / bc2) + eps)
+ *   p = p - lr*(u + wd*p)
+ * --------------------------------------------------------------------- */
+typedef struct brq_adamw_hparams {
+  float lr;
+  float beta1, beta2, eps;
+  float weight_decay;      /* 0 for normalisation weights */
+  float bias_correction1;  /* 1 - beta1^t (brq_adamw_bias_corrections) */
+  float bias_correction2;  /* 1 - beta2^t */
+} brq_adamw_hparams;
+
+/* Host: bias corrections of optimizer step t >= 1: bc = 1 - beta^t with
+ * beta^t the t-fold product of rounded binary32 multiplies (subnormal
+ * products flushed).  BRQ_E_ARG for t < 1 or NULL outputs. */
+int brq_adamw_bias_corrections(int64_t t, float beta1, float beta2, float* bc1,
+                               float* bc2);
+
+/* Device: the step's decision from the pre-clip global norm (norm: device
+ * float, e.g. the second output of brq_grad_norm).  A norm above
+ * spike_threshold, or not finite, (re)starts a window of skip_steps skipped
+ * steps, this one first; inside a window ctl = {0, 0}.  Otherwise
+ * ctl = {1, clip} with clip = max_norm / norm for a norm above max_norm, else
+ * 1.  skip_state: device int32 [1], the skipped steps still due (start at 0).
+ * ctl: device float [2].  A non-finite norm raises BRQ_FLAG_NONFINITE in
+ * dflags (may be NULL). */
+int brq_adamw_decide(const float* norm, float max_norm, float spike_threshold,
+                     int skip_steps, int32_t* skip_state, float* ctl,
+                     int32_t* dflags, void* stream);
+
+/* Device: one AdamW update of n elements in place.  param BRQ_BF16 or
+ * BRQ_F32, grad BRQ_F32 or BRQ_BF16, m and v fp32; all [n], 16-byte
+ * aligned, not overlapping.  ctl: the decision of brq_adamw_decide (device);
+ * with ctl[0] == 0 nothing is written.  No workspace. */
+int brq_adamw_step(void* param, int param_dtype, const void* grad, int grad_dtype,
+                   float* m, float* v, int64_t n, const brq_adamw_hparams* hp,
+                   const float* ctl, void* stream);
+
 /* Status text, HIP error of the last BRQ_E_HIP in this thread, version. */
 const char* brq_status_string(int status);
 int brq_last_hip_error(void);

@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -84,3 +85,15 @@ def test_workspace_sizes_are_monotone(lib):
     b = lib.brq_workspace_size(1, 16384, 8192, 0, 0, None)
     assert 0 < a < b
     assert lib.brq_workspace_size(3, 16384, 8192, 2048, 128, None) > 16384 * (8192 + 2048)
+
+
+def test_adamw_bias_corrections_host_matches_oracle():
+    """The library's host-side bias corrections (no GPU involved) equal the
+    oracle's, an independent implementation of the same definition."""
+    import bitwise_reproducible_int8_amd as brq
+    import oracle as orc
+    for t in (1, 2, 3, 10, 99, 1000, 50000, 200000):
+        for b1, b2 in ((0.9, 0.95), (0.8, 0.999)):
+            got = brq.adamw_bias_corrections(t, b1, b2)
+            want = orc.adamw_bias_corrections(t, b1, b2)
+            assert np.float32(got[0]) == want[0] and np.float32(got[1]) == want[1], (t, b1, b2)

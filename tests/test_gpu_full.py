@@ -190,3 +190,45 @@ def test_layer_full(brq):
     # a second step on the same inputs reproduces the digest
     step.run()
     assert bytes(to_np(step.digest)).hex() == stored("layer")["state"]
+
+
+@pytest.mark.parametrize("grad_std,expect", [(1e-4, "keep"), (3e-4, "clip"), (1e-3, "skip")])
+def test_optimizer_full(brq, grad_std, expect):
+    """The optimizer step over a layer-sized parameter set (the seven
+    linears' 60.8 M bf16 weights with weight decay, the two norm gains
+    without), clipped by the global norm of the same gradients: unclipped,
+    clipped and skipped steps, against the oracle, every element."""
+    n_lin = sum(N * K for _, K, N, _ in syn.LAYER_LINEARS)
+    n_nrm = sum(D for _, D in syn.LAYER_NORMS)
+    say("full optimizer", n_lin, n_nrm, grad_std, expect)
+    p1, g1, m1, v1 = syn.optimizer_group(n_lin, grad_std=grad_std, group=0)
+    p2, g2, m2, v2 = syn.optimizer_group(n_nrm, grad_std=grad_std, group=1)
+    g = np.concatenate([g1, g2])
+    t, lr = 5, 3e-4
+    _, onorm, _ = orc.grad_norm(g)
+    ap, cl, ost, _ = orc.adamw_decide(onorm, 0)
+    kind = "skip" if ap == 0 else ("clip" if cl != 1.0 else "keep")
+    assert kind == expect, (float(onorm), kind)
+    bc = orc.adamw_bias_corrections(t)
+    dp = to_dev(np.concatenate([p1, p2]))
+    dg = to_dev(g)
+    dm = to_dev(np.concatenate([m1, m2]))
+    dv = to_dev(np.concatenate([v1, v2]))
+    gn = torch.empty(2, dtype=torch.float32, device=DEV)
+    brq.grad_norm(dg, out=gn)
+    skip = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ctl = brq.adamw_decide(gn[1:2], skip)
+    bcd = brq.adamw_bias_corrections(t)
+    brq.adamw_step(dp[:n_lin], dg[:n_lin], dm[:n_lin], dv[:n_lin], ctl, lr, bcd, weight_decay=0.1)
+    brq.adamw_step(dp[n_lin:], dg[n_lin:], dm[n_lin:], dv[n_lin:], ctl, lr, bcd, weight_decay=0.0)
+    torch.cuda.synchronize()
+    assert_bitwise(gn[1:2], np.array([onorm], np.float32), "norm")
+    assert_bitwise(ctl, np.array([ap, cl], np.float32), "ctl")
+    assert int(skip.item()) == ost
+    del g, dg
+    for lo, hi, (p, gg, m, v), wd in ((0, n_lin, (p1, g1, m1, v1), 0.1),
+                                      (n_lin, n_lin + n_nrm, (p2, g2, m2, v2), 0.0)):
+        wp, wm, wv = orc.adamw_step(p, gg, m, v, lr, bc[0], bc[1], ap, cl, wd=wd)
+        assert_bitwise(dp[lo:hi], wp, f"param [{lo}, {hi})")
+        assert_bitwise(dm[lo:hi], wm, f"m [{lo}, {hi})")
+        assert_bitwise(dv[lo:hi], wv, f"v [{lo}, {hi})")
