@@ -350,6 +350,35 @@ def main():
                          "ms_per_step"}
     log(f"optimizer step: {opt_ms:.3f} ms, {optimizer['gb_per_s']} GB/s")
 
+    # Variant (not part of value): the forward and input-gradient GEMMs with
+    # bf16 outputs (each fp32 result rounded once), on the step's own codes.
+    yb = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, _, N, _ in syn.LAYER_LINEARS]
+    xb = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _, K, _, _ in syn.LAYER_LINEARS]
+
+    def bf16_gemms():
+        for i, (_n, _K, _N, xin) in enumerate(syn.LAYER_LINEARS):
+            brq.qgemm_fwd(step.q_x[xin], step.s_x[xin], step.q_w[i], step.s_w[i], out=yb[i],
+                          ws=step.ws, out_dtype=torch.bfloat16)
+            brq.qgemm_bwd_dx(step.q_g[i], step.s_g[i], step.q_wt[i], out=xb[i], ws=step.ws,
+                             out_dtype=torch.bfloat16)
+    for _ in range(args.warmup):
+        bf16_gemms()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        bf16_gemms()
+    e1.record()
+    torch.cuda.synchronize()
+    v_ms = e0.elapsed_time(e1) / args.steps
+    v_ops = sum(2 * 2 * M * N * K for _, K, N, _ in syn.LAYER_LINEARS)
+    variants = {"gemm_fwd_dx_bf16_outputs": {
+        "ms_per_step": round(v_ms, 4), "tops": round(v_ops / (v_ms * 1e-3) / 1e12, 2),
+        "fp32_outputs_ms_per_step": (round(kernels["gemm_fwd"]["ms_per_step"] +
+                                           kernels["gemm_dx"]["ms_per_step"], 4)
+                                     if kernels else None),
+        "note": "the 14 forward and input-gradient GEMMs with bf16 outputs; not part of value"}}
+    del yb, xb
+
     cpu = None
     if args.cpu_tokens > 0:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
@@ -370,6 +399,7 @@ def main():
         "ms_per_step_hash_off": round(ms_hash_off, 4),
         "tokens_per_s_hash_off": round(M / (ms_hash_off * 1e-3), 1),
         "bitwise_exact": exact, "state_digest": digest, "optimizer": optimizer,
+        "variants": variants,
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(line), flush=True)

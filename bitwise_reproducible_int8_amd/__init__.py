@@ -25,6 +25,7 @@ MAX_CONTRACTION = 133144
 SYMBOLS = [
     "brq_workspace_size", "brq_quantize_lsq", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
     "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
+    "brq_qgemm_fwd_ex", "brq_qgemm_bwd_dx_ex",
     "brq_quantize_dy_bwd",
     "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm",
     "brq_hash_workspace_size", "brq_hash_state", "brq_hash_digests_workspace_size",
@@ -79,6 +80,10 @@ def lib():
         L.brq_qgemm_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, sz, vp, vp]
         L.brq_qgemm_bwd_dx.restype = i32
         L.brq_qgemm_bwd_dx.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, sz, vp, vp]
+        L.brq_qgemm_fwd_ex.restype = i32
+        L.brq_qgemm_fwd_ex.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, i32, vp, sz, vp, vp]
+        L.brq_qgemm_bwd_dx_ex.restype = i32
+        L.brq_qgemm_bwd_dx_ex.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, vp, sz, vp, vp]
         L.brq_qgemm_bwd_dw_wht.restype = i32
         L.brq_qgemm_bwd_dw_wht.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp, vp, vp,
                                            sz, vp, vp, vp]
@@ -248,35 +253,49 @@ def quantize_lsq(x, per_row=False, col_mul=None, want_t=False, tune=None, ws=Non
     return q, q_t, scale, amax
 
 
-def qgemm_fwd(q_x, s_x, q_w, s_w, tune=None, out=None, ws=None):
+def qgemm_fwd(q_x, s_x, q_w, s_w, tune=None, out=None, ws=None, out_dtype=torch.float32):
+    """y = dequant(q_x q_w^T); out_dtype torch.float32 (the definition) or
+    torch.bfloat16 (each value rounded once to bf16)."""
     _dev(q_x, "q_x"); _dev(q_w, "q_w")
     M, K = q_x.shape
     N = q_w.shape[0]
     if q_w.shape[1] != K:
         raise BrqError("q_w: contraction length differs from q_x")
-    y = _out(out, (M, N), torch.float32, "y") if out is not None else \
-        torch.empty((M, N), dtype=torch.float32, device=q_x.device)
+    y = _out(out, (M, N), out_dtype, "y") if out is not None else \
+        torch.empty((M, N), dtype=out_dtype, device=q_x.device)
     need = workspace_size(OP_QGEMM, M, N, K, tune=tune)
     w = _ws(need, q_x.device, ws) if need else None
-    _check(lib().brq_qgemm_fwd(_ptr(q_x), _ptr(s_x), _ptr(q_w), _ptr(s_w), int(s_w.numel() > 1),
-                               M, N, K, _ptr(y), _ptr(w), 0 if w is None else w.numel(),
-                               _tune(tune), _stream()), "qgemm_fwd")
+    if out_dtype == torch.float32:
+        st = lib().brq_qgemm_fwd(_ptr(q_x), _ptr(s_x), _ptr(q_w), _ptr(s_w), int(s_w.numel() > 1),
+                                 M, N, K, _ptr(y), _ptr(w), 0 if w is None else w.numel(),
+                                 _tune(tune), _stream())
+    else:
+        st = lib().brq_qgemm_fwd_ex(_ptr(q_x), _ptr(s_x), _ptr(q_w), _ptr(s_w),
+                                    int(s_w.numel() > 1), M, N, K, _ptr(y), _fp_code(y), _ptr(w),
+                                    0 if w is None else w.numel(), _tune(tune), _stream())
+    _check(st, "qgemm_fwd")
     return y
 
 
-def qgemm_bwd_dx(q_g, s_g, q_wt, tune=None, out=None, ws=None):
+def qgemm_bwd_dx(q_g, s_g, q_wt, tune=None, out=None, ws=None, out_dtype=torch.float32):
+    """dx = dequant(q_g q_wt^T); out_dtype as qgemm_fwd."""
     _dev(q_g, "q_g"); _dev(q_wt, "q_wt")
     M, N = q_g.shape
     K = q_wt.shape[0]
     if q_wt.shape[1] != N:
         raise BrqError("q_wt: contraction length differs from q_g")
-    dx = _out(out, (M, K), torch.float32, "dx") if out is not None else \
-        torch.empty((M, K), dtype=torch.float32, device=q_g.device)
+    dx = _out(out, (M, K), out_dtype, "dx") if out is not None else \
+        torch.empty((M, K), dtype=out_dtype, device=q_g.device)
     need = workspace_size(OP_QGEMM, M, K, N, tune=tune)
     w = _ws(need, q_g.device, ws) if need else None
-    _check(lib().brq_qgemm_bwd_dx(_ptr(q_g), _ptr(s_g), _ptr(q_wt), M, N, K, _ptr(dx), _ptr(w),
-                                  0 if w is None else w.numel(), _tune(tune), _stream()),
-           "qgemm_bwd_dx")
+    if out_dtype == torch.float32:
+        st = lib().brq_qgemm_bwd_dx(_ptr(q_g), _ptr(s_g), _ptr(q_wt), M, N, K, _ptr(dx), _ptr(w),
+                                    0 if w is None else w.numel(), _tune(tune), _stream())
+    else:
+        st = lib().brq_qgemm_bwd_dx_ex(_ptr(q_g), _ptr(s_g), _ptr(q_wt), M, N, K, _ptr(dx),
+                                       _fp_code(dx), _ptr(w), 0 if w is None else w.numel(),
+                                       _tune(tune), _stream())
+    _check(st, "qgemm_bwd_dx")
     return dx
 
 

@@ -164,6 +164,24 @@ int brq_qgemm_bwd_dx(const int8_t* q_g, const float* s_g, const int8_t* q_wt, in
   return gemm_common(q_g, q_wt, M, K, N, dx, epi, ws, ws_bytes, tune, stream);
 }
 
+int brq_qgemm_fwd_ex(const int8_t* q_x, const float* s_x, const int8_t* q_w, const float* s_w,
+                     int w_per_row, int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                     void* ws, size_t ws_bytes, const brq_tune* tune, void* stream) {
+  if (!s_x || !s_w) return BRQ_E_NULL;
+  if (!fp_dtype(y_dtype)) return BRQ_E_DTYPE;
+  EpiArgs epi{EPI_FWD, s_x, s_w, nullptr, w_per_row ? 1 : 0, 1.0f, y_dtype == BRQ_BF16};
+  return gemm_common(q_x, q_w, M, N, K, (float*)y, epi, ws, ws_bytes, tune, stream);
+}
+
+int brq_qgemm_bwd_dx_ex(const int8_t* q_g, const float* s_g, const int8_t* q_wt, int64_t M,
+                        int64_t N, int64_t K, void* dx, int dx_dtype, void* ws, size_t ws_bytes,
+                        const brq_tune* tune, void* stream) {
+  if (!s_g) return BRQ_E_NULL;
+  if (!fp_dtype(dx_dtype)) return BRQ_E_DTYPE;
+  EpiArgs epi{EPI_SCALAR, s_g, nullptr, nullptr, 0, 1.0f, dx_dtype == BRQ_BF16};
+  return gemm_common(q_g, q_wt, M, K, N, (float*)dx, epi, ws, ws_bytes, tune, stream);
+}
+
 int brq_qgemm_dw(const int8_t* q_vt, const int8_t* q_ut, const float* s_x, const float* s_u,
                  const float* s_v, int64_t M, int64_t N, int64_t K, int block, float* dw,
                  void* ws, size_t ws_bytes, const brq_tune* tune, void* stream) {

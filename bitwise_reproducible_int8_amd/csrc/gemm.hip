@@ -24,6 +24,7 @@ struct Epi {
   const float* s2;
   int per_row;
   float inv_b;
+  int out_bf16;  // outputs rounded to bf16 (nearest even) instead of fp32
   // Column scale c_j, computed in the order the definitions give.
   __device__ __forceinline__ float scale(int64_t j) const {
     if (kind == EPI_FWD) return fmul(flush(s0[0]), flush(per_row ? s1[j] : s1[0]));
@@ -33,6 +34,12 @@ struct Epi {
 };
 
 __device__ __forceinline__ float dequant(int acc, float c) { return fmul((float)acc, c); }
+
+// One output element: the fp32 value, or its bf16 rounding.
+__device__ __forceinline__ void put_out(float* C, int64_t idx, float v, bool bf16) {
+  if (bf16) reinterpret_cast<uint16_t*>(C)[idx] = (uint16_t)f32_to_bf16(v);
+  else C[idx] = v;
+}
 
 // XCD-aware tile order.  Work-group p runs on XCD p % 8 (round-robin
 // dispatch), so when the tile count is a multiple of 8 the linear index is
@@ -74,7 +81,7 @@ __global__ __launch_bounds__(256) void k_gemm_ref(const int8_t* __restrict__ A,
     acc = __builtin_amdgcn_sdot4((int)x.z, (int)y.z, acc, false);
     acc = __builtin_amdgcn_sdot4((int)x.w, (int)y.w, acc, false);
   }
-  C[i * J + j] = dequant(acc, epi.scale(j));
+  put_out(C, i * J + j, dequant(acc, epi.scale(j)), epi.out_bf16);
 }
 
 // --------------------------------------------------------------------------
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
         const int64_t row = row0 + wm * WM + i * 16 + 4 * (lane >> 4) + r;
         if (row >= I) continue;
         if (Cpart) Cpart[((int64_t)blockIdx.z * I + row) * J + col] = acc[i][j][r];
-        else C[row * J + col] = dequant(acc[i][j][r], c);
+        else put_out(C, row * J + col, dequant(acc[i][j][r], c), epi.out_bf16);
       }
     }
   }
@@ -277,7 +284,7 @@ __device__ __forceinline__ v4i quad_transpose(v4i v, int q) {
 }
 
 // Epilogue of one output tile, staged through LDS so that every global
-// store instruction writes whole rows: one wave's 16-byte-per-lane store
+// store instruction writes whole rows (bf16 outputs: half rows of 512 bytes): one wave's 16-byte-per-lane store
 // covers BN * 4 / 1024 rows of 1 KiB contiguous (one row for BN = 256).
 // Straight from the MFMA layout (one column, four rows per lane) a store
 // instruction would touch 16 rows 64 bytes each, and the output write runs
@@ -295,13 +302,13 @@ __device__ __forceinline__ void store_tile(const v4i (&acc)[BM / WGM / 16][BN / 
                                            int64_t row0, int64_t col0, int wave, int lane,
                                            int64_t I, int64_t J, float* __restrict__ C,
                                            int* __restrict__ Cpart, int64_t z,
-                                           const Scale& scale, int8_t* stage) {
+                                           const Scale& scale, int8_t* stage, bool obf16) {
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TI = WM / 16, TJ = WN / 16;
   constexpr int CPR = BN / 4;                 // 16-byte chunks per staged row
   constexpr int GROUP = 16 * BN * 4;          // bytes per row group
   constexpr int RCH = 16 * CPR / (WGN * 64);  // chunks each lane stores per block
-  static_assert(CPR >= 8 && RCH * WGN * 64 == 16 * CPR, "staging layout");
+  static_assert(CPR >= 8 && RCH * WGN * 64 == 16 * CPR && RCH % 2 == 0, "staging layout");
   const int wm = wave / WGN, wn = wave % WGN;
   int8_t* grp = stage + wm * GROUP;
   const int rq = 4 * (lane >> 4);  // first of the lane's 4 rows in a block
@@ -327,6 +334,40 @@ __device__ __forceinline__ void store_tile(const v4i (&acc)[BM / WGM / 16][BN / 
       }
     }
     __syncthreads();
+    if (obf16 && !Cpart) {
+      // bf16: each lane takes two adjacent chunks (8 columns) and stores 16
+      // bytes, so a store instruction still writes whole 512-byte rows
+#pragma unroll
+      for (int k = 0; k < RCH / 2; ++k) {
+        const int pr = (k * WGN + wn) * 64 + lane;  // chunk pair of the group
+        const int r = pr / (CPR / 2), c8 = pr % (CPR / 2);
+        const v4i a = *reinterpret_cast<const v4i*>(grp + (r * CPR + ((2 * c8) ^ (r & 7))) * 16);
+        const v4i b =
+            *reinterpret_cast<const v4i*>(grp + (r * CPR + ((2 * c8 + 1) ^ (r & 7))) * 16);
+        const int64_t row = row0 + wm * WM + i * 16 + r;
+        const int64_t col = col0 + c8 * 8;
+        if (row >= I || col >= J) continue;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(C) + row * J + col;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          w[e] = f32_to_bf16(__int_as_float(a[2 * e])) |
+                 (f32_to_bf16(__int_as_float(a[2 * e + 1])) << 16);
+          w[2 + e] = f32_to_bf16(__int_as_float(b[2 * e])) |
+                     (f32_to_bf16(__int_as_float(b[2 * e + 1])) << 16);
+        }
+        if (col + 8 <= J && (J & 7) == 0) {
+          __builtin_nontemporal_store(v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
+                                      reinterpret_cast<v4i*>(dst));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < J) dst[e] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        }
+      }
+      __syncthreads();
+      continue;
+    }
 #pragma unroll
     for (int k = 0; k < RCH; ++k) {
       const int ch = (k * WGN + wn) * 64 + lane;  // chunk of the group
@@ -483,7 +524,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
   // frees the stages for the epilogue
   __syncthreads();
   store_tile<BM, BN, WGM, WGN>(acc, row0, col0, wave, lane, I, J, C, Cpart, blockIdx.z,
-                               [&](int64_t j) { return epi.scale(j); }, smem);
+                               [&](int64_t j) { return epi.scale(j); }, smem, epi.out_bf16);
 }
 
 // --------------------------------------------------------------------------
@@ -709,7 +750,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_stream(
                                  [&](int64_t j) {
                                    return col_scales ? fmul(c_uni, flush(cu[j - w.col0])) : c_uni;
                                  },
-                                 smem + last * STAGE);
+                                 smem + last * STAGE, epi.out_bf16);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -726,7 +767,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const int* __restrict__ C
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
     int acc = 0;
     for (int z = 0; z < splits; ++z) acc += Cpart[z * n + e];
-    C[e] = dequant(acc, epi.scale(e % J));
+    put_out(C, e, dequant(acc, epi.scale(e % J)), epi.out_bf16);
   }
 }
 
@@ -833,7 +874,7 @@ static hipError_t launch_stream(const int8_t* A, const int8_t* B, int64_t I, int
 hipError_t gemm_i8(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64_t Kc, float* C,
                    const EpiArgs& ea, void* ws, size_t ws_bytes, const brq_tune* t,
                    hipStream_t s) {
-  Epi epi{ea.kind, ea.s0, ea.s1, ea.s2, ea.per_row, ea.inv_b};
+  Epi epi{ea.kind, ea.s0, ea.s1, ea.s2, ea.per_row, ea.inv_b, ea.out_bf16};
   if (I == 0 || J == 0) return hipSuccess;
   // tile indices are unsigned 32-bit: at most 2^31 work units of the
   // smallest tile (128 x 128) times the largest split

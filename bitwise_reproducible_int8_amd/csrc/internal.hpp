@@ -71,6 +71,7 @@ struct EpiArgs {
   const float* s2;   // dw: s_v
   int per_row;       // fwd: s_w is per output column
   float inv_b;       // dw: exact 2^-log2(block)
+  int out_bf16 = 0;  // C holds bf16 (round to nearest even) instead of fp32
 };
 size_t gemm_ws(int64_t I, int64_t J, int64_t Kc, const brq_tune* t);
 // C[i][j] = epi(sum_k A[i][k] * B[j][k]); A [I][Kc], B [J][Kc], C [I][J].

@@ -147,6 +147,20 @@ int brq_qgemm_bwd_dx(const int8_t* q_g, const float* s_g, const int8_t* q_wt,
                      int64_t M, int64_t N, int64_t K, float* dx, void* ws,
                      size_t ws_bytes, const struct brq_tune* tune, void* stream);
 
+/* Output-dtype variants of the two GEMMs above (a §8(f) variant: bf16
+ * outputs, the dtype the next layer's input and the activation gradient
+ * take).  y_dtype / dx_dtype: BRQ_F32 (identical to the calls above) or
+ * BRQ_BF16, where each output is the fp32 value of the definition rounded
+ * once to bf16 (nearest even).  y / dx must be 16-byte aligned. */
+int brq_qgemm_fwd_ex(const int8_t* q_x, const float* s_x, const int8_t* q_w,
+                     const float* s_w, int w_per_row, int64_t M, int64_t N, int64_t K,
+                     void* y, int y_dtype, void* ws, size_t ws_bytes,
+                     const struct brq_tune* tune, void* stream);
+int brq_qgemm_bwd_dx_ex(const int8_t* q_g, const float* s_g, const int8_t* q_wt,
+                        int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype,
+                        void* ws, size_t ws_bytes, const struct brq_tune* tune,
+                        void* stream);
+
 /* ---------------------------------------------------------------------
  * qgemm_bwd_dw_wht -- weight-gradient GEMM in int8 after a Walsh-Hadamard
  * rotation along tokens (§3.2 "int8 computation").  With H_b the

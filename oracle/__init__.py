@@ -38,6 +38,8 @@ def lib():
         L.orc_bf16_to_f32.argtypes = [C.c_uint16]
         L.orc_f32_to_bf16.restype = C.c_uint16
         L.orc_f32_to_bf16.argtypes = [f32]
+        L.orc_f32_to_bf16_array.restype = None
+        L.orc_f32_to_bf16_array.argtypes = [vp, i64, vp]
         L.orc_lsq_k2.restype = f32
         L.orc_lsq_k2.argtypes = []
         L.orc_tree_sum.restype = f32
@@ -119,6 +121,15 @@ def bf16_to_f32(h: int) -> float:
 
 def f32_to_bf16(f: float) -> int:
     return lib().orc_f32_to_bf16(f)
+
+
+def to_bf16(a):
+    """fp32 array -> bf16 bit patterns (uint16), nearest even (the bf16
+    output variant of the GEMMs)."""
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib().orc_f32_to_bf16_array(_p(a), a.size, _p(out))
+    return out
 
 
 def lsq_k2() -> float:

@@ -60,6 +60,12 @@ uint16_t orc_f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+/* bf16 rounding of a whole fp32 tensor (the bf16-output variant of the
+ * GEMMs: each fp32 result rounded once, nearest even). */
+void orc_f32_to_bf16_array(const float* in, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; i++) out[i] = orc_f32_to_bf16(in[i]);
+}
+
 /* Element i of a tensor of dtype F32 or BF16, after DAZ. */
 static float load(const void* p, int dtype, int64_t i) {
   if (dtype == ORC_BF16) return orc_bf16_to_f32(((const uint16_t*)p)[i]);

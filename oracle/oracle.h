@@ -71,6 +71,7 @@ float orc_flush(float v);                 /* subnormal -> signed zero */
 float orc_bf16_to_f32(uint16_t h);        /* exact widen, then DAZ */
 uint16_t orc_f32_to_bf16(float f);        /* RNE on the bit pattern */
 float orc_lsq_k2(void);                   /* 2 * fl(1/fl(sqrt(127))) */
+void orc_f32_to_bf16_array(const float* in, int64_t n, uint16_t* out);
 
 /* Canonical pairwise tree over leaves[0..n): node(j+1,i) = node(j,2i) +
  * node(j,2i+1) when the right child exists, else node(j,2i).  Two codings. */

@@ -197,6 +197,44 @@ def test_qgemm_persistent_many_tiles(M, N, K, split):
                    f"dx rows {t}")
 
 
+BF16_TUNES = [dict(gemm_kernel=k, split_k=s) for k, s in
+              [(0, 0), (1, 1), (2, 1), (2, 4), (7, 1), (10, 1), (10, 4), (12, 1), (13, 1), (13, 2)]]
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 300, 2048), (333, 515, 1152), (1024, 2048, 128),
+                                   (256, 512, 256), (1, 1, 64)])
+def test_qgemm_bf16_outputs(M, N, K):
+    """bf16-output variant: each output is the fp32 result rounded once."""
+    say("qgemm bf16 outputs", M, N, K)
+    rng = np.random.default_rng(M + 3 * N + K)
+    qx, qw = codes(rng, (M, K)), codes(rng, (N, K))
+    sx = np.array([0.0173], np.float32)
+    sw = (np.abs(rng.standard_normal(N)) * 1e-3 + 1e-4).astype(np.float32)
+    sg = np.array([3.1e-5], np.float32)
+    want_y = orc.to_bf16(orc.qgemm_fwd(qx, sx, qw, sw))
+    want_dx = orc.to_bf16(orc.qgemm_bwd_dx(qx, sg, np.ascontiguousarray(qw.T)))
+    dqx, dqw, dsx, dsw, dsg = to_dev(qx), to_dev(qw), to_dev(sx), to_dev(sw), to_dev(sg)
+    for t in BF16_TUNES:
+        assert_bitwise(brq.qgemm_fwd(dqx, dsx, dqw, dsw, tune=t, out_dtype=torch.bfloat16),
+                       want_y, f"y bf16 {t}")
+        assert_bitwise(brq.qgemm_bwd_dx(dqx, dsg, dqw, tune=t, out_dtype=torch.bfloat16),
+                       want_dx, f"dx bf16 {t}")
+
+
+def test_qgemm_bf16_outputs_many_tiles():
+    M, N, K = 8200, 4001, 1088
+    say("qgemm bf16 outputs many tiles", M, N, K)
+    rng = np.random.default_rng(5)
+    qx, qw = codes(rng, (M, K)), codes(rng, (N, K))
+    sx = np.array([0.0173], np.float32)
+    sw = (np.abs(rng.standard_normal(N)) * 1e-3 + 1e-4).astype(np.float32)
+    rows = sorted(set([0, M - 1] + [r for b in range(256, M, 256) for r in (b - 1, b)]))
+    for t in (dict(gemm_kernel=13, split_k=1), dict(gemm_kernel=10, split_k=1), None):
+        y = to_np(brq.qgemm_fwd(to_dev(qx), to_dev(sx), to_dev(qw), to_dev(sw), tune=t,
+                                out_dtype=torch.bfloat16))
+        assert_bitwise(y[rows], orc.to_bf16(orc.qgemm_fwd(qx[rows], sx, qw, sw)), f"y rows {t}")
+
+
 def test_gemm_extreme_accumulator():
     """All-127 codes at the int32 bound of the contraction."""
     say("gemm_extreme")

@@ -836,3 +836,19 @@ def test_adamw_zero_gradient_and_skip_are_identities(orc):
     # decay alone (zero gradient and moments) shrinks every weight toward 0
     p3, _, _ = orc.adamw_step(p, z, z, z, 0.1, bc1, bc2, wd=0.5)
     assert np.all(np.abs(p3) <= np.abs(p)) and np.all(np.sign(p3) * np.sign(p) >= 0)
+
+
+def test_bf16_array_rounding_matches_torch(orc):
+    """The GEMMs' bf16-output variant rounds each fp32 result once to
+    nearest even: the oracle's array rounding equals torch's independent
+    float32 -> bfloat16 conversion, ties and extremes included."""
+    import torch
+    rng = np.random.default_rng(21)
+    a = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 20000).astype(np.float32),
+        np.array([1.00390625, 1.01171875, -1.00390625, 3.4e38, -3.4e38, 0.0, -0.0, 1e-38, 6e-39], np.float32),
+    ]).astype(np.float32)
+    want = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = orc.to_bf16(a)
+    finite = np.isfinite(a)
+    assert np.array_equal(got[finite], want[finite])
