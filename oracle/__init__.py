@@ -52,6 +52,10 @@ def lib():
         L.orc_quant1.argtypes = [f32, f32]
         L.orc_quantize_lsq.restype = i32
         L.orc_quantize_lsq.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
+        L.orc_quantize_lsq_exact.restype = i32
+        L.orc_quantize_lsq_exact.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
+        L.orc_exact_abs_sum.restype = f32
+        L.orc_exact_abs_sum.argtypes = [vp, i64]
         L.orc_qgemm_fwd.restype = None
         L.orc_qgemm_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp]
         L.orc_qgemm_bwd_dx.restype = None
@@ -153,8 +157,16 @@ def quant1(x: float, r: float) -> int:
     return int(lib().orc_quant1(x, r))
 
 
-def quantize_lsq(x: np.ndarray, per_row: bool = False, col_mul=None, want_t: bool = False):
-    """Returns (q, q_t or None, scale, amax, flags)."""
+def exact_abs_sum(v) -> np.float32:
+    """Sum of |v| taken exactly, rounded once to binary32 (nearest even)."""
+    a = _c(v, np.float32)
+    return np.float32(lib().orc_exact_abs_sum(_p(a), a.size))
+
+
+def quantize_lsq(x: np.ndarray, per_row: bool = False, col_mul=None, want_t: bool = False,
+                 exact: bool = False):
+    """Returns (q, q_t or None, scale, amax, flags).  exact=True takes the
+    statistic as the exact sum of |v| rounded once instead of the tree."""
     x = _c(x)
     rows, cols = x.shape
     q = np.empty((rows, cols), np.int8)
@@ -163,9 +175,9 @@ def quantize_lsq(x: np.ndarray, per_row: bool = False, col_mul=None, want_t: boo
     scale = np.empty(ns, np.float32)
     amax = np.empty(ns, np.float32)
     cm = None if col_mul is None else _c(col_mul, np.float32)
-    flags = lib().orc_quantize_lsq(_p(x), _dtype_code(x), rows, cols,
-                                   PER_ROW if per_row else PER_TENSOR,
-                                   _p(cm), _p(q), _p(q_t), _p(scale), _p(amax))
+    f = lib().orc_quantize_lsq_exact if exact else lib().orc_quantize_lsq
+    flags = f(_p(x), _dtype_code(x), rows, cols, PER_ROW if per_row else PER_TENSOR,
+              _p(cm), _p(q), _p(q_t), _p(scale), _p(amax))
     return q, q_t, scale, amax, flags
 
 

@@ -156,18 +156,89 @@ int8_t orc_quant1(float x, float r) {
   return (int8_t)t;
 }
 
-/* One quantisation group of n values: tree of |v|, scale, codes. */
-static int lsq_group(const float* v, int64_t n, int8_t* q, float* s_out,
-                     float* amax_out) {
-  float* leaves = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
-  assert(leaves);
-  float amax = 0.0f;
-  for (int64_t i = 0; i < n; i++) {
-    leaves[i] = fabs_(v[i]);
-    if (leaves[i] > amax) amax = leaves[i];
+/* ------------------------------------------------------------------------
+ * Exact statistic (a variant of the step-size statistic): the sum of |v|
+ * taken exactly and rounded once.  §3.2 "int8 computation" reaches bitwise
+ * reproducibility for the ∇Q accumulation of attention by summing in fixed
+ * point; here the same idea is applied to Σ|v|.  Every binary32 value is a
+ * whole multiple of 2^-149, so Σ|v| is a whole number N of such units.  N
+ * is kept in an array of 32-bit words wide enough for any input (the
+ * largest finite |v| is below 2^277 units, and n < 2^40), so no addition
+ * ever rounds and the order of the additions is immaterial.  N * 2^-149 is
+ * then rounded to binary32 once, to nearest, ties to even, and flushed like
+ * any other result (§2.1 "Subnormals").  A NaN among the inputs makes the
+ * sum NaN, otherwise an infinity makes it +inf; a sum beyond the binary32
+ * range rounds to +inf.
+ * ---------------------------------------------------------------------- */
+#define EXACT_WORDS 10 /* 320 bits */
+
+/* N += m * 2^bit, m < 2^24, with the carry run to the top. */
+static void exact_add(uint32_t* w, uint32_t m, int bit) {
+  int k = bit / 32;
+  uint64_t add = (uint64_t)m << (bit % 32); /* < 2^55: spans words k, k+1 */
+  for (; add != 0 && k < EXACT_WORDS; k++) {
+    uint64_t t = (uint64_t)w[k] + (add & 0xffffffffu);
+    w[k] = (uint32_t)t;
+    add = (add >> 32) + (t >> 32);
   }
-  float S = tree_inplace(leaves, n);
-  free(leaves);
+  assert(add == 0);
+}
+
+/* Bit `i` of N. */
+static int exact_bit(const uint32_t* w, int i) { return (int)((w[i / 32] >> (i % 32)) & 1u); }
+
+float orc_exact_abs_sum(const float* v, int64_t n) {
+  uint32_t w[EXACT_WORDS];
+  memset(w, 0, sizeof w);
+  int any_nan = 0, any_inf = 0;
+  for (int64_t i = 0; i < n; i++) {
+    uint32_t u = f2u(orc_flush(v[i])) & 0x7fffffffu;
+    uint32_t e = u >> 23, frac = u & 0x7fffffu;
+    if (e == 255) {
+      if (frac) any_nan = 1; else any_inf = 1;
+      continue;
+    }
+    if (e == 0) continue; /* zero (subnormals were flushed) */
+    /* |v| = (2^23 + frac) * 2^(e-150) = (2^23 + frac) * 2^(e-1) units */
+    exact_add(w, 0x800000u | frac, (int)e - 1);
+  }
+  if (any_nan) return u2f(0x7fc00000u);
+  if (any_inf) return u2f(0x7f800000u);
+  int top = -1; /* index of the highest set bit of N */
+  for (int i = 32 * EXACT_WORDS - 1; i >= 0; i--)
+    if (exact_bit(w, i)) { top = i; break; }
+  if (top < 0) return 0.0f;
+  /* keep the 24 bits top..top-23 (fewer when N < 2^24: then exact) */
+  int lo = top - 23 < 0 ? 0 : top - 23;
+  uint32_t q = 0;
+  for (int i = top; i >= lo; i--) q = (q << 1) | (uint32_t)exact_bit(w, i);
+  if (lo > 0) {
+    int half = exact_bit(w, lo - 1), sticky = 0;
+    for (int i = lo - 2; i >= 0 && !sticky; i--) sticky = exact_bit(w, i);
+    if (half && (sticky || (q & 1u))) q++;
+    if (q == (1u << 24)) { q >>= 1; lo++; }
+  }
+  /* value = q * 2^(lo - 149); q < 2^24 so the double is exact */
+  if (lo - 149 + 23 > 127) return u2f(0x7f800000u);
+  return orc_flush((float)ldexp((double)q, lo - 149));
+}
+
+/* One quantisation group of n values: the statistic S of |v| (the
+ * canonical tree, or the exact sum above), scale, codes. */
+static int lsq_group(const float* v, int64_t n, int exact, int8_t* q,
+                     float* s_out, float* amax_out) {
+  float amax = 0.0f, S;
+  for (int64_t i = 0; i < n; i++)
+    if (fabs_(v[i]) > amax) amax = fabs_(v[i]);
+  if (exact) {
+    S = orc_exact_abs_sum(v, n);
+  } else {
+    float* leaves = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    assert(leaves);
+    for (int64_t i = 0; i < n; i++) leaves[i] = fabs_(v[i]);
+    S = tree_inplace(leaves, n);
+    free(leaves);
+  }
   float s, r;
   orc_lsq_scale(S, n, &s, &r);
   for (int64_t i = 0; i < n; i++) q[i] = orc_quant1(v[i], r);
@@ -176,9 +247,9 @@ static int lsq_group(const float* v, int64_t n, int8_t* q, float* s_out,
   return isfinite(S) ? 0 : ORC_FLAG_NONFINITE;
 }
 
-int orc_quantize_lsq(const void* x, int dtype, int64_t rows, int64_t cols,
-                     int gran, const float* col_mul, int8_t* q, int8_t* q_t,
-                     float* scale, float* amax) {
+static int quantize_common(const void* x, int dtype, int64_t rows, int64_t cols,
+                           int gran, const float* col_mul, int exact, int8_t* q,
+                           int8_t* q_t, float* scale, float* amax) {
   int64_t n = rows * cols;
   float* v = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
   assert(v);
@@ -189,10 +260,10 @@ int orc_quantize_lsq(const void* x, int dtype, int64_t rows, int64_t cols,
   }
   int flags = 0;
   if (gran == ORC_PER_TENSOR) {
-    flags |= lsq_group(v, n, q, &scale[0], amax ? &amax[0] : NULL);
+    flags |= lsq_group(v, n, exact, q, &scale[0], amax ? &amax[0] : NULL);
   } else {
     for (int64_t r = 0; r < rows; r++)
-      flags |= lsq_group(v + r * cols, cols, q + r * cols, &scale[r],
+      flags |= lsq_group(v + r * cols, cols, exact, q + r * cols, &scale[r],
                          amax ? &amax[r] : NULL);
   }
   if (q_t)
@@ -200,6 +271,18 @@ int orc_quantize_lsq(const void* x, int dtype, int64_t rows, int64_t cols,
       for (int64_t c = 0; c < cols; c++) q_t[c * rows + r] = q[r * cols + c];
   free(v);
   return flags;
+}
+
+int orc_quantize_lsq(const void* x, int dtype, int64_t rows, int64_t cols,
+                     int gran, const float* col_mul, int8_t* q, int8_t* q_t,
+                     float* scale, float* amax) {
+  return quantize_common(x, dtype, rows, cols, gran, col_mul, 0, q, q_t, scale, amax);
+}
+
+int orc_quantize_lsq_exact(const void* x, int dtype, int64_t rows, int64_t cols,
+                           int gran, const float* col_mul, int8_t* q, int8_t* q_t,
+                           float* scale, float* amax) {
+  return quantize_common(x, dtype, rows, cols, gran, col_mul, 1, q, q_t, scale, amax);
 }
 
 /* ------------------------------------------------------------------------
@@ -319,7 +402,7 @@ int orc_wht_fp_quant(const void* dy, int dtype, int64_t M, int64_t N, int b,
     }
   }
   float amax;
-  int flags = lsq_group(v, n, q_v, s_v, &amax);
+  int flags = lsq_group(v, n, 0, q_v, s_v, &amax);
   if (v_out) memcpy(v_out, v, (size_t)n * sizeof(float));
   free(v);
   return flags;

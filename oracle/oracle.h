@@ -92,6 +92,16 @@ int orc_quantize_lsq(const void* x, int dtype, int64_t rows, int64_t cols,
                      int gran, const float* col_mul, int8_t* q, int8_t* q_t,
                      float* scale, float* amax);
 
+/* The same with the statistic S the exact sum of |v| rounded once to
+ * binary32 (nearest even, subnormal results flushed) in place of the tree. */
+int orc_quantize_lsq_exact(const void* x, int dtype, int64_t rows, int64_t cols,
+                           int gran, const float* col_mul, int8_t* q, int8_t* q_t,
+                           float* scale, float* amax);
+/* Exact sum of |v[i]| (each v[i] flushed first) rounded once to binary32;
+ * NaN if any v[i] is NaN, else +inf if any is infinite or the sum is out of
+ * range. */
+float orc_exact_abs_sum(const float* v, int64_t n);
+
 /* qgemm_fwd: y[m][n] = fl(fl(sum_k qx[m][k]*qw[n][k]) * fl(s_x*s_w[n]))
  * (s_w[0] for every n when w_per_row == 0). */
 void orc_qgemm_fwd(const int8_t* qx, const float* s_x, const int8_t* qw,

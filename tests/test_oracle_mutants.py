@@ -49,6 +49,18 @@ MUTANTS = {
     "adamw_bias_power_of_beta2": ("    p1 = fmul(p1, beta1);", "    p1 = fmul(p1, beta2);"),
     "spike_skips_four": ("if (!finite || norm > spike_threshold) *skip_state = skip_steps;",
                          "if (!finite || norm > spike_threshold) *skip_state = skip_steps - 1;"),
+    "exact_truncates": ("if (half && (sticky || (q & 1u))) q++;", "if (0) q++;"),
+    "exact_ties_away": ("if (half && (sticky || (q & 1u))) q++;", "if (half) q++;"),
+    "exact_no_sticky": ("for (int i = lo - 2; i >= 0 && !sticky; i--) sticky = exact_bit(w, i);",
+                        "(void)0;"),
+    "exact_drops_carry": ("add = (add >> 32) + (t >> 32);", "add = (add >> 32);"),
+    "exact_unit_off_by_one": ("return orc_flush((float)ldexp((double)q, lo - 149));",
+                              "return orc_flush((float)ldexp((double)q, lo - 150));"),
+    "exact_inf_before_nan": ("if (any_nan) return u2f(0x7fc00000u);", "if (any_nan) return u2f(0x7f800000u);"),
+    "exact_keeps_subnormals": ("uint32_t u = f2u(orc_flush(v[i])) & 0x7fffffffu;",
+                               "uint32_t u = f2u(v[i]) & 0x7fffffffu; if (u && u < 0x800000u) "
+                               "{ exact_add(w, u, 0); continue; }"),
+    "exact_uses_tree": ("    S = orc_exact_abs_sum(v, n);", "    S = orc_tree_sum(v, n);"),
     "clip_always_scales": ("*clip = norm > max_norm ? fdiv(orc_flush(max_norm), norm) : 1.0f;",
                            "*clip = fdiv(orc_flush(max_norm), norm);"),
 }

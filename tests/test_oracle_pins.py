@@ -852,3 +852,121 @@ def test_bf16_array_rounding_matches_torch(orc):
     got = orc.to_bf16(a)
     finite = np.isfinite(a)
     assert np.array_equal(got[finite], want[finite])
+
+
+# --------------------------------------------------------------------------
+# exact statistic: the sum of |v| without rounding, then one rounding
+# --------------------------------------------------------------------------
+def _exact_abs_sum_ref(v):
+    """Exact rational sum of |v| (each v flushed first), one binary32
+    rounding by tests/_exact.py, +inf past the binary32 range."""
+    v = np.asarray(v, np.float32).ravel()
+    if np.isnan(v).any():
+        return float("nan")
+    if np.isinf(v).any():
+        return float("inf")
+    tot = sum((Fraction(abs(float(x))) for x in v if abs(float(x)) >= 2.0 ** -126), Fraction(0))
+    r = X.op(tot)
+    return float("inf") if r >= Fraction(2) ** 128 else float(r)
+
+
+def _same(a, b):
+    a, b = float(a), float(b)
+    return (math.isnan(a) and math.isnan(b)) or bits(a) == bits(b)
+
+
+def test_exact_abs_sum_directed(orc):
+    """Ties to even, the sticky bit, carries, the range ends, specials."""
+    big = float(np.finfo(np.float32).max)
+    cases = [
+        ([], 0.0),
+        ([-3.0, 5.0], 8.0),
+        ([2.0 ** 24, 1.0], 2.0 ** 24),                      # tie, even kept
+        ([2.0 ** 24 + 2, 1.0], 2.0 ** 24 + 4),              # tie, odd rounds up
+        ([2.0 ** 24, 1.0, 2.0 ** -20], 2.0 ** 24 + 2),      # just above the tie
+        ([2.0 ** 24, 1.0, 2.0], 2.0 ** 24 + 4),
+        ([1.0, 2.0 ** -24, 2.0 ** -24], 1.0 + 2.0 ** -23),  # a tree gives 1.0
+        ([1.0] + [2.0 ** -30] * 1024, 1.0 + 2.0 ** -20),
+        ([2.0 ** -126 * (1 + 2.0 ** -23), 2.0 ** -126], 2.0 ** -125),  # tie at the bottom
+        ([2.0 ** -126], 2.0 ** -126),
+        ([X.bits_to_float(0x00000007), 1.0], 1.0),          # subnormal input reads as 0
+        ([X.bits_to_float(0x007FFFFF)], 0.0),
+        ([X.bits_to_float(0x007FFFFF)] * 2, 0.0),           # would sum to a normal
+        ([2.0 ** -126, X.bits_to_float(0x00400000)], 2.0 ** -126),
+        ([big, big], float("inf")),
+        ([big, 2.0 ** 103], float("inf")),                  # tie above FLT_MAX goes up
+        ([big, 2.0 ** 102], big),
+        ([float("inf"), 1.0], float("inf")),
+        ([-float("inf")], float("inf")),
+        ([float("nan"), float("inf")], float("nan")),
+    ]
+    for v, want in cases:
+        got = orc.exact_abs_sum(np.array(v, np.float32))
+        assert _same(got, want), (v, got, want)
+        assert _same(_exact_abs_sum_ref(v), want), v
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_exact_abs_sum_random_vs_rationals(orc, seed):
+    """Values whose exponents span the whole binary32 range (the sum of any
+    such set needs far more than 64 bits), random lengths, random signs."""
+    rng = np.random.default_rng(1000 + seed)
+    for trial in range(40):
+        n = int(rng.integers(1, 400))
+        lo, hi = sorted(rng.integers(1, 255, size=2))
+        e = rng.integers(lo, hi + 1, size=n).astype(np.uint32)
+        u = (e << 23) | rng.integers(0, 1 << 23, size=n).astype(np.uint32)
+        u |= (rng.integers(0, 2, size=n).astype(np.uint32) << 31)
+        v = u.view(np.float32)
+        got = orc.exact_abs_sum(v)
+        assert _same(got, _exact_abs_sum_ref(v)), (seed, trial)
+        # order-free: any permutation gives the same bits
+        assert _same(orc.exact_abs_sum(v[rng.permutation(n)]), got)
+
+
+def test_exact_abs_sum_gaussian_and_ties(orc, syn):
+    """Layer-like data (N(0,1) bf16 activations), and sums built to land on
+    exact ties of the final rounding."""
+    x = syn.normal((8, 1024), 1.0, tag=95, bf16=True)
+    v = (x.astype(np.uint32) << 16).view(np.float32)
+    assert _same(orc.exact_abs_sum(v), _exact_abs_sum_ref(v))
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        a = np.float32(rng.uniform(1.0, 2.0)) * np.float32(2.0 ** int(rng.integers(-40, 40)))
+        ulp = float(np.spacing(a))
+        for k in (0.5, 1.5, 0.25, 0.75):
+            v = np.array([a, k * ulp], np.float32)
+            assert _same(orc.exact_abs_sum(v), _exact_abs_sum_ref(v))
+
+
+def test_lsq_exact_statistic_scale_and_codes(orc, syn):
+    """The exact variant differs from the tree only in S: its step size is
+    lsq_scale(exact S) and its codes the reciprocal-multiply codes of that
+    step; per-row groups each take their own exact S; col_mul multiplies
+    first."""
+    x = syn.normal((64, 256), 1.0, tag=96)
+    q, _, s, amax, fl = orc.quantize_lsq(x, exact=True)
+    S = _exact_abs_sum_ref(x)
+    assert fl == 0 and amax[0] == np.abs(x).max()
+    s_want, r_want = orc.lsq_scale(S, x.size)
+    assert bits(s[0]) == bits(s_want)
+    exact = 2 * np.abs(x.astype(np.float64)).mean() / math.sqrt(127)
+    assert abs(float(s[0]) - exact) <= 4 * np.spacing(np.float32(exact))
+    prod = (x.astype(np.float64) * np.float64(r_want)).astype(np.float32)
+    want = np.clip(np.rint(prod.astype(np.float64)), -127, 127).astype(np.int8)
+    assert np.array_equal(q, want)
+    w = syn.normal((16, 256), 0.02, tag=97)
+    q, qt, s, amax, _ = orc.quantize_lsq(w, per_row=True, want_t=True, exact=True)
+    assert np.array_equal(qt, q.T)
+    for r in range(16):
+        assert bits(s[r]) == bits(orc.lsq_scale(_exact_abs_sum_ref(w[r]), 256)[0])
+    cm = syn.normal((256,), 0.01, mean=0.02, tag=98)
+    a = orc.quantize_lsq(x, col_mul=cm, exact=True)
+    prod = (x.astype(np.float64) * cm.astype(np.float64)[None, :]).astype(np.float32)
+    b = orc.quantize_lsq(prod, exact=True)
+    assert np.array_equal(a[0], b[0]) and a[2][0] == b[2][0]
+    z = np.zeros((4, 64), np.float32)
+    q, _, s, amax, fl = orc.quantize_lsq(z, exact=True)
+    assert s[0] == 0 and not q.any() and fl == 0
+    z[1, 3] = np.inf
+    assert orc.quantize_lsq(z, exact=True)[4] == orc.FLAG_NONFINITE
