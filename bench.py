@@ -379,6 +379,38 @@ def main():
         "note": "the 14 forward and input-gradient GEMMs with bf16 outputs; not part of value"}}
     del yb, xb
 
+    # Variant (not part of value): the step's 4 activation and 7 weight
+    # quantisations with the exact statistic (sum |v| without rounding, then
+    # one rounding), into buffers of their own.
+    xq = {k: (torch.empty_like(step.q_x[k]), torch.empty(1, device=dev), torch.empty(1, device=dev))
+          for k in step.x}
+    wq = [(torch.empty_like(step.q_w[i]), torch.empty_like(step.q_wt[i]),
+           torch.empty_like(step.s_w[i]), torch.empty_like(step.amax_w[i]))
+          for i in range(len(syn.LAYER_LINEARS))]
+    xws = torch.empty(max(brq.workspace_size(brq.OP_QUANTIZE_EXACT, *t.shape) for t in step.x.values()),
+                      dtype=torch.uint8, device=dev)
+
+    def exact_quant():
+        for k, t in step.x.items():
+            brq.quantize_lsq(t, ws=xws, exact=True, out=(xq[k][0], None, xq[k][1], xq[k][2]))
+        for i, w_i in enumerate(step.w):
+            brq.quantize_lsq(w_i, per_row=True, want_t=True, exact=True, out=wq[i])
+    for _ in range(args.warmup):
+        exact_quant()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        exact_quant()
+    e1.record()
+    torch.cuda.synchronize()
+    variants["quantize_exact_statistic"] = {
+        "ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4),
+        "tree_ms_per_step": (round(kernels["quant_x"]["ms_per_step"] +
+                                   kernels["quant_w"]["ms_per_step"], 4) if kernels else None),
+        "note": "the 4 activation and 7 weight quantisations with the exact statistic; not part of "
+                "value"}
+    del xq, wq, xws
+
     cpu = None
     if args.cpu_tokens > 0:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")

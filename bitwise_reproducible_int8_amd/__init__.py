@@ -20,10 +20,11 @@ F32, BF16, I8, I32, U8 = 0, 1, 2, 3, 4
 PER_TENSOR, PER_ROW = 0, 1
 FLAG_NONFINITE = 1
 OP_QUANTIZE, OP_QGEMM, OP_DW_WHT, OP_RMSNORM_BWD, OP_GRAD_NORM, OP_DY_BWD = 1, 2, 3, 4, 5, 6
+OP_QUANTIZE_EXACT = 7
 MAX_CONTRACTION = 133144
 
 SYMBOLS = [
-    "brq_workspace_size", "brq_quantize_lsq", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
+    "brq_workspace_size", "brq_quantize_lsq", "brq_quantize_lsq_exact", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
     "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
     "brq_qgemm_fwd_ex", "brq_qgemm_bwd_dx_ex",
     "brq_quantize_dy_bwd",
@@ -76,6 +77,8 @@ def lib():
         L.brq_workspace_size.argtypes = [i32, i64, i64, i64, i32, vp]
         L.brq_quantize_lsq.restype = i32
         L.brq_quantize_lsq.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.brq_quantize_lsq_exact.restype = i32
+        L.brq_quantize_lsq_exact.argtypes = L.brq_quantize_lsq.argtypes
         L.brq_qgemm_fwd.restype = i32
         L.brq_qgemm_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, sz, vp, vp]
         L.brq_qgemm_bwd_dx.restype = i32
@@ -217,10 +220,11 @@ def _ws(nbytes, device, ws):
 # entry points
 # ---------------------------------------------------------------------------
 def quantize_lsq(x, per_row=False, col_mul=None, want_t=False, tune=None, ws=None, flags=None,
-                 out=None):
+                 out=None, exact=False):
     """LSQ int8 quantisation.  Returns (q, q_t or None, scale, amax).
     ``out`` may hold preallocated (q, q_t, scale, amax); a None entry is
-    allocated here (q_t only when want_t)."""
+    allocated here (q_t only when want_t).  ``exact`` selects
+    brq_quantize_lsq_exact (the statistic summed exactly, rounded once)."""
     _dev(x, "x")
     rows, cols = x.shape
     ns = rows if per_row else 1
@@ -244,12 +248,13 @@ def quantize_lsq(x, per_row=False, col_mul=None, want_t=False, tune=None, ws=Non
             raise BrqError("q_t: expected int8 (cols, rows)")
     if col_mul is not None:
         _dev(col_mul, "col_mul")
-    need = workspace_size(OP_QUANTIZE, rows, cols, tune=tune)
+    need = workspace_size(OP_QUANTIZE_EXACT if exact else OP_QUANTIZE, rows, cols, tune=tune)
     w = _ws(need, x.device, ws)
-    _check(lib().brq_quantize_lsq(_ptr(x), _fp_code(x), rows, cols, PER_ROW if per_row else PER_TENSOR,
-                                  _ptr(col_mul), _ptr(q), _ptr(q_t), _ptr(scale), _ptr(amax),
-                                  _ptr(w), w.numel(), _ptr(flags), _tune(tune), _stream()),
-           "quantize_lsq")
+    fn = lib().brq_quantize_lsq_exact if exact else lib().brq_quantize_lsq
+    _check(fn(_ptr(x), _fp_code(x), rows, cols, PER_ROW if per_row else PER_TENSOR,
+              _ptr(col_mul), _ptr(q), _ptr(q_t), _ptr(scale), _ptr(amax),
+              _ptr(w), w.numel(), _ptr(flags), _tune(tune), _stream()),
+           "quantize_lsq_exact" if exact else "quantize_lsq")
     return q, q_t, scale, amax
 
 

@@ -32,6 +32,10 @@ size_t quant_ws(int64_t rows, int64_t cols, const brq_tune* t) {
   return flat_reduce_ws(rows * cols, flat_chunk_log2(t)) + kScalars;
 }
 
+size_t quant_exact_ws(int64_t rows, int64_t cols) {
+  return exact_reduce_ws(rows * cols) + kScalars;
+}
+
 size_t dw_stage_ws(int64_t M, int64_t N, int64_t K, int block, const brq_tune* t) {
   size_t a = wht_x_ws(M, K, block), b = wht_dy_ws(M, N, block, flat_chunk_log2(t));
   return a > b ? a : b;
@@ -85,6 +89,7 @@ size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block, co
   if (a < 0 || b < 0 || c < 0) return 0;
   switch (op) {
     case BRQ_OP_QUANTIZE: return quant_ws(a, b, t);
+    case BRQ_OP_QUANTIZE_EXACT: return quant_exact_ws(a, b);
     case BRQ_OP_QGEMM: return gemm_ws(a, b, c, t);
     case BRQ_OP_DW_WHT: return dw_ws(a, b, c, block > 0 ? block : 1, t);
     case BRQ_OP_RMSNORM_BWD: {
@@ -97,10 +102,14 @@ size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block, co
   }
 }
 
-int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
-                     const float* col_mul, int8_t* q, int8_t* q_t, float* scale, float* amax,
-                     void* ws, size_t ws_bytes, int32_t* dflags, const brq_tune* tune,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+int quantize_common(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                    const float* col_mul, bool exact, int8_t* q, int8_t* q_t, float* scale,
+                    float* amax, void* ws, size_t ws_bytes, int32_t* dflags,
+                    const brq_tune* tune, void* stream) {
   if (!fp_dtype(x_dtype)) return BRQ_E_DTYPE;
   if (rows < 0 || cols < 0) return BRQ_E_SHAPE;
   if (gran != BRQ_PER_TENSOR && gran != BRQ_PER_ROW) return BRQ_E_ARG;
@@ -115,16 +124,21 @@ int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols, int
     if (col_mul) return BRQ_E_UNSUPPORTED;
     if (cols > 16384 || cols == 0) return BRQ_E_UNSUPPORTED;
     if (rows == 0) return BRQ_OK;
-    if ((e = quant_rows(x, x_dtype, rows, cols, q, scale, amax, dflags, s)) != hipSuccess)
-      return hip_status(e);
+    e = exact ? quant_rows_exact(x, x_dtype, rows, cols, q, scale, amax, dflags, s)
+              : quant_rows(x, x_dtype, rows, cols, q, scale, amax, dflags, s);
+    if (e != hipSuccess) return hip_status(e);
   } else {
-    const size_t need = quant_ws(rows, cols, tune);
+    const size_t need = exact ? quant_exact_ws(rows, cols) : quant_ws(rows, cols, tune);
     if (!ws || ws_bytes < need) return BRQ_E_WORKSPACE;
     float* sc = (float*)((char*)ws + need - kScalars);  // [0]sum [1]max [2]s [3]r
-    const int leaf = col_mul ? LEAF_ABS_COLMUL : LEAF_ABS;
-    if ((e = flat_reduce(x, x_dtype, leaf, col_mul, n, cols > 0 ? cols : 1, sc, ws,
-                         flat_chunk_log2(tune), dflags, s)) != hipSuccess)
-      return hip_status(e);
+    if (exact) {
+      e = exact_reduce(x, x_dtype, col_mul, n, cols > 0 ? cols : 1, sc, ws, dflags, s);
+    } else {
+      const int leaf = col_mul ? LEAF_ABS_COLMUL : LEAF_ABS;
+      e = flat_reduce(x, x_dtype, leaf, col_mul, n, cols > 0 ? cols : 1, sc, ws,
+                      flat_chunk_log2(tune), dflags, s);
+    }
+    if (e != hipSuccess) return hip_status(e);
     // an empty group has step size 0 (no mean is taken)
     const float inv_n = n > 0 ? 1.0f / (float)n : 0.0f;
     if ((e = lsq_finalize(sc, inv_n, sc + 2, scale, amax, s)) != hipSuccess) return hip_status(e);
@@ -133,6 +147,26 @@ int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols, int
   }
   if (q_t && n > 0 && (e = transpose_i8(q, rows, cols, q_t, s)) != hipSuccess) return hip_status(e);
   return BRQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                     const float* col_mul, int8_t* q, int8_t* q_t, float* scale, float* amax,
+                     void* ws, size_t ws_bytes, int32_t* dflags, const brq_tune* tune,
+                     void* stream) {
+  return quantize_common(x, x_dtype, rows, cols, gran, col_mul, false, q, q_t, scale, amax, ws,
+                         ws_bytes, dflags, tune, stream);
+}
+
+int brq_quantize_lsq_exact(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                           const float* col_mul, int8_t* q, int8_t* q_t, float* scale,
+                           float* amax, void* ws, size_t ws_bytes, int32_t* dflags,
+                           const brq_tune* tune, void* stream) {
+  return quantize_common(x, x_dtype, rows, cols, gran, col_mul, true, q, q_t, scale, amax, ws,
+                         ws_bytes, dflags, tune, stream);
 }
 
 static int gemm_common(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64_t Kc,

@@ -58,6 +58,14 @@ hipError_t quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
                       int8_t* q, float* scale, float* amax, int32_t* dflags,
                       hipStream_t s);
 
+// Exact-sum statistic (exact.hip): per-tensor S and max |v| into out2[0..1]
+// (two launches), and the per-row quantiser with exact row statistics.
+size_t exact_reduce_ws(int64_t n);
+hipError_t exact_reduce(const void* x, int dtype, const float* col_mul, int64_t n, int64_t cols,
+                        float* out2, void* ws, int32_t* dflags, hipStream_t s);
+hipError_t quant_rows_exact(const void* x, int dtype, int64_t rows, int64_t cols, int8_t* q,
+                            float* scale, float* amax, int32_t* dflags, hipStream_t s);
+
 // int8 transpose: q [rows][cols] -> qt [cols][rows].
 hipError_t transpose_i8(const int8_t* q, int64_t rows, int64_t cols, int8_t* qt,
                         hipStream_t s);

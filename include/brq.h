@@ -93,7 +93,8 @@ enum brq_op {
   BRQ_OP_DW_WHT = 3,       /* a = M, b = N, c = K, block = Hadamard block */
   BRQ_OP_RMSNORM_BWD = 4,  /* a = T, b = D */
   BRQ_OP_GRAD_NORM = 5,    /* a = n */
-  BRQ_OP_DY_BWD = 6        /* a = M, b = N, block = Hadamard block */
+  BRQ_OP_DY_BWD = 6,       /* a = M, b = N, block = Hadamard block */
+  BRQ_OP_QUANTIZE_EXACT = 7 /* a = rows, b = cols */
 };
 size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block,
                           const struct brq_tune* tune);
@@ -119,6 +120,25 @@ int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols,
                      int gran, const float* col_mul, int8_t* q, int8_t* q_t,
                      float* scale, float* amax, void* ws, size_t ws_bytes,
                      int32_t* dflags, const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * quantize_lsq_exact -- brq_quantize_lsq with an exact statistic (a
+ * variant: the fixed-point accumulation that §3.2 "int8 computation" uses
+ * to make the attention-gradient sum reproducible, applied to S).
+ *     S = the exact real sum of |v| over the group, rounded once to
+ *         binary32 (nearest even; a subnormal result flushes to +0; NaN if
+ *         a v is NaN, else +inf if a v is infinite or the sum passes the
+ *         binary32 range)
+ * Every other step, argument, layout, shape rule and flag is as in
+ * brq_quantize_lsq; amax is the largest |v| (0 if all are zero or
+ * subnormal).  The bits depend on no launch shape, tune or add order.
+ * Workspace: BRQ_OP_QUANTIZE_EXACT (BRQ_PER_TENSOR only).
+ * --------------------------------------------------------------------- */
+int brq_quantize_lsq_exact(const void* x, int x_dtype, int64_t rows,
+                           int64_t cols, int gran, const float* col_mul,
+                           int8_t* q, int8_t* q_t, float* scale, float* amax,
+                           void* ws, size_t ws_bytes, int32_t* dflags,
+                           const struct brq_tune* tune, void* stream);
 
 /* ---------------------------------------------------------------------
  * qgemm_fwd -- forward W8A8 GEMM with int32 accumulation, then dequant
