@@ -69,6 +69,10 @@ def lib():
         L.orc_dw_gemm.restype = None
         L.orc_dw_gemm.argtypes = [vp, vp, i64, i64, i64, f32, f32, f32, i32, i64, i64, vp]
         L.orc_qgemm_bwd_dw_wht.restype = i32
+        L.orc_wht_fp_rows_quant.restype = i32
+        L.orc_wht_fp_rows_quant.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp]
+        L.orc_qgemm_bwd_dx_wht.restype = i32
+        L.orc_qgemm_bwd_dx_wht.argtypes = [vp, i32, vp, vp, i64, i64, i64, i32, vp, vp, vp]
         L.orc_qgemm_bwd_dw_wht.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp, vp]
         L.orc_rmsnorm_fwd.restype = i32
         L.orc_rmsnorm_fwd.argtypes = [vp, vp, i32, i64, i64, f32, vp, vp]
@@ -254,6 +258,35 @@ def qgemm_bwd_dw_wht(q_x, s_x, dy, b: int):
     flags = lib().orc_qgemm_bwd_dw_wht(_p(q_x), _p(s_x), _p(dy), _dtype_code(dy), M, N, K, b,
                                        _p(dw), _p(su), _p(sv))
     return dw, su[0], sv[0], flags
+
+
+def wht_fp_rows_quant(dy, b: int, s_w=None, want_v: bool = False):
+    """g = dy * s_w[n] rotated along each row in blocks of b, per-tensor
+    LSQ.  Returns (q, s, rotated values or None, flags)."""
+    dy = _c(dy)
+    M, N = dy.shape
+    q = np.empty((M, N), np.int8)
+    s = np.zeros(1, np.float32)
+    v = np.empty((M, N), np.float32) if want_v else None
+    sw = None if s_w is None else _c(s_w, np.float32)
+    flags = lib().orc_wht_fp_rows_quant(_p(dy), _dtype_code(dy), M, N, _p(sw), b, _p(q), _p(s),
+                                        _p(v))
+    return q, s[0], v, flags
+
+
+def qgemm_bwd_dx_wht(dy, s_w, q_w, b: int):
+    """Rotated input-gradient GEMM.  Returns (dx, s_g, s_h, flags)."""
+    dy = _c(dy)
+    q_w = _c(q_w, np.int8)
+    M, N = dy.shape
+    K = q_w.shape[1]
+    sw = _c(s_w, np.float32)
+    dx = np.empty((M, K), np.float32)
+    sg = np.zeros(1, np.float32)
+    sh = np.zeros(1, np.float32)
+    flags = lib().orc_qgemm_bwd_dx_wht(_p(dy), _dtype_code(dy), _p(sw), _p(q_w), M, N, K, b,
+                                       _p(dx), _p(sg), _p(sh))
+    return dx, sg[0], sh[0], flags
 
 
 def rmsnorm_fwd(x, g, eps: float = 1e-6):

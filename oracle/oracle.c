@@ -448,6 +448,89 @@ int orc_qgemm_bwd_dw_wht(const int8_t* qx, const float* s_x, const void* dy,
 }
 
 /* ------------------------------------------------------------------------
+ * Input-gradient GEMM with the rotation (a variant) -- §3.2 "int8
+ * computation" puts a Walsh-Hadamard rotation along the contraction
+ * dimension in front of both straight-through gradient GEMMs.  For
+ * dX = dY * W^ (W^ = s_w (.) q_w, per output channel n) the contraction runs
+ * over n.  The gradient side g = fl(dY * s_w[n]) (the same product the
+ * unrotated path quantises) is rotated in fp32 along n, per row m and
+ * aligned block of b; the weight side is rotated exactly in integers along
+ * n, per column k, and requantised like the rotated activations.  With
+ * H H^T = b I:  dX ~= (1/b) * (g H)(H q_w) * s_g * s_w'.
+ * ---------------------------------------------------------------------- */
+int orc_wht_fp_rows_quant(const void* dy, int dtype, int64_t M, int64_t N,
+                          const float* s_w, int b, int8_t* q, float* s_out,
+                          float* v_out) {
+  int64_t n = M * N;
+  float* v = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+  assert(v);
+  for (int64_t i = 0; i < n; i++) {
+    float e = load(dy, dtype, i);
+    if (s_w) e = fmul(e, orc_flush(s_w[i % N]));
+    v[i] = e;
+  }
+  /* Per row and aligned block of b consecutive n, butterflies in stage
+   * order h = 1, 2, 4, ..., b/2: (v_j, v_j+h) <- (v_j + v_j+h, v_j - v_j+h),
+   * the token rotation's stages, here along the row. */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t m = 0; m < M; m++) {
+    for (int64_t base = 0; base < N; base += b) {
+      float* blk = v + m * N + base;
+      for (int h = 1; h < b; h *= 2) {
+        for (int j = 0; j < b; j++) {
+          if ((j % (2 * h)) >= h) continue;
+          float x0 = blk[j], x1 = blk[j + h];
+          blk[j] = fadd(x0, x1);
+          blk[j + h] = fsub(x0, x1);
+        }
+      }
+    }
+  }
+  float amax;
+  int flags = lsq_group(v, n, 0, q, s_out, &amax);
+  if (v_out) memcpy(v_out, v, (size_t)n * sizeof(float));
+  free(v);
+  return flags;
+}
+
+int orc_qgemm_bwd_dx_wht(const void* dy, int dtype, const float* s_w,
+                         const int8_t* qw, int64_t M, int64_t N, int64_t K, int b,
+                         float* dx, float* s_g_out, float* s_h_out) {
+  int8_t* q_g = (int8_t*)malloc((size_t)(M * N > 0 ? M * N : 1));
+  int8_t* q_h = (int8_t*)malloc((size_t)(N * K > 0 ? N * K : 1));
+  assert(q_g && q_h);
+  float s_g, s_h;
+  int flags = orc_wht_fp_rows_quant(dy, dtype, M, N, s_w, b, q_g, &s_g, NULL);
+  /* q_w [N][K] rotated along its rows n, per column k: the same routine as
+   * the activation codes' rotation along tokens */
+  orc_wht_int_quant(qw, N, K, b, q_h, &s_h, NULL);
+  float inv_b = ldexpf(1.0f, -__builtin_ctz((unsigned)b)); /* exact 1/b */
+  float c = fmul(fmul(orc_flush(s_g), orc_flush(s_h)), inv_b);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t m = 0; m < M; m++) {
+    int64_t* acc = (int64_t*)calloc((size_t)K, sizeof(int64_t));
+    assert(acc);
+    for (int64_t nn = 0; nn < N; nn++) {
+      int64_t g = q_g[m * N + nn];
+      if (g == 0) continue;
+      const int8_t* row = q_h + nn * K;
+      for (int64_t k = 0; k < K; k++) acc[k] += g * (int64_t)row[k];
+    }
+    for (int64_t k = 0; k < K; k++) dx[m * K + k] = fmul(acc_to_f32(acc[k]), c);
+    free(acc);
+  }
+  if (s_g_out) *s_g_out = s_g;
+  if (s_h_out) *s_h_out = s_h;
+  free(q_g);
+  free(q_h);
+  return flags;
+}
+
+/* ------------------------------------------------------------------------
  * RMSNorm -- §3.1 "RMSNorm" (pre-norm, no bias) and the precision note
  * (normalisation in FP32, parameters BF16): y = x * rsqrt(mean(x^2)+eps)*g
  * with a correctly rounded sqrt followed by a reciprocal.

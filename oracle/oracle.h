@@ -140,6 +140,18 @@ int orc_qgemm_bwd_dw_wht(const int8_t* qx, const float* s_x, const void* dy,
                          int dtype, int64_t M, int64_t N, int64_t K, int b,
                          float* dw, float* s_u_out, float* s_v_out);
 
+/* Rotated input-gradient GEMM (variant): g = fl(dy * s_w[n]) rotated in
+ * fp32 along n per row and aligned block of b, per-tensor LSQ -> q_g, s_g;
+ * q_w [N][K] rotated exactly along n and requantised -> q_h, s_h;
+ * dx[m][k] = fl(fl(sum_n q_g[m][n] q_h[n][k]) * fl(fl(s_g*s_h) * 1/b)).
+ * s_w may be NULL (no multiplier) for the rotation alone. */
+int orc_wht_fp_rows_quant(const void* dy, int dtype, int64_t M, int64_t N,
+                          const float* s_w, int b, int8_t* q, float* s_out,
+                          float* v_out);
+int orc_qgemm_bwd_dx_wht(const void* dy, int dtype, const float* s_w,
+                         const int8_t* qw, int64_t M, int64_t N, int64_t K, int b,
+                         float* dx, float* s_g_out, float* s_h_out);
+
 /* RMSNorm forward per row: ss = tree(x*x), ms = ss*(1/D),
  * rstd = 1/sqrt(ms+eps), y = (x*rstd)*g.  x, g, y in `dtype`. */
 int orc_rmsnorm_fwd(const void* x, const void* g, int dtype, int64_t T,

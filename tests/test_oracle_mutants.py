@@ -61,6 +61,14 @@ MUTANTS = {
                                "uint32_t u = f2u(v[i]) & 0x7fffffffu; if (u && u < 0x800000u) "
                                "{ exact_add(w, u, 0); continue; }"),
     "exact_uses_tree": ("    S = orc_exact_abs_sum(v, n);", "    S = orc_tree_sum(v, n);"),
+    "rows_wht_sign": ("blk[j + h] = fsub(x0, x1);", "blk[j + h] = fsub(x1, x0);"),
+    "rows_wht_no_multiplier": ("if (s_w) e = fmul(e, orc_flush(s_w[i % N]));", "(void)s_w;"),
+    "rows_wht_multiplier_by_row": ("if (s_w) e = fmul(e, orc_flush(s_w[i % N]));",
+                                   "if (s_w) e = fmul(e, orc_flush(s_w[(i / N) % N]));"),
+    "dx_wht_missing_inv_b": ("float c = fmul(fmul(orc_flush(s_g), orc_flush(s_h)), inv_b);",
+                             "float c = fmul(orc_flush(s_g), orc_flush(s_h));"),
+    "dx_wht_weights_unrotated": ("orc_wht_int_quant(qw, N, K, b, q_h, &s_h, NULL);",
+                                 "orc_wht_int_quant(qw, N, K, 1, q_h, &s_h, NULL);"),
     "clip_always_scales": ("*clip = norm > max_norm ? fdiv(orc_flush(max_norm), norm) : 1.0f;",
                            "*clip = fdiv(orc_flush(max_norm), norm);"),
 }

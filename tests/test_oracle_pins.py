@@ -970,3 +970,85 @@ def test_lsq_exact_statistic_scale_and_codes(orc, syn):
     assert s[0] == 0 and not q.any() and fl == 0
     z[1, 3] = np.inf
     assert orc.quantize_lsq(z, exact=True)[4] == orc.FLAG_NONFINITE
+
+
+# --------------------------------------------------------------------------
+# rotated input-gradient GEMM (rotation along n)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("b", [1, 2, 8, 128])
+def test_wht_rows_integer_inputs_exact(orc, b):
+    """Integer-valued inputs stay exact: the row rotation must equal the
+    Sylvester transform of each aligned block of b consecutive n."""
+    H = scipy.linalg.hadamard(b).astype(np.int64)
+    rng = np.random.default_rng(b + 11)
+    M, N = 6, 2 * b if b >= 8 else 16
+    d = rng.integers(-1000, 1001, size=(M, N))
+    _, _, v, fl = orc.wht_fp_rows_quant(d.astype(np.float32), b, want_v=True)
+    want = np.concatenate([d[:, i:i + b] @ H.T for i in range(0, N, b)], axis=1)
+    assert fl == 0 and np.array_equal(v, want.astype(np.float32))
+
+
+def test_wht_rows_random_within_bound_and_multiplier(orc, syn):
+    """fp32 rows rotation of dy * s_w within the butterfly's rounding bound
+    of the fp64 transform of the fp64 product."""
+    b = 128
+    H = scipy.linalg.hadamard(b).astype(np.float64)
+    dy = syn.normal((8, 512), 1e-3, tag=310)
+    sw = syn.normal((512,), 0.01, mean=0.02, tag=311)
+    _, _, v, _ = orc.wht_fp_rows_quant(dy, b, s_w=sw, want_v=True)
+    g = dy.astype(np.float64) * sw.astype(np.float64)[None, :]
+    want = np.concatenate([g[:, i:i + b] @ H.T for i in range(0, 512, b)], axis=1)
+    l1 = np.concatenate([np.abs(g[:, i:i + b]) @ np.abs(H.T) for i in range(0, 512, b)], axis=1)
+    bound = (math.log2(b) + 1) * 2.0 ** -24 * l1 * 1.01
+    assert np.all(np.abs(v - want) <= bound)
+
+
+def test_wht_rows_b1_is_the_plain_quantiser(orc, syn):
+    """b = 1 rotates nothing: the codes and step of g = dy * s_w are those of
+    the unrotated path's quantiser."""
+    dy = syn.normal((64, 256), 1e-3, tag=312)
+    sw = syn.normal((256,), 0.01, mean=0.02, tag=313)
+    q, s, _, _ = orc.wht_fp_rows_quant(dy, 1, s_w=sw)
+    q0, _, s0, _, _ = orc.quantize_lsq(dy, col_mul=sw)
+    assert np.array_equal(q, q0) and bits(s) == bits(s0[0])
+
+
+@pytest.mark.parametrize("b", [16, 128])
+def test_dx_wht_epilogue_closed_form(orc, syn, b):
+    """dx = fl(fl(acc) * fl(fl(s_g * s_h) * 1/b)) with acc the exact int64
+    product of the two rotated code tensors (numpy integer algebra)."""
+    M, N, K = 64, 256, 96
+    dy = syn.normal((M, N), 1e-3, tag=314)
+    w = syn.normal((N, K), 0.02, tag=315)
+    qw, _, sw, _, _ = orc.quantize_lsq(w, per_row=True)
+    dx, s_g, s_h, fl = orc.qgemm_bwd_dx_wht(dy, sw, qw, b)
+    q_g, s_g2, _, _ = orc.wht_fp_rows_quant(dy, b, s_w=sw)
+    q_h, s_h2, _ = orc.wht_int_quant(qw, b)
+    assert fl == 0 and bits(s_g) == bits(s_g2) and bits(s_h) == bits(s_h2)
+    acc = q_g.astype(np.int64) @ q_h.astype(np.int64)
+    c = np.float32(np.float32(s_g) * np.float32(s_h)) * np.float32(1.0 / b)
+    want = (acc.astype(np.float32) * np.float32(c)).astype(np.float32)
+    assert np.array_equal(dx, want)
+
+
+def test_dx_wht_reduces_error_on_heavy_tails(orc, syn):
+    """§3.2 "int8 computation": the rotation along the contraction flattens
+    outliers.  On heavy-tailed gradients the rotated dX is closer to the
+    fp64 product dY * W^ than the plain int8 dX; on Gaussian gradients both
+    stay at the LSQ noise floor."""
+    M, N, K = 512, 512, 256
+    w = syn.normal((N, K), 0.02, tag=316)
+    qw, _, sw, _, _ = orc.quantize_lsq(w, per_row=True)
+    what = sw.astype(np.float64)[:, None] * qw.astype(np.float64)
+    for tag, dy, heavy in ((317, syn.student_t3((M, N), 1e-3, tag=317), True),
+                           (318, syn.normal((M, N), 1e-3, tag=318), False)):
+        ref = dy.astype(np.float64) @ what
+        q_g, _, s_g, _, _ = orc.quantize_lsq(dy, col_mul=sw)
+        plain = orc.qgemm_bwd_dx(q_g, s_g, qw)
+        rot, _, _, _ = orc.qgemm_bwd_dx_wht(dy, sw, qw, 128)
+        e0 = np.linalg.norm(plain - ref) / np.linalg.norm(ref)
+        e1 = np.linalg.norm(rot - ref) / np.linalg.norm(ref)
+        if heavy:
+            assert e1 < 0.7 * e0 and e1 < 0.07, (e0, e1)
+        else:
+            assert e0 < 0.06 and e1 < 0.07, (e0, e1)
