@@ -20,14 +20,14 @@ F32, BF16, I8, I32, U8 = 0, 1, 2, 3, 4
 PER_TENSOR, PER_ROW = 0, 1
 FLAG_NONFINITE = 1
 OP_QUANTIZE, OP_QGEMM, OP_DW_WHT, OP_RMSNORM_BWD, OP_GRAD_NORM, OP_DY_BWD = 1, 2, 3, 4, 5, 6
-OP_QUANTIZE_EXACT = 7
+OP_QUANTIZE_EXACT, OP_DX_WHT, OP_DY_ROWS_WHT = 7, 8, 9
 MAX_CONTRACTION = 133144
 
 SYMBOLS = [
     "brq_workspace_size", "brq_quantize_lsq", "brq_quantize_lsq_exact", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
     "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
     "brq_qgemm_fwd_ex", "brq_qgemm_bwd_dx_ex",
-    "brq_quantize_dy_bwd",
+    "brq_quantize_dy_bwd", "brq_qgemm_bwd_dx_wht", "brq_wht_quant_dy_rows",
     "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm",
     "brq_hash_workspace_size", "brq_hash_state", "brq_hash_digests_workspace_size",
     "brq_hash_tensor_digests", "brq_hash_combine", "brq_adamw_bias_corrections",
@@ -88,6 +88,12 @@ def lib():
         L.brq_qgemm_bwd_dx_ex.restype = i32
         L.brq_qgemm_bwd_dx_ex.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, vp, sz, vp, vp]
         L.brq_qgemm_bwd_dw_wht.restype = i32
+        L.brq_qgemm_bwd_dx_wht.restype = i32
+        L.brq_qgemm_bwd_dx_wht.argtypes = [vp, i32, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp,
+                                           sz, vp, vp, vp]
+        L.brq_wht_quant_dy_rows.restype = i32
+        L.brq_wht_quant_dy_rows.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, sz, vp, vp,
+                                            vp]
         L.brq_qgemm_bwd_dw_wht.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp, vp, vp,
                                            sz, vp, vp, vp]
         L.brq_wht_quant_x.restype = i32
@@ -328,6 +334,50 @@ def qgemm_bwd_dw_wht(q_x, s_x, dy, block, tune=None, out=None, ws=None, flags=No
     q_ut = w[:K * M].view(torch.int8).view(K, M).clone()
     q_vt = w[off:off + N * M].view(torch.int8).view(N, M).clone()
     return dw, s_u, s_v, q_ut, q_vt
+
+
+def qgemm_bwd_dx_wht(dy, s_w, q_w, block, tune=None, out=None, ws=None, flags=None,
+                     return_codes=False):
+    """Input-gradient GEMM with the rotation along n.  Returns (dx, s_g, s_h)
+    and, with return_codes, also (q_ht [K][N], q_g [M][N]): the rotated codes
+    the call left at the start of its workspace."""
+    _dev(dy, "dy"); _dev(s_w, "s_w"); _dev(q_w, "q_w")
+    M, N = dy.shape
+    K = q_w.shape[1]
+    if q_w.shape[0] != N or s_w.numel() != N:
+        raise BrqError("q_w / s_w: output-channel count differs from dy")
+    dx = _out(out, (M, K), torch.float32, "dx") if out is not None else \
+        torch.empty((M, K), dtype=torch.float32, device=dy.device)
+    s_g = torch.empty(1, dtype=torch.float32, device=dy.device)
+    s_h = torch.empty(1, dtype=torch.float32, device=dy.device)
+    need = workspace_size(OP_DX_WHT, M, N, K, block, tune=tune)
+    w = _ws(need, dy.device, ws)
+    _check(lib().brq_qgemm_bwd_dx_wht(_ptr(dy), _fp_code(dy), _ptr(s_w), _ptr(q_w), M, N, K,
+                                      block, _ptr(dx), _ptr(s_g), _ptr(s_h), _ptr(w), w.numel(),
+                                      _ptr(flags), _tune(tune), _stream()), "qgemm_bwd_dx_wht")
+    if not return_codes:
+        return dx, s_g, s_h
+    off = (K * N + 255) // 256 * 256
+    q_ht = w[:K * N].view(torch.int8).view(K, N).clone()
+    q_g = w[off:off + M * N].view(torch.int8).view(M, N).clone()
+    return dx, s_g, s_h, q_ht, q_g
+
+
+def wht_quant_dy_rows(dy, s_w, block, tune=None, ws=None, flags=None, out=None):
+    """Rows rotation of dy * s_w and its per-tensor codes: (q_g [M][N], s_g)."""
+    _dev(dy, "dy"); _dev(s_w, "s_w")
+    M, N = dy.shape
+    q_g, s_g = out if out is not None else (None, None)
+    if q_g is None:
+        q_g = torch.empty((M, N), dtype=torch.int8, device=dy.device)
+    if s_g is None:
+        s_g = torch.empty(1, dtype=torch.float32, device=dy.device)
+    need = workspace_size(OP_DY_ROWS_WHT, M, N, tune=tune)
+    w = _ws(need, dy.device, ws)
+    _check(lib().brq_wht_quant_dy_rows(_ptr(dy), _fp_code(dy), M, N, _ptr(s_w), block, _ptr(q_g),
+                                       _ptr(s_g), _ptr(w), w.numel(), _ptr(flags), _tune(tune),
+                                       _stream()), "wht_quant_dy_rows")
+    return q_g, s_g
 
 
 def wht_quant_x(q_x, block, tune=None, ws=None, out=None):

@@ -32,6 +32,27 @@ size_t quant_ws(int64_t rows, int64_t cols, const brq_tune* t) {
   return flat_reduce_ws(rows * cols, flat_chunk_log2(t)) + kScalars;
 }
 
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// rotated input-gradient GEMM: q_h^T [K][N], q_g [M][N], scalars, then the
+// larger of the two rotation stages' scratch, then the GEMM's
+size_t dx_wht_stage_ws(int64_t M, int64_t N, int64_t K, int block) {
+  size_t a = wht_x_ws(N, K, block), b = wht_rows_ws(M, N);
+  return a > b ? a : b;
+}
+size_t dx_wht_ws(int64_t M, int64_t N, int64_t K, int block, const brq_tune* t) {
+  return align256((size_t)(K * N)) + align256((size_t)(M * N)) + kScalars +
+         dx_wht_stage_ws(M, N, K, block) + gemm_ws(M, K, N, t);
+}
+
+int check_dx_wht_shape(int64_t M, int64_t N, int64_t K, int block) {
+  if (M < 0 || N < 0 || K < 0) return BRQ_E_SHAPE;
+  if (!pow2(block) || block > 128) return BRQ_E_UNSUPPORTED;
+  if (N == 0 || M % 16 || N % 64 || N % block || K % 64) return BRQ_E_UNSUPPORTED;
+  if (N > BRQ_MAX_CONTRACTION) return BRQ_E_RANGE;
+  return BRQ_OK;
+}
+
 size_t quant_exact_ws(int64_t rows, int64_t cols) {
   return exact_reduce_ws(rows * cols) + kScalars;
 }
@@ -45,8 +66,6 @@ size_t dw_ws(int64_t M, int64_t N, int64_t K, int block, const brq_tune* t) {
   return align256((size_t)(K * M)) + align256((size_t)(N * M)) + kScalars +
          dw_stage_ws(M, N, K, block, t) + gemm_ws(N, K, M, t);
 }
-
-bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
 size_t dy_bwd_ws(int64_t M, int64_t N, int block, const brq_tune* t) {
   const int c = flat_chunk_log2(t);
@@ -90,6 +109,8 @@ size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block, co
   switch (op) {
     case BRQ_OP_QUANTIZE: return quant_ws(a, b, t);
     case BRQ_OP_QUANTIZE_EXACT: return quant_exact_ws(a, b);
+    case BRQ_OP_DX_WHT: return dx_wht_ws(a, b, c, block > 0 ? block : 1, t);
+    case BRQ_OP_DY_ROWS_WHT: return wht_rows_ws(a, b) + kScalars;
     case BRQ_OP_QGEMM: return gemm_ws(a, b, c, t);
     case BRQ_OP_DW_WHT: return dw_ws(a, b, c, block > 0 ? block : 1, t);
     case BRQ_OP_RMSNORM_BWD: {
@@ -282,6 +303,60 @@ int brq_qgemm_bwd_dw_wht(const int8_t* q_x, const float* s_x, const void* dy, in
   if (r != BRQ_OK) return r;
   return brq_qgemm_dw(q_vt, q_ut, s_x, s_u, s_v, M, N, K, block, dw, gws, gemm_ws(N, K, M, tune),
                       tune, stream);
+}
+
+int brq_wht_quant_dy_rows(const void* dy, int dy_dtype, int64_t M, int64_t N, const float* s_w,
+                          int block, int8_t* q_g, float* s_g, void* ws, size_t ws_bytes,
+                          int32_t* dflags, const brq_tune* tune, void* stream) {
+  (void)tune;
+  if (!fp_dtype(dy_dtype)) return BRQ_E_DTYPE;
+  int st = check_dx_wht_shape(M, N, 64, block);
+  if (st != BRQ_OK) return st;
+  if (!s_g || (M * N > 0 && (!dy || !s_w || !q_g))) return BRQ_E_NULL;
+  if (!aligned16(dy) || !aligned16(q_g) || !aligned16(s_w)) return BRQ_E_ALIGN;
+  const size_t need = wht_rows_ws(M, N) + kScalars;
+  if (!ws || ws_bytes < need) return BRQ_E_WORKSPACE;
+  float* sr = (float*)((char*)ws + wht_rows_ws(M, N));
+  return hip_status(wht_rows_quant(dy, dy_dtype, M, N, s_w, block, q_g, s_g, sr, ws, dflags,
+                                   as_stream(stream)));
+}
+
+int brq_qgemm_bwd_dx_wht(const void* dy, int dy_dtype, const float* s_w, const int8_t* q_w,
+                         int64_t M, int64_t N, int64_t K, int block, float* dx, float* s_g_out,
+                         float* s_h_out, void* ws, size_t ws_bytes, int32_t* dflags,
+                         const brq_tune* tune, void* stream) {
+  if (!fp_dtype(dy_dtype)) return BRQ_E_DTYPE;
+  int st = check_dx_wht_shape(M, N, K, block);
+  if (st != BRQ_OK) return st;
+  if (M * N > 0 && (!dy || !s_w)) return BRQ_E_NULL;
+  if (N * K > 0 && !q_w) return BRQ_E_NULL;
+  if (M * K > 0 && !dx) return BRQ_E_NULL;
+  if (!aligned16(dy) || !aligned16(q_w) || !aligned16(dx) || !aligned16(s_w)) return BRQ_E_ALIGN;
+  if (M == 0 || K == 0) return BRQ_OK;  // dx is empty: nothing is computed
+  const size_t need = dx_wht_ws(M, N, K, block, tune);
+  if (!ws || ws_bytes < need) return BRQ_E_WORKSPACE;
+  char* w = (char*)ws;
+  int8_t* q_ht = (int8_t*)w;
+  w += align256((size_t)(K * N));
+  int8_t* q_g = (int8_t*)w;
+  w += align256((size_t)(M * N));
+  float* scal = (float*)w;  // [0] s_g [1] r_g [2] 1 [3] s_h (when s_h_out is NULL)
+  w += kScalars;
+  void* stage = w;
+  w += dx_wht_stage_ws(M, N, K, block);
+  void* gws = w;
+  hipStream_t s = as_stream(stream);
+  hipError_t e;
+  float* s_h = s_h_out ? s_h_out : scal + 3;
+  if ((e = wht_quant_x(q_w, N, K, block, q_ht, s_h, stage, s)) != hipSuccess) return hip_status(e);
+  if ((e = wht_rows_quant(dy, dy_dtype, M, N, s_w, block, q_g, s_g_out, scal, stage, dflags, s)) !=
+      hipSuccess)
+    return hip_status(e);
+  int lb = 0;
+  while ((1 << lb) < block) ++lb;
+  // c = fl(fl(fl(s_g * s_h) * 1) * 2^-lb)
+  EpiArgs epi{EPI_DW, scal, s_h, scal + 2, 0, ldexpf(1.0f, -lb)};
+  return hip_status(gemm_i8(q_g, q_ht, M, K, N, dx, epi, gws, gemm_ws(M, K, N, tune), tune, s));
 }
 
 int brq_quantize_dy_bwd(const void* dy, int dy_dtype, int64_t M, int64_t N, const float* s_w,

@@ -161,6 +161,36 @@ __device__ __forceinline__ void unpack_f32x4(u32x4 v, float* f) {
 }
 
 // Element type traits: values per 16-byte vector.
+// Walsh-Hadamard butterflies over aligned blocks of B consecutive values
+// (Sylvester order, unnormalised), stage order h = 1, 2, ..., B/2:
+// (v_j, v_j+h) <- (fl(v_j + v_j+h), fl(v_j - v_j+h)).  Each lane holds P
+// consecutive values; a block spans B / P consecutive lanes when B > P,
+// else it sits inside the lane.  Every lane of the wave must call this.
+template <int P, int B>
+__device__ __forceinline__ void wht_block(float* f, int lane) {
+#pragma unroll
+  for (int h = 1; h < B; h *= 2) {
+    if (h < P) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        if ((j % (2 * h)) < h) {
+          const float x0 = f[j], x1 = f[j + h];
+          f[j] = fadd(x0, x1);
+          f[j + h] = fsub(x0, x1);
+        }
+      }
+    } else {
+      const int dl = h / P;  // the partner lane holds the same j of the other half
+      const bool upper = (lane & dl) != 0;
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const float o = __shfl_xor(f[j], dl);
+        f[j] = upper ? fsub(o, f[j]) : fadd(f[j], o);
+      }
+    }
+  }
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int kPerVec = 4;

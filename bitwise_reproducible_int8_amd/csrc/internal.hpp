@@ -27,9 +27,12 @@ size_t flat_reduce_ws(int64_t n, int chunk_log2);
 // Reduce n leaves of kind `leaf` (dtype of x) to the tree sum; writes the
 // sum and the max of |leaf| into out[0], out[1] (device), raising
 // BRQ_FLAG_NONFINITE when the sum is not finite.  Uses ws.
+// wht_block > 0 (leaf LEAF_ABS_COLMUL): the leaves are |x * col_mul| after
+// the Walsh-Hadamard rotation along each row in blocks of wht_block
+// (cols % wht_block == 0, wht_block <= 128); the chunk is then fixed.
 hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul,
                        int64_t n, int64_t cols, float* out2, void* ws,
-                       int chunk_log2, int32_t* dflags, hipStream_t s);
+                       int chunk_log2, int32_t* dflags, hipStream_t s, int wht_block = 0);
 
 // Two raw fp32 leaf arrays of equal length n reduced as two flat_reduce
 // calls would, in one launch per level; workspace flat_reduce_pair_ws.
@@ -60,6 +63,12 @@ hipError_t quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
 
 // Exact-sum statistic (exact.hip): per-tensor S and max |v| into out2[0..1]
 // (two launches), and the per-row quantiser with exact row statistics.
+// Rows rotation of dY * s_w and its codes (dxwht.hip).
+size_t wht_rows_ws(int64_t M, int64_t N);
+hipError_t wht_rows_quant(const void* dy, int dtype, int64_t M, int64_t N, const float* s_w,
+                          int block, int8_t* q_g, float* s_g, float* sr, void* ws,
+                          int32_t* dflags, hipStream_t s);
+
 size_t exact_reduce_ws(int64_t n);
 hipError_t exact_reduce(const void* x, int dtype, const float* col_mul, int64_t n, int64_t cols,
                         float* out2, void* ws, int32_t* dflags, hipStream_t s);

@@ -27,7 +27,7 @@ namespace brq {
 // contiguous 64*16-byte run, and the 64 lanes' subtrees pair up through the
 // butterfly into node(log2(64E), .) of that run.
 // --------------------------------------------------------------------------
-template <typename T, int LEAF>
+template <typename T, int LEAF, int B = 0>
 __device__ __forceinline__ void leaves_of(const T* x, const float* cm, int64_t n,
                                           int64_t cols, int64_t idx0, float* f) {
   constexpr int E = Elem<T>::kPerVec;
@@ -42,6 +42,9 @@ __device__ __forceinline__ void leaves_of(const T* x, const float* cm, int64_t n
 #pragma unroll
     for (int e = 0; e < E; ++e) f[e] = fmul(f[e], flush(cm[col + e]));
   }
+  // rows rotation: the lanes of one aligned block of B run these together
+  // (every lane of the wave reaches this point)
+  if (B > 0) wht_block<E, B>(f, threadIdx.x & 63);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if (LEAF == LEAF_SQUARE) f[e] = flush_nonneg(f[e] * f[e]);
@@ -49,7 +52,7 @@ __device__ __forceinline__ void leaves_of(const T* x, const float* cm, int64_t n
   }
 }
 
-template <typename T, int LEAF, int V>
+template <typename T, int LEAF, int V, int B = 0>
 __device__ __forceinline__ void flat_leaves_body(const T* __restrict__ x,
                                                  const float* __restrict__ cm, int64_t n,
                                                  int64_t cols, float* __restrict__ psum,
@@ -63,7 +66,7 @@ __device__ __forceinline__ void flat_leaves_body(const T* __restrict__ x,
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     float f[E];
-    leaves_of<T, LEAF>(x, cm, n, cols, base + (int64_t)(v * 64 + lane) * E, f);
+    leaves_of<T, LEAF, B>(x, cm, n, cols, base + (int64_t)(v * 64 + lane) * E, f);
 #pragma unroll
     for (int e = 0; e < E; ++e) mx = fmaxf(mx, f[e]);
     node[v] = wave_tree<false>(reg_tree<false, E>(f));
@@ -86,6 +89,17 @@ __global__ __launch_bounds__(256) void k_flat_leaves(const T* __restrict__ x,
                                                      float* __restrict__ psum,
                                                      float* __restrict__ pmax) {
   flat_leaves_body<T, LEAF, V>(x, cm, n, cols, psum, pmax);
+}
+
+// The leaves |rows rotation of (x * cm)| in blocks of B along each row
+// (B <= 64 E, so every block sits in consecutive lanes of one wave).
+template <typename T, int V, int B>
+__global__ __launch_bounds__(256) void k_flat_leaves_wht(const T* __restrict__ x,
+                                                         const float* __restrict__ cm,
+                                                         int64_t n, int64_t cols,
+                                                         float* __restrict__ psum,
+                                                         float* __restrict__ pmax) {
+  flat_leaves_body<T, LEAF_ABS_COLMUL, V, B>(x, cm, n, cols, psum, pmax);
 }
 
 // Two independent raw-leaf reductions of equal length in one launch:
@@ -219,9 +233,31 @@ __global__ __launch_bounds__(256) void k_max_partials_pair(FlatPair below, FlatP
   max_partials_body(below.pm[y], P, level.pm[y]);
 }
 
+// Level 0 of the rows-rotation leaves: V = vectors_for(13, E) (4 for bf16,
+// 8 for fp32; the tree does not depend on the chunk), B a power of two.
+template <typename T, int V>
+static hipError_t launch_leaves_wht(const T* x, const float* cm, int64_t n, int64_t cols, int B,
+                                    int64_t P, float* ps, float* pm, hipStream_t s) {
+  dim3 g((unsigned)P), b(256);
+#define BRQ_LW(BB) hipLaunchKernelGGL((k_flat_leaves_wht<T, V, BB>), g, b, 0, s, x, cm, n, cols, ps, pm)
+  switch (B) {
+    case 1: BRQ_LW(1); break;
+    case 2: BRQ_LW(2); break;
+    case 4: BRQ_LW(4); break;
+    case 8: BRQ_LW(8); break;
+    case 16: BRQ_LW(16); break;
+    case 32: BRQ_LW(32); break;
+    case 64: BRQ_LW(64); break;
+    default: BRQ_LW(128); break;
+  }
+#undef BRQ_LW
+  return hipGetLastError();
+}
+
 hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul, int64_t n,
                        int64_t cols, float* out2, void* ws, int chunk_log2, int32_t* dflags,
-                       hipStream_t s) {
+                       hipStream_t s, int wht_block) {
+  if (wht_block > 0) chunk_log2 = 13;
   const int E = dtype == BRQ_BF16 ? 8 : 4;
   const int V = vectors_for(chunk_log2, E);
   const int64_t C0 = int64_t(256) * E * V;
@@ -237,7 +273,14 @@ hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul,
     w += align256(2 * sizeof(float) * (size_t)P[i]);
   }
   hipError_t e;
-  if (dtype == BRQ_BF16) {
+  if (wht_block > 0) {
+    if (dtype == BRQ_BF16)
+      e = launch_leaves_wht<uint16_t, 4>((const uint16_t*)x, col_mul, n, cols, wht_block, P[0],
+                                         ps[0], pm[0], s);
+    else
+      e = launch_leaves_wht<float, 8>((const float*)x, col_mul, n, cols, wht_block, P[0], ps[0],
+                                      pm[0], s);
+  } else if (dtype == BRQ_BF16) {
     const uint16_t* xb = (const uint16_t*)x;
     if (leaf == LEAF_ABS) e = launch_leaves<uint16_t, LEAF_ABS>(xb, col_mul, n, cols, V, P[0], ps[0], pm[0], s);
     else if (leaf == LEAF_ABS_COLMUL) e = launch_leaves<uint16_t, LEAF_ABS_COLMUL>(xb, col_mul, n, cols, V, P[0], ps[0], pm[0], s);

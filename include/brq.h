@@ -94,7 +94,9 @@ enum brq_op {
   BRQ_OP_RMSNORM_BWD = 4,  /* a = T, b = D */
   BRQ_OP_GRAD_NORM = 5,    /* a = n */
   BRQ_OP_DY_BWD = 6,       /* a = M, b = N, block = Hadamard block */
-  BRQ_OP_QUANTIZE_EXACT = 7 /* a = rows, b = cols */
+  BRQ_OP_QUANTIZE_EXACT = 7, /* a = rows, b = cols */
+  BRQ_OP_DX_WHT = 8,        /* a = M, b = N, c = K, block = Hadamard block */
+  BRQ_OP_DY_ROWS_WHT = 9    /* a = M, b = N */
 };
 size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block,
                           const struct brq_tune* tune);
@@ -222,6 +224,39 @@ int brq_qgemm_dw(const int8_t* q_vt, const int8_t* q_ut, const float* s_x,
                  const float* s_u, const float* s_v, int64_t M, int64_t N,
                  int64_t K, int block, float* dw, void* ws, size_t ws_bytes,
                  const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * qgemm_bwd_dx_wht -- the input-gradient GEMM with the Walsh-Hadamard
+ * rotation along its contraction n (a variant: §3.2 "int8 computation"
+ * puts the rotation in front of both straight-through gradient GEMMs).
+ *     g   = fl(dy[m][n] * s_w[n]); per row m and aligned block of `block`
+ *           consecutive n, fp32 butterflies in stage order h = 1, 2, ...,
+ *           block/2: (g_j, g_j+h) <- (fl(g_j + g_j+h), fl(g_j - g_j+h));
+ *           per-tensor LSQ over the rotated g (tree statistic) -> q_g, s_g
+ *     q_h = q_w [N][K] rotated exactly along n per column k and requantised,
+ *           as brq_wht_quant_x does for q_x along tokens -> s_h
+ *     dx[m][k] = fl(fl(sum_n q_g[m][n] * q_h[n][k]) * c),
+ *     c = fl(fl(s_g * s_h) * 2^-log2(block))
+ * dy [M][N] (BRQ_F32 or BRQ_BF16), s_w [N] fp32 (per-channel weight steps),
+ * q_w [N][K] int8 (the forward weight code), dx [M][K] fp32; s_g_out and
+ * s_h_out optional device floats.  Shapes: block a power of two in
+ * [1, 128]; M % 16 == 0; N > 0, N % 64 == 0, N % block == 0; K % 64 == 0;
+ * N <= BRQ_MAX_CONTRACTION.  M == 0 or K == 0 computes nothing.  Raises
+ * BRQ_FLAG_NONFINITE when s_g's statistic is not finite.
+ * Workspace: BRQ_OP_DX_WHT.
+ *
+ * brq_wht_quant_dy_rows: its first stage on its own, q_g [M][N] and s_g [1].
+ * Workspace: BRQ_OP_DY_ROWS_WHT.
+ * --------------------------------------------------------------------- */
+int brq_qgemm_bwd_dx_wht(const void* dy, int dy_dtype, const float* s_w,
+                         const int8_t* q_w, int64_t M, int64_t N, int64_t K,
+                         int block, float* dx, float* s_g_out, float* s_h_out,
+                         void* ws, size_t ws_bytes, int32_t* dflags,
+                         const struct brq_tune* tune, void* stream);
+int brq_wht_quant_dy_rows(const void* dy, int dy_dtype, int64_t M, int64_t N,
+                          const float* s_w, int block, int8_t* q_g, float* s_g,
+                          void* ws, size_t ws_bytes, int32_t* dflags,
+                          const struct brq_tune* tune, void* stream);
 
 /* ---------------------------------------------------------------------
  * quantize_dy_bwd -- both int8 codes of the upstream gradient for the two
