@@ -411,6 +411,62 @@ def main():
                 "value"}
     del xq, wq, xws
 
+    # Variant (not part of value): the 7 input-gradient GEMMs with the
+    # rotation along n (both rotations, codes and the GEMM), block 128.
+    dxb = [torch.empty_like(step.dx[i]) for i in range(len(syn.LAYER_LINEARS))]
+    dws = torch.empty(max(brq.workspace_size(brq.OP_DX_WHT, M, N, K, BLOCK)
+                          for _, K, N, _ in syn.LAYER_LINEARS), dtype=torch.uint8, device=dev)
+
+    def dx_wht():
+        for i in range(len(syn.LAYER_LINEARS)):
+            brq.qgemm_bwd_dx_wht(step.dy[i], step.s_w[i], step.q_w[i], BLOCK, out=dxb[i], ws=dws)
+    for _ in range(args.warmup):
+        dx_wht()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        dx_wht()
+    e1.record()
+    torch.cuda.synchronize()
+    variants["gemm_dx_wht_along_n"] = {
+        "ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4),
+        "plain_gemm_dx_ms_per_step": (round(kernels["gemm_dx"]["ms_per_step"], 4)
+                                      if kernels else None),
+        "note": "the 7 input-gradient GEMMs with the rotation along n (rows rotation of dY*s_w "
+                "and its codes, rotation and requantisation of the weight codes, GEMM); the plain "
+                "path's dY codes come fused with the weight-gradient codes; not part of value"}
+    del dxb, dws
+
+    # Variant (not part of value): per-tensor weight steps -- the 7 weight
+    # quantisations (with the transposed codes) and the 7 forward GEMMs with
+    # a scalar weight step.
+    wpt = [(torch.empty_like(step.q_w[i]), torch.empty_like(step.q_wt[i]),
+            torch.empty(1, device=dev), torch.empty(1, device=dev))
+           for i in range(len(syn.LAYER_LINEARS))]
+    ypt = [torch.empty_like(step.y[i]) for i in range(len(syn.LAYER_LINEARS))]
+    wws = torch.empty(max(brq.workspace_size(brq.OP_QUANTIZE, N, K) for _, K, N, _ in syn.LAYER_LINEARS),
+                      dtype=torch.uint8, device=dev)
+
+    def per_tensor_w():
+        for i, (_n, _K, _N, xin) in enumerate(syn.LAYER_LINEARS):
+            brq.quantize_lsq(step.w[i], want_t=True, ws=wws, out=wpt[i])
+            brq.qgemm_fwd(step.q_x[xin], step.s_x[xin], wpt[i][0], wpt[i][2], out=ypt[i], ws=step.ws)
+    for _ in range(args.warmup):
+        per_tensor_w()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        per_tensor_w()
+    e1.record()
+    torch.cuda.synchronize()
+    variants["weight_steps_per_tensor"] = {
+        "ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4),
+        "per_channel_ms_per_step": (round(kernels["quant_w"]["ms_per_step"] +
+                                          kernels["gemm_fwd"]["ms_per_step"], 4) if kernels else None),
+        "note": "the 7 weight quantisations (with transposed codes) and 7 forward GEMMs with one "
+                "step per weight tensor; not part of value"}
+    del wpt, ypt, wws
+
     cpu = None
     if args.cpu_tokens > 0:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")

@@ -181,11 +181,58 @@ __device__ __forceinline__ void wht_block(float* f, int lane) {
       }
     } else {
       const int dl = h / P;  // the partner lane holds the same j of the other half
-      const bool upper = (lane & dl) != 0;
+      // the lower lane keeps fl(own + other); the upper lane keeps
+      // fl(other - own), which IEEE defines as fl(other + (-own)): one add
+      // with the sign of `own` flipped in the upper lane
+      const uint32_t sgn = (lane & dl) ? 0x80000000u : 0u;
 #pragma unroll
       for (int j = 0; j < P; ++j) {
         const float o = __shfl_xor(f[j], dl);
-        f[j] = upper ? fsub(o, f[j]) : fadd(f[j], o);
+        f[j] = fadd(o, __uint_as_float(__float_as_uint(f[j]) ^ sgn));
+      }
+    }
+  }
+}
+
+// ---- speculative unflushed evaluation ----------------------------------------
+// A result that is not subnormal is left unchanged by the flush, so a run of
+// operations evaluated without flushes equals the flushed evaluation
+// whenever no input and no intermediate result is subnormal.  Kernels run
+// that fast form, collect in `bad` the lanes where a value was subnormal
+// (a compare into a lane mask, OR-ed on the scalar unit), and redo the
+// whole wave's work with the flushes when the mask is not empty.
+__device__ __forceinline__ uint64_t sub_mask(float v) {
+  // one compare straight into a scalar lane mask (class bits 4 and 7:
+  // -subnormal, +subnormal)
+  uint64_t m;
+  asm("v_cmp_class_f32_e64 %0, %1, %2" : "=s"(m) : "v"(v), "v"(0x090));
+  return m;
+}
+
+// The butterflies of wht_block without flushes; subnormal results are
+// recorded in `bad`.
+template <int P, int B>
+__device__ __forceinline__ void wht_block_fast(float* f, int lane, uint64_t& bad) {
+#pragma unroll
+  for (int h = 1; h < B; h *= 2) {
+    if (h < P) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        if ((j % (2 * h)) < h) {
+          const float x0 = f[j], x1 = f[j + h];
+          f[j] = x0 + x1;
+          f[j + h] = x0 - x1;
+          bad |= sub_mask(f[j]) | sub_mask(f[j + h]);
+        }
+      }
+    } else {
+      const int dl = h / P;
+      const uint32_t sgn = (lane & dl) ? 0x80000000u : 0u;
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const float o = __shfl_xor(f[j], dl);
+        f[j] = o + __uint_as_float(__float_as_uint(f[j]) ^ sgn);
+        bad |= sub_mask(f[j]);
       }
     }
   }
@@ -202,6 +249,30 @@ template <> struct Elem<uint16_t> {
   __device__ static void unpack(u32x4 v, float* f) { unpack_bf16x8(v, f); }
   __device__ static float load1(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 };
+
+// raw 16-byte vectors -> floats without the DAZ flush (bf16 widened by a
+// shift); subnormal inputs are recorded in `bad`
+template <typename T>
+__device__ __forceinline__ void widen_raw(u32x4 v, float* f, uint64_t& bad) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if (Elem<T>::kPerVec == 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  }
+#pragma unroll
+  for (int e = 0; e < Elem<T>::kPerVec; ++e) bad |= sub_mask(f[e]);
+}
+
+// col mod cols, with a mask when cols is a power of two
+__device__ __forceinline__ int64_t col_of(int64_t i, int64_t cols) {
+  return (cols & (cols - 1)) == 0 ? (i & (cols - 1)) : i % cols;
+}
 
 __device__ __forceinline__ void set_flag(int32_t* flags, int32_t bit) {
   if (flags) atomicOr(flags, bit);

@@ -32,16 +32,33 @@ __global__ __launch_bounds__(256) void k_quant_wht_rows(const T* __restrict__ x,
   const int lane = threadIdx.x & 63;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   // the loop bound is the same for the 64 lanes of a wave: every lane
-  // reaches the cross-lane butterflies
+  // reaches the cross-lane butterflies and the wave-wide fallback test
   for (int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); c < nchunks; c += nwaves) {
     const int64_t i0 = c * 1024 + lane * 16;
-    float f[16];
+    const int64_t col = col_of(i0, cols);  // cols % 16 == 0: the 16 values sit in one row
+    u32x4 raw[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) Elem<T>::unpack(ld16(x + i0 + v * E), f + v * E);
-    const int64_t col = i0 % cols;  // cols % 16 == 0: the 16 values sit in one row
+    for (int v = 0; v < NV; ++v) raw[v] = ld16(x + i0 + v * E);
+    float f[16], m[16];
+    uint64_t bad = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) f[e] = fmul(f[e], flush(cm[col + e]));
-    wht_block<16, B>(f, lane);
+    for (int v = 0; v < NV; ++v) widen_raw<T>(raw[v], f + v * E, bad);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      m[e] = cm[col + e];
+      bad |= sub_mask(m[e]);
+      f[e] = f[e] * m[e];
+      bad |= sub_mask(f[e]);
+    }
+    wht_block_fast<16, B>(f, lane, bad);
+    if (bad) {  // some value of the wave was subnormal: the flushed form
+#pragma unroll
+      for (int v = 0; v < NV; ++v) Elem<T>::unpack(raw[v], f + v * E);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) f[e] = fmul(f[e], flush(m[e]));
+      wht_block<16, B>(f, lane);
+    }
+    // (a subnormal product f * r rounds to code 0 with or without its flush)
     uint32_t p[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 16; ++e) p[e >> 2] |= (uint32_t)(quant_code(f[e], r) & 0xff) << (8 * (e & 3));

@@ -31,6 +31,34 @@ template <typename T, int LEAF, int B = 0>
 __device__ __forceinline__ void leaves_of(const T* x, const float* cm, int64_t n,
                                           int64_t cols, int64_t idx0, float* f) {
   constexpr int E = Elem<T>::kPerVec;
+  if (B > 0) {
+    // |rows rotation of (x * cm)|: n % B == 0, so a vector is wholly in
+    // range or wholly past the end (zeros).  Evaluated without flushes
+    // first; any subnormal value in the wave redoes it with them.  Every
+    // lane of the wave reaches the butterflies and the test.
+    const u32x4 raw = idx0 < n ? ld16(x + idx0) : u32x4{0, 0, 0, 0};
+    const int64_t col = col_of(idx0, cols);
+    float m[E];
+    uint64_t bad = 0;
+    widen_raw<T>(raw, f, bad);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      m[e] = cm[col + e];
+      bad |= sub_mask(m[e]);
+      f[e] = f[e] * m[e];
+      bad |= sub_mask(f[e]);
+    }
+    wht_block_fast<E, B>(f, threadIdx.x & 63, bad);
+    if (bad) {
+      Elem<T>::unpack(raw, f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] = fmul(f[e], flush(m[e]));
+      wht_block<E, B>(f, threadIdx.x & 63);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = fabs_bits(f[e]);
+    return;
+  }
   if (idx0 + E <= n) {
     Elem<T>::unpack(ld16(x + idx0), f);
   } else {
@@ -42,9 +70,6 @@ __device__ __forceinline__ void leaves_of(const T* x, const float* cm, int64_t n
 #pragma unroll
     for (int e = 0; e < E; ++e) f[e] = fmul(f[e], flush(cm[col + e]));
   }
-  // rows rotation: the lanes of one aligned block of B run these together
-  // (every lane of the wave reaches this point)
-  if (B > 0) wht_block<E, B>(f, threadIdx.x & 63);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if (LEAF == LEAF_SQUARE) f[e] = flush_nonneg(f[e] * f[e]);

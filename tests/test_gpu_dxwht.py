@@ -88,6 +88,31 @@ def test_qgemm_bwd_dx_wht_plans(tune):
     assert_bitwise(gdx, dx, f"dx {tune}")
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_wht_rows_subnormal_band(bf16):
+    """Values near the bottom of the binary32 range: products dY * s_w and
+    butterfly sums land on subnormals (flushed to signed zeros) in some
+    waves and not in others, so both evaluation forms run."""
+    say("wht_rows_subnormal_band", bf16)
+    M, N, b = 64, 512, 128
+    dy = syn.normal((M, N), 1e-36, tag=328)
+    dy[::3] *= np.float32(1e30)  # every third row well inside the normal range
+    sw = syn.normal((N,), 0.01, mean=0.02, tag=329)
+    sw[::17] = np.float32(3e-39)  # subnormal steps read as zero
+    if bf16:
+        dy = orc.to_bf16(dy)
+    q, s, _, _ = orc.wht_fp_rows_quant(dy, b, s_w=sw)
+    gq, gs = brq.wht_quant_dy_rows(to_dev(dy), to_dev(sw), b)
+    assert_bitwise(gs, np.array([s], np.float32), "s_g")
+    assert_bitwise(gq, q, "q_g")
+    # only tiny rows: the statistic itself is near the bottom of the range
+    tiny = np.ascontiguousarray(dy[1::3][:16])
+    q, s, _, _ = orc.wht_fp_rows_quant(tiny, b, s_w=sw)
+    gq, gs = brq.wht_quant_dy_rows(to_dev(tiny), to_dev(sw), b)
+    assert_bitwise(gs, np.array([s], np.float32), "s_g tiny")
+    assert_bitwise(gq, q, "q_g tiny")
+
+
 def test_qgemm_bwd_dx_wht_edges():
     say("qgemm_bwd_dx_wht_edges")
     qw, sw = weights(256, 64, 327)
