@@ -48,6 +48,33 @@ __device__ __forceinline__ u32x4 load_vec(const uint16_t* __restrict__ dy, int64
   return col < N ? ld16(dy + (m0 + r) * N + col) : u32x4{0, 0, 0, 0};
 }
 
+// Fast-path test, exact (the argument under column_wht): a bf16 tile whose
+// nonzero values all have magnitude >= 2^-103 has only normal inputs, and
+// every product with a step |s| >= 2^-23 (or 0) and every butterfly sum
+// and difference is normal or zero, so each flush is the identity.  The
+// test runs on 16-bit pairs: |h| - 1 wraps a zero to 0xffff, and the
+// packed minimum must stay >= 0x0BFF (the pattern of 2^-103 is 0x0C00).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 tiny_min(u16x2 lo, u32x4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const u16x2 one = {1, 1};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u16x2 h = __builtin_bit_cast(u16x2, w[k] & 0x7fff7fffu);
+    lo = __builtin_elementwise_min(lo, h - one);
+  }
+  return lo;
+}
+__device__ __forceinline__ bool tiny_ok(u16x2 lo) { return lo.x >= 0x0BFFu && lo.y >= 0x0BFFu; }
+// the row phase's products also need every step |s| >= 2^-23 or s = 0
+__device__ __forceinline__ bool steps_ok(const float* s8) {
+  bool ok = true;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ok = ok && (s8[e] == 0.0f || fabsf(s8[e]) >= 0x1p-23f);
+  return ok;
+}
+
 // Column phase: the lane's 64 tokens of its column (DAZ), then the
 // butterflies in stage order h = 1, 2, ..., b/2, each a rounded sum and
 // difference (v_j, v_j+h) <- (fl(v_j + v_j+h), fl(v_j - v_j+h)).
@@ -89,18 +116,17 @@ __device__ __forceinline__ void butterflies(float* v, int b, bool upper) {
   }
 }
 
+// tile_ok: the row phase found every nonzero value of the tile >= 2^-103
+// (uniform over the work-group).
 __device__ __forceinline__ void column_wht(const uint8_t* lds, int col, int half, int b,
-                                           float* v) {
-  uint32_t lo = 0xffffffffu;  // min over (|bits| - 1): zero wraps to the top
+                                           bool tile_ok, float* v) {
 #pragma unroll
   for (int r = 0; r < kHalf; ++r) {
     const uint32_t h =
         *reinterpret_cast<const uint16_t*>(lds + (kHalf * half + r) * kRowBytes + 2 * col);
-    lo = min(lo, (h & 0x7fffu) - 1u);
     v[r] = __uint_as_float(h << 16);
   }
-  // 0x0C00 is the bf16 pattern of 2^-103
-  if (__any(lo < 0x0C00u - 1u)) {
+  if (!tile_ok) {
 #pragma unroll
     for (int r = 0; r < kHalf; ++r) v[r] = flush(v[r]);
     butterflies<true>(v, b, half != 0);
@@ -118,6 +144,7 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
   constexpr int kTrBytes = 16 * kTrStride * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kTileBytes > kTrBytes ? kTileBytes : kTrBytes];
   __shared__ float wmax[4];
+  __shared__ int wok[4];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t m0 = (int64_t)blockIdx.y * kRows, c0 = (int64_t)blockIdx.x * kCols;
   const int64_t nb = N / 64;
@@ -131,32 +158,49 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
   u32x4 raw[kRows / 16];
 #pragma unroll
   for (int i = 0; i < kRows / 16; ++i) raw[i] = load_vec(dy, N, m0, colv, rb + 16 * i);
+  u16x2 lo = {0xffff, 0xffff};
+#pragma unroll
+  for (int i = 0; i < kRows / 16; ++i) lo = tiny_min(lo, raw[i]);
+  const bool wave_tiny_ok = __all(tiny_ok(lo));
+  const bool fast = wave_tiny_ok && __all(steps_ok(s8));
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < kRows / 16; ++i) {
     const int r = rb + 16 * i;
     st16(lds + r * kRowBytes + 16 * cg, raw[i]);
     float f[8];
-    unpack_bf16x8(raw[i], f);
+    if (fast) {
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      f[e] = fabs_bits(fmul(f[e], s8[e]));
-      mx = fmaxf(mx, f[e]);
+      for (int k = 0; k < 4; ++k) {
+        f[2 * k] = fabs_bits(__uint_as_float(w[k] << 16) * s8[2 * k]);
+        f[2 * k + 1] = fabs_bits(__uint_as_float(w[k] & 0xffff0000u) * s8[2 * k + 1]);
+      }
+    } else {
+      unpack_bf16x8(raw[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = fabs_bits(fmul(f[e], s8[e]));
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, f[e]);
     const float node = wave_tree_partial<false>(reg_tree<false, 8>(f), 8);
     if ((cg & 7) == 0 && colv < N) part_g[(m0 + r) * nb + colv / 64] = node;
   }
   mx = wave_max(mx);
-  if (lane == 0) wmax[wave] = mx;
+  if (lane == 0) {
+    wmax[wave] = mx;
+    wok[wave] = wave_tiny_ok ? 1 : 0;
+  }
   __syncthreads();
   if (t == 0)
     bmax[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] =
         fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const bool tile_ok = wok[0] && wok[1] && wok[2] && wok[3];
 
   // column phase
   const int ccol = 32 * wave + (lane & 31), half = lane >> 5;
   float v[kHalf];
-  column_wht(lds, ccol, half, b, v);
+  column_wht(lds, ccol, half, b, tile_ok, v);
   __syncthreads();  // every column read: the tile memory is reused below
   // |v| to row order, 16 rows at a time: the lanes owning rows
   // 16p .. 16p+15 (half p / 4) write them, then lane L reads row L >> 3,
@@ -195,6 +239,7 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
                                                   int8_t* __restrict__ q_g,
                                                   int8_t* __restrict__ q_vt) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kRows * kRowBytes];
+  __shared__ int wok[4];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t m0 = (int64_t)blockIdx.y * kRows, c0 = (int64_t)blockIdx.x * kCols;
   const float r_g = sr4[1], r_v = sr4[3];
@@ -207,24 +252,42 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
   u32x4 raw[kRows / 16];
 #pragma unroll
   for (int i = 0; i < kRows / 16; ++i) raw[i] = load_vec(dy, N, m0, colv, rb + 16 * i);
+  u16x2 lo = {0xffff, 0xffff};
+#pragma unroll
+  for (int i = 0; i < kRows / 16; ++i) lo = tiny_min(lo, raw[i]);
+  const bool wave_tiny_ok = __all(tiny_ok(lo));
+  const bool fast = wave_tiny_ok && __all(steps_ok(s8));
 #pragma unroll
   for (int i = 0; i < kRows / 16; ++i) {
     const int r = rb + 16 * i;
     st16(lds + r * kRowBytes + 16 * cg, raw[i]);
     if (colv < N) {
       float f[8];
-      unpack_bf16x8(raw[i], f);
+      if (fast) {
+        const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f[2 * k] = __uint_as_float(w[k] << 16) * s8[2 * k];
+          f[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u) * s8[2 * k + 1];
+        }
+      } else {
+        unpack_bf16x8(raw[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = fmul(f[e], s8[e]);
+      }
       uint32_t p[2] = {0, 0};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        p[e >> 2] |= (uint32_t)(quant_code(fmul(f[e], s8[e]), r_g) & 0xff) << (8 * (e & 3));
+        p[e >> 2] |= (uint32_t)(quant_code(f[e], r_g) & 0xff) << (8 * (e & 3));
       *reinterpret_cast<uint2*>(q_g + (m0 + r) * N + colv) = make_uint2(p[0], p[1]);
     }
   }
+  if (lane == 0) wok[wave] = wave_tiny_ok ? 1 : 0;
   __syncthreads();
+  const bool tile_ok = wok[0] && wok[1] && wok[2] && wok[3];
   const int ccol = 32 * wave + (lane & 31), half = lane >> 5;
   float v[kHalf];
-  column_wht(lds, ccol, half, b, v);
+  column_wht(lds, ccol, half, b, tile_ok, v);
   const int64_t col = c0 + ccol;
   if (col >= N) return;
 #pragma unroll
