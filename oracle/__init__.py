@@ -72,6 +72,10 @@ def lib():
         L.orc_wht_fp_rows_quant.restype = i32
         L.orc_wht_fp_rows_quant.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp]
         L.orc_qgemm_bwd_dx_wht.restype = i32
+        L.orc_exp_f.restype = f32
+        L.orc_exp_f.argtypes = [f32]
+        L.orc_attn_fwd.restype = i32
+        L.orc_attn_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp]
         L.orc_qgemm_bwd_dx_wht.argtypes = [vp, i32, vp, vp, i64, i64, i64, i32, vp, vp, vp]
         L.orc_qgemm_bwd_dw_wht.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp, vp]
         L.orc_rmsnorm_fwd.restype = i32
@@ -287,6 +291,26 @@ def qgemm_bwd_dx_wht(dy, s_w, q_w, b: int):
     flags = lib().orc_qgemm_bwd_dx_wht(_p(dy), _dtype_code(dy), _p(sw), _p(q_w), M, N, K, b,
                                        _p(dx), _p(sg), _p(sh))
     return dx, sg[0], sh[0], flags
+
+
+def exp_f(x: float) -> np.float32:
+    """The attention softmax's binary32 exp (x <= 0)."""
+    return np.float32(lib().orc_exp_f(x))
+
+
+def attn_fwd(q, k, v, window=None):
+    """Attention forward with an int8 P.V product.  q [Hq][T][d], k, v
+    [Hkv][T][d] bf16 bit patterns (uint16); window None = plain causal.
+    Returns (o [Hq][T][d] fp32, flags)."""
+    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    o = np.empty((Hq, T, d), np.float32)
+    w = T if window is None else int(window)
+    flags = lib().orc_attn_fwd(_p(q), _p(k), _p(v), Hq, Hkv, T, d, w, _p(o))
+    if flags < 0:
+        raise ValueError("attn_fwd: unsupported shape")
+    return o, flags
 
 
 def rmsnorm_fwd(x, g, eps: float = 1e-6):

@@ -531,6 +531,157 @@ int orc_qgemm_bwd_dx_wht(const void* dy, int dtype, const float* s_w,
 }
 
 /* ------------------------------------------------------------------------
+ * Attention forward with an int8 P.V product (a variant) -- §3.2 "int8
+ * computation": inside flash attention the P.V product quantises the
+ * attention weights and the values to int8 per block and multiplies on
+ * int8 tensor cores, while the QK^T logits and the softmax stay in higher
+ * precision.  §3.1 gives the shape: grouped-query attention (query head h
+ * reads key/value head h / (Hq / Hkv)), causal, with a sliding window.
+ *
+ * Every step below is one rounded, flushed binary32 operation, in order:
+ *   S_ij = fl(dot_ij * c),  c = fl(1 / fl(sqrt(d))),
+ *          dot_ij = fl(... fl(fl(q_0 k_0) + fl(q_1 k_1)) ... + fl(q_d-1 k_d-1))
+ *          (sequential over e; bf16 products are exact)
+ *   key j is visible from query i iff i - window < j <= i
+ *   key blocks of 64, ascending; per row: m = max(m, block max of S)
+ *   (order-free), a = exp_f(m_old - m) (0 when m_old = -inf),
+ *   p_ij = exp_f(S_ij - m) (0 for a hidden key),
+ *   l = fl(fl(l * a) + tree_j p_ij)   (canonical pairwise tree over the 64)
+ *   P tile (64 queries x 64 keys): s_p = fl(max p * fl(1/127)),
+ *   V block (64 keys x d): s_v = fl(max |v| * fl(1/127)); codes
+ *   clamp(rint(fl(x * fl(1/s))), -127, 127) (0 when s = 0);
+ *   o_ie = fl(fl(o_ie * a) + fl(fl(sum_j qp_ij qv_je) * fl(s_p * s_v)))
+ *   (exact integer sum), and at the end o_ie = fl(o_ie * fl(1 / l)).
+ * A row with no visible key in a block leaves m, l, o unchanged.
+ * ---------------------------------------------------------------------- */
+#define ATT_BLK 64
+
+/* exp for x <= 0: Cody-Waite reduction x = n ln2 + r (ln2 split in a
+ * 15-bit head and a tail, so n * head is exact), a degree-7 Taylor
+ * polynomial of e^r in Horner form, then the exact scaling by 2^n; each
+ * step one rounded, flushed binary32 operation.  -inf and x < -104 give 0. */
+float orc_exp_f(float x) {
+  if (!(x >= -104.0f)) return 0.0f; /* -inf too */
+  const float inv_ln2 = u2f(0x3fb8aa3bu); /* fl(1/ln 2) */
+  const float ln2_hi = u2f(0x3f317200u);  /* 0.693145751953125 */
+  const float ln2_lo = u2f(0x35bfbe8eu);  /* fl(ln 2 - ln2_hi) */
+  float n = rintf(fmul(x, inv_ln2));
+  float r = fsub(fsub(x, fmul(n, ln2_hi)), fmul(n, ln2_lo));
+  float c[8];
+  float fact = 1.0f;
+  for (int i = 0; i < 8; i++) {
+    if (i > 0) fact = fmul(fact, (float)i); /* i! exact for i <= 7 */
+    c[i] = fdiv(1.0f, fact);
+  }
+  float p = c[7];
+  for (int i = 6; i >= 0; i--) p = fadd(fmul(p, r), c[i]);
+  int ni = (int)n;
+  if (ni < -126) return 0.0f;
+  return fmul(p, u2f((uint32_t)(ni + 127) << 23));
+}
+
+static float att_quant_scale(float amax, float* r) {
+  float s = fmul(amax, fdiv(1.0f, 127.0f));
+  *r = (s == 0.0f) ? 0.0f : fdiv(1.0f, s);
+  return s;
+}
+
+int orc_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t Hq,
+                 int64_t Hkv, int64_t T, int64_t d, int64_t window, float* o) {
+  if (Hkv <= 0 || Hq % Hkv || T % ATT_BLK) return -1;
+  const int64_t group = Hq / Hkv, nb = T / ATT_BLK;
+  const float c = fdiv(1.0f, fsqrt((float)d));
+  int flags = 0;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic) collapse(2)
+#endif
+  for (int64_t h = 0; h < Hq; h++) {
+    for (int64_t qb = 0; qb < nb; qb++) {
+      const int64_t hk = h / group;
+      const uint16_t* Q = q + h * T * d;
+      const uint16_t* K = k + hk * T * d;
+      const uint16_t* V = v + hk * T * d;
+      float* O = o + h * T * d;
+      float S[ATT_BLK][ATT_BLK], P[ATT_BLK][ATT_BLK], m[ATT_BLK], l[ATT_BLK];
+      float* acc = (float*)malloc((size_t)(ATT_BLK * d) * sizeof(float));
+      int8_t* qv = (int8_t*)malloc((size_t)(ATT_BLK * d));
+      assert(acc && qv);
+      for (int i = 0; i < ATT_BLK; i++) { m[i] = -INFINITY; l[i] = 0.0f; }
+      for (int64_t x = 0; x < ATT_BLK * d; x++) acc[x] = 0.0f;
+      for (int64_t kb = 0; kb <= qb; kb++) {
+        /* a block no query of this block sees changes nothing: skipped */
+        const int64_t i_lo = qb * ATT_BLK, j_hi = kb * ATT_BLK + ATT_BLK - 1;
+        if (j_hi <= i_lo - window) continue;
+        int any[ATT_BLK];
+        float bmax[ATT_BLK];
+        for (int i = 0; i < ATT_BLK; i++) {
+          const int64_t gi = qb * ATT_BLK + i;
+          any[i] = 0;
+          bmax[i] = -INFINITY;
+          for (int j = 0; j < ATT_BLK; j++) {
+            const int64_t gj = kb * ATT_BLK + j;
+            if (gj > gi || gj <= gi - window) { S[i][j] = -INFINITY; continue; }
+            float dot = 0.0f;
+            for (int64_t e = 0; e < d; e++)
+              dot = fadd(dot, fmul(orc_bf16_to_f32(Q[gi * d + e]), orc_bf16_to_f32(K[gj * d + e])));
+            S[i][j] = fmul(dot, c);
+            any[i] = 1;
+            if (S[i][j] > bmax[i]) bmax[i] = S[i][j];
+          }
+        }
+        float alpha[ATT_BLK];
+        float pmax = 0.0f;
+        for (int i = 0; i < ATT_BLK; i++) {
+          if (!any[i]) { alpha[i] = 1.0f; for (int j = 0; j < ATT_BLK; j++) P[i][j] = 0.0f; continue; }
+          const float mn = bmax[i] > m[i] ? bmax[i] : m[i];
+          alpha[i] = (m[i] == -INFINITY) ? 0.0f : orc_exp_f(fsub(m[i], mn));
+          for (int j = 0; j < ATT_BLK; j++) {
+            P[i][j] = (S[i][j] == -INFINITY) ? 0.0f : orc_exp_f(fsub(S[i][j], mn));
+            if (P[i][j] > pmax) pmax = P[i][j];
+          }
+          float leaves[ATT_BLK];
+          for (int j = 0; j < ATT_BLK; j++) leaves[j] = P[i][j];
+          l[i] = fadd(fmul(l[i], alpha[i]), tree_inplace(leaves, ATT_BLK));
+          m[i] = mn;
+        }
+        /* the P tile's and the V block's int8 codes */
+        float rp, rv, vmax = 0.0f;
+        const float sp = att_quant_scale(pmax, &rp);
+        for (int j = 0; j < ATT_BLK; j++)
+          for (int64_t e = 0; e < d; e++) {
+            const float a = fabs_(orc_bf16_to_f32(V[(kb * ATT_BLK + j) * d + e]));
+            if (a > vmax) vmax = a;
+          }
+        const float sv = att_quant_scale(vmax, &rv);
+        for (int j = 0; j < ATT_BLK; j++)
+          for (int64_t e = 0; e < d; e++)
+            qv[j * d + e] = orc_quant1(orc_bf16_to_f32(V[(kb * ATT_BLK + j) * d + e]), rv);
+        const float cs = fmul(sp, sv);
+        for (int i = 0; i < ATT_BLK; i++) {
+          if (!any[i]) continue;
+          int8_t qp[ATT_BLK];
+          for (int j = 0; j < ATT_BLK; j++) qp[j] = orc_quant1(P[i][j], rp);
+          for (int64_t e = 0; e < d; e++) {
+            int32_t s32 = 0;
+            for (int j = 0; j < ATT_BLK; j++) s32 += (int32_t)qp[j] * (int32_t)qv[j * d + e];
+            const float contrib = fmul((float)s32, cs);
+            acc[i * d + e] = fadd(fmul(acc[i * d + e], alpha[i]), contrib);
+          }
+        }
+      }
+      for (int i = 0; i < ATT_BLK; i++) {
+        const float il = fdiv(1.0f, l[i]);
+        for (int64_t e = 0; e < d; e++) O[(qb * ATT_BLK + i) * d + e] = fmul(acc[i * d + e], il);
+        if (!isfinite(l[i])) flags |= ORC_FLAG_NONFINITE;
+      }
+      free(acc);
+      free(qv);
+    }
+  }
+  return flags;
+}
+
+/* ------------------------------------------------------------------------
  * RMSNorm -- §3.1 "RMSNorm" (pre-norm, no bias) and the precision note
  * (normalisation in FP32, parameters BF16): y = x * rsqrt(mean(x^2)+eps)*g
  * with a correctly rounded sqrt followed by a reciprocal.

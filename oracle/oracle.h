@@ -140,6 +140,14 @@ int orc_qgemm_bwd_dw_wht(const int8_t* qx, const float* s_x, const void* dy,
                          int dtype, int64_t M, int64_t N, int64_t K, int b,
                          float* dw, float* s_u_out, float* s_v_out);
 
+/* Attention forward with an int8 P.V product (variant), definitions in
+ * oracle.c: q [Hq][T][d], k, v [Hkv][T][d] bf16 patterns, o [Hq][T][d]
+ * fp32; T % 64 == 0, Hq % Hkv == 0; window >= T is plain causal.
+ * Returns flags (or -1 for a shape it does not take). */
+float orc_exp_f(float x);
+int orc_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t Hq,
+                 int64_t Hkv, int64_t T, int64_t d, int64_t window, float* o);
+
 /* Rotated input-gradient GEMM (variant): g = fl(dy * s_w[n]) rotated in
  * fp32 along n per row and aligned block of b, per-tensor LSQ -> q_g, s_g;
  * q_w [N][K] rotated exactly along n and requantised -> q_h, s_h;

@@ -69,6 +69,19 @@ MUTANTS = {
                              "float c = fmul(orc_flush(s_g), orc_flush(s_h));"),
     "dx_wht_weights_unrotated": ("orc_wht_int_quant(qw, N, K, b, q_h, &s_h, NULL);",
                                  "orc_wht_int_quant(qw, N, K, 1, q_h, &s_h, NULL);"),
+    "attn_window_off_by_one": ("if (gj > gi || gj <= gi - window) { S[i][j] = -INFINITY; continue; }",
+                               "if (gj > gi || gj < gi - window) { S[i][j] = -INFINITY; continue; }"),
+    "attn_sees_next_key": ("if (gj > gi || gj <= gi - window) { S[i][j] = -INFINITY; continue; }",
+                           "if (gj > gi + 1 || gj <= gi - window) { S[i][j] = -INFINITY; continue; }"),
+    "attn_gqa_modulo": ("const int64_t hk = h / group;", "const int64_t hk = h % Hkv;"),
+    "attn_l_not_rescaled": ("l[i] = fadd(fmul(l[i], alpha[i]), tree_inplace(leaves, ATT_BLK));",
+                            "l[i] = fadd(l[i], tree_inplace(leaves, ATT_BLK));"),
+    "attn_o_not_rescaled": ("acc[i * d + e] = fadd(fmul(acc[i * d + e], alpha[i]), contrib);",
+                            "acc[i * d + e] = fadd(acc[i * d + e], contrib);"),
+    "attn_no_logit_scale": ("S[i][j] = fmul(dot, c);", "S[i][j] = dot;"),
+    "attn_codes_255": ("float s = fmul(amax, fdiv(1.0f, 127.0f));", "float s = fmul(amax, fdiv(1.0f, 255.0f));"),
+    "exp_drops_a_term": ("for (int i = 6; i >= 0; i--) p = fadd(fmul(p, r), c[i]);",
+                         "for (int i = 5; i >= 0; i--) p = fadd(fmul(p, r), c[i]);"),
     "clip_always_scales": ("*clip = norm > max_norm ? fdiv(orc_flush(max_norm), norm) : 1.0f;",
                            "*clip = fdiv(orc_flush(max_norm), norm);"),
 }

@@ -1052,3 +1052,119 @@ def test_dx_wht_reduces_error_on_heavy_tails(orc, syn):
             assert e1 < 0.7 * e0 and e1 < 0.07, (e0, e1)
         else:
             assert e0 < 0.06 and e1 < 0.07, (e0, e1)
+
+
+# --------------------------------------------------------------------------
+# attention forward with an int8 P.V product
+# --------------------------------------------------------------------------
+def _bf16(a):
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _wide(h):
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_exp_f_within_bound(orc):
+    """The softmax's binary32 exp: within 2 ulp of e^x over the normal
+    range, exact at 0, 0 below the range, monotone."""
+    xs = np.linspace(-87.0, 0.0, 40001).astype(np.float32)
+    got = np.array([orc.exp_f(float(x)) for x in xs], np.float32)
+    ref = np.exp(xs.astype(np.float64))
+    assert np.all(np.abs(got - ref) <= 2 * np.spacing(ref.astype(np.float32)))
+    assert np.all(np.diff(got) >= 0)
+    assert orc.exp_f(0.0) == 1.0 and orc.exp_f(-np.inf) == 0.0 and orc.exp_f(-104.5) == 0.0
+    for kk in (-1, -10, -60):  # near x = k ln 2 the reduction leaves r ~ 0
+        x = np.float32(kk * math.log(2))
+        assert abs(float(orc.exp_f(float(x))) / math.exp(float(x)) - 1) < 2 ** -23
+
+
+@pytest.mark.parametrize("Hq,Hkv,T,d,window", [(4, 1, 256, 128, None), (2, 2, 192, 64, 64),
+                                               (4, 2, 128, 128, 100)])
+def test_attn_fp64_bound(orc, Hq, Hkv, T, d, window):
+    """Against fp64 softmax attention on the same bf16 inputs: only the int8
+    P.V product is coarse (codes of P in [0, 127], of V per 64-key block)."""
+    rng = np.random.default_rng(Hq * 100 + T)
+    q = _bf16(rng.standard_normal((Hq, T, d)))
+    k = _bf16(rng.standard_normal((Hkv, T, d)))
+    v = _bf16(rng.standard_normal((Hkv, T, d)))
+    o, fl = orc.attn_fwd(q, k, v, window)
+    Q, K, V = (_wide(a).astype(np.float64) for a in (q, k, v))
+    w = T if window is None else window
+    i, j = np.meshgrid(np.arange(T), np.arange(T), indexing="ij")
+    vis = (j <= i) & (j > i - w)
+    ref = np.empty_like(o, dtype=np.float64)
+    for h in range(Hq):
+        S = Q[h] @ K[h // (Hq // Hkv)].T / math.sqrt(d)
+        S[~vis] = -np.inf
+        P = np.exp(S - S.max(1, keepdims=True))
+        ref[h] = (P / P.sum(1, keepdims=True)) @ V[h // (Hq // Hkv)]
+    assert fl == 0
+    assert np.linalg.norm(o - ref) / np.linalg.norm(ref) < 0.03
+
+
+def test_attn_window_one_closed_form(orc):
+    """window = 1: each query sees only its own key, p = 1, l = 1, so
+    o = fl(fl(127 * qv) * fl(s_p * s_v)) with s_p = fl(1 * fl(1/127)) and the
+    V block's own absmax step (numpy binary32 arithmetic)."""
+    rng = np.random.default_rng(3)
+    T, d = 128, 64
+    q = _bf16(rng.standard_normal((1, T, d)))
+    k = _bf16(rng.standard_normal((1, T, d)))
+    v = _bf16(rng.standard_normal((1, T, d)))
+    o, _ = orc.attn_fwd(q, k, v, 1)
+    f = np.float32
+    inv127 = f(1) / f(127)
+    sp = f(1) * inv127
+    V = _wide(v)[0]
+    want = np.empty((T, d), np.float32)
+    for b in range(T // 64):
+        blk = V[64 * b:64 * b + 64]
+        sv = f(np.abs(blk).max()) * inv127
+        qv = np.clip(np.rint(blk * (f(1) / sv)), -127, 127)
+        assert np.rint(f(1) * (f(1) / sp)) == 127
+        want[64 * b:64 * b + 64] = (f(127) * qv.astype(np.float32)) * (sp * sv)
+    assert np.array_equal(o[0], want)
+
+
+def test_attn_uniform_closed_form(orc):
+    """q = 0: every visible logit is 0, p = 1, the rescale factor is 1, and
+    o is the running sum of each block's dequantised integer product over
+    the visible keys divided by their count (numpy binary32, same order)."""
+    rng = np.random.default_rng(4)
+    T, d = 192, 64
+    q = np.zeros((1, T, d), np.uint16)
+    k = _bf16(rng.standard_normal((1, T, d)))
+    v = _bf16(rng.integers(-3, 4, size=(1, T, d)).astype(np.float32))
+    o, _ = orc.attn_fwd(q, k, v)
+    f = np.float32
+    inv127 = f(1) / f(127)
+    sp = f(1) * inv127
+    V = _wide(v)[0]
+    want = np.empty((T, d), np.float32)
+    for i in range(T):
+        acc = np.zeros(d, np.float32)
+        for b in range(i // 64 + 1):
+            blk = V[64 * b:64 * b + 64]
+            sv = f(np.abs(blk).max()) * inv127
+            qv = np.clip(np.rint(blk * (f(1) / sv)), -127, 127).astype(np.int64)
+            hi = min(64, i - 64 * b + 1)
+            s32 = 127 * qv[:hi].sum(0)
+            acc = acc * f(1) + s32.astype(np.float32) * (sp * sv)
+        want[i] = acc * (f(1) / f(i + 1))
+    assert np.array_equal(o[0], want)
+
+
+def test_attn_gqa_mapping(orc):
+    """Query head h reads key/value head h / (Hq / Hkv)."""
+    rng = np.random.default_rng(5)
+    Hq, Hkv, T, d = 4, 2, 128, 64
+    q = _bf16(rng.standard_normal((Hq, T, d)))
+    k = _bf16(rng.standard_normal((Hkv, T, d)))
+    v = _bf16(rng.standard_normal((Hkv, T, d)))
+    o, _ = orc.attn_fwd(q, k, v, 80)
+    for h in range(Hq):
+        g = h // 2
+        o1, _ = orc.attn_fwd(q[h:h + 1], k[g:g + 1], v[g:g + 1], 80)
+        assert np.array_equal(o[h], o1[0])
