@@ -27,7 +27,7 @@ SYMBOLS = [
     "brq_workspace_size", "brq_quantize_lsq", "brq_quantize_lsq_exact", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
     "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
     "brq_qgemm_fwd_ex", "brq_qgemm_bwd_dx_ex",
-    "brq_quantize_dy_bwd", "brq_qgemm_bwd_dx_wht", "brq_wht_quant_dy_rows",
+    "brq_quantize_dy_bwd", "brq_qgemm_bwd_dx_wht", "brq_wht_quant_dy_rows", "brq_attn_fwd",
     "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm",
     "brq_hash_workspace_size", "brq_hash_state", "brq_hash_digests_workspace_size",
     "brq_hash_tensor_digests", "brq_hash_combine", "brq_adamw_bias_corrections",
@@ -91,6 +91,8 @@ def lib():
         L.brq_qgemm_bwd_dx_wht.restype = i32
         L.brq_qgemm_bwd_dx_wht.argtypes = [vp, i32, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp,
                                            sz, vp, vp, vp]
+        L.brq_attn_fwd.restype = i32
+        L.brq_attn_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp]
         L.brq_wht_quant_dy_rows.restype = i32
         L.brq_wht_quant_dy_rows.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, sz, vp, vp,
                                             vp]
@@ -361,6 +363,25 @@ def qgemm_bwd_dx_wht(dy, s_w, q_w, block, tune=None, out=None, ws=None, flags=No
     q_ht = w[:K * N].view(torch.int8).view(K, N).clone()
     q_g = w[off:off + M * N].view(torch.int8).view(M, N).clone()
     return dx, s_g, s_h, q_ht, q_g
+
+
+def attn_fwd(q, k, v, window=None, out=None, flags=None):
+    """Attention forward with an int8 P.V product.  q [Hq][T][d], k, v
+    [Hkv][T][d] bf16; window None = plain causal.  Returns o [Hq][T][d] fp32."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+        if t.dtype != torch.bfloat16 or t.dim() != 3:
+            raise BrqError(f"{n}: expected bf16 [heads][T][d]")
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    if tuple(k.shape) != (Hkv, T, d) or tuple(v.shape) != (Hkv, T, d):
+        raise BrqError("k / v: expected [Hkv][T][d] like q")
+    o = _out(out, (Hq, T, d), torch.float32, "o") if out is not None else \
+        torch.empty((Hq, T, d), dtype=torch.float32, device=q.device)
+    w = max(T, 1) if window is None else int(window)
+    _check(lib().brq_attn_fwd(_ptr(q), _ptr(k), _ptr(v), Hq, Hkv, T, d, w, _ptr(o), _ptr(flags),
+                              None, _stream()), "attn_fwd")
+    return o
 
 
 def wht_quant_dy_rows(dy, s_w, block, tune=None, ws=None, flags=None, out=None):

@@ -305,6 +305,20 @@ int brq_qgemm_bwd_dw_wht(const int8_t* q_x, const float* s_x, const void* dy, in
                       tune, stream);
 }
 
+int brq_attn_fwd(const void* q, const void* k, const void* v, int64_t Hq, int64_t Hkv, int64_t T,
+                 int64_t d, int64_t window, float* o, int32_t* dflags, const brq_tune* tune,
+                 void* stream) {
+  (void)tune;
+  if (Hq < 0 || Hkv <= 0 || T < 0 || window < 1) return BRQ_E_SHAPE;
+  if (Hq % Hkv || T % 64 || (d != 64 && d != 128)) return BRQ_E_UNSUPPORTED;
+  if (Hq * T > 0 && (!q || !k || !v || !o)) return BRQ_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BRQ_E_ALIGN;
+  if (Hq == 0 || T == 0) return BRQ_OK;
+  if (T / 64 > 65535) return BRQ_E_UNSUPPORTED;
+  return hip_status(attn_fwd((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, Hq, Hkv,
+                             T, d, window, o, dflags, as_stream(stream)));
+}
+
 int brq_wht_quant_dy_rows(const void* dy, int dy_dtype, int64_t M, int64_t N, const float* s_w,
                           int block, int8_t* q_g, float* s_g, void* ws, size_t ws_bytes,
                           int32_t* dflags, const brq_tune* tune, void* stream) {

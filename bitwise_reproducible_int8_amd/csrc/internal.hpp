@@ -63,6 +63,11 @@ hipError_t quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
 
 // Exact-sum statistic (exact.hip): per-tensor S and max |v| into out2[0..1]
 // (two launches), and the per-row quantiser with exact row statistics.
+// Attention forward with an int8 P.V product (attn.hip).
+hipError_t attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t Hq,
+                    int64_t Hkv, int64_t T, int64_t d, int64_t window, float* o, int32_t* dflags,
+                    hipStream_t s);
+
 // Rows rotation of dY * s_w and its codes (dxwht.hip).
 size_t wht_rows_ws(int64_t M, int64_t N);
 hipError_t wht_rows_quant(const void* dy, int dtype, int64_t M, int64_t N, const float* s_w,

@@ -259,6 +259,33 @@ int brq_wht_quant_dy_rows(const void* dy, int dy_dtype, int64_t M, int64_t N,
                           const struct brq_tune* tune, void* stream);
 
 /* ---------------------------------------------------------------------
+ * attn_fwd -- attention forward with an int8 P.V product (a variant:
+ * §3.2 "int8 computation" quantises the attention weights and values to
+ * int8 per block for the P.V product, QK^T and softmax in higher
+ * precision; §3.1: grouped-query attention, causal, sliding window).
+ * q [Hq][T][d], k, v [Hkv][T][d] bf16; o [Hq][T][d] fp32.  Query head h
+ * reads key/value head h / (Hq / Hkv); key j is visible from query i iff
+ * i - window < j <= i (window >= T: plain causal).  Per 64-query block and
+ * ascending 64-key blocks, every step one rounded, flushed binary32 op:
+ *     S_ij = fl(dot_ij * c), c = fl(1/fl(sqrt d)), dot_ij sequential over
+ *            e of the exact bf16 products;
+ *     m = max(m, block max); a = exp_f(m_old - m) (0 while m_old = -inf);
+ *     p = exp_f(S - m) (0 for a hidden key); l = fl(fl(l * a) + tree(p));
+ *     s_p = fl(max_tile p * fl(1/127)), s_v = fl(max_block |v| * fl(1/127));
+ *     codes clamp(rint(fl(x * fl(1/s))), -127, 127);
+ *     o = fl(fl(o * a) + fl(fl(sum_j qp_ij qv_je) * fl(s_p * s_v)));
+ *     finally o = fl(o * fl(1/l)).
+ * exp_f: Cody-Waite reduction by ln 2 (head 0x3f317200, tail 0x35bfbe8e,
+ * fl(1/ln 2) = 0x3fb8aa3b), n = rint(fl(x / ln 2)), degree-7 Taylor
+ * polynomial in Horner form with coefficients fl(1/i!), times 2^n; 0 for
+ * x < -104 or n < -126.  A row with no visible key in a block is left as
+ * it was.  Shapes: d = 64 or 128, T % 64 == 0, Hq % Hkv == 0.
+ * --------------------------------------------------------------------- */
+int brq_attn_fwd(const void* q, const void* k, const void* v, int64_t Hq,
+                 int64_t Hkv, int64_t T, int64_t d, int64_t window, float* o,
+                 int32_t* dflags, const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
  * quantize_dy_bwd -- both int8 codes of the upstream gradient for the two
  * straight-through gradient GEMMs (§3.2 "int8 computation"), in two passes
  * over dY.  Bit-identical to the two calls it fuses:
