@@ -32,6 +32,8 @@ if ROOT not in sys.path:
 METRIC = "bitwise-exact W8A8 QAT linear fwd+bwd int8 TOPS (% MFMA peak), tokens/s"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+# binary32 vector FMAs (not packed): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+PEAK_FP32_FMA = 256 * 4 * 16 * 2.4e9
 BLOCK = 128
 EPS = 1e-6
 
@@ -466,6 +468,43 @@ def main():
         "note": "the 7 weight quantisations (with transposed codes) and 7 forward GEMMs with one "
                 "step per weight tensor; not part of value"}
     del wpt, ypt, wws
+
+    # Variant (not part of value): the layer's attention forward with an int8
+    # P.V product -- 8 windows x 16 query heads over 8 x 4 key/value heads,
+    # 4096 tokens, head dim 128 -- with the 512-token sliding window and
+    # fully causal.  Logit work is binary32 fused multiply-adds on the vector
+    # units (exact bf16 products, sequential order), so its roofline is the
+    # vector FMA rate.
+    Ta, Da, Hqa, Hkva = 4096, 128, 8 * 16, 8 * 4
+    g = torch.Generator(device="cpu").manual_seed(7)
+    qa = torch.randn((Hqa, Ta, Da), generator=g).to(dev, torch.bfloat16)
+    ka = torch.randn((Hkva, Ta, Da), generator=g).to(dev, torch.bfloat16)
+    va = torch.randn((Hkva, Ta, Da), generator=g).to(dev, torch.bfloat16)
+    oa = torch.empty((Hqa, Ta, Da), dtype=torch.float32, device=dev)
+    att = {}
+    for name, win in (("window_512", 512), ("causal", None)):
+        for _ in range(max(args.warmup, 1)):
+            brq.attn_fwd(qa, ka, va, win, out=oa)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            brq.attn_fwd(qa, ka, va, win, out=oa)
+        e1.record()
+        torch.cuda.synchronize()
+        a_ms = e0.elapsed_time(e1) / args.steps
+        w = Ta if win is None else win
+        # visible (query, key) pairs per head, counted by the 64 x 64 blocks
+        # the kernel computes (every block with a visible key)
+        nb = Ta // 64
+        blocks = sum(1 for qb in range(nb) for kb in range(qb + 1) if kb * 64 + 63 > qb * 64 - w)
+        fma = blocks * 64 * 64 * Da * Hqa
+        att[name] = {"ms": round(a_ms, 4), "logit_fma_per_s_T": round(fma / (a_ms * 1e-3) / 1e12, 2),
+                     "frac_vector_fma_peak": round(fma / (a_ms * 1e-3) / PEAK_FP32_FMA, 4)}
+    variants["attention_fwd_int8_pv"] = dict(att, note=(
+        "8 windows x 16 query heads (4 key/value heads each), 4096 tokens, head dim 128; "
+        "logits as binary32 FMAs on the vector units against their peak "
+        f"({PEAK_FP32_FMA / 1e12:.1f} T FMA/s); not part of value"))
+    del qa, ka, va, oa
 
     cpu = None
     if args.cpu_tokens > 0:

@@ -61,6 +61,32 @@ __device__ __forceinline__ float exp_f(float x) {
   return fmul(p, __uint_as_float((uint32_t)(ni + 127) << 23));
 }
 
+// The same value without the flushes when they cannot act: for x = 0 or
+// |x| >= 2^-100 the reduced argument r is 0 or at least 2^-100 in
+// magnitude (|x - n ln 2| for a binary32 x in [-104, 0] is never that
+// small otherwise), so every Horner product and sum is 0 or normal; only
+// the final scaling can land below 2^-126 and keeps its flush.
+__device__ __forceinline__ float exp_f_fast(float x) {
+  if (x != 0.0f && fabsf(x) < 0x1p-100f) return exp_f(x);
+  if (!(x >= -104.0f)) return 0.0f;
+  const float inv_ln2 = __uint_as_float(0x3fb8aa3bu);
+  const float ln2_hi = __uint_as_float(0x3f317200u);
+  const float ln2_lo = __uint_as_float(0x35bfbe8eu);
+  const float n = __builtin_rintf(x * inv_ln2);
+  const float r = (x - n * ln2_hi) - n * ln2_lo;
+  float p = 1.0f / 5040.0f;
+  p = p * r + 1.0f / 720.0f;
+  p = p * r + 1.0f / 120.0f;
+  p = p * r + 1.0f / 24.0f;
+  p = p * r + 1.0f / 6.0f;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  const int ni = (int)n;
+  if (ni < -126) return 0.0f;
+  return fmul(p, __uint_as_float((uint32_t)(ni + 127) << 23));
+}
+
 __device__ __forceinline__ int8_t code_of(float x, float r) { return (int8_t)quant_code(x, r); }
 
 // max over the 16 lanes of a row group (xor 1, 2, 4, 8: inside the group)
@@ -86,7 +112,8 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ q
   __shared__ int s_slow[2];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t qb = blockIdx.x, h = blockIdx.y, hk = h / group;
+  // the last query blocks see the most key blocks: they start first
+  const int64_t qb = (int64_t)gridDim.x - 1 - blockIdx.x, h = blockIdx.y, hk = h / group;
   const uint16_t* Q = q + (h * T + qb * kBlk) * D;
   const uint16_t* K = k + hk * T * D;
   const uint16_t* V = v + hk * T * D;
@@ -199,10 +226,10 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ q
     for (int a = 0; a < 4; ++a) {
       const bool any = bmax[a] != -INFINITY;
       const float mn = fmaxf(bmax[a], m[a]);
-      const float alpha = !any ? 1.0f : (m[a] == -INFINITY ? 0.0f : exp_f(fsub(m[a], mn)));
+      const float alpha = !any ? 1.0f : (m[a] == -INFINITY ? 0.0f : exp_f_fast(fsub(m[a], mn)));
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        pr[a][b] = (!any || s[a][b] == -INFINITY) ? 0.0f : exp_f(fsub(s[a][b], mn));
+        pr[a][b] = (!any || s[a][b] == -INFINITY) ? 0.0f : exp_f_fast(fsub(s[a][b], mn));
         pmax = fmaxf(pmax, pr[a][b]);
       }
       float node = fadd(fadd(pr[a][0], pr[a][1]), fadd(pr[a][2], pr[a][3]));
