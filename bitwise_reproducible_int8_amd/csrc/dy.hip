@@ -24,7 +24,7 @@
 //                 32w + (l & 31), tokens 64 (l >> 5) .. +63.  Butterfly
 //                 stages h = 1 .. 32 run in registers; stage 64 pairs lane l
 //                 with lane l ^ 32.  The |v| leaves go back through LDS to
-//                 row order, 16 rows at a time, to form node(6) per row and
+//                 row order, 64 rows at a time, to form node(6) per row and
 //                 64 columns.
 #include "device.hpp"
 #include "internal.hpp"
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
                                                   float* __restrict__ part_v,
                                                   float* __restrict__ bmax) {
   constexpr int kTileBytes = kRows * kRowBytes;
-  constexpr int kTrBytes = 16 * kTrStride * 4;
+  constexpr int kTrBytes = kHalf * kTrStride * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kTileBytes > kTrBytes ? kTileBytes : kTrBytes];
   __shared__ float wmax[4];
   __shared__ int wok[4];
@@ -202,32 +202,28 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
   float v[kHalf];
   column_wht(lds, ccol, half, b, tile_ok, v);
   __syncthreads();  // every column read: the tile memory is reused below
-  // |v| to row order, 16 rows at a time: the lanes owning rows
-  // 16p .. 16p+15 (half p / 4) write them, then lane L reads row L >> 3,
-  // columns 16 (L & 7) .. +15 (128 lanes cover 16 rows x 128 columns)
+  // |v| to row order, 64 rows at a time: the half-p lanes write their 64
+  // tokens, then lane t reads row t >> 2, columns 32 (t & 3) .. +31, and
+  // the lane pairs (t, t ^ 1) join their 32-column nodes into node(6)
   float* tr = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int p = 0; p < kRows / 16; ++p) {
-    if (half == p / 4) {
+  for (int p = 0; p < 2; ++p) {
+    if (half == p) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tr[i * kTrStride + ccol] = fabs_bits(v[16 * (p & 3) + i]);
+      for (int i = 0; i < kHalf; ++i) tr[i * kTrStride + ccol] = fabs_bits(v[i]);
     }
     __syncthreads();
-    if (t < 128) {
-      const int r = t >> 3, c16 = (t & 7) * 16;
-      float a[16];
+    const int r = t >> 2, c32 = (t & 3) * 32;
+    float a[32];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 x4 = *reinterpret_cast<const float4*>(&tr[r * kTrStride + c16 + 4 * q]);
-        a[4 * q] = x4.x; a[4 * q + 1] = x4.y; a[4 * q + 2] = x4.z; a[4 * q + 3] = x4.w;
-      }
-      float node = reg_tree<false, 16>(a);
-      // lanes 4k .. 4k+3 hold the four 16-column nodes of one 64-column run
-      node = node + dpp_xor1(node);  // non-negative leaves: no flush needed
-      node = node + dpp_xor2(node);
-      const int64_t cc = c0 + c16;
-      if ((t & 3) == 0 && cc < N) part_v[(m0 + 16 * p + r) * nb + cc / 64] = node;
+    for (int q = 0; q < 8; ++q) {
+      const float4 x4 = *reinterpret_cast<const float4*>(&tr[r * kTrStride + c32 + 4 * q]);
+      a[4 * q] = x4.x; a[4 * q + 1] = x4.y; a[4 * q + 2] = x4.z; a[4 * q + 3] = x4.w;
     }
+    float node = reg_tree<false, 32>(a);
+    node = node + dpp_xor1(node);  // non-negative leaves: no flush needed
+    const int64_t cc = c0 + c32;
+    if ((t & 1) == 0 && cc < N) part_v[(m0 + kHalf * p + r) * nb + cc / 64] = node;
     __syncthreads();
   }
 }
