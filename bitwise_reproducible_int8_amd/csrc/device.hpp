@@ -53,11 +53,10 @@ __device__ __forceinline__ float lsq_k2() { return __uint_as_float(0x3e35bb0au);
 
 // q = clamp(rint(fl(v * r)), -127, 127); v_rndne_f32 rounds half to even.
 // The product is not flushed: a subnormal v * r and its flushed zero both
-// round to the code 0.
+// round to the code 0.  The clamp is one median of three (exact for finite
+// and infinite values; a NaN product has no defined code).
 __device__ __forceinline__ int quant_code(float v, float r) {
-  float t = __builtin_rintf(v * r);
-  t = t > 127.0f ? 127.0f : t;
-  t = t < -127.0f ? -127.0f : t;
+  const float t = __builtin_amdgcn_fmed3f(__builtin_rintf(v * r), -127.0f, 127.0f);
   return (int)t;
 }
 
