@@ -47,6 +47,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two binary32 values rounded to bf16 (nearest even) by one conversion
+// instruction (v_cvt_pk_bf16_f32), packed lo | hi << 16.  For every input
+// that is not a NaN this is f32_to_bf16 of each (the instruction rounds to
+// nearest even in the default mode and keeps subnormals); a NaN gives a
+// quiet NaN whose payload may differ.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
 // LSQ factor 2 * fl(1/fl(sqrt(127))) as binary32 bits 0x3e35bb0a:
 // fl(sqrt(127)) = 0x41344f93, its binary32 reciprocal 0x3db5bb0a, times 2.
 __device__ __forceinline__ float lsq_k2() { return __uint_as_float(0x3e35bb0au); }

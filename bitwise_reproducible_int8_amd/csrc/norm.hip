@@ -30,7 +30,7 @@ template <>
 __device__ __forceinline__ u32x4 pack_out<uint16_t>(const float* y) {
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(y[2 * i]) | (f32_to_bf16(y[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) w[i] = pack2_bf16(y[2 * i], y[2 * i + 1]);
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 template <>

@@ -59,7 +59,7 @@ struct Hp {
 __device__ __forceinline__ u32x4 pack8_bf16(const float* f) {
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(f[2 * i]) | (f32_to_bf16(f[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) w[i] = pack2_bf16(f[2 * i], f[2 * i + 1]);
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 __device__ __forceinline__ u32x4 pack4_f32(const float* f) {
