@@ -257,14 +257,17 @@ __global__ __launch_bounds__(256) void k_dg_fold(const float* __restrict__ in, i
   const int64_t c = (((int64_t)blockIdx.x % col_blocks) * 256 + threadIdx.x) * 4;
   if (c >= D) return;
   float stk[kFoldLog + 1][4];
-#pragma unroll 1
+  // every load of the group first (one round trip), then the stack
+  float4 v4[1 << kFoldLog];
+#pragma unroll
   for (int i = 0; i < (1 << kFoldLog); ++i) {
     const int64_t p = q * (1 << kFoldLog) + i;
-    float val[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
-    if (p < P) {
-      const float4 v4 = *reinterpret_cast<const float4*>(in + p * D + c);
-      val[0] = v4.x; val[1] = v4.y; val[2] = v4.z; val[3] = v4.w;
-    }
+    v4[i] = p < P ? *reinterpret_cast<const float4*>(in + p * D + c)
+                  : make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+  }
+#pragma unroll
+  for (int i = 0; i < (1 << kFoldLog); ++i) {
+    float val[4] = {v4[i].x, v4[i].y, v4[i].z, v4[i].w};
     bool carry = true;
 #pragma unroll
     for (int l = 0; l <= kFoldLog; ++l) {
