@@ -185,6 +185,64 @@ def cpu_baseline(tokens):
             "tokens_per_s": round(M / dt, 3), "seconds": round(dt, 3)}
 
 
+def norm_workload(torch, brq, syn, dev, args, e0, e1):
+    """RMSNorm forward, backward and the global gradient norm at their full
+    sizes, each timed alone with HIP events on the current stream."""
+    import numpy as np
+
+    T, D = 32768, 2048
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    def raw(t):
+        t = t.detach().cpu().contiguous()
+        return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).numpy().tobytes()
+
+    d = syn.norm(T, D, n_grad=0)
+    X, G, DY = (up(d[k]) for k in ("x", "g", "dy"))
+    del d
+    V = torch.from_numpy(syn.normal((syn.GRAD_NORM_N,), 1e-4, tag=syn.TAG_V)).to(dev)
+    y = torch.empty_like(X)
+    rstd = torch.empty(T, dtype=torch.float32, device=dev)
+    dx = torch.empty_like(X)
+    dg = torch.empty(D, dtype=torch.float32, device=dev)
+    gn = torch.empty(2, dtype=torch.float32, device=dev)
+    bws = torch.empty(brq.workspace_size(brq.OP_RMSNORM_BWD, T, D), dtype=torch.uint8, device=dev)
+    gws = torch.empty(brq.workspace_size(brq.OP_GRAD_NORM, V.numel()), dtype=torch.uint8,
+                      device=dev)
+    calls = {
+        "rmsnorm_fwd": (lambda: brq.rmsnorm_fixed_fwd(X, G, EPS, out=(y, rstd)),
+                        T * D * (2 + 2) + 4 * T),
+        "rmsnorm_bwd": (lambda: brq.rmsnorm_fixed_bwd(X, G, rstd, DY, ws=bws, out=(dx, dg)),
+                        T * D * (2 + 2 + 2) + 4 * T + 4 * D),
+        "grad_norm": (lambda: brq.grad_norm(V, ws=gws, out=gn), 4 * V.numel()),
+    }
+    res = {}
+    for name, (fn, nbytes) in calls.items():
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t_ms = e0.elapsed_time(e1) / args.steps
+        gbs = nbytes / (t_ms * 1e-3) / 1e9
+        res[name] = {"us_per_call": round(1e3 * t_ms, 2), "algorithmic_bytes": nbytes,
+                     "gb_per_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    outs = {"y": y, "rstd": rstd, "dx": dx, "dg": dg, "grad_norm": gn}
+    exact = all(hashlib.sha256(raw(t)).hexdigest() == stored_digest("norm", k)
+                for k, t in outs.items())
+    del X, G, DY, V, y, dx, bws, gws
+    return dict(res, bitwise_exact=exact, workload=(
+        "x, dy [32768 x 2048] bf16 (x N(0,1) with 1% bf16 subnormals, dy N(0,1e-3)), "
+        "g [2048] bf16 1+N(0,0.1); grad-norm over 1.61e9 fp32 N(0,1e-4)"))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +254,9 @@ def main():
                     help="tokens of the CPU-oracle sample (0 skips it)")
     ap.add_argument("--no-instrument", action="store_true",
                     help="skip the per-call event pass (for profiler runs)")
+    ap.add_argument("--no-norm-config", dest="norm_config", action="store_false",
+                    help="skip the RMSNorm / grad-norm workload at its full sizes "
+                         "(32768 x 2048; 1.61e9 gradient values)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy one 1 GiB device buffer once, so "
                          "that a counter run sees a kernel of known HBM traffic")
@@ -506,6 +567,16 @@ def main():
         f"({PEAK_FP32_FMA / 1e12:.1f} T FMA/s); not part of value"))
     del qa, ka, va, oa
 
+    # The fixed-order RMSNorm workload on its own: forward and backward over
+    # 32768 x 2048 bf16 activations (1% bf16 subnormals) and the global
+    # gradient norm over 1.61e9 fp32 values (6.44 GB, 393066 full 4096-leaf
+    # chunks and a 1664-leaf tail), each timed alone; outputs checked against
+    # the oracle's stored digests.  Not part of value.
+    norm_cfg = None
+    if args.norm_config:
+        norm_cfg = norm_workload(torch, brq, syn, dev, args, e0, e1)
+        log(f"norm workload: {json.dumps(norm_cfg)}")
+
     cpu = None
     if args.cpu_tokens > 0:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
@@ -526,7 +597,7 @@ def main():
         "ms_per_step_hash_off": round(ms_hash_off, 4),
         "tokens_per_s_hash_off": round(M / (ms_hash_off * 1e-3), 1),
         "bitwise_exact": exact, "state_digest": digest, "optimizer": optimizer,
-        "variants": variants,
+        "variants": variants, "norm_workload": norm_cfg,
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(line), flush=True)

@@ -124,8 +124,138 @@ hipError_t rmsnorm_fwd(const void* x, const void* g, int dtype, int64_t T, int64
 
 // ---- backward: one work-group (4 waves) per R rows ---------------------------
 // Thread t owns vector v's elements [(256 v + t) E, + E) of every row.
+//
+// The rows' x and dy go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the instruction's LDS
+// base + 16 l, so wave w's load of vector v fills thread (256 v + 64 w + l)'s
+// slot) through kRmsStages stages, issued kRmsStages - 1 rows ahead: each
+// work-group keeps three rows in flight without holding them in registers.
+// Per row: wait until this wave's loads of the row have landed.  Vector
+// memory operations (loads and stores) complete in issue order, so the wait
+// allows exactly the operations this wave issued after those loads to stay
+// in flight: the later rows' loads and the dx stores of the rows between.
+// A store is counted only where the wave certainly issued it (a row inside
+// T, a vector with at least one lane inside D): a count that is too low
+// only makes the wait stricter.  Then one bare barrier (every wave's part of
+// the row is in LDS, every wave has read the previous row's stage and
+// written that row's dot partials), finish the previous row (dot, dx, dg
+// push), read the row, issue the loads of row + 3 into the freed stage, and
+// write the row's dot partials for the next barrier.  Lanes
+// past D and rows past T load clamped in-bounds addresses and mask the
+// values.
+constexpr int kRmsStages = 4;
+
+template <int N>
+__device__ __forceinline__ void rms_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt (7) and
+  // lgkmcnt (15) left at their no-wait values
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void rms_wait_lgkm0() {
+  // lgkmcnt 0; vmcnt (63) and expcnt (7) at their no-wait values
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (0x7 << 4));
+}
+// wait until at most n vector memory operations are outstanding (n is
+// clamped to [0, MAXN]; callers pass a count that never exceeds MAXN)
+template <int MAXN>
+__device__ __forceinline__ void rms_wait_upto(int n) {
+  if constexpr (MAXN == 0) {
+    rms_wait_vmcnt<0>();
+  } else {
+    if (n >= MAXN) rms_wait_vmcnt<MAXN>();
+    else rms_wait_upto<MAXN - 1>(n);
+  }
+}
+
+// ---- unflushed row work of the backward, proved safe from the inputs --------
+// A result that is not subnormal is left unchanged by the flush, so a chain
+// of operations evaluated without flushes equals the flushed chain whenever
+// no intermediate result is subnormal.  For bf16 rows the kernel proves that
+// from exponent bounds before evaluating a wave's elements unflushed.  With
+// biased exponents Ex, Edy, Eg of the smallest nonzero x, dy, g of a lane
+// (after DAZ) and Er of rstd, every rounded product is at least the power of
+// two of its operands' bounds (rounding is monotone), so
+//   x^ = x rstd       >= 2^(Ex + Er - 254)
+//   d  = dy g         >= 2^(Edy + Eg - 254)
+//   d x^              >= 2^(Edy + Eg + Ex + Er - 508)
+//   dy x^             >= 2^(Edy + Ex + Er - 381)
+//   x^ mu             >= 2^(Ex + Er + Emu - 381)
+// (or exactly zero).  A value of at least 2^-103 is a multiple of 2^-126,
+// and sums and differences of such multiples are multiples of 2^-126 again
+// (exact below 2^-102, rounded to a grid of at least 2^-126 above), so they
+// are zero or normal.  The conditions therefore are: x^ normal
+// (Ex + Er >= 128), d, d x^, dy x^ and x^ mu at least 2^-103
+// (Edy + Eg >= 151, Edy + Eg + Ex + Er >= 405, Edy + Ex + Er >= 278,
+// Ex + Er + Emu >= 278); then the dot tree, d - x^ mu and the dg stack never
+// see a subnormal.  The last product dx = rstd (d - x^ mu) can still be
+// subnormal: it is checked (one v_cmp_class per value) and flushed when any
+// is.  A wave where a condition fails takes the flushed form.
+
+// DAZ of 8 bf16 values (two per 32-bit word: a half whose exponent field is
+// zero keeps only its sign), their exact widening to binary32, and the
+// biased exponent of the smallest nonzero value (512 when all are zero).
+// Packed 16-bit operations: per word one mask, two for the DAZ, two for the
+// exponent minimum.
+__device__ __forceinline__ int widen_bf16x8_daz(u32x4 v, float* f) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  u16x2 emin = {0xffff, 0xffff};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = w[i] & 0x7f807f80u;
+    const u16x2 th = __builtin_bit_cast(u16x2, t);
+    const u16x2 m = __builtin_elementwise_min(th, u16x2{0x7f, 0x7f});
+    // 0x7f in the halves whose exponent is zero: their mantissa bits go
+    const uint32_t z = __builtin_bit_cast(uint32_t, m) ^ 0x007f007fu;
+    const uint32_t u = w[i] & ~z;
+    f[2 * i] = __uint_as_float(u << 16);
+    f[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
+    // (E - 1) << 7 for E >= 1; a zero exponent wraps to 0xff80
+    emin = __builtin_elementwise_min(emin, th - u16x2{0x80, 0x80});
+  }
+  const uint32_t lo = emin.x, hi = emin.y;
+  return (int)((lo < hi ? lo : hi) >> 7) + 1;
+}
+
+// biased exponent of a binary32 value's magnitude
+__device__ __forceinline__ int f32_exp(float v) { return (int)((__float_as_uint(v) >> 23) & 0xffu); }
+
+// Front of one row's work on a lane's E elements: x^ = x rstd, d = dy g,
+// the dot leaves d x^ and the dg leaves dy x^ (-0 where the lane's vector
+// is padding), and the wave's node of the dot's tree.
+template <bool kFast, int E>
+__device__ __forceinline__ float rms_bwd_front(const float* xv, const float* dv, const float* gv,
+                                               float rs, bool live, float* xh, float* d,
+                                               float* leaf) {
+  auto mul = [](float a, float b) { return kFast ? a * b : fmul(a, b); };
+  auto add = [](float a, float b) { return kFast ? a + b : fadd(a, b); };
+  float p[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    xh[e] = mul(xv[e], rs);
+    d[e] = mul(dv[e], gv[e]);
+    // padding (past D or past T) is -0: exact identity for signed sums
+    const float pe = mul(d[e], xh[e]), le = mul(dv[e], xh[e]);
+    p[e] = live ? pe : -0.0f;
+    leaf[e] = live ? le : -0.0f;
+  }
+#pragma unroll
+  for (int w = E; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) p[i] = add(p[2 * i], p[2 * i + 1]);
+  float n = p[0];
+  n = add(n, dpp_xor1(n));
+  n = add(n, dpp_xor2(n));
+  n = add(n, dpp_half_mirror(n));
+  n = add(n, dpp_mirror(n));
+  n = add(n, __shfl_xor(n, 16, kWave));
+  n = add(n, __shfl_xor(n, 32, kWave));
+  return n;
+}
+
 template <typename T, int V, int LOGR>
-__global__ __launch_bounds__(256) void k_rms_bwd(const T* __restrict__ x, const T* __restrict__ g,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(V == 1 ? 4 : 2))) void k_rms_bwd(const T* __restrict__ x, const T* __restrict__ g,
                                                  const float* __restrict__ rstd,
                                                  const T* __restrict__ dy, int64_t Tn, int64_t D,
                                                  float invD, T* __restrict__ dx,
@@ -133,103 +263,205 @@ __global__ __launch_bounds__(256) void k_rms_bwd(const T* __restrict__ x, const 
   constexpr int E = Elem<T>::kPerVec;
   constexpr int R = 1 << LOGR;
   constexpr int NE = V * E;
+  constexpr int S = kRmsStages;
+  constexpr int ROWB = 2 * V * 256 * 16;  // one staged row: x vectors, then dy vectors
+  static_assert(R <= 64, "rstd of the block's rows: one per lane");
+  // one LDS object: the compiler then does not make the stage reads wait
+  // for every direct-to-LDS load in flight
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[S * ROWB + 2 * V * 4 * 4];
+  float(*red)[V][4] = reinterpret_cast<float(*)[V][4]>(stage + S * ROWB);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t r0 = (int64_t)blockIdx.x * R;
-  __shared__ float red[2][V][4];
 
   float gv[NE];
   bool colok[V];
+  int64_t coff[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int64_t c0 = (int64_t)(v * 256 + t) * E;
     colok[v] = c0 < D;
+    coff[v] = colok[v] ? c0 : 0;
     if (colok[v]) Elem<T>::unpack(ld16(g + c0), gv + v * E);
     else
 #pragma unroll
       for (int e = 0; e < E; ++e) gv[v * E + e] = 0.0f;
   }
+  // lane l holds rstd of the block's row l (rows past T: 0)
+  const float rs_lane = (lane < R && r0 + lane < Tn) ? flush(rstd[r0 + lane]) : 0.0f;
   float stk[LOGR + 1][NE];
+  // biased exponent of the lane's smallest nonzero g per vector (bf16)
+  int eg[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    int m = 512;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (gv[v * E + e] != 0.0f && f32_exp(gv[v * E + e]) < m) m = f32_exp(gv[v * E + e]);
+    eg[v] = m;
+  }
+  // sfast: every row pushed on the dg stack so far took the unflushed form
+  bool sfast = E == 8;
+  // dx store instructions this wave issues per row inside T
+  int nst = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) nst += __ballot(colok[v]) != 0 ? 1 : 0;
 
-  // raw 16-byte vectors of the next row: its loads are in flight while the
-  // current row is reduced and written
-  u32x4 xn[V], dn[V];
-  auto fetch = [&](int rr) {
-    const int64_t row = r0 + rr;
+  auto issue = [&](int rr) {
+    int64_t row = r0 + rr;
+    row = row < Tn ? row : Tn - 1;
+    uint8_t* st = stage + (rr % S) * ROWB;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const int64_t c0 = (int64_t)(v * 256 + t) * E;
-      const bool ok = rr < R && row < Tn && colok[v];
-      xn[v] = ok ? ld16(x + row * D + c0) : u32x4{0, 0, 0, 0};
-      dn[v] = ok ? ld16(dy + row * D + c0) : u32x4{0, 0, 0, 0};
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(x + row * D + coff[v]),
+          (__attribute__((address_space(3))) void*)(st + (v * 256 + wave * 64) * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(dy + row * D + coff[v]),
+          (__attribute__((address_space(3))) void*)(st + ((V + v) * 256 + wave * 64) * 16), 16,
+          0, 0);
     }
   };
-  fetch(0);
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < R) issue(s);
 
+  // bf16 rows take the unflushed form where the exponent bounds allow
+  constexpr bool kSpec = E == 8;
+  // the row in flight between its front (before a barrier) and its back
+  // (after it): x^, d, dg leaves, rstd, exponent bounds
+  float xh[NE], d[NE], leaf[NE];
+  int exv[V];
+  float rs = 0.0f;
+  bool lfast = true;  // every vector of the row took the unflushed form
+
+  // One barrier per row: iteration rr waits for row rr's loads, then (after
+  // the barrier, which also publishes row rr - 1's dot partials) finishes
+  // row rr - 1 and starts row rr, whose partials the next barrier publishes.
 #pragma unroll 1
-  for (int rr = 0; rr < R; ++rr) {
+  for (int rr = 0; rr <= R; ++rr) {
+    if (rr < R) {
+      const int later = (R - 1 - rr) < (S - 2) ? (R - 1 - rr) : (S - 2);
+      // rows whose dx stores were issued after this row's loads: those of
+      // [rr - S + 1, rr - 2] inside T
+      const int w0 = rr - S + 1 > 0 ? rr - S + 1 : 0;
+      const int64_t w1 = r0 + rr - 2 < Tn - 1 ? r0 + rr - 2 : Tn - 1;  // last row inside T
+      const int nrows = (int)(w1 - (r0 + w0) + 1) > 0 ? (int)(w1 - (r0 + w0) + 1) : 0;
+      rms_wait_upto<3 * V * (S - 2)>(2 * V * later + nst * nrows);
+    }
+    // this wave's dot partials of row rr - 1 are in LDS; a bare barrier (a
+    // fenced one would also wait for the rows in flight)
+    __builtin_amdgcn_sched_barrier(0);
+    rms_wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    if (rr > 0) {
+      // back of row pr = rr - 1 (its dot partials are in red[pr & 1]): dx,
+      // then the binary-carry push of its dg leaves
+      const int pr = rr - 1;
+      const int64_t row = r0 + pr;
+      const bool rowok = row < Tn;  // uniform across the work-group
+      float n4[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        n4[v] = fadd(fadd(red[pr & 1][v][0], red[pr & 1][v][1]),
+                     fadd(red[pr & 1][v][2], red[pr & 1][v][3]));
+      const float dot = reg_tree<true, V>(n4);
+      const float mu = fmul(dot, invD);
+      // exponent bound of mu (a zero mu makes x^ mu an exact zero)
+      const int emu = mu == 0.0f ? 512 : f32_exp(mu);
+      const int er = f32_exp(rs);
+      if (rowok) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const int64_t c0 = (int64_t)(v * 256 + t) * E;
+          if (!colok[v]) continue;
+          const int k0 = v * E;
+          float o[E];
+          bool fast = false;
+          if constexpr (kSpec) fast = lfast && __ballot(exv[v] + er + emu < 278) == 0;
+          if (fast) {
+            uint64_t bad = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              o[e] = rs * (d[k0 + e] - xh[k0 + e] * mu);
+              bad |= sub_mask(o[e]);
+            }
+            if (bad)
+#pragma unroll
+              for (int e = 0; e < E; ++e) o[e] = flush(o[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              o[e] = fmul(rs, fsub(d[k0 + e], fmul(xh[k0 + e], mu)));
+          }
+          st16(dx + row * D + c0, pack_out<T>(o));
+        }
+      }
+      // every dg leaf pushed so far is zero or at least 2^-103 while sfast
+      // holds: the stack's sums need no flush
+      sfast = __builtin_amdgcn_readfirstlane(sfast && lfast);
+      // row pr merges with the pending nodes of the levels where pr has a 1
+      // bit (lowest first)
+      bool carry = true;
+#pragma unroll
+      for (int l = 0; l <= LOGR; ++l) {
+        if (carry) {
+          if ((pr >> l) & 1) {
+            if (sfast) {
+#pragma unroll
+              for (int k = 0; k < NE; ++k) leaf[k] = stk[l][k] + leaf[k];
+            } else {
+#pragma unroll
+              for (int k = 0; k < NE; ++k) leaf[k] = fadd(stk[l][k], leaf[k]);
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < NE; ++k) stk[l][k] = leaf[k];
+            carry = false;
+          }
+        }
+      }
+    }
+    if (rr == R) break;
+
     const int64_t row = r0 + rr;
     const bool rowok = row < Tn;  // uniform across the work-group
+    const uint8_t* st = stage + (rr % S) * ROWB;
     u32x4 xc[V], dc[V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) { xc[v] = xn[v]; dc[v] = dn[v]; }
-    fetch(rr + 1);
-    float xh[NE], d[NE], leaf[NE];
-    const float rs = rowok ? flush(rstd[row]) : 0.0f;
+    for (int v = 0; v < V; ++v) {
+      xc[v] = *reinterpret_cast<const u32x4*>(st + (v * 256 + t) * 16);
+      dc[v] = *reinterpret_cast<const u32x4*>(st + ((V + v) * 256 + t) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (rr + S - 1 < R) issue(rr + S - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    rs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs_lane), rr));
+    lfast = true;
+    const int er = f32_exp(rs);
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       float xv[E], dv[E];
-      Elem<T>::unpack(xc[v], xv);
-      Elem<T>::unpack(dc[v], dv);
-      float p[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int k = v * E + e;
-        xh[k] = fmul(xv[e], rs);
-        d[k] = fmul(dv[e], gv[k]);
-        // padding (past D or past T) is -0: exact identity for signed sums
-        p[e] = (rowok && colok[v]) ? fmul(d[k], xh[k]) : -0.0f;
-        leaf[k] = (rowok && colok[v]) ? fmul(dv[e], xh[k]) : -0.0f;
+      const bool live = rowok && colok[v];
+      const int k0 = v * E;
+      float nd;
+      if constexpr (kSpec) {
+        const int ex = widen_bf16x8_daz(xc[v], xv);
+        const int ed = widen_bf16x8_daz(dc[v], dv);
+        exv[v] = ex;
+        const bool ok = ex + er >= 128 && ed + eg[v] >= 151 && ed + eg[v] + ex + er >= 405 &&
+                        ed + ex + er >= 278;
+        const bool fast = __ballot(!ok) == 0;  // wave-uniform
+        lfast = lfast && fast;
+        if (fast) nd = rms_bwd_front<true, E>(xv, dv, gv + k0, rs, live, xh + k0, d + k0, leaf + k0);
+        else nd = rms_bwd_front<false, E>(xv, dv, gv + k0, rs, live, xh + k0, d + k0, leaf + k0);
+      } else {
+        Elem<T>::unpack(xc[v], xv);
+        Elem<T>::unpack(dc[v], dv);
+        nd = rms_bwd_front<false, E>(xv, dv, gv + k0, rs, live, xh + k0, d + k0, leaf + k0);
       }
-      float nd = wave_tree<true>(reg_tree<true, E>(p));
       if (lane == 0) red[rr & 1][v][wave] = nd;
-    }
-    __syncthreads();
-    float n4[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      n4[v] = fadd(fadd(red[rr & 1][v][0], red[rr & 1][v][1]),
-                   fadd(red[rr & 1][v][2], red[rr & 1][v][3]));
-    const float dot = reg_tree<true, V>(n4);
-    const float mu = fmul(dot, invD);
-    if (rowok) {
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int64_t c0 = (int64_t)(v * 256 + t) * E;
-        if (!colok[v]) continue;
-        float o[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int k = v * E + e;
-          o[e] = fmul(rs, fsub(d[k], fmul(xh[k], mu)));
-        }
-        st16(dx + row * D + c0, pack_out<T>(o));
-      }
-    }
-    // binary-carry push of this row's dg leaves: row rr merges with the
-    // pending nodes of the levels where rr has a 1 bit (lowest first)
-    bool carry = true;
-#pragma unroll
-    for (int l = 0; l <= LOGR; ++l) {
-      if (carry) {
-        if ((rr >> l) & 1) {
-#pragma unroll
-          for (int k = 0; k < NE; ++k) leaf[k] = fadd(stk[l][k], leaf[k]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < NE; ++k) stk[l][k] = leaf[k];
-          carry = false;
-        }
-      }
     }
   }
   // R is a power of two: the block's node sits at level LOGR.

@@ -414,6 +414,24 @@ def test_rmsnorm_bwd(T, D, bf16, rows):
     assert_bitwise(gdg, dg, "dg")
 
 
+@pytest.mark.parametrize("T,D,xstd,dystd", [(64, 2048, 1.0, 1e-36), (40, 264, 1e-19, 1e-19),
+                                             (96, 2048, 1.0, 1e-3)])
+def test_rmsnorm_bwd_subnormal_band(T, D, xstd, dystd):
+    """Gradients in or near the subnormal band: products and sums of the
+    backward land below 2^-126, so the unflushed row evaluation must fall
+    back to the flushed one (and does not, for the last, ordinary case)."""
+    say("rmsnorm_bwd subnormal band", T, D, xstd, dystd)
+    x = syn.normal((T, D), xstd, tag=214, bf16=True)
+    syn.bf16_subnormals(x, 100, tag=215)
+    g = syn.normal((D,), 0.1, mean=1.0, tag=216, bf16=True)
+    dy = syn.normal((T, D), dystd, tag=217, bf16=True)
+    _, rstd, _ = orc.rmsnorm_fwd(x, g, 1e-6)
+    dx, dg = orc.rmsnorm_bwd(x, g, rstd, dy)
+    gdx, gdg = brq.rmsnorm_fixed_bwd(to_dev(x), to_dev(g), to_dev(rstd), to_dev(dy))
+    assert_bitwise(gdx, dx, "dx")
+    assert_bitwise(gdg, dg, "dg")
+
+
 @pytest.mark.parametrize("n", [1, 1000, 4096 * 5 + 1664, (1 << 20) + 3])
 @pytest.mark.parametrize("chunk", [0, 10, 14])
 def test_grad_norm(n, chunk):
