@@ -62,13 +62,33 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 // fl(sqrt(127)) = 0x41344f93, its binary32 reciprocal 0x3db5bb0a, times 2.
 __device__ __forceinline__ float lsq_k2() { return __uint_as_float(0x3e35bb0au); }
 
-// q = clamp(rint(fl(v * r)), -127, 127); v_rndne_f32 rounds half to even.
-// The product is not flushed: a subnormal v * r and its flushed zero both
-// round to the code 0.  The clamp is one median of three (exact for finite
-// and infinite values; a NaN product has no defined code).
+// q = clamp(rint(fl(v * r)), -127, 127), rounding half to even, returned
+// as the low byte of a binary32 bit pattern.  The clamp comes first (one
+// median of three): the bounds are integers and rint is monotone, so
+// clamping before or after rounding gives the same integer.  Adding
+// 1.5 * 2^23 to a value of magnitude at most 127 then lands in the binade
+// [2^23, 2^24), whose spacing is 1: the add rounds to the nearest integer
+// (ties to even) and the sum's bit pattern is 0x4b400000 + q, whose low
+// byte is q as an int8.  The product is not flushed: a subnormal v * r and
+// its flushed zero both give the code 0.  (A NaN product has no defined
+// code.)
+__device__ __forceinline__ uint32_t quant_code_bits(float v, float r) {
+  const float t = __builtin_amdgcn_fmed3f(v * r, -127.0f, 127.0f);
+  return __float_as_uint(t + 12582912.0f);
+}
 __device__ __forceinline__ int quant_code(float v, float r) {
-  const float t = __builtin_amdgcn_fmed3f(__builtin_rintf(v * r), -127.0f, 127.0f);
-  return (int)t;
+  return (int)(int8_t)(quant_code_bits(v, r) & 0xffu);
+}
+// The codes of four values packed little-endian into one word (two byte
+// permutes and an or).
+__device__ __forceinline__ uint32_t quant_pack4(float v0, float v1, float v2, float v3, float r) {
+  const uint32_t a = quant_code_bits(v0, r), b = quant_code_bits(v1, r);
+  const uint32_t c = quant_code_bits(v2, r), d = quant_code_bits(v3, r);
+  // v_perm_b32(S0, S1, sel): selector byte 0..3 takes byte of S1, 4..7 of
+  // S0, 0x0c gives 0
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // a0, b0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000c0cu);  // 0, 0, c0, d0
+  return lo | hi;
 }
 
 // ---- wave-level canonical tree ---------------------------------------------

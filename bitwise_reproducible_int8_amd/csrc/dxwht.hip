@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void k_quant_wht_rows(const T* __restrict__ x,
     // (a subnormal product f * r rounds to code 0 with or without its flush)
     uint32_t p[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) p[e >> 2] |= (uint32_t)(quant_code(f[e], r) & 0xff) << (8 * (e & 3));
+    for (int e = 0; e < 16; e += 4) p[e >> 2] = quant_pack4(f[e], f[e + 1], f[e + 2], f[e + 3], r);
     st16(q + i0, u32x4{p[0], p[1], p[2], p[3]});
   }
 }

@@ -273,8 +273,7 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
       }
       uint32_t p[2] = {0, 0};
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        p[e >> 2] |= (uint32_t)(quant_code(f[e], r_g) & 0xff) << (8 * (e & 3));
+      for (int e = 0; e < 8; e += 4) p[e >> 2] = quant_pack4(f[e], f[e + 1], f[e + 2], f[e + 3], r_g);
       *reinterpret_cast<uint2*>(q_g + (m0 + r) * N + colv) = make_uint2(p[0], p[1]);
     }
   }
@@ -290,8 +289,8 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
   for (int p = 0; p < kHalf / 16; ++p) {
     uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      w[i >> 2] |= (uint32_t)(quant_code(v[16 * p + i], r_v) & 0xff) << (8 * (i & 3));
+    for (int i = 0; i < 16; i += 4)
+      w[i >> 2] = quant_pack4(v[16 * p + i], v[16 * p + i + 1], v[16 * p + i + 2], v[16 * p + i + 3], r_v);
     st16(q_vt + col * M + m0 + kHalf * half + 16 * p, u32x4{w[0], w[1], w[2], w[3]});
   }
 }

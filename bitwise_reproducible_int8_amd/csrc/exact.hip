@@ -484,7 +484,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_exact(const T* __restrict__ 
     Elem<T>::unpack(raw[v], f);
     uint32_t p[2] = {0, 0};
 #pragma unroll
-    for (int e = 0; e < E; ++e) p[e >> 2] |= (uint32_t)(quant_code(f[e], r) & 0xff) << (8 * (e & 3));
+    for (int e = 0; e < E; e += 4) p[e >> 2] = quant_pack4(f[e], f[e + 1], f[e + 2], f[e + 3], r);
     if (E == 8) *reinterpret_cast<uint2*>(q + row * cols + c0) = make_uint2(p[0], p[1]);
     else *reinterpret_cast<uint32_t*>(q + row * cols + c0) = p[0];
   }

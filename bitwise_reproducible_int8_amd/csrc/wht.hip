@@ -30,16 +30,44 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---- integer rotation ---------------------------------------------------------
+// A work-group owns a tile of TB tokens x 512 columns of q_x.  The tile goes
+// from global memory straight into LDS (global_load_lds_dwordx4, row-major
+// 16-byte chunks: chunk c holds row c / 32, columns 16 (c % 32) .. + 15;
+// wave w's load i fills chunks 256 i + 64 w + lane), so every global load
+// reads whole 512-byte row segments.  Thread t then takes columns 2t and
+// 2t + 1 of every row from LDS as one packed pair of int16 lanes and runs
+// the butterflies in registers.  Chunks past K read a clamped in-bounds
+// chunk whose columns are never used.
+constexpr int kWhtCols = 512;
+
 template <int TB>
-__device__ __forceinline__ void load_int_cols(const int8_t* __restrict__ q_x, int64_t M, int64_t K,
-                                              int64_t m0, int64_t k, s16x2* u) {
+__device__ __forceinline__ void wht_tile_load(const int8_t* __restrict__ q_x, int64_t K,
+                                              int64_t m0, int64_t k0, int8_t* tile) {
+  const int t = threadIdx.x, wave = t >> 6;
+#pragma unroll
+  for (int i = 0; i < TB * (kWhtCols / 16) / 256; ++i) {
+    const int c = i * 256 + t;
+    const int row = c / (kWhtCols / 16);
+    int64_t col = k0 + (c % (kWhtCols / 16)) * 16;
+    col = col < K ? col : k0;
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(q_x + (m0 + row) * K + col),
+        (__attribute__((address_space(3))) void*)(tile + (i * 256 + wave * 64) * 16), 16, 0, 0);
+  }
+  // every load of the tile has landed (this wave's), then every wave's
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
+  __syncthreads();
+}
+
+template <int TB>
+__device__ __forceinline__ void load_int_cols(const int8_t* tile, s16x2* u) {
+  const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
-    uint32_t w = *reinterpret_cast<const uint16_t*>(q_x + (m0 + i) * K + k);
-    s16x2 p;
-    p.x = (short)(int8_t)(w & 0xffu);
-    p.y = (short)(int8_t)(w >> 8);
-    u[i] = p;
+    const uint32_t w = *reinterpret_cast<const uint16_t*>(tile + i * kWhtCols + 2 * t);
+    // bytes (0, c0, 0, c1), then an arithmetic shift of each 16-bit half by 8
+    const uint32_t hi = __builtin_amdgcn_perm(w, w, 0x010c000cu);
+    u[i] = __builtin_bit_cast(s16x2, hi) >> (s16x2){8, 8};
   }
 }
 
@@ -64,17 +92,21 @@ template <int TB>
 __global__ __launch_bounds__(256) void k_wht_int_stats(const int8_t* __restrict__ q_x, int64_t M,
                                                        int64_t K, int b,
                                                        long long* __restrict__ part) {
-  const int64_t k = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+  __shared__ __attribute__((aligned(1024))) int8_t tile[TB * kWhtCols];
+  const int64_t k0 = (int64_t)blockIdx.x * kWhtCols;
+  const int64_t k = k0 + 2 * threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.y * TB;
+  wht_tile_load<TB>(q_x, K, m0, k0, tile);
   int s = 0;
   if (k < K) {
     s16x2 u[TB];
-    load_int_cols<TB>(q_x, M, K, m0, k, u);
+    load_int_cols<TB>(tile, u);
     butterflies_int<TB>(u, b);
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
-      int a = u[i].x, c = u[i].y;
-      s += (a < 0 ? -a : a) + (c < 0 ? -c : c);
+      // |u| <= 127 * 128 fits both halves; the dot with (1, 1) adds them
+      const s16x2 a = __builtin_elementwise_max(u[i], -u[i]);
+      s = __builtin_amdgcn_sdot2(a, (s16x2){1, 1}, s, false);
     }
   }
   // integer sums: exact in any order
@@ -108,43 +140,67 @@ __global__ __launch_bounds__(256) void k_wht_int_finalize(const long long* __res
   }
 }
 
-// Pass 2: recompute u, quantise, write q_u^T [K][M] (16 tokens per store).
+// Pass 2: recompute u, quantise, write q_u^T [K][M].  The codes go through
+// the same LDS tile transposed, [512 columns][TB tokens], 16-token chunks
+// XOR-swizzled by column (the 8 lanes of one LDS access cycle write 8
+// different bank groups), so that each global store instruction writes
+// whole TB-byte column runs: 16 bytes per lane, TB / 16 lanes per column.
 template <int TB>
 __global__ __launch_bounds__(256) void k_wht_int_quant(const int8_t* __restrict__ q_x, int64_t M,
                                                        int64_t K, int b, const float* __restrict__ sr,
                                                        int8_t* __restrict__ q_ut) {
-  const int64_t k = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+  constexpr int QC = TB / 16;  // 16-token chunks per column
+  __shared__ __attribute__((aligned(1024))) int8_t tile[TB * kWhtCols];
+  const int t = threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * kWhtCols;
+  const int64_t k = k0 + 2 * t;
   const int64_t m0 = (int64_t)blockIdx.y * TB;
-  if (k >= K) return;
   const float r = sr[1];
+  wht_tile_load<TB>(q_x, K, m0, k0, tile);
   s16x2 u[TB];
-  load_int_cols<TB>(q_x, M, K, m0, k, u);
+  load_int_cols<TB>(tile, u);
   butterflies_int<TB>(u, b);
+  // every thread has read its columns: the tile takes the codes
+  __syncthreads();
+  if (k < K) {
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 2; ++c) {
+      const int cc = 2 * t + c;
 #pragma unroll
-    for (int p = 0; p < TB / 16; ++p) {
-      uint32_t w[4] = {0, 0, 0, 0};
+      for (int p = 0; p < QC; ++p) {
+        uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        int val = c ? u[16 * p + i].y : u[16 * p + i].x;
-        w[i >> 2] |= (uint32_t)(quant_code((float)val, r) & 0xff) << (8 * (i & 3));
+        for (int i = 0; i < 16; i += 4) {
+          float f[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = (float)(c ? u[16 * p + i + e].y : u[16 * p + i + e].x);
+          w[i >> 2] = quant_pack4(f[0], f[1], f[2], f[3], r);
+        }
+        st16(tile + cc * TB + ((p ^ ((cc >> 1) & (QC - 1))) * 16), u32x4{w[0], w[1], w[2], w[3]});
       }
-      st16(q_ut + (k + c) * M + m0 + 16 * p, u32x4{w[0], w[1], w[2], w[3]});
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kWhtCols * QC / 256; ++j) {
+    const int ch = j * 256 + t;
+    const int cc = ch / QC, q = ch % QC;
+    if (k0 + cc >= K) continue;
+    st16(q_ut + (k0 + cc) * M + m0 + 16 * q,
+         ld16(tile + cc * TB + ((q ^ ((cc >> 1) & (QC - 1))) * 16)));
   }
 }
 
 size_t wht_x_ws(int64_t M, int64_t K, int block) {
   const int TB = block > 64 ? 128 : 64;
-  int64_t P = cdiv(K, 512) * (M / TB);
+  int64_t P = cdiv(K, kWhtCols) * (M / TB);
   return align256((size_t)(P > 0 ? P : 1) * sizeof(long long)) + 256;
 }
 
 hipError_t wht_quant_x(const int8_t* q_x, int64_t M, int64_t K, int block, int8_t* q_ut,
                        float* s_u, void* ws, hipStream_t s) {
   const int TB = block > 64 ? 128 : 64;
-  dim3 g((unsigned)cdiv(K, 512), (unsigned)(M / TB)), bl(256);
+  dim3 g((unsigned)cdiv(K, kWhtCols), (unsigned)(M / TB)), bl(256);
   const int64_t P = (int64_t)g.x * g.y;
   long long* part = (long long*)ws;
   float* sr = (float*)((char*)ws + align256((size_t)(P > 0 ? P : 1) * sizeof(long long)));
@@ -240,8 +296,8 @@ __global__ __launch_bounds__(256) void k_wht_fp_quant(const T* __restrict__ dy, 
   for (int p = 0; p < TB / 16; ++p) {
     uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      w[i >> 2] |= (uint32_t)(quant_code(v[16 * p + i], r) & 0xff) << (8 * (i & 3));
+    for (int i = 0; i < 16; i += 4)
+      w[i >> 2] = quant_pack4(v[16 * p + i], v[16 * p + i + 1], v[16 * p + i + 2], v[16 * p + i + 3], r);
     st16(q_vt + col * M + m0 + 16 * p, u32x4{w[0], w[1], w[2], w[3]});
   }
 }
