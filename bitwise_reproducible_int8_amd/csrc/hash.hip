@@ -14,8 +14,8 @@
 //   - a full slice streams its 64 blocks (other waves hide the load
 //     latency), and its 65th (padding) block is a constant;
 //   - the round function is written in the shapes gfx950 has single
-//     instructions for: rotate (v_alignbit_b32), three-way xor
-//     (v_xor3_b32), bit select (v_bfi_b32), three-way add (v_add3_u32).
+//     instructions for: rotate (v_alignbit_b32), three-way xor, choose and
+//     majority (v_bitop3_b32), three-way add (v_add3_u32).
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -49,9 +49,10 @@ __device__ __forceinline__ uint32_t bswap(uint32_t x) { return __builtin_bswap32
 __device__ __forceinline__ uint32_t xor3(uint32_t x, uint32_t y, uint32_t z) {
   return __builtin_amdgcn_bitop3_b32(x, y, z, 0x96);
 }
-// (m & x) | (~m & y)
+// (m & x) | (~m & y) in one v_bitop3_b32: the truth table is indexed by
+// (m << 2) | (x << 1) | y, so entries 1, 3 (y), 6, 7 (x) are set: 0xCA
 __device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t x, uint32_t y) {
-  return (m & x) | (~m & y);
+  return __builtin_amdgcn_bitop3_b32(m, x, y, 0xCA);
 }
 
 struct Sha {
