@@ -8,7 +8,8 @@
 // shape, split-K and launch order cannot change a bit of it; only the
 // dequantisation epilogue is floating point:
 //     out = fl(fl(acc) * c_j)   one int->fp32 conversion (round to nearest
-//                               even) and one multiply, flushed, no FMA.
+//                               even) and one multiply, no FMA (the flush
+//                               of the product can never act: see dequant).
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -33,7 +34,12 @@ struct Epi {
   }
 };
 
-__device__ __forceinline__ float dequant(int acc, float c) { return fmul((float)acc, c); }
+// fl(fl(acc) * c) without an explicit flush: every column scale c is
+// itself flushed (0 or normal), and a nonzero int32 sum converts to a
+// binary32 of magnitude at least 1, so the exact product is 0 or at least
+// |c| >= 2^-126 and its rounding is 0 or normal -- the flush of the
+// definition never changes it.
+__device__ __forceinline__ float dequant(int acc, float c) { return (float)acc * c; }
 
 // One output element: the fp32 value, or its bf16 rounding.
 __device__ __forceinline__ void put_out(float* C, int64_t idx, float v, bool bf16) {
@@ -549,6 +555,17 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
 // order among themselves, so step t's loads cannot be pending while fewer
 // ops than the later steps' loads are.
 // --------------------------------------------------------------------------
+// wait until at most n vector memory operations are outstanding, n <= MAXN
+template <int MAXN>
+__device__ __forceinline__ void wait_upto(int n) {
+  if constexpr (MAXN == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAXN) wait_vmcnt<MAXN>();
+    else wait_upto<MAXN - 1>(n);
+  }
+}
+
 template <int L, int MAXL>
 __device__ __forceinline__ void wait_later(int64_t later) {
   if constexpr (MAXL == 0) {
@@ -697,12 +714,21 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_stream(
   int cslot = 0;
   int64_t computed = 0;
   uint32_t cord = 0;  // ordinal of unit uc
+  // store instructions this wave issued in the previous unit's epilogue
+  // that certainly follow the loads of this unit's first kStages - 1 steps
+  // (loads and stores complete in issue order, so the first kStages - 1
+  // waits of a unit may leave them in flight); 0 where not certain
+  constexpr int kStoreInstr = BM / WGM / 16 * (16 * (BN / 4) / (WGN * 64));
+  int stores_prev = 0;
 #pragma unroll 1
   for (int64_t uc = blockIdx.x; uc < units; uc += G, ++cord) {
     const Unit w = unit_at(uc);
 #pragma unroll 1
     for (int64_t it = 0; it < w.nk; ++it) {
-      wait_later<L, kStages - 2>(issued - computed - 1);
+      if (it < kStages - 1 && stores_prev > 0)
+        wait_upto<(kStages - 2) * L + kStoreInstr>((int)(issued - computed - 1) * L + stores_prev);
+      else
+        wait_later<L, kStages - 2>(issued - computed - 1);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -751,6 +777,13 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_stream(
                                    return col_scales ? fmul(c_uni, flush(cu[j - w.col0])) : c_uni;
                                  },
                                  smem + last * STAGE, epi.out_bf16);
+    // a tile wholly inside the output, with rows a multiple of the store
+    // width: every lane takes the one-instruction store of each chunk
+    {
+      const bool b16 = epi.out_bf16 && !Cpart;
+      const bool whole = w.row0 + BM <= I && w.col0 + BN <= J && (J % (b16 ? 8 : 4)) == 0;
+      stores_prev = whole ? (b16 ? kStoreInstr / 2 : kStoreInstr) : 0;
+    }
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
