@@ -100,20 +100,31 @@ __device__ __forceinline__ void butterflies(float* v, int b, bool upper) {
     }
   }
   if (b > kHalf) {
-    // stage 64: the lower lane holds v_j, the upper lane v_j+64.
-    // v_permlane32_swap exchanges lanes 32..63 of its first operand with
-    // lanes 0..31 of its second: with both operands v_j, the first result
-    // carries the lower half's values in the upper lanes and the second the
-    // upper half's values in the lower lanes.
+    // stage 64 pairs token t (lower lane, v[t]) with token t + 64 (upper
+    // lane, v[t]).  v_permlane32_swap(x, y) exchanges lanes 32..63 of x
+    // with lanes 0..31 of y; applied to registers j and j + 32 it leaves
+    // in every lane the two operands of one butterfly: lower lanes get
+    // tokens (j, j + 64), upper lanes tokens (j + 32, j + 96), as (x, y).
+    // The sum and difference stay where they are, so afterwards register
+    // i of half h holds token tok_after64(h, i).
+    (void)upper;
 #pragma unroll
-    for (int j = 0; j < kHalf; ++j) {
-      const uint32_t x = __float_as_uint(v[j]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-      const float p = __uint_as_float(upper ? sw[0] : sw[1]);
-      const float a = upper ? p : v[j], c = upper ? v[j] : p;
-      v[j] = upper ? (kFlush ? fsub(a, c) : a - c) : (kFlush ? fadd(a, c) : a + c);
+    for (int j = 0; j < kHalf / 2; ++j) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]),
+                                                        __float_as_uint(v[j + kHalf / 2]), false,
+                                                        false);
+      const float a = __uint_as_float(sw[0]), c = __uint_as_float(sw[1]);
+      v[j] = kFlush ? fadd(a, c) : a + c;
+      v[j + kHalf / 2] = kFlush ? fsub(a, c) : a - c;
     }
   }
+}
+
+// Token (0..127 in the tile) held in register i of lane half h after the
+// butterflies: 64 h + i below block 128; after stage 64 the lower half
+// holds tokens 0..31 and 64..95, the upper half 32..63 and 96..127.
+__device__ __forceinline__ int tok_after(int b, int h, int i) {
+  return b > kHalf ? i + 32 * h + (i >= kHalf / 2 ? kHalf / 2 : 0) : kHalf * h + i;
 }
 
 // tile_ok: the row phase found every nonzero value of the tile >= 2^-103
@@ -208,7 +219,13 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
   float* tr = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    if (half == p) {
+    // tokens 64 p .. 64 p + 63 to rows 0..63 of the transpose
+    if (b > kHalf) {
+#pragma unroll
+      for (int j = 0; j < kHalf / 2; ++j)
+        tr[(tok_after(b, half, (kHalf / 2) * p + j) - kHalf * p) * kTrStride + ccol] =
+            fabs_bits(v[(kHalf / 2) * p + j]);
+    } else if (half == p) {
 #pragma unroll
       for (int i = 0; i < kHalf; ++i) tr[i * kTrStride + ccol] = fabs_bits(v[i]);
     }
@@ -291,7 +308,8 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
 #pragma unroll
     for (int i = 0; i < 16; i += 4)
       w[i >> 2] = quant_pack4(v[16 * p + i], v[16 * p + i + 1], v[16 * p + i + 2], v[16 * p + i + 3], r_v);
-    st16(q_vt + col * M + m0 + kHalf * half + 16 * p, u32x4{w[0], w[1], w[2], w[3]});
+    // registers 16 p .. 16 p + 15 hold 16 consecutive tokens
+    st16(q_vt + col * M + m0 + tok_after(b, half, 16 * p), u32x4{w[0], w[1], w[2], w[3]});
   }
 }
 
