@@ -181,10 +181,10 @@ struct SliceBatch {
 
 // Full 4096-byte slices, one lane each; a buffer's partial last slice (or
 // the one empty slice of an empty buffer) is left to k_sha_partial.  Kept
-// apart from the generic path so the 4 KiB loop needs few registers: the
-// hash runs beside the GEMMs on a second stream, and its waves must fit next
-// to a GEMM work-group's.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_sha_full(
+// apart from the generic path so the 4 KiB loop needs few registers: six
+// waves per SIMD is the most at which the loop keeps its state in registers
+// (at eight the compiler spills the chaining value inside the block loop).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void k_sha_full(
     SliceBatch b) {
   const uint64_t g = (uint64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= b.first[b.n]) return;
