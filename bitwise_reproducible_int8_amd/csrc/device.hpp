@@ -174,13 +174,27 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// DAZ of two bf16 values in one 32-bit word, on 16-bit halves: a half
+// whose exponent field is zero keeps only its sign.  The exponent field is
+// masked out, a packed minimum with 0x7f gives 0x7f in the halves whose
+// exponent is nonzero and 0 in the others, and the mantissa bits of the
+// latter are cleared (with the xor, one v_bitop3_b32).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_daz(uint32_t w) {
+  const u16x2_t e = __builtin_bit_cast(u16x2_t, w & 0x7f807f80u);
+  const u16x2_t m = __builtin_elementwise_min(e, u16x2_t{0x7f, 0x7f});
+  return w & ~(__builtin_bit_cast(uint32_t, m) ^ 0x007f007fu);
+}
+
 // Unpack 16 bytes of bf16 (8 values) or fp32 (4 values) into floats (DAZ).
+// bf16 widening is exact: the DAZ-ed halves shifted into the high bits.
 __device__ __forceinline__ void unpack_bf16x8(u32x4 v, float* f) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_to_f32(w[i] & 0xffffu);
-    f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    const uint32_t u = bf16x2_daz(w[i]);
+    f[2 * i] = __uint_as_float(u << 16);
+    f[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
   }
 }
 __device__ __forceinline__ void unpack_f32x4(u32x4 v, float* f) {

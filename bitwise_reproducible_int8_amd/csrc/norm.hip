@@ -198,21 +198,16 @@ __device__ __forceinline__ void rms_wait_upto(int n) {
 // Packed 16-bit operations: per word one mask, two for the DAZ, two for the
 // exponent minimum.
 __device__ __forceinline__ int widen_bf16x8_daz(u32x4 v, float* f) {
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  u16x2 emin = {0xffff, 0xffff};
+  u16x2_t emin = {0xffff, 0xffff};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t t = w[i] & 0x7f807f80u;
-    const u16x2 th = __builtin_bit_cast(u16x2, t);
-    const u16x2 m = __builtin_elementwise_min(th, u16x2{0x7f, 0x7f});
-    // 0x7f in the halves whose exponent is zero: their mantissa bits go
-    const uint32_t z = __builtin_bit_cast(uint32_t, m) ^ 0x007f007fu;
-    const uint32_t u = w[i] & ~z;
+    const uint32_t u = bf16x2_daz(w[i]);
     f[2 * i] = __uint_as_float(u << 16);
     f[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
     // (E - 1) << 7 for E >= 1; a zero exponent wraps to 0xff80
-    emin = __builtin_elementwise_min(emin, th - u16x2{0x80, 0x80});
+    const u16x2_t th = __builtin_bit_cast(u16x2_t, w[i] & 0x7f807f80u);
+    emin = __builtin_elementwise_min(emin, th - u16x2_t{0x80, 0x80});
   }
   const uint32_t lo = emin.x, hi = emin.y;
   return (int)((lo < hi ? lo : hi) >> 7) + 1;

@@ -30,3 +30,16 @@ def test_code_rounding_identity():
     got, want = _codes_magic(vals), _codes_ref(vals)
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, vals[bad[:8]]
+
+
+def test_bf16_packed_daz_identity():
+    """The library flushes bf16 inputs (DAZ) with packed 16-bit operations:
+    e = h & 0x7f80, m = min(e, 0x7f), h & ~(m ^ 0x7f).  Every one of the
+    65536 bf16 patterns must give h with only its sign kept when the
+    exponent field is zero, and h itself otherwise."""
+    h = np.arange(1 << 16, dtype=np.uint32)
+    e = h & 0x7F80
+    m = np.minimum(e, 0x7F)
+    got = h & ~(m ^ 0x7F) & 0xFFFF
+    want = np.where(e == 0, h & 0x8000, h)
+    assert np.array_equal(got, want)
