@@ -23,9 +23,10 @@
 //   column phase: wave w owns columns 32w .. 32w+31; lane l holds column
 //                 32w + (l & 31), tokens 64 (l >> 5) .. +63.  Butterfly
 //                 stages h = 1 .. 32 run in registers; stage 64 pairs lane l
-//                 with lane l ^ 32.  The |v| leaves go back through LDS to
-//                 row order, 64 rows at a time, to form node(6) per row and
-//                 64 columns.
+//                 with lane l ^ 32, one register swap per two values, after
+//                 which the halves hold tokens in the order tok_after gives.
+//                 The |v| leaves go back through LDS to row order, 64 rows
+//                 at a time, to form node(6) per row and 64 columns.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -86,7 +87,7 @@ __device__ __forceinline__ bool steps_ok(const float* s8) {
 // 2^-110 and never subnormal: the flushes are no-ops and DAZ has nothing to
 // clear.  A wave holding a smaller nonzero input takes the flushing path.
 template <bool kFlush>
-__device__ __forceinline__ void butterflies(float* v, int b, bool upper) {
+__device__ __forceinline__ void butterflies(float* v, int b) {
 #pragma unroll
   for (int h = 1; h < kHalf; h *= 2) {
     if (h < b) {
@@ -106,8 +107,7 @@ __device__ __forceinline__ void butterflies(float* v, int b, bool upper) {
     // in every lane the two operands of one butterfly: lower lanes get
     // tokens (j, j + 64), upper lanes tokens (j + 32, j + 96), as (x, y).
     // The sum and difference stay where they are, so afterwards register
-    // i of half h holds token tok_after64(h, i).
-    (void)upper;
+    // i of half h holds token tok_after(b, h, i).
 #pragma unroll
     for (int j = 0; j < kHalf / 2; ++j) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]),
@@ -140,9 +140,9 @@ __device__ __forceinline__ void column_wht(const uint8_t* lds, int col, int half
   if (!tile_ok) {
 #pragma unroll
     for (int r = 0; r < kHalf; ++r) v[r] = flush(v[r]);
-    butterflies<true>(v, b, half != 0);
+    butterflies<true>(v, b);
   } else {
-    butterflies<false>(v, b, half != 0);
+    butterflies<false>(v, b);
   }
 }
 
