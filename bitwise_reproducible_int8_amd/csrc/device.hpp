@@ -313,6 +313,29 @@ __device__ __forceinline__ void widen_raw(u32x4 v, float* f, uint64_t& bad) {
   for (int e = 0; e < Elem<T>::kPerVec; ++e) bad |= sub_mask(f[e]);
 }
 
+// ---- explicit waits on the memory counters ----------------------------------
+// gfx9 s_waitcnt immediate: vmcnt in bits [3:0] and [15:14], expcnt in
+// [6:4], lgkmcnt in [11:8]; a field at its maximum does not wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+// wait until at most n vector memory operations are outstanding; n is
+// clamped to [0, MAXN] (callers pass counts that never exceed MAXN)
+template <int MAXN>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  if constexpr (MAXN == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAXN) wait_vmcnt<MAXN>();
+    else wait_vmcnt_upto<MAXN - 1>(n);
+  }
+}
+
 // col mod cols, with a mask when cols is a power of two
 __device__ __forceinline__ int64_t col_of(int64_t i, int64_t cols) {
   return (cols & (cols - 1)) == 0 ? (i & (cols - 1)) : i % cols;

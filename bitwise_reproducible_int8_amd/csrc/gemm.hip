@@ -252,14 +252,6 @@ constexpr int kStages = 4;
 // MFMA row groups of a step issued before that step's loads
 constexpr int kIssueAfter = 2;
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt (7) and
-  // lgkmcnt (15) left at their no-wait values
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // 4x4 transpose inside each quad of lanes.  On entry lane q of a quad holds
 // v[r] = M[r][q] (the MFMA result layout: one column, four rows); on exit it
 // holds v[e] = M[q][e] (one row, four consecutive columns), so each lane can
@@ -555,17 +547,6 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
 // order among themselves, so step t's loads cannot be pending while fewer
 // ops than the later steps' loads are.
 // --------------------------------------------------------------------------
-// wait until at most n vector memory operations are outstanding, n <= MAXN
-template <int MAXN>
-__device__ __forceinline__ void wait_upto(int n) {
-  if constexpr (MAXN == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (n >= MAXN) wait_vmcnt<MAXN>();
-    else wait_upto<MAXN - 1>(n);
-  }
-}
-
 template <int L, int MAXL>
 __device__ __forceinline__ void wait_later(int64_t later) {
   if constexpr (MAXL == 0) {
@@ -726,7 +707,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_stream(
 #pragma unroll 1
     for (int64_t it = 0; it < w.nk; ++it) {
       if (it < kStages - 1 && stores_prev > 0)
-        wait_upto<(kStages - 2) * L + kStoreInstr>((int)(issued - computed - 1) * L + stores_prev);
+        wait_vmcnt_upto<(kStages - 2) * L + kStoreInstr>((int)(issued - computed - 1) * L +
+                                                          stores_prev);
       else
         wait_later<L, kStages - 2>(issued - computed - 1);
       __builtin_amdgcn_sched_barrier(0);

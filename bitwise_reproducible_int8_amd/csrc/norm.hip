@@ -145,28 +145,6 @@ hipError_t rmsnorm_fwd(const void* x, const void* g, int dtype, int64_t T, int64
 // values.
 constexpr int kRmsStages = 4;
 
-template <int N>
-__device__ __forceinline__ void rms_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt (7) and
-  // lgkmcnt (15) left at their no-wait values
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-__device__ __forceinline__ void rms_wait_lgkm0() {
-  // lgkmcnt 0; vmcnt (63) and expcnt (7) at their no-wait values
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (0x7 << 4));
-}
-// wait until at most n vector memory operations are outstanding (n is
-// clamped to [0, MAXN]; callers pass a count that never exceeds MAXN)
-template <int MAXN>
-__device__ __forceinline__ void rms_wait_upto(int n) {
-  if constexpr (MAXN == 0) {
-    rms_wait_vmcnt<0>();
-  } else {
-    if (n >= MAXN) rms_wait_vmcnt<MAXN>();
-    else rms_wait_upto<MAXN - 1>(n);
-  }
-}
 
 // ---- unflushed row work of the backward, proved safe from the inputs --------
 // A result that is not subnormal is left unchanged by the flush, so a chain
@@ -341,12 +319,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(V == 1 ? 4 
       const int w0 = rr - S + 1 > 0 ? rr - S + 1 : 0;
       const int64_t w1 = r0 + rr - 2 < Tn - 1 ? r0 + rr - 2 : Tn - 1;  // last row inside T
       const int nrows = (int)(w1 - (r0 + w0) + 1) > 0 ? (int)(w1 - (r0 + w0) + 1) : 0;
-      rms_wait_upto<3 * V * (S - 2)>(2 * V * later + nst * nrows);
+      wait_vmcnt_upto<3 * V * (S - 2)>(2 * V * later + nst * nrows);
     }
     // this wave's dot partials of row rr - 1 are in LDS; a bare barrier (a
     // fenced one would also wait for the rows in flight)
     __builtin_amdgcn_sched_barrier(0);
-    rms_wait_lgkm0();
+    wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
