@@ -212,7 +212,11 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ q
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int64_t gj = kb * kBlk + 4 * kg + b;
-        s[a][b] = (gj > gi || gj <= gi - window) ? -INFINITY : fmul(s[a][b], c);
+        // without the slow inputs every nonzero logit is a multiple of
+        // 2^-114, so s * c (c = 1/sqrt(d) > 2^-4) is 0 or above 2^-118 and
+        // its flush cannot act
+        const float sc = slow ? fmul(s[a][b], c) : s[a][b] * c;
+        s[a][b] = (gj > gi || gj <= gi - window) ? -INFINITY : sc;
         bmax[a] = fmaxf(bmax[a], s[a][b]);
       }
       bmax[a] = group16_max(bmax[a]);
@@ -281,7 +285,9 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ q
         int dot = 0;
 #pragma unroll
         for (int j4 = 0; j4 < kBlk / 4; ++j4) dot = __builtin_amdgcn_sdot4(prow[j4], vcol[j4], dot, false);
-        acc[e] = fadd(fmul(acc[e], alpha), fmul((float)dot, cs));
+        // fl(fl(dot) * cs) needs no flush: cs is flushed (0 or normal) and
+        // a nonzero integer sum converts to a magnitude of at least 1
+        acc[e] = fadd(fmul(acc[e], alpha), (float)dot * cs);
       }
     }
     __syncthreads();  // pc, vT, s_alpha, s_any reused by the next block
