@@ -236,9 +236,11 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ q
         pr[a][b] = (!any || s[a][b] == -INFINITY) ? 0.0f : exp_f_fast(fsub(s[a][b], mn));
         pmax = fmaxf(pmax, pr[a][b]);
       }
-      float node = fadd(fadd(pr[a][0], pr[a][1]), fadd(pr[a][2], pr[a][3]));
+      // the probabilities are +0 or normal and non-negative, so no partial
+      // sum of the tree can be subnormal: plain adds equal flushed ones
+      float node = (pr[a][0] + pr[a][1]) + (pr[a][2] + pr[a][3]);
 #pragma unroll
-      for (int o2 = 1; o2 < 16; o2 <<= 1) node = fadd(node, __shfl_xor(node, o2));
+      for (int o2 = 1; o2 < 16; o2 <<= 1) node = node + __shfl_xor(node, o2);
       if (any) {
         l[a] = fadd(fmul(l[a], alpha), node);
         m[a] = mn;
