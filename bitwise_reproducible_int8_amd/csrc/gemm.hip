@@ -402,6 +402,73 @@ __device__ __forceinline__ void store_tile(const v4i (&acc)[BM / WGM / 16][BN / 
   }
 }
 
+// The same epilogue for a tile wholly inside an fp32 output, or inside a
+// split-K slice of int32 partials (Cpart != nullptr, slice z): identical
+// layout, stores and values, with the bound checks gone and each lane's LDS
+// offsets and global addresses computed once instead of per row block.
+template <int BM, int BN, int WGM, int WGN, class Scale>
+__device__ __forceinline__ void store_tile_full(const v4i (&acc)[BM / WGM / 16][BN / WGN / 16],
+                                                int64_t row0, int64_t col0, int wave, int lane,
+                                                int64_t I, int64_t J, float* __restrict__ C,
+                                                int* __restrict__ Cpart, int64_t z,
+                                                const Scale& scale, int8_t* stage) {
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int CPR = BN / 4;                 // 16-byte chunks per staged row
+  constexpr int GROUP = 16 * BN * 4;          // bytes per row group
+  constexpr int RCH = 16 * CPR / (WGN * 64);  // chunks each lane stores per block
+  const int wm = wave / WGN, wn = wave % WGN;
+  int8_t* grp = stage + wm * GROUP;
+  const int rq = 4 * (lane >> 4);
+  const int cc = wn * WN + (lane & 15);
+  float cj[TJ];
+  int woff[TJ][4];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    cj[j] = Cpart ? 0.0f : scale(col0 + cc + j * 16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = rq + r, c = cc + j * 16;
+      woff[j][r] = (rr * CPR + ((c >> 2) ^ (rr & 7))) * 16 + (c & 3) * 4;
+    }
+  }
+  // element offsets of the lane's chunks in the output (fp32 C, or slice z
+  // of the int32 partials: both 4-byte elements)
+  int roff[RCH];
+  int64_t eoff[RCH];
+  const int64_t zbase = Cpart ? z * I * J : 0;
+#pragma unroll
+  for (int k = 0; k < RCH; ++k) {
+    const int ch = (k * WGN + wn) * 64 + lane;
+    const int r = ch / CPR, c4 = ch % CPR;
+    roff[k] = (r * CPR + (c4 ^ (r & 7))) * 16;
+    eoff[k] = zbase + (row0 + wm * WM + r) * J + col0 + c4 * 4;
+  }
+#pragma unroll  // fully: acc must stay in registers
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<int*>(grp + woff[j][r]) =
+            Cpart ? acc[i][j][r] : __float_as_int(dequant(acc[i][j][r], cj[j]));
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < RCH; ++k) {
+      const v4i v = *reinterpret_cast<const v4i*>(grp + roff[k]);
+      const int64_t e = eoff[k] + (int64_t)i * 16 * J;
+      // partials are cached (the reduction reads them); outputs stream
+      if (Cpart)
+        *reinterpret_cast<v4i*>(Cpart + e) = v;
+      else
+        __builtin_nontemporal_store(f32x4{__int_as_float(v[0]), __int_as_float(v[1]),
+                                          __int_as_float(v[2]), __int_as_float(v[3])},
+                                    reinterpret_cast<f32x4*>(C + e));
+    }
+    __syncthreads();
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t I, int64_t J,
@@ -521,8 +588,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
   // every load has landed (the last step waited for all); the barrier
   // frees the stages for the epilogue
   __syncthreads();
-  store_tile<BM, BN, WGM, WGN>(acc, row0, col0, wave, lane, I, J, C, Cpart, blockIdx.z,
-                               [&](int64_t j) { return epi.scale(j); }, smem, epi.out_bf16);
+  if ((Cpart || !epi.out_bf16) && row0 + BM <= I && col0 + BN <= J && (J & 3) == 0)
+    store_tile_full<BM, BN, WGM, WGN>(acc, row0, col0, wave, lane, I, J, C, Cpart, blockIdx.z,
+                                      [&](int64_t j) { return epi.scale(j); }, smem);
+  else
+    store_tile<BM, BN, WGM, WGN>(acc, row0, col0, wave, lane, I, J, C, Cpart, blockIdx.z,
+                                 [&](int64_t j) { return epi.scale(j); }, smem, epi.out_bf16);
 }
 
 // --------------------------------------------------------------------------
@@ -753,12 +824,17 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_stream(
     // is issued after the next step's barrier
     const int last = cslot == 0 ? kStages - 1 : cslot - 1;
     __syncthreads();  // every wave has read its last fragments
-    store_tile<BM, BN, WGM, WGN>(acc, w.row0, w.col0, wave, lane, I, J, C, Cpart,
-                                 (uint32_t)uc / (uint32_t)tiles,
-                                 [&](int64_t j) {
-                                   return col_scales ? fmul(c_uni, flush(cu[j - w.col0])) : c_uni;
-                                 },
-                                 smem + last * STAGE, epi.out_bf16);
+    const auto unit_scale = [&](int64_t j) {
+      return col_scales ? fmul(c_uni, flush(cu[j - w.col0])) : c_uni;
+    };
+    if ((Cpart || !epi.out_bf16) && w.row0 + BM <= I && w.col0 + BN <= J && (J & 3) == 0)
+      store_tile_full<BM, BN, WGM, WGN>(acc, w.row0, w.col0, wave, lane, I, J, C, Cpart,
+                                        (uint32_t)uc / (uint32_t)tiles, unit_scale,
+                                        smem + last * STAGE);
+    else
+      store_tile<BM, BN, WGM, WGN>(acc, w.row0, w.col0, wave, lane, I, J, C, Cpart,
+                                   (uint32_t)uc / (uint32_t)tiles, unit_scale,
+                                   smem + last * STAGE, epi.out_bf16);
     // a tile wholly inside the output, with rows a multiple of the store
     // width: every lane takes the one-instruction store of each chunk
     {
