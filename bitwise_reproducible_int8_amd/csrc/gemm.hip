@@ -402,10 +402,18 @@ __device__ __forceinline__ void store_tile(const v4i (&acc)[BM / WGM / 16][BN / 
   }
 }
 
-// The same epilogue for a tile wholly inside an fp32 output, or inside a
-// split-K slice of int32 partials (Cpart != nullptr, slice z): identical
-// layout, stores and values, with the bound checks gone and each lane's LDS
-// offsets and global addresses computed once instead of per row block.
+// Epilogue of a tile wholly inside an fp32 output, or inside a split-K
+// slice of int32 partials (Cpart != nullptr, slice z), staged per wave
+// instead of per row group: each wave writes its 16 x WN block into a
+// private LDS area (16 * WN * 4 bytes; all waves together take the same
+// space as the per-group staging) and reads it back as 16-byte chunks, so
+// one store instruction writes 64 * 16 bytes in whole rows of WN * 4
+// contiguous bytes (256 bytes, two 128-byte lines, for WN = 64).  A wave's own LDS writes and reads
+// execute in order, so no work-group barrier is needed.  The 16-byte
+// chunk index is XOR-ed with row bit 2: the four row groups of a 32-bit
+// write then cover all 32 banks twice, and the 8 lanes of a 128-bit read
+// cycle hit 8 different chunks.  Offsets and global addresses are
+// computed once per tile.
 template <int BM, int BN, int WGM, int WGN, class Scale>
 __device__ __forceinline__ void store_tile_full(const v4i (&acc)[BM / WGM / 16][BN / WGN / 16],
                                                 int64_t row0, int64_t col0, int wave, int lane,
@@ -414,35 +422,33 @@ __device__ __forceinline__ void store_tile_full(const v4i (&acc)[BM / WGM / 16][
                                                 const Scale& scale, int8_t* stage) {
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TI = WM / 16, TJ = WN / 16;
-  constexpr int CPR = BN / 4;                 // 16-byte chunks per staged row
-  constexpr int GROUP = 16 * BN * 4;          // bytes per row group
-  constexpr int RCH = 16 * CPR / (WGN * 64);  // chunks each lane stores per block
+  constexpr int CPW = WN / 4;     // 16-byte chunks per staged row
+  constexpr int KR = 16 * CPW / 64;  // chunks each lane reads back per block
+  static_assert(CPW >= 8 && CPW <= 64 && KR * 64 == 16 * CPW, "staging layout");
   const int wm = wave / WGN, wn = wave % WGN;
-  int8_t* grp = stage + wm * GROUP;
+  int8_t* own = stage + wave * (16 * WN * 4);
   const int rq = 4 * (lane >> 4);
-  const int cc = wn * WN + (lane & 15);
+  const int lcol = lane & 15;  // the lane's column in each 16-column block
   float cj[TJ];
   int woff[TJ][4];
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
-    cj[j] = Cpart ? 0.0f : scale(col0 + cc + j * 16);
+    cj[j] = Cpart ? 0.0f : scale(col0 + wn * WN + lcol + j * 16);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rr = rq + r, c = cc + j * 16;
-      woff[j][r] = (rr * CPR + ((c >> 2) ^ (rr & 7))) * 16 + (c & 3) * 4;
+      const int row = rq + r, c = lcol + j * 16;
+      woff[j][r] = row * (WN * 4) + (((c >> 2) ^ (((row >> 2) & 1) << 2)) << 4) + (c & 3) * 4;
     }
   }
-  // element offsets of the lane's chunks in the output (fp32 C, or slice z
-  // of the int32 partials: both 4-byte elements)
-  int roff[RCH];
-  int64_t eoff[RCH];
+  // read-back: chunk x = lane % CPW of rows (64 / CPW) k + lane / CPW
+  int roff[KR];
+  int64_t eoff[KR];
   const int64_t zbase = Cpart ? z * I * J : 0;
 #pragma unroll
-  for (int k = 0; k < RCH; ++k) {
-    const int ch = (k * WGN + wn) * 64 + lane;
-    const int r = ch / CPR, c4 = ch % CPR;
-    roff[k] = (r * CPR + (c4 ^ (r & 7))) * 16;
-    eoff[k] = zbase + (row0 + wm * WM + r) * J + col0 + c4 * 4;
+  for (int k = 0; k < KR; ++k) {
+    const int row = (64 / CPW) * k + lane / CPW, x = lane % CPW;
+    roff[k] = row * (WN * 4) + ((x ^ (((row >> 2) & 1) << 2)) << 4);
+    eoff[k] = zbase + (row0 + wm * WM + row) * J + col0 + wn * WN + x * 4;
   }
 #pragma unroll  // fully: acc must stay in registers
   for (int i = 0; i < TI; ++i) {
@@ -450,12 +456,11 @@ __device__ __forceinline__ void store_tile_full(const v4i (&acc)[BM / WGM / 16][
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<int*>(grp + woff[j][r]) =
+        *reinterpret_cast<int*>(own + woff[j][r]) =
             Cpart ? acc[i][j][r] : __float_as_int(dequant(acc[i][j][r], cj[j]));
-    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < RCH; ++k) {
-      const v4i v = *reinterpret_cast<const v4i*>(grp + roff[k]);
+    for (int k = 0; k < KR; ++k) {
+      const v4i v = *reinterpret_cast<const v4i*>(own + roff[k]);
       const int64_t e = eoff[k] + (int64_t)i * 16 * J;
       // partials are cached (the reduction reads them); outputs stream
       if (Cpart)
@@ -465,7 +470,6 @@ __device__ __forceinline__ void store_tile_full(const v4i (&acc)[BM / WGM / 16][
                                           __int_as_float(v[2]), __int_as_float(v[3])},
                                     reinterpret_cast<f32x4*>(C + e));
     }
-    __syncthreads();
   }
 }
 
