@@ -252,35 +252,6 @@ constexpr int kStages = 4;
 // MFMA row groups of a step issued before that step's loads
 constexpr int kIssueAfter = 2;
 
-// 4x4 transpose inside each quad of lanes.  On entry lane q of a quad holds
-// v[r] = M[r][q] (the MFMA result layout: one column, four rows); on exit it
-// holds v[e] = M[q][e] (one row, four consecutive columns), so each lane can
-// store 16 contiguous bytes.  Two exchange stages: off-diagonal elements of
-// the 2x2 sub-blocks between lanes q, q^1, then off-diagonal 2x2 blocks
-// between lanes q, q^2.  Integer moves only.
-__device__ __forceinline__ int dpp_xor1_i(int v) {
-  return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
-}
-__device__ __forceinline__ int dpp_xor2_i(int v) {
-  return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
-}
-__device__ __forceinline__ v4i quad_transpose(v4i v, int q) {
-  const bool odd = q & 1, hi = q & 2;
-#pragma unroll
-  for (int r0 = 0; r0 < 4; r0 += 2) {
-    const int recv = dpp_xor1_i(odd ? v[r0] : v[r0 + 1]);
-    if (odd) v[r0] = recv;
-    else v[r0 + 1] = recv;
-  }
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int recv = dpp_xor2_i(hi ? v[r] : v[r + 2]);
-    if (hi) v[r] = recv;
-    else v[r + 2] = recv;
-  }
-  return v;
-}
-
 // Epilogue of one output tile, staged through LDS so that every global
 // store instruction writes whole rows (bf16 outputs: half rows of 512 bytes): one wave's 16-byte-per-lane store
 // covers BN * 4 / 1024 rows of 1 KiB contiguous (one row for BN = 256).
