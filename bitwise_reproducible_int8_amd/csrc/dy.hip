@@ -49,6 +49,19 @@ __device__ __forceinline__ u32x4 load_vec(const uint16_t* __restrict__ dy, int64
   return col < N ? ld16(dy + (m0 + r) * N + col) : u32x4{0, 0, 0, 0};
 }
 
+// The lane's 8 column steps (DAZ); N % 64 == 0 and colv % 8 == 0, so the 8
+// columns are all inside the matrix or all outside it.
+__device__ __forceinline__ void load_steps(const float* __restrict__ sw, int64_t N, int64_t colv,
+                                           float* s8) {
+  if (colv < N) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s8[e] = flush(sw[colv + e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s8[e] = 0.0f;
+  }
+}
+
 // Fast-path test, exact (the argument under column_wht): a bf16 tile whose
 // nonzero values all have magnitude >= 2^-103 has only normal inputs, and
 // every product with a step |s| >= 2^-23 (or 0) and every butterfly sum
@@ -164,8 +177,7 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
   const int cg = t & 15, rb = t >> 4;
   const int64_t colv = c0 + 8 * cg;
   float s8[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) s8[e] = colv + e < N ? flush(sw[colv + e]) : 0.0f;
+  load_steps(sw, N, colv, s8);
   u32x4 raw[kRows / 16];
 #pragma unroll
   for (int i = 0; i < kRows / 16; ++i) raw[i] = load_vec(dy, N, m0, colv, rb + 16 * i);
@@ -181,11 +193,12 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
     st16(lds + r * kRowBytes + 16 * cg, raw[i]);
     float f[8];
     if (fast) {
+      // |fl(x s)| = fl(|x| |s|): the sign bits are dropped before the product
       const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        f[2 * k] = fabs_bits(__uint_as_float(w[k] << 16) * s8[2 * k]);
-        f[2 * k + 1] = fabs_bits(__uint_as_float(w[k] & 0xffff0000u) * s8[2 * k + 1]);
+        f[2 * k] = __uint_as_float((w[k] & 0x7fffu) << 16) * fabs_bits(s8[2 * k]);
+        f[2 * k + 1] = __uint_as_float(w[k] & 0x7fff0000u) * fabs_bits(s8[2 * k + 1]);
       }
     } else {
       unpack_bf16x8(raw[i], f);
@@ -260,8 +273,7 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
   const int cg = t & 15, rb = t >> 4;
   const int64_t colv = c0 + 8 * cg;
   float s8[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) s8[e] = colv + e < N ? flush(sw[colv + e]) : 0.0f;
+  load_steps(sw, N, colv, s8);
   u32x4 raw[kRows / 16];
 #pragma unroll
   for (int i = 0; i < kRows / 16; ++i) raw[i] = load_vec(dy, N, m0, colv, rb + 16 * i);
@@ -300,8 +312,13 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
   const int ccol = 32 * wave + (lane & 31), half = lane >> 5;
   float v[kHalf];
   column_wht(lds, ccol, half, b, tile_ok, v);
-  const int64_t col = c0 + ccol;
-  if (col >= N) return;
+  // The codes go through LDS as [column][token] (after the barrier no lane
+  // reads the bf16 tile any more), so that each store instruction writes
+  // whole 128-token runs of 8 columns instead of 16-byte pieces of 64.
+  // Columns past N are computed from the zero tile and not stored.
+  constexpr int kCodeStride = kRows + 16;  // padded bytes per column
+  static_assert(kCols * kCodeStride <= kRows * kRowBytes, "codes fit the tile memory");
+  __syncthreads();
 #pragma unroll
   for (int p = 0; p < kHalf / 16; ++p) {
     uint32_t w[4] = {0, 0, 0, 0};
@@ -309,7 +326,14 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
     for (int i = 0; i < 16; i += 4)
       w[i >> 2] = quant_pack4(v[16 * p + i], v[16 * p + i + 1], v[16 * p + i + 2], v[16 * p + i + 3], r_v);
     // registers 16 p .. 16 p + 15 hold 16 consecutive tokens
-    st16(q_vt + col * M + m0 + tok_after(b, half, 16 * p), u32x4{w[0], w[1], w[2], w[3]});
+    st16(lds + ccol * kCodeStride + tok_after(b, half, 16 * p), u32x4{w[0], w[1], w[2], w[3]});
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kCols * kRows / 16 / 256; ++k) {
+    const int c = k * 32 + (t >> 3), ch = 16 * (t & 7);
+    if (c0 + c < N)
+      st16(q_vt + (c0 + c) * M + m0 + ch, *reinterpret_cast<const u32x4*>(lds + c * kCodeStride + ch));
   }
 }
 

@@ -297,7 +297,7 @@ def test_qgemm_bwd_dw_wht(M, N, K, b):
 @pytest.mark.parametrize("M,N,b,bf16", [(384, 320, 128, True), (256, 512, 64, True),
                                         (128, 64, 16, True), (1024, 2048, 128, True),
                                         (64, 256, 64, False), (192, 256, 64, True),
-                                        (512, 768, 1, True)])
+                                        (512, 768, 1, True), (256, 128, 32, True)])
 def test_quantize_dy_bwd(M, N, b, bf16):
     """Both dY codes in one call equal quantize_lsq(col_mul) and the rotated
     LSQ of the oracle (two-pass form and its fallbacks)."""
@@ -316,6 +316,26 @@ def test_quantize_dy_bwd(M, N, b, bf16):
         assert_bitwise(gqvt, np.ascontiguousarray(qv.T), "q_v^T")
         assert_bitwise(gsv, np.array([sv], np.float32), "s_v")
         assert int(flags.item()) == fl == fl2 == 0
+
+
+@pytest.mark.parametrize("M,N,b", [(256, 256, 128), (128, 320, 64), (256, 128, 32)])
+def test_quantize_dy_bwd_tiny(M, N, b):
+    """dY near the bottom of the binary32 range, with bf16 subnormals: the
+    tiles take the flushing forms of the products and the butterflies."""
+    say("quantize_dy_bwd tiny", M, N, b)
+    dy = syn.student_t3((M, N), 1e-36, tag=232, bf16=True)
+    syn.bf16_subnormals(dy, 50, tag=233)
+    sw = syn.normal((N,), 0.01, mean=0.02, tag=234)
+    qg, _, sg, ag, fl = orc.quantize_lsq(dy, col_mul=sw)
+    qv, sv, _, fl2 = orc.wht_fp_quant(dy, b)
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gqg, gsg, gag, gqvt, gsv = brq.quantize_dy_bwd(to_dev(dy), to_dev(sw), b, flags=flags)
+    assert_bitwise(gqg, qg, "q_g")
+    assert_bitwise(gsg, sg, "s_g")
+    assert_bitwise(gag, ag, "amax_g")
+    assert_bitwise(gqvt, np.ascontiguousarray(qv.T), "q_v^T")
+    assert_bitwise(gsv, np.array([sv], np.float32), "s_v")
+    assert int(flags.item()) == (fl | fl2)
 
 
 def test_quantize_dy_bwd_edges():
