@@ -121,10 +121,44 @@ def stored_traffic():
     return float(rec["bytes_per_launch"])
 
 
-def cpu_baseline(tokens):
+def cpu_baseline(tokens, one_core_tokens):
     """The plain CPU oracle on the first `tokens` tokens of the same layer
-    workload: both norms, the seven linears forward and backward, grad-norm
-    over the gradients, state hash (the oracle as written, untuned)."""
+    workload, on all host threads: both norms, the seven linears forward and
+    backward, grad-norm over the gradients, state hash (the oracle as
+    written, untuned).  Then the same on `one_core_tokens` tokens with one
+    thread (0 skips it)."""
+    import oracle as orc
+
+    ops = gemm_ops(_layer_linears(), tokens)
+    dt = _oracle_layer(tokens)
+    out = {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": orc.num_threads(),
+           "kind": "oracle",
+           "sample": (f"the whole layer step (2 RMSNorms, 7 W8A8 linears fwd+bwd with WHT, "
+                      f"grad-norm, state hash) on the first {tokens} of 32768 tokens; "
+                      f"{dt:.2f} s wall, {tokens / dt:.1f} tokens/s"),
+           "tokens_per_s": round(tokens / dt, 3), "seconds": round(dt, 3)}
+    if one_core_tokens > 0:
+        n = orc.num_threads()
+        orc.set_num_threads(1)
+        try:
+            dt1 = _oracle_layer(one_core_tokens)
+        finally:
+            orc.set_num_threads(n)
+        ops1 = gemm_ops(_layer_linears(), one_core_tokens)
+        out["one_core"] = {"value": round(ops1 / dt1 / 1e12, 6), "unit": "TOPS", "cores": 1,
+                           "tokens": one_core_tokens, "seconds": round(dt1, 3),
+                           "tokens_per_s": round(one_core_tokens / dt1, 3)}
+    return out
+
+
+def _layer_linears():
+    import brq_synth as syn
+    return syn.LAYER_LINEARS
+
+
+def _oracle_layer(tokens):
+    """Wall seconds of the oracle's layer step on the first `tokens` tokens
+    (input generation outside the timed region)."""
     import numpy as np
 
     import brq_synth as syn
@@ -175,14 +209,7 @@ def cpu_baseline(tokens):
     ss, n2, _ = orc.grad_norm(np.concatenate(arena))
     outs.append(("grad_norm", np.array([ss, n2], np.float32)))
     orc.hash_state(outs)
-    dt = time.perf_counter() - t0
-    ops = gemm_ops(syn.LAYER_LINEARS, M)
-    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": orc.num_threads(),
-            "kind": "oracle",
-            "sample": (f"the whole layer step (2 RMSNorms, 7 W8A8 linears fwd+bwd with WHT, "
-                       f"grad-norm, state hash) on the first {M} of 32768 tokens; "
-                       f"{dt:.2f} s wall, {M / dt:.1f} tokens/s"),
-            "tokens_per_s": round(M / dt, 3), "seconds": round(dt, 3)}
+    return time.perf_counter() - t0
 
 
 def norm_workload(torch, brq, syn, dev, args, e0, e1):
@@ -252,6 +279,9 @@ def main():
                     help="tokens per step (a multiple of 128; 32768 is the measured workload)")
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="tokens of the CPU-oracle sample (0 skips it)")
+    ap.add_argument("--cpu-one-core-tokens", type=int, default=128,
+                    help="tokens of the one-thread CPU-oracle sample, a multiple of the "
+                         "128-token rotation block (0 skips it)")
     ap.add_argument("--no-instrument", action="store_true",
                     help="skip the per-call event pass (for profiler runs)")
     ap.add_argument("--no-norm-config", dest="norm_config", action="store_false",
@@ -580,7 +610,7 @@ def main():
     cpu = None
     if args.cpu_tokens > 0:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
-        cpu = cpu_baseline(args.cpu_tokens)
+        cpu = cpu_baseline(args.cpu_tokens, args.cpu_one_core_tokens)
 
     line = {
         "metric": METRIC, "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1,

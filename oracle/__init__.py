@@ -32,6 +32,8 @@ def lib():
         vp, i64, f32, i32 = C.c_void_p, C.c_int64, C.c_float, C.c_int
         L.orc_num_threads.restype = i32
         L.orc_num_threads.argtypes = []
+        L.orc_set_num_threads.restype = None
+        L.orc_set_num_threads.argtypes = [i32]
         L.orc_flush.restype = f32
         L.orc_flush.argtypes = [f32]
         L.orc_bf16_to_f32.restype = f32
@@ -123,6 +125,10 @@ def num_threads() -> int:
     return lib().orc_num_threads()
 
 
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
+
+
 def flush(v: float) -> float:
     return lib().orc_flush(v)
 
@@ -211,9 +217,18 @@ def qgemm_bwd_dx(q_g, s_g, q_w):
     return dx
 
 
+def _block(length: int, b: int, what: str) -> None:
+    """The rotation runs over aligned blocks of b along one dimension: b must
+    be a power of two dividing that dimension (the C loops index whole
+    blocks and would run past a ragged end)."""
+    if b < 1 or b & (b - 1) or length % b:
+        raise ValueError(f"rotation block {b}: needs a power of two dividing {what} = {length}")
+
+
 def wht_int(q_x, b: int):
     q_x = _c(q_x, np.int8)
     M, K = q_x.shape
+    _block(M, b, "tokens")
     u = np.empty((M, K), np.int32)
     lib().orc_wht_int(_p(q_x), M, K, b, _p(u))
     return u
@@ -222,6 +237,7 @@ def wht_int(q_x, b: int):
 def wht_int_quant(q_x, b: int):
     q_x = _c(q_x, np.int8)
     M, K = q_x.shape
+    _block(M, b, "tokens")
     q_u = np.empty((M, K), np.int8)
     s_u = np.zeros(1, np.float32)
     S = np.zeros(1, np.int64)
@@ -232,6 +248,7 @@ def wht_int_quant(q_x, b: int):
 def wht_fp_quant(dy, b: int, want_v: bool = False):
     dy = _c(dy)
     M, N = dy.shape
+    _block(M, b, "tokens")
     q_v = np.empty((M, N), np.int8)
     s_v = np.zeros(1, np.float32)
     v = np.empty((M, N), np.float32) if want_v else None
@@ -255,6 +272,9 @@ def qgemm_bwd_dw_wht(q_x, s_x, dy, b: int):
     dy = _c(dy)
     M, K = q_x.shape
     N = dy.shape[1]
+    if dy.shape[0] != M:
+        raise ValueError("dy: token count differs from q_x")
+    _block(M, b, "tokens")
     s_x = _c(np.atleast_1d(s_x), np.float32)
     dw = np.empty((N, K), np.float32)
     su = np.zeros(1, np.float32)
@@ -269,6 +289,7 @@ def wht_fp_rows_quant(dy, b: int, s_w=None, want_v: bool = False):
     LSQ.  Returns (q, s, rotated values or None, flags)."""
     dy = _c(dy)
     M, N = dy.shape
+    _block(N, b, "columns")
     q = np.empty((M, N), np.int8)
     s = np.zeros(1, np.float32)
     v = np.empty((M, N), np.float32) if want_v else None
@@ -284,6 +305,7 @@ def qgemm_bwd_dx_wht(dy, s_w, q_w, b: int):
     q_w = _c(q_w, np.int8)
     M, N = dy.shape
     K = q_w.shape[1]
+    _block(N, b, "columns")
     sw = _c(s_w, np.float32)
     dx = np.empty((M, K), np.float32)
     sg = np.zeros(1, np.float32)

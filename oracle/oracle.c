@@ -31,6 +31,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------
  * Arithmetic model -- §2.1 "Subnormals", "Fused multiply-add", Table 1.
  * Each helper performs exactly one IEEE binary32 operation and then flushes

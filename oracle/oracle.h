@@ -65,6 +65,9 @@ enum { ORC_FLAG_NONFINITE = 1 };
 
 /* OpenMP threads available to the loops over independent outputs. */
 int orc_num_threads(void);
+/* Sets that thread count (n >= 1); every value is computed by the same
+   sequential code whatever the count, so results do not depend on it. */
+void orc_set_num_threads(int n);
 
 /* ---- arithmetic model helpers, exported so the pins can probe them ---- */
 float orc_flush(float v);                 /* subnormal -> signed zero */

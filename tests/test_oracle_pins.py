@@ -468,6 +468,19 @@ def test_wht_fp_bf16_and_f32_agree(orc, syn):
     assert np.array_equal(a[0], b[0]) and a[1] == b[1]
 
 
+def test_wht_rejects_ragged_blocks(orc):
+    """The rotations need a power-of-two block dividing the rotated
+    dimension; anything else is refused before the C loops run."""
+    q = np.zeros((64, 32), np.int8)
+    dy = np.zeros((64, 32), np.float32)
+    for call in (lambda: orc.wht_int(q, 128), lambda: orc.wht_int_quant(q, 128),
+                 lambda: orc.wht_fp_quant(dy, 128), lambda: orc.wht_fp_quant(dy, 24),
+                 lambda: orc.qgemm_bwd_dw_wht(q, np.ones(1, np.float32), dy, 128),
+                 lambda: orc.wht_fp_rows_quant(dy, 64)):
+        with pytest.raises(ValueError):
+            call()
+
+
 def test_dw_gemm_rotation_identity(orc):
     """(H qx)^T (H qv) = b * qx^T qv in integers; with unit scales the dW
     GEMM returns acc * 2^-log2(b) exactly (checks transposition/indexing)."""
