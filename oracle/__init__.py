@@ -92,6 +92,14 @@ def lib():
         L.orc_adamw_decide.argtypes = [f32, f32, f32, i32, vp, vp, vp]
         L.orc_adamw_step.restype = None
         L.orc_adamw_step.argtypes = [vp, i32, vp, i32, vp, vp, i64] + [f32] * 9
+        L.orc_ascending_sum.restype = None
+        L.orc_ascending_sum.argtypes = [vp, i32, i64, vp]
+        L.orc_average.restype = None
+        L.orc_average.argtypes = [vp, i64, i64, vp]
+        L.orc_treefold.restype = None
+        L.orc_treefold.argtypes = [vp, i32, i64, vp]
+        L.orc_dp_reduce.restype = i32
+        L.orc_dp_reduce.argtypes = [vp, i32, i32, i32, i64, i32, vp]
         L.orc_sha256.restype = None
         L.orc_sha256.argtypes = [vp, C.c_uint64, vp]
         L.orc_merkle_root.restype = None
@@ -394,6 +402,57 @@ def adamw_step(param, grad, m, v, lr: float, bc1: float, bc2: float, apply: floa
     lib().orc_adamw_step(_p(p), _dtype_code(p), _p(g), _dtype_code(g), _p(m2), _p(v2), p.size,
                          lr, beta1, beta2, eps, wd, bc1, bc2, apply, clip)
     return p, m2, v2
+
+
+def _part_ptrs(parts):
+    """Contiguous fp32 copies of the contributions and a C array of their
+    addresses (the arrays are returned too, to keep them alive)."""
+    arrs = [_c(p, np.float32).reshape(-1) for p in parts]
+    n = arrs[0].size if arrs else 0
+    if any(a.size != n for a in arrs):
+        raise ValueError("contributions differ in length")
+    ptrs = (C.c_void_p * max(len(arrs), 1))(*[a.ctypes.data for a in arrs])
+    return arrs, ptrs, n
+
+
+def ascending_sum(parts):
+    """Running sum of the contributions in index order (App. A.2)."""
+    arrs, ptrs, n = _part_ptrs(parts)
+    out = np.zeros(n, np.float32)
+    lib().orc_ascending_sum(ptrs, len(arrs), n, _p(out))
+    return out
+
+
+def average(x, k: int):
+    """x * fl(1/k) (App. A.3)."""
+    x = _c(x, np.float32).reshape(-1)
+    out = np.zeros(x.size, np.float32)
+    lib().orc_average(_p(x), x.size, int(k), _p(out))
+    return out
+
+
+def treefold(parts):
+    """TreeFold over replica partials in replica order (App. A.1)."""
+    arrs, ptrs, n = _part_ptrs(parts)
+    if not 1 <= len(arrs) <= 64:
+        raise ValueError("1..64 replicas")
+    out = np.zeros(n, np.float32)
+    lib().orc_treefold(ptrs, len(arrs), n, _p(out))
+    return out
+
+
+def dp_reduce(parts, replicas: int, shards: int, accum: int = 1, average: bool = True):
+    """The whole exchange of one step (App. A): parts holds replicas*shards*
+    accum contributions in mesh order (replica-major, then shard, then
+    microbatch).  Returns (out, flags)."""
+    arrs, ptrs, n = _part_ptrs(parts)
+    if len(arrs) != replicas * shards * accum:
+        raise ValueError("parts must hold replicas * shards * accum arrays")
+    out = np.zeros(n, np.float32)
+    fl = lib().orc_dp_reduce(ptrs, replicas, shards, accum, n, int(bool(average)), _p(out))
+    if fl < 0:
+        raise ValueError("dp_reduce: counts outside 1..64 contributions")
+    return out, int(fl)
 
 
 def sha256(data: bytes) -> bytes:

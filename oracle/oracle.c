@@ -848,6 +848,129 @@ void orc_adamw_step(void* param, int pdtype, const void* grad, int gdtype,
 }
 
 /* ------------------------------------------------------------------------
+ * Deterministic data-parallel gradient exchange -- App. A "Deterministic
+ * Gradient Reduction".  The gradient of one step is reduced at three
+ * levels: microbatches on one rank, the shards of a node (intra-node
+ * reduce-scatter), and the replicas (inter-node all-reduce).  Every step is
+ * elementwise, so the reduction of element i depends only on the values at
+ * index i of the contributions; the routines below take each element
+ * through the definition on its own.
+ *
+ *   App. A.2: the contributions of shards 0 .. S-1 are added into a
+ *     running sum in ascending rank order (the inner accumulator); the
+ *     microbatch accumulation on a rank is the same running sum over its
+ *     microbatches in order.
+ *   App. A.3: every average (by the microbatch count, by dp_shard, by
+ *     dp_replicate) is a multiply by the binary32 reciprocal fl(1/k), never
+ *     a division.
+ *   App. A "Deterministic Gradient Reduction": the inner sum is finalised
+ *     and averaged once per replica (every dp_shard virtual ranks), and the
+ *     averaged replica partials go to TreeFold.
+ *   App. A.1: TreeFold pushes each replica partial once onto a stack of
+ *     (level, partial) entries; an incoming entry merges with the top while
+ *     the two have the same level, the lower replica (the stack entry) on
+ *     the left, and the merged entry moves one level up, as in binary
+ *     counting.  Result combines the entries left on the stack (one per set
+ *     bit of the replica count) in ascending level order: the entry of the
+ *     lowest level (the smallest, highest-numbered block) first, each time
+ *     with the lower-replica block on the left.  (The page's parenthesis
+ *     also calls the lowest level the largest block; the level of an entry
+ *     as Push defines it grows with the block, and §5 describes the cluster
+ *     combining the largest power-of-two block with the remainder, so the
+ *     smallest block is taken first.)
+ * ---------------------------------------------------------------------- */
+#define ORC_FOLD_MAX 64
+
+/* One element of the running sum over count contributions in ascending
+ * order: acc = c_0, then acc = fl(acc + c_j). */
+static float ascending_sum1(const float* const* parts, int count, int64_t i) {
+  float acc = orc_flush(parts[0][i]);
+  for (int j = 1; j < count; j++) acc = fadd(acc, orc_flush(parts[j][i]));
+  return acc;
+}
+
+void orc_ascending_sum(const float* const* parts, int count, int64_t n, float* out) {
+  if (count < 1 || n <= 0) return;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = ascending_sum1(parts, count, i);
+}
+
+void orc_average(const float* x, int64_t n, int64_t k, float* out) {
+  const float inv = inv_count(k);
+  for (int64_t i = 0; i < n; i++) out[i] = fmul(orc_flush(x[i]), inv);
+}
+
+/* TreeFold over the values v[0..R) of one element (replica order). */
+typedef struct {
+  int level;
+  float val;
+} fold_entry;
+
+static void fold_push(fold_entry* stack, int* depth, float v) {
+  fold_entry e = {0, v};
+  while (*depth > 0 && stack[*depth - 1].level == e.level) {
+    e.val = fadd(stack[*depth - 1].val, e.val);  /* lower replica on the left */
+    e.level += 1;
+    *depth -= 1;
+  }
+  stack[(*depth)++] = e;
+}
+
+static float fold_result(const fold_entry* stack, int depth) {
+  /* the top of the stack holds the lowest level */
+  float acc = stack[depth - 1].val;
+  for (int k = depth - 2; k >= 0; k--) acc = fadd(stack[k].val, acc);
+  return acc;
+}
+
+static float treefold1(const float* v, int R) {
+  fold_entry stack[ORC_FOLD_MAX];
+  int depth = 0;
+  for (int r = 0; r < R; r++) fold_push(stack, &depth, v[r]);
+  return fold_result(stack, depth);
+}
+
+void orc_treefold(const float* const* parts, int R, int64_t n, float* out) {
+  if (R < 1 || R > ORC_FOLD_MAX || n <= 0) return;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) {
+    float v[ORC_FOLD_MAX];
+    for (int r = 0; r < R; r++) v[r] = orc_flush(parts[r][i]);
+    out[i] = treefold1(v, R);
+  }
+}
+
+/* The whole exchange of one step, as a single device would replay it.
+ * parts: R*S*A contributions in mesh order (replica-major, then shard,
+ * then microbatch), each [n] fp32.  With average != 0 each level
+ * multiplies by the reciprocal of its count (App. A.3). */
+int orc_dp_reduce(const float* const* parts, int R, int S, int A, int64_t n,
+                  int average, float* out) {
+  if (R < 1 || S < 1 || A < 1 || R * S * A > ORC_FOLD_MAX || n < 0) return -1;
+  const float inv_a = inv_count(A), inv_s = inv_count(S), inv_r = inv_count(R);
+  int flags = 0;
+#pragma omp parallel for schedule(static) reduction(| : flags)
+  for (int64_t i = 0; i < n; i++) {
+    float rep[ORC_FOLD_MAX];
+    for (int r = 0; r < R; r++) {
+      float inner = 0.0f;
+      for (int s = 0; s < S; s++) {
+        float g = ascending_sum1(parts + (size_t)(r * S + s) * A, A, i);
+        if (average) g = fmul(g, inv_a);
+        inner = s == 0 ? g : fadd(inner, g);
+      }
+      if (average) inner = fmul(inner, inv_s);
+      rep[r] = inner;
+    }
+    float res = treefold1(rep, R);
+    if (average) res = fmul(res, inv_r);
+    out[i] = res;
+    if (!isfinite(res)) flags |= ORC_FLAG_NONFINITE;
+  }
+  return flags;
+}
+
+/* ------------------------------------------------------------------------
  * SHA-256, FIPS 180-4 §6.2, and the canonical state hash (§5 "Runtime
  * overhead" and App. B: a canonical per-step hash of the training state;
  * computed here over raw little-endian tensor bytes in a Merkle tree).

@@ -23,6 +23,8 @@
  *     "Optimizer-state precision": BF16 parameters, FP32 moments.
  *   - §3.4.2: the spike protocol (five skipped optimizer steps).
  *   - App. A.3: every average is a multiply by a precomputed reciprocal.
+ *   - App. A.1, A.2: the replicas' TreeFold and the shards' ascending-rank
+ *     running sum of the deterministic gradient exchange.
  *   - §5 "Runtime overhead" / App. B: a canonical state hash per step.
  *
  * Arithmetic model: each floating-point operation is one IEEE-754 binary32
@@ -45,6 +47,11 @@
  *   SHA-256 ......... Python hashlib (FIPS 180-4), independent Python Merkle
  *   AdamW ........... fp64 evaluation within rounding bounds, zero-gradient
  *                     and first-step closed forms, the skip-window sequence
+ *   exchange ........ hand-derived order-sensitive vectors for the ascending
+ *                     sum and TreeFold, a simulated recursive-doubling
+ *                     all-reduce (exact rationals), closed forms on powers
+ *                     of two, reciprocal averages within one ulp of the
+ *                     correctly rounded quotient
  * The butterfly stage order of the fp WHT and the RMSNorm backward operation
  * order are definitions that no external value fixes: parity unpinned beyond
  * the bounds and special cases above.
@@ -191,6 +198,24 @@ void orc_adamw_step(void* param, int pdtype, const void* grad, int gdtype,
                     float* m, float* v, int64_t n, float lr, float beta1,
                     float beta2, float eps, float wd, float bc1, float bc2,
                     float apply, float clip);
+
+/* Deterministic gradient exchange (App. A).  parts: host array of pointers
+ * to [n] fp32 contributions.
+ *   orc_ascending_sum: out = (((c_0 + c_1) + c_2) + ...) in index order.
+ *   orc_average: out = x * fl(1/k).
+ *   orc_treefold: TreeFold (binary-carry Push, Result in ascending level
+ *     order, lower replica on the left) over R <= 64 replica partials.
+ *   orc_dp_reduce: R*S*A contributions in mesh order (replica-major, then
+ *     shard, then microbatch): per shard the microbatch running sum (times
+ *     fl(1/A)), per replica the ascending shard sum (times fl(1/S)), then
+ *     TreeFold over replicas (times fl(1/R)); averages only when average
+ *     != 0.  R*S*A <= 64.  Returns flags (non-finite output), or -1 for a
+ *     count it does not take. */
+void orc_ascending_sum(const float* const* parts, int count, int64_t n, float* out);
+void orc_average(const float* x, int64_t n, int64_t k, float* out);
+void orc_treefold(const float* const* parts, int R, int64_t n, float* out);
+int orc_dp_reduce(const float* const* parts, int R, int S, int A, int64_t n,
+                  int average, float* out);
 
 /* SHA-256 (FIPS 180-4). */
 void orc_sha256(const uint8_t* msg, uint64_t len, uint8_t out[32]);

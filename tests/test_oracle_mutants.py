@@ -2,9 +2,10 @@
 
 Each mutant edits one line of oracle.c (a dropped term, a wrong sign, a
 transposed operand, a wrong rounding or constant), builds it into a
-temporary library, and runs tests/test_oracle_pins.py against it in a child
-process.  The pins pass on the real oracle and must fail on every mutant.
-All of this runs on the CPU.
+temporary library, and runs tests/test_oracle_pins.py and
+tests/test_oracle_exchange_pins.py against it in a child process.  The
+pins pass on the real oracle and must fail on every mutant.  All of this
+runs on the CPU.
 """
 import os
 import subprocess
@@ -82,6 +83,20 @@ MUTANTS = {
     "attn_codes_255": ("float s = fmul(amax, fdiv(1.0f, 127.0f));", "float s = fmul(amax, fdiv(1.0f, 255.0f));"),
     "exp_drops_a_term": ("for (int i = 6; i >= 0; i--) p = fadd(fmul(p, r), c[i]);",
                          "for (int i = 5; i >= 0; i--) p = fadd(fmul(p, r), c[i]);"),
+    "ascending_sum_descending": (
+        "  float acc = orc_flush(parts[0][i]);\n  for (int j = 1; j < count; j++) acc = fadd(acc, orc_flush(parts[j][i]));",
+        "  float acc = orc_flush(parts[count - 1][i]);\n  for (int j = count - 2; j >= 0; j--) acc = fadd(acc, orc_flush(parts[j][i]));"),
+    "treefold_result_largest_first": (
+        "  float acc = stack[depth - 1].val;\n  for (int k = depth - 2; k >= 0; k--) acc = fadd(stack[k].val, acc);",
+        "  float acc = stack[0].val;\n  for (int k = 1; k < depth; k++) acc = fadd(acc, stack[k].val);"),
+    "treefold_never_merges": ("while (*depth > 0 && stack[*depth - 1].level == e.level) {",
+                              "while (0) {"),
+    "average_divides": ("for (int64_t i = 0; i < n; i++) out[i] = fmul(orc_flush(x[i]), inv);",
+                        "for (int64_t i = 0; i < n; i++) out[i] = fdiv(orc_flush(x[i]), (float)k);"),
+    "dp_shard_average_divides": ("if (average) inner = fmul(inner, inv_s);",
+                                 "if (average) inner = fdiv(inner, (float)S);"),
+    "dp_no_replica_average": ("if (average) res = fmul(res, inv_r);", "(void)inv_r;"),
+    "dp_shard_major_mesh": ("parts + (size_t)(r * S + s) * A", "parts + (size_t)(s * R + r) * A"),
     "clip_always_scales": ("*clip = norm > max_norm ? fdiv(orc_flush(max_norm), norm) : 1.0f;",
                            "*clip = fdiv(orc_flush(max_norm), norm);"),
 }
@@ -100,6 +115,7 @@ def test_mutant_fails_pins(name, tmp_path):
                    check=True)
     env = dict(os.environ, BRQ_ORACLE_LIB=str(lib), OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_exchange_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
