@@ -21,7 +21,9 @@ PER_TENSOR, PER_ROW = 0, 1
 FLAG_NONFINITE = 1
 OP_QUANTIZE, OP_QGEMM, OP_DW_WHT, OP_RMSNORM_BWD, OP_GRAD_NORM, OP_DY_BWD = 1, 2, 3, 4, 5, 6
 OP_QUANTIZE_EXACT, OP_DX_WHT, OP_DY_ROWS_WHT = 7, 8, 9
-MAX_CONTRACTION = 133144
+MAX_CONTRACTION = 131071
+DP_MAX_PARTS = 64
+PRIM_SQRT, PRIM_RCP, PRIM_RSQRT, PRIM_BF16_CVT, PRIM_BF16_INT = 0, 1, 2, 3, 4
 
 SYMBOLS = [
     "brq_workspace_size", "brq_quantize_lsq", "brq_quantize_lsq_exact", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
@@ -31,7 +33,7 @@ SYMBOLS = [
     "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm",
     "brq_hash_workspace_size", "brq_hash_state", "brq_hash_digests_workspace_size",
     "brq_hash_tensor_digests", "brq_hash_combine", "brq_adamw_bias_corrections",
-    "brq_adamw_decide", "brq_adamw_step", "brq_status_string",
+    "brq_adamw_decide", "brq_adamw_step", "brq_dp_reduce", "brq_fp32_primitive", "brq_status_string",
     "brq_last_hip_error", "brq_spec_version",
 ]
 
@@ -129,6 +131,10 @@ def lib():
         L.brq_adamw_decide.argtypes = [vp, C.c_float, C.c_float, i32, vp, vp, vp, vp]
         L.brq_adamw_step.restype = i32
         L.brq_adamw_step.argtypes = [vp, i32, vp, i32, vp, vp, i64, vp, vp, vp]
+        L.brq_dp_reduce.restype = i32
+        L.brq_dp_reduce.argtypes = [vp, i32, i32, i32, i64, i32, vp, vp, vp]
+        L.brq_fp32_primitive.restype = i32
+        L.brq_fp32_primitive.argtypes = [i32, C.c_uint32, i64, vp, vp]
         L.brq_status_string.restype = C.c_char_p
         L.brq_status_string.argtypes = [i32]
         L.brq_last_hip_error.restype = i32
@@ -194,17 +200,22 @@ _HASH_CODES = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.i
 
 
 class Workspace:
-    """A growable device byte buffer (one per device), reused across calls
-    issued on the same stream."""
+    """Growable device byte buffers, one per (device, stream): calls on one
+    stream are ordered and may share a buffer; calls on different streams
+    get different buffers, so they may overlap (a caller that orders calls
+    across streams itself may pass ``ws=`` instead).  A buffer is allocated
+    on the stream it serves, and growing it frees the old one on that
+    stream, after the calls already issued there."""
 
     def __init__(self):
         self.buf = {}
 
     def get(self, nbytes: int, device) -> torch.Tensor:
-        key = torch.device(device)
+        dev = torch.device(device)
+        key = (dev, torch.cuda.current_stream(dev).cuda_stream)
         b = self.buf.get(key)
         if b is None or b.numel() < nbytes:
-            b = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=key)
+            b = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
             self.buf[key] = b
         return b
 
@@ -638,3 +649,39 @@ def adamw_step(param, grad, m, v, ctl, lr: float, bias_corrections, beta1: float
     _check(lib().brq_adamw_step(param.data_ptr(), _fp_code(param), grad.data_ptr(), _fp_code(grad),
                                 m.data_ptr(), v.data_ptr(), n, C.byref(hp), ctl.data_ptr(),
                                 _stream()), "adamw_step")
+
+
+# --------------------------------------------------------------------------
+# deterministic gradient exchange
+# --------------------------------------------------------------------------
+def dp_reduce(parts, replicas: int, shards: int, accum: int = 1, average: bool = True,
+              out=None, flags=None):
+    """The exchange of one step over contributions resident on this device
+    (brq_dp_reduce): parts is a list of replicas*shards*accum fp32 device
+    tensors of equal size in mesh order (replica-major, then shard, then
+    microbatch).  Returns out (fp32, the parts' shape); ``out`` may be one of
+    the parts."""
+    P = replicas * shards * accum
+    if len(parts) != P or P < 1:
+        raise BrqError("parts must hold replicas * shards * accum tensors")
+    for j, t in enumerate(parts):
+        _dev(t, f"parts[{j}]")
+        if t.dtype != torch.float32 or t.shape != parts[0].shape or t.device != parts[0].device:
+            raise BrqError("parts: fp32 tensors of one shape on one device")
+    o = _out(out, tuple(parts[0].shape), torch.float32, "out") if out is not None else \
+        torch.empty_like(parts[0])
+    ptrs = (C.c_void_p * P)(*[t.data_ptr() for t in parts])
+    _check(lib().brq_dp_reduce(ptrs, replicas, shards, accum, parts[0].numel(), int(bool(average)),
+                               _ptr(o), _ptr(flags), _stream()), "dp_reduce")
+    return o
+
+
+def fp32_primitive(prim: int, first: int, count: int, out=None, device="cuda"):
+    """The device's binary32 primitive ``prim`` (PRIM_*) on the bit patterns
+    first, first + 1, ... (mod 2^32): returns a device uint32 tensor of the
+    result bits (brq_fp32_primitive)."""
+    o = _out(out, (count,), torch.int32, "out") if out is not None else \
+        torch.empty(count, dtype=torch.int32, device=device)
+    _check(lib().brq_fp32_primitive(prim, first & 0xFFFFFFFF, count, _ptr(o), _stream()),
+           "fp32_primitive")
+    return o

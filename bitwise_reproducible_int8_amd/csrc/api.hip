@@ -473,6 +473,33 @@ int brq_adamw_step(void* param, int param_dtype, const void* grad, int grad_dtyp
       adamw_step(param, param_dtype, grad, grad_dtype, m, v, n, *hp, ctl, as_stream(stream)));
 }
 
+int brq_dp_reduce(const float* const* parts, int replicas, int shards, int accum, int64_t n,
+                  int average, float* out, int32_t* dflags, void* stream) {
+  if (n < 0) return BRQ_E_SHAPE;
+  if (replicas < 1 || shards < 1 || accum < 1) return BRQ_E_ARG;
+  if ((int64_t)replicas * shards * accum > BRQ_DP_MAX_PARTS) return BRQ_E_UNSUPPORTED;
+  if (!parts) return BRQ_E_NULL;
+  const int P = replicas * shards * accum;
+  if (n > 0) {
+    if (!out) return BRQ_E_NULL;
+    for (int j = 0; j < P; ++j)
+      if (!parts[j]) return BRQ_E_NULL;
+  }
+  if (!aligned16(out)) return BRQ_E_ALIGN;
+  for (int j = 0; j < P; ++j)
+    if (!aligned16(parts[j])) return BRQ_E_ALIGN;
+  return hip_status(
+      dp_reduce(parts, replicas, shards, accum, n, average, out, dflags, as_stream(stream)));
+}
+
+int brq_fp32_primitive(int prim, uint32_t first, int64_t count, uint32_t* out, void* stream) {
+  if (prim < BRQ_PRIM_SQRT || prim > BRQ_PRIM_BF16_INT) return BRQ_E_ARG;
+  if (count < 0 || count > ((int64_t)1 << 32)) return BRQ_E_SHAPE;
+  if (count > 0 && !out) return BRQ_E_NULL;
+  if (!aligned16(out)) return BRQ_E_ALIGN;
+  return hip_status(fp32_primitive(prim, first, count, out, as_stream(stream)));
+}
+
 size_t brq_hash_workspace_size(const brq_tensor_ref* t, int n) {
   if (n < 0 || (n > 0 && !t)) return 0;
   return hash_ws(t, n);

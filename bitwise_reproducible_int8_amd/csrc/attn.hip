@@ -257,8 +257,8 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ q
     pmax = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
     const float inv127 = 1.0f / 127.0f;
     const float sp = fmul(pmax, inv127), sv = fmul(vmax, inv127);
-    const float rp = sp == 0.0f ? 0.0f : flush(1.0f / sp);
-    const float rv = sv == 0.0f ? 0.0f : flush(1.0f / sv);
+    const float rp = sp == 0.0f ? 0.0f : fl_div(1.0f, sp);
+    const float rv = sv == 0.0f ? 0.0f : fl_div(1.0f, sv);
     // P codes
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ q
   }
   __syncthreads();
   const float lr = s_l[orow];
-  const float il = flush(1.0f / lr);
+  const float il = fl_div(1.0f, lr);
   float* O = o + (h * T + qb * kBlk + orow) * D + ocol;
 #pragma unroll
   for (int e = 0; e < kOut; e += 4) {

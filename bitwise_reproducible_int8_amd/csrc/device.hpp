@@ -31,6 +31,13 @@ __device__ __forceinline__ float flush_nonneg(float v) {
 __device__ __forceinline__ float fadd(float a, float b) { return flush(a + b); }
 __device__ __forceinline__ float fsub(float a, float b) { return flush(a - b); }
 __device__ __forceinline__ float fmul(float a, float b) { return flush(a * b); }
+// Division and square root: the correctly rounded binary32 operations (the
+// library is built with -fhip-fp32-correctly-rounded-divide-sqrt), then the
+// flush.  Every kernel divides and takes square roots through these two, and
+// brq_fp32_primitive runs the same two on any range of inputs, so a sweep of
+// all 2^32 binary32 patterns checks what the kernels execute.
+__device__ __forceinline__ float fl_div(float a, float b) { return flush(a / b); }
+__device__ __forceinline__ float fl_sqrt(float a) { return flush(__builtin_sqrtf(a)); }
 __device__ __forceinline__ float fabs_bits(float a) {
   return __uint_as_float(__float_as_uint(a) & 0x7fffffffu);
 }

@@ -366,9 +366,9 @@ __global__ __launch_bounds__(1024) void k_dy_finalize(const float* __restrict__ 
     const float sg = fmul(fmul(sum_g[0], inv_n), lsq_k2());
     const float sv = fmul(fmul(sum_v[0], inv_n), lsq_k2());
     sr4[0] = sg;
-    sr4[1] = sg == 0.0f ? 0.0f : flush(1.0f / sg);
+    sr4[1] = sg == 0.0f ? 0.0f : fl_div(1.0f, sg);
     sr4[2] = sv;
-    sr4[3] = sv == 0.0f ? 0.0f : flush(1.0f / sv);
+    sr4[3] = sv == 0.0f ? 0.0f : fl_div(1.0f, sv);
     s_g[0] = sg;
     s_v[0] = sv;
     if (amax_g) amax_g[0] = fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3]));

@@ -475,7 +475,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_exact(const T* __restrict__ 
   if (!live) return;
   const float S = srow[wave];
   const float sc = fmul(fmul(S, inv_cols), lsq_k2());
-  const float r = (sc == 0.0f) ? 0.0f : flush(1.0f / sc);
+  const float r = (sc == 0.0f) ? 0.0f : fl_div(1.0f, sc);
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int64_t c0 = (int64_t)(v * 64 + lane) * E;

@@ -4,7 +4,7 @@
 // Every GEMM of the layer is C[i][j] = epi(sum_k A[i][k] * B[j][k]) with both
 // operands contiguous along the contraction (forward: q_x, q_w; dX: q_g,
 // q_w^T; dW: the token-contiguous rotated codes q_v^T, q_u^T).  The int32
-// sum is exact -- 127*127*K < 2^31 for K <= 133144 -- so tile shape, MFMA
+// sum is exact -- 128*128*K < 2^31 for K <= 131071 -- so tile shape, MFMA
 // shape, split-K and launch order cannot change a bit of it; only the
 // dequantisation epilogue is floating point:
 //     out = fl(fl(acc) * c_j)   one int->fp32 conversion (round to nearest

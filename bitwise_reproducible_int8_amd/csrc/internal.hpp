@@ -130,6 +130,14 @@ hipError_t rmsnorm_bwd(const void* x, const void* g, const float* rstd,
 hipError_t grad_norm(const float* v, int64_t n, float* sumsq, float* norm,
                      void* ws, int chunk_log2, int32_t* dflags, hipStream_t s);
 
+// ---- deterministic gradient exchange (exchange.hip) ------------------------------
+// parts: host array of R*S*A device pointers in mesh order.
+hipError_t dp_reduce(const float* const* parts, int R, int S, int A, int64_t n, int average,
+                     float* out, int32_t* dflags, hipStream_t s);
+
+// ---- binary32 primitives over a range of bit patterns (primitive.hip) -------------
+hipError_t fp32_primitive(int prim, uint32_t first, int64_t count, uint32_t* out, hipStream_t s);
+
 // ---- hash ------------------------------------------------------------------------
 size_t hash_ws(const brq_tensor_ref* t, int n);
 size_t hash_digests_ws(const brq_tensor_ref* t, int n);

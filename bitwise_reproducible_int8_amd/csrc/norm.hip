@@ -17,6 +17,8 @@
 // of the token tree.  Fold kernels then combine those per-block nodes 32 at
 // a time with the same stack, padding past the last block with -0, until one
 // node per column remains.
+#include <string.h>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256) void k_rms_fwd(const T* __restrict__ x, const 
   }
   const float ss = reg_tree<false, V>(node);
   const float ms = fmul(ss, invD);
-  const float r = flush(1.0f / flush(__builtin_sqrtf(fadd(ms, eps))));
+  const float r = fl_div(1.0f, fl_sqrt(fadd(ms, eps)));
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int64_t c0 = (int64_t)(v * 64 + lane) * E;
@@ -93,7 +95,12 @@ hipError_t rmsnorm_fwd(const void* x, const void* g, int dtype, int64_t T, int64
   int V = 1;
   while (V < per) V *= 2;
   const float invD = 1.0f / (float)D;
-  const float e = eps;
+  // eps is an input like any other: a subnormal eps reads as a signed zero
+  uint32_t eb;
+  memcpy(&eb, &eps, 4);
+  if ((eb & 0x7f800000u) == 0u) eb &= 0x80000000u;
+  float e;
+  memcpy(&e, &eb, 4);
   dim3 gr((unsigned)cdiv(T, 4)), b(256);
 #define BRQ_F(TT, VV)                                                                            \
   hipLaunchKernelGGL((k_rms_fwd<TT, VV>), gr, b, 0, s, (const TT*)x, (const TT*)g, T, D, invD, \
@@ -588,7 +595,7 @@ hipError_t rmsnorm_bwd(const void* x, const void* g, const float* rstd, const vo
 __global__ void k_gn_finalize(const float* sum_max, float* sumsq, float* norm) {
   const float ss = sum_max[0];
   sumsq[0] = ss;
-  norm[0] = flush(__builtin_sqrtf(ss));
+  norm[0] = fl_sqrt(ss);
 }
 
 hipError_t grad_norm(const float* v, int64_t n, float* sumsq, float* norm, void* ws,

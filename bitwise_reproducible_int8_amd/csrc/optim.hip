@@ -25,9 +25,6 @@ namespace brq {
 
 namespace {
 
-__device__ __forceinline__ float fdiv(float a, float b) { return flush(a / b); }
-__device__ __forceinline__ float fsqrt(float a) { return flush(__builtin_sqrtf(a)); }
-
 __global__ void k_adamw_decide(const float* __restrict__ norm_in, float max_norm, float spike,
                                int skip_steps, int32_t* skip_state, float* ctl,
                                int32_t* dflags) {
@@ -43,7 +40,7 @@ __global__ void k_adamw_decide(const float* __restrict__ norm_in, float max_norm
     clip = 0.0f;
   } else {
     apply = 1.0f;
-    clip = norm > flush(max_norm) ? fdiv(flush(max_norm), norm) : 1.0f;
+    clip = norm > flush(max_norm) ? fl_div(flush(max_norm), norm) : 1.0f;
   }
   skip_state[0] = st;
   ctl[0] = apply;
@@ -125,9 +122,9 @@ __global__ __launch_bounds__(256) void k_adamw_step(TP* __restrict__ param,
     if (clip != 1.0f) ge = fmul(ge, clip);
     const float mi = fadd(fmul(hp.beta1, mm[e]), fmul(omb1, ge));
     const float vi = fadd(fmul(hp.beta2, vv[e]), fmul(omb2, fmul(ge, ge)));
-    const float mh = fdiv(mi, hp.bc1);
-    const float vh = fdiv(vi, hp.bc2);
-    const float u = fdiv(mh, fadd(fsqrt(vh), hp.eps));
+    const float mh = fl_div(mi, hp.bc1);
+    const float vh = fl_div(vi, hp.bc2);
+    const float u = fl_div(mh, fadd(fl_sqrt(vh), hp.eps));
     p[e] = fsub(p[e], fmul(hp.lr, fadd(u, fmul(hp.wd, p[e]))));
     mm[e] = mi;
     vv[e] = vi;

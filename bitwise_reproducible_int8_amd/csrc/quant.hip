@@ -389,7 +389,7 @@ __global__ void k_lsq_finalize(const float* sum_max, float inv_n, float* sr, flo
                                float* amax) {
   float m = fmul(sum_max[0], inv_n);
   float sc = fmul(m, lsq_k2());
-  float r = (sc == 0.0f) ? 0.0f : flush(1.0f / sc);
+  float r = (sc == 0.0f) ? 0.0f : fl_div(1.0f, sc);
   sr[0] = sc;
   sr[1] = r;
   if (scale) scale[0] = sc;
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
   const float S = reg_tree<false, V>(node);
   mx = wave_max(mx);
   const float sc = fmul(fmul(S, inv_cols), lsq_k2());
-  const float r = (sc == 0.0f) ? 0.0f : flush(1.0f / sc);
+  const float r = (sc == 0.0f) ? 0.0f : fl_div(1.0f, sc);
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int64_t c0 = (int64_t)(v * 64 + lane) * E;

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void k_wht_int_finalize(const long long* __res
     long long S = ws[0] + ws[1] + ws[2] + ws[3];
     float Sf = (float)(double)S;  // exact in double (S < 2^53), one rounding
     float sc = fmul(fmul(Sf, inv_n), lsq_k2());
-    float r = (sc == 0.0f) ? 0.0f : flush(1.0f / sc);
+    float r = (sc == 0.0f) ? 0.0f : fl_div(1.0f, sc);
     sr[0] = sc;
     sr[1] = r;
     if (s_out) s_out[0] = sc;

@@ -24,6 +24,10 @@ micro-batches; §3.1 Table 3, §3.2 "Batch size"):
          4096): inputs bf16 N(0,1), weights bf16 N(0,0.02), dY per linear bf16
          N(0,1e-3); plus the layer's two RMSNorms at the norm recipe's
          distributions (h with 1% bf16 subnormals, g 1+N(0,0.1), dy N(0,1e-3))
+  exchange  fp32 gradient contributions N(0,1e-4), one Philox tag each; at
+         full size one rank's share of the Open-1B gradient (1.61e9 values)
+         reduce-scattered over 8 shards: the grad-norm vector (the norm
+         recipe's v) viewed as 8 contributions of 201.25e6 values
 """
 from __future__ import annotations
 
@@ -223,3 +227,9 @@ def optimizer_group(n, grad_std=1e-4, param_bf16=True, grad_bf16=False, group=0,
     m = normal((n,), grad_std / 10, tag=tag_for(base, TAG_M), seed=seed)
     v = np.abs(normal((n,), grad_std * grad_std, tag=tag_for(base, TAG_S), seed=seed))
     return p, g, m, v
+
+
+def exchange_parts(count, n, std=1e-4, seed=SEED):
+    """count fp32 gradient contributions of n values, N(0, std), tag per
+    contribution."""
+    return [normal((n,), std, tag=tag_for(60 + j, TAG_V), seed=seed) for j in range(count)]

@@ -60,9 +60,10 @@ enum brq_dtype { BRQ_F32 = 0, BRQ_BF16 = 1, BRQ_I8 = 2, BRQ_I32 = 3, BRQ_U8 = 4 
 enum brq_gran { BRQ_PER_TENSOR = 0, BRQ_PER_ROW = 1 };
 enum brq_flag { BRQ_FLAG_NONFINITE = 1 };
 
-/* Longest contraction whose int8 x int8 sums stay inside int32:
- * 127 * 127 * 133144 < 2^31. */
-#define BRQ_MAX_CONTRACTION 133144
+/* Longest contraction whose int8 x int8 sums stay inside int32 for any
+ * int8 codes, -128 included: 128 * 128 * 131071 < 2^31.  (The quantisers
+ * here emit codes in [-127, 127]; the bound does not rely on it.) */
+#define BRQ_MAX_CONTRACTION 131071
 
 /* Launch geometry.  None of these fields changes any result bit. */
 typedef struct brq_tune {
@@ -426,6 +427,68 @@ int brq_adamw_decide(const float* norm, float max_norm, float spike_threshold,
 int brq_adamw_step(void* param, int param_dtype, const void* grad, int grad_dtype,
                    float* m, float* v, int64_t n, const brq_adamw_hparams* hp,
                    const float* ctl, void* stream);
+
+/* ---------------------------------------------------------------------
+ * dp_reduce -- the arithmetic of the deterministic data-parallel gradient
+ * exchange (App. A "Deterministic Gradient Reduction"), over contributions
+ * resident on this device.  Per element i, every operation one rounded
+ * binary32 operation (inputs read with DAZ, results flushed):
+ *   for each replica r and shard s: g = c[r][s][0] + c[r][s][1] + ...,
+ *     a running sum over the accum microbatches in order; g = fl(g * fl(1/A));
+ *   for each replica r: inner = g[r][0] + g[r][1] + ..., a running sum over
+ *     the shards in ascending rank order (App. A.2, the local sum of the
+ *     deterministic reduce-scatter after its all-to-all);
+ *     p[r] = fl(inner * fl(1/S));
+ *   TreeFold over p[0..R) (App. A.1, the pairing of the recursive-doubling
+ *     all-reduce): each p[r] is pushed once onto a stack of (level, value);
+ *     an entry merges with the top while their levels are equal, the
+ *     stack's (lower-replica) value on the left, and moves one level up;
+ *     the entries left (one per set bit of R) are combined from the lowest
+ *     level (the smallest block) up, the lower-replica block on the left.
+ *     For R a power of two this is the balanced pairwise tree.
+ *   out[i] = fl(result * fl(1/R)).
+ * Each fl(1/k) is the binary32 reciprocal of the count (App. A.3: averages
+ * are reciprocal multiplies, never divisions); with average == 0 no level
+ * multiplies.  Special cases: replicas = accum = 1 is the reduce-scatter's
+ * ascending-rank sum; shards = accum = 1 is the replica all-reduce; R = 2,
+ * S = A = 1, average = 0 is one recursive-doubling hop fl(lo + hi).
+ * parts: HOST array of replicas*shards*accum DEVICE pointers in mesh order
+ * (replica-major, then shard, then microbatch), each [n] fp32, 16-byte
+ * aligned; out [n] fp32, 16-byte aligned, may be one of the parts (in
+ * place).  1 <= replicas*shards*accum <= BRQ_DP_MAX_PARTS.  Raises
+ * BRQ_FLAG_NONFINITE when an output is not finite.  No workspace.
+ * --------------------------------------------------------------------- */
+#define BRQ_DP_MAX_PARTS 64
+int brq_dp_reduce(const float* const* parts, int replicas, int shards, int accum,
+                  int64_t n, int average, float* out, int32_t* dflags, void* stream);
+
+/* ---------------------------------------------------------------------
+ * fp32_primitive -- the device's binary32 primitives over a range of inputs,
+ * to check them bit for bit against another machine (§2 "The same
+ * operation compiles to different instructions", §2.1 Table 1).  Input i
+ * is the binary32 bit pattern x = first + i (mod 2^32), i < count; out[i]
+ * (device uint32 [count], 16-byte aligned) receives the result's bits:
+ *   BRQ_PRIM_SQRT      fl(sqrt(daz(x)))             (grad-norm, AdamW)
+ *   BRQ_PRIM_RCP       fl(1 / daz(x))               (quantiser reciprocal)
+ *   BRQ_PRIM_RSQRT     fl(1 / fl(sqrt(daz(x))))     (RMSNorm rstd)
+ *   BRQ_PRIM_BF16_CVT  bf16 of x, nearest even, by the conversion
+ *                      instruction the bf16 stores use (low 16 bits)
+ *   BRQ_PRIM_BF16_INT  bf16 of x, nearest even, by integer arithmetic on
+ *                      the bit pattern (low 16 bits)
+ * daz() reads a subnormal as a signed zero and fl() flushes a subnormal
+ * result, as in every kernel; division and square root are the ones every
+ * kernel uses.  A NaN result may carry any quiet-NaN payload.  No
+ * workspace; count <= 2^32.
+ * --------------------------------------------------------------------- */
+enum brq_prim {
+  BRQ_PRIM_SQRT = 0,
+  BRQ_PRIM_RCP = 1,
+  BRQ_PRIM_RSQRT = 2,
+  BRQ_PRIM_BF16_CVT = 3,
+  BRQ_PRIM_BF16_INT = 4
+};
+int brq_fp32_primitive(int prim, uint32_t first, int64_t count, uint32_t* out,
+                       void* stream);
 
 /* Status text, HIP error of the last BRQ_E_HIP in this thread, version. */
 const char* brq_status_string(int status);

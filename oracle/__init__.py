@@ -100,6 +100,8 @@ def lib():
         L.orc_treefold.argtypes = [vp, i32, i64, vp]
         L.orc_dp_reduce.restype = i32
         L.orc_dp_reduce.argtypes = [vp, i32, i32, i32, i64, i32, vp]
+        L.orc_prim_sweep.restype = None
+        L.orc_prim_sweep.argtypes = [i32, C.c_uint32, i64, vp]
         L.orc_sha256.restype = None
         L.orc_sha256.argtypes = [vp, C.c_uint64, vp]
         L.orc_merkle_root.restype = None
@@ -453,6 +455,14 @@ def dp_reduce(parts, replicas: int, shards: int, accum: int = 1, average: bool =
     if fl < 0:
         raise ValueError("dp_reduce: counts outside 1..64 contributions")
     return out, int(fl)
+
+
+def prim_sweep(prim: int, first: int, count: int, out=None):
+    """The model's primitive ``prim`` on the bit patterns first + i (uint32
+    results; see orc_prim_sweep)."""
+    o = np.empty(count, np.uint32) if out is None else out
+    lib().orc_prim_sweep(prim, first & 0xFFFFFFFF, count, _p(o))
+    return o
 
 
 def sha256(data: bytes) -> bytes:

@@ -85,6 +85,26 @@ static void store(void* p, int dtype, int64_t i, float v) {
   else ((float*)p)[i] = v;
 }
 
+/* The model's primitives over a range of bit patterns, input i being the
+ * pattern first + i: the host side of a sweep that compares a device's
+ * division, square root and bf16 rounding with these (§2 "The same operation
+ * compiles to different instructions").  x86 SSE division and square root
+ * are the correctly rounded IEEE operations. */
+void orc_prim_sweep(int prim, uint32_t first, int64_t count, uint32_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < count; i++) {
+    const float x = u2f(first + (uint32_t)i);
+    uint32_t r;
+    switch (prim) {
+      case 0: r = f2u(fsqrt(orc_flush(x))); break;
+      case 1: r = f2u(fdiv(1.0f, orc_flush(x))); break;
+      case 2: r = f2u(fdiv(1.0f, fsqrt(orc_flush(x)))); break;
+      default: r = orc_f32_to_bf16(x); break;
+    }
+    out[i] = r;
+  }
+}
+
 /* ------------------------------------------------------------------------
  * Canonical reduction tree -- §2.1 "Reduction order", Table 1 row 2.
  * Level 0 holds the leaves in logical row-major order; each level pairs

@@ -83,6 +83,11 @@ uint16_t orc_f32_to_bf16(float f);        /* RNE on the bit pattern */
 float orc_lsq_k2(void);                   /* 2 * fl(1/fl(sqrt(127))) */
 void orc_f32_to_bf16_array(const float* in, int64_t n, uint16_t* out);
 
+/* Primitives over the bit patterns first, first + 1, ... (count of them):
+ * prim 0 fl(sqrt(daz(x))), 1 fl(1/daz(x)), 2 fl(1/fl(sqrt(daz(x)))), 3 and 4
+ * the bf16 rounding of x (nearest even) in the low 16 bits. */
+void orc_prim_sweep(int prim, uint32_t first, int64_t count, uint32_t* out);
+
 /* Canonical pairwise tree over leaves[0..n): node(j+1,i) = node(j,2i) +
  * node(j,2i+1) when the right child exists, else node(j,2i).  Two codings. */
 float orc_tree_sum(const float* leaves, int64_t n);

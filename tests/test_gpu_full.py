@@ -1,5 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (default tune): every output's SHA-256 against the digests
+benchmark times (default tune) and, for the MLP and layer workloads, under
+two other launch configurations (GEMM kernel, split-K, reduction chunk and
+RMSNorm backward rows per block): every output's SHA-256 against the digests
 the CPU oracle wrote (tests/golden/config_digests.txt, produced by
 tests/golden/make_digests.py from oracle/ alone), plus outputs the oracle
 recomputes here row by row, so a mismatch names where it is.
@@ -85,19 +87,40 @@ def test_qkv_full(brq):
                           "y": y, "q_w_pt": qp, "s_w_pt": sp, "amax_w_pt": ap, "y_pt": ypt})
 
 
-@pytest.mark.timeout(900)
-def test_mlp_full(brq):
-    say("full mlp 16384x2048->8192 fwd+bwd")
+# Launch configurations the full-size workloads also run under: the
+# benchmark's default plan, the 8-wave direct-to-LDS GEMM with the
+# contraction split in two (exact int32 partials) and the smallest
+# reduction chunk, and the persistent GEMM split in two with the largest
+# chunk; RMSNorm backward at 4 and 8 rows per block.
+FULL_TUNES = [None,
+              dict(gemm_kernel=10, split_k=2, chunk_log2=10, rows_per_block=4),
+              dict(gemm_kernel=13, split_k=2, chunk_log2=16, rows_per_block=8)]
+
+
+def _tid(t):
+    return "default" if t is None else "k{gemm_kernel}-s{split_k}-c{chunk_log2}-r{rows_per_block}".format(**t)
+
+
+@pytest.fixture(scope="module")
+def mlp_data():
     d = syn.mlp()
+    return d, to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("tune", FULL_TUNES, ids=_tid)
+def test_mlp_full(brq, mlp_data, tune):
+    say("full mlp 16384x2048->8192 fwd+bwd", tune)
+    d, X, W, DY = mlp_data
     b = d["block"]
-    X, W, DY = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
     flags = torch.zeros(1, dtype=torch.int32, device=DEV)
-    qx, _, sx, ax = brq.quantize_lsq(X, flags=flags)
-    qw, qwt, sw, aw = brq.quantize_lsq(W, per_row=True, want_t=True, flags=flags)
-    y = brq.qgemm_fwd(qx, sx, qw, sw)
-    qg, _, sg, ag = brq.quantize_lsq(DY, col_mul=sw, flags=flags)
-    dx = brq.qgemm_bwd_dx(qg, sg, qwt)
-    dw, su, sv, qut, qvt = brq.qgemm_bwd_dw_wht(qx, sx, DY, b, flags=flags, return_codes=True)
+    qx, _, sx, ax = brq.quantize_lsq(X, flags=flags, tune=tune)
+    qw, qwt, sw, aw = brq.quantize_lsq(W, per_row=True, want_t=True, flags=flags, tune=tune)
+    y = brq.qgemm_fwd(qx, sx, qw, sw, tune=tune)
+    qg, _, sg, ag = brq.quantize_lsq(DY, col_mul=sw, flags=flags, tune=tune)
+    dx = brq.qgemm_bwd_dx(qg, sg, qwt, tune=tune)
+    dw, su, sv, qut, qvt = brq.qgemm_bwd_dw_wht(qx, sx, DY, b, flags=flags, return_codes=True,
+                                                tune=tune)
     torch.cuda.synchronize()
     assert int(flags.item()) == 0
     got = {"q_x": qx, "s_x": sx, "amax_x": ax, "q_w": qw, "q_wt": qwt, "s_w": sw, "amax_w": aw,
@@ -146,19 +169,26 @@ def test_norm_full(brq):
     check_digests("norm", got)
 
 
-@pytest.mark.timeout(900)
-def test_layer_full(brq):
-    """The benchmark's step: digests of every output, gradient and scale,
-    and the on-device state hash."""
-    say("full layer 32768 tokens (the benchmark step)")
-    from bitwise_reproducible_int8_amd.layer import LayerStep
+@pytest.fixture(scope="module")
+def layer_data():
     M = 32768
     x = {name: to_dev(syn.layer_input(name, M)) for name, _ in syn.LAYER_INPUTS}
     w = [to_dev(syn.layer_weight(i)) for i in range(len(syn.LAYER_LINEARS))]
     dy = [to_dev(syn.layer_dy(i, M)) for i in range(len(syn.LAYER_LINEARS))]
     norms = [(n,) + tuple(to_dev(a) for a in syn.layer_norm_inputs(j, M))
              for j, (n, _) in enumerate(syn.LAYER_NORMS)]
-    step = LayerStep(syn.LAYER_LINEARS, x, w, dy, norms, block=128)
+    return M, x, w, dy, norms
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("tune", FULL_TUNES, ids=_tid)
+def test_layer_full(brq, layer_data, tune):
+    """The benchmark's step: digests of every output, gradient and scale,
+    and the on-device state hash."""
+    say("full layer 32768 tokens (the benchmark step)", tune)
+    from bitwise_reproducible_int8_amd.layer import LayerStep
+    M, x, w, dy, norms = layer_data
+    step = LayerStep(syn.LAYER_LINEARS, x, w, dy, norms, block=128, tune=tune)
     step.run()
     torch.cuda.synchronize()
     assert int(step.flags.item()) == 0

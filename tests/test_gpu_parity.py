@@ -110,20 +110,85 @@ def test_quantize_edge_cases():
     assert_bitwise(gs, s, "s subnormal")
 
 
-def test_quantize_ties_and_clamps():
-    """Values landing exactly on x*r = k + 1/2 and beyond +-127.5."""
-    say("quantize_ties")
+def _plant_ties(x, scale, per_row, cm, rng, pairs_per_group):
+    """Turn level-1 leaf pairs (2i, 2i+1) of the |x| tree into (t, u) with
+    fl(t * r) = k + 1/2 for a random k, and u = c - t exact where c is the
+    pair's node fl(leaf_2i + leaf_2i+1): the node, and with it the tree sum
+    and the step size, keep their bits, so the codes of the t values are
+    exact ties.  Leaves are |x * cm[col]|; cm holds powers of two, so the
+    leaf is |x| times cm exactly.  Returns the number of pairs changed."""
+    rows, cols = x.shape
+    mult = np.ones(cols, np.float32) if cm is None else cm
+    planted = 0
+    groups = range(rows) if per_row else [None]
+    flat = x.reshape(-1)
+    for g in groups:
+        s = np.float32(scale[g if per_row else 0])
+        r = np.float32(1) / s
+        base = g * cols if per_row else 0
+        n = cols if per_row else x.size
+        for p in rng.choice(n // 2, size=min(pairs_per_group, n // 2), replace=False):
+            i0 = base + 2 * p
+            m0, m1 = mult[i0 % cols], mult[(i0 + 1) % cols]
+            a, b = abs(flat[i0]) * m0, abs(flat[i0 + 1]) * m1
+            c = np.float32(a + b)
+            top = int(np.floor(float(c) * float(r) - 0.5))
+            if top < 0:
+                continue
+            k = int(rng.integers(0, min(126, top) + 1))
+            t0 = np.float32((k + 0.5) / float(r))
+            found = None
+            for d in range(-4, 5):
+                t = t0
+                for _ in range(abs(d)):
+                    t = np.nextafter(t, np.float32(np.inf) if d > 0 else np.float32(-np.inf))
+                if np.float32(t * r) == np.float32(k + 0.5) and t <= c:
+                    u = np.float32(c - t)
+                    if float(u) == float(c) - float(t) and np.float32(t + u) == c:
+                        found = (t, u)
+                        break
+            if found is None:
+                continue
+            t, u = found
+            sg = rng.choice([-1.0, 1.0], size=2).astype(np.float32)
+            flat[i0] = sg[0] * t / m0
+            flat[i0 + 1] = sg[1] * u / m1
+            planted += 1
+    return planted
+
+
+def _count_ties(x, scale, per_row, cm):
+    rows, cols = x.shape
+    v = x * (np.ones(cols, np.float32) if cm is None else cm)[None, :]
+    r = (np.float32(1) / np.asarray(scale, np.float32)).astype(np.float32)
+    p = (v * (r[:, None] if per_row else r[0])).astype(np.float32)
+    return int(np.sum(np.abs(p - np.trunc(p)) == np.float32(0.5)))
+
+
+@pytest.mark.parametrize("mode", ["per_tensor", "per_row", "col_mul"])
+def test_quantize_ties_and_clamps(mode):
+    """Exact ties x*r = k + 1/2 (round half to even) that leave the step
+    size's bits unchanged, plus clamps beyond +-127.5."""
+    say("quantize_ties", mode)
     rng = np.random.default_rng(5)
-    base = rng.standard_normal((64, 128)).astype(np.float32)
-    q0, _, s0, _, _ = orc.quantize_lsq(base)
-    st = np.float32(s0[0])
-    half = (np.arange(-130, 130, dtype=np.float32) + np.float32(0.5)) * st
-    base.reshape(-1)[:half.size] = half
-    base[10, :8] = np.float32(1000) * st
-    q, _, s, _, _ = orc.quantize_lsq(base)
-    gq, _, gs, _ = brq.quantize_lsq(to_dev(base))
-    assert_bitwise(gq, q, "q ties")
-    assert_bitwise(gs, s, "s ties")
+    per_row = mode == "per_row"
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    x[10, :8] = np.float32(1000)  # clamps: in the tensor before its statistic
+    x[11, 8:16] = np.float32(-1000)
+    cm = np.exp2(rng.integers(-2, 3, 256)).astype(np.float32) if mode == "col_mul" else None
+    _, _, s0, _, _ = orc.quantize_lsq(x, per_row=per_row, col_mul=cm)
+    planted = _plant_ties(x, s0, per_row, cm, rng, 8 if per_row else 400)
+    q, _, s, amax, fl = orc.quantize_lsq(x, per_row=per_row, col_mul=cm)
+    assert np.array_equal(np.asarray(s).view(np.uint32), np.asarray(s0).view(np.uint32)), \
+        "planting must keep the step size"
+    ties = _count_ties(x, s, per_row, cm)
+    assert planted >= 100 and ties >= 100, (planted, ties)
+    assert np.any(np.abs(q) == 127)
+    gq, _, gs, gamax = brq.quantize_lsq(to_dev(x), per_row=per_row,
+                                        col_mul=None if cm is None else to_dev(cm))
+    assert_bitwise(gq, q, f"q ties {mode}")
+    assert_bitwise(gs, s, f"s ties {mode}")
+    assert_bitwise(gamax, amax, f"amax ties {mode}")
 
 
 # --------------------------------------------------------------------------
@@ -236,12 +301,15 @@ def test_qgemm_bf16_outputs_many_tiles():
 
 
 def test_gemm_extreme_accumulator():
-    """All-127 codes at the int32 bound of the contraction."""
+    """Codes of magnitude 127 and 128 at the int32 bound of the contraction
+    (128 * 128 * K < 2^31)."""
     say("gemm_extreme")
-    K = 133136  # multiple of 16, <= 133144
-    qx = np.full((2, K), 127, np.int8)
+    K = 131056  # the largest multiple of 16 <= 131071
+    qx = np.full((3, K), 127, np.int8)
     qx[1] = -127
+    qx[2] = -128
     qw = np.full((3, K), 127, np.int8)
+    qw[2] = -128
     one = np.ones(1, np.float32)
     want = orc.qgemm_fwd(qx, one, qw, np.ones(3, np.float32))
     for t in GEMM_TUNES:
@@ -414,6 +482,27 @@ def test_rmsnorm_fwd(T, D, bf16):
     gy, grstd = brq.rmsnorm_fixed_fwd(to_dev(x), to_dev(g), 1e-6)
     assert_bitwise(gy, y, "y")
     assert_bitwise(grstd, rstd, "rstd")
+
+
+def test_rmsnorm_fwd_subnormal_eps():
+    """A subnormal eps reads as zero (DAZ on every input): rows whose mean
+    square sits just above 2^-126, where an unflushed eps of 1e-40 would
+    move rstd."""
+    say("rmsnorm_fwd_subnormal_eps")
+    rng = np.random.default_rng(11)
+    T, D = 40, 512
+    x = (rng.standard_normal((T, D)) * 2.0 ** -62).astype(np.float32)
+    x[0] = np.float32(2.0 ** -63)  # ms = 2^-126 exactly
+    x[1] = np.float32(-(2.0 ** -62))
+    g = syn.normal((D,), 0.1, mean=1.0, tag=209)
+    for eps in (1e-40, -1e-40, 0.0, 1e-6):
+        y, rstd, fl = orc.rmsnorm_fwd(x, g, eps)
+        gy, grstd = brq.rmsnorm_fixed_fwd(to_dev(x), to_dev(g), eps)
+        assert_bitwise(grstd, rstd, f"rstd eps={eps}")
+        assert_bitwise(gy, y, f"y eps={eps}")
+    _, r0, _ = orc.rmsnorm_fwd(x, g, 0.0)
+    _, r1, _ = orc.rmsnorm_fwd(x, g, 1e-40)
+    assert np.array_equal(r0, r1)
 
 
 @pytest.mark.parametrize("T,D,bf16", [(100, 2048, True), (64, 264, True), (33, 512, False),

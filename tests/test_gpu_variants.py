@@ -82,9 +82,5 @@ def test_per_tensor_w_scales_k_linear_full():
                           (gsw, sw, "s_w"), (gqg, qg, "q_g"), (gsg, sg, "s_g")):
         assert_bitwise(g, want, name)
     rows = np.array([0, 3, 8191, 8192, 20000, 32767])
-    c = np.float32(np.float32(sx[0]) * np.float32(sw[0]))
-    acc = qx[rows].astype(np.int64) @ qw.astype(np.int64).T
-    assert_bitwise(to_np(gy)[rows], (acc.astype(np.float32) * c).astype(np.float32), "y rows")
-    acc = qg[rows].astype(np.int64) @ qw.astype(np.int64)
-    assert_bitwise(to_np(gdx)[rows], (acc.astype(np.float32) * np.float32(sg[0])).astype(np.float32),
-                   "dx rows")
+    assert_bitwise(to_np(gy)[rows], orc.qgemm_fwd(qx[rows], sx, qw, sw), "y rows")
+    assert_bitwise(to_np(gdx)[rows], orc.qgemm_bwd_dx(qg[rows], sg, qw), "dx rows")

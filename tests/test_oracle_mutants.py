@@ -33,6 +33,8 @@ MUTANTS = {
     "hadamard_or_not_and": ("__builtin_popcount((unsigned)(i & j))", "__builtin_popcount((unsigned)(i | j))"),
     "fp_wht_sign": ("*d = fsub(x0, x1);", "*d = fsub(x1, x0);"),
     "dw_missing_inv_b": ("orc_flush(s_v)), inv_b);", "orc_flush(s_v)), 1.0f);"),
+    "rmsnorm_y_groups_rstd_with_g": ("store(y, dtype, t * D + j, fmul(fmul(xs[j], r), load(g, dtype, j)));",
+                                     "store(y, dtype, t * D + j, fmul(xs[j], fmul(r, load(g, dtype, j))));"),
     "rmsnorm_no_eps": ("float r = fdiv(1.0f, fsqrt(fadd(ms, e)));", "float r = fdiv(1.0f, fsqrt(ms));"),
     "rmsnorm_bwd_sign": ("fmul(r, fsub(d[j], fmul(xh[j], mu)))", "fmul(r, fadd(d[j], fmul(xh[j], mu)))"),
     "gradnorm_abs_not_square": ("sq[i] = fmul(e, e);", "sq[i] = fabs_(e);"),

@@ -25,6 +25,10 @@ def f32(x):
     return np.float32(x)
 
 
+def _bits(f):
+    return struct.unpack("<I", struct.pack("<f", float(f)))[0]
+
+
 def bits(f):
     return struct.unpack("<I", struct.pack("<f", float(f)))[0]
 
@@ -95,6 +99,57 @@ def _golden_kv(name):
             k, v = line.split("=")
             out[k.strip()] = int(v.strip(), 16)
     return out
+
+
+def _next_up(f):
+    return np.nextafter(np.float32(f), np.float32(np.inf))
+
+
+def _next_down(f):
+    return np.nextafter(np.float32(f), np.float32(-np.inf))
+
+
+def test_prim_sweep_host_correctly_rounded(orc):
+    """The host side of the device primitive sweep: square root and
+    reciprocal correctly rounded (checked in exact rationals), with the
+    model's flushes, and bf16 rounding as the scalar routine."""
+    rng = np.random.default_rng(17)
+    pats = rng.integers(0, 2 ** 32, 6000, dtype=np.uint64).astype(np.uint32)
+    edge = np.array([0, 1, 0x007FFFFF, 0x00800000, 0x00800001, 0x3F800000, 0x3F800001,
+                     0x7F7FFFFF, 0x7F800000, 0x7FC00000, 0x80000000, 0x80800000, 0xFF800000,
+                     0x1F800000, 0x7E800000, 0x7E7FFFFF, 0x00400000],
+                    np.uint32)
+    pats = np.concatenate([pats, edge])
+    for p in pats:
+        x = X.bits_to_float(int(p))
+        xd = 0.0 if (int(p) & 0x7F800000) == 0 else x  # DAZ (sign is irrelevant below)
+        sq = orc.prim_sweep(0, int(p), 1)[0]
+        rc = orc.prim_sweep(1, int(p), 1)[0]
+        r = X.bits_to_float(int(sq))
+        if math.isnan(xd) or xd < 0:
+            assert math.isnan(r)
+        elif math.isinf(xd) or xd == 0:
+            assert r == math.sqrt(xd)
+        else:
+            fx = Fraction(xd)
+            assert Fraction(float(r)) > 0
+            lo = (Fraction(float(_next_down(r))) + Fraction(float(r))) / 2
+            hi = (Fraction(float(r)) + Fraction(float(_next_up(r)))) / 2
+            assert lo * lo <= fx <= hi * hi, (hex(int(p)), r)
+        q = X.bits_to_float(int(rc))
+        if math.isnan(xd):
+            assert math.isnan(q)
+        elif math.isinf(xd):
+            assert q == 0.0
+        elif xd == 0:
+            assert math.isinf(q)
+        else:
+            want = X.op(Fraction(1) / Fraction(xd))
+            if want == 0:  # 1/x subnormal: flushed to a zero with x's sign
+                assert q == 0.0 and math.copysign(1, q) == math.copysign(1, xd), hex(int(p))
+            else:
+                assert _bits(q) == X.float_to_bits(float(want)), (hex(int(p)), q, float(want))
+        assert orc.prim_sweep(3, int(p), 1)[0] == orc.f32_to_bf16(x) or math.isnan(x)
 
 
 def test_lsq_k2_constant(orc):
@@ -350,15 +405,18 @@ def test_qgemm_fwd_exact_int(orc):
 
 
 def test_qgemm_fwd_extreme_acc(orc):
-    """K = 133144 codes of +-127 keep |acc| < 2^31 (the int32 bound)."""
-    K = 133144
-    qx = np.full((1, K), 127, np.int8)
-    qw = np.full((2, K), 127, np.int8)
-    qw[1] = -127
+    """K = 131071 codes of -128 keep acc = 2^14 * K = 2^31 - 2^14 < 2^31 (the
+    int32 bound for any int8 code); that value is a multiple of 2^7, the
+    binary32 spacing there, so it converts exactly."""
+    K = 131071
+    qx = np.full((2, K), -128, np.int8)
+    qx[1] = 127
+    qw = np.full((2, K), -128, np.int8)
+    qw[1] = 127
     y = orc.qgemm_fwd(qx, np.float32(1.0), qw, np.ones(2, np.float32))
-    acc = 127 * 127 * K
-    assert acc < 2 ** 31
-    assert y[0, 0] == np.float32(acc) and y[0, 1] == np.float32(-acc)
+    assert 128 * 128 * K == 2 ** 31 - 2 ** 14
+    assert y[0, 0] == np.float32(2 ** 31 - 2 ** 14)
+    assert y[0, 1] == np.float32(-128 * 127 * K) and y[1, 1] == np.float32(127 * 127 * K)
 
 
 def test_qgemm_fwd_epilogue_closed_form(orc):
@@ -544,6 +602,36 @@ def test_rmsnorm_pm1_rows_closed_form(orc):
     want = X.op(1 / sq)
     assert fl == 0 and np.all(rstd == np.float32(float(want)))
     assert np.array_equal(y, x * rstd[:, None])
+
+
+def test_rmsnorm_y_grouping_closed_form(orc, syn):
+    """y = fl(fl(x * rstd) * g), not fl(x * fl(rstd * g)).  Rows of 1536
+    entries +-1, 192 entries +-1.5 and 320 entries +-0.5 have sum of squares
+    2048 exactly (every partial sum is a multiple of 1/4), so ms = 1 and
+    rstd = fl(1/fl(sqrt(fl(1 + 1e-6)))) = 1 - 2^-21 (fl(1 + 1e-6) =
+    1 + 2^-20, its square root rounds to 1 + 2^-21, whose reciprocal rounds
+    to 1 - 2^-21).  Then x * rstd is exact for these x, and y is the one
+    rounding of an exact product, computed in double (48-bit products are
+    exact there).  For x = +-1.5 the other grouping rounds twice and differs
+    for some g."""
+    D = 2048
+    rng = np.random.default_rng(3)
+    T = 16
+    x = np.empty((T, D), np.float32)
+    for t in range(T):
+        row = np.array([1.0] * 1536 + [1.5] * 192 + [0.5] * 320, np.float32)
+        rng.shuffle(row)
+        x[t] = row * rng.choice([-1.0, 1.0], size=D).astype(np.float32)
+    g = syn.normal((D,), 0.1, mean=1.0, tag=5)
+    y, rstd, fl = orc.rmsnorm_fwd(x, g, 1e-6)
+    r = np.float32(1.0 - 2.0 ** -21)
+    assert fl == 0 and np.all(rstd == r)
+    xr = x.astype(np.float64) * np.float64(r)
+    assert np.array_equal(xr.astype(np.float32).astype(np.float64), xr)  # x * rstd exact
+    want = (xr * g.astype(np.float64)[None, :]).astype(np.float32)
+    assert np.array_equal(y.view(np.uint32), want.view(np.uint32))
+    other = (x * (r * g).astype(np.float32)[None, :]).astype(np.float32)
+    assert np.any(other.view(np.uint32) != want.view(np.uint32))
 
 
 def test_rmsnorm_fwd_fp64_bound(orc, syn):
