@@ -23,10 +23,12 @@ OP_QUANTIZE, OP_QGEMM, OP_DW_WHT, OP_RMSNORM_BWD, OP_GRAD_NORM, OP_DY_BWD = 1, 2
 OP_QUANTIZE_EXACT, OP_DX_WHT, OP_DY_ROWS_WHT = 7, 8, 9
 MAX_CONTRACTION = 131071
 DP_MAX_PARTS = 64
+STATIC_SCRATCH_BYTES = 4 << 20
+E_SCRATCH = -10
 PRIM_SQRT, PRIM_RCP, PRIM_RSQRT, PRIM_BF16_CVT, PRIM_BF16_INT = 0, 1, 2, 3, 4
 
 SYMBOLS = [
-    "brq_workspace_size", "brq_quantize_lsq", "brq_quantize_lsq_exact", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
+    "brq_workspace_size", "brq_quantize_lsq", "brq_quantize_lsq_exact", "brq_quantize_lsq_static", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
     "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
     "brq_qgemm_fwd_ex", "brq_qgemm_bwd_dx_ex",
     "brq_quantize_dy_bwd", "brq_qgemm_bwd_dx_wht", "brq_wht_quant_dy_rows", "brq_attn_fwd",
@@ -81,6 +83,8 @@ def lib():
         L.brq_quantize_lsq.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         L.brq_quantize_lsq_exact.restype = i32
         L.brq_quantize_lsq_exact.argtypes = L.brq_quantize_lsq.argtypes
+        L.brq_quantize_lsq_static.restype = i32
+        L.brq_quantize_lsq_static.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.brq_qgemm_fwd.restype = i32
         L.brq_qgemm_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, sz, vp, vp]
         L.brq_qgemm_bwd_dx.restype = i32

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "internal.hpp"
 
@@ -100,6 +101,7 @@ const char* brq_status_string(int s) {
     case BRQ_E_WORKSPACE: return "workspace missing or too small";
     case BRQ_E_HIP: return "HIP launch error";
     case BRQ_E_ARG: return "invalid argument";
+    case BRQ_E_SCRATCH: return "input too large for the library's static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -180,6 +182,61 @@ int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols, int
                      void* stream) {
   return quantize_common(x, x_dtype, rows, cols, gran, col_mul, false, q, q_t, scale, amax, ws,
                          ws_bytes, dflags, tune, stream);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free variant's scratch ---------------------------------------
+// One static device array per GPU the library runs on (it stays until the
+// process ends).  In host code `scratch` names a host-side stand-in, not a
+// device address: the device address comes from hipGetSymbolAddress, looked
+// up once per device with that device current, and only that address is
+// ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[BRQ_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return BRQ_E_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return BRQ_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BRQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int brq_quantize_lsq_static(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                            const float* col_mul, int8_t* q, int8_t* q_t, float* scale,
+                            float* amax, int32_t* dflags, const brq_tune* tune, void* stream) {
+  // size check first: nothing is looked up or launched for an input the
+  // scratch cannot hold
+  if (rows < 0 || cols < 0) return BRQ_E_SHAPE;
+  if (gran == BRQ_PER_TENSOR &&
+      quant_ws(rows, cols, tune) > (size_t)BRQ_STATIC_SCRATCH_BYTES)
+    return BRQ_E_SCRATCH;
+  void* ws = nullptr;
+  const int st = scratch_of_current_device(&ws);
+  if (st != BRQ_OK) return st;
+  return quantize_common(x, x_dtype, rows, cols, gran, col_mul, false, q, q_t, scale, amax, ws,
+                         BRQ_STATIC_SCRATCH_BYTES, dflags, tune, stream);
 }
 
 int brq_quantize_lsq_exact(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,

@@ -53,7 +53,8 @@ enum brq_status {
   BRQ_E_RANGE = -6,       /* contraction too long for exact int32 sums */
   BRQ_E_WORKSPACE = -7,   /* workspace missing or too small */
   BRQ_E_HIP = -8,         /* kernel launch failed */
-  BRQ_E_ARG = -9          /* other invalid argument */
+  BRQ_E_ARG = -9,         /* other invalid argument */
+  BRQ_E_SCRATCH = -10     /* input too large for the static scratch buffer */
 };
 
 enum brq_dtype { BRQ_F32 = 0, BRQ_BF16 = 1, BRQ_I8 = 2, BRQ_I32 = 3, BRQ_U8 = 4 };
@@ -123,6 +124,31 @@ int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols,
                      int gran, const float* col_mul, int8_t* q, int8_t* q_t,
                      float* scale, float* amax, void* ws, size_t ws_bytes,
                      int32_t* dflags, const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * quantize_lsq_static -- brq_quantize_lsq without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The per-tensor
+ * statistic's tree partials live in one static device array of
+ * BRQ_STATIC_SCRATCH_BYTES per GPU, created with the library's code object
+ * and held until the process ends; nothing is allocated or freed here.
+ * Results, arguments, shapes and flags are those of brq_quantize_lsq with
+ * the same x, gran, col_mul and tune.  Nothing in the scratch needs to start
+ * at zero (every partial is written before it is read).
+ * Limits: a BRQ_PER_TENSOR input whose workspace (brq_workspace_size with
+ * BRQ_OP_QUANTIZE) exceeds BRQ_STATIC_SCRATCH_BYTES returns BRQ_E_SCRATCH
+ * before anything is launched (about 2^31 values at the default chunk).
+ * BRQ_PER_ROW uses no scratch.  The scratch of the current device is used,
+ * so `stream` must belong to it.  Every call on one GPU shares that GPU's
+ * scratch: calls that may overlap in time on one GPU (different streams, no
+ * ordering between them) race and give unspecified results.
+ * --------------------------------------------------------------------- */
+#define BRQ_STATIC_SCRATCH_BYTES (4u << 20)
+int brq_quantize_lsq_static(const void* x, int x_dtype, int64_t rows,
+                            int64_t cols, int gran, const float* col_mul,
+                            int8_t* q, int8_t* q_t, float* scale, float* amax,
+                            int32_t* dflags, const struct brq_tune* tune,
+                            void* stream);
 
 /* ---------------------------------------------------------------------
  * quantize_lsq_exact -- brq_quantize_lsq with an exact statistic (a

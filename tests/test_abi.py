@@ -71,6 +71,7 @@ def test_host_side_status_codes(lib):
     g.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, C.c_size_t, vp, vp]
     assert g(fake, fake, fake, fake, 1, 64, 64, 24, fake, None, 0, None, None) == -5   # K % 16
     assert g(fake, fake, fake, fake, 1, 64, 64, 133152, fake, None, 0, None, None) == -6  # int32 range
+    assert g(fake, fake, fake, fake, 1, 64, 64, 131072, fake, None, 0, None, None) == -6  # 128*128*K
     d = lib.brq_qgemm_bwd_dw_wht
     d.restype = i32
     d.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp, vp, vp, C.c_size_t, vp, vp, vp]
@@ -97,3 +98,18 @@ def test_adamw_bias_corrections_host_matches_oracle():
             got = brq.adamw_bias_corrections(t, b1, b2)
             want = orc.adamw_bias_corrections(t, b1, b2)
             assert np.float32(got[0]) == want[0] and np.float32(got[1]) == want[1], (t, b1, b2)
+
+
+def test_static_quantiser_rejects_what_its_scratch_cannot_hold(lib):
+    """brq_quantize_lsq_static refuses, before any device call, a per-tensor
+    input whose tree partials exceed the static scratch (so this runs
+    without a GPU)."""
+    vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
+    f = lib.brq_quantize_lsq_static
+    f.restype = i32
+    f.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    fake = 0x1000
+    assert f(fake, 1, 1 << 20, 1 << 14, 0, None, fake, None, fake, None, None, None, None) == -10
+    assert f(fake, 1, -1, 8, 0, None, fake, None, fake, None, None, None, None) == -3
+    lib.brq_status_string.restype = C.c_char_p
+    assert b"static scratch" in lib.brq_status_string(-10)
