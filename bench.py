@@ -121,33 +121,101 @@ def stored_traffic():
     return float(rec["bytes_per_launch"])
 
 
-def cpu_baseline(tokens, one_core_tokens):
-    """The plain CPU oracle on the first `tokens` tokens of the same layer
-    workload, on all host threads: both norms, the seven linears forward and
-    backward, grad-norm over the gradients, state hash (the oracle as
-    written, untuned).  Then the same on `one_core_tokens` tokens with one
-    thread (0 skips it)."""
+def _timed(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(tokens, one_core):
+    """The plain CPU oracle, as written (untuned), timed on the host in the
+    same run.  All host threads (OpenMP splits only independent outputs):
+    the layer step (the timed workload) and the MLP workload on their first
+    `tokens` tokens, rates extrapolated to the full token counts.  One
+    thread (when one_core): the tiny workload, the QKV forward and the
+    RMSNorm forward + backward in full, and the grad-norm on the first 2^26
+    of its 1.61e9 values, extrapolated.  Input generation is outside every
+    timed region."""
+    import numpy as np
+
+    import brq_synth as syn
     import oracle as orc
 
+    n_all = orc.num_threads()
     ops = gemm_ops(_layer_linears(), tokens)
     dt = _oracle_layer(tokens)
-    out = {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": orc.num_threads(),
-           "kind": "oracle",
+    full_s = dt * 32768 / tokens
+    out = {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": n_all, "kind": "oracle",
+           "nproc": os.cpu_count(),
            "sample": (f"the whole layer step (2 RMSNorms, 7 W8A8 linears fwd+bwd with WHT, "
-                      f"grad-norm, state hash) on the first {tokens} of 32768 tokens; "
-                      f"{dt:.2f} s wall, {tokens / dt:.1f} tokens/s"),
+                      f"grad-norm, state hash) on the first {tokens} of 32768 tokens, {n_all} "
+                      f"threads; {dt:.2f} s wall, {tokens / dt:.1f} tokens/s; the full step "
+                      f"extrapolated: {full_s:.0f} s"),
            "tokens_per_s": round(tokens / dt, 3), "seconds": round(dt, 3)}
-    if one_core_tokens > 0:
-        n = orc.num_threads()
+    cfg = {"layer": {"cores": n_all, "tokens": tokens, "seconds": round(dt, 3),
+                     "extrapolated_full_s": round(full_s, 1), "tops": out["value"]}}
+
+    # MLP workload (2048 -> 8192 fwd + bwd, block 128) on a token slice
+    d = syn.mlp()
+    x, w, dy = d["x"][:tokens], d["w"], d["dy"][:tokens]
+    del d
+
+    def mlp():
+        qx, _, sx, _, _ = orc.quantize_lsq(x)
+        qw, _, sw, _, _ = orc.quantize_lsq(w, per_row=True)
+        orc.qgemm_fwd(qx, sx, qw, sw)
+        qg, _, sg, _, _ = orc.quantize_lsq(dy, col_mul=sw)
+        orc.qgemm_bwd_dx(qg, sg, qw)
+        orc.qgemm_bwd_dw_wht(qx, sx, dy, BLOCK)
+    t = _timed(mlp)
+    mops = 3 * 2 * tokens * 8192 * 2048
+    cfg["mlp"] = {"cores": n_all, "tokens": tokens, "seconds": round(t, 3),
+                  "extrapolated_full_s": round(t * 16384 / tokens, 1),
+                  "tops": round(mops / t / 1e12, 6)}
+    del x, w, dy
+    if one_core:
         orc.set_num_threads(1)
         try:
-            dt1 = _oracle_layer(one_core_tokens)
+            d = syn.tiny()
+
+            def tiny():
+                qx, _, sx, _, _ = orc.quantize_lsq(d["x"])
+                qw, _, sw, _, _ = orc.quantize_lsq(d["w"], per_row=True)
+                orc.qgemm_fwd(qx, sx, qw, sw)
+                qg, _, sg, _, _ = orc.quantize_lsq(d["dy"], col_mul=sw)
+                orc.qgemm_bwd_dx(qg, sg, qw)
+                orc.qgemm_bwd_dw_wht(qx, sx, d["dy"], d["block"])
+            t = _timed(tiny)
+            cfg["tiny"] = {"cores": 1, "seconds": round(t, 4), "full": True,
+                           "tops": round(3 * 2 * 64 * 256 * 256 / t / 1e12, 6)}
+            d = syn.qkv()
+
+            def qkv():
+                qx, _, sx, _, _ = orc.quantize_lsq(d["x"])
+                qw, _, sw, _, _ = orc.quantize_lsq(d["w"], per_row=True)
+                orc.qgemm_fwd(qx, sx, qw, sw)
+            t = _timed(qkv)
+            cfg["qkv"] = {"cores": 1, "seconds": round(t, 3), "full": True,
+                          "tops": round(2 * 4096 * 3072 * 2048 / t / 1e12, 6)}
+            d = syn.norm(n_grad=0)
+
+            def norm():
+                y, r, _ = orc.rmsnorm_fwd(d["x"], d["g"], EPS)
+                orc.rmsnorm_bwd(d["x"], d["g"], r, d["dy"])
+            t = _timed(norm)
+            del d
+            v = syn.normal((1 << 26,), 1e-4, tag=syn.TAG_V)
+            tg = _timed(lambda: orc.grad_norm(v))
+            del v
+            scale = syn.GRAD_NORM_N / (1 << 26)
+            cfg["norm"] = {"cores": 1, "rmsnorm_fwd_bwd_seconds": round(t, 3), "full_rmsnorm": True,
+                           "grad_norm_seconds_on_2^26": round(tg, 3),
+                           "grad_norm_extrapolated_full_s": round(tg * scale, 1),
+                           "gb_per_s": round(((32768 * 2048 * (4 + 6)) + 4 * (1 << 26)) /
+                                             (t + tg) / 1e9, 3)}
         finally:
-            orc.set_num_threads(n)
-        ops1 = gemm_ops(_layer_linears(), one_core_tokens)
-        out["one_core"] = {"value": round(ops1 / dt1 / 1e12, 6), "unit": "TOPS", "cores": 1,
-                           "tokens": one_core_tokens, "seconds": round(dt1, 3),
-                           "tokens_per_s": round(one_core_tokens / dt1, 3)}
+            orc.set_num_threads(n_all)
+    out["configs"] = cfg
     return out
 
 
@@ -264,10 +332,47 @@ def norm_workload(torch, brq, syn, dev, args, e0, e1):
     outs = {"y": y, "rstd": rstd, "dx": dx, "dg": dg, "grad_norm": gn}
     exact = all(hashlib.sha256(raw(t)).hexdigest() == stored_digest("norm", k)
                 for k, t in outs.items())
-    del X, G, DY, V, y, dx, bws, gws
-    return dict(res, bitwise_exact=exact, workload=(
+    del X, G, DY, y, dx, bws, gws
+    exchange = exchange_workload(torch, brq, V, args, e0, e1)
+    del V
+    return dict(res, bitwise_exact=exact, exchange=exchange, workload=(
         "x, dy [32768 x 2048] bf16 (x N(0,1) with 1% bf16 subnormals, dy N(0,1e-3)), "
         "g [2048] bf16 1+N(0,0.1); grad-norm over 1.61e9 fp32 N(0,1e-4)"))
+
+
+def exchange_workload(torch, brq, V, args, e0, e1):
+    """The deterministic gradient exchange's arithmetic (brq_dp_reduce) on
+    one rank's share of the Open-1B gradient: the 1.61e9-value gradient
+    vector viewed as contributions.  Timed alone with HIP events:
+      reduce_scatter_sum  8 shard contributions of 201.25e6 values summed in
+                          ascending rank order, times fl(1/8);
+      replica_fold        TreeFold of 6 replica partials of 201.25e6 values,
+                          times fl(1/6);
+      audit_replay        6 replicas x 8 shards of 33.5e6 values: the
+                          single-device replay of the whole exchange.
+    Algorithmic bytes: (contributions + 1) x 4 per output element."""
+    cases = {"reduce_scatter_sum": (1, 8, 201_250_000), "replica_fold": (6, 1, 201_250_000),
+             "audit_replay": (6, 8, 33_541_664)}
+    out = {}
+    for name, (R, S, n) in cases.items():
+        parts = [V[j * n:(j + 1) * n] for j in range(R * S)]
+        o = torch.empty(n, dtype=torch.float32, device=V.device)
+        for _ in range(max(args.warmup, 1)):
+            brq.dp_reduce(parts, R, S, out=o)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            brq.dp_reduce(parts, R, S, out=o)
+        e1.record()
+        torch.cuda.synchronize()
+        t_ms = e0.elapsed_time(e1) / args.steps
+        nbytes = (R * S + 1) * 4 * n
+        gbs = nbytes / (t_ms * 1e-3) / 1e9
+        out[name] = {"replicas": R, "shards": S, "elements": n, "us_per_call": round(1e3 * t_ms, 2),
+                     "algorithmic_bytes": nbytes, "gb_per_s": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del o, parts
+    return out
 
 
 def main():
@@ -278,10 +383,12 @@ def main():
     ap.add_argument("--tokens", type=int, default=32768,
                     help="tokens per step (a multiple of 128; 32768 is the measured workload)")
     ap.add_argument("--cpu-tokens", type=int, default=512,
-                    help="tokens of the CPU-oracle sample (0 skips it)")
-    ap.add_argument("--cpu-one-core-tokens", type=int, default=128,
-                    help="tokens of the one-thread CPU-oracle sample, a multiple of the "
-                         "128-token rotation block (0 skips it)")
+                    help="tokens of the all-threads CPU-oracle samples of the layer and MLP "
+                         "workloads, a multiple of the 128-token rotation block (0 skips the "
+                         "CPU baseline)")
+    ap.add_argument("--no-cpu-one-core", dest="cpu_one_core", action="store_false",
+                    help="skip the one-thread CPU-oracle legs (tiny, QKV and RMSNorm in full, "
+                         "grad-norm on a slice)")
     ap.add_argument("--no-instrument", action="store_true",
                     help="skip the per-call event pass (for profiler runs)")
     ap.add_argument("--no-norm-config", dest="norm_config", action="store_false",
@@ -298,6 +405,8 @@ def main():
         sys.exit(2)
     if args.tokens % BLOCK or args.tokens <= 0:
         sys.exit("--tokens must be a positive multiple of 128")
+    if args.cpu_tokens % BLOCK or args.cpu_tokens < 0:
+        sys.exit("--cpu-tokens must be a non-negative multiple of 128")
 
     import numpy as np
     import torch
@@ -610,7 +719,7 @@ def main():
     cpu = None
     if args.cpu_tokens > 0:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
-        cpu = cpu_baseline(args.cpu_tokens, args.cpu_one_core_tokens)
+        cpu = cpu_baseline(args.cpu_tokens, args.cpu_one_core)
 
     line = {
         "metric": METRIC, "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1,
