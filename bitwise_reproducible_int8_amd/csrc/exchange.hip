@@ -16,13 +16,19 @@
 // read with DAZ and results flushed.
 //
 // The contributions arrive in mesh order (replica-major, then shard, then
-// microbatch).  Each lane owns four consecutive elements and walks the
-// contributions in that order with four 16-byte loads in flight; the level
-// counters are wave-uniform, so the branches are scalar.  The fold keeps one
-// register slot per level: pushing replica r merges with the slots of r's
-// trailing one bits, exactly the stack that binary counting leaves.  The
-// kernel is bound by HBM reads: (P + 1) * 4 bytes per element for P
-// contributions.
+// microbatch).  Each lane owns kGroups groups of four consecutive elements,
+// the groups 1024 elements apart, so every load instruction of a wave reads
+// one contiguous kilobyte; loads are nontemporal (each value is read once)
+// and two contributions are loaded ahead of their adds.  More groups per
+// lane measured no faster and cost registers that the fold needs.  The
+// level counters are uniform across the grid, so every branch on them is
+// scalar, and each level starts from its first term rather than from a
+// select.  The fold keeps one register slot per level (LV levels hold up to
+// 2^LV - 1 replicas): pushing replica r merges the slots of r's trailing one
+// bits, exactly the stack that binary counting leaves.  A multiply by the
+// reciprocal of a count of one is the identity on flushed values and is
+// skipped.  The kernel reads (P + 1) * 4 bytes per element for P
+// contributions and is bound by HBM.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -30,120 +36,185 @@ namespace brq {
 
 namespace {
 
-constexpr int kLevels = 7;  // 64 replicas need levels 0..6
+constexpr int kLanes = 256;
+constexpr int kGroups = 1;  // groups of four elements per lane
+constexpr int kStride = kLanes * 4;  // elements between a lane's groups
 
 struct PartPtrs {
   const float* p[BRQ_DP_MAX_PARTS];
 };
 
-struct F4 {
-  float v[4];
-};
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ F4 load4(const float* base, int64_t i0, int64_t n) {
-  F4 r;
-  if (i0 + 4 <= n) {
-    const u32x4 w = ld16(base + i0);
-    unpack_f32x4(w, r.v);
-  } else {
+template <int G>
+struct Vec {
+  float v[4 * G];
+};
+
+// Contribution `p` at the lane's elements; EDGE: the work-group straddles n
+// (elements at or beyond n read as 0 and are never stored).
+template <int G, bool EDGE>
+__device__ __forceinline__ Vec<G> vload(const float* p, int64_t i0, int64_t n) {
+  Vec<G> r;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r.v[e] = i0 + e < n ? flush(base[i0 + e]) : 0.0f;
+  for (int g = 0; g < G; ++g) {
+    const int64_t i = i0 + (int64_t)g * kStride;
+    if (!EDGE) {
+      // each value is read once: a nontemporal load
+      const f32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + i));
+      const u32x4 u{__float_as_uint(w[0]), __float_as_uint(w[1]), __float_as_uint(w[2]),
+                    __float_as_uint(w[3])};
+      unpack_f32x4(u, r.v + 4 * g);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r.v[4 * g + e] = i + e < n ? flush(p[i + e]) : 0.0f;
+    }
   }
   return r;
 }
 
-__device__ __forceinline__ F4 add4(const F4& a, const F4& b) {
-  F4 r;
+template <int G>
+__device__ __forceinline__ Vec<G> vadd(const Vec<G>& a, const Vec<G>& b) {
+  Vec<G> r;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) r.v[e] = fadd(a.v[e], b.v[e]);
+  for (int k = 0; k < 4 * G; ++k) r.v[k] = fadd(a.v[k], b.v[k]);
   return r;
 }
 
-__device__ __forceinline__ F4 mul4(const F4& a, float c) {
-  F4 r;
+template <int G>
+__device__ __forceinline__ Vec<G> vmul(const Vec<G>& a, float c) {
+  Vec<G> r;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) r.v[e] = fmul(a.v[e], c);
+  for (int k = 0; k < 4 * G; ++k) r.v[k] = fmul(a.v[k], c);
   return r;
 }
 
-__global__ __launch_bounds__(256) void k_dp_reduce(PartPtrs parts, int R, int S, int A,
-                                                   int64_t n, int average, float inv_a,
-                                                   float inv_s, float inv_r,
-                                                   float* __restrict__ out,
-                                                   int32_t* dflags) {
-  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i0 >= n) return;
-  const int P = R * S * A;
+// Running sum of contributions j .. j + count - 1, left to right.
+template <int G, bool EDGE>
+__device__ __forceinline__ Vec<G> run_sum(const PartPtrs& parts, int j, int count, int64_t i0,
+                                          int64_t n) {
+  Vec<G> acc = vload<G, EDGE>(parts.p[j], i0, n);
+  int k = 1;
+  for (; k + 1 < count; k += 2) {
+    const Vec<G> x = vload<G, EDGE>(parts.p[j + k], i0, n);
+    const Vec<G> y = vload<G, EDGE>(parts.p[j + k + 1], i0, n);
+    acc = vadd(acc, x);
+    acc = vadd(acc, y);
+  }
+  if (k < count) acc = vadd(acc, vload<G, EDGE>(parts.p[j + k], i0, n));
+  return acc;
+}
 
-  // four contributions in flight ahead of the one being added
-  F4 q0 = load4(parts.p[0], i0, n);
-  F4 q1 = P > 1 ? load4(parts.p[1], i0, n) : q0;
-  F4 q2 = P > 2 ? load4(parts.p[2], i0, n) : q0;
-  F4 q3 = P > 3 ? load4(parts.p[3], i0, n) : q0;
-
-  F4 acc_a = q0, inner = q0;
-  F4 slot[kLevels];
+// Push replica r's value e: with t = the number of trailing one bits of r,
+// merge the slots below level t into it (lower replicas on the left) and
+// keep the sum at level t.
+template <int G, int LV>
+__device__ __forceinline__ void push(Vec<G> (&slot)[LV], Vec<G> e, int t) {
 #pragma unroll
-  for (int l = 0; l < kLevels; ++l) slot[l] = q0;
+  for (int l = 0; l < LV; ++l) {
+    if (l == t) slot[l] = e;
+    if (l < t) e = vadd(slot[l], e);
+  }
+}
 
-  int a = 0, s = 0, r = 0;
-  for (int j = 0; j < P; ++j) {
-    const F4 cur = q0;
-    q0 = q1;
-    q1 = q2;
-    q2 = q3;
-    if (j + 4 < P) q3 = load4(parts.p[j + 4], i0, n);
-
-    acc_a = a == 0 ? cur : add4(acc_a, cur);  // microbatch running sum
-    if (++a < A) continue;
-    a = 0;
-    F4 g = average ? mul4(acc_a, inv_a) : acc_a;
-    inner = s == 0 ? g : add4(inner, g);  // ascending shard sum
-    if (++s < S) continue;
-    s = 0;
-    F4 e = average ? mul4(inner, inv_s) : inner;
-    // push replica r: merge with the slots of r's trailing one bits (the
-    // stack entries, which hold the lower replicas, on the left), then
-    // store at the level above them
-    const int t = __builtin_ctz(~(unsigned)r);
+template <int G, int LV, bool EDGE>
+__device__ __forceinline__ void reduce_lane(const PartPtrs& parts, int R, int S, int A,
+                                            int64_t i0, int64_t n, int average, float inv_a,
+                                            float inv_s, float inv_r, float* out,
+                                            int32_t* dflags) {
+  const bool avg_a = average && A > 1, avg_s = average && S > 1, avg_r = average && R > 1;
+  Vec<G> slot[LV];
 #pragma unroll
-    for (int l = 0; l < kLevels; ++l) {
-      if (l < t) e = add4(slot[l], e);
-      if (l == t) slot[l] = e;
+  for (int l = 0; l < LV; ++l)
+#pragma unroll
+    for (int k = 0; k < 4 * G; ++k) slot[l].v[k] = 0.0f;
+  int j = 0;
+  for (int r = 0; r < R; ++r) {
+    Vec<G> e;
+    if (A == 1) {
+      e = run_sum<G, EDGE>(parts, j, S, i0, n);  // ascending shard sum
+      j += S;
+    } else {
+      e = run_sum<G, EDGE>(parts, j, A, i0, n);  // microbatches of shard 0
+      j += A;
+      if (avg_a) e = vmul(e, inv_a);
+      for (int s = 1; s < S; ++s) {
+        Vec<G> g = run_sum<G, EDGE>(parts, j, A, i0, n);
+        j += A;
+        if (avg_a) g = vmul(g, inv_a);
+        e = vadd(e, g);
+      }
     }
-    ++r;
+    if (avg_s) e = vmul(e, inv_s);
+    push(slot, e, __builtin_ctz(~(unsigned)r));
   }
 
   // Result: the entries at the set bits of R, lowest level first
-  F4 res = q0;
+  Vec<G> res = slot[0];
   bool have = false;
 #pragma unroll
-  for (int l = 0; l < kLevels; ++l) {
+  for (int l = 0; l < LV; ++l) {
     if ((R >> l) & 1) {
-      res = have ? add4(slot[l], res) : slot[l];
+      res = have ? vadd(slot[l], res) : slot[l];
       have = true;
     }
   }
-  if (average) res = mul4(res, inv_r);
+  if (avg_r) res = vmul(res, inv_r);
 
   bool bad = false;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) bad |= (i0 + e < n) && !__builtin_isfinite(res.v[e]);
-  if (i0 + 4 <= n) {
-    __builtin_nontemporal_store(f32x4_t{res.v[0], res.v[1], res.v[2], res.v[3]},
-                                reinterpret_cast<f32x4_t*>(out + i0));
-  } else {
+  for (int g = 0; g < G; ++g) {
+    const int64_t i = i0 + (int64_t)g * kStride;
+    float* v = res.v + 4 * g;
+    if (average) {
+      // a multiply by one skipped above would have quieted a lone
+      // signalling NaN; every other value is unchanged by this
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (i0 + e < n) out[i0 + e] = res.v[e];
+      for (int e = 0; e < 4; ++e) v[e] = __builtin_canonicalizef(v[e]);
+    }
+    if (!EDGE) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bad |= !__builtin_isfinite(v[e]);
+      __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]},
+                                  reinterpret_cast<f32x4_t*>(out + i));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (i + e < n) {
+          bad |= !__builtin_isfinite(v[e]);
+          out[i + e] = v[e];
+        }
+      }
+    }
   }
   if (bad) set_flag(dflags, BRQ_FLAG_NONFINITE);
+}
+
+template <int G, int LV>
+__global__ __launch_bounds__(kLanes) void k_dp_reduce(PartPtrs parts, int R, int S, int A,
+                                                      int64_t n, int average, float inv_a,
+                                                      float inv_s, float inv_r, float* out,
+                                                      int32_t* dflags) {
+  const int64_t base = (int64_t)blockIdx.x * (G * kStride);
+  const int64_t i0 = base + (int64_t)threadIdx.x * 4;
+  if (base + G * kStride <= n)
+    reduce_lane<G, LV, false>(parts, R, S, A, i0, n, average, inv_a, inv_s, inv_r, out, dflags);
+  else
+    reduce_lane<G, LV, true>(parts, R, S, A, i0, n, average, inv_a, inv_s, inv_r, out, dflags);
 }
 
 // binary32 reciprocal of a count on the host: one correctly rounded divide
 // (a count <= 64 is exact in binary32, and its reciprocal is normal)
 float host_reciprocal(int k) { return 1.0f / (float)k; }
+
+template <int G, int LV>
+void launch(const PartPtrs& pp, int R, int S, int A, int64_t n, int average, float* out,
+            int32_t* dflags, hipStream_t st) {
+  const int64_t blocks = (n + G * kStride - 1) / (G * kStride);
+  hipLaunchKernelGGL((k_dp_reduce<G, LV>), dim3((unsigned)blocks), dim3(kLanes), 0, st, pp, R,
+                     S, A, n, average, host_reciprocal(A), host_reciprocal(S),
+                     host_reciprocal(R), out, dflags);
+}
 
 }  // namespace
 
@@ -153,11 +224,15 @@ hipError_t dp_reduce(const float* const* parts, int R, int S, int A, int64_t n, 
   PartPtrs pp{};
   const int P = R * S * A;
   for (int j = 0; j < P; ++j) pp.p[j] = parts[j];
-  const int64_t threads = (n + 3) / 4;
-  const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL(k_dp_reduce, dim3((unsigned)blocks), dim3(256), 0, st, pp, R, S, A, n,
-                     average, host_reciprocal(A), host_reciprocal(S), host_reciprocal(R), out,
-                     dflags);
+  // levels of the fold: floor(log2 R) + 1
+  constexpr int G = kGroups;
+  if (R == 1) launch<G, 1>(pp, R, S, A, n, average, out, dflags, st);
+  else if (R < 4) launch<G, 2>(pp, R, S, A, n, average, out, dflags, st);
+  else if (R < 8) launch<G, 3>(pp, R, S, A, n, average, out, dflags, st);
+  else if (R < 16) launch<G, 4>(pp, R, S, A, n, average, out, dflags, st);
+  else if (R < 32) launch<G, 5>(pp, R, S, A, n, average, out, dflags, st);
+  else if (R < 64) launch<G, 6>(pp, R, S, A, n, average, out, dflags, st);
+  else launch<G, 7>(pp, R, S, A, n, average, out, dflags, st);
   return hipGetLastError();
 }
 

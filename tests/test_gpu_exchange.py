@@ -110,6 +110,26 @@ def test_dp_reduce_nonfinite_flag(brq, orc):
     assert np.isinf(got.cpu().numpy()[17])
 
 
+def test_dp_reduce_nan_inputs_flagged(brq, orc):
+    """A NaN contribution (quiet or signalling) gives a NaN output and the
+    non-finite flag on both sides, also where every count is one (no add
+    and, with average, only multiplies by one); the payload bits of a NaN
+    are not compared."""
+    nan_bits = np.array([0x7FC00000, 0x7F800001, 0xFFC12345, 0x7FA00000], np.uint32)
+    for R, S in ((1, 1), (1, 2), (2, 1), (3, 3)):
+        parts = [np.full(37, 0.25 * (j + 1), np.float32) for j in range(R * S)]
+        for k, b in enumerate(nan_bits):
+            parts[k % (R * S)][5 + k] = b.view(np.float32)
+        for average in (True, False):
+            want, wfl = orc.dp_reduce(parts, R, S, 1, average=average)
+            got, gfl = _run(brq, parts, R, S, 1, average)
+            g = got.cpu().numpy()
+            assert gfl == wfl == 1
+            assert np.array_equal(np.isnan(g), np.isnan(want))
+            finite = ~np.isnan(want)
+            assert np.array_equal(g[finite].view(np.uint32), want[finite].view(np.uint32))
+
+
 def test_dp_reduce_in_place_and_repeat(brq, orc, syn):
     from tests.gpu_util import assert_bitwise
     parts = syn.exchange_parts(6, N_RAGGED)

@@ -67,7 +67,9 @@ def test_quantize_per_tensor(shape, bf16, cm, chunk):
 
 @pytest.mark.parametrize("shape,bf16", [((256, 256), False), ((3072, 2048), True),
                                         ((48, 8192), True), ((16, 264), True), ((5, 16384), True),
-                                        ((33, 100), False)])
+                                        ((33, 100), False), ((64, 16384), True), ((32, 8192), False),
+                                        ((16, 4096), True), ((8192, 2048), True), ((2048, 8192), True),
+                                        ((512, 2048), True), ((48, 1024), False)])
 def test_quantize_per_row(shape, bf16):
     say("quantize_per_row", shape, bf16)
     w = syn.normal(shape, 0.02, tag=203, bf16=bf16)
