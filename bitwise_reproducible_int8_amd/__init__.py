@@ -28,7 +28,8 @@ E_SCRATCH = -10
 PRIM_SQRT, PRIM_RCP, PRIM_RSQRT, PRIM_BF16_CVT, PRIM_BF16_INT = 0, 1, 2, 3, 4
 
 SYMBOLS = [
-    "brq_workspace_size", "brq_quantize_lsq", "brq_quantize_lsq_exact", "brq_quantize_lsq_static", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
+    "brq_workspace_size", "brq_quantize_lsq", "brq_quantize_lsq_exact", "brq_quantize_lsq_static",
+    "brq_quantize_lsq_rows_multi", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
     "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
     "brq_qgemm_fwd_ex", "brq_qgemm_bwd_dx_ex",
     "brq_quantize_dy_bwd", "brq_qgemm_bwd_dx_wht", "brq_wht_quant_dy_rows", "brq_attn_fwd",
@@ -54,6 +55,13 @@ class AdamWHparams(C.Structure):
 # §3.4.2)
 ADAMW_BETA1, ADAMW_BETA2, ADAMW_EPS, ADAMW_WD = 0.9, 0.95, 1e-8, 0.1
 CLIP_MAX_NORM, SPIKE_THRESHOLD, SPIKE_SKIP_STEPS = 1.0, 5.0, 5
+
+
+class RowsJob(C.Structure):
+    """One tensor of brq_quantize_lsq_rows_multi (struct brq_rows_job)."""
+    _fields_ = [("x", C.c_void_p), ("x_dtype", C.c_int), ("rows", C.c_int64), ("cols", C.c_int64),
+                ("q", C.c_void_p), ("q_t", C.c_void_p), ("scale", C.c_void_p),
+                ("amax", C.c_void_p)]
 
 
 class Tune(C.Structure):
@@ -85,6 +93,8 @@ def lib():
         L.brq_quantize_lsq_exact.argtypes = L.brq_quantize_lsq.argtypes
         L.brq_quantize_lsq_static.restype = i32
         L.brq_quantize_lsq_static.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.brq_quantize_lsq_rows_multi.restype = i32
+        L.brq_quantize_lsq_rows_multi.argtypes = [vp, i32, vp, vp]
         L.brq_qgemm_fwd.restype = i32
         L.brq_qgemm_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, sz, vp, vp]
         L.brq_qgemm_bwd_dx.restype = i32
@@ -279,6 +289,43 @@ def quantize_lsq(x, per_row=False, col_mul=None, want_t=False, tune=None, ws=Non
               _ptr(w), w.numel(), _ptr(flags), _tune(tune), _stream()),
            "quantize_lsq_exact" if exact else "quantize_lsq")
     return q, q_t, scale, amax
+
+
+def quantize_lsq_rows_multi(xs, want_t=True, flags=None, outs=None):
+    """Per-row LSQ quantisation of several tensors in one call
+    (brq_quantize_lsq_rows_multi).  Returns a list of (q, q_t or None,
+    scale, amax), each equal to quantize_lsq(x, per_row=True, want_t=...);
+    ``outs`` may hold such tuples preallocated (None entries allocated)."""
+    res = []
+    jobs = (RowsJob * max(len(xs), 1))()
+    for k, x in enumerate(xs):
+        _dev(x, f"xs[{k}]")
+        rows, cols = x.shape
+        q, q_t, scale, amax = outs[k] if outs is not None else (None, None, None, None)
+        if q is None:
+            q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+        if q_t is None and want_t:
+            q_t = torch.empty((cols, rows), dtype=torch.int8, device=x.device)
+        if scale is None:
+            scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+        if amax is None:
+            amax = torch.empty(rows, dtype=torch.float32, device=x.device)
+        for t, shape, dt, name in ((q, (rows, cols), torch.int8, "q"),
+                                   (scale, (rows,), torch.float32, "scale"),
+                                   (amax, (rows,), torch.float32, "amax")):
+            _dev(t, name)
+            if tuple(t.shape) != shape or t.dtype != dt:
+                raise BrqError(f"{name}[{k}]: expected {dt} {shape}, got {t.dtype} {tuple(t.shape)}")
+        if q_t is not None:
+            _dev(q_t, "q_t")
+            if tuple(q_t.shape) != (cols, rows) or q_t.dtype != torch.int8:
+                raise BrqError(f"q_t[{k}]: expected int8 (cols, rows)")
+        jobs[k] = RowsJob(_ptr(x), _fp_code(x), rows, cols, _ptr(q), _ptr(q_t), _ptr(scale),
+                          _ptr(amax))
+        res.append((q, q_t, scale, amax))
+    _check(lib().brq_quantize_lsq_rows_multi(jobs, len(xs), _ptr(flags), _stream()),
+           "quantize_lsq_rows_multi")
+    return res
 
 
 def qgemm_fwd(q_x, s_x, q_w, s_w, tune=None, out=None, ws=None, out_dtype=torch.float32):

@@ -184,6 +184,26 @@ int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols, int
                          ws_bytes, dflags, tune, stream);
 }
 
+int brq_quantize_lsq_rows_multi(const brq_rows_job* jobs, int count, int32_t* dflags,
+                                void* stream) {
+  if (count < 0 || count > BRQ_ROWS_MULTI_MAX) return BRQ_E_ARG;
+  if (count == 0) return BRQ_OK;
+  if (!jobs) return BRQ_E_NULL;
+  // every job is checked before anything is launched (the per-row rules
+  // of quantize_common)
+  for (int c = 0; c < count; ++c) {
+    const brq_rows_job& j = jobs[c];
+    if (!fp_dtype(j.x_dtype)) return BRQ_E_DTYPE;
+    if (j.rows < 0 || j.cols < 0) return BRQ_E_SHAPE;
+    if ((j.rows > 0 && !j.scale) || (j.rows * j.cols > 0 && (!j.x || !j.q))) return BRQ_E_NULL;
+    if (!aligned16(j.x) || !aligned16(j.q) || !aligned16(j.q_t)) return BRQ_E_ALIGN;
+    if (j.cols % vec_elems(j.x_dtype)) return BRQ_E_UNSUPPORTED;
+    if (j.q_t && (j.rows % 16 || j.cols % 16)) return BRQ_E_UNSUPPORTED;
+    if (j.cols > 16384 || j.cols == 0) return BRQ_E_UNSUPPORTED;
+  }
+  return hip_status(quant_rows_multi(jobs, count, dflags, as_stream(stream)));
+}
+
 }  // extern "C"
 
 // ---- the allocation-free variant's scratch ---------------------------------------

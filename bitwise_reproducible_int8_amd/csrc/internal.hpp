@@ -60,6 +60,9 @@ hipError_t quant_flat(const void* x, int dtype, const float* col_mul, int64_t n,
 hipError_t quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
                       int8_t* q, float* scale, float* amax, int32_t* dflags,
                       hipStream_t s);
+// Per-row quantisation (and transposes) of count tensors in a few grouped
+// launches; jobs validated by the caller, count <= BRQ_ROWS_MULTI_MAX.
+hipError_t quant_rows_multi(const brq_rows_job* jobs, int count, int32_t* dflags, hipStream_t s);
 
 // Exact-sum statistic (exact.hip): per-tensor S and max |v| into out2[0..1]
 // (two launches), and the per-row quantiser with exact row statistics.

@@ -463,15 +463,12 @@ hipError_t quant_flat(const void* x, int dtype, const float* col_mul, int64_t n,
 // covers columns [(64 v + l) E, + E); columns past the end are +0 leaves.
 // --------------------------------------------------------------------------
 template <typename T, int V>
-__global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int64_t rows,
-                                                    int64_t cols, float inv_cols,
-                                                    int8_t* __restrict__ q,
-                                                    float* __restrict__ scale,
-                                                    float* __restrict__ amax, int32_t* flags) {
+__device__ __forceinline__ void quant_one_row(const T* __restrict__ x, int64_t row, int64_t cols,
+                                              float inv_cols, int8_t* __restrict__ q,
+                                              float* __restrict__ scale,
+                                              float* __restrict__ amax, int32_t* flags,
+                                              int lane) {
   constexpr int E = Elem<T>::kPerVec;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
   const T* xr = x + row * cols;
   u32x4 raw[V];
   float node[V];
@@ -518,12 +515,165 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
   }
 }
 
-hipError_t quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int8_t* q,
-                      float* scale, float* amax, int32_t* dflags, hipStream_t s) {
+template <typename T, int V>
+__global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int64_t rows,
+                                                    int64_t cols, float inv_cols,
+                                                    int8_t* __restrict__ q,
+                                                    float* __restrict__ scale,
+                                                    float* __restrict__ amax, int32_t* flags) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  quant_one_row<T, V>(x, row, cols, inv_cols, q, scale, amax, flags, threadIdx.x & 63);
+}
+
+// One row over W waves of a work-group (wide rows: fewer registers per lane
+// and W times the work-groups): wave wv of the row owns vectors wv V/W ..
+// (wv + 1) V/W - 1, so its node is the pairwise tree over an aligned run of
+// V/W of the row's V vector nodes, and the W nodes, exchanged through LDS,
+// close the same tree.  Every wave of the work-group reaches the barrier
+// (rows past the end take no loads and store nothing).
+template <typename T, int V, int W>
+__device__ __forceinline__ void quant_row_split(const T* __restrict__ x, int64_t row, bool live,
+                                                int64_t cols, float inv_cols,
+                                                int8_t* __restrict__ q, float* __restrict__ scale,
+                                                float* __restrict__ amax, int32_t* flags,
+                                                int lane, int wave, float (*red)[2]) {
+  constexpr int E = Elem<T>::kPerVec;
+  constexpr int VW = V / W;
+  const int wv = wave % W;
+  const T* xr = x + row * cols;
+  u32x4 raw[VW];
+  float node[VW];
+  float mx = 0.0f;
+#pragma unroll
+  for (int v = 0; v < VW; ++v) {
+    const int64_t c0 = (int64_t)((wv * VW + v) * 64 + lane) * E;
+    float f[E];
+    if (live && c0 < cols) {
+      raw[v] = ld16(xr + c0);
+      Elem<T>::unpack(raw[v], f);
+    } else {
+      raw[v] = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      f[e] = fabs_bits(f[e]);
+      mx = fmaxf(mx, f[e]);
+    }
+    node[v] = wave_tree<false>(reg_tree<false, E>(f));
+  }
+  const float part = reg_tree<false, VW>(node);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    red[wave][0] = part;
+    red[wave][1] = mx;
+  }
+  __syncthreads();
+  if (!live) return;
+  float parts[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    parts[k] = red[wave - wv + k][0];
+    mx = fmaxf(mx, red[wave - wv + k][1]);
+  }
+  const float S = reg_tree<false, W>(parts);
+  const float sc = fmul(fmul(S, inv_cols), lsq_k2());
+  const float r = (sc == 0.0f) ? 0.0f : fl_div(1.0f, sc);
+#pragma unroll
+  for (int v = 0; v < VW; ++v) {
+    const int64_t c0 = (int64_t)((wv * VW + v) * 64 + lane) * E;
+    if (c0 >= cols) continue;
+    float f[E];
+    Elem<T>::unpack(raw[v], f);
+    uint32_t p[2] = {0, 0};
+#pragma unroll
+    for (int e = 0; e < E; e += 4) p[e >> 2] = quant_pack4(f[e], f[e + 1], f[e + 2], f[e + 3], r);
+    if (E == 8) *reinterpret_cast<uint2*>(q + row * cols + c0) = make_uint2(p[0], p[1]);
+    else *reinterpret_cast<uint32_t*>(q + row * cols + c0) = p[0];
+  }
+  if (wv == 0 && lane == 0) {
+    scale[row] = sc;
+    if (amax) amax[row] = mx;
+    if (!__builtin_isfinite(S)) set_flag(flags, BRQ_FLAG_NONFINITE);
+  }
+}
+
+// tensors per grouped launch (the tables travel as kernel arguments)
+constexpr int kMultiMax = 16;
+
+// waves per row of the grouped per-row kernel
+constexpr int rows_waves(int V) { return V >= 16 ? 4 : V >= 8 ? 2 : 1; }
+
+// Several tensors' per-row quantisations in one launch: work-group b
+// belongs to the tensor whose block range [start[k], start[k + 1]) holds
+// it and quantises its rows 4/W (b - start[k]) .., W = rows_waves(V) waves
+// per row, V the tensor's vectors per lane and row.
+struct RowsJob {
+  const void* x;
+  int64_t rows, cols;
+  int8_t* q;
+  float* scale;
+  float* amax;
+  float inv_cols;
+  int V;
+};
+struct RowsTable {
+  RowsJob j[kMultiMax];
+  int64_t start[kMultiMax + 1];
+  int count;
+};
+
+template <typename T, int V>
+__device__ __forceinline__ void rows_job(const RowsJob& j, int64_t blk, int wave, int lane,
+                                         int32_t* flags, float (*red)[2]) {
+  constexpr int W = rows_waves(V);
+  const int64_t row = blk * (4 / W) + wave / W;
+  if constexpr (W == 1) {
+    if (row < j.rows)
+      quant_one_row<T, V>((const T*)j.x, row, j.cols, j.inv_cols, j.q, j.scale, j.amax, flags,
+                          lane);
+  } else {
+    quant_row_split<T, V, W>((const T*)j.x, row, row < j.rows, j.cols, j.inv_cols, j.q, j.scale,
+                             j.amax, flags, lane, wave, red);
+  }
+}
+
+// VMAX: the widest V the launch holds (its register budget); each job's V
+// is dispatched at run time (uniform per work-group).
+template <typename T, int VMAX>
+__global__ __launch_bounds__(256) void k_quant_rows_multi(RowsTable tab, int32_t* flags) {
+  __shared__ float red[4][2];
+  const int64_t b = blockIdx.x;
+  int k = 0;
+  while (k + 1 < tab.count && b >= tab.start[k + 1]) ++k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const RowsJob& j = tab.j[k];
+  const int64_t blk = b - tab.start[k];
+  switch (j.V) {
+    case 1: rows_job<T, 1>(j, blk, wave, lane, flags, red); break;
+    case 2: rows_job<T, 2>(j, blk, wave, lane, flags, red); break;
+    case 4: rows_job<T, 4>(j, blk, wave, lane, flags, red); break;
+    case 8: if constexpr (VMAX >= 8) rows_job<T, 8>(j, blk, wave, lane, flags, red); break;
+    case 16: if constexpr (VMAX >= 16) rows_job<T, 16>(j, blk, wave, lane, flags, red); break;
+    case 32: if constexpr (VMAX >= 32) rows_job<T, 32>(j, blk, wave, lane, flags, red); break;
+    default: if constexpr (VMAX >= 64) rows_job<T, 64>(j, blk, wave, lane, flags, red); break;
+  }
+}
+
+// vectors of 16 bytes per lane and row: the power of two covering cols
+int rows_vectors(int dtype, int64_t cols) {
   const int E = dtype == BRQ_BF16 ? 8 : 4;
-  int64_t per = (cols + 64 * E - 1) / (64 * E);
+  const int64_t per = (cols + 64 * E - 1) / (64 * E);
   int V = 1;
   while (V < per) V *= 2;
+  return V;
+}
+
+hipError_t quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int8_t* q,
+                      float* scale, float* amax, int32_t* dflags, hipStream_t s) {
+  const int V = rows_vectors(dtype, cols);
   const float inv_cols = 1.0f / (float)cols;  // host binary32 division, correctly rounded
   dim3 g((unsigned)cdiv(rows, 4)), b(256);
 #define BRQ_ROWS(TT, VV)                                                                    \
@@ -556,11 +706,11 @@ hipError_t quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int8
 // --------------------------------------------------------------------------
 // int8 transpose through LDS, 64x64 tiles.  rows % 16 == 0, cols % 16 == 0.
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_transpose_i8(const int8_t* __restrict__ q, int64_t rows,
-                                                      int64_t cols, int8_t* __restrict__ qt) {
+__device__ __forceinline__ void transpose_tile(const int8_t* __restrict__ q, int64_t rows,
+                                               int64_t cols, int8_t* __restrict__ qt, int64_t r0,
+                                               int64_t c0) {
   __shared__ uint32_t tile[64][17];  // 64 rows x 64 bytes, one padding word per row
   const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
   {
     const int r = t >> 2, ch = t & 3;
     u32x4 v = {0, 0, 0, 0};
@@ -583,10 +733,160 @@ __global__ __launch_bounds__(256) void k_transpose_i8(const int8_t* __restrict__
   st16(qt + (c0 + c) * rows + r0 + rg, u32x4{p[0], p[1], p[2], p[3]});
 }
 
+__global__ __launch_bounds__(256) void k_transpose_i8(const int8_t* __restrict__ q, int64_t rows,
+                                                      int64_t cols, int8_t* __restrict__ qt) {
+  transpose_tile(q, rows, cols, qt, (int64_t)blockIdx.y * 64, (int64_t)blockIdx.x * 64);
+}
+
+// 128 x 128 tile per work-group (16 KiB each way): each lane loads four
+// 16-byte pieces of input rows (8 lanes per 128-byte row), and each store
+// writes 16 bytes of one output row, 8 neighbouring lanes covering an
+// output row's 128 bytes.  rows % 16 == 0 and cols % 16 == 0 (whole
+// 16-byte pieces).
+__device__ __forceinline__ void transpose_tile128(const int8_t* __restrict__ q, int64_t rows,
+                                                  int64_t cols, int8_t* __restrict__ qt,
+                                                  int64_t r0, int64_t c0) {
+  __shared__ uint32_t tile[128][33];  // 128 rows x 128 bytes, one padding word per row
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = i * 256 + t, r = id >> 3, ch = id & 7;
+    u32x4 v = {0, 0, 0, 0};
+    if (r0 + r < rows && c0 + ch * 16 < cols) v = ld16(q + (r0 + r) * cols + c0 + ch * 16);
+    tile[r][ch * 4 + 0] = v.x;
+    tile[r][ch * 4 + 1] = v.y;
+    tile[r][ch * 4 + 2] = v.z;
+    tile[r][ch * 4 + 3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = i * 256 + t, c = id >> 3, rg = (id & 7) * 16;
+    if (c0 + c >= cols || r0 + rg >= rows) continue;
+    uint32_t p[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t byte = (tile[rg + k][c >> 2] >> (8 * (c & 3))) & 0xffu;
+      p[k >> 2] |= byte << (8 * (k & 3));
+    }
+    st16(qt + (c0 + c) * rows + r0 + rg, u32x4{p[0], p[1], p[2], p[3]});
+  }
+}
+
+// Several transposes in one launch: work-group b is tile b - start[k] of
+// tensor k (tiles_x tiles of 128 x 128 per row of tiles).
+struct TrJob {
+  const int8_t* q;
+  int64_t rows, cols;
+  int8_t* qt;
+  int64_t tiles_x;
+};
+struct TrTable {
+  TrJob j[kMultiMax];
+  int64_t start[kMultiMax + 1];
+  int count;
+};
+
+__global__ __launch_bounds__(256) void k_transpose_i8_multi(TrTable tab) {
+  const int64_t b = blockIdx.x;
+  int k = 0;
+  while (k + 1 < tab.count && b >= tab.start[k + 1]) ++k;
+  const int64_t tile = b - tab.start[k], tx = tab.j[k].tiles_x;
+  const int64_t by = tile / tx, bx = tile - by * tx;
+  transpose_tile128(tab.j[k].q, tab.j[k].rows, tab.j[k].cols, tab.j[k].qt, by * 128, bx * 128);
+}
+
 hipError_t transpose_i8(const int8_t* q, int64_t rows, int64_t cols, int8_t* qt, hipStream_t s) {
   dim3 g((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows, 64)), b(256);
   hipLaunchKernelGGL(k_transpose_i8, g, b, 0, s, q, rows, cols, qt);
   return hipGetLastError();
+}
+
+// Per-row quantisation of several tensors (with transposed codes where
+// asked): one launch per table of up to kMultiMax tensors of one element
+// type and width class (rows up to 16 vectors a lane, or one wider V),
+// then one launch per table of transposes.
+hipError_t quant_rows_multi(const brq_rows_job* jobs, int count, int32_t* dflags, hipStream_t s) {
+  bool done[BRQ_ROWS_MULTI_MAX] = {};
+  for (int a = 0; a < count; ++a) {
+    if (done[a]) continue;
+    const int dtype = jobs[a].x_dtype;
+    // one launch class for every V up to 16 (at most 67 registers a lane),
+    // one per wider V
+    auto vclass = [&](int64_t cols) {
+      const int V = rows_vectors(dtype, cols);
+      return V <= 16 ? 16 : V;
+    };
+    const int VC = vclass(jobs[a].cols);
+    RowsTable tab{};
+    int64_t blocks = 0;
+    auto flush_table = [&]() -> hipError_t {
+      if (tab.count == 0) return hipSuccess;
+      tab.start[tab.count] = blocks;
+      dim3 g((unsigned)blocks), b(256);
+#define BRQ_MULTI(TT, VV) hipLaunchKernelGGL((k_quant_rows_multi<TT, VV>), g, b, 0, s, tab, dflags)
+      if (dtype == BRQ_BF16) {
+        if (VC == 16) BRQ_MULTI(uint16_t, 16);
+        else BRQ_MULTI(uint16_t, 32);
+      } else {
+        if (VC == 16) BRQ_MULTI(float, 16);
+        else if (VC == 32) BRQ_MULTI(float, 32);
+        else BRQ_MULTI(float, 64);
+      }
+#undef BRQ_MULTI
+      tab = RowsTable{};
+      blocks = 0;
+      return hipGetLastError();
+    };
+    for (int c = a; c < count; ++c) {
+      if (done[c] || jobs[c].x_dtype != dtype || vclass(jobs[c].cols) != VC) continue;
+      done[c] = true;
+      if (jobs[c].rows == 0) continue;
+      RowsJob& j = tab.j[tab.count];
+      j.x = jobs[c].x;
+      j.rows = jobs[c].rows;
+      j.cols = jobs[c].cols;
+      j.q = jobs[c].q;
+      j.scale = jobs[c].scale;
+      j.amax = jobs[c].amax;
+      j.inv_cols = 1.0f / (float)jobs[c].cols;  // host binary32 division, correctly rounded
+      j.V = rows_vectors(dtype, jobs[c].cols);
+      tab.start[tab.count] = blocks;
+      blocks += cdiv(jobs[c].rows, 4 / rows_waves(j.V));
+      if (++tab.count == kMultiMax) {
+        const hipError_t e = flush_table();
+        if (e != hipSuccess) return e;
+      }
+    }
+    const hipError_t e = flush_table();
+    if (e != hipSuccess) return e;
+  }
+  TrTable tt{};
+  int64_t tblocks = 0;
+  auto flush_tr = [&]() -> hipError_t {
+    if (tt.count == 0) return hipSuccess;
+    tt.start[tt.count] = tblocks;
+    hipLaunchKernelGGL(k_transpose_i8_multi, dim3((unsigned)tblocks), dim3(256), 0, s, tt);
+    tt = TrTable{};
+    tblocks = 0;
+    return hipGetLastError();
+  };
+  for (int c = 0; c < count; ++c) {
+    if (!jobs[c].q_t || jobs[c].rows == 0) continue;
+    TrJob& j = tt.j[tt.count];
+    j.q = jobs[c].q;
+    j.rows = jobs[c].rows;
+    j.cols = jobs[c].cols;
+    j.qt = jobs[c].q_t;
+    j.tiles_x = cdiv(jobs[c].cols, 128);
+    tt.start[tt.count] = tblocks;
+    tblocks += j.tiles_x * cdiv(jobs[c].rows, 128);
+    if (++tt.count == kMultiMax) {
+      const hipError_t e = flush_tr();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return flush_tr();
 }
 
 }  // namespace brq

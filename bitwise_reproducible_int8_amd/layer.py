@@ -49,8 +49,8 @@ import torch
 from . import (ADAMW_WD, SPIKE_THRESHOLD, BrqError, OP_DW_WHT, OP_DY_BWD, OP_GRAD_NORM, OP_QGEMM, OP_QUANTIZE,
                OP_RMSNORM_BWD, adamw_bias_corrections, adamw_decide, adamw_step, grad_norm,
                hash_state, hash_state_workspace_size, qgemm_bwd_dx, qgemm_dw, qgemm_fwd,
-               quantize_dy_bwd, quantize_lsq, rmsnorm_fixed_bwd, rmsnorm_fixed_fwd, wht_quant_x,
-               workspace_size)
+               quantize_dy_bwd, quantize_lsq, quantize_lsq_rows_multi, rmsnorm_fixed_bwd,
+               rmsnorm_fixed_fwd, wht_quant_x, workspace_size)
 
 
 class _NoTimer:
@@ -114,6 +114,7 @@ class LayerStep:
             self.q_vt.append(e(N, M, dt=i8)); self.s_v.append(e(1))
             self.dw.append(self.arena[off:off + N * K].view(N, K))
             off += N * K
+        self.w_outs = list(zip(self.q_w, self.q_wt, self.s_w, self.amax_w))
         self.ny, self.nrstd, self.ndx, self.ndg = [], [], [], []
         for (_name, h, g, ndy) in self.norms:
             T, D = h.shape
@@ -165,11 +166,11 @@ class LayerStep:
             quantize_lsq(t, tune=tune, ws=ws, flags=fl,
                          out=(self.q_x[xin], None, self.s_x[xin], self.amax_x[xin]))
             T.end("quant_x")
+        # every linear's per-channel weight steps and codes: one grouped call
+        T.begin("quant_w")
+        quantize_lsq_rows_multi(self.w, flags=fl, outs=self.w_outs)
+        T.end("quant_w")
         for i, (_name, _K, _N, xin) in enumerate(self.linears):
-            T.begin("quant_w")
-            quantize_lsq(self.w[i], per_row=True, want_t=True, tune=tune, ws=ws, flags=fl,
-                         out=(self.q_w[i], self.q_wt[i], self.s_w[i], self.amax_w[i]))
-            T.end("quant_w")
             T.begin("gemm_fwd")
             qgemm_fwd(self.q_x[xin], self.s_x[xin], self.q_w[i], self.s_w[i], tune=tune,
                       out=self.y[i], ws=ws)

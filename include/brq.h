@@ -126,6 +126,36 @@ int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols,
                      int32_t* dflags, const struct brq_tune* tune, void* stream);
 
 /* ---------------------------------------------------------------------
+ * quantize_lsq_rows_multi -- the per-row (BRQ_PER_ROW) brq_quantize_lsq of
+ * several tensors in one call: the per-channel weight steps of every linear
+ * of a layer (§3.1 "int8 quantization-aware training": learned per-channel
+ * step sizes for weights).  Each job is one tensor:
+ *     x [rows][cols] (x_dtype BRQ_F32 or BRQ_BF16), q [rows][cols] int8,
+ *     q_t [cols][rows] int8 or NULL, scale [rows], amax [rows] or NULL,
+ * all device pointers owned by the caller; the results of every job are
+ * those of brq_quantize_lsq(x, x_dtype, rows, cols, BRQ_PER_ROW, NULL, q,
+ * q_t, scale, amax, ...) bit for bit.  Jobs of one element type and row
+ * width class share one launch (up to 16 per launch), and every transpose
+ * of the call shares one more.  No workspace.  Errors: count < 0 or
+ * count > BRQ_ROWS_MULTI_MAX -> BRQ_E_ARG; a job failing the shape, dtype,
+ * null or alignment rules of brq_quantize_lsq per row -> that code, and
+ * nothing is launched.  A job with rows == 0 does nothing (its pointers
+ * may be NULL).  Jobs must not overlap in their outputs.
+ * --------------------------------------------------------------------- */
+#define BRQ_ROWS_MULTI_MAX 1024
+typedef struct brq_rows_job {
+  const void* x;
+  int x_dtype;
+  int64_t rows, cols;
+  int8_t* q;
+  int8_t* q_t;
+  float* scale;
+  float* amax;
+} brq_rows_job;
+int brq_quantize_lsq_rows_multi(const brq_rows_job* jobs, int count,
+                                int32_t* dflags, void* stream);
+
+/* ---------------------------------------------------------------------
  * quantize_lsq_static -- brq_quantize_lsq without a workspace argument, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation).  The per-tensor

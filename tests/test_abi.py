@@ -113,3 +113,36 @@ def test_static_quantiser_rejects_what_its_scratch_cannot_hold(lib):
     assert f(fake, 1, -1, 8, 0, None, fake, None, fake, None, None, None, None) == -3
     lib.brq_status_string.restype = C.c_char_p
     assert b"static scratch" in lib.brq_status_string(-10)
+
+
+def test_rows_multi_argument_checks(lib):
+    """brq_quantize_lsq_rows_multi checks every job before anything runs
+    (these return without a device call)."""
+    class Job(C.Structure):
+        _fields_ = [("x", C.c_void_p), ("x_dtype", C.c_int), ("rows", C.c_int64),
+                    ("cols", C.c_int64), ("q", C.c_void_p), ("q_t", C.c_void_p),
+                    ("scale", C.c_void_p), ("amax", C.c_void_p)]
+    f = lib.brq_quantize_lsq_rows_multi
+    f.restype = C.c_int
+    f.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]
+    fake = 0x1000
+    jobs = (Job * 2)(Job(fake, 1, 16, 64, fake, None, fake, None),
+                     Job(fake, 1, 16, 64, fake, None, fake, None))
+    assert f(None, 0, None, None) == 0          # nothing to do
+    assert f(jobs, -1, None, None) == -9        # count out of range
+    assert f(jobs, 1025, None, None) == -9
+    assert f(None, 2, None, None) == -1         # no job array
+    jobs[1].cols = 20000                        # wider than a per-row group may be
+    assert f(jobs, 2, None, None) == -5
+    jobs[1].cols = 60                           # not a whole bf16 vector
+    assert f(jobs, 2, None, None) == -5
+    jobs[1].cols, jobs[1].x_dtype = 64, 2       # int8 input
+    assert f(jobs, 2, None, None) == -2
+    jobs[1].x_dtype, jobs[1].rows = 1, -1
+    assert f(jobs, 2, None, None) == -3
+    jobs[1].rows, jobs[1].q_t, jobs[1].cols = 8, fake, 64   # transpose needs rows % 16
+    assert f(jobs, 2, None, None) == -5
+    jobs[1].q_t, jobs[1].x = None, fake + 4     # misaligned input
+    assert f(jobs, 2, None, None) == -4
+    jobs[1].x, jobs[1].scale = fake, None
+    assert f(jobs, 2, None, None) == -1

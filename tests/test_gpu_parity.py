@@ -83,6 +83,51 @@ def test_quantize_per_row(shape, bf16):
         assert_bitwise(gqt, qt, "q_t")
 
 
+def _rows_multi_check(shapes, tag):
+    ws = []
+    for k, (rows, cols, bf16) in enumerate(shapes):
+        ws.append(syn.normal((rows, cols), 0.02, tag=tag + k, bf16=bf16))
+    want_t = all(r % 16 == 0 and c % 16 == 0 for r, c, _ in shapes)
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = brq.quantize_lsq_rows_multi([to_dev(w) for w in ws], want_t=want_t, flags=flags)
+    for k, w in enumerate(ws):
+        q, qt, s, amax, fl = orc.quantize_lsq(w, per_row=True, want_t=want_t)
+        gq, gqt, gs, gamax = got[k]
+        name = f"job {k} {shapes[k]}"
+        assert_bitwise(gq, q, f"{name} q")
+        assert_bitwise(gs, s, f"{name} scale")
+        assert_bitwise(gamax, amax, f"{name} amax")
+        if want_t:
+            assert_bitwise(gqt, qt, f"{name} q_t")
+    assert int(flags.item()) == 0
+
+
+def test_quantize_rows_multi_layer_weights():
+    """The seven Open-1B weights of a layer in one grouped call (two row
+    width classes, one transpose launch) equal the per-row quantiser."""
+    say("quantize_rows_multi layer weights")
+    shapes = [(N, K, True) for _, K, N, _ in syn.LAYER_LINEARS]
+    _rows_multi_check(shapes, 500)
+
+
+@pytest.mark.parametrize("case", ["mixed", "many", "ragged"])
+def test_quantize_rows_multi_edges(case):
+    """Mixed element types and widths in one call, more tensors than one
+    launch table holds, rows that are not a multiple of the 4 rows of a
+    work-group, and an empty tensor among the jobs."""
+    say("quantize_rows_multi", case)
+    if case == "mixed":
+        shapes = [(48, 1024, False), (32, 8192, True), (64, 272, True), (16, 16384, True),
+                  (0, 512, True), (80, 2048, False), (16, 64, True)]
+        _rows_multi_check(shapes, 540)
+    elif case == "many":
+        shapes = [(16 * (1 + k % 5), 64 * (1 + k % 7), k % 2 == 0) for k in range(37)]
+        _rows_multi_check(shapes, 560)
+    else:
+        shapes = [(5, 64, True), (33, 136, True), (1, 8, True), (7, 1000, False), (3, 16384, True)]
+        _rows_multi_check(shapes, 600)
+
+
 def test_quantize_edge_cases():
     say("quantize_edge_cases")
     z = np.zeros((32, 64), np.float32)
