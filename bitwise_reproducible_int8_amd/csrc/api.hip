@@ -154,17 +154,20 @@ int quantize_common(const void* x, int x_dtype, int64_t rows, int64_t cols, int 
     const size_t need = exact ? quant_exact_ws(rows, cols) : quant_ws(rows, cols, tune);
     if (!ws || ws_bytes < need) return BRQ_E_WORKSPACE;
     float* sc = (float*)((char*)ws + need - kScalars);  // [0]sum [1]max [2]s [3]r
-    if (exact) {
-      e = exact_reduce(x, x_dtype, col_mul, n, cols > 0 ? cols : 1, sc, ws, dflags, s);
-    } else {
-      const int leaf = col_mul ? LEAF_ABS_COLMUL : LEAF_ABS;
-      e = flat_reduce(x, x_dtype, leaf, col_mul, n, cols > 0 ? cols : 1, sc, ws,
-                      flat_chunk_log2(tune), dflags, s);
-    }
-    if (e != hipSuccess) return hip_status(e);
     // an empty group has step size 0 (no mean is taken)
     const float inv_n = n > 0 ? 1.0f / (float)n : 0.0f;
-    if ((e = lsq_finalize(sc, inv_n, sc + 2, scale, amax, s)) != hipSuccess) return hip_status(e);
+    if (exact) {
+      e = exact_reduce(x, x_dtype, col_mul, n, cols > 0 ? cols : 1, sc, ws, dflags, s);
+      if (e != hipSuccess) return hip_status(e);
+      if ((e = lsq_finalize(sc, inv_n, sc + 2, scale, amax, s)) != hipSuccess) return hip_status(e);
+    } else {
+      // the step size is computed by the reduction's final work-group
+      const int leaf = col_mul ? LEAF_ABS_COLMUL : LEAF_ABS;
+      const FlatFin fin{FIN_LSQ, inv_n, sc + 2, scale, amax, nullptr, nullptr};
+      e = flat_reduce(x, x_dtype, leaf, col_mul, n, cols > 0 ? cols : 1, sc, ws,
+                      flat_chunk_log2(tune), dflags, s, 0, &fin);
+      if (e != hipSuccess) return hip_status(e);
+    }
     if (n > 0 && (e = quant_flat(x, x_dtype, col_mul, n, cols, sc + 2, q, s)) != hipSuccess)
       return hip_status(e);
   }

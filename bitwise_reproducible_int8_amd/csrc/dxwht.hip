@@ -102,10 +102,11 @@ hipError_t wht_rows_quant(const void* dy, int dtype, int64_t M, int64_t N, const
                           int32_t* dflags, hipStream_t s) {
   const int64_t n = M * N;
   float* sc = (float*)((char*)ws + flat_reduce_ws(n, 13));  // [0] sum [1] max
-  hipError_t e = flat_reduce(dy, dtype, LEAF_ABS_COLMUL, s_w, n, N, sc, ws, 13, dflags, s, block);
-  if (e != hipSuccess) return e;
   const float inv_n = n > 0 ? 1.0f / (float)n : 0.0f;
-  if ((e = lsq_finalize(sc, inv_n, sr, s_g, nullptr, s)) != hipSuccess) return e;
+  const FlatFin fin{FIN_LSQ, inv_n, sr, s_g, nullptr, nullptr, nullptr};
+  hipError_t e =
+      flat_reduce(dy, dtype, LEAF_ABS_COLMUL, s_w, n, N, sc, ws, 13, dflags, s, block, &fin);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scale_one, dim3(1), dim3(1), 0, s, sr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (n == 0) return hipSuccess;

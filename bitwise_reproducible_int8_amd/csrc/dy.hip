@@ -337,44 +337,6 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
   }
 }
 
-// Order-free max of the per-work-group maxima, then both LSQ steps:
-// sr4 = {s_g, r_g, s_v, r_v}.
-__global__ __launch_bounds__(1024) void k_dy_finalize(const float* __restrict__ sum_g,
-                                                      const float* __restrict__ sum_v,
-                                                      const float* __restrict__ bmax, int64_t nb,
-                                                      float inv_n, float* sr4, float* s_g,
-                                                      float* amax_g, float* s_v) {
-  // 8 independent loads in flight per lane per round (max is order-free)
-  float m = 0.0f;
-  for (int64_t i0 = 0; i0 < nb; i0 += 8 * 1024) {
-    float x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t i = i0 + u * 1024 + threadIdx.x;
-      x[u] = i < nb ? bmax[i] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m = fmaxf(m, x[u]);
-  }
-  m = wave_max(m);
-  __shared__ float w[16];
-  if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int i = 4; i < 16; ++i) w[0] = fmaxf(w[0], w[i]);
-    const float sg = fmul(fmul(sum_g[0], inv_n), lsq_k2());
-    const float sv = fmul(fmul(sum_v[0], inv_n), lsq_k2());
-    sr4[0] = sg;
-    sr4[1] = sg == 0.0f ? 0.0f : fl_div(1.0f, sg);
-    sr4[2] = sv;
-    sr4[3] = sv == 0.0f ? 0.0f : fl_div(1.0f, sv);
-    s_g[0] = sg;
-    s_v[0] = sv;
-    if (amax_g) amax_g[0] = fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3]));
-  }
-}
-
 }  // namespace
 
 bool dy_fused_ok(int dtype, int64_t M, int64_t N, int block) {
@@ -410,13 +372,13 @@ hipError_t quantize_dy_fused(const void* dy, int64_t M, int64_t N, const float* 
                      bmax);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = flat_reduce_pair(part_g, part_v, P, sc, sc + 2, fws, chunk_log2, dflags, s)) !=
+  // both step sizes and the max of |g| come from the reduction's two
+  // final work-groups
+  const float inv_n = 1.0f / (float)(M * N);  // host binary32 division, correctly rounded
+  const PairFin fin{1, inv_n, sc + 4, s_g, s_v, amax_g, bmax, gx * gy};
+  if ((e = flat_reduce_pair(part_g, part_v, P, sc, sc + 2, fws, chunk_log2, dflags, s, &fin)) !=
       hipSuccess)
     return e;
-  const float inv_n = 1.0f / (float)(M * N);  // host binary32 division, correctly rounded
-  hipLaunchKernelGGL(k_dy_finalize, dim3(1), dim3(1024), 0, s, sc, sc + 2, bmax, gx * gy, inv_n,
-                     sc + 4, s_g, amax_g, s_v);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_dy_codes, g, b, 0, s, (const uint16_t*)dy, sw, M, N, block, sc + 4, q_g,
                      q_vt);
   return hipGetLastError();

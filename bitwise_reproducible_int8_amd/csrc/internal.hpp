@@ -30,16 +30,42 @@ size_t flat_reduce_ws(int64_t n, int chunk_log2);
 // wht_block > 0 (leaf LEAF_ABS_COLMUL): the leaves are |x * col_mul| after
 // the Walsh-Hadamard rotation along each row in blocks of wht_block
 // (cols % wht_block == 0, wht_block <= 128); the chunk is then fixed.
+// fin (optional): the scalar step the caller would launch after the sum,
+// run by the final work-group instead (same operations, same order).
+enum FinKind { FIN_NONE = 0, FIN_LSQ = 1, FIN_NORM = 2 };
+struct FlatFin {
+  int kind;
+  float inv_n;   // FIN_LSQ: s = fl(fl(S * inv_n) * K2), r = fl(1/s) (0 when s == 0)
+  float* sr;     // FIN_LSQ: {s, r}
+  float* scale;  // FIN_LSQ: s (optional)
+  float* amax;   // FIN_LSQ: the max (optional)
+  float* sumsq;  // FIN_NORM: S
+  float* norm;   // FIN_NORM: fl(sqrt S)
+};
 hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul,
                        int64_t n, int64_t cols, float* out2, void* ws,
-                       int chunk_log2, int32_t* dflags, hipStream_t s, int wht_block = 0);
+                       int chunk_log2, int32_t* dflags, hipStream_t s, int wht_block = 0,
+                       const FlatFin* fin = nullptr);
 
 // Two raw fp32 leaf arrays of equal length n reduced as two flat_reduce
 // calls would, in one launch per level; workspace flat_reduce_pair_ws.
 size_t flat_reduce_pair_ws(int64_t n, int chunk_log2);
+// fin (optional): both LSQ steps from the two sums -- sr4 = {s0, r0, s1, r1},
+// s0/s1 copies -- and amax0 = the max over bmax[0 .. nb) (order-free), run
+// by the two final work-groups.
+struct PairFin {
+  int on;
+  float inv_n;
+  float* sr4;
+  float* s0;
+  float* s1;
+  float* amax0;
+  const float* bmax;
+  int64_t nb;
+};
 hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* out0,
                             float* out1, void* ws, int chunk_log2, int32_t* dflags,
-                            hipStream_t s);
+                            hipStream_t s, const PairFin* fin = nullptr);
 
 // Optimizer step (optim.hip).
 hipError_t adamw_decide(const float* norm, float max_norm, float spike, int skip_steps,

@@ -592,20 +592,15 @@ hipError_t rmsnorm_bwd(const void* x, const void* g, const float* rstd, const vo
 }
 
 // ---- global gradient norm ------------------------------------------------------
-__global__ void k_gn_finalize(const float* sum_max, float* sumsq, float* norm) {
-  const float ss = sum_max[0];
-  sumsq[0] = ss;
-  norm[0] = fl_sqrt(ss);
-}
-
+// S = the tree sum of squares, norm = fl(sqrt S): computed by the
+// reduction's final work-group
 hipError_t grad_norm(const float* v, int64_t n, float* sumsq, float* norm, void* ws,
                      int chunk_log2, int32_t* dflags, hipStream_t s) {
   float* sum2 = (float*)ws;
   void* fws = (char*)ws + 256;
-  hipError_t e = flat_reduce(v, BRQ_F32, LEAF_SQUARE, nullptr, n, 1, sum2, fws, chunk_log2, dflags, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gn_finalize, dim3(1), dim3(1), 0, s, sum2, sumsq, norm);
-  return hipGetLastError();
+  const FlatFin fin{FIN_NORM, 0.0f, nullptr, nullptr, nullptr, sumsq, norm};
+  return flat_reduce(v, BRQ_F32, LEAF_SQUARE, nullptr, n, 1, sum2, fws, chunk_log2, dflags, s, 0,
+                     &fin);
 }
 
 }  // namespace brq

@@ -144,7 +144,8 @@ __global__ __launch_bounds__(256) void k_flat_leaves_pair(FlatPair a, int64_t n)
 // lane an aligned run of 32.  Writes out[0] = sum, out[1] = max.
 __device__ __forceinline__ void flat_final_body(const float* __restrict__ psum,
                                                 const float* __restrict__ pmax, int64_t P,
-                                                float* out, int32_t* flags) {
+                                                float* out, int32_t* flags, float* s_out = nullptr,
+                                                float* m_out = nullptr) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   float a[32];
   float mx = 0.0f;
@@ -167,20 +168,69 @@ __device__ __forceinline__ void flat_final_body(const float* __restrict__ psum,
     out[0] = s;
     out[1] = m;
     if (!__builtin_isfinite(s)) set_flag(flags, BRQ_FLAG_NONFINITE);
+    if (s_out) *s_out = s;
+    if (m_out) *m_out = m;
   }
+}
+
+// LSQ step size and reciprocal from a tree sum S (the operations of
+// k_lsq_finalize): m = fl(S * inv_n), s = fl(m * K2), r = fl(1/s).
+__device__ __forceinline__ void lsq_step(float S, float inv_n, float& sc, float& r) {
+  sc = fmul(fmul(S, inv_n), lsq_k2());
+  r = (sc == 0.0f) ? 0.0f : fl_div(1.0f, sc);
 }
 
 __global__ __launch_bounds__(1024) void k_flat_final(const float* __restrict__ psum,
                                                      const float* __restrict__ pmax,
-                                                     int64_t P, float* out, int32_t* flags) {
-  flat_final_body(psum, pmax, P, out, flags);
+                                                     int64_t P, float* out, int32_t* flags,
+                                                     FlatFin fin) {
+  float S = 0.0f, M = 0.0f;
+  flat_final_body(psum, pmax, P, out, flags, &S, &M);
+  if (threadIdx.x != 0) return;
+  if (fin.kind == FIN_LSQ) {
+    float sc, r;
+    lsq_step(S, fin.inv_n, sc, r);
+    fin.sr[0] = sc;
+    fin.sr[1] = r;
+    if (fin.scale) fin.scale[0] = sc;
+    if (fin.amax) fin.amax[0] = M;
+  } else if (fin.kind == FIN_NORM) {
+    fin.sumsq[0] = S;
+    fin.norm[0] = fl_sqrt(S);
+  }
 }
 
 // blockIdx.x selects the array of the pair
 __global__ __launch_bounds__(1024) void k_flat_final_pair(FlatPair a, int64_t P, float* out0,
-                                                          float* out1, int32_t* flags) {
+                                                          float* out1, int32_t* flags,
+                                                          PairFin fin) {
   const int y = blockIdx.x;
-  flat_final_body(a.ps[y], a.pm[y], P, y ? out1 : out0, flags);
+  float S = 0.0f;
+  flat_final_body(a.ps[y], a.pm[y], P, y ? out1 : out0, flags, &S);
+  if (!fin.on) return;
+  float m = 0.0f;
+  if (y == 0) {
+    // order-free max of the work-group maxima
+    for (int64_t i = threadIdx.x; i < fin.nb; i += 1024) m = fmaxf(m, fin.bmax[i]);
+    m = wave_max(m);
+    __shared__ float wm[16];
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, wm[i]);
+  }
+  if (threadIdx.x != 0) return;
+  float sc, r;
+  lsq_step(S, fin.inv_n, sc, r);
+  fin.sr4[2 * y] = sc;
+  fin.sr4[2 * y + 1] = r;
+  if (y == 0) {
+    if (fin.s0) fin.s0[0] = sc;
+    if (fin.amax0) fin.amax0[0] = m;
+  } else if (fin.s1) {
+    fin.s1[0] = sc;
+  }
 }
 
 int flat_chunk_log2(const brq_tune* t) {
@@ -281,7 +331,7 @@ static hipError_t launch_leaves_wht(const T* x, const float* cm, int64_t n, int6
 
 hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul, int64_t n,
                        int64_t cols, float* out2, void* ws, int chunk_log2, int32_t* dflags,
-                       hipStream_t s, int wht_block) {
+                       hipStream_t s, int wht_block, const FlatFin* fin) {
   if (wht_block > 0) chunk_log2 = 13;
   const int E = dtype == BRQ_BF16 ? 8 : 4;
   const int V = vectors_for(chunk_log2, E);
@@ -326,8 +376,9 @@ hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul,
                        P[i - 1], pm[i]);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  const FlatFin f = fin ? *fin : FlatFin{FIN_NONE, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr};
   hipLaunchKernelGGL(k_flat_final, dim3(1), dim3(1024), 0, s, ps[L - 1], pm[L - 1], P[L - 1],
-                     out2, dflags);
+                     out2, dflags, f);
   return hipGetLastError();
 }
 
@@ -337,7 +388,7 @@ size_t flat_reduce_pair_ws(int64_t n, int chunk_log2) { return 2 * flat_reduce_w
 // flat_reduce calls would (same chunks, same tree), in one launch per level.
 hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* out0,
                             float* out1, void* ws, int chunk_log2, int32_t* dflags,
-                            hipStream_t s) {
+                            hipStream_t s, const PairFin* fin) {
   const int V = vectors_for(chunk_log2, 4);
   const int64_t C0 = int64_t(256) * 4 * V;
   const int Vr = 16;
@@ -377,8 +428,9 @@ hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* 
                        lv[i], P[i - 1]);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  const PairFin f = fin ? *fin : PairFin{0, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, 0};
   hipLaunchKernelGGL(k_flat_final_pair, dim3(2), dim3(1024), 0, s, lv[L - 1], P[L - 1], out0,
-                     out1, dflags);
+                     out1, dflags, f);
   return hipGetLastError();
 }
 

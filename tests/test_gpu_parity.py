@@ -379,6 +379,25 @@ def test_wht_quant_x(b):
     assert_bitwise(gsu, np.array([su], np.float32), "s_u")
 
 
+def test_wht_quant_x_empty_and_wide():
+    """No tokens or no columns: step size 0 as for any empty group; and a
+    wide input (K = 8192; the first pass's partials are summed by every
+    work-group of the second: 128 of them here; the layer's 32768 x 8192
+    input, with 4096, is in the full-size layer test)."""
+    say("wht_quant_x empty and wide")
+    for shape in ((0, 64), (64, 0)):
+        qx = np.zeros(shape, np.int8)
+        _, su, _ = orc.wht_int_quant(qx, 64)
+        _, gsu = brq.wht_quant_x(to_dev(qx), 64)
+        assert_bitwise(gsu, np.array([su], np.float32), f"s_u {shape}")
+    rng = np.random.default_rng(77)
+    qx = codes(rng, (1024, 8192))
+    qu, su, _ = orc.wht_int_quant(qx, 128)
+    gqut, gsu = brq.wht_quant_x(to_dev(qx), 128)
+    assert_bitwise(gqut, np.ascontiguousarray(qu.T), "q_u^T wide")
+    assert_bitwise(gsu, np.array([su], np.float32), "s_u wide")
+
+
 @pytest.mark.parametrize("b", [1, 16, 64, 128])
 @pytest.mark.parametrize("bf16", [False, True])
 def test_wht_quant_dy(b, bf16):
