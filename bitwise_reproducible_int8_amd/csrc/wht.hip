@@ -41,8 +41,8 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int kWhtCols = 512;
 
 template <int TB>
-__device__ __forceinline__ void wht_tile_issue(const int8_t* __restrict__ q_x, int64_t K,
-                                               int64_t m0, int64_t k0, int8_t* tile) {
+__device__ __forceinline__ void wht_tile_load(const int8_t* __restrict__ q_x, int64_t K,
+                                              int64_t m0, int64_t k0, int8_t* tile) {
   const int t = threadIdx.x, wave = t >> 6;
 #pragma unroll
   for (int i = 0; i < TB * (kWhtCols / 16) / 256; ++i) {
@@ -54,17 +54,9 @@ __device__ __forceinline__ void wht_tile_issue(const int8_t* __restrict__ q_x, i
         (const void*)(q_x + (m0 + row) * K + col),
         (__attribute__((address_space(3))) void*)(tile + (i * 256 + wave * 64) * 16), 16, 0, 0);
   }
-}
-// every load of the tile has landed (this wave's), then every wave's
-__device__ __forceinline__ void wht_tile_wait() {
+  // every load of the tile has landed (this wave's), then every wave's
   __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
   __syncthreads();
-}
-template <int TB>
-__device__ __forceinline__ void wht_tile_load(const int8_t* __restrict__ q_x, int64_t K,
-                                              int64_t m0, int64_t k0, int8_t* tile) {
-  wht_tile_issue<TB>(q_x, K, m0, k0, tile);
-  wht_tile_wait();
 }
 
 template <int TB>
@@ -127,38 +119,44 @@ __global__ __launch_bounds__(256) void k_wht_int_stats(const int8_t* __restrict_
         (long long)ws[0] + ws[1] + ws[2] + ws[3];
 }
 
-// Pass 2: recompute u, quantise, write q_u^T [K][M].  Each work-group
-// first adds the P int64 partials of pass 1 (exact: any order; read while
-// its tile loads are in flight) and takes the LSQ step from the total,
-// fl(double(S)) -> fl(* inv_n) -> fl(* K2); work-group 0 stores it.  The
-// codes go through
+// Exact total, then the LSQ step: fl(double(S)) -> fl(* inv_n) -> fl(* K2).
+__global__ __launch_bounds__(256) void k_wht_int_finalize(const long long* __restrict__ part,
+                                                          int64_t P, float inv_n, float* sr,
+                                                          float* s_out) {
+  long long s = 0;
+  for (int64_t i = threadIdx.x; i < P; i += 256) s += part[i];
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  __shared__ long long ws[4];
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long S = ws[0] + ws[1] + ws[2] + ws[3];
+    float Sf = (float)(double)S;  // exact in double (S < 2^53), one rounding
+    float sc = fmul(fmul(Sf, inv_n), lsq_k2());
+    float r = (sc == 0.0f) ? 0.0f : fl_div(1.0f, sc);
+    sr[0] = sc;
+    sr[1] = r;
+    if (s_out) s_out[0] = sc;
+  }
+}
+
+// Pass 2: recompute u, quantise, write q_u^T [K][M].  The codes go through
 // the same LDS tile transposed, [512 columns][TB tokens], 16-token chunks
 // XOR-swizzled by column (the 8 lanes of one LDS access cycle write 8
 // different bank groups), so that each global store instruction writes
 // whole TB-byte column runs: 16 bytes per lane, TB / 16 lanes per column.
 template <int TB>
 __global__ __launch_bounds__(256) void k_wht_int_quant(const int8_t* __restrict__ q_x, int64_t M,
-                                                       int64_t K, int b,
-                                                       const long long* __restrict__ part,
-                                                       int64_t P, float inv_n, float* s_out,
+                                                       int64_t K, int b, const float* __restrict__ sr,
                                                        int8_t* __restrict__ q_ut) {
   constexpr int QC = TB / 16;  // 16-token chunks per column
   __shared__ __attribute__((aligned(1024))) int8_t tile[TB * kWhtCols];
-  __shared__ long long wsum[4];
   const int t = threadIdx.x;
   const int64_t k0 = (int64_t)blockIdx.x * kWhtCols;
   const int64_t k = k0 + 2 * t;
   const int64_t m0 = (int64_t)blockIdx.y * TB;
-  wht_tile_issue<TB>(q_x, K, m0, k0, tile);
-  long long acc = 0;
-  for (int64_t i = t; i < P; i += 256) acc += part[i];
-  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if ((t & 63) == 0) wsum[t >> 6] = acc;
-  wht_tile_wait();
-  const long long S = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  const float sc = fmul(fmul((float)(double)S, inv_n), lsq_k2());  // S < 2^53: exact in double
-  const float r = (sc == 0.0f) ? 0.0f : fl_div(1.0f, sc);
-  if (s_out && blockIdx.x == 0 && blockIdx.y == 0 && t == 0) s_out[0] = sc;
+  const float r = sr[1];
+  wht_tile_load<TB>(q_x, K, m0, k0, tile);
   s16x2 u[TB];
   load_int_cols<TB>(tile, u);
   butterflies_int<TB>(u, b);
@@ -212,17 +210,16 @@ hipError_t wht_quant_x(const int8_t* q_x, int64_t M, int64_t K, int block, int8_
   dim3 g((unsigned)cdiv(K, kWhtCols), (unsigned)(M / TB)), bl(256);
   const int64_t P = (int64_t)g.x * g.y;
   long long* part = (long long*)ws;
+  float* sr = (float*)((char*)ws + align256((size_t)(P > 0 ? P : 1) * sizeof(long long)));
   const float inv_n = 1.0f / (float)(M * K);
   if (TB == 128) hipLaunchKernelGGL(k_wht_int_stats<128>, g, bl, 0, s, q_x, M, K, block, part);
   else hipLaunchKernelGGL(k_wht_int_stats<64>, g, bl, 0, s, q_x, M, K, block, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (TB == 128)
-    hipLaunchKernelGGL(k_wht_int_quant<128>, g, bl, 0, s, q_x, M, K, block, part, P, inv_n, s_u,
-                       q_ut);
-  else
-    hipLaunchKernelGGL(k_wht_int_quant<64>, g, bl, 0, s, q_x, M, K, block, part, P, inv_n, s_u,
-                       q_ut);
+  hipLaunchKernelGGL(k_wht_int_finalize, dim3(1), dim3(256), 0, s, part, P, inv_n, sr, s_u);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (TB == 128) hipLaunchKernelGGL(k_wht_int_quant<128>, g, bl, 0, s, q_x, M, K, block, sr, q_ut);
+  else hipLaunchKernelGGL(k_wht_int_quant<64>, g, bl, 0, s, q_x, M, K, block, sr, q_ut);
   return hipGetLastError();
 }
 
