@@ -149,11 +149,23 @@ __device__ __forceinline__ void flat_final_body(const float* __restrict__ psum,
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   float a[32];
   float mx = 0.0f;
+  const int64_t j0 = (int64_t)t * 32;
+  if (j0 + 32 <= P) {
+    // both arrays start 16-byte aligned: eight 16-byte loads each
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    int64_t j = (int64_t)t * 32 + i;
-    a[i] = j < P ? psum[j] : 0.0f;
-    mx = fmaxf(mx, j < P ? pmax[j] : 0.0f);
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(psum + j0 + 4 * i);
+      const float4 m = *reinterpret_cast<const float4*>(pmax + j0 + 4 * i);
+      a[4 * i] = v.x; a[4 * i + 1] = v.y; a[4 * i + 2] = v.z; a[4 * i + 3] = v.w;
+      mx = fmaxf(fmaxf(mx, fmaxf(m.x, m.y)), fmaxf(m.z, m.w));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int64_t j = j0 + i;
+      a[i] = j < P ? psum[j] : 0.0f;
+      mx = fmaxf(mx, j < P ? pmax[j] : 0.0f);
+    }
   }
   float w = wave_tree<false>(reg_tree<false, 32>(a));
   mx = wave_max(mx);
@@ -253,6 +265,9 @@ static int levels_of(int64_t n, int64_t C0, int64_t C, int64_t* P, int maxlev) {
   return L;
 }
 
+// Each level holds P sums, then P maxima from the next 16-byte boundary:
+// 4 round4(P) + 4 P <= align256(8 P) for every P, so the level's share of
+// the workspace is unchanged.
 size_t flat_reduce_ws(int64_t n, int chunk_log2) {
   int64_t P[16];
   int64_t C0 = int64_t(256) * 8 * vectors_for(chunk_log2, 8);  // conservative (bf16 chunk)
@@ -344,7 +359,7 @@ hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul,
   float* pm[16];
   for (int i = 0; i < L; ++i) {
     ps[i] = (float*)w;
-    pm[i] = ps[i] + P[i];
+    pm[i] = ps[i] + ((P[i] + 3) & ~int64_t(3));  // 16-byte aligned (fits: see flat_reduce_ws)
     w += align256(2 * sizeof(float) * (size_t)P[i]);
   }
   hipError_t e;
@@ -399,7 +414,7 @@ hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* 
   for (int y = 0; y < 2; ++y) {
     for (int i = 0; i < L; ++i) {
       lv[i].ps[y] = (float*)w;
-      lv[i].pm[y] = lv[i].ps[y] + P[i];
+      lv[i].pm[y] = lv[i].ps[y] + ((P[i] + 3) & ~int64_t(3));  // 16-byte aligned
       w += align256(2 * sizeof(float) * (size_t)P[i]);
     }
   }
