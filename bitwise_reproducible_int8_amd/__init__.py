@@ -20,7 +20,7 @@ F32, BF16, I8, I32, U8 = 0, 1, 2, 3, 4
 PER_TENSOR, PER_ROW = 0, 1
 FLAG_NONFINITE = 1
 OP_QUANTIZE, OP_QGEMM, OP_DW_WHT, OP_RMSNORM_BWD, OP_GRAD_NORM, OP_DY_BWD = 1, 2, 3, 4, 5, 6
-OP_QUANTIZE_EXACT, OP_DX_WHT, OP_DY_ROWS_WHT = 7, 8, 9
+OP_QUANTIZE_EXACT, OP_DX_WHT, OP_DY_ROWS_WHT, OP_QUANTIZE_X_WHT = 7, 8, 9, 10
 MAX_CONTRACTION = 131071
 DP_MAX_PARTS = 64
 STATIC_SCRATCH_BYTES = 4 << 20
@@ -29,7 +29,7 @@ PRIM_SQRT, PRIM_RCP, PRIM_RSQRT, PRIM_BF16_CVT, PRIM_BF16_INT = 0, 1, 2, 3, 4
 
 SYMBOLS = [
     "brq_workspace_size", "brq_quantize_lsq", "brq_quantize_lsq_exact", "brq_quantize_lsq_static",
-    "brq_quantize_lsq_rows_multi", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
+    "brq_quantize_lsq_rows_multi", "brq_quantize_x_wht", "brq_qgemm_fwd", "brq_qgemm_bwd_dx",
     "brq_qgemm_bwd_dw_wht", "brq_wht_quant_x", "brq_wht_quant_dy", "brq_qgemm_dw",
     "brq_qgemm_fwd_ex", "brq_qgemm_bwd_dx_ex",
     "brq_quantize_dy_bwd", "brq_qgemm_bwd_dx_wht", "brq_wht_quant_dy_rows", "brq_attn_fwd",
@@ -95,6 +95,9 @@ def lib():
         L.brq_quantize_lsq_static.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.brq_quantize_lsq_rows_multi.restype = i32
         L.brq_quantize_lsq_rows_multi.argtypes = [vp, i32, vp, vp]
+        L.brq_quantize_x_wht.restype = i32
+        L.brq_quantize_x_wht.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp,
+                                         vp]
         L.brq_qgemm_fwd.restype = i32
         L.brq_qgemm_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, sz, vp, vp]
         L.brq_qgemm_bwd_dx.restype = i32
@@ -326,6 +329,34 @@ def quantize_lsq_rows_multi(xs, want_t=True, flags=None, outs=None):
     _check(lib().brq_quantize_lsq_rows_multi(jobs, len(xs), _ptr(flags), _stream()),
            "quantize_lsq_rows_multi")
     return res
+
+
+def quantize_x_wht(x, block, tune=None, ws=None, flags=None, out=None):
+    """Per-tensor LSQ codes of x and the integer rotation of those codes along
+    tokens (brq_quantize_x_wht).  Returns (q_x, s_x, amax_x, q_ut, s_u), the
+    results of quantize_lsq(x) then wht_quant_x(q_x, block); ``out`` may hold
+    them preallocated (None entries allocated)."""
+    _dev(x, "x")
+    M, K = x.shape
+    q_x, s_x, amax_x, q_ut, s_u = out if out is not None else (None,) * 5
+    dev = x.device
+    q_x = torch.empty((M, K), dtype=torch.int8, device=dev) if q_x is None else q_x
+    q_ut = torch.empty((K, M), dtype=torch.int8, device=dev) if q_ut is None else q_ut
+    s_x = torch.empty(1, dtype=torch.float32, device=dev) if s_x is None else s_x
+    amax_x = torch.empty(1, dtype=torch.float32, device=dev) if amax_x is None else amax_x
+    s_u = torch.empty(1, dtype=torch.float32, device=dev) if s_u is None else s_u
+    for t, shape, dt, name in ((q_x, (M, K), torch.int8, "q_x"), (q_ut, (K, M), torch.int8, "q_ut"),
+                               (s_x, (1,), torch.float32, "s_x"), (amax_x, (1,), torch.float32, "amax_x"),
+                               (s_u, (1,), torch.float32, "s_u")):
+        _dev(t, name)
+        if tuple(t.shape) != shape or t.dtype != dt:
+            raise BrqError(f"{name}: expected {dt} {shape}, got {t.dtype} {tuple(t.shape)}")
+    need = workspace_size(OP_QUANTIZE_X_WHT, M, K, 0, block, tune=tune)
+    w = _ws(need, dev, ws)
+    _check(lib().brq_quantize_x_wht(_ptr(x), _fp_code(x), M, K, block, _ptr(q_x), _ptr(s_x),
+                                    _ptr(amax_x), _ptr(q_ut), _ptr(s_u), _ptr(w), w.numel(),
+                                    _ptr(flags), _tune(tune), _stream()), "quantize_x_wht")
+    return q_x, s_x, amax_x, q_ut, s_u
 
 
 def qgemm_fwd(q_x, s_x, q_w, s_w, tune=None, out=None, ws=None, out_dtype=torch.float32):

@@ -121,6 +121,8 @@ size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block, co
     }
     case BRQ_OP_GRAD_NORM: return kScalars + flat_reduce_ws(a, flat_chunk_log2(t));
     case BRQ_OP_DY_BWD: return dy_bwd_ws(a, b, block > 0 ? block : 1, t);
+    case BRQ_OP_QUANTIZE_X_WHT:
+      return quant_x_wht_ws(a, b, block > 0 ? block : 1, flat_chunk_log2(t));
     default: return 0;
   }
 }
@@ -337,6 +339,20 @@ int brq_wht_quant_x(const int8_t* q_x, int64_t M, int64_t K, int block, int8_t* 
   if (!aligned16(q_x) || !aligned16(q_ut)) return BRQ_E_ALIGN;
   if (!ws || ws_bytes < wht_x_ws(M, K, block)) return BRQ_E_WORKSPACE;
   return hip_status(wht_quant_x(q_x, M, K, block, q_ut, s_u, ws, as_stream(stream)));
+}
+
+int brq_quantize_x_wht(const void* x, int x_dtype, int64_t M, int64_t K, int block, int8_t* q_x,
+                       float* s_x, float* amax_x, int8_t* q_ut, float* s_u, void* ws,
+                       size_t ws_bytes, int32_t* dflags, const brq_tune* tune, void* stream) {
+  if (!fp_dtype(x_dtype)) return BRQ_E_DTYPE;
+  int st = check_dw_shape(M, 64, K, block);
+  if (st != BRQ_OK) return st;
+  if (!s_x || !s_u || (M * K > 0 && (!x || !q_x || !q_ut))) return BRQ_E_NULL;
+  if (!aligned16(x) || !aligned16(q_x) || !aligned16(q_ut)) return BRQ_E_ALIGN;
+  const int c = flat_chunk_log2(tune);
+  if (!ws || ws_bytes < quant_x_wht_ws(M, K, block, c)) return BRQ_E_WORKSPACE;
+  return hip_status(quantize_x_wht(x, x_dtype, M, K, block, q_x, s_x, amax_x, q_ut, s_u, ws, c,
+                                   dflags, as_stream(stream)));
 }
 
 int brq_wht_quant_dy(const void* dy, int dy_dtype, int64_t M, int64_t N, int block, int8_t* q_vt,

@@ -132,6 +132,12 @@ hipError_t gemm_i8(const int8_t* A, const int8_t* B, int64_t I, int64_t J,
 
 // ---- Walsh-Hadamard rotations ----------------------------------------------
 size_t wht_x_ws(int64_t M, int64_t K, int block);
+// Per-tensor LSQ codes of x and the integer rotation of those codes in one
+// call (one read of x for the codes and the rotation's statistic).
+size_t quant_x_wht_ws(int64_t M, int64_t K, int block, int chunk_log2);
+hipError_t quantize_x_wht(const void* x, int dtype, int64_t M, int64_t K, int block,
+                          int8_t* q_x, float* s_x, float* amax_x, int8_t* q_ut, float* s_u,
+                          void* ws, int chunk_log2, int32_t* dflags, hipStream_t s);
 size_t wht_dy_ws(int64_t M, int64_t N, int block, int chunk_log2);
 hipError_t wht_quant_x(const int8_t* q_x, int64_t M, int64_t K, int block,
                        int8_t* q_ut, float* s_u, void* ws, hipStream_t s);

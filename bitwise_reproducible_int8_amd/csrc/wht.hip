@@ -87,16 +87,12 @@ __device__ __forceinline__ void butterflies_int(V* u, int b) {
   }
 }
 
-// Pass 1: sum |u| per work-group (int64 partials).
+// Pass 1 on a tile already in LDS: sum |u| over the work-group's tile
+// (one int64 partial per work-group).
 template <int TB>
-__global__ __launch_bounds__(256) void k_wht_int_stats(const int8_t* __restrict__ q_x, int64_t M,
-                                                       int64_t K, int b,
-                                                       long long* __restrict__ part) {
-  __shared__ __attribute__((aligned(1024))) int8_t tile[TB * kWhtCols];
-  const int64_t k0 = (int64_t)blockIdx.x * kWhtCols;
+__device__ __forceinline__ void wht_int_stats_tile(const int8_t* tile, int64_t K, int64_t k0,
+                                                   int b, long long* __restrict__ part) {
   const int64_t k = k0 + 2 * threadIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.y * TB;
-  wht_tile_load<TB>(q_x, K, m0, k0, tile);
   int s = 0;
   if (k < K) {
     s16x2 u[TB];
@@ -117,6 +113,62 @@ __global__ __launch_bounds__(256) void k_wht_int_stats(const int8_t* __restrict_
   if (threadIdx.x == 0)
     part[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] =
         (long long)ws[0] + ws[1] + ws[2] + ws[3];
+}
+
+// Pass 1: sum |u| per work-group (int64 partials).
+template <int TB>
+__global__ __launch_bounds__(256) void k_wht_int_stats(const int8_t* __restrict__ q_x, int64_t M,
+                                                       int64_t K, int b,
+                                                       long long* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) int8_t tile[TB * kWhtCols];
+  const int64_t k0 = (int64_t)blockIdx.x * kWhtCols;
+  const int64_t m0 = (int64_t)blockIdx.y * TB;
+  wht_tile_load<TB>(q_x, K, m0, k0, tile);
+  wht_int_stats_tile<TB>(tile, K, k0, b, part);
+}
+
+// The activation codes and pass 1 in one kernel: the work-group quantises
+// its TB x 512 tile of x (the per-tensor LSQ codes, exactly as k_quant_flat
+// forms them: DAZ, fl(v * r), clamp, round half to even), writes them to
+// q_x row by row, and keeps them in LDS in the layout wht_tile_load gives,
+// so pass 1 needs no read of q_x.  Lane t quantises 16 elements of one row
+// per step (32 lanes per 512-column row segment); columns past K are zero
+// codes in LDS and are never used.  K % 16 == 0.
+template <typename T, int TB>
+__global__ __launch_bounds__(256) void k_quant_x_wht(const T* __restrict__ x, int64_t M,
+                                                     int64_t K, int b,
+                                                     const float* __restrict__ sr,
+                                                     int8_t* __restrict__ q,
+                                                     long long* __restrict__ part) {
+  constexpr int E = Elem<T>::kPerVec;
+  constexpr int NV = 16 / E;
+  __shared__ __attribute__((aligned(1024))) int8_t tile[TB * kWhtCols];
+  const int t = threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * kWhtCols;
+  const int64_t m0 = (int64_t)blockIdx.y * TB;
+  const float r = sr[1];
+#pragma unroll 4
+  for (int i = 0; i < TB * (kWhtCols / 16) / 256; ++i) {
+    const int c = i * 256 + t;
+    const int row = c / (kWhtCols / 16);
+    const int64_t col = k0 + (c % (kWhtCols / 16)) * 16;
+    uint32_t packed[4] = {0, 0, 0, 0};
+    if (col < K) {
+      const T* src = x + (m0 + row) * K + col;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float f[E];
+        Elem<T>::unpack(ld16(src + v * E), f);
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+          packed[(v * E + e) >> 2] = quant_pack4(f[e], f[e + 1], f[e + 2], f[e + 3], r);
+      }
+      st16(q + (m0 + row) * K + col, u32x4{packed[0], packed[1], packed[2], packed[3]});
+    }
+    st16(tile + (int64_t)c * 16, u32x4{packed[0], packed[1], packed[2], packed[3]});
+  }
+  __syncthreads();
+  wht_int_stats_tile<TB>(tile, K, k0, b, part);
 }
 
 // Exact total, then the LSQ step: fl(double(S)) -> fl(* inv_n) -> fl(* K2).
@@ -217,6 +269,56 @@ hipError_t wht_quant_x(const int8_t* q_x, int64_t M, int64_t K, int block, int8_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_wht_int_finalize, dim3(1), dim3(256), 0, s, part, P, inv_n, sr, s_u);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (TB == 128) hipLaunchKernelGGL(k_wht_int_quant<128>, g, bl, 0, s, q_x, M, K, block, sr, q_ut);
+  else hipLaunchKernelGGL(k_wht_int_quant<64>, g, bl, 0, s, q_x, M, K, block, sr, q_ut);
+  return hipGetLastError();
+}
+
+// The activation codes with the integer rotation of those codes, in one
+// call: the per-tensor statistic of x (tree, step size formed by the final
+// work-group), the codes and the rotation's pass 1 from one read of x
+// (k_quant_x_wht), then the rotation's step size and pass 2.  The results
+// are those of quantize_lsq (per tensor) followed by wht_quant_x on its
+// codes; the statistic pass over q_x is the read this saves.
+size_t quant_x_wht_ws(int64_t M, int64_t K, int block, int chunk_log2) {
+  return align256(flat_reduce_ws(M * K, chunk_log2) + 256) + wht_x_ws(M, K, block);
+}
+
+hipError_t quantize_x_wht(const void* x, int dtype, int64_t M, int64_t K, int block,
+                          int8_t* q_x, float* s_x, float* amax_x, int8_t* q_ut, float* s_u,
+                          void* ws, int chunk_log2, int32_t* dflags, hipStream_t s) {
+  const int64_t n = M * K;
+  char* w = (char*)ws;
+  const size_t fsz = flat_reduce_ws(n, chunk_log2);
+  float* sc = (float*)(w + fsz);  // [0] sum [1] max [2] s [3] r
+  void* wws = w + align256(fsz + 256);
+  // an empty tensor has step size 0 (no mean is taken)
+  const float inv_n = n > 0 ? 1.0f / (float)n : 0.0f;  // host binary32 division
+  const FlatFin fin{FIN_LSQ, inv_n, sc + 2, s_x, amax_x, nullptr, nullptr};
+  hipError_t e = flat_reduce(x, dtype, LEAF_ABS, nullptr, n, K > 0 ? K : 1, sc, w, chunk_log2,
+                             dflags, s, 0, &fin);
+  if (e != hipSuccess) return e;
+  if (n == 0) return wht_quant_x(q_x, M, K, block, q_ut, s_u, wws, s);
+  const int TB = block > 64 ? 128 : 64;
+  dim3 g((unsigned)cdiv(K, kWhtCols), (unsigned)(M / TB)), bl(256);
+  const int64_t P = (int64_t)g.x * g.y;
+  long long* part = (long long*)wws;
+  float* sr = (float*)((char*)wws + align256((size_t)P * sizeof(long long)));
+#define BRQ_QXW(TT, BB)                                                                       \
+  hipLaunchKernelGGL((k_quant_x_wht<TT, BB>), g, bl, 0, s, (const TT*)x, M, K, block, sc + 2, \
+                     q_x, part)
+  if (dtype == BRQ_BF16) {
+    if (TB == 128) BRQ_QXW(uint16_t, 128);
+    else BRQ_QXW(uint16_t, 64);
+  } else {
+    if (TB == 128) BRQ_QXW(float, 128);
+    else BRQ_QXW(float, 64);
+  }
+#undef BRQ_QXW
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_wht_int_finalize, dim3(1), dim3(256), 0, s, part, P,
+                     1.0f / (float)(M * K), sr, s_u);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (TB == 128) hipLaunchKernelGGL(k_wht_int_quant<128>, g, bl, 0, s, q_x, M, K, block, sr, q_ut);
   else hipLaunchKernelGGL(k_wht_int_quant<64>, g, bl, 0, s, q_x, M, K, block, sr, q_ut);

@@ -9,18 +9,21 @@ micro-batch of tokens.  One call of :meth:`LayerStep.run` enqueues, on
 torch's current stream:
 
   1. RMSNorm forward of each norm input                       (rmsnorm_fixed)
-  2. per-tensor LSQ codes of each distinct linear input        (quantize_lsq)
-  3. per-output-channel LSQ codes of each weight, plus the
-     transposed copy for the input-gradient GEMM, then the
-     forward GEMM + dequantisation                             (qgemm_fwd)
+  2. per-tensor LSQ codes of each distinct linear input, and
+     the Walsh-Hadamard rotation + requantisation of those
+     codes along tokens for the weight-gradient GEMM            (quantize_x_wht)
+  3. per-output-channel LSQ codes of every weight, plus the
+     transposed copies for the input-gradient GEMM, in one
+     call, then each forward GEMM + dequantisation             (quantize_lsq_rows_multi,
+                                                                qgemm_fwd)
   4. both backward codes of each dY in two passes over it: dY
      scaled by the weight step sizes and quantised, and dY
      rotated along tokens and quantised                       (quantize_dy_bwd)
      then the input-gradient GEMM                              (qgemm_bwd_dx)
-  5. Walsh-Hadamard rotation + requantisation of each distinct
-     activation code along tokens, then the weight-gradient
-     GEMM into the gradient arena                              (qgemm_bwd_dw_wht,
-                                                                in its stages)
+  5. the weight-gradient GEMM of each linear into the
+     gradient arena                                            (qgemm_dw: the
+                                                                stages of
+                                                                qgemm_bwd_dw_wht)
   6. RMSNorm backward of each norm into the arena              (rmsnorm_fixed)
   7. global l2 norm over the gradient arena                     (grad_norm)
   8. SHA-256 state hash of every output and gradient          (hash_state)
@@ -31,8 +34,10 @@ MI355X: the integer-ALU hash and the GEMMs then share CUs and both slow
 down.)
 
 The rotated code of an activation depends on that activation alone, so
-linears that share an input (Q/K/V, gate/up) share one rotation; the results
-are the same bits as the one-call qgemm_bwd_dw_wht per linear.
+linears that share an input (Q/K/V, gate/up) share one rotation, made with
+the activation's own codes (one read of the activation gives the codes and
+the rotation's statistic); the results are the same bits as the one-call
+qgemm_bwd_dw_wht per linear.
 
 Gradient arena: one fp32 buffer holding, in order, dW of every linear
 ([N][K] row-major each) and then dg of every norm; grad_norm reduces it as
@@ -46,11 +51,12 @@ from __future__ import annotations
 
 import torch
 
-from . import (ADAMW_WD, SPIKE_THRESHOLD, BrqError, OP_DW_WHT, OP_DY_BWD, OP_GRAD_NORM, OP_QGEMM, OP_QUANTIZE,
+from . import (ADAMW_WD, SPIKE_THRESHOLD, BrqError, OP_DW_WHT, OP_DY_BWD, OP_GRAD_NORM, OP_QGEMM,
+               OP_QUANTIZE, OP_QUANTIZE_X_WHT,
                OP_RMSNORM_BWD, adamw_bias_corrections, adamw_decide, adamw_step, grad_norm,
                hash_state, hash_state_workspace_size, qgemm_bwd_dx, qgemm_dw, qgemm_fwd,
-               quantize_dy_bwd, quantize_lsq, quantize_lsq_rows_multi, rmsnorm_fixed_bwd,
-               rmsnorm_fixed_fwd, wht_quant_x, workspace_size)
+               quantize_dy_bwd, quantize_lsq_rows_multi, quantize_x_wht, rmsnorm_fixed_bwd,
+               rmsnorm_fixed_fwd, workspace_size)
 
 
 class _NoTimer:
@@ -129,8 +135,7 @@ class LayerStep:
         # one workspace, large enough for every call (calls are stream-ordered)
         need = [workspace_size(OP_GRAD_NORM, self.arena.numel(), tune=tune)]
         for xin, t in x.items():
-            need.append(workspace_size(OP_QUANTIZE, *t.shape, tune=tune))
-            need.append(workspace_size(OP_DW_WHT, M, 64, t.shape[1], block, tune=tune))
+            need.append(workspace_size(OP_QUANTIZE_X_WHT, M, t.shape[1], 0, block, tune=tune))
         for (name, K, N, _xin) in self.linears:
             need += [workspace_size(OP_QUANTIZE, M, N, tune=tune),
                      workspace_size(OP_QGEMM, M, N, K, tune=tune),
@@ -162,10 +167,12 @@ class LayerStep:
             rmsnorm_fixed_fwd(h, g, self.eps, flags=fl, tune=tune, out=(self.ny[j], self.nrstd[j]))
             T.end("rmsnorm_fwd")
         for xin, t in self.x.items():
-            T.begin("quant_x")
-            quantize_lsq(t, tune=tune, ws=ws, flags=fl,
-                         out=(self.q_x[xin], None, self.s_x[xin], self.amax_x[xin]))
-            T.end("quant_x")
+            # the activation codes and the rotation of those codes (for dW)
+            T.begin("quant_x_wht")
+            quantize_x_wht(t, b, tune=tune, ws=ws, flags=fl,
+                           out=(self.q_x[xin], self.s_x[xin], self.amax_x[xin], self.q_ut[xin],
+                                self.s_u[xin]))
+            T.end("quant_x_wht")
         # every linear's per-channel weight steps and codes: one grouped call
         T.begin("quant_w")
         quantize_lsq_rows_multi(self.w, flags=fl, outs=self.w_outs)
@@ -184,10 +191,6 @@ class LayerStep:
             T.begin("gemm_dx")
             qgemm_bwd_dx(self.q_g[i], self.s_g[i], self.q_wt[i], tune=tune, out=self.dx[i], ws=ws)
             T.end("gemm_dx")
-        for xin in self.x:
-            T.begin("wht_x")
-            wht_quant_x(self.q_x[xin], b, tune=tune, ws=ws, out=(self.q_ut[xin], self.s_u[xin]))
-            T.end("wht_x")
         for i, (_name, _K, _N, xin) in enumerate(self.linears):
             T.begin("gemm_dw")
             qgemm_dw(self.q_vt[i], self.q_ut[xin], self.s_x[xin], self.s_u[xin], self.s_v[i], b,

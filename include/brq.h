@@ -98,7 +98,8 @@ enum brq_op {
   BRQ_OP_DY_BWD = 6,       /* a = M, b = N, block = Hadamard block */
   BRQ_OP_QUANTIZE_EXACT = 7, /* a = rows, b = cols */
   BRQ_OP_DX_WHT = 8,        /* a = M, b = N, c = K, block = Hadamard block */
-  BRQ_OP_DY_ROWS_WHT = 9    /* a = M, b = N */
+  BRQ_OP_DY_ROWS_WHT = 9,   /* a = M, b = N */
+  BRQ_OP_QUANTIZE_X_WHT = 10 /* a = M, b = K, block = Hadamard block */
 };
 size_t brq_workspace_size(int op, int64_t a, int64_t b, int64_t c, int block,
                           const struct brq_tune* tune);
@@ -124,6 +125,24 @@ int brq_quantize_lsq(const void* x, int x_dtype, int64_t rows, int64_t cols,
                      int gran, const float* col_mul, int8_t* q, int8_t* q_t,
                      float* scale, float* amax, void* ws, size_t ws_bytes,
                      int32_t* dflags, const struct brq_tune* tune, void* stream);
+
+/* ---------------------------------------------------------------------
+ * quantize_x_wht -- the per-tensor LSQ codes of an activation and the
+ * integer Walsh-Hadamard rotation of those codes along tokens with its own
+ * step, in one call (§3.1 "int8 quantization-aware training"; §3.2 "int8
+ * computation": the rotation in front of the weight-gradient GEMM).
+ * x [M][K] (BRQ_F32 or BRQ_BF16); outputs q_x [M][K] int8, s_x [1],
+ * amax_x [1] (optional), q_ut [K][M] int8 (token-contiguous), s_u [1].
+ * Every output equals brq_quantize_lsq(x, PER_TENSOR) followed by
+ * brq_wht_quant_x on its codes, bit for bit; the codes and the rotation's
+ * statistic come from one read of x.  Shapes, block and flags as those two
+ * calls (M % 64 == 0, K % 64 == 0, M % block == 0, block a power of two in
+ * [1, 128], M <= BRQ_MAX_CONTRACTION).  Workspace: BRQ_OP_QUANTIZE_X_WHT.
+ * --------------------------------------------------------------------- */
+int brq_quantize_x_wht(const void* x, int x_dtype, int64_t M, int64_t K, int block,
+                       int8_t* q_x, float* s_x, float* amax_x, int8_t* q_ut,
+                       float* s_u, void* ws, size_t ws_bytes, int32_t* dflags,
+                       const struct brq_tune* tune, void* stream);
 
 /* ---------------------------------------------------------------------
  * quantize_lsq_rows_multi -- the per-row (BRQ_PER_ROW) brq_quantize_lsq of

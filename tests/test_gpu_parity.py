@@ -379,6 +379,46 @@ def test_wht_quant_x(b):
     assert_bitwise(gsu, np.array([su], np.float32), "s_u")
 
 
+@pytest.mark.parametrize("shape,b,bf16", [((256, 192), 1, True), ((256, 192), 16, False),
+                                          ((384, 640), 64, True), ((256, 1088), 128, True),
+                                          ((512, 2048), 128, False), ((128, 64), 128, True)])
+def test_quantize_x_wht(shape, b, bf16):
+    """The activation codes and their rotation in one call equal the oracle's
+    per-tensor quantiser followed by its integer rotation, bit for bit
+    (ragged 512-column tiles, both element types, every tile height)."""
+    say("quantize_x_wht", shape, b, bf16)
+    x = syn.normal(shape, 1.0, tag=610 + b, bf16=bf16)
+    if bf16:
+        x = x.copy()
+        x.reshape(-1)[::97] = np.uint16(0x0005)  # bf16 subnormals read as zero
+    q, _, s, amax, fl = orc.quantize_lsq(x)
+    qu, su, _ = orc.wht_int_quant(q, b)
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gq, gs, gamax, gqut, gsu = brq.quantize_x_wht(to_dev(x), b, flags=flags)
+    assert_bitwise(gq, q, "q_x")
+    assert_bitwise(gs, np.array([s], np.float32).reshape(-1), "s_x")
+    assert_bitwise(gamax, np.array([amax], np.float32).reshape(-1), "amax_x")
+    assert_bitwise(gqut, np.ascontiguousarray(qu.T), "q_u^T")
+    assert_bitwise(gsu, np.array([su], np.float32), "s_u")
+    assert int(flags.item()) == fl == 0
+
+
+def test_quantize_x_wht_empty_and_flags():
+    """No tokens or no columns: both step sizes 0; a non-finite input raises
+    the flag as the per-tensor quantiser does."""
+    say("quantize_x_wht empty and flags")
+    for shape in ((0, 64), (64, 0)):
+        x = np.zeros(shape, np.float32)
+        _, gs, _, _, gsu = brq.quantize_x_wht(to_dev(x), 64)
+        assert float(gs.item()) == 0.0 and float(gsu.item()) == 0.0
+    x = np.ones((64, 64), np.float32)
+    x[5, 7] = np.inf
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    brq.quantize_x_wht(to_dev(x), 64, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 1
+
+
 def test_wht_quant_x_empty_and_wide():
     """No tokens or no columns: step size 0 as for any empty group; and a
     wide input (K = 8192; the first pass's partials are summed by every
