@@ -104,8 +104,8 @@ __device__ __forceinline__ uint32_t quant_pack4(float v0, float v1, float v2, fl
 // is l ^ s, and because binary32 addition is commutative bit for bit the
 // two partners compute the same value node(2i) + node(2i+1).
 // The first four steps use DPP (quad permutes, half-row and row mirrors,
-// valid because each group is uniform by then); the last two go through
-// ds_swizzle / bpermute.
+// valid because each group is uniform by then); the last two use one
+// cross-lane swap each (lanes_16, lanes_32).
 __device__ __forceinline__ float dpp_xor1(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
@@ -117,6 +117,26 @@ __device__ __forceinline__ float dpp_half_mirror(float v) {
 }
 __device__ __forceinline__ float dpp_mirror(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+}
+
+// Both values of the lane pair (l, l ^ 16), resp. (l, l ^ 32), in every
+// lane: v_permlane16_swap (v_permlane32_swap) of a register with itself
+// swaps its odd 16-lane rows with the even ones (its upper 32 lanes with
+// the lower), so the first result holds the value of the pair's lower lane
+// and the second that of its upper lane.  One instruction, no LDS round
+// trip.  Every lane of the wave must be active.
+struct LanePair {
+  float lo, hi;
+};
+__device__ __forceinline__ LanePair lanes_16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair lanes_32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
 template <bool kSigned>
@@ -132,8 +152,12 @@ __device__ __forceinline__ float wave_tree(float v) {
   v = tree_add<kSigned>(v, dpp_xor2(v));
   v = tree_add<kSigned>(v, dpp_half_mirror(v));
   v = tree_add<kSigned>(v, dpp_mirror(v));
-  v = tree_add<kSigned>(v, __shfl_xor(v, 16, kWave));
-  v = tree_add<kSigned>(v, __shfl_xor(v, 32, kWave));
+  // binary32 addition is commutative bit for bit: lo + hi is each lane's
+  // value plus its partner's
+  LanePair p = lanes_16(v);
+  v = tree_add<kSigned>(p.lo, p.hi);
+  p = lanes_32(v);
+  v = tree_add<kSigned>(p.lo, p.hi);
   return v;
 }
 
@@ -145,8 +169,14 @@ __device__ __forceinline__ float wave_tree_partial(float v, int w) {
   if (w >= 4) v = tree_add<kSigned>(v, dpp_xor2(v));
   if (w >= 8) v = tree_add<kSigned>(v, dpp_half_mirror(v));
   if (w >= 16) v = tree_add<kSigned>(v, dpp_mirror(v));
-  if (w >= 32) v = tree_add<kSigned>(v, __shfl_xor(v, 16, kWave));
-  if (w >= 64) v = tree_add<kSigned>(v, __shfl_xor(v, 32, kWave));
+  if (w >= 32) {
+    const LanePair p = lanes_16(v);
+    v = tree_add<kSigned>(p.lo, p.hi);
+  }
+  if (w >= 64) {
+    const LanePair p = lanes_32(v);
+    v = tree_add<kSigned>(p.lo, p.hi);
+  }
   return v;
 }
 
@@ -166,8 +196,10 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_xor2(v));
   v = fmaxf(v, dpp_half_mirror(v));
   v = fmaxf(v, dpp_mirror(v));
-  v = fmaxf(v, __shfl_xor(v, 16, kWave));
-  v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  LanePair p = lanes_16(v);
+  v = fmaxf(p.lo, p.hi);
+  p = lanes_32(v);
+  v = fmaxf(p.lo, p.hi);
   return v;
 }
 

@@ -229,8 +229,10 @@ __device__ __forceinline__ float rms_bwd_front(const float* xv, const float* dv,
   n = add(n, dpp_xor2(n));
   n = add(n, dpp_half_mirror(n));
   n = add(n, dpp_mirror(n));
-  n = add(n, __shfl_xor(n, 16, kWave));
-  n = add(n, __shfl_xor(n, 32, kWave));
+  LanePair pr = lanes_16(n);
+  n = add(pr.lo, pr.hi);
+  pr = lanes_32(n);
+  n = add(pr.lo, pr.hi);
   return n;
 }
 
