@@ -27,6 +27,9 @@
 //                 which the halves hold tokens in the order tok_after gives.
 //                 The |v| leaves go back through LDS to row order, 64 rows
 //                 at a time, to form node(6) per row and 64 columns.
+// The node(6) arrays are stored tile by tile (TileMap): a tile's 128 rows x
+// 2 nodes are one contiguous 1 KiB run, so its node stores fill whole
+// lines; the reduction reads them in the row-major order of the tree.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -171,7 +174,8 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
   __shared__ int wok[4];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t m0 = (int64_t)blockIdx.y * kRows, c0 = (int64_t)blockIdx.x * kCols;
-  const int64_t nb = N / 64;
+  // this tile's run of 128 rows x 2 nodes in the tile-by-tile node arrays
+  const int64_t tbase = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 256;
 
   // row phase: g leaves and their node(6) per 64 columns
   const int cg = t & 15, rb = t >> 4;
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
 #pragma unroll
     for (int e = 0; e < 8; ++e) mx = fmaxf(mx, f[e]);
     const float node = wave_tree_partial<false>(reg_tree<false, 8>(f), 8);
-    if ((cg & 7) == 0 && colv < N) part_g[(m0 + r) * nb + colv / 64] = node;
+    if ((cg & 7) == 0 && colv < N) part_g[tbase + 2 * r + (cg >> 3)] = node;
   }
   mx = wave_max(mx);
   if (lane == 0) {
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
     float node = reg_tree<false, 32>(a);
     node = node + dpp_xor1(node);  // non-negative leaves: no flush needed
     const int64_t cc = c0 + c32;
-    if ((t & 1) == 0 && cc < N) part_v[(m0 + kHalf * p + r) * nb + cc / 64] = node;
+    if ((t & 1) == 0 && cc < N) part_v[tbase + 2 * (kHalf * p + r) + (c32 >> 6)] = node;
     __syncthreads();
   }
 }
@@ -346,8 +350,9 @@ bool dy_fused_ok(int dtype, int64_t M, int64_t N, int block) {
 
 size_t dy_fused_ws(int64_t M, int64_t N, int chunk_log2) {
   const int64_t P = M * (N / 64);
+  const int64_t PT = tile_map_size(M, N / 64);  // tile-by-tile node arrays
   const int64_t nblk = cdiv(N, kCols) * (M / kRows);
-  return 2 * align256((size_t)(P > 0 ? P : 1) * sizeof(float)) +
+  return 2 * align256((size_t)(PT > 0 ? PT : 1) * sizeof(float)) +
          align256((size_t)(nblk > 0 ? nblk : 1) * sizeof(float)) +
          flat_reduce_pair_ws(P, chunk_log2) + 256;
 }
@@ -355,13 +360,15 @@ size_t dy_fused_ws(int64_t M, int64_t N, int chunk_log2) {
 hipError_t quantize_dy_fused(const void* dy, int64_t M, int64_t N, const float* sw, int block,
                              int8_t* q_g, float* s_g, float* amax_g, int8_t* q_vt, float* s_v,
                              void* ws, int chunk_log2, int32_t* dflags, hipStream_t s) {
-  const int64_t P = M * (N / 64);
+  const int64_t nb = N / 64;
+  const int64_t P = M * nb;
+  const int64_t PT = tile_map_size(M, nb);
   const int64_t gx = cdiv(N, kCols), gy = M / kRows;
   char* w = (char*)ws;
   float* part_g = (float*)w;
-  w += align256((size_t)P * sizeof(float));
+  w += align256((size_t)PT * sizeof(float));
   float* part_v = (float*)w;
-  w += align256((size_t)P * sizeof(float));
+  w += align256((size_t)PT * sizeof(float));
   float* bmax = (float*)w;
   w += align256((size_t)(gx * gy) * sizeof(float));
   void* fws = w;
@@ -376,8 +383,12 @@ hipError_t quantize_dy_fused(const void* dy, int64_t M, int64_t N, const float* 
   // final work-groups
   const float inv_n = 1.0f / (float)(M * N);  // host binary32 division, correctly rounded
   const PairFin fin{1, inv_n, sc + 4, s_g, s_v, amax_g, bmax, gx * gy};
-  if ((e = flat_reduce_pair(part_g, part_v, P, sc, sc + 2, fws, chunk_log2, dflags, s, &fin)) !=
-      hipSuccess)
+  int lognb = -1;
+  if ((nb & (nb - 1)) == 0)
+    for (lognb = 0; (int64_t(1) << lognb) < nb;) ++lognb;
+  const TileMap tm{nb, gx, lognb};
+  if ((e = flat_reduce_pair(part_g, part_v, P, sc, sc + 2, fws, chunk_log2, dflags, s, &fin,
+                            &tm)) != hipSuccess)
     return e;
   hipLaunchKernelGGL(k_dy_codes, g, b, 0, s, (const uint16_t*)dy, sw, M, N, block, sc + 4, q_g,
                      q_vt);

@@ -50,6 +50,20 @@ hipError_t flat_reduce(const void* x, int dtype, int leaf, const float* col_mul,
 // Two raw fp32 leaf arrays of equal length n reduced as two flat_reduce
 // calls would, in one launch per level; workspace flat_reduce_pair_ws.
 size_t flat_reduce_pair_ws(int64_t n, int chunk_log2);
+// Storage of a leaf array kept tile by tile: leaf i = (row, c) of a
+// row-major [rows][nb] array (row = i / nb, c = i % nb) sits at
+// ((row / 128) gx + c / 2) 256 + (row % 128) 2 + c % 2, i.e. each 128-row x
+// 2-column tile is one contiguous run of 256 values.  The tree is still the
+// one over the row-major order.  lognb = log2(nb) when nb is a power of
+// two, else -1.
+struct TileMap {
+  int64_t nb;
+  int64_t gx;
+  int lognb;
+};
+inline int64_t tile_map_size(int64_t rows, int64_t nb) {
+  return ((rows + 127) / 128) * ((nb + 1) / 2) * 256;
+}
 // fin (optional): both LSQ steps from the two sums -- sr4 = {s0, r0, s1, r1},
 // s0/s1 copies -- and amax0 = the max over bmax[0 .. nb) (order-free), run
 // by the two final work-groups.
@@ -63,9 +77,11 @@ struct PairFin {
   const float* bmax;
   int64_t nb;
 };
+// tm (optional): both leaf arrays are stored tile by tile (TileMap).
 hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* out0,
                             float* out1, void* ws, int chunk_log2, int32_t* dflags,
-                            hipStream_t s, const PairFin* fin = nullptr);
+                            hipStream_t s, const PairFin* fin = nullptr,
+                            const TileMap* tm = nullptr);
 
 // Optimizer step (optim.hip).
 hipError_t adamw_decide(const float* norm, float max_norm, float spike, int skip_steps,

@@ -77,11 +77,39 @@ __device__ __forceinline__ void leaves_of(const T* x, const float* cm, int64_t n
   }
 }
 
-template <typename T, int LEAF, int V, int B = 0>
+// Raw fp32 leaves idx0 .. idx0 + 3 of an array stored tile by tile
+// (TileMap); leaves past n are 0.  Two leaves (row, c), (row, c + 1) with c
+// even sit side by side, so when nb is an even power of two (idx0 % 4 == 0,
+// the four leaves in one row) two 8-byte loads fetch them.
+__device__ __forceinline__ int64_t tile_index(int64_t i, const TileMap& m) {
+  int64_t row, c;
+  if (m.lognb >= 0) {
+    row = i >> m.lognb;
+    c = i & (m.nb - 1);
+  } else {
+    row = i / m.nb;
+    c = i - row * m.nb;
+  }
+  return (((row >> 7) * m.gx + (c >> 1)) << 8) + ((row & 127) << 1) + (c & 1);
+}
+__device__ __forceinline__ void leaves_tiled(const float* x, int64_t n, const TileMap& m,
+                                             int64_t idx0, float* f) {
+  if (m.lognb >= 2 && idx0 + 4 <= n) {
+    const float2 a = *reinterpret_cast<const float2*>(x + tile_index(idx0, m));
+    const float2 b = *reinterpret_cast<const float2*>(x + tile_index(idx0 + 2, m));
+    f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = idx0 + e < n ? x[tile_index(idx0 + e, m)] : 0.0f;
+  }
+}
+
+template <typename T, int LEAF, int V, int B = 0, bool TILED = false>
 __device__ __forceinline__ void flat_leaves_body(const T* __restrict__ x,
                                                  const float* __restrict__ cm, int64_t n,
                                                  int64_t cols, float* __restrict__ psum,
-                                                 float* __restrict__ pmax) {
+                                                 float* __restrict__ pmax,
+                                                 const TileMap tm = TileMap{0, 0, -1}) {
   constexpr int E = Elem<T>::kPerVec;
   constexpr int64_t WAVE_SPAN = int64_t(64) * E * V;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -91,7 +119,11 @@ __device__ __forceinline__ void flat_leaves_body(const T* __restrict__ x,
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     float f[E];
-    leaves_of<T, LEAF, B>(x, cm, n, cols, base + (int64_t)(v * 64 + lane) * E, f);
+    if constexpr (TILED)
+      leaves_tiled(reinterpret_cast<const float*>(x), n, tm, base + (int64_t)(v * 64 + lane) * E,
+                   f);
+    else
+      leaves_of<T, LEAF, B>(x, cm, n, cols, base + (int64_t)(v * 64 + lane) * E, f);
 #pragma unroll
     for (int e = 0; e < E; ++e) mx = fmaxf(mx, f[e]);
     node[v] = wave_tree<false>(reg_tree<false, E>(f));
@@ -138,6 +170,12 @@ template <int V>
 __global__ __launch_bounds__(256) void k_flat_leaves_pair(FlatPair a, int64_t n) {
   const int y = blockIdx.y;
   flat_leaves_body<float, LEAF_RAW, V>(a.x[y], nullptr, n, 1, a.ps[y], a.pm[y]);
+}
+// the same over two arrays stored tile by tile
+template <int V>
+__global__ __launch_bounds__(256) void k_flat_leaves_pair_tiled(FlatPair a, int64_t n, TileMap tm) {
+  const int y = blockIdx.y;
+  flat_leaves_body<float, LEAF_RAW, V, 0, true>(a.x[y], nullptr, n, 1, a.ps[y], a.pm[y], tm);
 }
 
 // Final level: up to 32768 partials in one work-group of 1024 lanes, each
@@ -403,7 +441,7 @@ size_t flat_reduce_pair_ws(int64_t n, int chunk_log2) { return 2 * flat_reduce_w
 // flat_reduce calls would (same chunks, same tree), in one launch per level.
 hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* out0,
                             float* out1, void* ws, int chunk_log2, int32_t* dflags,
-                            hipStream_t s, const PairFin* fin) {
+                            hipStream_t s, const PairFin* fin, const TileMap* tm) {
   const int V = vectors_for(chunk_log2, 4);
   const int64_t C0 = int64_t(256) * 4 * V;
   const int Vr = 16;
@@ -435,7 +473,20 @@ hipError_t flat_reduce_pair(const float* x0, const float* x1, int64_t n, float* 
     }
     return hipGetLastError();
   };
-  hipError_t e = leaves(0, V, n);
+  hipError_t e;
+  if (tm) {
+    dim3 g((unsigned)P[0], 2), b(256);
+    switch (V) {
+      case 1: hipLaunchKernelGGL((k_flat_leaves_pair_tiled<1>), g, b, 0, s, lv[0], n, *tm); break;
+      case 2: hipLaunchKernelGGL((k_flat_leaves_pair_tiled<2>), g, b, 0, s, lv[0], n, *tm); break;
+      case 4: hipLaunchKernelGGL((k_flat_leaves_pair_tiled<4>), g, b, 0, s, lv[0], n, *tm); break;
+      case 8: hipLaunchKernelGGL((k_flat_leaves_pair_tiled<8>), g, b, 0, s, lv[0], n, *tm); break;
+      default: hipLaunchKernelGGL((k_flat_leaves_pair_tiled<16>), g, b, 0, s, lv[0], n, *tm); break;
+    }
+    e = hipGetLastError();
+  } else {
+    e = leaves(0, V, n);
+  }
   if (e != hipSuccess) return e;
   for (int i = 1; i < L; ++i) {
     if ((e = leaves(i, Vr, P[i - 1])) != hipSuccess) return e;
