@@ -512,7 +512,10 @@ int rmsnorm_bwd_rows(int64_t D, int dtype, const brq_tune* t) {
   int64_t per = cdiv(D, 256 * E);
   int V = 1;
   while (V < per) V *= 2;
-  int R = (t && t->rows_per_block) ? t->rows_per_block : 32 / V;
+  // default: 8 rows per block for one vector per lane (the 2048-wide bf16
+  // rows measured fastest there, 4% ahead of 32 with its one fold level
+  // fewer), else 32 / V
+  int R = (t && t->rows_per_block) ? t->rows_per_block : (V == 1 ? 8 : 32 / V);
   int cap = 32 / V;
   if (R > cap) R = cap;
   int r = 1;

@@ -91,10 +91,10 @@ def test_qkv_full(brq):
 # benchmark's default plan, the 8-wave direct-to-LDS GEMM with the
 # contraction split in two (exact int32 partials) and the smallest
 # reduction chunk, and the persistent GEMM split in two with the largest
-# chunk; RMSNorm backward at 4 and 8 rows per block.
+# chunk; RMSNorm backward at 4 and 32 rows per block (the default is 8).
 FULL_TUNES = [None,
               dict(gemm_kernel=10, split_k=2, chunk_log2=10, rows_per_block=4),
-              dict(gemm_kernel=13, split_k=2, chunk_log2=16, rows_per_block=8)]
+              dict(gemm_kernel=13, split_k=2, chunk_log2=16, rows_per_block=32)]
 
 
 def _tid(t):
