@@ -109,10 +109,12 @@ __global__ __launch_bounds__(256) void k_gemm_ref(const int8_t* __restrict__ A,
 // contraction terms.  Result: lane l holds rows 4*(l>>4)+r, column l&15.
 // --------------------------------------------------------------------------
 template <int BK>
+__device__ __forceinline__ int lds_swz(int row) {
+  return BK / 16 == 8 ? ((row ^ (row >> 3)) & 7) : (((row >> 1) ^ (row >> 2)) & 3);
+}
+template <int BK>
 __device__ __forceinline__ int lds_off(int row, int kc) {
-  constexpr int CH = BK / 16;
-  const int f = CH == 8 ? ((row ^ (row >> 3)) & 7) : (((row >> 1) ^ (row >> 2)) & 3);
-  return row * BK + ((kc ^ f) << 4);
+  return row * BK + ((kc ^ lds_swz<BK>(row)) << 4);
 }
 
 template <int BM, int BN, int WGM, int WGN, int BK>
@@ -233,7 +235,9 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
 // instruction's LDS base + 16 * lane), through kStages LDS stages, with the
 // loads for contraction step t + kStages - 1 issued while step t is
 // multiplied -- so each load has kStages - 1 steps of MFMA work to arrive.
-// BK = 64 bytes (4 chunks of 16 per operand row).  The XOR-swizzled LDS
+// BK = 64 bytes (4 chunks of 16 per operand row) through 4 stages, or
+// BK = 128 (8 chunks: every load request covers a whole 128-byte line, two
+// MFMA sub-steps per step) through 2 stages of 64 KiB.  The XOR-swizzled LDS
 // layout of the register-staged kernel is kept: since a lane's LDS slot is
 // fixed by its lane number, each lane picks the global chunk that belongs in
 // its slot.  Rows past the matrix edge read a clamped (valid) row; they only
@@ -444,11 +448,12 @@ __device__ __forceinline__ void store_tile_full(const v4i (&acc)[BM / WGM / 16][
   }
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int BK = 64, int NS = kStages>
 __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t I, int64_t J,
     int64_t Kc, float* __restrict__ C, int* __restrict__ Cpart, int ktiles_per_split, Epi epi) {
-  constexpr int BK = 64, CH = BK / 16;
+  static_assert((BK == 64 && NS >= 2) || (BK == 128 && NS == 2), "step and stages");
+  constexpr int CH = BK / 16;
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TI = WM / 16, TJ = WN / 16;
@@ -456,8 +461,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
   constexpr int L = DA + DB;
   static_assert(DA * 64 * NW == BM * CH && DB * 64 * NW == BN * CH, "tile/waves");
   constexpr int STAGE = (BM + BN) * BK;
-  static_assert(WGM * 16 * BN * 4 <= kStages * STAGE, "epilogue staging fits the stages");
-  __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * STAGE];
+  static_assert(WGM * 16 * BN * 4 <= NS * STAGE, "epilogue staging fits the stages");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
 #pragma unroll
   for (int i = 0; i < DA; ++i) {
     const int sg = (wave * DA + i) * 64 + lane, r = sg / CH;
-    const int f = ((r >> 1) ^ (r >> 2)) & 3;
+    const int f = lds_swz<BK>(r);
     int64_t gr = row0 + r;
     gr = gr < I ? gr : I - 1;
     srcA[i] = A + gr * Kc + (int64_t)(((sg % CH) ^ f) * 16) + kt0 * BK;
@@ -488,13 +493,13 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
 #pragma unroll
   for (int i = 0; i < DB; ++i) {
     const int sg = (wave * DB + i) * 64 + lane, r = sg / CH;
-    const int f = ((r >> 1) ^ (r >> 2)) & 3;
+    const int f = lds_swz<BK>(r);
     int64_t gr = col0 + r;
     gr = gr < J ? gr : J - 1;
     srcB[i] = B + gr * Kc + (int64_t)(((sg % CH) ^ f) * 16) + kt0 * BK;
   }
   auto issue = [&](int64_t it) {
-    int8_t* st = smem + (it % kStages) * STAGE;
+    int8_t* st = smem + (it % NS) * STAGE;
 #pragma unroll
     for (int i = 0; i < DA; ++i)
       __builtin_amdgcn_global_load_lds(
@@ -515,49 +520,83 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
+  for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s);
 
   const int kc = lane >> 4;
 #pragma unroll 1
   for (int64_t it = 0; it < nk; ++it) {
-    // loads still allowed in flight: those of the (up to kStages - 2) later
+    // loads still allowed in flight: those of the (up to NS - 2) later
     // steps already issued
     const int64_t later = nk - 1 - it;
-    if (later >= 2) wait_vmcnt<2 * L>();
-    else if (later == 1) wait_vmcnt<L>();
+    if (NS >= 4 && later >= 2) wait_vmcnt<(NS >= 4 ? 2 : 0) * L>();
+    else if (NS >= 3 && later >= 1) wait_vmcnt<(NS >= 3 ? 1 : 0) * L>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    const int8_t* st = smem + (it % kStages) * STAGE;
-    v4i af[TI], bf[TJ];
+    const int8_t* st = smem + (it % NS) * STAGE;
+    if constexpr (BK == 64) {
+      v4i af[TI], bf[TJ];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int r = wm * WM + i * 16 + (lane & 15);
-      af[i] = *reinterpret_cast<const v4i*>(st + lds_off<BK>(r, kc));
+      for (int i = 0; i < TI; ++i) {
+        const int r = wm * WM + i * 16 + (lane & 15);
+        af[i] = *reinterpret_cast<const v4i*>(st + lds_off<BK>(r, kc));
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int r = wn * WN + j * 16 + (lane & 15);
+        bf[j] = *reinterpret_cast<const v4i*>(st + BM * BK + lds_off<BK>(r, kc));
+      }
+      constexpr int IA = kIssueAfter < TI ? kIssueAfter : TI;
+#pragma unroll
+      for (int i = 0; i < IA; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + NS - 1 < nk) issue(it + NS - 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = IA; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+      asm volatile("" ::: "memory");
+    } else {
+      // two MFMA sub-steps per 128-byte step; the next loads go out after the
+      // first one's leading row groups
+#pragma unroll
+      for (int kh = 0; kh < BK / 64; ++kh) {
+        v4i af[TI], bf[TJ];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const int r = wm * WM + i * 16 + (lane & 15);
+          af[i] = *reinterpret_cast<const v4i*>(st + lds_off<BK>(r, 4 * kh + kc));
+        }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int r = wn * WN + j * 16 + (lane & 15);
+          bf[j] = *reinterpret_cast<const v4i*>(st + BM * BK + lds_off<BK>(r, 4 * kh + kc));
+        }
+        constexpr int IA = kIssueAfter < TI ? kIssueAfter : TI;
+#pragma unroll
+        for (int i = 0; i < IA; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kh == 0 && it + NS - 1 < nk) issue(it + NS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = IA; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        asm volatile("" ::: "memory");
+      }
     }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int r = wn * WN + j * 16 + (lane & 15);
-      bf[j] = *reinterpret_cast<const v4i*>(st + BM * BK + lds_off<BK>(r, kc));
-    }
-    constexpr int IA = kIssueAfter < TI ? kIssueAfter : TI;
-#pragma unroll
-    for (int i = 0; i < IA; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (it + kStages - 1 < nk) issue(it + kStages - 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = IA; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    asm volatile("" ::: "memory");
   }
 
   // every load has landed (the last step waited for all); the barrier
@@ -888,6 +927,10 @@ static Plan plan_of(int64_t I, int64_t J, int64_t Kc, const brq_tune* t) {
     const int64_t steps = Kc / 64 / s;
     if (tiles * s > cu_count() && steps >= kStages && steps < 64 && (Kc / 64) % s == 0)
       p.kern = 13;
+    // one tile per work-group over a long contraction (the weight-gradient
+    // GEMMs of the wide linears): 128-byte steps, whole-line load requests
+    else if (s == 1 && tiles <= cu_count() && Kc >= 8192 && Kc % 128 == 0)
+      p.kern = 14;
   }
   if (p.kern == 1) p.splits = 1;
   return p;
@@ -911,15 +954,15 @@ static hipError_t launch_mfma(const int8_t* A, const int8_t* B, int64_t I, int64
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int BK = 64, int NS = kStages>
 static hipError_t launch_dma(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64_t Kc,
                              float* C, int* Cpart, int splits, Epi epi, hipStream_t s) {
   const int64_t tiles = cdiv(I, BM) * cdiv(J, BN);
-  const int64_t nk = Kc / 64;
+  const int64_t nk = Kc / BK;
   const int kps = (int)cdiv(nk, splits);
   dim3 g((unsigned)tiles, 1, (unsigned)splits), b(WGM * WGN * 64);
-  hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN>), g, b, 0, s, A, B, I, J, Kc, C, Cpart, kps,
-                     epi);
+  hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, BK, NS>), g, b, 0, s, A, B, I, J, Kc, C, Cpart,
+                     kps, epi);
   return hipGetLastError();
 }
 
@@ -959,13 +1002,16 @@ hipError_t gemm_i8(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64
     part = (int*)ws;
   }
   hipError_t e;
-  // the direct-to-LDS kernels need whole 64-byte contraction chunks
+  // the direct-to-LDS kernels need whole 64-byte (kernel 14: 128-byte)
+  // contraction chunks
+  if (kern == 14 && Kc % 128) kern = 10;
   if (kern >= 9 && kern <= 13 && Kc % 64) kern = 2;
   switch (kern) {
     case 9: e = launch_dma<256, 256, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
     case 10: e = launch_dma<256, 256, 2, 4>(A, B, I, J, Kc, C, part, splits, epi, s); break;
     case 11: e = launch_dma<128, 256, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
     case 12: e = launch_dma<128, 128, 2, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
+    case 14: e = launch_dma<256, 256, 2, 4, 128, 2>(A, B, I, J, Kc, C, part, splits, epi, s); break;
     case 13:
       // every unit must hold at least kStages contraction steps
       if (Kc / 64 / splits >= kStages && (Kc / 64) % splits == 0)

@@ -79,7 +79,9 @@ typedef struct brq_tune {
                         per CU walks its tiles with the load pipeline
                         running across tile boundaries (10 is used when a
                         tile's contraction slice has fewer than 4 steps of
-                        64 or the slices are unequal) */
+                        64 or the slices are unequal), 14 256x256 (8 waves)
+                        with 128-byte contraction steps through 2 stages
+                        (contraction a multiple of 128, else 10 is used) */
   int split_k;       /* 0 default (by shape), else 1, 2, 4, 8 or 16
                         contraction slices (exact int32 partials) */
   int chunk_log2;    /* 0 default (13), else log2 of the leaves each

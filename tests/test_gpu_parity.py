@@ -245,7 +245,7 @@ GEMM_TUNES = [dict(gemm_kernel=k, split_k=s) for k, s in
               [(1, 1), (2, 1), (3, 1), (4, 1), (2, 2), (2, 4), (3, 2), (4, 4),
                (5, 1), (6, 1), (7, 1), (8, 1), (7, 2), (5, 4), (0, 0),
                (9, 1), (10, 1), (11, 1), (12, 1), (10, 2), (12, 4), (10, 16), (0, 8),
-               (13, 1), (13, 2), (13, 4)]]
+               (13, 1), (13, 2), (13, 4), (14, 1), (14, 2), (14, 4)]]
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 2048), (128, 512, 16),
