@@ -102,8 +102,14 @@ __device__ __forceinline__ bool steps_ok(const float* s8) {
 // rounded to binary32, whose ulp is then at least 2^-109 -- is a multiple of
 // 2^-110 and never subnormal: the flushes are no-ops and DAZ has nothing to
 // clear.  A wave holding a smaller nonzero input takes the flushing path.
-template <bool kFlush>
+//
+// BC > 0 fixes the block at compile time: every stage then runs
+// unconditionally and the compiler renames registers from stage to stage,
+// where a run-time block keeps the values in place across the optional
+// stages at the cost of a register move per butterfly.
+template <bool kFlush, int BC = 0>
 __device__ __forceinline__ void butterflies(float* v, int b) {
+  if (BC) b = BC;
 #pragma unroll
   for (int h = 1; h < kHalf; h *= 2) {
     if (h < b) {
@@ -157,6 +163,8 @@ __device__ __forceinline__ void column_wht(const uint8_t* lds, int col, int half
 #pragma unroll
     for (int r = 0; r < kHalf; ++r) v[r] = flush(v[r]);
     butterflies<true>(v, b);
+  } else if (b == kRows) {
+    butterflies<false, kRows>(v, b);
   } else {
     butterflies<false>(v, b);
   }
