@@ -238,9 +238,10 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
   float v[kHalf];
   column_wht(lds, ccol, half, b, tile_ok, v);
   __syncthreads();  // every column read: the tile memory is reused below
-  // |v| to row order, 64 rows at a time: the half-p lanes write their 64
-  // tokens, then lane t reads row t >> 2, columns 32 (t & 3) .. +31, and
-  // the lane pairs (t, t ^ 1) join their 32-column nodes into node(6)
+  // v to row order, 64 rows at a time: the half-p lanes write their 64
+  // tokens, then lane t reads row t >> 2, columns 32 (t & 3) .. +31, takes
+  // |v| as the abs modifiers of the tree's first adds, and the lane pairs
+  // (t, t ^ 1) join their 32-column nodes into node(6)
   float* tr = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -249,20 +250,21 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
 #pragma unroll
       for (int j = 0; j < kHalf / 2; ++j)
         tr[(tok_after(b, half, (kHalf / 2) * p + j) - kHalf * p) * kTrStride + ccol] =
-            fabs_bits(v[(kHalf / 2) * p + j]);
+            v[(kHalf / 2) * p + j];
     } else if (half == p) {
 #pragma unroll
-      for (int i = 0; i < kHalf; ++i) tr[i * kTrStride + ccol] = fabs_bits(v[i]);
+      for (int i = 0; i < kHalf; ++i) tr[i * kTrStride + ccol] = v[i];
     }
     __syncthreads();
     const int r = t >> 2, c32 = (t & 3) * 32;
-    float a[32];
+    float a[16];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const float4 x4 = *reinterpret_cast<const float4*>(&tr[r * kTrStride + c32 + 4 * q]);
-      a[4 * q] = x4.x; a[4 * q + 1] = x4.y; a[4 * q + 2] = x4.z; a[4 * q + 3] = x4.w;
+      a[2 * q] = fabsf(x4.x) + fabsf(x4.y);
+      a[2 * q + 1] = fabsf(x4.z) + fabsf(x4.w);
     }
-    float node = reg_tree<false, 32>(a);
+    float node = reg_tree<false, 16>(a);
     node = node + dpp_xor1(node);  // non-negative leaves: no flush needed
     const int64_t cc = c0 + c32;
     if ((t & 1) == 0 && cc < N) part_v[tbase + 2 * (kHalf * p + r) + (c32 >> 6)] = node;
