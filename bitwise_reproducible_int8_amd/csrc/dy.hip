@@ -150,9 +150,14 @@ __device__ __forceinline__ int tok_after(int b, int h, int i) {
 }
 
 // tile_ok: the row phase found every nonzero value of the tile >= 2^-103
-// (uniform over the work-group).
+// (uniform over the work-group).  tail(v) runs the rest of the kernel on
+// the rotated values inside each of the three forms, so their results
+// never meet in one set of registers (a join would cost a register copy
+// per value).
+template <class Tail>
 __device__ __forceinline__ void column_wht(const uint8_t* lds, int col, int half, int b,
-                                           bool tile_ok, float* v) {
+                                           bool tile_ok, Tail&& tail) {
+  float v[kHalf];
 #pragma unroll
   for (int r = 0; r < kHalf; ++r) {
     const uint32_t h =
@@ -163,10 +168,13 @@ __device__ __forceinline__ void column_wht(const uint8_t* lds, int col, int half
 #pragma unroll
     for (int r = 0; r < kHalf; ++r) v[r] = flush(v[r]);
     butterflies<true>(v, b);
+    tail(v);
   } else if (b == kRows) {
     butterflies<false, kRows>(v, b);
+    tail(v);
   } else {
     butterflies<false>(v, b);
+    tail(v);
   }
 }
 
@@ -235,8 +243,7 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
 
   // column phase
   const int ccol = 32 * wave + (lane & 31), half = lane >> 5;
-  float v[kHalf];
-  column_wht(lds, ccol, half, b, tile_ok, v);
+  column_wht(lds, ccol, half, b, tile_ok, [&](const float* v) {
   __syncthreads();  // every column read: the tile memory is reused below
   // v to row order, 64 rows at a time: the half-p lanes write their 64
   // tokens, then lane t reads row t >> 2, columns 32 (t & 3) .. +31, takes
@@ -270,6 +277,7 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
     if ((t & 1) == 0 && cc < N) part_v[tbase + 2 * (kHalf * p + r) + (c32 >> 6)] = node;
     __syncthreads();
   }
+  });
 }
 
 __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ dy,
@@ -324,8 +332,7 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
   __syncthreads();
   const bool tile_ok = wok[0] && wok[1] && wok[2] && wok[3];
   const int ccol = 32 * wave + (lane & 31), half = lane >> 5;
-  float v[kHalf];
-  column_wht(lds, ccol, half, b, tile_ok, v);
+  column_wht(lds, ccol, half, b, tile_ok, [&](const float* v) {
   // The codes go through LDS as [column][token] (after the barrier no lane
   // reads the bf16 tile any more), so that each store instruction writes
   // whole 128-token runs of 8 columns instead of 16-byte pieces of 64.
@@ -349,6 +356,7 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
     if (c0 + c < N)
       st16(q_vt + (c0 + c) * M + m0 + ch, *reinterpret_cast<const u32x4*>(lds + c * kCodeStride + ch));
   }
+  });
 }
 
 }  // namespace
