@@ -79,9 +79,14 @@ __device__ __forceinline__ void butterflies_int(V* u, int b) {
 #pragma unroll
       for (int j = 0; j < TB; ++j) {
         if (j & h) continue;
-        V a = u[j], c = u[j + h];
-        u[j] = a + c;
-        u[j + h] = a - c;
+        // in place, two instructions and no temporary: s = a + c, then
+        // a - c as c * -2 + s (v_pk_mad_i16; every value and partial sum
+        // fits 16 bits, so the wrapped product sum is the exact difference)
+        const V sum = u[j] + u[j + h];
+        V dif;
+        asm("v_pk_mad_i16 %0, %1, %2, %3" : "=v"(dif) : "v"(u[j + h]), "v"(0xfffefffeu), "v"(sum));
+        u[j] = sum;
+        u[j + h] = dif;
       }
     }
   }
