@@ -41,6 +41,30 @@ __device__ __forceinline__ u32x4 pack_out<float>(const float* y) {
                __float_as_uint(y[3])};
 }
 
+// DAZ of 8 bf16 values (two per 32-bit word: a half whose exponent field is
+// zero keeps only its sign), their exact widening to binary32, and the
+// biased exponent of the smallest nonzero value (512 when all are zero).
+// Packed 16-bit operations: per word one mask, two for the DAZ, two for the
+// exponent minimum.
+__device__ __forceinline__ int widen_bf16x8_daz(u32x4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  u16x2_t emin = {0xffff, 0xffff};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t u = bf16x2_daz(w[i]);
+    f[2 * i] = __uint_as_float(u << 16);
+    f[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
+    // (E - 1) << 7 for E >= 1; a zero exponent wraps to 0xff80
+    const u16x2_t th = __builtin_bit_cast(u16x2_t, w[i] & 0x7f807f80u);
+    emin = __builtin_elementwise_min(emin, th - u16x2_t{0x80, 0x80});
+  }
+  const uint32_t lo = emin.x, hi = emin.y;
+  return (int)((lo < hi ? lo : hi) >> 7) + 1;
+}
+
+// biased exponent of a binary32 value's magnitude
+__device__ __forceinline__ int f32_exp(float v) { return (int)((__float_as_uint(v) >> 23) & 0xffu); }
+
 // ---- forward: one wave per row, 4 rows per work-group ------------------------
 template <typename T, int V>
 __global__ __launch_bounds__(256) void k_rms_fwd(const T* __restrict__ x, const T* __restrict__ g,
@@ -52,35 +76,61 @@ __global__ __launch_bounds__(256) void k_rms_fwd(const T* __restrict__ x, const 
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= Tn) return;
   const T* xr = x + row * D;
-  u32x4 raw[V];
-  float node[V];
+  // bf16 rows skip the flushes where exponent bounds prove them identities
+  // (the argument of the backward's unflushed form): with Ex the biased
+  // exponent of the wave's smallest nonzero x (after DAZ), every square is
+  // at least 2^(2 Ex - 254), normal when Ex >= 64; with Er of rstd and Eg
+  // of the lane's smallest nonzero g, x r >= 2^(Ex + Er - 254) and
+  // (x r) g >= 2^(Ex + Er + Eg - 381), normal when Ex + Er >= 128 and
+  // Ex + Er + Eg >= 255.  Sums of normal non-negative squares are never
+  // subnormal.
+  constexpr bool kSpec = E == 8;
+  float f[V][E];
+  int ex = 512;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int64_t c0 = (int64_t)(v * 64 + lane) * E;
-    raw[v] = c0 < D ? ld16(xr + c0) : u32x4{0, 0, 0, 0};
-    float f[E];
-    Elem<T>::unpack(raw[v], f);
+    const u32x4 raw = c0 < D ? ld16(xr + c0) : u32x4{0, 0, 0, 0};
+    if constexpr (kSpec) {
+      const int e = widen_bf16x8_daz(raw, f[v]);
+      ex = e < ex ? e : ex;
+    } else {
+      Elem<T>::unpack(raw, f[v]);
+    }
+  }
+  const bool sq_fast = kSpec && __ballot(ex < 64) == 0;
+  float node[V];
 #pragma unroll
-    for (int e = 0; e < E; ++e) f[e] = flush_nonneg(f[e] * f[e]);
-    node[v] = wave_tree<false>(reg_tree<false, E>(f));
+  for (int v = 0; v < V; ++v) {
+    float sq[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) sq[e] = sq_fast ? f[v][e] * f[v][e] : flush_nonneg(f[v][e] * f[v][e]);
+    node[v] = wave_tree<false>(reg_tree<false, E>(sq));
   }
   const float ss = reg_tree<false, V>(node);
   const float ms = fmul(ss, invD);
   const float r = fl_div(1.0f, fl_sqrt(fadd(ms, eps)));
+  const int er = f32_exp(r);
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int64_t c0 = (int64_t)(v * 64 + lane) * E;
-    if (c0 >= D) continue;
-    float f[E], gv[E], o[E];
-    Elem<T>::unpack(raw[v], f);
-    Elem<T>::unpack(ld16(g + c0), gv);
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmul(fmul(f[e], r), gv[e]);
-    if (E == 8) {
-      st16(y + row * D + c0, pack_out<T>(o));
+    float gv[E], o[E];
+    bool fast = false;
+    const u32x4 graw = c0 < D ? ld16(g + c0) : u32x4{0, 0, 0, 0};
+    if constexpr (kSpec) {
+      const int eg = widen_bf16x8_daz(graw, gv);
+      fast = __ballot(c0 < D && (ex + er < 128 || ex + er + eg < 255)) == 0;
     } else {
-      st16(y + row * D + c0, pack_out<T>(o));
+      Elem<T>::unpack(graw, gv);
     }
+    if (fast) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = (f[v][e] * r) * gv[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = fmul(fmul(f[v][e], r), gv[e]);
+    }
+    if (c0 < D) st16(y + row * D + c0, pack_out<T>(o));
   }
   if (lane == 0) {
     rstd[row] = r;
@@ -176,30 +226,6 @@ constexpr int kRmsStages = 4;
 // see a subnormal.  The last product dx = rstd (d - x^ mu) can still be
 // subnormal: it is checked (one v_cmp_class per value) and flushed when any
 // is.  A wave where a condition fails takes the flushed form.
-
-// DAZ of 8 bf16 values (two per 32-bit word: a half whose exponent field is
-// zero keeps only its sign), their exact widening to binary32, and the
-// biased exponent of the smallest nonzero value (512 when all are zero).
-// Packed 16-bit operations: per word one mask, two for the DAZ, two for the
-// exponent minimum.
-__device__ __forceinline__ int widen_bf16x8_daz(u32x4 v, float* f) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  u16x2_t emin = {0xffff, 0xffff};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t u = bf16x2_daz(w[i]);
-    f[2 * i] = __uint_as_float(u << 16);
-    f[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
-    // (E - 1) << 7 for E >= 1; a zero exponent wraps to 0xff80
-    const u16x2_t th = __builtin_bit_cast(u16x2_t, w[i] & 0x7f807f80u);
-    emin = __builtin_elementwise_min(emin, th - u16x2_t{0x80, 0x80});
-  }
-  const uint32_t lo = emin.x, hi = emin.y;
-  return (int)((lo < hi ? lo : hi) >> 7) + 1;
-}
-
-// biased exponent of a binary32 value's magnitude
-__device__ __forceinline__ int f32_exp(float v) { return (int)((__float_as_uint(v) >> 23) & 0xffu); }
 
 // Front of one row's work on a lane's E elements: x^ = x rstd, d = dy g,
 // the dot leaves d x^ and the dg leaves dy x^ (-0 where the lane's vector

@@ -590,6 +590,27 @@ def test_rmsnorm_fwd(T, D, bf16):
     assert_bitwise(grstd, rstd, "rstd")
 
 
+@pytest.mark.parametrize("T,D,xstd,gstd,gmean", [(64, 2048, 2.0 ** -63, 0.1, 1.0),
+                                                 (48, 512, 1e-30, 0.1, 1.0),
+                                                 (64, 2048, 1.0, 1e-37, 0.0),
+                                                 (40, 264, 1e-19, 1e-30, 0.0)])
+def test_rmsnorm_fwd_subnormal_band(T, D, xstd, gstd, gmean):
+    """bf16 rows whose squares or products land at or below 2^-126: the
+    unflushed evaluation of the squares (exponent bound on x) and of
+    x * rstd * g (bounds on x, rstd and g) must fall back to the flushed one
+    wherever a bound fails."""
+    say("rmsnorm_fwd subnormal band", T, D, xstd, gstd)
+    x = syn.normal((T, D), xstd, tag=218, bf16=True)
+    syn.bf16_subnormals(x, 50, tag=219)
+    # every other row at full scale, so waves of both kinds meet
+    x[::2] = syn.normal((T, D), 1.0, tag=220, bf16=True)[::2]
+    g = syn.normal((D,), gstd, mean=gmean, tag=221, bf16=True)
+    y, rstd, fl = orc.rmsnorm_fwd(x, g, 1e-6)
+    gy, grstd = brq.rmsnorm_fixed_fwd(to_dev(x), to_dev(g), 1e-6)
+    assert_bitwise(gy, y, "y")
+    assert_bitwise(grstd, rstd, "rstd")
+
+
 def test_rmsnorm_fwd_subnormal_eps():
     """A subnormal eps reads as zero (DAZ on every input): rows whose mean
     square sits just above 2^-126, where an unflushed eps of 1e-40 would
