@@ -633,9 +633,11 @@ def test_rmsnorm_fwd_subnormal_eps():
 
 
 @pytest.mark.parametrize("T,D,bf16", [(100, 2048, True), (64, 264, True), (33, 512, False),
-                                      (70, 4096, True)])
+                                      (70, 4096, True), (1025, 264, True)])
 @pytest.mark.parametrize("rows", [0, 1, 4])
 def test_rmsnorm_bwd(T, D, bf16, rows):
+    """dg's block nodes folded 32 at a time over one to three levels (1025
+    single-row blocks: 1025 -> 33 -> 2 -> 1)."""
     say("rmsnorm_bwd", T, D, bf16, rows)
     x = syn.normal((T, D), 1.0, tag=210, bf16=bf16)
     if bf16:
