@@ -52,12 +52,8 @@ __device__ __forceinline__ void put_out(float* C, int64_t idx, float v, bool bf1
 // permuted to give each XCD a contiguous range; inside a range, groups of 8
 // tile rows are swept column by column, so concurrently running tiles share
 // operand rows in that XCD's L2.
-__device__ __forceinline__ void tile_of(uint32_t p, uint32_t gm, uint32_t gn, int64_t& bm,
-                                        int64_t& bn) {
-  // tile counts fit 32 bits (the host rejects larger launches), so the
-  // index arithmetic is unsigned 32-bit
-  const uint32_t total = gm * gn;
-  if ((total & 7) == 0) p = (p & 7) * (total >> 3) + (p >> 3);
+__device__ __forceinline__ void tile_grouped(uint32_t p, uint32_t gm, uint32_t gn, int64_t& bm,
+                                             int64_t& bn) {
   const uint32_t group = 8 * gn;
   const uint32_t g = p / group, in = p - g * group;
   const uint32_t first_m = g * 8;
@@ -65,6 +61,36 @@ __device__ __forceinline__ void tile_of(uint32_t p, uint32_t gm, uint32_t gn, in
   const uint32_t n = in / gsz;
   bm = first_m + (in - n * gsz);
   bn = n;
+}
+__device__ __forceinline__ void tile_of(uint32_t p, uint32_t gm, uint32_t gn, int64_t& bm,
+                                        int64_t& bn) {
+  // tile counts fit 32 bits (the host rejects larger launches), so the
+  // index arithmetic is unsigned 32-bit
+  const uint32_t total = gm * gn;
+  if ((total & 7) == 0) p = (p & 7) * (total >> 3) + (p >> 3);
+  tile_grouped(p, gm, gn, bm, bn);
+}
+
+// Tile and contraction slice z of a work-group of a (tiles, 1, slices)
+// grid.  Work-groups go to the XCDs round-robin in launch order (x fastest,
+// then z), so with one slice tile_of applies.  With several, the (tile,
+// slice) units are renumbered the same way over the whole grid: XCD x runs
+// a contiguous range of them, i.e. one slice's block of neighbouring tiles
+// (sharing operand panels in that XCD's L2) instead of every slice of a few
+// tiles (whose contraction ranges share nothing).
+__device__ __forceinline__ void unit_of(uint32_t gm, uint32_t gn, int64_t& bm, int64_t& bn,
+                                        int64_t& z) {
+  if (gridDim.z == 1) {
+    tile_of(blockIdx.x, gm, gn, bm, bn);
+    z = 0;
+    return;
+  }
+  const uint32_t tiles = gm * gn, units = tiles * gridDim.z;
+  uint32_t p = blockIdx.x + gridDim.x * blockIdx.z;
+  if ((units & 7) == 0) p = (p & 7) * (units >> 3) + (p >> 3);
+  const uint32_t zz = p / tiles;
+  tile_grouped(p - zz * tiles, gm, gn, bm, bn);
+  z = zz;
 }
 
 // --------------------------------------------------------------------------
@@ -134,12 +160,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
   const int wm = wave / WGN, wn = wave % WGN;
 
   const int64_t gm = (I + BM - 1) / BM, gn = (J + BN - 1) / BN;
-  int64_t bm, bn;
-  tile_of(blockIdx.x, (uint32_t)gm, (uint32_t)gn, bm, bn);
+  int64_t bm, bn, zs;
+  unit_of((uint32_t)gm, (uint32_t)gn, bm, bn, zs);
   const int64_t row0 = bm * BM, col0 = bn * BN;
 
   const int64_t nk_total = (Kc + BK - 1) / BK;
-  const int64_t kt0 = (int64_t)blockIdx.z * ktiles_per_split;
+  const int64_t kt0 = zs * ktiles_per_split;
   int64_t kt1 = kt0 + ktiles_per_split;
   if (kt1 > nk_total) kt1 = nk_total;
 
@@ -222,7 +248,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_mfma(
       for (int r = 0; r < 4; ++r) {
         const int64_t row = row0 + wm * WM + i * 16 + 4 * (lane >> 4) + r;
         if (row >= I) continue;
-        if (Cpart) Cpart[((int64_t)blockIdx.z * I + row) * J + col] = acc[i][j][r];
+        if (Cpart) Cpart[(zs * I + row) * J + col] = acc[i][j][r];
         else put_out(C, row * J + col, dequant(acc[i][j][r], c), epi.out_bf16);
       }
     }
@@ -468,12 +494,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
   const int wm = wave / WGN, wn = wave % WGN;
 
   const int64_t gm = (I + BM - 1) / BM, gn = (J + BN - 1) / BN;
-  int64_t bm, bn;
-  tile_of(blockIdx.x, (uint32_t)gm, (uint32_t)gn, bm, bn);
+  int64_t bm, bn, zs;
+  unit_of((uint32_t)gm, (uint32_t)gn, bm, bn, zs);
   const int64_t row0 = bm * BM, col0 = bn * BN;
 
   const int64_t nk_total = Kc / BK;
-  const int64_t kt0 = (int64_t)blockIdx.z * ktiles_per_split;
+  const int64_t kt0 = zs * ktiles_per_split;
   int64_t kt1 = kt0 + ktiles_per_split;
   if (kt1 > nk_total) kt1 = nk_total;
   const int64_t nk = kt1 > kt0 ? kt1 - kt0 : 0;
@@ -603,10 +629,10 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_dma(
   // frees the stages for the epilogue
   __syncthreads();
   if ((Cpart || !epi.out_bf16) && row0 + BM <= I && col0 + BN <= J && (J & 3) == 0)
-    store_tile_full<BM, BN, WGM, WGN>(acc, row0, col0, wave, lane, I, J, C, Cpart, blockIdx.z,
+    store_tile_full<BM, BN, WGM, WGN>(acc, row0, col0, wave, lane, I, J, C, Cpart, zs,
                                       [&](int64_t j) { return epi.scale(j); }, smem);
   else
-    store_tile<BM, BN, WGM, WGN>(acc, row0, col0, wave, lane, I, J, C, Cpart, blockIdx.z,
+    store_tile<BM, BN, WGM, WGN>(acc, row0, col0, wave, lane, I, J, C, Cpart, zs,
                                  [&](int64_t j) { return epi.scale(j); }, smem, epi.out_bf16);
 }
 
