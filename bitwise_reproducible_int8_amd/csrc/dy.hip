@@ -46,10 +46,17 @@ constexpr int kTrStride = kCols + 4;       // padded fp32 row of the |v| transpo
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Row phase shared by both passes: lane t covers columns 8 (t & 15) .. +7 of
-// rows (t >> 4) + 16 i, i = 0..7.
-__device__ __forceinline__ u32x4 load_vec(const uint16_t* __restrict__ dy, int64_t N, int64_t m0,
-                                          int64_t col, int r) {
-  return col < N ? ld16(dy + (m0 + r) * N + col) : u32x4{0, 0, 0, 0};
+// rows (t >> 4) + 16 i, i = 0..7.  The row addresses step by 16 N from the
+// first one (64-bit adds, not a 64-bit multiply per row).
+__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ dy, int64_t N, int64_t m0,
+                                          int64_t col, int rb, u32x4 (&raw)[kRows / 16]) {
+  const uint16_t* p = dy + (m0 + rb) * N + col;
+  const int64_t step = 16 * N;
+#pragma unroll
+  for (int i = 0; i < kRows / 16; ++i) {
+    raw[i] = col < N ? ld16(p) : u32x4{0, 0, 0, 0};
+    p += step;
+  }
 }
 
 // The lane's 8 column steps (DAZ); N % 64 == 0 and colv % 8 == 0, so the 8
@@ -199,8 +206,7 @@ __global__ __launch_bounds__(256) void k_dy_stats(const uint16_t* __restrict__ d
   float s8[8];
   load_steps(sw, N, colv, s8);
   u32x4 raw[kRows / 16];
-#pragma unroll
-  for (int i = 0; i < kRows / 16; ++i) raw[i] = load_vec(dy, N, m0, colv, rb + 16 * i);
+  load_rows(dy, N, m0, colv, rb, raw);
   u16x2 lo = {0xffff, 0xffff};
 #pragma unroll
   for (int i = 0; i < kRows / 16; ++i) lo = tiny_min(lo, raw[i]);
@@ -297,15 +303,16 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
   float s8[8];
   load_steps(sw, N, colv, s8);
   u32x4 raw[kRows / 16];
-#pragma unroll
-  for (int i = 0; i < kRows / 16; ++i) raw[i] = load_vec(dy, N, m0, colv, rb + 16 * i);
+  load_rows(dy, N, m0, colv, rb, raw);
   u16x2 lo = {0xffff, 0xffff};
 #pragma unroll
   for (int i = 0; i < kRows / 16; ++i) lo = tiny_min(lo, raw[i]);
   const bool wave_tiny_ok = __all(tiny_ok(lo));
   const bool fast = wave_tiny_ok && __all(steps_ok(s8));
+  int8_t* qg_row = q_g + (m0 + rb) * N + colv;  // steps by 16 N per row
+  const int64_t qg_step = 16 * N;
 #pragma unroll
-  for (int i = 0; i < kRows / 16; ++i) {
+  for (int i = 0; i < kRows / 16; ++i, qg_row += qg_step) {
     const int r = rb + 16 * i;
     st16(lds + r * kRowBytes + 16 * cg, raw[i]);
     if (colv < N) {
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
       uint32_t p[2] = {0, 0};
 #pragma unroll
       for (int e = 0; e < 8; e += 4) p[e >> 2] = quant_pack4(f[e], f[e + 1], f[e + 2], f[e + 3], r_g);
-      *reinterpret_cast<uint2*>(q_g + (m0 + r) * N + colv) = make_uint2(p[0], p[1]);
+      *reinterpret_cast<uint2*>(qg_row) = make_uint2(p[0], p[1]);
     }
   }
   if (lane == 0) wok[wave] = wave_tiny_ok ? 1 : 0;
@@ -350,11 +357,13 @@ __global__ __launch_bounds__(256) void k_dy_codes(const uint16_t* __restrict__ d
     st16(lds + ccol * kCodeStride + tok_after(b, half, 16 * p), u32x4{w[0], w[1], w[2], w[3]});
   }
   __syncthreads();
+  // lane t stores 16 tokens of columns (t >> 3) + 32 k: 32 M apart in q_vt
+  int8_t* vt = q_vt + (c0 + (t >> 3)) * M + m0 + 16 * (t & 7);
+  const int64_t vt_step = 32 * M;
 #pragma unroll
-  for (int k = 0; k < kCols * kRows / 16 / 256; ++k) {
+  for (int k = 0; k < kCols * kRows / 16 / 256; ++k, vt += vt_step) {
     const int c = k * 32 + (t >> 3), ch = 16 * (t & 7);
-    if (c0 + c < N)
-      st16(q_vt + (c0 + c) * M + m0 + ch, *reinterpret_cast<const u32x4*>(lds + c * kCodeStride + ch));
+    if (c0 + c < N) st16(vt, *reinterpret_cast<const u32x4*>(lds + c * kCodeStride + ch));
   }
   });
 }

@@ -44,14 +44,15 @@ template <int TB>
 __device__ __forceinline__ void wht_tile_load(const int8_t* __restrict__ q_x, int64_t K,
                                               int64_t m0, int64_t k0, int8_t* tile) {
   const int t = threadIdx.x, wave = t >> 6;
+  // load i of thread t: row 8 i + t / 32, the same columns for every i
+  int64_t col = k0 + (t % (kWhtCols / 16)) * 16;
+  col = col < K ? col : k0;
+  const int8_t* src = q_x + (m0 + t / (kWhtCols / 16)) * K + col;
+  const int64_t step = (int64_t)(256 / (kWhtCols / 16)) * K;
 #pragma unroll
-  for (int i = 0; i < TB * (kWhtCols / 16) / 256; ++i) {
-    const int c = i * 256 + t;
-    const int row = c / (kWhtCols / 16);
-    int64_t col = k0 + (c % (kWhtCols / 16)) * 16;
-    col = col < K ? col : k0;
+  for (int i = 0; i < TB * (kWhtCols / 16) / 256; ++i, src += step) {
     __builtin_amdgcn_global_load_lds(
-        (const void*)(q_x + (m0 + row) * K + col),
+        (const void*)src,
         (__attribute__((address_space(3))) void*)(tile + (i * 256 + wave * 64) * 16), 16, 0, 0);
   }
   // every load of the tile has landed (this wave's), then every wave's
@@ -152,14 +153,16 @@ __global__ __launch_bounds__(256) void k_quant_x_wht(const T* __restrict__ x, in
   const int64_t k0 = (int64_t)blockIdx.x * kWhtCols;
   const int64_t m0 = (int64_t)blockIdx.y * TB;
   const float r = sr[1];
+  // chunk i of thread t: row 8 i + t / 32, the same columns for every i
+  const int64_t col = k0 + (t % (kWhtCols / 16)) * 16;
+  const int64_t rstep = (int64_t)(256 / (kWhtCols / 16)) * K;
+  const T* src = x + (m0 + t / (kWhtCols / 16)) * K + col;
+  int8_t* dst = q + (m0 + t / (kWhtCols / 16)) * K + col;
 #pragma unroll 4
-  for (int i = 0; i < TB * (kWhtCols / 16) / 256; ++i) {
+  for (int i = 0; i < TB * (kWhtCols / 16) / 256; ++i, src += rstep, dst += rstep) {
     const int c = i * 256 + t;
-    const int row = c / (kWhtCols / 16);
-    const int64_t col = k0 + (c % (kWhtCols / 16)) * 16;
     uint32_t packed[4] = {0, 0, 0, 0};
     if (col < K) {
-      const T* src = x + (m0 + row) * K + col;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         float f[E];
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(256) void k_quant_x_wht(const T* __restrict__ x, in
         for (int e = 0; e < E; e += 4)
           packed[(v * E + e) >> 2] = quant_pack4(f[e], f[e + 1], f[e + 2], f[e + 3], r);
       }
-      st16(q + (m0 + row) * K + col, u32x4{packed[0], packed[1], packed[2], packed[3]});
+      st16(dst, u32x4{packed[0], packed[1], packed[2], packed[3]});
     }
     st16(tile + (int64_t)c * 16, u32x4{packed[0], packed[1], packed[2], packed[3]});
   }
@@ -238,13 +241,16 @@ __global__ __launch_bounds__(256) void k_wht_int_quant(const int8_t* __restrict_
     }
   }
   __syncthreads();
+  // store j of thread t: column (256 / QC) j + t / QC, the same tokens for
+  // every j, so the destination steps by (256 / QC) M
+  int8_t* dst = q_ut + (k0 + t / QC) * M + m0 + 16 * (t % QC);
+  const int64_t dstep = (int64_t)(256 / QC) * M;
 #pragma unroll
-  for (int j = 0; j < kWhtCols * QC / 256; ++j) {
+  for (int j = 0; j < kWhtCols * QC / 256; ++j, dst += dstep) {
     const int ch = j * 256 + t;
     const int cc = ch / QC, q = ch % QC;
     if (k0 + cc >= K) continue;
-    st16(q_ut + (k0 + cc) * M + m0 + 16 * q,
-         ld16(tile + cc * TB + ((q ^ ((cc >> 1) & (QC - 1))) * 16)));
+    st16(dst, ld16(tile + cc * TB + ((q ^ ((cc >> 1) & (QC - 1))) * 16)));
   }
 }
 
