@@ -580,29 +580,32 @@ hipError_t quant_flat(const void* x, int dtype, const float* col_mul, int64_t n,
 // Per-row LSQ: one wave per row, 4 rows per work-group.  Vector v of lane l
 // covers columns [(64 v + l) E, + E); columns past the end are +0 leaves.
 // --------------------------------------------------------------------------
+// The row's V 16-byte vectors of lane `lane` (zero past cols).
 template <typename T, int V>
-__device__ __forceinline__ void quant_one_row(const T* __restrict__ x, int64_t row, int64_t cols,
-                                              float inv_cols, int8_t* __restrict__ q,
-                                              float* __restrict__ scale,
-                                              float* __restrict__ amax, int32_t* flags,
-                                              int lane) {
+__device__ __forceinline__ void load_row(const T* __restrict__ x, int64_t row, int64_t cols,
+                                         int lane, u32x4 (&raw)[V]) {
   constexpr int E = Elem<T>::kPerVec;
   const T* xr = x + row * cols;
-  u32x4 raw[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int64_t c0 = (int64_t)(v * 64 + lane) * E;
+    raw[v] = c0 < cols ? ld16(xr + c0) : u32x4{0, 0, 0, 0};
+  }
+}
+
+// Statistic, step size and codes of one row whose vectors are loaded.
+template <typename T, int V>
+__device__ __forceinline__ void finish_row(const u32x4 (&raw)[V], int64_t row, int64_t cols,
+                                           float inv_cols, int8_t* __restrict__ q,
+                                           float* __restrict__ scale, float* __restrict__ amax,
+                                           int32_t* flags, int lane) {
+  constexpr int E = Elem<T>::kPerVec;
   float node[V];
   float mx = 0.0f;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const int64_t c0 = (int64_t)(v * 64 + lane) * E;
     float f[E];
-    if (c0 < cols) {
-      raw[v] = ld16(xr + c0);
-      Elem<T>::unpack(raw[v], f);
-    } else {
-      raw[v] = u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < E; ++e) f[e] = 0.0f;
-    }
+    Elem<T>::unpack(raw[v], f);  // zero vectors past cols unpack to +0
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       f[e] = fabs_bits(f[e]);
@@ -631,6 +634,17 @@ __device__ __forceinline__ void quant_one_row(const T* __restrict__ x, int64_t r
     if (amax) amax[row] = mx;
     if (!__builtin_isfinite(S)) set_flag(flags, BRQ_FLAG_NONFINITE);
   }
+}
+
+template <typename T, int V>
+__device__ __forceinline__ void quant_one_row(const T* __restrict__ x, int64_t row, int64_t cols,
+                                              float inv_cols, int8_t* __restrict__ q,
+                                              float* __restrict__ scale,
+                                              float* __restrict__ amax, int32_t* flags,
+                                              int lane) {
+  u32x4 raw[V];
+  load_row<T, V>(x, row, cols, lane, raw);
+  finish_row<T, V>(raw, row, cols, inv_cols, q, scale, amax, flags, lane);
 }
 
 template <typename T, int V>
@@ -723,11 +737,19 @@ constexpr int kMultiMax = 16;
 
 // waves per row of the grouped per-row kernel
 constexpr int rows_waves(int V) { return V >= 16 ? 4 : V >= 8 ? 2 : 1; }
+// rows per work-group of the grouped kernel: a one-wave row takes
+// kRowsPerWave rows per wave, every row's loads issued before any row's
+// work, so each wave waits for memory once per kRowsPerWave rows
+constexpr int kRowsPerWave = 2;
+constexpr int rows_per_block(int V) {
+  return rows_waves(V) == 1 ? 4 * kRowsPerWave : 4 / rows_waves(V);
+}
 
 // Several tensors' per-row quantisations in one launch: work-group b
 // belongs to the tensor whose block range [start[k], start[k + 1]) holds
-// it and quantises its rows 4/W (b - start[k]) .., W = rows_waves(V) waves
-// per row, V the tensor's vectors per lane and row.
+// it and quantises its rows rows_per_block(V) (b - start[k]) .. (two rows
+// per wave when a row takes one wave, else W = rows_waves(V) waves per
+// row), V the tensor's vectors per lane and row.
 struct RowsJob {
   const void* x;
   int64_t rows, cols;
@@ -747,12 +769,20 @@ template <typename T, int V>
 __device__ __forceinline__ void rows_job(const RowsJob& j, int64_t blk, int wave, int lane,
                                          int32_t* flags, float (*red)[2]) {
   constexpr int W = rows_waves(V);
-  const int64_t row = blk * (4 / W) + wave / W;
   if constexpr (W == 1) {
-    if (row < j.rows)
-      quant_one_row<T, V>((const T*)j.x, row, j.cols, j.inv_cols, j.q, j.scale, j.amax, flags,
-                          lane);
+    // rows blk 4 R + wave + 4 i, i < R = kRowsPerWave
+    const int64_t r0 = blk * (4 * kRowsPerWave) + wave;
+    u32x4 xr[kRowsPerWave][V];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i)
+      if (r0 + 4 * i < j.rows) load_row<T, V>((const T*)j.x, r0 + 4 * i, j.cols, lane, xr[i]);
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i)
+      if (r0 + 4 * i < j.rows)
+        finish_row<T, V>(xr[i], r0 + 4 * i, j.cols, j.inv_cols, j.q, j.scale, j.amax, flags,
+                         lane);
   } else {
+    const int64_t row = blk * (4 / W) + wave / W;
     quant_row_split<T, V, W>((const T*)j.x, row, row < j.rows, j.cols, j.inv_cols, j.q, j.scale,
                              j.amax, flags, lane, wave, red);
   }
@@ -970,7 +1000,7 @@ hipError_t quant_rows_multi(const brq_rows_job* jobs, int count, int32_t* dflags
       j.inv_cols = 1.0f / (float)jobs[c].cols;  // host binary32 division, correctly rounded
       j.V = rows_vectors(dtype, jobs[c].cols);
       tab.start[tab.count] = blocks;
-      blocks += cdiv(jobs[c].rows, 4 / rows_waves(j.V));
+      blocks += cdiv(jobs[c].rows, rows_per_block(j.V));
       if (++tab.count == kMultiMax) {
         const hipError_t e = flush_table();
         if (e != hipSuccess) return e;
