@@ -890,15 +890,42 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm_stream(
 }
 
 // Sum of the split-K partials in split order (exact in int32), then the
-// same epilogue.
+// same epilogue.  Thread x of the grid owns 4 consecutive columns (J a
+// multiple of 4: 16-byte partial loads and fp32 stores) or one column, so
+// its column scales are formed once; rows go y, y + gridDim.y, ...
 __global__ __launch_bounds__(256) void k_splitk_reduce(const int* __restrict__ Cpart, int splits,
                                                        int64_t I, int64_t J, float* __restrict__ C,
                                                        Epi epi) {
   const int64_t n = I * J;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-    int acc = 0;
-    for (int z = 0; z < splits; ++z) acc += Cpart[z * n + e];
-    put_out(C, e, dequant(acc, epi.scale(e % J)), epi.out_bf16);
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if ((J & 3) == 0) {
+    const int64_t j = 4 * x;
+    if (j >= J) return;
+    float c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = epi.scale(j + k);
+    for (int64_t i = blockIdx.y; i < I; i += gridDim.y) {
+      const int64_t e = i * J + j;
+      v4i acc = {0, 0, 0, 0};
+      for (int z = 0; z < splits; ++z) acc += *reinterpret_cast<const v4i*>(Cpart + z * n + e);
+      if (epi.out_bf16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) put_out(C, e + k, dequant(acc[k], c[k]), true);
+      } else {
+        *reinterpret_cast<f32x4*>(C + e) = f32x4{dequant(acc[0], c[0]), dequant(acc[1], c[1]),
+                                                 dequant(acc[2], c[2]), dequant(acc[3], c[3])};
+      }
+    }
+  } else {
+    const int64_t j = x;
+    if (j >= J) return;
+    const float c = epi.scale(j);
+    for (int64_t i = blockIdx.y; i < I; i += gridDim.y) {
+      const int64_t e = i * J + j;
+      int acc = 0;
+      for (int z = 0; z < splits; ++z) acc += Cpart[z * n + e];
+      put_out(C, e, dequant(acc, c), epi.out_bf16);
+    }
   }
 }
 
@@ -1054,9 +1081,14 @@ hipError_t gemm_i8(const int8_t* A, const int8_t* B, int64_t I, int64_t J, int64
     default: e = launch_mfma<128, 128, 2, 2, 128>(A, B, I, J, Kc, C, part, splits, epi, s); break;
   }
   if (e != hipSuccess || splits == 1) return e;
-  int64_t blocks = cdiv(I * J, 256);
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, splits, I, J,
+  // columns across x (4 per thread when J % 4 == 0), rows across y: about
+  // 2048 work-groups, each thread walking I / gridDim.y rows
+  const int64_t gx = cdiv((J & 3) == 0 ? J / 4 : J, 256);
+  int64_t gy = 2048 / gx;
+  if (gy < 1) gy = 1;
+  if (gy > I) gy = I;
+  if (gy > 65535) gy = 65535;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, part, splits, I, J,
                      C, epi);
   return hipGetLastError();
 }
