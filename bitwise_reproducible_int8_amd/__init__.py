@@ -35,7 +35,8 @@ SYMBOLS = [
     "brq_quantize_dy_bwd", "brq_qgemm_bwd_dx_wht", "brq_wht_quant_dy_rows", "brq_attn_fwd",
     "brq_rmsnorm_fixed_fwd", "brq_rmsnorm_fixed_bwd", "brq_grad_norm",
     "brq_hash_workspace_size", "brq_hash_state", "brq_hash_digests_workspace_size",
-    "brq_hash_tensor_digests", "brq_hash_combine", "brq_adamw_bias_corrections",
+    "brq_hash_tensor_digests", "brq_hash_combine", "brq_hash_tensor_leaves",
+    "brq_hash_tensor_finish", "brq_adamw_bias_corrections",
     "brq_adamw_decide", "brq_adamw_step", "brq_dp_reduce", "brq_fp32_primitive", "brq_status_string",
     "brq_last_hip_error", "brq_spec_version",
 ]
@@ -142,6 +143,10 @@ def lib():
         L.brq_hash_tensor_digests.argtypes = [vp, i32, vp, vp, sz, vp]
         L.brq_hash_combine.restype = i32
         L.brq_hash_combine.argtypes = [vp, i32, vp, vp]
+        L.brq_hash_tensor_leaves.restype = i32
+        L.brq_hash_tensor_leaves.argtypes = [vp, i32, vp, sz, vp]
+        L.brq_hash_tensor_finish.restype = i32
+        L.brq_hash_tensor_finish.argtypes = [vp, i32, vp, vp, sz, vp]
         L.brq_adamw_bias_corrections.restype = i32
         L.brq_adamw_bias_corrections.argtypes = [i64, C.c_float, C.c_float, vp, vp]
         L.brq_adamw_decide.restype = i32
@@ -669,6 +674,33 @@ def hash_tensor_digests(tensors, out, ws=None):
     w = _ws(need, out.device, ws)
     _check(lib().brq_hash_tensor_digests(refs, len(tensors), _ptr(out), _ptr(w), w.numel(),
                                          _stream()), "hash_tensor_digests")
+    return out
+
+
+def hash_tensor_leaves(tensors, ws):
+    """First stage of hash_tensor_digests: the leaf digests of ``tensors``
+    into ``ws`` (a device workspace of hash_digests_workspace_size bytes),
+    on the current stream.  The only stage that reads the tensors."""
+    refs, _keep = _refs(tensors)
+    _dev(ws, "ws")
+    need = int(lib().brq_hash_digests_workspace_size(refs, len(tensors)))
+    w = _ws(need, ws.device, ws)
+    _check(lib().brq_hash_tensor_leaves(refs, len(tensors), _ptr(w), w.numel(), _stream()),
+           "hash_tensor_leaves")
+
+
+def hash_tensor_finish(tensors, out, ws):
+    """Second stage: every level above the leaves and the tensor digests
+    into ``out`` (uint8 [32 * n]), on the current stream, reading only
+    ``ws`` as the first stage left it."""
+    refs, _keep = _refs(tensors)
+    _dev(out, "out"); _dev(ws, "ws")
+    if out.dtype != torch.uint8 or out.numel() != 32 * len(tensors):
+        raise BrqError("out: expected uint8 [32 * n]")
+    need = int(lib().brq_hash_digests_workspace_size(refs, len(tensors)))
+    w = _ws(need, ws.device, ws)
+    _check(lib().brq_hash_tensor_finish(refs, len(tensors), _ptr(out), _ptr(w), w.numel(),
+                                        _stream()), "hash_tensor_finish")
     return out
 
 

@@ -644,6 +644,24 @@ int brq_hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* digests, vo
   return hip_status(hash_tensor_digests(t, n, digests, ws, as_stream(stream)));
 }
 
+int brq_hash_tensor_leaves(const brq_tensor_ref* t, int n, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int st = check_refs(t, n);
+  if (st != BRQ_OK) return st;
+  if (!ws || ws_bytes < hash_digests_ws(t, n)) return BRQ_E_WORKSPACE;
+  return hip_status(hash_tensor_leaves(t, n, ws, as_stream(stream)));
+}
+
+int brq_hash_tensor_finish(const brq_tensor_ref* t, int n, uint8_t* digests, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int st = check_refs(t, n);
+  if (st != BRQ_OK) return st;
+  if (n > 0 && !digests) return BRQ_E_NULL;
+  if (!aligned16(digests)) return BRQ_E_ALIGN;
+  if (!ws || ws_bytes < hash_digests_ws(t, n)) return BRQ_E_WORKSPACE;
+  return hip_status(hash_tensor_finish(t, n, digests, ws, as_stream(stream)));
+}
+
 int brq_hash_combine(const uint8_t* digests, int n, uint8_t* digest32, void* stream) {
   if (n < 0) return BRQ_E_SHAPE;
   if (!digest32 || (n > 0 && !digests)) return BRQ_E_NULL;

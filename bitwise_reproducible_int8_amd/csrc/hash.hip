@@ -16,6 +16,8 @@
 //   - the round function is written in the shapes gfx950 has single
 //     instructions for: rotate (v_alignbit_b32), three-way xor, choose and
 //     majority (v_bitop3_b32), three-way add (v_add3_u32).
+#include <limits.h>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -315,14 +317,16 @@ size_t hash_ws(const brq_tensor_ref* t, int n) {
   return align256(32 * (uint64_t)(n > 0 ? n : 1)) + hash_digests_ws(t, n);
 }
 
-hipError_t hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* tdig, void* ws,
-                               hipStream_t s) {
+namespace {
+
+// Merkle levels l0 <= l < l1 of every tensor: level 0 hashes tensor bytes,
+// level l > 0 the digests of level l - 1; tensors whose tree has ended drop
+// out, and the pass stops when every tree has.
+hipError_t hash_levels(const brq_tensor_ref* t, int n, void* ws, int l0, int l1, hipStream_t s) {
   uint8_t* base = (uint8_t*)ws;
   hipError_t e;
   SliceBatch b{};
-  // pass over levels: level 0 hashes tensor bytes, level l > 0 hashes the
-  // digests of level l - 1; tensors whose tree has ended drop out
-  for (int l = 0;; ++l) {
+  for (int l = l0; l < l1; ++l) {
     bool any = false;
     uint8_t* region = base;
     for (int i = 0; i < n; ++i) {
@@ -345,7 +349,13 @@ hipError_t hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* tdig, vo
     if ((e = launch_slices(b, s)) != hipSuccess) return e;
     if (!any) break;
   }
-  // tensor digests: SHA-256(header | root)
+  return hipSuccess;
+}
+
+// Tensor digests SHA-256(header | root) once every tree is complete.
+hipError_t hash_headers(const brq_tensor_ref* t, int n, uint8_t* tdig, void* ws, hipStream_t s) {
+  uint8_t* base = (uint8_t*)ws;
+  hipError_t e;
   HeaderBatch hb{};
   uint8_t* region = base;
   for (int i = 0; i < n; ++i) {
@@ -382,6 +392,28 @@ hipError_t hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* tdig, vo
     }
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* tdig, void* ws,
+                               hipStream_t s) {
+  hipError_t e = hash_levels(t, n, ws, 0, INT_MAX, s);
+  if (e != hipSuccess) return e;
+  return hash_headers(t, n, tdig, ws, s);
+}
+
+// The leaf level alone: the only part that reads the tensors.
+hipError_t hash_tensor_leaves(const brq_tensor_ref* t, int n, void* ws, hipStream_t s) {
+  return hash_levels(t, n, ws, 0, 1, s);
+}
+
+// Every level above the leaves, then the tensor digests: reads only ws.
+hipError_t hash_tensor_finish(const brq_tensor_ref* t, int n, uint8_t* tdig, void* ws,
+                              hipStream_t s) {
+  hipError_t e = hash_levels(t, n, ws, 1, INT_MAX, s);
+  if (e != hipSuccess) return e;
+  return hash_headers(t, n, tdig, ws, s);
 }
 
 hipError_t hash_combine(const uint8_t* tdig, int n, uint8_t* digest32, hipStream_t s) {

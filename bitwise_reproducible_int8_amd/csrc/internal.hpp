@@ -195,6 +195,9 @@ size_t hash_digests_ws(const brq_tensor_ref* t, int n);
 hipError_t hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* digests, void* ws,
                                hipStream_t s);
 hipError_t hash_combine(const uint8_t* digests, int n, uint8_t* digest32, hipStream_t s);
+hipError_t hash_tensor_leaves(const brq_tensor_ref* t, int n, void* ws, hipStream_t s);
+hipError_t hash_tensor_finish(const brq_tensor_ref* t, int n, uint8_t* digests, void* ws,
+                              hipStream_t s);
 hipError_t hash_state(const brq_tensor_ref* t, int n, uint8_t* digest32,
                       void* ws, hipStream_t s);
 

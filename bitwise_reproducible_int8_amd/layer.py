@@ -28,10 +28,13 @@ torch's current stream:
   7. global l2 norm over the gradient arena                     (grad_norm)
   8. SHA-256 state hash of every output and gradient          (hash_state)
 
-The hash runs last, in one batched call on the same stream.  (Hashing each
-tensor on a second stream as soon as it is written measured slower on
-MI355X: the integer-ALU hash and the GEMMs then share CUs and both slow
-down.)
+The hash runs last, in one batched call on the same stream, or (with
+overlap_hash) with only its leaf level there and the levels above it on a
+second stream, where they overlap the next step: those levels are a few
+long SHA chains on a few hundred lanes, about 0.6 ms of latency with the
+GPU otherwise idle.  (Hashing each tensor's leaves on a second stream as
+soon as it is written measured slower on MI355X: the integer-ALU hash and
+the GEMMs then share CUs and both slow down.)
 
 The rotated code of an activation depends on that activation alone, so
 linears that share an input (Q/K/V, gate/up) share one rotation, made with
@@ -54,7 +57,8 @@ import torch
 from . import (ADAMW_WD, SPIKE_THRESHOLD, BrqError, OP_DW_WHT, OP_DY_BWD, OP_GRAD_NORM, OP_QGEMM,
                OP_QUANTIZE, OP_QUANTIZE_X_WHT,
                OP_RMSNORM_BWD, adamw_bias_corrections, adamw_decide, adamw_step, grad_norm,
-               hash_state, hash_state_workspace_size, qgemm_bwd_dx, qgemm_dw, qgemm_fwd,
+               hash_combine, hash_digests_workspace_size, hash_state, hash_state_workspace_size,
+               hash_tensor_finish, hash_tensor_leaves, qgemm_bwd_dx, qgemm_dw, qgemm_fwd,
                quantize_dy_bwd, quantize_lsq_rows_multi, quantize_x_wht, rmsnorm_fixed_bwd,
                rmsnorm_fixed_fwd, workspace_size)
 
@@ -132,6 +136,12 @@ class LayerStep:
             off += D
         self.gn = e(2)
         self.digest = torch.empty(32, dtype=torch.uint8, device=dev)
+        # the overlapped hash's own workspace, tensor digests and stream (see run)
+        hl = self.hash_list()
+        self.hws = torch.zeros(hash_digests_workspace_size(hl), dtype=torch.uint8, device=dev)
+        self.tdig = torch.empty(32 * len(hl), dtype=torch.uint8, device=dev)
+        self._side = None
+        self._finish_done = None
         # one workspace, large enough for every call (calls are stream-ordered)
         need = [workspace_size(OP_GRAD_NORM, self.arena.numel(), tune=tune)]
         for xin, t in x.items():
@@ -159,7 +169,13 @@ class LayerStep:
         return out
 
     # -- one step --------------------------------------------------------------
-    def run(self, timer=None, hash_outputs=True):
+    def run(self, timer=None, hash_outputs=True, overlap_hash=False, digest_out=None):
+        """One layer step.  With overlap_hash the state hash's leaf level
+        (the only part that reads the outputs) runs on the current stream
+        and the levels above it, the tensor digests and the state digest on
+        a second stream, overlapping the next step's work; call finish()
+        before reading the digest.  digest_out receives the state digest
+        (default self.digest)."""
         T = timer or _NoTimer()
         tune, ws, fl, b = self.tune, self.ws, self.flags, self.block
         for j, (_name, h, g, _d) in enumerate(self.norms):
@@ -205,9 +221,34 @@ class LayerStep:
         grad_norm(self.arena, flags=fl, tune=tune, ws=ws, out=self.gn)
         T.end("grad_norm")
         if hash_outputs:
+            dout = self.digest if digest_out is None else digest_out
             T.begin("hash_state")
-            hash_state(self.hash_list(), ws=ws, out=self.digest)
+            if overlap_hash:
+                hl = self.hash_list()
+                cur = torch.cuda.current_stream()
+                if self._finish_done is not None:
+                    # the previous step's upper levels still read self.hws
+                    cur.wait_event(self._finish_done)
+                hash_tensor_leaves(hl, self.hws)
+                leaves_done = torch.cuda.Event()
+                leaves_done.record(cur)
+                if self._side is None:
+                    self._side = torch.cuda.Stream(device=self.device)
+                self._side.wait_event(leaves_done)
+                with torch.cuda.stream(self._side):
+                    hash_tensor_finish(hl, self.tdig, self.hws)
+                    hash_combine(self.tdig, out=dout)
+                    self._finish_done = torch.cuda.Event()
+                    self._finish_done.record(self._side)
+            else:
+                self.finish()
+                hash_state(self.hash_list(), ws=ws, out=dout)
             T.end("hash_state")
+
+    def finish(self):
+        """Make the current stream wait for the last overlapped hash."""
+        if self._finish_done is not None:
+            torch.cuda.current_stream().wait_event(self._finish_done)
 
 
 class OptimizerStep:

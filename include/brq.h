@@ -456,6 +456,24 @@ int brq_hash_tensor_digests(const brq_tensor_ref* t, int n, uint8_t* digests,
 int brq_hash_combine(const uint8_t* digests, int n, uint8_t* digest32,
                      void* stream);
 
+/* brq_hash_tensor_digests in two stages, so that a step's hash need not
+ * hold up the next step (same definitions as above):
+ *   brq_hash_tensor_leaves: the leaf digests of every t[i] into ws -- the
+ *     only stage that reads the tensors; once it has completed on `stream`
+ *     they may be overwritten.
+ *   brq_hash_tensor_finish: every level above the leaves and the tensor
+ *     digests into `digests`, reading only ws (the tensors' sizes, dtypes
+ *     and names come from t; t[i].data is not read), so it may run on
+ *     another stream once the leaves stage has completed.
+ * Both take the same t, n and workspace (brq_hash_digests_workspace_size);
+ * the workspace must not be used by anything else from the start of the
+ * leaves stage until the finish stage has completed.  Errors as
+ * brq_hash_tensor_digests. */
+int brq_hash_tensor_leaves(const brq_tensor_ref* t, int n, void* ws, size_t ws_bytes,
+                           void* stream);
+int brq_hash_tensor_finish(const brq_tensor_ref* t, int n, uint8_t* digests, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------
  * Optimizer step after the layer: AdamW with global-norm clipping and the
  * spike protocol (§3.2 "Optimizer": beta1 0.9, beta2 0.95, eps 1e-8,

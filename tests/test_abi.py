@@ -146,3 +146,31 @@ def test_rows_multi_argument_checks(lib):
     assert f(jobs, 2, None, None) == -4
     jobs[1].x, jobs[1].scale = fake, None
     assert f(jobs, 2, None, None) == -1
+
+
+def test_hash_stage_argument_checks(lib):
+    """The two stages of the tensor digests check their arguments before
+    any device call (a missing workspace, a missing or misaligned digest
+    buffer)."""
+    class Ref(C.Structure):
+        _fields_ = [("data", C.c_void_p), ("dtype", C.c_int), ("ndim", C.c_int),
+                    ("dims", C.c_int64 * 8), ("name", C.c_char_p)]
+    refs = (Ref * 1)()
+    refs[0].data, refs[0].dtype, refs[0].ndim, refs[0].name = 0x1000, 0, 1, b"a"
+    refs[0].dims[0] = 4096
+    vp, i32, sz = C.c_void_p, C.c_int, C.c_size_t
+    lib.brq_hash_digests_workspace_size.restype = sz
+    lib.brq_hash_digests_workspace_size.argtypes = [vp, i32]
+    need = lib.brq_hash_digests_workspace_size(refs, 1)
+    assert need > 0
+    lv = lib.brq_hash_tensor_leaves
+    lv.restype = i32
+    lv.argtypes = [vp, i32, vp, sz, vp]
+    fn = lib.brq_hash_tensor_finish
+    fn.restype = i32
+    fn.argtypes = [vp, i32, vp, vp, sz, vp]
+    assert lv(refs, 1, None, 0, None) == -7
+    assert lv(refs, 1, 0x2000, need - 1, None) == -7
+    assert fn(refs, 1, None, 0x2000, need, None) == -1
+    assert fn(refs, 1, 0x3008, 0x2000, need, None) == -4
+    assert fn(refs, 1, 0x3000, 0x2000, need - 1, None) == -7

@@ -222,6 +222,29 @@ def test_layer_full(brq, layer_data, tune):
     assert bytes(to_np(step.digest)).hex() == stored("layer")["state"]
 
 
+@pytest.mark.timeout(900)
+def test_layer_full_overlapped_hash(brq, layer_data):
+    """The benchmark's timed loop: steps back to back with each step's hash
+    above its leaf level on a second stream, overlapping the next step.
+    Every step's state digest (each into its own buffer) equals the
+    oracle's, and a step without the overlap after them still does."""
+    say("full layer 32768 tokens, overlapped hash, 4 steps")
+    from bitwise_reproducible_int8_amd.layer import LayerStep
+    M, x, w, dy, norms = layer_data
+    step = LayerStep(syn.LAYER_LINEARS, x, w, dy, norms, block=128)
+    outs = [torch.zeros(32, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    for d in outs:
+        step.run(overlap_hash=True, digest_out=d)
+    step.finish()
+    torch.cuda.synchronize()
+    want = stored("layer")["state"]
+    for k, d in enumerate(outs):
+        assert bytes(to_np(d)).hex() == want, f"step {k}"
+    step.run()
+    torch.cuda.synchronize()
+    assert bytes(to_np(step.digest)).hex() == want
+
+
 @pytest.mark.parametrize("grad_std,expect", [(1e-4, "keep"), (3e-4, "clip"), (1e-3, "skip")])
 def test_optimizer_full(brq, grad_std, expect):
     """The optimizer step over a layer-sized parameter set (the seven

@@ -736,6 +736,18 @@ def test_hash_split_equals_state():
     assert bytes(to_np(brq.hash_combine(dig))) == want
     for i, (n, a) in enumerate(ts):
         assert bytes(to_np(dig[32 * i:32 * i + 32])) == orc.tensor_digest(n, a)
+    # the two stages: leaves on this stream, the rest on another once the
+    # leaves are done -- after the tensors themselves have been overwritten
+    ws = torch.zeros(brq.hash_digests_workspace_size(dts), dtype=torch.uint8, device=DEV)
+    brq.hash_tensor_leaves(dts, ws)
+    for _, t in dts:
+        t.zero_()
+    dig2 = torch.zeros_like(dig)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        brq.hash_tensor_finish(dts, dig2, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    assert bytes(to_np(dig2)) == bytes(to_np(dig))
 
 
 # --------------------------------------------------------------------------
