@@ -17,6 +17,7 @@
 //     instructions for: rotate (v_alignbit_b32), three-way xor, choose and
 //     majority (v_bitop3_b32), three-way add (v_add3_u32).
 #include <limits.h>
+#include <string.h>
 
 #include "device.hpp"
 #include "internal.hpp"
@@ -28,8 +29,9 @@ namespace {
 constexpr int kLeaf = 4096;     // bytes per leaf (and per interior node's input)
 constexpr int kFan = 128;       // digests per interior node
 constexpr int kBatch = 32;      // buffers per slice launch
-constexpr int kHdrBatch = 8;    // tensor headers per header launch
+constexpr int kHdrBatch = 32;   // tensor headers per header launch
 constexpr int kHdrMax = 336;    // header bytes: 4+1+1+8*8+2+255 = 327
+constexpr int kHdrBlob = 2048;  // header bytes per launch, packed back to back
 
 __constant__ uint32_t kSha256K[64] = {
     0x428a2f98u, 0x71374491u, 0xb5c0fbcfu, 0xe9b5dba5u, 0x3956c25bu, 0x59f111f1u, 0x923f82a4u,
@@ -209,30 +211,27 @@ __global__ __launch_bounds__(64) void k_sha_partial(SliceBatch b) {
 }
 
 // Tensor digests: SHA-256(header | root), one lane per tensor.
+// Headers packed back to back in one blob (header k at bytes off[k] ..
+// off[k] + len[k] - 1), so that a launch's kernel argument holds up to
+// kHdrBatch of them.
 struct HeaderBatch {
-  uint8_t bytes[kHdrBatch][kHdrMax];
-  int len[kHdrBatch];
+  uint8_t bytes[kHdrBlob];
+  uint16_t off[kHdrBatch];
+  uint16_t len[kHdrBatch];
   const uint8_t* root[kHdrBatch];
   uint8_t* out[kHdrBatch];
   int n;
 };
 
 __global__ __launch_bounds__(64) void k_sha_headers(HeaderBatch hb) {
-  // the batch's header bytes and each tensor's root, staged in LDS with
-  // coalesced word copies, then one lane per tensor hashes its message
+  // lane i stages its header (out of the blob) and its tensor's root in
+  // LDS and hashes that message
+  static_assert(kHdrBatch <= 64, "one lane per header");
   __shared__ __attribute__((aligned(16))) uint8_t msg[kHdrBatch][kHdrMax + 32];
-  static_assert(kHdrMax % 4 == 0, "word copies");
-  {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(&hb.bytes[0][0]);
-    for (int w = threadIdx.x; w < kHdrBatch * kHdrMax / 4; w += 64) {
-      const int row = w / (kHdrMax / 4), col = w % (kHdrMax / 4);
-      *reinterpret_cast<uint32_t*>(&msg[row][4 * col]) = src[w];
-    }
-  }
-  __syncthreads();
   const int i = threadIdx.x;
   if (i >= hb.n) return;
   const int n = hb.len[i];
+  for (int k = 0; k < n; ++k) msg[i][k] = hb.bytes[hb.off[i] + k];
   const int len = n + 32;
   for (int k = 0; k < 32; ++k) msg[i][n + k] = hb.root[i][k];
   Sha st;
@@ -357,6 +356,7 @@ hipError_t hash_headers(const brq_tensor_ref* t, int n, uint8_t* tdig, void* ws,
   uint8_t* base = (uint8_t*)ws;
   hipError_t e;
   HeaderBatch hb{};
+  int used = 0;  // blob bytes taken by the batch
   uint8_t* region = base;
   for (int i = 0; i < n; ++i) {
     const uint64_t nb = tensor_bytes(t[i]);
@@ -369,9 +369,8 @@ hipError_t hash_headers(const brq_tensor_ref* t, int n, uint8_t* tdig, void* ws,
       r += align256(32 * cnt[k]);
     }
     region = r;
-    const int k = hb.n;
+    uint8_t h[kHdrMax];
     int o = 0;
-    uint8_t* h = hb.bytes[k];
     h[o++] = 'B'; h[o++] = 'R'; h[o++] = 'Q'; h[o++] = '1';
     h[o++] = (uint8_t)t[i].dtype;
     h[o++] = (uint8_t)t[i].ndim;
@@ -382,14 +381,24 @@ hipError_t hash_headers(const brq_tensor_ref* t, int n, uint8_t* tdig, void* ws,
     h[o++] = (uint8_t)(nl & 0xff);
     h[o++] = (uint8_t)(nl >> 8);
     for (size_t c = 0; c < nl; ++c) h[o++] = (uint8_t)t[i].name[c];
-    hb.len[k] = o;
-    hb.root[k] = root;
-    hb.out[k] = tdig + 32 * i;
-    if (++hb.n == kHdrBatch || i == n - 1) {
+    // a full batch or blob goes out first
+    if (hb.n == kHdrBatch || used + o > kHdrBlob) {
       hipLaunchKernelGGL(k_sha_headers, dim3(1), dim3(64), 0, s, hb);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       hb.n = 0;
+      used = 0;
     }
+    const int k = hb.n++;
+    memcpy(hb.bytes + used, h, (size_t)o);
+    hb.off[k] = (uint16_t)used;
+    hb.len[k] = (uint16_t)o;
+    hb.root[k] = root;
+    hb.out[k] = tdig + 32 * i;
+    used += o;
+  }
+  if (hb.n > 0) {
+    hipLaunchKernelGGL(k_sha_headers, dim3(1), dim3(64), 0, s, hb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }
