@@ -240,6 +240,10 @@ class LayerStep:
                     hash_combine(self.tdig, out=dout)
                     self._finish_done = torch.cuda.Event()
                     self._finish_done.record(self._side)
+                # memory the second stream uses is not handed out again by
+                # the caching allocator before that stream's work is done
+                for t in (self.hws, self.tdig, dout):
+                    t.record_stream(self._side)
             else:
                 self.finish()
                 hash_state(self.hash_list(), ws=ws, out=dout)
