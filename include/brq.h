@@ -463,8 +463,10 @@ int brq_hash_combine(const uint8_t* digests, int n, uint8_t* digest32,
  *     they may be overwritten.
  *   brq_hash_tensor_finish: every level above the leaves and the tensor
  *     digests into `digests`, reading only ws (the tensors' sizes, dtypes
- *     and names come from t; t[i].data is not read), so it may run on
- *     another stream once the leaves stage has completed.
+ *     and names come from t; t[i].data is checked as by the leaves stage
+ *     but not dereferenced), so it may run on another stream once the
+ *     leaves stage has completed (§5 "Runtime overhead": the hash should
+ *     not hold up training).
  * Both take the same t, n and workspace (brq_hash_digests_workspace_size);
  * the workspace must not be used by anything else from the start of the
  * leaves stage until the finish stage has completed.  Errors as
