@@ -465,8 +465,8 @@ int brq_hash_combine(const uint8_t* digests, int n, uint8_t* digest32,
  *     digests into `digests`, reading only ws (the tensors' sizes, dtypes
  *     and names come from t; t[i].data is checked as by the leaves stage
  *     but not dereferenced), so it may run on another stream once the
- *     leaves stage has completed (§5 "Runtime overhead": the hash should
- *     not hold up training).
+ *     leaves stage has completed (§5 "Strong Scaling", Table 11: the
+ *     per-step hash lowers the run's throughput).
  * Both take the same t, n and workspace (brq_hash_digests_workspace_size);
  * the workspace must not be used by anything else from the start of the
  * leaves stage until the finish stage has completed.  Errors as
